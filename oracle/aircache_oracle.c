@@ -1,0 +1,314 @@
+/*
+ * AirCache oracle: a plain, slow, single-threaded CPU implementation, in
+ * double precision, of the post-prefill visual KV-cache compression pass.
+ *
+ * Source of every step: the paper-notes page "AirCache: Activating Inter-Modal
+ * Relevancy KV Cache Compression for Efficient Large Vision-Language Model
+ * Inference" (ICCV 2025), sections "Elite Observation Window" (key design 1),
+ * "Layer-wise KV Cache Budget Allocation" (key design 2) and the training-free
+ * procedure (prefill, then one budget-and-compress step over all layers).
+ *
+ * TEST INFRASTRUCTURE ONLY. The test suite, the smoke check and the
+ * benchmark's CPU-baseline leg are the only callers. The HIP library never
+ * links, loads or calls this file, and this file includes nothing from it.
+ *
+ * Every floating-point quantity is computed in double precision from inputs
+ * widened exactly (float32 or bfloat16 bit patterns). Build with
+ * -ffp-contract=off so that no multiply-add is fused behind the reader's back.
+ *
+ * Readings where the page leaves a step open (each also listed in the design
+ * notes of the repository):
+ *  - multi-head: per-head attention with D = head_dim; query head h reads
+ *    KV head h / (H_q / H_kv); step 1 averages the per-head softmax rows over
+ *    the query heads and yields one elite set per (layer, sample); step 2
+ *    averages over all query heads and all elite rows;
+ *  - step 2 normalises each elite row over the N_v visual keys plus the N_tk
+ *    elite text keys only, with no causal mask;
+ *  - skewness uses the sample standard deviation (n - 1); sigma = 0 gives 0;
+ *  - cross-layer normalisation is mean-1 scaling per sample; skewness is first
+ *    shifted by min(0, min_l s_k) so that it is non-negative (all-zero after
+ *    the shift gives 1 for every layer);
+ *  - r = ratio * N_v as a real number, floored once at the end, clamped to
+ *    [0, N_v];
+ *  - top-r selection by I_v, equal scores go to the lower index, kept indices
+ *    are emitted in ascending order;
+ *  - compacted layout per (layer, sample, KV head): kept visual rows in
+ *    ascending order, then all text rows, samples packed one after another.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+  int L, B, Hq, Hkv, D, Nv, Nt;
+  int dtype; /* 0: float32, 1: bfloat16 bit patterns */
+  double alpha;
+  double ratio;
+} orc_desc;
+
+static double elem(const void *base, size_t i, int dtype) {
+  if (dtype == 0) return (double)((const float *)base)[i];
+  uint32_t u = (uint32_t)((const uint16_t *)base)[i] << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static size_t q_index(const orc_desc *w, int b, int h, int j) {
+  return (((size_t)b * w->Hq + h) * w->Nt + j) * (size_t)w->D;
+}
+
+static size_t k_index(const orc_desc *w, int b, int g, int s) {
+  return (((size_t)b * w->Hkv + g) * (size_t)(w->Nv + w->Nt) + s) * (size_t)w->D;
+}
+
+/* Scaled dot product q_{b,h,jq} . k_{b,g,s} / sqrt(D). */
+static double logit(const orc_desc *w, const void *q_l, const void *k_l, int b,
+                    int h, int jq, int g, int s) {
+  size_t qi = q_index(w, b, h, jq), ki = k_index(w, b, g, s);
+  double acc = 0.0;
+  for (int d = 0; d < w->D; ++d) acc += elem(q_l, qi + d, w->dtype) * elem(k_l, ki + d, w->dtype);
+  return acc / sqrt((double)w->D);
+}
+
+/* Softmax of z[0..n) in place: exp(z - max) / sum. */
+static void softmax(double *z, int n) {
+  double m = z[0];
+  for (int i = 1; i < n; ++i)
+    if (z[i] > m) m = z[i];
+  double s = 0.0;
+  for (int i = 0; i < n; ++i) {
+    z[i] = exp(z[i] - m);
+    s += z[i];
+  }
+  for (int i = 0; i < n; ++i) z[i] /= s;
+}
+
+/*
+ * Step 1, elite observation window (text-only attention and the elite set).
+ * For every query head: the softmax row of the last text query over the N_t
+ * text keys. pbar = mean of those rows over the query heads. The elite set is
+ * { j : pbar[j] >= alpha * max(pbar) }, written in ascending order.
+ * Returns N_tk. pbar receives N_t values.
+ */
+int orc_elite_select(const orc_desc *w, const void *q_l, const void *k_l, int b,
+                     double *pbar, int32_t *elite) {
+  const int G = w->Hq / w->Hkv;
+  double *z = (double *)malloc(sizeof(double) * (size_t)w->Nt);
+  for (int j = 0; j < w->Nt; ++j) pbar[j] = 0.0;
+  for (int h = 0; h < w->Hq; ++h) {
+    int g = h / G;
+    for (int j = 0; j < w->Nt; ++j) z[j] = logit(w, q_l, k_l, b, h, w->Nt - 1, g, w->Nv + j);
+    softmax(z, w->Nt);
+    for (int j = 0; j < w->Nt; ++j) pbar[j] += z[j];
+  }
+  for (int j = 0; j < w->Nt; ++j) pbar[j] /= (double)w->Hq;
+  double pmax = pbar[0];
+  for (int j = 1; j < w->Nt; ++j)
+    if (pbar[j] > pmax) pmax = pbar[j];
+  int n = 0;
+  for (int j = 0; j < w->Nt; ++j)
+    if (pbar[j] >= w->alpha * pmax) elite[n++] = j;
+  free(z);
+  return n;
+}
+
+/*
+ * Step 2, cross-modal attention of the elite queries and visual importance.
+ * For every query head h and elite query j: softmax over the columns
+ * [visual keys 0..N_v-1, elite text keys], then I_v[i] is the mean over all
+ * (h, j) rows of the probability at visual column i.
+ */
+void orc_cross_score(const orc_desc *w, const void *q_l, const void *k_l, int b,
+                     const int32_t *elite, int ntk, double *iv) {
+  const int G = w->Hq / w->Hkv;
+  const int ncol = w->Nv + ntk;
+  double *z = (double *)malloc(sizeof(double) * (size_t)ncol);
+  for (int i = 0; i < w->Nv; ++i) iv[i] = 0.0;
+  for (int h = 0; h < w->Hq; ++h) {
+    int g = h / G;
+    for (int e = 0; e < ntk; ++e) {
+      int jq = elite[e];
+      for (int c = 0; c < w->Nv; ++c) z[c] = logit(w, q_l, k_l, b, h, jq, g, c);
+      for (int e2 = 0; e2 < ntk; ++e2) z[w->Nv + e2] = logit(w, q_l, k_l, b, h, jq, g, w->Nv + elite[e2]);
+      softmax(z, ncol);
+      for (int i = 0; i < w->Nv; ++i) iv[i] += z[i];
+    }
+  }
+  for (int i = 0; i < w->Nv; ++i) iv[i] /= (double)w->Hq * (double)ntk;
+  free(z);
+}
+
+/*
+ * Step 3, layer strength and skewness of I_v.
+ * s_t = sum I_v; s_k = n / ((n-1)(n-2)) * sum(((I_v - mu) / sigma)^3) with mu
+ * the mean and sigma the sample standard deviation; sigma = 0 gives s_k = 0.
+ */
+void orc_layer_stats(const double *iv, int n, double *s_t, double *s_k) {
+  double s = 0.0;
+  for (int i = 0; i < n; ++i) s += iv[i];
+  /* sigma and the skewness do not change when every value is shifted by the
+   * same amount; working on y = I_v - I_v[0] keeps an exactly constant vector
+   * exactly zero, so its sigma is 0 rather than a rounding residue. */
+  const double x0 = iv[0];
+  double sy = 0.0;
+  for (int i = 0; i < n; ++i) sy += iv[i] - x0;
+  double mu = sy / (double)n;
+  double v = 0.0;
+  for (int i = 0; i < n; ++i) v += ((iv[i] - x0) - mu) * ((iv[i] - x0) - mu);
+  double sigma = sqrt(v / (double)(n - 1));
+  double k3 = 0.0;
+  if (sigma > 0.0) {
+    for (int i = 0; i < n; ++i) {
+      double t = ((iv[i] - x0) - mu) / sigma;
+      k3 += t * t * t;
+    }
+    k3 *= (double)n / ((double)(n - 1) * (double)(n - 2));
+  }
+  *s_t = s;
+  *s_k = k3;
+}
+
+/*
+ * Step 4, budget of every layer of one sample (L layers, ascending order).
+ * s't = s_t * L / sum(s_t); shift m = min(0, min s_k), u = s_k - m,
+ * s'k = u * L / sum(u) (1 for every layer when sum(u) = 0);
+ * x = 0.5 * (s't + s'k) * (ratio * N_v); budget = clamp(floor(x), 0, N_v).
+ */
+void orc_budget(const double *s_t, const double *s_k, int L, double ratio, int Nv,
+                double *x, int32_t *budget) {
+  double st_sum = 0.0, m = 0.0, u_sum = 0.0;
+  for (int l = 0; l < L; ++l) st_sum += s_t[l];
+  for (int l = 0; l < L; ++l)
+    if (s_k[l] < m) m = s_k[l];
+  for (int l = 0; l < L; ++l) u_sum += s_k[l] - m;
+  double r = ratio * (double)Nv;
+  for (int l = 0; l < L; ++l) {
+    double stn = s_t[l] * (double)L / st_sum;
+    double skn = (u_sum > 0.0) ? (s_k[l] - m) * (double)L / u_sum : 1.0;
+    x[l] = 0.5 * (stn + skn) * r;
+    double f = floor(x[l]);
+    if (!(f > 0.0)) f = 0.0; /* also maps NaN to 0 */
+    if (f > (double)Nv) f = (double)Nv;
+    budget[l] = (int32_t)f;
+  }
+}
+
+typedef struct {
+  double score;
+  int32_t index;
+} scored;
+
+static int by_score_desc(const void *a, const void *b) {
+  const scored *x = (const scored *)a, *y = (const scored *)b;
+  if (x->score > y->score) return -1;
+  if (x->score < y->score) return 1;
+  return (x->index > y->index) - (x->index < y->index);
+}
+
+static int by_int_asc(const void *a, const void *b) {
+  int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+  return (x > y) - (x < y);
+}
+
+/*
+ * Step 5, top-k selection of the visual tokens of one layer: order by
+ * (I_v descending, index ascending), keep the first k, write them ascending.
+ */
+void orc_topk(const double *iv, int n, int k, int32_t *kept) {
+  scored *s = (scored *)malloc(sizeof(scored) * (size_t)(n > 0 ? n : 1));
+  for (int i = 0; i < n; ++i) {
+    s[i].score = iv[i];
+    s[i].index = i;
+  }
+  qsort(s, (size_t)n, sizeof(scored), by_score_desc);
+  for (int i = 0; i < k; ++i) kept[i] = s[i].index;
+  qsort(kept, (size_t)k, sizeof(int32_t), by_int_asc);
+  free(s);
+}
+
+/*
+ * Step 6, compaction of one sample of one layer: for each KV head, the kept
+ * visual rows (in the order given) followed by all text rows, copied byte for
+ * byte into out_seg, laid out [H_kv][k + N_t][D].
+ */
+void orc_gather(const orc_desc *w, const void *src_l, int b, const int32_t *kept, int k,
+                void *out_seg) {
+  const size_t esz = (w->dtype == 0) ? 4 : 2;
+  const size_t row = (size_t)w->D * esz;
+  const char *src = (const char *)src_l;
+  char *dst = (char *)out_seg;
+  for (int g = 0; g < w->Hkv; ++g) {
+    for (int i = 0; i < k; ++i) {
+      memcpy(dst, src + k_index(w, b, g, kept[i]) * esz, row);
+      dst += row;
+    }
+    for (int j = 0; j < w->Nt; ++j) {
+      memcpy(dst, src + k_index(w, b, g, w->Nv + j) * esz, row);
+      dst += row;
+    }
+  }
+}
+
+/*
+ * The whole pass. Arrays indexed [l][b] are row-major with B columns.
+ *   elite [L][B][N_t] (first n_elite valid), pbar [L][B][N_t],
+ *   iv [L][B][N_v], s_t, s_k, x [L][B], budget [L][B],
+ *   out_off [L][B+1] element offsets of each sample's segment in the layer,
+ *   kept [L][B][N_v] (first budget valid).
+ * k_out / v_out: per-layer output buffers, or NULL to skip compaction.
+ * Returns 0, or -1 on an invalid descriptor.
+ */
+int orc_run(const orc_desc *w, const void *const *q, const void *const *k,
+            const void *const *v, int32_t *elite, int32_t *n_elite, double *pbar,
+            double *iv, double *s_t, double *s_k, double *x, int32_t *budget,
+            int64_t *out_off, int32_t *kept, void *const *k_out, void *const *v_out) {
+  if (w->L < 1 || w->B < 1 || w->Hq < 1 || w->Hkv < 1 || w->Hq % w->Hkv != 0 || w->D < 1 ||
+      w->Nv < 3 || w->Nt < 1 || (w->dtype != 0 && w->dtype != 1))
+    return -1;
+  const int L = w->L, B = w->B;
+  for (int l = 0; l < L; ++l) {
+    for (int b = 0; b < B; ++b) {
+      size_t lb = (size_t)l * B + b;
+      int32_t *el = elite + lb * w->Nt;
+      int ntk = orc_elite_select(w, q[l], k[l], b, pbar + lb * w->Nt, el);
+      n_elite[lb] = ntk;
+      orc_cross_score(w, q[l], k[l], b, el, ntk, iv + lb * w->Nv);
+      orc_layer_stats(iv + lb * w->Nv, w->Nv, &s_t[lb], &s_k[lb]);
+    }
+  }
+  double *st = (double *)malloc(sizeof(double) * (size_t)L);
+  double *sk = (double *)malloc(sizeof(double) * (size_t)L);
+  double *xx = (double *)malloc(sizeof(double) * (size_t)L);
+  int32_t *bb = (int32_t *)malloc(sizeof(int32_t) * (size_t)L);
+  for (int b = 0; b < B; ++b) {
+    for (int l = 0; l < L; ++l) {
+      st[l] = s_t[(size_t)l * B + b];
+      sk[l] = s_k[(size_t)l * B + b];
+    }
+    orc_budget(st, sk, L, w->ratio, w->Nv, xx, bb);
+    for (int l = 0; l < L; ++l) {
+      x[(size_t)l * B + b] = xx[l];
+      budget[(size_t)l * B + b] = bb[l];
+    }
+  }
+  free(st);
+  free(sk);
+  free(xx);
+  free(bb);
+  for (int l = 0; l < L; ++l) {
+    int64_t off = 0;
+    for (int b = 0; b < B; ++b) {
+      size_t lb = (size_t)l * B + b;
+      out_off[(size_t)l * (B + 1) + b] = off;
+      orc_topk(iv + lb * w->Nv, w->Nv, budget[lb], kept + lb * w->Nv);
+      const size_t esz = (w->dtype == 0) ? 4 : 2;
+      if (k_out) orc_gather(w, k[l], b, kept + lb * w->Nv, budget[lb], (char *)k_out[l] + (size_t)off * esz);
+      if (v_out) orc_gather(w, v[l], b, kept + lb * w->Nv, budget[lb], (char *)v_out[l] + (size_t)off * esz);
+      off += (int64_t)w->Hkv * (budget[lb] + w->Nt) * w->D;
+    }
+    out_off[(size_t)l * (B + 1) + B] = off;
+  }
+  return 0;
+}

@@ -1,0 +1,367 @@
+"""Pins of the CPU oracle against facts fixed by the AirCache page and by
+mathematics (no GPU). Each check would fail on a plausible slip in the oracle:
+a dropped term, a wrong sign or index, a transposed operand, a wrong
+normaliser or a wrong tie rule.
+
+The page prints no worked numeric example of the method, so the pins are
+invariants, closed forms, library routines on special cases and brute force on
+tiny inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+
+import oracle
+import workloads as wl
+
+
+def tiny(seed=0, **kw):
+    w = wl.custom(**kw)
+    return w, wl.make_inputs(w, seed)
+
+
+# ---------------------------------------------------------------- step 1 ----
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("shape", [dict(Hq=1, Hkv=1, Nt=5), dict(Hq=4, Hkv=2, Nt=9),
+                                   dict(Hq=6, Hkv=1, Nt=3, dtype="bf16"),
+                                   dict(Hq=7, Hkv=7, Nt=1)])
+def test_elite_rows_sum_to_one_and_argmax_is_elite(seed, shape):
+    w, inp = tiny(seed, Nv=11, D=16, **shape)
+    el, pbar = oracle.elite_select(w, inp.q[0], inp.k[0], 0)
+    # every per-head softmax row sums to 1, so does their mean
+    assert abs(pbar.sum() - 1.0) < 1e-12
+    assert (pbar > 0).all()
+    assert int(np.argmax(pbar)) in set(el.tolist())
+    assert list(el) == sorted(el) and len(set(el.tolist())) == len(el)
+    # the set is exactly the threshold set
+    thr = 0.9 * pbar.max()
+    assert set(el.tolist()) == set(np.nonzero(pbar >= thr)[0].tolist())
+
+
+def test_elite_alpha_extremes():
+    w, inp = tiny(3, Nv=8, Nt=12, Hq=3, Hkv=3, D=32)
+    el0, _ = oracle.elite_select(w, inp.q[0], inp.k[0], 0, alpha=0.0)
+    assert list(el0) == list(range(12))           # alpha = 0: every text token
+    el1, pbar = oracle.elite_select(w, inp.q[0], inp.k[0], 0, alpha=1.0)
+    assert list(el1) == [int(np.argmax(pbar))]     # alpha = 1: the maximum only
+
+
+def test_elite_uniform_when_queries_are_zero():
+    w = wl.custom(Nv=10, Nt=7, Hq=4, Hkv=2, D=16)
+    inp = wl.make_inputs(w, 5, zero_q=True)
+    el, pbar = oracle.elite_select(w, inp.q[0], inp.k[0], 0)
+    assert np.allclose(pbar, 1.0 / 7, rtol=0, atol=1e-15)
+    assert list(el) == list(range(7))
+
+
+def test_elite_matches_library_softmax_single_head():
+    # one head: pbar is exactly the softmax row of the last text query
+    w, inp = tiny(9, Nv=5, Nt=13, Hq=1, Hkv=1, D=24)
+    q = inp.q[0, 0, 0].astype(np.float64)
+    k = inp.k[0, 0, 0].astype(np.float64)
+    z = k[w.Nv:] @ q[-1] / math.sqrt(w.D)
+    ref = scipy.special.softmax(z)
+    _, pbar = oracle.elite_select(w, inp.q[0], inp.k[0], 0)
+    assert np.allclose(pbar, ref, rtol=1e-13, atol=0)
+
+
+def test_elite_gqa_head_mapping():
+    # 4 query heads on 2 KV heads: heads 0,1 read KV head 0 and heads 2,3 read
+    # KV head 1. Checked against per-head library softmax with that mapping.
+    w, inp = tiny(4, Nv=6, Nt=10, Hq=4, Hkv=2, D=16)
+    rows = []
+    for h in range(4):
+        q = inp.q[0, 0, h, -1].astype(np.float64)
+        k = inp.k[0, 0, h // 2, w.Nv:].astype(np.float64)
+        rows.append(scipy.special.softmax(k @ q / 4.0))
+    _, pbar = oracle.elite_select(w, inp.q[0], inp.k[0], 0)
+    assert np.allclose(pbar, np.mean(rows, axis=0), rtol=1e-13, atol=0)
+    # a transposed mapping (h % Hkv) gives a different answer on this input
+    rows_bad = [scipy.special.softmax(inp.k[0, 0, h % 2, w.Nv:].astype(np.float64)
+                                      @ inp.q[0, 0, h, -1].astype(np.float64) / 4.0)
+                for h in range(4)]
+    assert not np.allclose(pbar, np.mean(rows_bad, axis=0), rtol=1e-6, atol=0)
+
+
+def test_elite_uses_last_text_query_only():
+    w, inp = tiny(8, Nv=6, Nt=6, Hq=2, Hkv=1, D=16)
+    _, p0 = oracle.elite_select(w, inp.q[0], inp.k[0], 0)
+    q2 = inp.q.copy()
+    q2[0, 0, :, :-1] = 0.0   # change every text query but the last
+    _, p1 = oracle.elite_select(w, q2[0], inp.k[0], 0)
+    assert np.array_equal(p0, p1)
+    k2 = inp.k.copy()
+    k2[0, 0, :, :w.Nv] += 1.0   # visual keys do not enter step 1
+    _, p2 = oracle.elite_select(w, inp.q[0], k2[0], 0)
+    assert np.array_equal(p0, p2)
+
+
+# ---------------------------------------------------------------- step 2 ----
+
+def library_iv(w, inp, b, elite):
+    """I_v from numpy matrix products and scipy's softmax."""
+    G = w.Hq // w.Hkv
+    acc = np.zeros(w.Nv)
+    for h in range(w.Hq):
+        K = inp.as_f32("k")[0, b, h // G].astype(np.float64)
+        cols = np.concatenate([K[:w.Nv], K[w.Nv + np.asarray(elite, int)]])
+        Qe = inp.as_f32("q")[0, b, h][np.asarray(elite, int)].astype(np.float64)
+        P = scipy.special.softmax(Qe @ cols.T / math.sqrt(w.D), axis=1)
+        acc += P[:, :w.Nv].sum(0)
+    return acc / (w.Hq * len(elite))
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("shape", [dict(Hq=1, Hkv=1), dict(Hq=6, Hkv=2), dict(Hq=3, Hkv=3, dtype="bf16")])
+def test_cross_score_matches_library_softmax(seed, shape):
+    w, inp = tiny(seed, Nv=17, Nt=9, D=32, B=2, **shape)
+    for b in range(2):
+        el, _ = oracle.elite_select(w, inp.q[0], inp.k[0], b, alpha=0.5)
+        iv = oracle.cross_score(w, inp.q[0], inp.k[0], b, el)
+        assert np.allclose(iv, library_iv(w, inp, b, el), rtol=1e-12, atol=0)
+        # s_t < 1 because the elite text keys also take probability mass
+        assert 0.0 < iv.sum() < 1.0
+
+
+def test_cross_score_single_row_closed_form():
+    # D = 1, one head, query 1: logits are the key values themselves.
+    # Keys ln(c_i) give probabilities c_i / sum(c) exactly (up to rounding).
+    c_vis = np.array([1, 2, 3, 4, 6], np.float64)
+    c_txt = np.array([5, 7], np.float64)     # text key 1 is the elite one
+    w = wl.custom(Nv=5, Nt=2, Hq=1, Hkv=1, D=1)
+    q = np.ones((1, 1, 1, 2, 1), np.float32)
+    k = np.log(np.concatenate([c_vis, c_txt])).astype(np.float32).reshape(1, 1, 1, 7, 1)
+    # make the softmax exact in float32 inputs by using what the keys round to
+    cv = np.exp(k.ravel()[:5].astype(np.float64))
+    ct = np.exp(k.ravel()[6].astype(np.float64))
+    iv = oracle.cross_score(w, q[0], k[0], 0, [1])
+    assert np.allclose(iv, cv / (cv.sum() + ct), rtol=1e-14, atol=0)
+    assert np.allclose(iv, c_vis / 23.0, rtol=1e-6, atol=0)
+
+
+def test_cross_score_uniform_when_queries_are_zero():
+    w = wl.custom(Nv=12, Nt=5, Hq=4, Hkv=2, D=16)
+    inp = wl.make_inputs(w, 1, zero_q=True)
+    el, _ = oracle.elite_select(w, inp.q[0], inp.k[0], 0)
+    assert len(el) == 5
+    iv = oracle.cross_score(w, inp.q[0], inp.k[0], 0, el)
+    assert np.allclose(iv, 1.0 / (12 + 5), rtol=1e-14, atol=0)
+    s_t, s_k = oracle.layer_stats(iv)
+    assert abs(s_t - 12 / 17) < 1e-14 and s_k == 0.0
+
+
+def test_cross_score_only_elite_text_columns_in_denominator():
+    # adding a huge non-elite text key must not change I_v
+    w, inp = tiny(2, Nv=9, Nt=6, Hq=2, Hkv=1, D=8)
+    el = np.array([0, 3], np.int32)
+    iv0 = oracle.cross_score(w, inp.q[0], inp.k[0], 0, el)
+    k2 = inp.k.copy()
+    k2[0, 0, 0, w.Nv + 5] *= 50.0
+    iv1 = oracle.cross_score(w, inp.q[0], k2[0], 0, el)
+    assert np.array_equal(iv0, iv1)
+    # and the non-elite queries do not enter either
+    q2 = inp.q.copy()
+    q2[0, 0, :, [1, 2, 4, 5]] = 7.0
+    iv2 = oracle.cross_score(w, q2[0], inp.k[0], 0, el)
+    assert np.array_equal(iv0, iv2)
+
+
+# ---------------------------------------------------------------- step 3 ----
+
+@pytest.mark.parametrize("n", [3, 4, 64, 576, 2880])
+def test_skew_one_hot_is_sqrt_n(n):
+    x = np.zeros(n)
+    x[n // 3] = 1.0
+    s_t, s_k = oracle.layer_stats(x)
+    assert s_t == 1.0
+    assert abs(s_k - math.sqrt(n)) <= 1e-12 * math.sqrt(n)
+
+
+@pytest.mark.parametrize("n,m", [(10, 1), (10, 3), (50, 5), (64, 8), (7, 6)])
+def test_skew_two_point_closed_form(n, m):
+    # m ones and n-m zeros: fraction p = m/n,
+    # s_k = sqrt(n(n-1))/(n-2) * (1-2p)/sqrt(p(1-p))
+    x = np.zeros(n)
+    x[:m] = 1.0
+    p = m / n
+    ref = math.sqrt(n * (n - 1)) / (n - 2) * (1 - 2 * p) / math.sqrt(p * (1 - p))
+    _, s_k = oracle.layer_stats(x)
+    assert abs(s_k - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def test_skew_symmetric_affine_negation_and_scipy():
+    rng = np.random.default_rng(0)
+    sym = np.concatenate([rng.random(20), -rng.random(20)])
+    sym = np.concatenate([sym, -sym])
+    assert abs(oracle.layer_stats(sym)[1]) < 1e-12
+    for _ in range(20):
+        n = int(rng.integers(3, 300))
+        x = rng.exponential(size=n) ** 2
+        _, s = oracle.layer_stats(x)
+        assert abs(s - scipy.stats.skew(x, bias=False)) <= 1e-10 * max(1, abs(s))
+        _, s2 = oracle.layer_stats(3.5 * x + 2.0)
+        assert abs(s2 - s) <= 1e-10 * max(1, abs(s))
+        _, s3 = oracle.layer_stats(-x)
+        assert abs(s3 + s) <= 1e-10 * max(1, abs(s))
+        assert abs(oracle.layer_stats(x)[0] - x.sum()) <= 1e-12 * x.sum()
+
+
+def test_skew_constant_is_zero():
+    assert oracle.layer_stats(np.full(9, 0.25)) == (2.25, 0.0)
+
+
+# ---------------------------------------------------------------- step 4 ----
+
+# Hand-derived two-layer cases (r = ratio * N_v):
+#  a) s_t=[.25,.75] -> s't=[.5,1.5]; s_k=[1,3] -> s'k=[.5,1.5]; r=8 -> x=[4,12]
+#  b) s_t=[.5,.5] -> [1,1]; s_k=[-1,1] shift by -1 -> u=[0,2] -> [0,2];
+#     r=8 -> x=[.5*1*8, .5*3*8]=[4,12]
+#  c) s_k=[-2,-2] -> u=[0,0], sum 0 -> s'k=[1,1]; s_t=[.5,.5]; r=8 -> [8,8]
+#  d) N_v=10, ratio .9 -> r=9; s_t=[.25,.75] -> [.5,1.5]; s_k=[0,0] -> [1,1];
+#     x=[.5*1.5*9, .5*2.5*9]=[6.75,11.25] -> floor [6,11] -> clamp [6,10]
+#  e) s_k=[2,6] (no shift) -> [.5,1.5]; s_t=[.5,.5]; N_v=64, ratio .25 -> r=16;
+#     x=[.5*1.5*16, .5*2.5*16]=[12,20]
+BUDGET_CASES = [
+    ([0.25, 0.75], [1.0, 3.0], 0.125, 64, [4.0, 12.0], [4, 12]),
+    ([0.5, 0.5], [-1.0, 1.0], 0.125, 64, [4.0, 12.0], [4, 12]),
+    ([0.5, 0.5], [-2.0, -2.0], 0.125, 64, [8.0, 8.0], [8, 8]),
+    ([0.25, 0.75], [0.0, 0.0], 0.9, 10, [6.75, 11.25], [6, 10]),
+    ([0.5, 0.5], [2.0, 6.0], 0.25, 64, [12.0, 20.0], [12, 20]),
+]
+
+
+@pytest.mark.parametrize("case", BUDGET_CASES)
+def test_budget_hand_cases(case):
+    st, sk, ratio, nv, x_ref, r_ref = case
+    x, r = oracle.budget(st, sk, ratio, nv)
+    assert np.allclose(x, x_ref, rtol=0, atol=1e-12)
+    assert list(r) == r_ref
+
+
+@pytest.mark.parametrize("L", [1, 2, 4, 8])
+@pytest.mark.parametrize("ratio,nv", [(0.25, 64), (0.1, 576), (0.1, 2880)])
+def test_budget_identical_layers(L, ratio, nv):
+    # dyadic statistics keep every sum exact: each layer gets floor(r)
+    x, r = oracle.budget([0.75] * L, [1.5] * L, ratio, nv)
+    assert list(r) == [math.floor(ratio * nv)] * L
+    x, r = oracle.budget([0.75] * L, [-0.5] * L, ratio, nv)   # shifted to 0
+    assert list(r) == [math.floor(ratio * nv)] * L
+
+
+def test_budget_mean_is_r_and_single_layer():
+    rng = np.random.default_rng(1)
+    for _ in range(50):
+        L = int(rng.integers(1, 40))
+        st = rng.uniform(0.5, 1.0, L)
+        sk = rng.normal(1.0, 2.0, L)
+        ratio, nv = float(rng.uniform(0.01, 0.3)), int(rng.integers(3, 7000))
+        x, r = oracle.budget(st, sk, ratio, nv)
+        assert abs(x.sum() - L * ratio * nv) <= 1e-9 * L * ratio * nv
+        assert ((r >= 0) & (r <= nv)).all()
+        assert np.array_equal(r, np.clip(np.floor(x), 0, nv).astype(int))
+    x, r = oracle.budget([0.3], [-4.0], 0.1, 576)
+    assert abs(x[0] - 57.6) < 1e-12 and r[0] == 57
+
+
+# ---------------------------------------------------------------- step 5 ----
+
+def check_topk(scores, k, kept):
+    """The unique answer: k indices, ascending, every kept score >= every
+    dropped score, and among equal scores at the cut the lower indices win."""
+    kept = list(kept)
+    assert len(kept) == k and kept == sorted(kept) and len(set(kept)) == k
+    drop = [i for i in range(len(scores)) if i not in set(kept)]
+    if kept and drop:
+        kmin = min(scores[i] for i in kept)
+        dmax = max(scores[i] for i in drop)
+        assert kmin >= dmax
+        if kmin == dmax:
+            assert max(i for i in kept if scores[i] == kmin) < min(i for i in drop if scores[i] == dmax)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_topk_brute_force_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 40))
+    s = rng.integers(0, 4, n).astype(np.float64) * 0.125   # many ties
+    for k in range(0, n + 1):
+        kept = oracle.topk(s, k)
+        check_topk(s, k, kept)
+        ref = np.sort(np.lexsort((np.arange(n), -s))[:k])   # numpy's sort
+        assert np.array_equal(kept, ref)
+
+
+def test_topk_extremes():
+    s = np.array([0.3, 0.1, 0.2])
+    assert oracle.topk(s, 0).size == 0
+    assert list(oracle.topk(s, 3)) == [0, 1, 2]
+    assert list(oracle.topk(s, 1)) == [0]
+    assert list(oracle.topk(np.zeros(5), 2)) == [0, 1]
+
+
+# ---------------------------------------------------------------- step 6 ----
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gather_identity_when_everything_is_kept(dtype):
+    # L = 1 gives s't = s'k = 1, so ratio 1 keeps every visual token and the
+    # compacted cache is the input byte for byte
+    w = wl.custom(Nv=9, Nt=4, Hq=4, Hkv=2, D=16, B=3, dtype=dtype, ratio=1.0)
+    inp = wl.make_inputs(w, 7)
+    out = oracle.run(inp)
+    assert (out["budget"] == 9).all()
+    assert np.array_equal(out["k_out"][0], inp.k[0].ravel())
+    assert np.array_equal(out["v_out"][0], inp.v[0].ravel())
+
+
+def test_gather_layout_and_text_rows():
+    w = wl.custom(Nv=12, Nt=3, Hq=2, Hkv=2, D=8, B=2, L=2, ratio=0.3)
+    inp = wl.make_inputs(w, 11)
+    out = oracle.run(inp)
+    for l in range(2):
+        for b in range(2):
+            r = int(out["budget"][l, b])
+            o = int(out["out_off"][l, b])
+            seg = out["k_out"][l][o:o + 2 * (r + 3) * 8].reshape(2, r + 3, 8)
+            kept = out["kept"][l, b, :r]
+            for g in range(2):
+                assert np.array_equal(seg[g, :r], inp.k[l, b, g, kept])
+                assert np.array_equal(seg[g, r:], inp.k[l, b, g, 12:])
+        assert out["out_off"][l, 2] == sum(2 * (int(out["budget"][l, b]) + 3) * 8 for b in range(2))
+
+
+# ------------------------------------------------------------ end to end ----
+
+def test_run_threads_equals_single_call():
+    w = wl.custom(Nv=40, Nt=8, Hq=4, Hkv=2, D=32, B=2, L=3, dtype="bf16", ratio=0.2)
+    inp = wl.make_inputs(w, 3)
+    a = oracle.run(inp)
+    b = oracle.run(inp, threads=4)
+    for key in ["n_elite", "iv", "s_t", "s_k", "x", "budget", "out_off", "kept"]:
+        assert np.array_equal(a[key], b[key]), key
+    for l in range(3):
+        assert np.array_equal(a["k_out"][l], b["k_out"][l])
+        assert np.array_equal(a["v_out"][l], b["v_out"][l])
+
+
+def test_config1_end_to_end_properties():
+    inp = wl.make_inputs(1, 1)
+    o = oracle.run(inp)
+    w = inp.w
+    assert (o["n_elite"] >= 1).all()
+    assert np.all((o["s_t"] > 0) & (o["s_t"] < 1))
+    assert abs(o["x"].sum() - w.L * w.ratio * w.Nv) < 1e-9
+    assert (o["budget"] <= w.Nv).all()
+
+
+def test_config2_generator_reading_elite_is_all_text():
+    # the mean-query planting of the 7B-like workload aims at the mean of all
+    # text queries; under its N(0,1)/sqrt(D) base the elite window is all text
+    w = wl.CONFIGS[2]
+    small = wl.Workload(**{**w.__dict__, "L": 2, "cid": 0})
+    inp = wl.make_inputs(small, 2)
+    o = oracle.run(inp, compact=False, threads=4)
+    assert (o["n_elite"] == w.Nt).all()
