@@ -1,0 +1,163 @@
+/*
+ * aircache.h: C ABI of the MI355X (gfx950) AirCache visual KV-cache compression pass.
+ *
+ * The pass follows the paper-notes page "AirCache: Activating Inter-Modal
+ * Relevancy KV Cache Compression for Efficient Large Vision-Language Model
+ * Inference" (ICCV 2025):
+ *   - "Elite Observation Window" (key design 1): the text-only attention row of
+ *     the last text token picks the elite text tokens (threshold alpha times the
+ *     row maximum); the elite queries' softmax over the visual keys plus the
+ *     elite text keys, mean-pooled over the elite rows, scores every visual
+ *     token (I_v);
+ *   - "Layer-wise KV Cache Budget Allocation" (key design 2): strength
+ *     s_t = sum I_v and skewness s_k of I_v, normalised across layers, give each
+ *     layer's budget r_hat = (s'_t + s'_k) / 2 * r;
+ *   - the training-free procedure: after prefill has stored every layer's cache,
+ *     budgets are computed for all layers at once and the cache is compressed
+ *     before decoding.
+ *
+ * Two calls carry the pass: aircache_plan (scores, statistics, budgets, top-k
+ * selection) and aircache_compress (compaction of the kept visual rows and all
+ * text rows into a dense per-layer cache). Both are asynchronous on the given
+ * HIP stream, never synchronise the host, allocate nothing, and are
+ * deterministic (bit-identical results for identical inputs).
+ *
+ * Where the page leaves a step open, the library takes these readings:
+ *   - per-head attention with D = head_dim; query head h reads KV head
+ *     h / (n_q_heads / n_kv_heads); the elite set is chosen once per
+ *     (layer, sample) from the mean over query heads of the per-head softmax
+ *     rows; I_v averages over all query heads and all elite rows;
+ *   - the elite rows' softmax runs over the N_v visual keys plus the N_tk elite
+ *     text keys only (no causal mask), so s_t < 1;
+ *   - s_k uses the sample standard deviation (n - 1); sigma = 0 gives s_k = 0;
+ *   - cross-layer normalisation is per sample: s'_t = s_t * L / sum_l s_t;
+ *     s_k is shifted by min(0, min_l s_k) and scaled the same way (all layers 1
+ *     when the shifted sum is 0); x = (s'_t + s'_k) / 2 * ratio * N_v in double
+ *     precision, budget = clamp(floor(x), 0, N_v);
+ *   - top-k keeps the budget largest I_v, equal scores to the lower index, and
+ *     lists the kept indices in ascending order;
+ *   - compacted layout per layer: samples one after another; inside a sample,
+ *     [n_kv_heads][budget + N_t][head_dim]: the kept visual rows (ascending),
+ *     then all N_t text rows in their original order.
+ *
+ * Input layout (per layer l, all device memory, contiguous, read-only):
+ *   q_txt[l] : [batch][n_q_heads][n_txt][head_dim]            text queries
+ *   k[l], v[l]: [batch][n_kv_heads][n_vis + n_txt][head_dim]   visual rows
+ *              first, then text rows (the regrouped sequence)
+ * Element type: float32 or bfloat16 (aircache_dtype). Pointers must be 16-byte
+ * aligned.
+ *
+ * Errors: every function returns an aircache_status. Arguments are validated
+ * on the host before any launch; on AIRCACHE_EINVAL nothing is enqueued.
+ * AIRCACHE_EHIP reports a failed HIP launch. Faults inside the kernels surface
+ * through the next HIP call or stream synchronisation. Conditions found on the
+ * device are OR-ed into plan->status (AIRCACHE_DEV_*), which the caller reads
+ * after synchronising. aircache_last_error() returns a thread-local message
+ * describing the last failure of the calling thread.
+ */
+#ifndef AIRCACHE_H
+#define AIRCACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AIRCACHE_ABI_VERSION 1
+#define AIRCACHE_MAX_LAYERS 128
+
+typedef enum {
+  AIRCACHE_OK = 0,
+  AIRCACHE_EINVAL = 1,      /* invalid argument; nothing was enqueued */
+  AIRCACHE_EWORKSPACE = 2,  /* workspace missing or smaller than aircache_workspace_size */
+  AIRCACHE_EHIP = 3         /* a HIP runtime call failed */
+} aircache_status;
+
+typedef enum { AIRCACHE_F32 = 0, AIRCACHE_BF16 = 1 } aircache_dtype;
+
+/* Device-side condition bits OR-ed into plan->status. */
+#define AIRCACHE_DEV_ELITE_OVERFLOW 1 /* some (layer, sample) had more elite tokens than
+                                         desc.max_elite; its results are not valid */
+
+typedef struct {
+  int32_t n_layers;   /* L, 1 .. AIRCACHE_MAX_LAYERS */
+  int32_t batch;      /* B >= 1 */
+  int32_t n_q_heads;  /* H_q >= 1, a multiple of n_kv_heads */
+  int32_t n_kv_heads; /* H_kv >= 1 */
+  int32_t head_dim;   /* D: 64 or 128 */
+  int32_t n_vis;      /* N_v >= 3 (the skewness needs three values) */
+  int32_t n_txt;      /* N_t >= 1 */
+  int32_t dtype;      /* aircache_dtype */
+  double alpha;       /* elite threshold in [0, 1]; the page uses 0.9 */
+  double ratio;       /* r / N_v, the retention ratio in [0, 1] */
+  int32_t max_elite;  /* workspace cap on elite tokens per (layer, sample); 0 means n_txt */
+  int32_t reserved;   /* must be 0 */
+} aircache_desc;
+
+/* Outputs of aircache_plan; all device pointers, allocated by the caller with
+ * the sizes given, written by the library (row-major, [l][b] means index
+ * l * batch + b). */
+typedef struct {
+  int32_t *elite_idx; /* [L][B][N_t] elite text indices, ascending; first n_elite valid */
+  int32_t *n_elite;   /* [L][B] N_tk */
+  float *iv;          /* [L][B][N_v] visual importance I_v */
+  double *s_t;        /* [L][B] strength, sum of I_v */
+  double *s_k;        /* [L][B] skewness of I_v */
+  double *budget_x;   /* [L][B] budget before the floor (may be NULL) */
+  int32_t *budget;    /* [L][B] r_hat, in [0, N_v] */
+  int64_t *out_off;   /* [L][B+1] element offset of each sample's segment in the layer's
+                         compacted buffer; out_off[l][B] is the layer's total element count */
+  int32_t *kept_idx;  /* [L][B][N_v] kept visual indices, ascending; first budget valid */
+  int32_t *status;    /* [1] AIRCACHE_DEV_* bits, reset by every aircache_plan call */
+} aircache_plan_buf;
+
+/* Library version (AIRCACHE_ABI_VERSION). */
+int aircache_abi_version(void);
+
+/* Bytes of device workspace aircache_plan needs for this descriptor, or 0 if
+ * the descriptor is invalid (aircache_last_error() says why). The workspace is
+ * caller-owned scratch: its content need not be preserved between calls and
+ * one workspace must not be used by two calls that can run concurrently. */
+size_t aircache_workspace_size(const aircache_desc *desc);
+
+/* Largest compacted element count per layer (every visual row kept): the
+ * worst-case capacity of each k_out[l] / v_out[l] buffer in elements. */
+int64_t aircache_max_compacted_elems(const aircache_desc *desc);
+
+/* Scores, statistics, budgets and top-k selection for all layers.
+ *   q_txt, k : host arrays of n_layers device pointers (layout above)
+ *   plan     : output buffers (see aircache_plan_buf)
+ *   workspace: device scratch of ws_bytes >= aircache_workspace_size(desc)
+ *   stream   : a hipStream_t (NULL: the default stream)
+ * The elite selection, scoring and statistics read K and the text queries
+ * once; the budget of every layer waits for all layers of its sample, as the
+ * procedure on the page prescribes. */
+int aircache_plan(const aircache_desc *desc, const void *const *q_txt, const void *const *k,
+                  const aircache_plan_buf *plan, void *workspace, size_t ws_bytes, void *stream);
+
+/* Compaction (the page's compress step): for every (layer, sample, KV head)
+ * copy the kept visual rows (plan->kept_idx, ascending) and then all text rows
+ * of K and V into k_out[l] / v_out[l] at plan->out_off[l][b]. Bit-exact copies.
+ *   k, v        : host arrays of n_layers device pointers (inputs, read-only)
+ *   k_out, v_out: host arrays of n_layers device pointers to buffers of at
+ *                 least out_off[l][B] elements (aircache_max_compacted_elems is
+ *                 always enough); they must not overlap the inputs
+ *   plan        : the buffers filled by aircache_plan on the same stream (only
+ *                 budget, out_off and kept_idx are read) */
+int aircache_compress(const aircache_desc *desc, const aircache_plan_buf *plan,
+                      const void *const *k, const void *const *v, void *const *k_out,
+                      void *const *v_out, void *stream);
+
+/* Text of an aircache_status value. */
+const char *aircache_strerror(int status);
+
+/* Message describing the calling thread's last failure ("" if none). */
+const char *aircache_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AIRCACHE_H */

@@ -1,0 +1,99 @@
+"""ctypes binding of libaircache.so (include/aircache.h).
+
+Argument marshalling only: every step of the pass runs in the HIP library.
+PyTorch supplies device memory and the current stream. There is no fallback:
+if the library is missing, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_build", "libaircache.so")
+
+AIRCACHE_OK, AIRCACHE_EINVAL, AIRCACHE_EWORKSPACE, AIRCACHE_EHIP = 0, 1, 2, 3
+AIRCACHE_F32, AIRCACHE_BF16 = 0, 1
+AIRCACHE_DEV_ELITE_OVERFLOW = 1
+MAX_LAYERS = 128
+
+EXPORTS = ["aircache_abi_version", "aircache_workspace_size", "aircache_max_compacted_elems",
+           "aircache_plan", "aircache_compress", "aircache_strerror", "aircache_last_error"]
+
+
+class Desc(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("batch", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("n_vis", C.c_int32),
+                ("n_txt", C.c_int32), ("dtype", C.c_int32), ("alpha", C.c_double),
+                ("ratio", C.c_double), ("max_elite", C.c_int32), ("reserved", C.c_int32)]
+
+
+class PlanBuf(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("elite_idx", "n_elite", "iv", "s_t", "s_k", "budget_x",
+                                          "budget", "out_off", "kept_idx", "status")]
+
+
+class AirCacheError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"aircache status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> C.CDLL:
+    """Load the in-tree HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with lvlm_kv_cache_amd.build.build()")
+        lib = C.CDLL(LIB_PATH)
+        P = C.c_void_p
+        lib.aircache_abi_version.restype = C.c_int
+        lib.aircache_abi_version.argtypes = []
+        lib.aircache_workspace_size.restype = C.c_size_t
+        lib.aircache_workspace_size.argtypes = [C.POINTER(Desc)]
+        lib.aircache_max_compacted_elems.restype = C.c_int64
+        lib.aircache_max_compacted_elems.argtypes = [C.POINTER(Desc)]
+        lib.aircache_plan.restype = C.c_int
+        lib.aircache_plan.argtypes = [C.POINTER(Desc), P, P, C.POINTER(PlanBuf), P, C.c_size_t, P]
+        lib.aircache_compress.restype = C.c_int
+        lib.aircache_compress.argtypes = [C.POINTER(Desc), C.POINTER(PlanBuf), P, P, P, P, P]
+        lib.aircache_strerror.restype = C.c_char_p
+        lib.aircache_strerror.argtypes = [C.c_int]
+        lib.aircache_last_error.restype = C.c_char_p
+        lib.aircache_last_error.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != AIRCACHE_OK:
+        lib = load()
+        raise AirCacheError(status, f"{lib.aircache_strerror(status).decode()}: "
+                                    f"{lib.aircache_last_error().decode()}")
+
+
+def ptr_array(ptrs) -> C.Array:
+    return (C.c_void_p * len(ptrs))(*[C.c_void_p(int(p)) for p in ptrs])
+
+
+def workspace_size(desc: Desc) -> int:
+    return int(load().aircache_workspace_size(C.byref(desc)))
+
+
+def max_compacted_elems(desc: Desc) -> int:
+    return int(load().aircache_max_compacted_elems(C.byref(desc)))
+
+
+def plan(desc: Desc, q_ptrs, k_ptrs, buf: PlanBuf, ws_ptr: int, ws_bytes: int, stream: int) -> int:
+    q = ptr_array(q_ptrs) if q_ptrs is not None else None
+    k = ptr_array(k_ptrs) if k_ptrs is not None else None
+    return load().aircache_plan(C.byref(desc), q, k, C.byref(buf), C.c_void_p(ws_ptr), ws_bytes,
+                                C.c_void_p(stream))
+
+
+def compress(desc: Desc, buf: PlanBuf, k_ptrs, v_ptrs, ko_ptrs, vo_ptrs, stream: int) -> int:
+    arrs = [ptr_array(p) if p is not None else None for p in (k_ptrs, v_ptrs, ko_ptrs, vo_ptrs)]
+    return load().aircache_compress(C.byref(desc), C.byref(buf), *arrs, C.c_void_p(stream))

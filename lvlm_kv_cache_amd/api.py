@@ -1,0 +1,134 @@
+"""PyTorch-facing wrapper of the AirCache C ABI (argument marshalling only).
+
+PyTorch provides device memory and the stream; every step of the pass runs in
+the HIP kernels of libaircache.so. Shapes, dtypes, devices and contiguity are
+checked here, because the C ABI only sees raw pointers.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.AIRCACHE_F32, torch.bfloat16: _lib.AIRCACHE_BF16}
+
+
+def make_desc(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt, dtype,
+              alpha=0.9, ratio=0.1, max_elite=0) -> _lib.Desc:
+    if isinstance(dtype, torch.dtype):
+        dtype = _DTYPES[dtype]
+    elif isinstance(dtype, str):
+        dtype = {"f32": _lib.AIRCACHE_F32, "bf16": _lib.AIRCACHE_BF16}[dtype]
+    return _lib.Desc(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt, dtype,
+                     float(alpha), float(ratio), int(max_elite), 0)
+
+
+@dataclasses.dataclass
+class PlanOutputs:
+    elite_idx: torch.Tensor  # int32 [L, B, N_t]
+    n_elite: torch.Tensor    # int32 [L, B]
+    iv: torch.Tensor         # float32 [L, B, N_v]
+    s_t: torch.Tensor        # float64 [L, B]
+    s_k: torch.Tensor        # float64 [L, B]
+    budget_x: torch.Tensor   # float64 [L, B]
+    budget: torch.Tensor     # int32 [L, B]
+    out_off: torch.Tensor    # int64 [L, B + 1]
+    kept_idx: torch.Tensor   # int32 [L, B, N_v]
+    status: torch.Tensor     # int32 [1]
+
+    @classmethod
+    def empty(cls, L, B, Nv, Nt, device) -> "PlanOutputs":
+        i32 = dict(dtype=torch.int32, device=device)
+        f64 = dict(dtype=torch.float64, device=device)
+        return cls(elite_idx=torch.empty(L, B, Nt, **i32), n_elite=torch.empty(L, B, **i32),
+                   iv=torch.empty(L, B, Nv, dtype=torch.float32, device=device),
+                   s_t=torch.empty(L, B, **f64), s_k=torch.empty(L, B, **f64),
+                   budget_x=torch.empty(L, B, **f64), budget=torch.empty(L, B, **i32),
+                   out_off=torch.empty(L, B + 1, dtype=torch.int64, device=device),
+                   kept_idx=torch.empty(L, B, Nv, **i32), status=torch.zeros(1, **i32))
+
+    def buf(self) -> _lib.PlanBuf:
+        return _lib.PlanBuf(*[getattr(self, f.name).data_ptr() for f in dataclasses.fields(self)])
+
+
+class AirCache:
+    """One compression pass configuration with its workspace.
+
+    plan(q_txt, k) scores, budgets and selects; compress(...) writes the
+    compacted per-layer K/V. Both run on the current stream of the device and
+    return without synchronising.
+    """
+
+    def __init__(self, n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt,
+                 dtype=torch.bfloat16, alpha=0.9, ratio=0.1, max_elite=0, device="cuda"):
+        self.shape = dict(L=n_layers, B=batch, Hq=n_q_heads, Hkv=n_kv_heads, D=head_dim,
+                          Nv=n_vis, Nt=n_txt)
+        self.dtype = dtype
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        self.desc = make_desc(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt,
+                              dtype, alpha, ratio, max_elite)
+        ws = _lib.workspace_size(self.desc)
+        if ws == 0:
+            _lib.check(_lib.AIRCACHE_EINVAL)
+        self.ws_bytes = ws
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
+
+    # -- validation ------------------------------------------------------
+    def _check_layers(self, ts, shape, name):
+        s = self.shape
+        if len(ts) != s["L"]:
+            raise ValueError(f"{name}: {len(ts)} layers given, {s['L']} expected")
+        for l, t in enumerate(ts):
+            if t.device != self.device or t.dtype != self.dtype:
+                raise ValueError(f"{name}[{l}]: {t.dtype} on {t.device}, expected {self.dtype} on {self.device}")
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name}[{l}]: shape {tuple(t.shape)}, expected {shape}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name}[{l}] is not contiguous")
+
+    def _stream(self, stream):
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+    # -- calls -------------------------------------------------------------
+    def alloc_plan(self) -> PlanOutputs:
+        s = self.shape
+        return PlanOutputs.empty(s["L"], s["B"], s["Nv"], s["Nt"], self.device)
+
+    def plan(self, q_txt, k, out: PlanOutputs | None = None, stream=None) -> PlanOutputs:
+        s = self.shape
+        self._check_layers(q_txt, (s["B"], s["Hq"], s["Nt"], s["D"]), "q_txt")
+        self._check_layers(k, (s["B"], s["Hkv"], s["Nv"] + s["Nt"], s["D"]), "k")
+        out = out or self.alloc_plan()
+        _lib.check(_lib.plan(self.desc, [t.data_ptr() for t in q_txt], [t.data_ptr() for t in k],
+                             out.buf(), self.workspace.data_ptr(), self.ws_bytes, self._stream(stream)))
+        return out
+
+    def alloc_compacted(self):
+        """Worst-case (every visual row kept) per-layer output buffers for K and V."""
+        n = _lib.max_compacted_elems(self.desc)
+        L = self.shape["L"]
+        mk = lambda: [torch.empty(n, dtype=self.dtype, device=self.device) for _ in range(L)]
+        return mk(), mk()
+
+    def compress(self, plan: PlanOutputs, k, v, k_out, v_out, stream=None) -> None:
+        s = self.shape
+        shp = (s["B"], s["Hkv"], s["Nv"] + s["Nt"], s["D"])
+        self._check_layers(k, shp, "k")
+        self._check_layers(v, shp, "v")
+        cap = _lib.max_compacted_elems(self.desc)
+        for name, outs in (("k_out", k_out), ("v_out", v_out)):
+            if len(outs) != s["L"]:
+                raise ValueError(f"{name}: {len(outs)} layers given")
+            for l, t in enumerate(outs):
+                if t.device != self.device or t.dtype != self.dtype or not t.is_contiguous() or t.numel() < cap:
+                    raise ValueError(f"{name}[{l}] must be a contiguous {self.dtype} tensor on "
+                                     f"{self.device} with at least {cap} elements")
+        _lib.check(_lib.compress(self.desc, plan.buf(), [t.data_ptr() for t in k],
+                                 [t.data_ptr() for t in v], [t.data_ptr() for t in k_out],
+                                 [t.data_ptr() for t in v_out], self._stream(stream)))

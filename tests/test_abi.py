@@ -1,0 +1,103 @@
+"""The C ABI library: it loads, exports every function include/aircache.h
+declares, and rejects invalid arguments on the host before touching the GPU
+(no compute call is made here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from lvlm_kv_cache_amd import _lib, make_desc
+from lvlm_kv_cache_amd.build import build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        build(force=False)
+    return _lib.load()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "aircache.h")).read()
+    return sorted(set(re.findall(r"^[a-z_0-9 ]+[ *](aircache_[a-z_]+)\(", text, re.M)))
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert len(names) >= 7, names
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.aircache_abi_version() == 1
+
+
+def test_struct_layouts():
+    assert C.sizeof(_lib.Desc) == 8 * 4 + 2 * 8 + 2 * 4
+    assert C.sizeof(_lib.PlanBuf) == 10 * 8
+
+
+def desc(**kw):
+    base = dict(n_layers=28, batch=1, n_q_heads=28, n_kv_heads=4, head_dim=128, n_vis=2880,
+                n_txt=128, dtype="bf16", alpha=0.9, ratio=0.1, max_elite=0)
+    base.update(kw)
+    return make_desc(*[base[k] for k in ("n_layers", "batch", "n_q_heads", "n_kv_heads", "head_dim",
+                                         "n_vis", "n_txt", "dtype", "alpha", "ratio", "max_elite")])
+
+
+def test_workspace_size(lib):
+    assert _lib.workspace_size(desc()) > 0
+    assert _lib.workspace_size(desc(max_elite=8)) < _lib.workspace_size(desc())
+    assert _lib.max_compacted_elems(desc()) == 1 * 4 * 3008 * 128
+
+
+@pytest.mark.parametrize("bad", [dict(n_layers=0), dict(n_layers=129), dict(batch=0), dict(n_kv_heads=5),
+                                 dict(head_dim=96), dict(n_vis=2), dict(n_vis=9000), dict(n_txt=0),
+                                 dict(dtype="x"), dict(alpha=1.5), dict(alpha=float("nan")),
+                                 dict(ratio=-0.1), dict(max_elite=129), dict(n_txt=4000)])
+def test_invalid_descriptor(lib, bad):
+    if bad.get("dtype") == "x":
+        d = desc()
+        d.dtype = 7
+    else:
+        d = desc(**bad)
+    assert _lib.workspace_size(d) == 0
+    assert lib.aircache_last_error().decode()
+    rc = _lib.plan(d, [1] * max(d.n_layers, 1), [1] * max(d.n_layers, 1), _lib.PlanBuf(), 16, 1 << 40, 0)
+    assert rc == _lib.AIRCACHE_EINVAL
+
+
+def fake_buf():
+    return _lib.PlanBuf(*([4096] * 10))
+
+
+def test_plan_argument_errors(lib):
+    d = desc(n_layers=2)
+    ws = _lib.workspace_size(d)
+    ok = [4096, 8192]
+    assert _lib.plan(d, ok, ok, _lib.PlanBuf(), 4096, ws, 0) == _lib.AIRCACHE_EINVAL       # NULL outputs
+    assert _lib.plan(d, ok, ok, fake_buf(), 0, ws, 0) == _lib.AIRCACHE_EWORKSPACE         # no workspace
+    assert _lib.plan(d, ok, ok, fake_buf(), 4096, ws - 1, 0) == _lib.AIRCACHE_EWORKSPACE  # too small
+    assert _lib.plan(d, ok, ok, fake_buf(), 4100, ws, 0) == _lib.AIRCACHE_EINVAL          # misaligned
+    assert _lib.plan(d, None, ok, fake_buf(), 4096, ws, 0) == _lib.AIRCACHE_EINVAL
+    assert _lib.plan(d, [4096, 0], ok, fake_buf(), 4096, ws, 0) == _lib.AIRCACHE_EINVAL   # NULL layer
+    assert _lib.plan(d, ok, [4096, 8200], fake_buf(), 4096, ws, 0) == _lib.AIRCACHE_EINVAL
+    assert "not 16-byte aligned" in lib.aircache_last_error().decode()
+
+
+def test_compress_argument_errors(lib):
+    d = desc(n_layers=1, batch=1, n_vis=64, n_txt=16)
+    k, v = [1 << 20], [2 << 20]
+    layer = 4 * 80 * 128 * 2
+    assert _lib.compress(d, fake_buf(), k, v, None, [3 << 20], 0) == _lib.AIRCACHE_EINVAL
+    # an output that overlaps an input is rejected
+    assert _lib.compress(d, fake_buf(), k, v, [(1 << 20) + layer // 2], [3 << 20], 0) == _lib.AIRCACHE_EINVAL
+    assert "overlap" in lib.aircache_last_error().decode()
+    assert _lib.compress(d, _lib.PlanBuf(), k, v, [3 << 20], [4 << 20], 0) == _lib.AIRCACHE_EINVAL
+
+
+def test_strerror(lib):
+    assert lib.aircache_strerror(0) == b"ok"
+    assert lib.aircache_strerror(2) == b"workspace too small"
