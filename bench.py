@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Benchmark of the AirCache visual KV-cache compression pass on one MI355X.
+
+One step is one whole pass (aircache_plan + aircache_compress: elite window,
+cross-modal scores, statistics, budgets, top-k, compaction) over one batch of
+synthetic, seeded inputs already resident in HBM. Inputs rotate over several
+device copies (>= 1 GiB in total, four times the 256 MB Infinity Cache) so a
+step cannot reuse the previous step's data from the last-level cache.
+
+Prints one JSON line: visual KV token-layers compressed per second (L*B*N_v per
+step), achieved HBM bandwidth of the pass and of its dominant kernel against
+the 8 TB/s peak, and the single-threaded CPU oracle timed on the same inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "visual KV tokens compressed/sec (all layers) + achieved HBM GB/s vs peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=3, help="workload number 1-5 (3: the headline)")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--hot", action="store_true", help="no input rotation (cache-warm)")
+    ap.add_argument("--max-elite", type=int, default=64)
+    ap.add_argument("--path", default="auto", choices=["auto", "tiled", "rows"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, n_elite, budget):
+    """Bytes the method must move in one pass (reads and writes), from the
+    measured elite counts and budgets. Dropped visual V rows are never read."""
+    e, D = w.elem_bytes, w.D
+    L, B = w.L, w.B
+    ntk = n_elite.astype("int64")
+    rhat = budget.astype("int64")
+    k_scan = L * B * w.Hkv * (w.Nv + w.Nt) * D * e          # all keys, once
+    q_rows = int((w.Hq * (ntk + 1)).sum()) * D * e          # last + elite text queries
+    gather = 4 * int((w.Hkv * (rhat + w.Nt)).sum()) * D * e  # kept + text rows of K and V, read + write
+    iv = 8 * L * B * w.Nv                                     # I_v written and read
+    cross = L * B * w.Hkv * w.Nv * D * e + int((w.Hq * ntk).sum()) * D * e + int((w.Hkv * ntk).sum()) * D * e
+    return dict(total=k_scan + q_rows + gather + iv, cross_score=cross, kv_gather=gather,
+                elite_select=L * B * w.Hkv * w.Nt * D * e + L * B * w.Hq * D * e)
+
+
+def cpu_baseline(inp, target_s):
+    import oracle
+    w = inp.w
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.run(inp, threads=1, compact=True)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 30:
+            break
+    return {"value": w.L * w.B * w.Nv * reps / el, "unit": "visual KV token-layers/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the full pass of workload {w.name} (all {w.L} layers, batch {w.B}) on the same "
+                      f"inputs, {reps} repetition(s), {el:.1f} s, single-threaded C in double precision"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: the pass runs on a single MI355X; --gpus {a.gpus} is not "
+              "supported (see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from lvlm_kv_cache_amd import AirCache
+    from lvlm_kv_cache_amd import _lib
+
+    _lib.load()  # the HIP library must be built; there is no fallback
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = wl.CONFIGS[a.workload]
+    seed = a.workload if a.seed is None else a.seed
+    inp = wl.make_inputs(w, seed)
+    tdtype = torch.float32 if w.dtype == wl.F32 else torch.bfloat16
+
+    def dev_layers(arr):
+        out = []
+        for l in range(w.L):
+            t = torch.from_numpy(np.ascontiguousarray(arr[l]))
+            if w.dtype == wl.BF16:
+                t = t.view(torch.int16).view(tdtype)
+            out.append(t.to(dev))
+        return out
+
+    base = (dev_layers(inp.q), dev_layers(inp.k), dev_layers(inp.v))
+    per_copy = sum(t.numel() * t.element_size() for ts in base for t in ts)
+    ncopy = 1 if a.hot else max(1, math.ceil((1 << 30) / per_copy))
+    copies = [base] + [tuple([t.clone() for t in ts] for ts in base) for _ in range(ncopy - 1)]
+
+    ac = AirCache(w.L, w.B, w.Hq, w.Hkv, w.D, w.Nv, w.Nt, dtype=tdtype, alpha=w.alpha, ratio=w.ratio,
+                  max_elite=min(a.max_elite, w.Nt) if a.max_elite > 0 else 0, device=dev, path=a.path)
+    plan = ac.alloc_plan()
+    k_out, v_out = ac.alloc_compacted()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, pev=None, cev=None):
+        q, k, v = copies[i % ncopy]
+        ac.plan(q, k, out=plan, events=pev)
+        ac.compress(plan, k, v, k_out, v_out, events=cev)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if int(plan.status.item()) != 0:
+        raise RuntimeError(f"device status {int(plan.status.item())} (raise --max-elite)")
+    n_elite = plan.n_elite.cpu().numpy()
+    budget = plan.budget.cpu().numpy()
+    nbytes = algorithmic_bytes(w, n_elite, budget)
+
+    # Headline: K whole passes between two events, no instrumentation inside.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(a.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+
+    # Per-kernel durations: the same K passes with an event between kernels.
+    names = _lib.PLAN_KERNELS + _lib.COMPRESS_KERNELS
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(_lib.PLAN_KERNELS) + 1)] +
+          [torch.cuda.Event(enable_timing=True) for _ in range(len(_lib.COMPRESS_KERNELS) + 1)]
+          for _ in range(a.steps)]
+    np_ = len(_lib.PLAN_KERNELS) + 1
+    for evs in ev:              # torch creates the underlying HIP event on first record
+        for e in evs:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(a.steps):
+        step(i, pev=ev[i][:np_], cev=ev[i][np_:])
+    torch.cuda.synchronize()
+    kern = {n: 0.0 for n in names}
+    for i in range(a.steps):
+        p, c = ev[i][:np_], ev[i][np_:]
+        for j, n in enumerate(_lib.PLAN_KERNELS):
+            kern[n] += p[j].elapsed_time(p[j + 1])
+        kern["kv_gather"] += c[0].elapsed_time(c[1])
+    kern_us = {n: 1e3 * t / a.steps for n, t in kern.items()}
+
+    tokens = w.L * w.B * w.Nv
+    value = tokens / (ms * 1e-3)
+    gbps = nbytes["total"] / (ms * 1e-3) / 1e9
+    dom = "cross_score"
+    dom_gbps = nbytes[dom] / (kern_us[dom] * 1e-6) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "visual KV token-layers/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == wl.BF16 else "f32",
+        "data": "synthetic",
+        "config": dict(w.describe(), seed=seed, input_copies=ncopy, cache="hot" if a.hot else "rotated",
+                       path=a.path),
+        "samples_per_s": w.B / (ms * 1e-3),
+        "hbm": {"algorithmic_bytes_per_step": nbytes["total"], "achieved_gbps": gbps,
+                "peak_gbps": PEAK_HBM_GBPS, "frac_of_peak": gbps / PEAK_HBM_GBPS},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": dom_gbps, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": dom_gbps / PEAK_HBM_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes[dom], "avg_launch_us": kern_us[dom]},
+        "kernel_us": kern_us,
+        "elite_mean": float(n_elite.mean()),
+        "budget_sum": int(budget.sum()),
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, a.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -93,8 +93,17 @@ typedef struct {
   double alpha;       /* elite threshold in [0, 1]; the page uses 0.9 */
   double ratio;       /* r / N_v, the retention ratio in [0, 1] */
   int32_t max_elite;  /* workspace cap on elite tokens per (layer, sample); 0 means n_txt */
-  int32_t reserved;   /* must be 0 */
+  int32_t path;       /* scoring kernels: AIRCACHE_PATH_AUTO (0), _TILED (1) or _ROWS (2);
+                         every path computes the same results */
 } aircache_desc;
+
+/* Scoring paths. TILED: column tiles of every (layer, sample, KV head) with
+ * the exponentials spilled to the workspace and a separate merge kernel; any
+ * size. ROWS: one workgroup per 16 elite-query rows keeps a whole row of
+ * logits in registers (n_vis <= 3072). AUTO picks ROWS when it applies. */
+#define AIRCACHE_PATH_AUTO 0
+#define AIRCACHE_PATH_TILED 1
+#define AIRCACHE_PATH_ROWS 2
 
 /* Outputs of aircache_plan; all device pointers, allocated by the caller with
  * the sizes given, written by the library (row-major, [l][b] means index
@@ -149,6 +158,22 @@ int aircache_plan(const aircache_desc *desc, const void *const *q_txt, const voi
 int aircache_compress(const aircache_desc *desc, const aircache_plan_buf *plan,
                       const void *const *k, const void *const *v, void *const *k_out,
                       void *const *v_out, void *stream);
+
+/* Instrumented variants of aircache_plan / aircache_compress for timing
+ * individual kernels. events is a host array of hipEvent_t handles created by
+ * the caller: events[i] is recorded on the stream just before the i-th kernel
+ * of the call and events[n_events - 1] after the last one. n_events must be
+ * AIRCACHE_PLAN_KERNELS + 1 (kernels: elite_select, cross_score, finalize,
+ * topk_select) or AIRCACHE_COMPRESS_KERNELS + 1 (kernel: kv_gather); NULL
+ * events gives the plain call. Results are identical to the plain calls. */
+#define AIRCACHE_PLAN_KERNELS 4
+#define AIRCACHE_COMPRESS_KERNELS 1
+int aircache_plan_profiled(const aircache_desc *desc, const void *const *q_txt, const void *const *k,
+                           const aircache_plan_buf *plan, void *workspace, size_t ws_bytes, void *stream,
+                           void *const *events, int n_events);
+int aircache_compress_profiled(const aircache_desc *desc, const aircache_plan_buf *plan,
+                               const void *const *k, const void *const *v, void *const *k_out,
+                               void *const *v_out, void *stream, void *const *events, int n_events);
 
 /* Text of an aircache_status value. */
 const char *aircache_strerror(int status);

@@ -15,17 +15,21 @@ LIB_PATH = os.path.join(HERE, "_build", "libaircache.so")
 AIRCACHE_OK, AIRCACHE_EINVAL, AIRCACHE_EWORKSPACE, AIRCACHE_EHIP = 0, 1, 2, 3
 AIRCACHE_F32, AIRCACHE_BF16 = 0, 1
 AIRCACHE_DEV_ELITE_OVERFLOW = 1
+PATH_AUTO, PATH_TILED, PATH_ROWS = 0, 1, 2
 MAX_LAYERS = 128
 
 EXPORTS = ["aircache_abi_version", "aircache_workspace_size", "aircache_max_compacted_elems",
-           "aircache_plan", "aircache_compress", "aircache_strerror", "aircache_last_error"]
+           "aircache_plan", "aircache_compress", "aircache_plan_profiled", "aircache_compress_profiled",
+           "aircache_strerror", "aircache_last_error"]
+PLAN_KERNELS = ["elite_select", "cross_score", "finalize", "topk_select"]
+COMPRESS_KERNELS = ["kv_gather"]
 
 
 class Desc(C.Structure):
     _fields_ = [("n_layers", C.c_int32), ("batch", C.c_int32), ("n_q_heads", C.c_int32),
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("n_vis", C.c_int32),
                 ("n_txt", C.c_int32), ("dtype", C.c_int32), ("alpha", C.c_double),
-                ("ratio", C.c_double), ("max_elite", C.c_int32), ("reserved", C.c_int32)]
+                ("ratio", C.c_double), ("max_elite", C.c_int32), ("path", C.c_int32)]
 
 
 class PlanBuf(C.Structure):
@@ -60,6 +64,11 @@ def load() -> C.CDLL:
         lib.aircache_plan.argtypes = [C.POINTER(Desc), P, P, C.POINTER(PlanBuf), P, C.c_size_t, P]
         lib.aircache_compress.restype = C.c_int
         lib.aircache_compress.argtypes = [C.POINTER(Desc), C.POINTER(PlanBuf), P, P, P, P, P]
+        lib.aircache_plan_profiled.restype = C.c_int
+        lib.aircache_plan_profiled.argtypes = [C.POINTER(Desc), P, P, C.POINTER(PlanBuf), P, C.c_size_t, P,
+                                               P, C.c_int]
+        lib.aircache_compress_profiled.restype = C.c_int
+        lib.aircache_compress_profiled.argtypes = [C.POINTER(Desc), C.POINTER(PlanBuf), P, P, P, P, P, P, C.c_int]
         lib.aircache_strerror.restype = C.c_char_p
         lib.aircache_strerror.argtypes = [C.c_int]
         lib.aircache_last_error.restype = C.c_char_p
@@ -87,13 +96,20 @@ def max_compacted_elems(desc: Desc) -> int:
     return int(load().aircache_max_compacted_elems(C.byref(desc)))
 
 
-def plan(desc: Desc, q_ptrs, k_ptrs, buf: PlanBuf, ws_ptr: int, ws_bytes: int, stream: int) -> int:
+def plan(desc: Desc, q_ptrs, k_ptrs, buf: PlanBuf, ws_ptr: int, ws_bytes: int, stream: int,
+         events=None) -> int:
     q = ptr_array(q_ptrs) if q_ptrs is not None else None
     k = ptr_array(k_ptrs) if k_ptrs is not None else None
-    return load().aircache_plan(C.byref(desc), q, k, C.byref(buf), C.c_void_p(ws_ptr), ws_bytes,
-                                C.c_void_p(stream))
+    if events is None:
+        return load().aircache_plan(C.byref(desc), q, k, C.byref(buf), C.c_void_p(ws_ptr), ws_bytes,
+                                    C.c_void_p(stream))
+    return load().aircache_plan_profiled(C.byref(desc), q, k, C.byref(buf), C.c_void_p(ws_ptr), ws_bytes,
+                                         C.c_void_p(stream), ptr_array(events), len(events))
 
 
-def compress(desc: Desc, buf: PlanBuf, k_ptrs, v_ptrs, ko_ptrs, vo_ptrs, stream: int) -> int:
+def compress(desc: Desc, buf: PlanBuf, k_ptrs, v_ptrs, ko_ptrs, vo_ptrs, stream: int, events=None) -> int:
     arrs = [ptr_array(p) if p is not None else None for p in (k_ptrs, v_ptrs, ko_ptrs, vo_ptrs)]
-    return load().aircache_compress(C.byref(desc), C.byref(buf), *arrs, C.c_void_p(stream))
+    if events is None:
+        return load().aircache_compress(C.byref(desc), C.byref(buf), *arrs, C.c_void_p(stream))
+    return load().aircache_compress_profiled(C.byref(desc), C.byref(buf), *arrs, C.c_void_p(stream),
+                                             ptr_array(events), len(events))

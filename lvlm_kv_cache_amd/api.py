@@ -15,14 +15,17 @@ from . import _lib
 _DTYPES = {torch.float32: _lib.AIRCACHE_F32, torch.bfloat16: _lib.AIRCACHE_BF16}
 
 
+_PATHS = {"auto": _lib.PATH_AUTO, "tiled": _lib.PATH_TILED, "rows": _lib.PATH_ROWS}
+
+
 def make_desc(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt, dtype,
-              alpha=0.9, ratio=0.1, max_elite=0) -> _lib.Desc:
+              alpha=0.9, ratio=0.1, max_elite=0, path="auto") -> _lib.Desc:
     if isinstance(dtype, torch.dtype):
         dtype = _DTYPES[dtype]
     elif isinstance(dtype, str):
         dtype = {"f32": _lib.AIRCACHE_F32, "bf16": _lib.AIRCACHE_BF16}[dtype]
     return _lib.Desc(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt, dtype,
-                     float(alpha), float(ratio), int(max_elite), 0)
+                     float(alpha), float(ratio), int(max_elite), _PATHS[path] if isinstance(path, str) else int(path))
 
 
 @dataclasses.dataclass
@@ -62,7 +65,7 @@ class AirCache:
     """
 
     def __init__(self, n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt,
-                 dtype=torch.bfloat16, alpha=0.9, ratio=0.1, max_elite=0, device="cuda"):
+                 dtype=torch.bfloat16, alpha=0.9, ratio=0.1, max_elite=0, device="cuda", path="auto"):
         self.shape = dict(L=n_layers, B=batch, Hq=n_q_heads, Hkv=n_kv_heads, D=head_dim,
                           Nv=n_vis, Nt=n_txt)
         self.dtype = dtype
@@ -70,7 +73,7 @@ class AirCache:
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
         self.desc = make_desc(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt,
-                              dtype, alpha, ratio, max_elite)
+                              dtype, alpha, ratio, max_elite, path)
         ws = _lib.workspace_size(self.desc)
         if ws == 0:
             _lib.check(_lib.AIRCACHE_EINVAL)
@@ -100,13 +103,16 @@ class AirCache:
         s = self.shape
         return PlanOutputs.empty(s["L"], s["B"], s["Nv"], s["Nt"], self.device)
 
-    def plan(self, q_txt, k, out: PlanOutputs | None = None, stream=None) -> PlanOutputs:
+    def plan(self, q_txt, k, out: PlanOutputs | None = None, stream=None, events=None) -> PlanOutputs:
+        """events: optional list of 5 torch.cuda.Event (timing=True) recorded
+        around the plan's 4 kernels."""
         s = self.shape
         self._check_layers(q_txt, (s["B"], s["Hq"], s["Nt"], s["D"]), "q_txt")
         self._check_layers(k, (s["B"], s["Hkv"], s["Nv"] + s["Nt"], s["D"]), "k")
         out = out or self.alloc_plan()
         _lib.check(_lib.plan(self.desc, [t.data_ptr() for t in q_txt], [t.data_ptr() for t in k],
-                             out.buf(), self.workspace.data_ptr(), self.ws_bytes, self._stream(stream)))
+                             out.buf(), self.workspace.data_ptr(), self.ws_bytes, self._stream(stream),
+                             events=None if events is None else [e.cuda_event for e in events]))
         return out
 
     def alloc_compacted(self):
@@ -116,7 +122,7 @@ class AirCache:
         mk = lambda: [torch.empty(n, dtype=self.dtype, device=self.device) for _ in range(L)]
         return mk(), mk()
 
-    def compress(self, plan: PlanOutputs, k, v, k_out, v_out, stream=None) -> None:
+    def compress(self, plan: PlanOutputs, k, v, k_out, v_out, stream=None, events=None) -> None:
         s = self.shape
         shp = (s["B"], s["Hkv"], s["Nv"] + s["Nt"], s["D"])
         self._check_layers(k, shp, "k")
@@ -131,4 +137,5 @@ class AirCache:
                                      f"{self.device} with at least {cap} elements")
         _lib.check(_lib.compress(self.desc, plan.buf(), [t.data_ptr() for t in k],
                                  [t.data_ptr() for t in v], [t.data_ptr() for t in k_out],
-                                 [t.data_ptr() for t in v_out], self._stream(stream)))
+                                 [t.data_ptr() for t in v_out], self._stream(stream),
+                                 events=None if events is None else [e.cuda_event for e in events]))

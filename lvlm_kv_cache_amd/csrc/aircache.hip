@@ -52,6 +52,7 @@ struct Ws {
   unsigned *cnt_all;  // [1]   finished samples
   float2 *stats;      // [units][rcap16][ntiles] (tile max, tile sum) per row, base 2
   float *e;           // [units][Nv][row stride] exp2(logit - tile max) of visual keys
+  float *part;        // [units][rt_grid][Nv] column sums of one row tile (row-complete path)
 };
 
 struct LayerTable {
@@ -63,26 +64,31 @@ struct LayerTableOut {
 
 // ----------------------------------------------------------------------------
 // Step 1: elite observation window ("Elite Observation Window", the Att and k
-// equations). One workgroup per (layer, sample). For each query head the last
-// text query's logits over the N_t text keys of its KV head come from MFMA
-// (keys as the A operand, up to 16 heads of one KV group as the B operand);
-// each wave then normalises whole rows (max, sum of exp2) and the rows are
-// summed into pbar in a fixed head order. Elite = { j : pbar_j >= alpha max },
-// compacted in ascending j by a block scan.
+// equations). One workgroup of 8 waves per (layer, sample). The logits of the
+// last text query of every query head over the N_t text keys of its KV head
+// come from MFMA (16 text keys as the A operand, up to 16 query heads of one KV
+// group as the B operand); the (KV head, head tile, key tile) items are spread
+// over the waves and all H_q x N_t logits land in LDS. Each wave then
+// normalises whole rows (max, sum of exp2), rows are summed into pbar in
+// ascending head order, and elite = { j : pbar_j >= alpha max pbar }, compacted
+// in ascending j by a block scan.
 // ----------------------------------------------------------------------------
+constexpr int kEliteThreads = 512;
+constexpr int kEliteWaves = kEliteThreads / 64;
+
 template <typename Tag, int D>
-__global__ __launch_bounds__(256) void elite_select_kernel(Shape sh, LayerTable qt, LayerTable kt, PlanPtrs plan,
-                                                           Ws ws) {
+__global__ __launch_bounds__(kEliteThreads) void elite_select_kernel(Shape sh, LayerTable qt, LayerTable kt,
+                                                                     PlanPtrs plan, Ws ws) {
   using E = typename Tag::store_t;
-  extern __shared__ float lds[];  // z[16][Nt], pbar[Nt]
-  __shared__ float red[4];
-  __shared__ int wtot[4];
+  extern __shared__ float lds[];  // z[Hq][Nt], pbar[Nt]
+  __shared__ float red[kEliteWaves];
+  __shared__ int wtot[kEliteWaves];
   const int lb = blockIdx.x, l = lb / sh.B, b = lb % sh.B;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, grp = lane >> 4;
   const int Nt = sh.Nt, G = sh.G;
   float *z = lds;
-  float *pbar = lds + 16 * Nt;
+  float *pbar = lds + (size_t)sh.Hq * Nt;
 
   // This kernel opens every plan: reset the counters of finalize_kernel.
   if (tid == 0) {
@@ -93,93 +99,110 @@ __global__ __launch_bounds__(256) void elite_select_kernel(Shape sh, LayerTable 
       *plan.status = 0;
     }
   }
-  for (int j = tid; j < Nt; j += 256) pbar[j] = 0.f;
 
   const E *q = static_cast<const E *>(qt.p[l]);
   const E *k = static_cast<const E *>(kt.p[l]);
   const int nkt = (Nt + 15) >> 4;
-  for (int g = 0; g < sh.Hkv; ++g) {
-    const E *ktxt = k + ((size_t)(b * sh.Hkv + g) * sh.S + sh.Nv) * D;
-    for (int h0 = 0; h0 < G; h0 += 16) {
+  const int nht = (G + 15) >> 4;
+  const int items = sh.Hkv * nht * nkt;
+  // Items (KV head, head tile, key tile) in batches of 4 per wave: all
+  // fragments of a batch are loaded before its MFMAs so the loads overlap.
+  constexpr int kBatch = 4;
+  for (int it0 = wave; it0 < items; it0 += kEliteWaves * kBatch) {
+    Frag<Tag> qf[kBatch][D / 32], kf[kBatch][D / 32];
+#pragma unroll
+    for (int bi = 0; bi < kBatch; ++bi) {
+      const int it = it0 + bi * kEliteWaves;
+      const int kt_ = it % nkt, gh = it / nkt;
+      const int ht = gh % nht, g = gh / nht;
+      const int h0 = ht * 16;
       const int nh = min(16, G - h0);
-      Frag<Tag> qf[D / 32];
-      if (n < nh) {
+      const int key = kt_ * 16 + n;
+      if (it < items && n < nh) {
         const E *qrow = q + ((size_t)(b * sh.Hq + g * G + h0 + n) * Nt + (Nt - 1)) * D;
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) qf[c].load(qrow + c * 32 + grp * 8);
+        for (int c = 0; c < D / 32; ++c) qf[bi][c].load(qrow + c * 32 + grp * 8);
       } else {
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) qf[c].zero();
+        for (int c = 0; c < D / 32; ++c) qf[bi][c].zero();
       }
-      __syncthreads();  // z is free (previous group fully consumed)
-      for (int t = wave; t < nkt; t += 4) {
-        Frag<Tag> kf[D / 32];
-        const int key = t * 16 + n;
-        if (key < Nt) {
-          const E *krow = ktxt + (size_t)key * D;
+      if (it < items && key < Nt) {
+        const E *krow = k + ((size_t)(b * sh.Hkv + g) * sh.S + sh.Nv + key) * D;
 #pragma unroll
-          for (int c = 0; c < D / 32; ++c) kf[c].load(krow + c * 32 + grp * 8);
-        } else {
+        for (int c = 0; c < D / 32; ++c) kf[bi][c].load(krow + c * 32 + grp * 8);
+      } else {
 #pragma unroll
-          for (int c = 0; c < D / 32; ++c) kf[c].zero();
-        }
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) mfma_slice(acc, kf[c], qf[c]);
-        if (n < nh) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kk = t * 16 + grp * 4 + i;
-            if (kk < Nt) z[n * Nt + kk] = acc[i] * sh.scale2;
-          }
-        }
+        for (int c = 0; c < D / 32; ++c) kf[bi][c].zero();
       }
-      __syncthreads();
-      for (int hh = wave; hh < nh; hh += 4) {
-        float *zr = z + hh * Nt;
-        float m = -INFINITY;
-        for (int j = lane; j < Nt; j += 64) m = fmaxf(m, zr[j]);
-        m = wave_max(m);
-        float s = 0.f;
-        for (int j = lane; j < Nt; j += 64) {
-          const float ev = exp2f(zr[j] - m);
-          zr[j] = ev;
-          s += ev;
+    }
+#pragma unroll
+    for (int bi = 0; bi < kBatch; ++bi) {
+      const int it = it0 + bi * kEliteWaves;
+      if (it >= items) break;  // wave-uniform
+      const int kt_ = it % nkt, gh = it / nkt;
+      const int ht = gh % nht, g = gh / nht;
+      const int h0 = ht * 16;
+      const int nh = min(16, G - h0);
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) mfma_slice(acc, kf[bi][c], qf[bi][c]);
+      if (n < nh) {
+        float *zr = z + (size_t)(g * G + h0 + n) * Nt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = kt_ * 16 + grp * 4 + i;
+          if (kk < Nt) zr[kk] = acc[i] * sh.scale2;
         }
-        s = wave_sum(s);
-        const float inv = 1.f / s;
-        for (int j = lane; j < Nt; j += 64) zr[j] *= inv;
-      }
-      __syncthreads();
-      for (int j = tid; j < Nt; j += 256) {
-        float a = pbar[j];
-        for (int hh = 0; hh < nh; ++hh) a += z[hh * Nt + j];
-        pbar[j] = a;
       }
     }
   }
   __syncthreads();
+  for (int h = wave; h < sh.Hq; h += kEliteWaves) {
+    float *zr = z + (size_t)h * Nt;
+    float m = -INFINITY;
+    for (int j = lane; j < Nt; j += 64) m = fmaxf(m, zr[j]);
+    m = wave_max(m);
+    float s = 0.f;
+    for (int j = lane; j < Nt; j += 64) {
+      const float ev = exp2f(zr[j] - m);
+      zr[j] = ev;
+      s += ev;
+    }
+    s = wave_sum(s);
+    const float inv = 1.f / s;
+    for (int j = lane; j < Nt; j += 64) zr[j] *= inv;
+  }
+  __syncthreads();
   float m = -INFINITY;
-  for (int j = tid; j < Nt; j += 256) m = fmaxf(m, pbar[j]);
+  for (int j = tid; j < Nt; j += kEliteThreads) {
+    float a = 0.f;
+    for (int h = 0; h < sh.Hq; ++h) a += z[(size_t)h * Nt + j];
+    pbar[j] = a;
+    m = fmaxf(m, a);
+  }
   m = wave_max(m);
   if (lane == 0) red[wave] = m;
   __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  m = red[0];
+  for (int w = 1; w < kEliteWaves; ++w) m = fmaxf(m, red[w]);
   const float thr = sh.alpha * m;
-  const int per = (Nt + 255) / 256;
+  const int per = (Nt + kEliteThreads - 1) / kEliteThreads;
   const int j0 = min(Nt, tid * per), j1 = min(Nt, j0 + per);
   int cnt = 0;
   for (int j = j0; j < j1; ++j) cnt += (pbar[j] >= thr) ? 1 : 0;
   const int incl = wave_incl_scan(cnt);
   if (lane == 63) wtot[wave] = incl;
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += wtot[w];
+  int base = 0, total = 0;
+  for (int w = 0; w < kEliteWaves; ++w) {
+    if (w < wave) base += wtot[w];
+    total += wtot[w];
+  }
   int pos = base + incl - cnt;
   int32_t *el = plan.elite + (size_t)lb * Nt;
   for (int j = j0; j < j1; ++j)
     if (pbar[j] >= thr) el[pos++] = j;
-  if (tid == 0) plan.n_elite[lb] = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+  if (tid == 0) plan.n_elite[lb] = total;
 }
 
 // ----------------------------------------------------------------------------
@@ -309,15 +332,15 @@ __global__ __launch_bounds__(256) void cross_score_kernel(Shape sh, LayerTable q
     if (lane < 16) red_z[wave][lane] = zs;
     __syncthreads();
     zs = red_z[0][n] + red_z[1][n] + red_z[2][n] + red_z[3][n];
-    if (r < R) {
-      if (wave == 0 && grp == 0) st_out[(size_t)r * sh.ntiles + t] = make_float2(m, zs);
+    if (r < R && wave == 0 && grp == 0) st_out[(size_t)r * sh.ntiles + t] = make_float2(m, zs);
+    // rows R .. RP-1 of the last row tile are written as zeros, so that readers
+    // can sum whole 16-row groups without masking
 #pragma unroll
-      for (int i = 0; i < KTW; ++i) {
+    for (int i = 0; i < KTW; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = (wave + 4 * i) * 16 + grp * 4 + j;
-          if (key < nvis) e_out[(size_t)(c0 + key) * RP + r] = acc[i][j];
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int key = (wave + 4 * i) * 16 + grp * 4 + j;
+        if (key < nvis) e_out[(size_t)(c0 + key) * RP + r] = (r < R) ? acc[i][j] : 0.f;
       }
     }
     __syncthreads();  // red_m / red_z are reused by the next row tile
@@ -326,30 +349,114 @@ __global__ __launch_bounds__(256) void cross_score_kernel(Shape sh, LayerTable q
 
 // Budget of every layer of one sample ("Layer-wise KV Cache Budget
 // Allocation", the r_hat equation with the cross-layer normalisation reading
-// documented in aircache.h). Plain double arithmetic in a fixed order with no
-// fused multiply-add, so the same statistics give the same integers anywhere.
-__device__ void sample_budgets(const Shape &sh, const PlanPtrs &plan, int b) {
+// documented in aircache.h), from the sample's L statistics already in LDS.
+// Plain double arithmetic in a fixed order with no fused multiply-add, so the
+// same statistics give the same integers anywhere.
+__device__ void sample_budgets(const Shape &sh, const double *st, const double *sk, double *x_out, int *b_out) {
 #pragma clang fp contract(off)
-  const int L = sh.L, B = sh.B;
+  const int L = sh.L;
   double st_sum = 0.0, mshift = 0.0, u_sum = 0.0;
-  for (int l = 0; l < L; ++l) st_sum += load_coherent(&plan.s_t[l * B + b]);
-  for (int l = 0; l < L; ++l) {
-    const double sk = load_coherent(&plan.s_k[l * B + b]);
-    if (sk < mshift) mshift = sk;
-  }
-  for (int l = 0; l < L; ++l) u_sum += load_coherent(&plan.s_k[l * B + b]) - mshift;
+  for (int l = 0; l < L; ++l) st_sum += st[l];
+  for (int l = 0; l < L; ++l)
+    if (sk[l] < mshift) mshift = sk[l];
+  for (int l = 0; l < L; ++l) u_sum += sk[l] - mshift;
   const double r = sh.ratio * (double)sh.Nv;
   for (int l = 0; l < L; ++l) {
-    const double st = load_coherent(&plan.s_t[l * B + b]);
-    const double sk = load_coherent(&plan.s_k[l * B + b]);
-    const double stn = st * (double)L / st_sum;
-    const double skn = (u_sum > 0.0) ? (sk - mshift) * (double)L / u_sum : 1.0;
+    const double stn = st[l] * (double)L / st_sum;
+    const double skn = (u_sum > 0.0) ? (sk[l] - mshift) * (double)L / u_sum : 1.0;
     const double x = 0.5 * (stn + skn) * r;
     double f = floor(x);
     if (!(f > 0.0)) f = 0.0;
     if (f > (double)sh.Nv) f = (double)sh.Nv;
-    if (plan.bx) store_coherent(&plan.bx[l * B + b], x);
-    store_coherent(&plan.budget[l * B + b], (int32_t)f);
+    x_out[l] = x;
+    b_out[l] = (int)f;
+  }
+}
+
+// The last workgroup to finish a (layer, sample) runs this with the layer's
+// I_v in LDS: strength and skewness ("Layer-wise KV Cache Budget Allocation",
+// the s_t and s_k equations) in double precision, then, if it is the last
+// layer of its sample to finish, that sample's budgets, and if it is the last
+// sample, the compacted layout's offsets. Elections use relaxed device-scope
+// counters; published values are written with agent-coherent stores whose
+// completion is awaited before the counter moves, and read back with
+// agent-coherent loads.
+template <int NT>
+__device__ void finish_layer_sample(const Shape &sh, const PlanPtrs &plan, const Ws &ws, int lb, const float *ivc) {
+  constexpr int NW = NT / 64;
+  __shared__ double redd[NW];
+  __shared__ double lst[AIRCACHE_MAX_LAYERS], lsk[AIRCACHE_MAX_LAYERS], lx[AIRCACHE_MAX_LAYERS];
+  __shared__ int lbud[AIRCACHE_MAX_LAYERS];
+  __shared__ int flag;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Nv = sh.Nv, b = lb % sh.B;
+  auto block_sum = [&](double v) {
+    v = wave_sum_d(v);
+    if (lane == 0) redd[wave] = v;
+    __syncthreads();
+    double t = 0.0;
+    for (int w = 0; w < NW; ++w) t += redd[w];
+    __syncthreads();
+    return t;
+  };
+  double s = 0.0;
+  for (int c = tid; c < Nv; c += NT) s += (double)ivc[c];
+  s = block_sum(s);
+  const double mu = s / (double)Nv;
+  double v2 = 0.0;
+  for (int c = tid; c < Nv; c += NT) {
+    const double d = (double)ivc[c] - mu;
+    v2 += d * d;
+  }
+  v2 = block_sum(v2);
+  const double sigma = sqrt(v2 / (double)(Nv - 1));
+  double k3 = 0.0;
+  if (sigma > 0.0) {
+    for (int c = tid; c < Nv; c += NT) {
+      const double d = ((double)ivc[c] - mu) / sigma;
+      k3 += d * d * d;
+    }
+  }
+  k3 = block_sum(k3);
+  if (tid == 0) {
+    const double skew = (sigma > 0.0) ? k3 * ((double)Nv / ((double)(Nv - 1) * (double)(Nv - 2))) : 0.0;
+    store_coherent(&plan.s_t[lb], s);
+    store_coherent(&plan.s_k[lb], skew);
+    wait_all_memory();
+    flag = (counter_add(&ws.cnt_b[b], 1u) == (unsigned)sh.L - 1);
+  }
+  __syncthreads();
+  if (!flag) return;
+
+  // Last layer of sample b: budgets of all its layers.
+  const int L = sh.L, B = sh.B;
+  acquire_device();
+  for (int l = tid; l < L; l += NT) {
+    lst[l] = plan.s_t[l * B + b];
+    lsk[l] = plan.s_k[l * B + b];
+  }
+  __syncthreads();
+  if (tid == 0) sample_budgets(sh, lst, lsk, lx, lbud);
+  __syncthreads();
+  for (int l = tid; l < L; l += NT) {
+    if (plan.bx) store_coherent(&plan.bx[l * B + b], lx[l]);
+    store_coherent(&plan.budget[l * B + b], (int32_t)lbud[l]);
+  }
+  wait_all_memory();
+  __syncthreads();
+  if (tid == 0) flag = (counter_add(ws.cnt_all, 1u) == (unsigned)B - 1);
+  __syncthreads();
+  if (!flag) return;
+
+  // Last sample: element offsets of every sample's segment in each layer.
+  acquire_device();
+  for (int l = tid; l < L; l += NT) {
+    int64_t off = 0;
+    for (int bb = 0; bb < B; ++bb) {
+      plan.out_off[(size_t)l * (B + 1) + bb] = off;
+      off += (int64_t)sh.Hkv * (plan.budget[l * B + bb] + sh.Nt) * sh.D;
+    }
+    plan.out_off[(size_t)l * (B + 1) + B] = off;
   }
 }
 
@@ -363,13 +470,12 @@ __device__ void sample_budgets(const Shape &sh, const PlanPtrs &plan, int b) {
 // sample computes that sample's budgets; the last sample writes the compacted
 // layout's offsets. Finisher election is a relaxed device-scope counter; the
 // data it publishes is written with agent-coherent stores whose completion is
-// awaited before the counter moves.
+// awaited before the counter moves, and read back with agent-coherent loads.
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void finalize_kernel(Shape sh, PlanPtrs plan, Ws ws) {
   extern __shared__ float wl[];  // weights [Hkv][rcap16], then I_v cache [Nv] for the finisher
-  __shared__ double redd[4];
-  __shared__ int is_last;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int flag;
+  const int tid = threadIdx.x;
   const int t = blockIdx.x % sh.ntiles;
   const int lb = blockIdx.x / sh.ntiles, b = lb % sh.B;
   int ntk = plan.n_elite[lb];
@@ -377,14 +483,28 @@ __global__ __launch_bounds__(256) void finalize_kernel(Shape sh, PlanPtrs plan, 
   if (ntk < 0) ntk = 0;
   const int R = sh.G * ntk;
   const int RP = (R + 15) & ~15;
-  for (int idx = tid; idx < sh.Hkv * R; idx += 256) {
-    const int g = idx / R, r = idx - g * R;
-    const float2 *st = ws.stats + ((size_t)(lb * sh.Hkv + g) * sh.rcap16 + r) * sh.ntiles;
-    float M = -INFINITY;
-    for (int tt = 0; tt < sh.ntiles; ++tt) M = fmaxf(M, st[tt].x);
-    float Z = 0.f;
-    for (int tt = 0; tt < sh.ntiles; ++tt) Z += st[tt].y * exp2f(st[tt].x - M);
-    wl[g * sh.rcap16 + r] = exp2f(st[t].x - M) / Z;
+  for (int idx = tid; idx < sh.Hkv * RP; idx += 256) {
+    const int g = idx / RP, r = idx - g * RP;
+    float wv = 0.f;
+    if (r < R) {
+      const float2 *st = ws.stats + ((size_t)(lb * sh.Hkv + g) * sh.rcap16 + r) * sh.ntiles;
+      // online merge of the tiles' (max, sum) in ascending tile order, eight loads at a time
+      float M = -INFINITY, Z = 0.f;
+      for (int t0 = 0; t0 < sh.ntiles; t0 += 8) {
+        float2 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = (t0 + j < sh.ntiles) ? st[t0 + j] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (v[j].x == -INFINITY) continue;
+          const float mn = fmaxf(M, v[j].x);
+          Z = Z * exp2f(M - mn) + v[j].y * exp2f(v[j].x - mn);
+          M = mn;
+        }
+      }
+      wv = exp2f(st[t].x - M) / Z;
+    }
+    wl[g * RP + r] = wv;
   }
   __syncthreads();
   const float inv_rows = (ntk > 0) ? 1.f / (float)(sh.Hq * ntk) : 0.f;
@@ -392,72 +512,264 @@ __global__ __launch_bounds__(256) void finalize_kernel(Shape sh, PlanPtrs plan, 
   for (int c = c0 + tid; c < c1; c += 256) {
     float acc = 0.f;
     for (int g = 0; g < sh.Hkv; ++g) {
-      const float *e = ws.e + (size_t)(lb * sh.Hkv + g) * sh.Nv * sh.rcap16 + (size_t)c * RP;
-      const float *w = wl + g * sh.rcap16;
-      for (int r = 0; r < R; ++r) acc += e[r] * w[r];
+      const f32x4_t *e4 =
+          reinterpret_cast<const f32x4_t *>(ws.e + (size_t)(lb * sh.Hkv + g) * sh.Nv * sh.rcap16 + (size_t)c * RP);
+      const f32x4_t *w4 = reinterpret_cast<const f32x4_t *>(wl + g * RP);
+      for (int r0 = 0; r0 < RP / 4; r0 += 4) {  // RP is a multiple of 16
+        f32x4_t ev[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ev[j] = e4[r0 + j];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4_t wv = w4[r0 + j];
+          acc += ev[j].x * wv.x;
+          acc += ev[j].y * wv.y;
+          acc += ev[j].z * wv.z;
+          acc += ev[j].w * wv.w;
+        }
+      }
     }
     store_coherent(&plan.iv[(size_t)lb * sh.Nv + c], acc * inv_rows);
   }
   wait_all_memory();
   __syncthreads();
-  if (tid == 0) is_last = (counter_add(&ws.cnt_lb[lb], 1u) == (unsigned)sh.ntiles - 1);
+  if (tid == 0) flag = (counter_add(&ws.cnt_lb[lb], 1u) == (unsigned)sh.ntiles - 1);
   __syncthreads();
-  if (!is_last) return;
+  if (!flag) return;
 
-  // Statistics of I_v for this (layer, sample), in double precision.
   float *ivc = wl + sh.Hkv * sh.rcap16;
+  acquire_device();
+  for (int c = tid; c < sh.Nv; c += 256) ivc[c] = plan.iv[(size_t)lb * sh.Nv + c];
+  __syncthreads();
+  finish_layer_sample<256>(sh, plan, ws, lb, ivc);
+}
+
+// ----------------------------------------------------------------------------
+// Steps 2 + 3 + 4 in one launch when a whole row of logits fits in registers
+// (N_v + elite text keys <= 8 waves x 16 x KT): one workgroup of 8 waves per
+// (layer, sample, KV head, row tile of 16 elite-query rows). The elite
+// queries are the MFMA A operand, 16 keys at a time the B operand; wave w owns
+// key tiles w, w + 8, ... (visual tiles first, then elite text tiles), keeps
+// their logits in registers, and the exact row max and row sum come from
+// in-lane, cross-lane and cross-wave reductions in a fixed order. Column sums
+// of exp2(S - M) / Z over the tile's rows are accumulated in LDS, written to
+// the workspace as this row tile's partial I_v, and the last workgroup of the
+// (layer, sample) adds the partials in a fixed order and runs the finisher.
+// Workgroups are numbered so that the rt_grid row tiles of one (l, b, g) sit
+// on one XCD (round-robin dispatch over the 8 XCDs) and share K through L2.
+// ----------------------------------------------------------------------------
+constexpr int kRowsThreads = 768;
+constexpr int kRowsWaves = kRowsThreads / 64;
+
+template <typename Tag, int D, int KT>
+__global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh, LayerTable qt, LayerTable kt,
+                                                                        PlanPtrs plan, Ws ws, int rt_grid,
+                                                                        int units) {
+  using E = typename Tag::store_t;
+  constexpr int NW = kRowsWaves;
+  constexpr int kTileBytes = 16 * D * Tag::kBytes;  // one 16-key tile
+  constexpr int kDma = kTileBytes / 1024;           // 16-byte DMA loads per lane per tile
+  constexpr int kRing = 2;                          // tiles in flight per wave
+  static_assert(KT >= kRing, "ring deeper than the tile count");
+  extern __shared__ float dyn[];  // ring[NW][kRing][kTileBytes], colacc[Nv] (reused for I_v), el[cap]
+  __shared__ float red[NW][16];
+  __shared__ float rowv[16];
+  __shared__ int flag;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, grp = lane >> 4;
+  const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
+  const int u = (loc / rt_grid) * 8 + xcd, rt0 = loc % rt_grid;
+  if (u >= units) return;
+  const int g = u % sh.Hkv, lb = u / sh.Hkv, l = lb / sh.B, b = lb % sh.B;
   const int Nv = sh.Nv;
-  double s = 0.0;
-  for (int c = tid; c < Nv; c += 256) {
-    const float x = load_coherent(&plan.iv[(size_t)lb * Nv + c]);
-    ivc[c] = x;
-    s += (double)x;
-  }
-  s = wave_sum_d(s);
-  if (lane == 0) redd[wave] = s;
+  unsigned char *ring = reinterpret_cast<unsigned char *>(dyn) + (size_t)wave * kRing * kTileBytes;
+  float *colacc = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(dyn) + (size_t)NW * kRing * kTileBytes);
+  int *el = reinterpret_cast<int *>(colacc + Nv);
+  int ntk = plan.n_elite[lb];
+  if (ntk > sh.cap) ntk = sh.cap;
+  if (ntk < 0) ntk = 0;
+  const int R = sh.G * ntk;
+  const int nrt = (R + 15) >> 4;
+  for (int i = tid; i < ntk; i += kRowsThreads) el[i] = plan.elite[(size_t)lb * sh.Nt + i];
+  for (int c = tid; c < Nv; c += kRowsThreads) colacc[c] = 0.f;
   __syncthreads();
-  s = (redd[0] + redd[1]) + (redd[2] + redd[3]);
-  const double mu = s / (double)Nv;
-  __syncthreads();
-  double v2 = 0.0;
-  for (int c = tid; c < Nv; c += 256) {
-    const double d = (double)ivc[c] - mu;
-    v2 += d * d;
-  }
-  v2 = wave_sum_d(v2);
-  if (lane == 0) redd[wave] = v2;
-  __syncthreads();
-  v2 = (redd[0] + redd[1]) + (redd[2] + redd[3]);
-  const double sigma = sqrt(v2 / (double)(Nv - 1));
-  __syncthreads();
-  double k3 = 0.0;
-  if (sigma > 0.0) {
-    for (int c = tid; c < Nv; c += 256) {
-      const double d = ((double)ivc[c] - mu) / sigma;
-      k3 += d * d * d;
+
+  const E *q = static_cast<const E *>(qt.p[l]);
+  const E *kb = static_cast<const E *>(kt.p[l]) + (size_t)(b * sh.Hkv + g) * sh.S * D;
+  const int nvt = (Nv + 15) >> 4;
+  const int nxt = (ntk + 15) >> 4;
+  for (int rt = rt0; rt < nrt; rt += rt_grid) {
+    const int r = rt * 16 + n;
+    Frag<Tag> qf[D / 32];
+    if (r < R) {
+      const int hl = r / ntk, e = r - hl * ntk;
+      const E *qrow = q + ((size_t)(b * sh.Hq + g * sh.G + hl) * sh.Nt + el[e]) * D;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) qf[c].load(qrow + c * 32 + grp * 8);
+    } else {
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) qf[c].zero();
     }
-  }
-  k3 = wave_sum_d(k3);
-  if (lane == 0) redd[wave] = k3;
-  __syncthreads();
-  if (tid != 0) return;
-  k3 = (redd[0] + redd[1]) + (redd[2] + redd[3]);
-  const double skew = (sigma > 0.0) ? k3 * ((double)Nv / ((double)(Nv - 1) * (double)(Nv - 2))) : 0.0;
-  store_coherent(&plan.s_t[lb], s);
-  store_coherent(&plan.s_k[lb], skew);
-  wait_all_memory();
-  if (counter_add(&ws.cnt_b[b], 1u) != (unsigned)sh.L - 1) return;
-  sample_budgets(sh, plan, b);
-  wait_all_memory();
-  if (counter_add(ws.cnt_all, 1u) != (unsigned)sh.B - 1) return;
-  for (int l = 0; l < sh.L; ++l) {
-    int64_t off = 0;
-    for (int bb = 0; bb < sh.B; ++bb) {
-      plan.out_off[(size_t)l * (sh.B + 1) + bb] = off;
-      off += (int64_t)sh.Hkv * (load_coherent(&plan.budget[l * sh.B + bb]) + sh.Nt) * sh.D;
+    // Elite text keys (at most a few tiles): online max / sum per row, wave w
+    // takes text tiles w, w + NW, ...
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    float zx[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int xt = wave; xt < nxt; xt += NW) {
+      const int e = xt * 16 + n;
+      Frag<Tag> kf[D / 32];
+      if (e < ntk) {
+        const E *kr = kb + (size_t)(Nv + el[e]) * D;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) kf[c].load(kr + c * 32 + grp * 8);
+      } else {
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) kf[c].zero();
+      }
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) mfma_slice(acc, qf[c], kf[c]);
+      if (e < ntk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = acc[i] * sh.scale2;
+          const float mn = fmaxf(mx[i], v);
+          zx[i] = zx[i] * exp2f(mx[i] - mn) + exp2f(v - mn);
+          mx[i] = mn;
+        }
+      }
     }
-    plan.out_off[(size_t)l * (sh.B + 1) + sh.B] = off;
+    // Visual keys: wave w owns tiles w, w + NW, ...; their logits stay in
+    // registers. Tiles stream through a per-wave LDS ring by DMA; loads are
+    // issued for every slot (an empty slot rereads the last visual row and is
+    // ignored) so the count of loads in flight is static.
+    f32x4_t S[KT];
+    float mr[4] = {mx[0], mx[1], mx[2], mx[3]};
+    auto stage = [&](int k) {
+      int row = (wave + NW * k) * 16 + n;
+      // keep the address computation inside its iteration instead of letting
+      // all of a wave's tile addresses be precomputed (and spilled)
+      asm volatile("" : "+v"(row));
+      const unsigned char *src = reinterpret_cast<const unsigned char *>(kb + (size_t)(row < Nv ? row : Nv - 1) * D);
+      unsigned char *slot = ring + (k % kRing) * kTileBytes;
+      if (k >= kRing) wait_lds_reads();  // the slot's previous tile has been read
+#pragma unroll
+      for (int j = 0; j < kDma; ++j) load_lds16(src + 16 * grp + 64 * j, slot + 1024 * j);
+    };
+#pragma unroll
+    for (int k = 0; k < kRing; ++k) stage(k);
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      // tile k has landed once only the loads of the tiles staged after it remain
+      wait_tiles<kDma>(min(kRing - 1, KT - 1 - k));
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      const unsigned char *slot = ring + (k % kRing) * kTileBytes;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        Frag<Tag> kf;
+        LdsTile<Tag>::read(kf, slot, c, lane);
+        mfma_slice(acc, qf[c], kf);
+      }
+      if (k + kRing < KT) stage(k + kRing);
+      const bool ok = (wave + NW * k) * 16 + n < Nv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        S[k][i] = ok ? acc[i] * sh.scale2 : -INFINITY;
+        mr[i] = fmaxf(mr[i], S[k][i]);
+      }
+    }
+    // lane holds rows grp*4+i of key n: reduce over keys (lanes of equal grp), then waves
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) mr[i] = fmaxf(mr[i], __shfl_xor(mr[i], o));
+    }
+    if (n == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][grp * 4 + i] = mr[i];
+    }
+    __syncthreads();
+    if (tid < 16) {
+      float m = red[0][tid];
+      for (int w = 1; w < NW; ++w) m = fmaxf(m, red[w][tid]);
+      rowv[tid] = m;
+    }
+    __syncthreads();
+    float zr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float M = rowv[grp * 4 + i];
+      zr[i] = (mx[i] > -INFINITY) ? zx[i] * exp2f(mx[i] - M) : 0.f;
+#pragma unroll
+      for (int k = 0; k < KT; ++k) {
+        const float ev = exp2f(S[k][i] - M);
+        S[k][i] = ev;
+        zr[i] += ev;
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) zr[i] += __shfl_xor(zr[i], o);
+    }
+    __syncthreads();  // every lane has read rowv
+    if (n == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][grp * 4 + i] = zr[i];
+    }
+    __syncthreads();
+    if (tid < 16) {
+      float z = 0.f;
+      for (int w = 0; w < NW; ++w) z += red[w][tid];
+      rowv[tid] = (rt * 16 + tid < R) ? 1.f / z : 0.f;
+    }
+    __syncthreads();
+    float W[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) W[i] = rowv[grp * 4 + i];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      const int ti = wave + NW * k;
+      if (ti < nvt) {  // wave-uniform
+        float cs = S[k][0] * W[0] + S[k][1] * W[1] + S[k][2] * W[2] + S[k][3] * W[3];
+        cs += __shfl_xor(cs, 16);
+        cs += __shfl_xor(cs, 32);
+        const int c = ti * 16 + n;
+        if (grp == 0 && c < Nv) colacc[c] += cs;
+      }
+    }
+    __syncthreads();  // red / rowv are reused by the next row tile
   }
+  if (rt0 < nrt) {
+    float *part = ws.part + ((size_t)u * rt_grid + rt0) * Nv;
+    for (int c = tid; c < Nv; c += kRowsThreads) store_coherent(&part[c], colacc[c]);
+  }
+  wait_all_memory();
+  __syncthreads();
+  if (tid == 0) flag = (counter_add(&ws.cnt_lb[lb], 1u) == (unsigned)(sh.Hkv * rt_grid) - 1);
+  __syncthreads();
+  if (!flag) return;
+
+  // Last workgroup of (l, b): I_v = sum of the row-tile partials over KV heads
+  // and row tiles (ascending), divided by H_q * N_tk.
+  acquire_device();
+  const int nact = min(nrt, rt_grid);
+  const float inv_rows = (ntk > 0) ? 1.f / (float)(sh.Hq * ntk) : 0.f;
+  const int np = sh.Hkv * nact;  // partials per column, summed in (KV head, row tile) order
+  for (int c = tid; c < Nv; c += kRowsThreads) {
+    float a = 0.f;
+    for (int i0 = 0; i0 < np; i0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {  // eight independent loads in flight
+        const int i = i0 + j, gg = i / nact, t = i - gg * nact;
+        v[j] = (i < np) ? ws.part[(((size_t)lb * sh.Hkv + gg) * rt_grid + t) * Nv + c] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a += v[j];
+    }
+    a *= inv_rows;
+    colacc[c] = a;
+    plan.iv[(size_t)lb * Nv + c] = a;
+  }
+  __syncthreads();
+  finish_layer_sample<kRowsThreads>(sh, plan, ws, lb, colacc);
 }
 
 // Block-wide exclusive scan for 1024 threads; returns the exclusive prefix and
@@ -480,20 +792,26 @@ __device__ __forceinline__ int block_excl_scan_1024(int v, int *wtot, int *total
 
 // ----------------------------------------------------------------------------
 // Step 5: top-r_hat selection per (layer, sample). I_v >= 0, so the raw
-// float32 bits order like the values; a 4-pass MSB-first radix select (8 bits
-// per pass, LDS histogram) finds the key T of the r_hat-th largest score. Kept:
-// every key > T, plus the lowest-index keys equal to T up to r_hat in total;
+// float32 bits order like the values. MSB-first radix select finds the key T
+// of the r_hat-th largest score: the bits above the highest bit in which the
+// minimum and maximum keys differ are common to all keys and skipped; each
+// pass histograms the next (up to) 8 bits of the keys that match the prefix
+// found so far, in per-wave LDS histograms merged in a fixed order. Kept:
+// every key > T, plus the lowest-index keys equal to T up to r_hat in total,
 // written in ascending index order by block scans. Each thread holds a
 // contiguous run of indices.
 // ----------------------------------------------------------------------------
 constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kTopkPer = 8;  // N_v <= 8192
 
 __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(Shape sh, PlanPtrs plan) {
-  __shared__ unsigned hist[256];
-  __shared__ int wtot[16];
+  __shared__ unsigned hist[kTopkWaves][256];
+  __shared__ unsigned tot[256];
+  __shared__ int wtot[kTopkWaves];
+  __shared__ unsigned wmin[kTopkWaves], wmax[kTopkWaves];
   __shared__ unsigned sel_digit, sel_above;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lb = blockIdx.x;
   const int Nv = sh.Nv;
   if (tid == 0 && plan.n_elite[lb] > sh.cap) atomicOr(plan.status, AIRCACHE_DEV_ELITE_OVERFLOW);
@@ -507,31 +825,63 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(Shape sh, Pla
     return;
   }
   unsigned key[kTopkPer];
+  unsigned kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int p = 0; p < kTopkPer; ++p) {
     const int i = i0 + p;
     key[p] = (i < i1) ? __float_as_uint(plan.iv[(size_t)lb * Nv + i]) : 0u;
+    if (i < i1) {
+      kmin = min(kmin, key[p]);
+      kmax = max(kmax, key[p]);
+    }
   }
-  unsigned prefix = 0, mask = 0;
-  int need = kbud;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    if (tid < 256) hist[tid] = 0;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmin = min(kmin, (unsigned)__shfl_xor((int)kmin, o));
+    kmax = max(kmax, (unsigned)__shfl_xor((int)kmax, o));
+  }
+  if (lane == 0) {
+    wmin[wave] = kmin;
+    wmax[wave] = kmax;
+  }
+  __syncthreads();
+  kmin = wmin[0];
+  kmax = wmax[0];
+  for (int w = 1; w < kTopkWaves; ++w) {
+    kmin = min(kmin, wmin[w]);
+    kmax = max(kmax, wmax[w]);
+  }
+  const unsigned diff = kmin ^ kmax;
+  int hb = diff ? 31 - __clz((int)diff) : -1;  // highest bit in which keys can differ
+  unsigned mask = (hb < 0) ? 0xffffffffu : (hb >= 31) ? 0u : ~((2u << hb) - 1u);
+  unsigned prefix = kmin & mask;
+  int need = kbud;  // keys still to take among those matching prefix
+  while (hb >= 0) {
+    const int width = min(8, hb + 1);
+    const int shift = hb + 1 - width;
+    const unsigned dmask = (1u << width) - 1u;
+    for (int i = tid; i < kTopkWaves * 256; i += kTopkThreads) (&hist[0][0])[i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < kTopkPer; ++p)
-      if (i0 + p < i1 && (key[p] & mask) == prefix) atomicAdd(&hist[(key[p] >> shift) & 255u], 1u);
+      if (i0 + p < i1 && (key[p] & mask) == prefix) atomicAdd(&hist[wave][(key[p] >> shift) & dmask], 1u);
+    __syncthreads();
+    if (tid < 256) {
+      unsigned c = 0;
+      for (int w = 0; w < kTopkWaves; ++w) c += hist[w][tid];
+      tot[tid] = c;
+    }
     __syncthreads();
     if (tid < 64) {
-      // lane owns digits 255-4*lane .. 252-4*lane (descending); suffix counts
+      // lane owns digits 255-4*lane .. 252-4*lane (descending)
       unsigned c[4], s4 = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        c[q] = hist[255 - 4 * lane - q];
+        c[q] = tot[255 - 4 * lane - q];
         s4 += c[q];
       }
-      const int incl = wave_incl_scan((int)s4);  // count of digits >= this lane's lowest
-      unsigned above = (unsigned)(incl - (int)s4);  // count of digits above this lane's highest
+      const int incl = wave_incl_scan((int)s4);
+      unsigned above = (unsigned)(incl - (int)s4);  // keys with a larger digit
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (above < (unsigned)need && above + c[q] >= (unsigned)need) {
@@ -543,16 +893,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(Shape sh, Pla
     }
     __syncthreads();
     prefix |= sel_digit << shift;
-    mask |= 255u << shift;
+    mask |= dmask << shift;
     need -= (int)sel_above;
+    hb -= width;
     __syncthreads();
   }
   const unsigned T = prefix;
   int neq = 0;
 #pragma unroll
   for (int p = 0; p < kTopkPer; ++p) neq += (i0 + p < i1 && key[p] == T) ? 1 : 0;
-  int tot;
-  int eq_rank = block_excl_scan_1024(neq, wtot, &tot);
+  int total;
+  int eq_rank = block_excl_scan_1024(neq, wtot, &total);
   int nkeep = 0;
   unsigned keepbits = 0;
 #pragma unroll
@@ -569,11 +920,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(Shape sh, Pla
       }
     }
   }
-  int pos = block_excl_scan_1024(nkeep, wtot, &tot);
+  int pos = block_excl_scan_1024(nkeep, wtot, &total);
 #pragma unroll
   for (int p = 0; p < kTopkPer; ++p)
     if (keepbits & (1u << p)) kept[pos++] = i0 + p;
-  (void)lane;
 }
 
 // ----------------------------------------------------------------------------
@@ -642,10 +992,15 @@ constexpr size_t kMaxLds = 160 * 1024;
 
 struct Config {
   Shape sh;
-  size_t off_cnt, off_stats, off_e, ws_bytes;
-  size_t elite_lds, score_lds, final_lds;
+  size_t off_cnt, off_stats, off_e, off_part, ws_bytes;
+  size_t elite_lds, score_lds, final_lds, rows_lds;
   int ktw;
+  int rows_kt;  // key tiles per wave of cross_score_rows_kernel; 0: the tiled path with spilled exponentials
+  int rt_grid, units;
 };
+
+// Register budgets of cross_score_rows_kernel instantiations (key tiles per wave).
+constexpr int kRowsKt[] = {4, 8, 16};
 
 int make_config(const aircache_desc *d, Config *cfg) {
   g_last_error.clear();
@@ -665,7 +1020,7 @@ int make_config(const aircache_desc *d, Config *cfg) {
   if (!(d->ratio >= 0.0 && d->ratio <= 1.0)) return fail(AIRCACHE_EINVAL, "ratio=%g outside [0, 1]", d->ratio);
   if (d->max_elite < 0 || d->max_elite > d->n_txt)
     return fail(AIRCACHE_EINVAL, "max_elite=%d outside [0, n_txt=%d]", d->max_elite, d->n_txt);
-  if (d->reserved != 0) return fail(AIRCACHE_EINVAL, "reserved field must be 0");
+  if (d->path < AIRCACHE_PATH_AUTO || d->path > AIRCACHE_PATH_ROWS) return fail(AIRCACHE_EINVAL, "path=%d unknown", d->path);
   Shape &s = cfg->sh;
   s.L = d->n_layers;
   s.B = d->batch;
@@ -691,19 +1046,46 @@ int make_config(const aircache_desc *d, Config *cfg) {
   s.ratio = d->ratio;
   const int esz = d->dtype == AIRCACHE_BF16 ? 2 : 4;
   (void)esz;
-  cfg->elite_lds = (size_t)17 * s.Nt * sizeof(float);
+  cfg->elite_lds = ((size_t)s.Hq + 1) * s.Nt * sizeof(float);
   cfg->score_lds = (size_t)s.cap * sizeof(int);
   cfg->final_lds = ((size_t)s.Hkv * s.rcap16 + s.Nv) * sizeof(float);
-  if (cfg->elite_lds > kMaxLds) return fail(AIRCACHE_EINVAL, "n_txt=%d too large for the elite stage", s.Nt);
+  if (cfg->elite_lds > kMaxLds)
+    return fail(AIRCACHE_EINVAL, "(n_q_heads + 1) * n_txt = %lld too large for the elite stage (max %zu)",
+                ((long long)s.Hq + 1) * s.Nt, kMaxLds / sizeof(float));
   if (cfg->score_lds > kMaxLds || cfg->final_lds > kMaxLds)
     return fail(AIRCACHE_EINVAL, "n_q_heads * max_elite too large (%lld rows); lower max_elite",
                 (long long)s.Hq * s.cap);
   const size_t units = (size_t)s.L * s.B * s.Hkv;
   const size_t n_cnt = (size_t)s.L * s.B + s.B + 1;
+  cfg->units = (int)units;
+  // Row-complete scoring when the visual keys plus the largest elite window
+  // fit in the registers of one 8-wave workgroup.
+  const int tiles_needed = (s.Nv + 15) / 16;
+  cfg->rows_kt = 0;
+  for (int kt : kRowsKt)
+    if (kRowsWaves * kt >= tiles_needed) {
+      cfg->rows_kt = kt;
+      break;
+    }
+  const long long rt_need = ((long long)s.G * s.cap + 15) / 16;
+  cfg->rt_grid = (int)(rt_need < 1 ? 1 : (rt_need > 4 ? 4 : rt_need));
+  const size_t tile_bytes = (size_t)16 * s.D * (d->dtype == AIRCACHE_BF16 ? 2 : 4);
+  cfg->rows_lds = (size_t)kRowsWaves * 2 * tile_bytes + ((size_t)s.Nv + s.cap) * sizeof(float);
+  if (cfg->rows_kt && cfg->rows_lds > kMaxLds) cfg->rows_kt = 0;
+  if (d->path == AIRCACHE_PATH_ROWS && !cfg->rows_kt)
+    return fail(AIRCACHE_EINVAL, "the rows path needs n_vis <= %d", kRowsWaves * 16 * kRowsKt[2]);
+  if (d->path == AIRCACHE_PATH_TILED) cfg->rows_kt = 0;
   cfg->off_cnt = 0;
   cfg->off_stats = align_up(n_cnt * sizeof(unsigned));
-  cfg->off_e = cfg->off_stats + align_up(units * s.rcap16 * s.ntiles * sizeof(float2));
-  cfg->ws_bytes = cfg->off_e + align_up(units * s.Nv * (size_t)s.rcap16 * sizeof(float));
+  if (cfg->rows_kt) {
+    cfg->off_e = cfg->off_stats;
+    cfg->off_part = cfg->off_stats;
+    cfg->ws_bytes = cfg->off_part + align_up(units * cfg->rt_grid * (size_t)s.Nv * sizeof(float));
+  } else {
+    cfg->off_e = cfg->off_stats + align_up(units * s.rcap16 * s.ntiles * sizeof(float2));
+    cfg->off_part = cfg->off_e;
+    cfg->ws_bytes = cfg->off_e + align_up(units * s.Nv * (size_t)s.rcap16 * sizeof(float));
+  }
   return AIRCACHE_OK;
 }
 
@@ -716,6 +1098,7 @@ Ws ws_of(const Config &cfg, void *base) {
   w.cnt_all = w.cnt_b + s.B;
   w.stats = reinterpret_cast<float2 *>(p + cfg.off_stats);
   w.e = reinterpret_cast<float *>(p + cfg.off_e);
+  w.part = reinterpret_cast<float *>(p + cfg.off_part);
   return w;
 }
 
@@ -733,24 +1116,58 @@ template <typename K> int allow_lds(K kernel, size_t bytes) {
                    "hipFuncSetAttribute");
 }
 
-template <typename Tag, int D, int KTW>
-int launch_plan(const Config &cfg, const LayerTable &qt, const LayerTable &kt, const PlanPtrs &pp, const Ws &ws,
+// Optional instrumentation: when ev is non-NULL, ev[i] is recorded on the
+// stream right before the i-th kernel and ev[n] after the last one.
+int mark(hipEvent_t *ev, int i, hipStream_t st) {
+  if (!ev) return AIRCACHE_OK;
+  return check_hip(hipEventRecord(ev[i], st), "hipEventRecord");
+}
+
+template <typename Tag, int D, int KT>
+int launch_rows(const Config &cfg, const LayerTable &qt, const LayerTable &kt, const PlanPtrs &pp, const Ws &ws,
                 hipStream_t st) {
   const Shape &s = cfg.sh;
   int rc;
+  if ((rc = allow_lds(cross_score_rows_kernel<Tag, D, KT>, cfg.rows_lds))) return rc;
+  const unsigned u8 = (unsigned)((cfg.units + 7) / 8 * 8);
+  hipLaunchKernelGGL((cross_score_rows_kernel<Tag, D, KT>), dim3(u8 * cfg.rt_grid), dim3(kRowsThreads), cfg.rows_lds,
+                     st, s, qt, kt, pp, ws, cfg.rt_grid, cfg.units);
+  return check_hip(hipGetLastError(), "cross_score_rows_kernel launch");
+}
+
+template <typename Tag, int D, int KTW>
+int launch_plan(const Config &cfg, const LayerTable &qt, const LayerTable &kt, const PlanPtrs &pp, const Ws &ws,
+                hipStream_t st, hipEvent_t *ev) {
+  const Shape &s = cfg.sh;
+  int rc;
   if ((rc = allow_lds(elite_select_kernel<Tag, D>, cfg.elite_lds))) return rc;
-  if ((rc = allow_lds(cross_score_kernel<Tag, D, KTW>, cfg.score_lds))) return rc;
-  if ((rc = allow_lds(finalize_kernel, cfg.final_lds))) return rc;
   const unsigned nlb = (unsigned)(s.L * s.B);
-  hipLaunchKernelGGL((elite_select_kernel<Tag, D>), dim3(nlb), dim3(256), cfg.elite_lds, st, s, qt, kt, pp, ws);
+  if ((rc = mark(ev, 0, st))) return rc;
+  hipLaunchKernelGGL((elite_select_kernel<Tag, D>), dim3(nlb), dim3(kEliteThreads), cfg.elite_lds, st, s, qt, kt, pp,
+                     ws);
   if ((rc = check_hip(hipGetLastError(), "elite_select_kernel launch"))) return rc;
-  hipLaunchKernelGGL((cross_score_kernel<Tag, D, KTW>), dim3(nlb * s.Hkv * s.ntiles), dim3(256), cfg.score_lds, st, s,
-                     qt, kt, pp, ws);
-  if ((rc = check_hip(hipGetLastError(), "cross_score_kernel launch"))) return rc;
-  hipLaunchKernelGGL(finalize_kernel, dim3(nlb * s.ntiles), dim3(256), cfg.final_lds, st, s, pp, ws);
-  if ((rc = check_hip(hipGetLastError(), "finalize_kernel launch"))) return rc;
+  if ((rc = mark(ev, 1, st))) return rc;
+  if (cfg.rows_kt) {
+    // scoring, statistics and budgets in one launch; the finalize stage is empty
+    if (cfg.rows_kt == 4) rc = launch_rows<Tag, D, 4>(cfg, qt, kt, pp, ws, st);
+    else if (cfg.rows_kt == 8) rc = launch_rows<Tag, D, 8>(cfg, qt, kt, pp, ws, st);
+    else rc = launch_rows<Tag, D, 16>(cfg, qt, kt, pp, ws, st);
+    if (rc) return rc;
+    if ((rc = mark(ev, 2, st))) return rc;
+  } else {
+    if ((rc = allow_lds(cross_score_kernel<Tag, D, KTW>, cfg.score_lds))) return rc;
+    if ((rc = allow_lds(finalize_kernel, cfg.final_lds))) return rc;
+    hipLaunchKernelGGL((cross_score_kernel<Tag, D, KTW>), dim3(nlb * s.Hkv * s.ntiles), dim3(256), cfg.score_lds,
+                       st, s, qt, kt, pp, ws);
+    if ((rc = check_hip(hipGetLastError(), "cross_score_kernel launch"))) return rc;
+    if ((rc = mark(ev, 2, st))) return rc;
+    hipLaunchKernelGGL(finalize_kernel, dim3(nlb * s.ntiles), dim3(256), cfg.final_lds, st, s, pp, ws);
+    if ((rc = check_hip(hipGetLastError(), "finalize_kernel launch"))) return rc;
+  }
+  if ((rc = mark(ev, 3, st))) return rc;
   hipLaunchKernelGGL(topk_select_kernel, dim3(nlb), dim3(kTopkThreads), 0, st, s, pp);
-  return check_hip(hipGetLastError(), "topk_select_kernel launch");
+  if ((rc = check_hip(hipGetLastError(), "topk_select_kernel launch"))) return rc;
+  return mark(ev, 4, st);
 }
 
 PlanPtrs plan_ptrs(const aircache_plan_buf *p) {
@@ -809,8 +1226,12 @@ int64_t aircache_max_compacted_elems(const aircache_desc *desc) {
   return (int64_t)s.B * s.Hkv * (int64_t)(s.Nv + s.Nt) * s.D;
 }
 
-int aircache_plan(const aircache_desc *desc, const void *const *q_txt, const void *const *k,
-                  const aircache_plan_buf *plan, void *workspace, size_t ws_bytes, void *stream) {
+int aircache_plan_profiled(const aircache_desc *desc, const void *const *q_txt, const void *const *k,
+                           const aircache_plan_buf *plan, void *workspace, size_t ws_bytes, void *stream,
+                           void *const *events, int n_events) {
+  if (events && n_events != AIRCACHE_PLAN_KERNELS + 1)
+    return fail(AIRCACHE_EINVAL, "n_events=%d, expected %d", n_events, AIRCACHE_PLAN_KERNELS + 1);
+  hipEvent_t *ev = events ? reinterpret_cast<hipEvent_t *>(const_cast<void **>(events)) : nullptr;
   Config cfg;
   int rc;
   if ((rc = make_config(desc, &cfg))) return rc;
@@ -826,14 +1247,23 @@ int aircache_plan(const aircache_desc *desc, const void *const *q_txt, const voi
   const Ws ws = ws_of(cfg, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = desc->dtype == AIRCACHE_BF16;
-  if (bf && cfg.sh.D == 128) return launch_plan<Bf16Tag, 128, 4>(cfg, qt, kt, pp, ws, st);
-  if (bf && cfg.sh.D == 64) return launch_plan<Bf16Tag, 64, 4>(cfg, qt, kt, pp, ws, st);
-  if (!bf && cfg.sh.D == 128) return launch_plan<F32Tag, 128, 2>(cfg, qt, kt, pp, ws, st);
-  return launch_plan<F32Tag, 64, 2>(cfg, qt, kt, pp, ws, st);
+  if (bf && cfg.sh.D == 128) return launch_plan<Bf16Tag, 128, 4>(cfg, qt, kt, pp, ws, st, ev);
+  if (bf && cfg.sh.D == 64) return launch_plan<Bf16Tag, 64, 4>(cfg, qt, kt, pp, ws, st, ev);
+  if (!bf && cfg.sh.D == 128) return launch_plan<F32Tag, 128, 2>(cfg, qt, kt, pp, ws, st, ev);
+  return launch_plan<F32Tag, 64, 2>(cfg, qt, kt, pp, ws, st, ev);
 }
 
-int aircache_compress(const aircache_desc *desc, const aircache_plan_buf *plan, const void *const *k,
-                      const void *const *v, void *const *k_out, void *const *v_out, void *stream) {
+int aircache_plan(const aircache_desc *desc, const void *const *q_txt, const void *const *k,
+                  const aircache_plan_buf *plan, void *workspace, size_t ws_bytes, void *stream) {
+  return aircache_plan_profiled(desc, q_txt, k, plan, workspace, ws_bytes, stream, nullptr, 0);
+}
+
+int aircache_compress_profiled(const aircache_desc *desc, const aircache_plan_buf *plan, const void *const *k,
+                               const void *const *v, void *const *k_out, void *const *v_out, void *stream,
+                               void *const *events, int n_events) {
+  if (events && n_events != AIRCACHE_COMPRESS_KERNELS + 1)
+    return fail(AIRCACHE_EINVAL, "n_events=%d, expected %d", n_events, AIRCACHE_COMPRESS_KERNELS + 1);
+  hipEvent_t *ev = events ? reinterpret_cast<hipEvent_t *>(const_cast<void **>(events)) : nullptr;
   Config cfg;
   int rc;
   if ((rc = make_config(desc, &cfg))) return rc;
@@ -871,13 +1301,20 @@ int aircache_compress(const aircache_desc *desc, const aircache_plan_buf *plan, 
   const int rb = s.D * esz;
   const int64_t cap = (int64_t)s.B * s.Hkv * s.S * s.D;
   const dim3 grid((unsigned)(units * nch));
+  if ((rc = mark(ev, 0, st))) return rc;
   if (rb == 128)
     hipLaunchKernelGGL(kv_gather_kernel<128>, grid, dim3(256), 0, st, s, tb, pp, nch, esz, cap);
   else if (rb == 256)
     hipLaunchKernelGGL(kv_gather_kernel<256>, grid, dim3(256), 0, st, s, tb, pp, nch, esz, cap);
   else
     hipLaunchKernelGGL(kv_gather_kernel<512>, grid, dim3(256), 0, st, s, tb, pp, nch, esz, cap);
-  return check_hip(hipGetLastError(), "kv_gather_kernel launch");
+  if ((rc = check_hip(hipGetLastError(), "kv_gather_kernel launch"))) return rc;
+  return mark(ev, 1, st);
+}
+
+int aircache_compress(const aircache_desc *desc, const aircache_plan_buf *plan, const void *const *k,
+                      const void *const *v, void *const *k_out, void *const *v_out, void *stream) {
+  return aircache_compress_profiled(desc, plan, k, v, k_out, v_out, stream, nullptr, 0);
 }
 
 const char *aircache_strerror(int status) {

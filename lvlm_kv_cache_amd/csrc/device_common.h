@@ -110,9 +110,75 @@ template <typename T> __device__ __forceinline__ T load_coherent(const T *p) {
 __device__ __forceinline__ unsigned counter_add(unsigned *p, unsigned v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Acquire at device scope: after it, ordinary loads observe every value that
+// another workgroup published with store_coherent before its counter update
+// (invalidates this CU's L1 and the XCD's non-coherent L2 lines). Used once
+// per elected finisher, so its reads can be ordinary, batched loads instead
+// of one atomic load at a time.
+__device__ __forceinline__ void acquire_device() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
 __device__ __forceinline__ void store_nt(u32x4_t *p, u32x4_t v) { __builtin_nontemporal_store(v, p); }
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (vector memory operations complete in issue order). Also a compiler memory
+// fence, so no LDS access is moved across it.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// Wait until every LDS access of this wave has completed (before an LDS-DMA
+// load overwrites a region the wave just read); also a compiler memory fence.
+__device__ __forceinline__ void wait_lds_reads() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // vmcnt, expcnt at maximum; lgkmcnt 0
+  asm volatile("" ::: "memory");
+}
+
+// wait_vmcnt<t * PER>() for a count t in 0..3 known after unrolling.
+template <int PER> __device__ __forceinline__ void wait_tiles(int t) {
+  switch (t) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<PER>(); break;
+    case 2: wait_vmcnt<2 * PER>(); break;
+    default: wait_vmcnt<3 * PER>(); break;
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// LDS-DMA: every lane copies 16 bytes from its own global address to
+// lds + 16 * lane (gfx950 global_load_lds_dwordx4). lds must be wave-uniform.
+__device__ __forceinline__ void load_lds16(const void *gsrc, void *lds) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t *)lds, 16, 0, 0);
+}
+
+// Staging of one 16-key tile in LDS for MFMA B operands. DMA instruction j
+// (j < 16 * row_bytes / 1024) moves, for lane i, bytes [16 (i / 16) + 64 j,
+// +16) of key row i % 16 to tile + 1024 j + 16 i. The fragment of lane
+// (n = lane % 16, grp = lane / 16) for 32-element slice c is then read back as
+// whole 16-byte pieces.
+template <typename Tag> struct LdsTile;
+
+template <> struct LdsTile<Bf16Tag> {
+  // slice c of row n is bytes [64 c + 16 grp, +16): DMA j = c, lane group grp
+  __device__ static __forceinline__ void read(Frag<Bf16Tag> &f, const unsigned char *tile, int c, int lane) {
+    f.v = *reinterpret_cast<const u16x8_t *>(tile + 1024 * c + 16 * lane);
+  }
+};
+
+template <> struct LdsTile<F32Tag> {
+  // slice c of row n is bytes [128 c + 32 grp, +32): DMA j = 2c + grp / 2,
+  // lane groups 2 (grp % 2) and 2 (grp % 2) + 1
+  __device__ static __forceinline__ void read(Frag<F32Tag> &f, const unsigned char *tile, int c, int lane) {
+    const int n = lane & 15, grp = lane >> 4;
+    const unsigned char *b = tile + 1024 * (2 * c + (grp >> 1)) + 16 * (32 * (grp & 1) + n);
+    f.lo = *reinterpret_cast<const f32x4_t *>(b);
+    f.hi = *reinterpret_cast<const f32x4_t *>(b + 256);
+  }
+};
 
 }  // namespace aircache

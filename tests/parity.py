@@ -47,11 +47,11 @@ def torch_dtype(w):
     return torch.float32 if w.dtype == wl.F32 else torch.bfloat16
 
 
-def run_gpu(inp: wl.Inputs, alpha=None, ratio=None, max_elite=0, tensors=None, compress=True):
+def run_gpu(inp: wl.Inputs, alpha=None, ratio=None, max_elite=0, tensors=None, compress=True, path="auto"):
     w = inp.w
     ac = AirCache(w.L, w.B, w.Hq, w.Hkv, w.D, w.Nv, w.Nt, dtype=torch_dtype(w),
                   alpha=w.alpha if alpha is None else alpha,
-                  ratio=w.ratio if ratio is None else ratio, max_elite=max_elite)
+                  ratio=w.ratio if ratio is None else ratio, max_elite=max_elite, path=path)
     q, k, v = tensors if tensors is not None else to_torch(inp)
     plan = ac.plan(q, k)
     out = {}

@@ -41,22 +41,25 @@ def test_struct_layouts():
 
 def desc(**kw):
     base = dict(n_layers=28, batch=1, n_q_heads=28, n_kv_heads=4, head_dim=128, n_vis=2880,
-                n_txt=128, dtype="bf16", alpha=0.9, ratio=0.1, max_elite=0)
+                n_txt=128, dtype="bf16", alpha=0.9, ratio=0.1, max_elite=0, path=0)
     base.update(kw)
     return make_desc(*[base[k] for k in ("n_layers", "batch", "n_q_heads", "n_kv_heads", "head_dim",
-                                         "n_vis", "n_txt", "dtype", "alpha", "ratio", "max_elite")])
+                                         "n_vis", "n_txt", "dtype", "alpha", "ratio", "max_elite", "path")])
 
 
 def test_workspace_size(lib):
     assert _lib.workspace_size(desc()) > 0
-    assert _lib.workspace_size(desc(max_elite=8)) < _lib.workspace_size(desc())
+    # the tiled path spills exponentials for up to max_elite elite rows
+    assert _lib.workspace_size(desc(max_elite=8, path=1)) < _lib.workspace_size(desc(path=1))
+    assert _lib.workspace_size(desc(path=2)) < _lib.workspace_size(desc(path=1))
     assert _lib.max_compacted_elems(desc()) == 1 * 4 * 3008 * 128
 
 
 @pytest.mark.parametrize("bad", [dict(n_layers=0), dict(n_layers=129), dict(batch=0), dict(n_kv_heads=5),
                                  dict(head_dim=96), dict(n_vis=2), dict(n_vis=9000), dict(n_txt=0),
                                  dict(dtype="x"), dict(alpha=1.5), dict(alpha=float("nan")),
-                                 dict(ratio=-0.1), dict(max_elite=129), dict(n_txt=4000)])
+                                 dict(ratio=-0.1), dict(max_elite=129), dict(n_txt=4000), dict(path=3),
+                                 dict(path=2, n_vis=4000)])
 def test_invalid_descriptor(lib, bad):
     if bad.get("dtype") == "x":
         d = desc()

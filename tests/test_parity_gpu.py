@@ -38,6 +38,14 @@ def test_workload(cid, seed):
     print(f"[parity] workload {cid} seed {seed}: {rep}", flush=True)
 
 
+@pytest.mark.parametrize("cid", [1, 2, 3, 5])
+def test_workload_tiled_path(cid):
+    """The general tiled path on the workloads the rows path serves by default."""
+    inp = wl.make_inputs(cid, cid)
+    g = run_gpu(inp, max_elite=0 if cid <= 2 else 64, path="tiled")
+    compare(inp, g, reference(inp, g))
+
+
 EDGE = [
     dict(Nv=17, Nt=3, Hq=1, Hkv=1, D=64, dtype="f32"),
     dict(Nv=3, Nt=1, Hq=2, Hkv=1, D=64, dtype="bf16"),
@@ -51,10 +59,11 @@ EDGE = [
 
 @pytest.mark.parametrize("shape", EDGE, ids=lambda s: "x".join(f"{k}{v}" for k, v in s.items()))
 @pytest.mark.parametrize("seed", [0, 1])
-def test_edge_shapes(shape, seed):
+@pytest.mark.parametrize("path", ["auto", "tiled"])
+def test_edge_shapes(shape, seed, path):
     w = wl.custom(ratio=0.2, **shape)
     inp = wl.make_inputs(w, seed)
-    g = run_gpu(inp)
+    g = run_gpu(inp, path=path)
     compare(inp, g, reference(inp, g))
 
 
