@@ -47,7 +47,8 @@ struct PlanPtrs {
 };
 
 struct Ws {
-  unsigned *cnt_lb;   // [L*B] finished scoring tiles per (l, b)
+  unsigned *cnt_unit; // [L*B*Hkv] finished row tiles per (l, b, g)
+  unsigned *cnt_lb;   // [L*B] finished scoring tiles (tiled path) or KV heads (rows path) per (l, b)
   unsigned *cnt_b;    // [B]   finished layers per sample
   unsigned *cnt_all;  // [1]   finished samples
   float2 *stats;      // [units][rcap16][ntiles] (tile max, tile sum) per row, base 2
@@ -91,6 +92,7 @@ __global__ __launch_bounds__(kEliteThreads) void elite_select_kernel(Shape sh, L
   float *pbar = lds + (size_t)sh.Hq * Nt;
 
   // This kernel opens every plan: reset the counters of finalize_kernel.
+  for (int g = tid; g < sh.Hkv; g += kEliteThreads) ws.cnt_unit[(size_t)lb * sh.Hkv + g] = 0;
   if (tid == 0) {
     ws.cnt_lb[lb] = 0;
     if (l == 0) ws.cnt_b[b] = 0;
@@ -349,28 +351,33 @@ __global__ __launch_bounds__(256) void cross_score_kernel(Shape sh, LayerTable q
 
 // Budget of every layer of one sample ("Layer-wise KV Cache Budget
 // Allocation", the r_hat equation with the cross-layer normalisation reading
-// documented in aircache.h), from the sample's L statistics already in LDS.
-// Plain double arithmetic in a fixed order with no fused multiply-add, so the
-// same statistics give the same integers anywhere.
-__device__ void sample_budgets(const Shape &sh, const double *st, const double *sk, double *x_out, int *b_out) {
+// documented in aircache.h). The three sums over layers run in ascending layer
+// order on one thread; each layer's value is then formed independently. Plain
+// double arithmetic with no fused multiply-add, so the same statistics give
+// the same integers anywhere.
+struct BudgetSums {
+  double st_sum, mshift, u_sum;
+};
+__device__ BudgetSums budget_sums(int L, const double *st, const double *sk) {
 #pragma clang fp contract(off)
-  const int L = sh.L;
-  double st_sum = 0.0, mshift = 0.0, u_sum = 0.0;
-  for (int l = 0; l < L; ++l) st_sum += st[l];
+  BudgetSums r{0.0, 0.0, 0.0};
+  for (int l = 0; l < L; ++l) r.st_sum += st[l];
   for (int l = 0; l < L; ++l)
-    if (sk[l] < mshift) mshift = sk[l];
-  for (int l = 0; l < L; ++l) u_sum += sk[l] - mshift;
-  const double r = sh.ratio * (double)sh.Nv;
-  for (int l = 0; l < L; ++l) {
-    const double stn = st[l] * (double)L / st_sum;
-    const double skn = (u_sum > 0.0) ? (sk[l] - mshift) * (double)L / u_sum : 1.0;
-    const double x = 0.5 * (stn + skn) * r;
-    double f = floor(x);
-    if (!(f > 0.0)) f = 0.0;
-    if (f > (double)sh.Nv) f = (double)sh.Nv;
-    x_out[l] = x;
-    b_out[l] = (int)f;
-  }
+    if (sk[l] < r.mshift) r.mshift = sk[l];
+  for (int l = 0; l < L; ++l) r.u_sum += sk[l] - r.mshift;
+  return r;
+}
+__device__ void layer_budget(const Shape &sh, const BudgetSums &r, double st, double sk, double *x_out, int *b_out) {
+#pragma clang fp contract(off)
+  const double rr = sh.ratio * (double)sh.Nv;
+  const double stn = st * (double)sh.L / r.st_sum;
+  const double skn = (r.u_sum > 0.0) ? (sk - r.mshift) * (double)sh.L / r.u_sum : 1.0;
+  const double x = 0.5 * (stn + skn) * rr;
+  double f = floor(x);
+  if (!(f > 0.0)) f = 0.0;
+  if (f > (double)sh.Nv) f = (double)sh.Nv;
+  *x_out = x;
+  *b_out = (int)f;
 }
 
 // The last workgroup to finish a (layer, sample) runs this with the layer's
@@ -385,8 +392,8 @@ template <int NT>
 __device__ void finish_layer_sample(const Shape &sh, const PlanPtrs &plan, const Ws &ws, int lb, const float *ivc) {
   constexpr int NW = NT / 64;
   __shared__ double redd[NW];
-  __shared__ double lst[AIRCACHE_MAX_LAYERS], lsk[AIRCACHE_MAX_LAYERS], lx[AIRCACHE_MAX_LAYERS];
-  __shared__ int lbud[AIRCACHE_MAX_LAYERS];
+  __shared__ double lst[AIRCACHE_MAX_LAYERS], lsk[AIRCACHE_MAX_LAYERS];
+  __shared__ BudgetSums sums;
   __shared__ int flag;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Nv = sh.Nv, b = lb % sh.B;
@@ -430,17 +437,23 @@ __device__ void finish_layer_sample(const Shape &sh, const PlanPtrs &plan, const
 
   // Last layer of sample b: budgets of all its layers.
   const int L = sh.L, B = sh.B;
-  acquire_device();
-  for (int l = tid; l < L; l += NT) {
-    lst[l] = plan.s_t[l * B + b];
-    lsk[l] = plan.s_k[l * B + b];
+  {
+    const auto rst = coherent_rsrc(plan.s_t, (unsigned)(L * B * sizeof(double)));
+    const auto rsk = coherent_rsrc(plan.s_k, (unsigned)(L * B * sizeof(double)));
+    for (int l = tid; l < L; l += NT) {
+      lst[l] = load_sc1_d(rst, (unsigned)((l * B + b) * sizeof(double)));
+      lsk[l] = load_sc1_d(rsk, (unsigned)((l * B + b) * sizeof(double)));
+    }
   }
   __syncthreads();
-  if (tid == 0) sample_budgets(sh, lst, lsk, lx, lbud);
+  if (tid == 0) sums = budget_sums(L, lst, lsk);
   __syncthreads();
   for (int l = tid; l < L; l += NT) {
-    if (plan.bx) store_coherent(&plan.bx[l * B + b], lx[l]);
-    store_coherent(&plan.budget[l * B + b], (int32_t)lbud[l]);
+    double x;
+    int bud;
+    layer_budget(sh, sums, lst[l], lsk[l], &x, &bud);
+    if (plan.bx) store_coherent(&plan.bx[l * B + b], x);
+    store_coherent(&plan.budget[l * B + b], (int32_t)bud);
   }
   wait_all_memory();
   __syncthreads();
@@ -449,12 +462,12 @@ __device__ void finish_layer_sample(const Shape &sh, const PlanPtrs &plan, const
   if (!flag) return;
 
   // Last sample: element offsets of every sample's segment in each layer.
-  acquire_device();
+  const auto rbud = coherent_rsrc(plan.budget, (unsigned)(L * B * sizeof(int32_t)));
   for (int l = tid; l < L; l += NT) {
     int64_t off = 0;
     for (int bb = 0; bb < B; ++bb) {
       plan.out_off[(size_t)l * (B + 1) + bb] = off;
-      off += (int64_t)sh.Hkv * (plan.budget[l * B + bb] + sh.Nt) * sh.D;
+      off += (int64_t)sh.Hkv * (load_sc1_i(rbud, (unsigned)((l * B + bb) * sizeof(int32_t))) + sh.Nt) * sh.D;
     }
     plan.out_off[(size_t)l * (B + 1) + B] = off;
   }
@@ -538,67 +551,83 @@ __global__ __launch_bounds__(256) void finalize_kernel(Shape sh, PlanPtrs plan, 
   if (!flag) return;
 
   float *ivc = wl + sh.Hkv * sh.rcap16;
-  acquire_device();
-  for (int c = tid; c < sh.Nv; c += 256) ivc[c] = plan.iv[(size_t)lb * sh.Nv + c];
+  const auto riv = coherent_rsrc(plan.iv + (size_t)lb * sh.Nv, (unsigned)(sh.Nv * sizeof(float)));
+  for (int c = tid; c < sh.Nv; c += 256) ivc[c] = load_sc1_f(riv, (unsigned)(c * sizeof(float)));
   __syncthreads();
   finish_layer_sample<256>(sh, plan, ws, lb, ivc);
 }
 
 // ----------------------------------------------------------------------------
 // Steps 2 + 3 + 4 in one launch when a whole row of logits fits in registers
-// (N_v + elite text keys <= 8 waves x 16 x KT): one workgroup of 8 waves per
-// (layer, sample, KV head, row tile of 16 elite-query rows). The elite
-// queries are the MFMA A operand, 16 keys at a time the B operand; wave w owns
-// key tiles w, w + 8, ... (visual tiles first, then elite text tiles), keeps
-// their logits in registers, and the exact row max and row sum come from
-// in-lane, cross-lane and cross-wave reductions in a fixed order. Column sums
-// of exp2(S - M) / Z over the tile's rows are accumulated in LDS, written to
-// the workspace as this row tile's partial I_v, and the last workgroup of the
-// (layer, sample) adds the partials in a fixed order and runs the finisher.
-// Workgroups are numbered so that the rt_grid row tiles of one (l, b, g) sit
-// on one XCD (round-robin dispatch over the 8 XCDs) and share K through L2.
+// (N_v <= 8 waves x 16 x KT). A persistent grid of one 8-wave workgroup per
+// CU walks the work items (layer-sample, KV head, row tile of 16 elite-query
+// rows) in order; the item count of each (layer, sample) follows from its
+// elite count. Per item: the elite queries are the MFMA A operand and 16 keys
+// at a time the B operand; wave w owns visual key tiles w, w + 8, ..., which
+// stream through a per-wave LDS ring by DMA and whose logits stay in
+// registers; the few elite text keys enter the row max and row sum through an
+// online update. Exact row max and sum come from DPP row reductions, then a
+// fixed-order sum over the waves. Each wave writes the column sums of
+// exp2(S - M) / Z over the tile's rows for its key tiles as this item's partial
+// I_v; the last item of a (layer, sample) adds the partials in a fixed order
+// and runs the statistics and budget finisher.
 // ----------------------------------------------------------------------------
-constexpr int kRowsThreads = 768;
+constexpr int kRowsThreads = 512;
 constexpr int kRowsWaves = kRowsThreads / 64;
+
+// LDS ring depth: up to 4 tiles per wave within 128 KB of LDS.
+template <typename Tag, int D> constexpr int rows_ring() {
+  return (131072 / (kRowsWaves * 16 * D * Tag::kBytes)) < 4 ? (131072 / (kRowsWaves * 16 * D * Tag::kBytes)) : 4;
+}
 
 template <typename Tag, int D, int KT>
 __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh, LayerTable qt, LayerTable kt,
-                                                                        PlanPtrs plan, Ws ws, int rt_grid,
-                                                                        int units) {
+                                                                        PlanPtrs plan, Ws ws, int rt_max) {
   using E = typename Tag::store_t;
   constexpr int NW = kRowsWaves;
   constexpr int kTileBytes = 16 * D * Tag::kBytes;  // one 16-key tile
   constexpr int kDma = kTileBytes / 1024;           // 16-byte DMA loads per lane per tile
-  constexpr int kRing = 2;                          // tiles in flight per wave
+  constexpr int kRing = rows_ring<Tag, D>();        // tiles in flight per wave
   static_assert(KT >= kRing, "ring deeper than the tile count");
-  extern __shared__ float dyn[];  // ring[NW][kRing][kTileBytes], colacc[Nv] (reused for I_v), el[cap]
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];  // ring[NW][kRing][tile] | el[cap]
   __shared__ float red[NW][16];
   __shared__ float rowv[16];
   __shared__ int flag;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, grp = lane >> 4;
-  const int xcd = blockIdx.x & 7, loc = blockIdx.x >> 3;
-  const int u = (loc / rt_grid) * 8 + xcd, rt0 = loc % rt_grid;
-  if (u >= units) return;
-  const int g = u % sh.Hkv, lb = u / sh.Hkv, l = lb / sh.B, b = lb % sh.B;
-  const int Nv = sh.Nv;
-  unsigned char *ring = reinterpret_cast<unsigned char *>(dyn) + (size_t)wave * kRing * kTileBytes;
-  float *colacc = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(dyn) + (size_t)NW * kRing * kTileBytes);
-  int *el = reinterpret_cast<int *>(colacc + Nv);
-  int ntk = plan.n_elite[lb];
-  if (ntk > sh.cap) ntk = sh.cap;
-  if (ntk < 0) ntk = 0;
-  const int R = sh.G * ntk;
-  const int nrt = (R + 15) >> 4;
-  for (int i = tid; i < ntk; i += kRowsThreads) el[i] = plan.elite[(size_t)lb * sh.Nt + i];
-  for (int c = tid; c < Nv; c += kRowsThreads) colacc[c] = 0.f;
-  __syncthreads();
+  const int Nv = sh.Nv, LB = sh.L * sh.B;
+  unsigned char *ring = dyn + (size_t)wave * kRing * kTileBytes;
+  int *el = reinterpret_cast<int *>(dyn + (size_t)NW * kRing * kTileBytes);
+  auto elite_count = [&](int x) {
+    int t = plan.n_elite[x];
+    return t < 0 ? 0 : (t > sh.cap ? sh.cap : t);
+  };
+  auto item_count = [&](int x) { return sh.Hkv * ((sh.G * elite_count(x) + 15) >> 4); };
+  int lb = 0, base = 0, cnt = item_count(0);
+  // Pass p covers items [p * grid, (p + 1) * grid); XCD x (blocks x, x + 8, ...
+  // under round-robin dispatch) takes a contiguous eighth of each pass, so the
+  // row tiles of one (l, b, g), which share K, run together under one L2.
+  const int per_xcd = gridDim.x >> 3;
+  const int pos = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  for (int item = pos;; item += gridDim.x) {
+    while (lb < LB && item >= base + cnt) {
+      base += cnt;
+      if (++lb < LB) cnt = item_count(lb);
+    }
+    if (lb >= LB) break;
+    const int nrt = cnt / sh.Hkv;
+    const int local = item - base, g = local / nrt, rt = local - g * nrt;
+    const int l = lb / sh.B, b = lb % sh.B;
+    const int ntk = elite_count(lb);
+    const int R = sh.G * ntk;
+    __syncthreads();  // the previous item is done with el[] and the ring
+    for (int i = tid; i < ntk; i += kRowsThreads) el[i] = plan.elite[(size_t)lb * sh.Nt + i];
+    __syncthreads();
 
-  const E *q = static_cast<const E *>(qt.p[l]);
-  const E *kb = static_cast<const E *>(kt.p[l]) + (size_t)(b * sh.Hkv + g) * sh.S * D;
-  const int nvt = (Nv + 15) >> 4;
-  const int nxt = (ntk + 15) >> 4;
-  for (int rt = rt0; rt < nrt; rt += rt_grid) {
+    const E *q = static_cast<const E *>(qt.p[l]);
+    const E *kb = static_cast<const E *>(kt.p[l]) + (size_t)(b * sh.Hkv + g) * sh.S * D;
+    const int nvt = (Nv + 15) >> 4;
+    const int nxt = (ntk + 15) >> 4;
     const int r = rt * 16 + n;
     Frag<Tag> qf[D / 32];
     if (r < R) {
@@ -610,11 +639,66 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) qf[c].zero();
     }
-    // Elite text keys (at most a few tiles): online max / sum per row, wave w
-    // takes text tiles w, w + NW, ...
+    // Visual key tiles through the LDS ring. Loads are issued for every slot
+    // (an empty slot rereads the last visual row and is ignored) so the count
+    // of loads in flight is static.
+    // Tile sequence of a wave: t = 0 is its elite text tile (text tile w for
+    // wave w; an empty one for waves beyond the elite window), t = 1 .. KT its
+    // visual tiles w, w + NW, .... Tiles stream through a per-wave LDS ring by
+    // DMA; loads are issued for every slot (an empty slot rereads a valid row
+    // and is ignored) so the count of loads in flight is static.
+    f32x4_t S[KT];
     float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     float zx[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int xt = wave; xt < nxt; xt += NW) {
+    auto stage = [&](int t) {
+      int row;
+      if (t == 0) {
+        const int e = wave * 16 + n;
+        row = (wave < nxt && e < ntk) ? Nv + el[e] : Nv - 1;
+      } else {
+        row = (wave + NW * (t - 1)) * 16 + n;
+        row = row < Nv ? row : Nv - 1;
+      }
+      // keep the address computation inside its iteration instead of letting
+      // all of a wave's tile addresses be precomputed (and spilled)
+      asm volatile("" : "+v"(row));
+      const unsigned char *src = reinterpret_cast<const unsigned char *>(kb + (size_t)row * D);
+      unsigned char *slot = ring + (t % kRing) * kTileBytes;
+      if (t >= kRing) wait_lds_reads();  // the slot's previous tile has been read
+#pragma unroll
+      for (int j = 0; j < kDma; ++j) load_lds16(src + 16 * grp + 64 * j, slot + 1024 * j);
+    };
+#pragma unroll
+    for (int t = 0; t < kRing; ++t) stage(t);
+#pragma unroll
+    for (int t = 0; t <= KT; ++t) {
+      // tile t has landed once only the loads of the tiles staged after it remain
+      wait_tiles<kDma>(min(kRing - 1, KT - t));
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      const unsigned char *slot = ring + (t % kRing) * kTileBytes;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        Frag<Tag> kf;
+        LdsTile<Tag>::read(kf, slot, c, lane);
+        mfma_slice(acc, qf[c], kf);
+      }
+      if (t + kRing <= KT) stage(t + kRing);
+      if (t == 0) {
+        if (wave < nxt && wave * 16 + n < ntk) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            mx[i] = acc[i] * sh.scale2;
+            zx[i] = 1.f;
+          }
+        }
+      } else {
+        const bool ok = (wave + NW * (t - 1)) * 16 + n < Nv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[t - 1][i] = ok ? acc[i] * sh.scale2 : -INFINITY;
+      }
+    }
+    // Elite text tiles beyond one per wave (elite windows over 16 x NW tokens).
+    for (int xt = wave + NW; xt < nxt; xt += NW) {
       const int e = xt * 16 + n;
       Frag<Tag> kf[D / 32];
       if (e < ntk) {
@@ -638,51 +722,15 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
         }
       }
     }
-    // Visual keys: wave w owns tiles w, w + NW, ...; their logits stay in
-    // registers. Tiles stream through a per-wave LDS ring by DMA; loads are
-    // issued for every slot (an empty slot rereads the last visual row and is
-    // ignored) so the count of loads in flight is static.
-    f32x4_t S[KT];
     float mr[4] = {mx[0], mx[1], mx[2], mx[3]};
-    auto stage = [&](int k) {
-      int row = (wave + NW * k) * 16 + n;
-      // keep the address computation inside its iteration instead of letting
-      // all of a wave's tile addresses be precomputed (and spilled)
-      asm volatile("" : "+v"(row));
-      const unsigned char *src = reinterpret_cast<const unsigned char *>(kb + (size_t)(row < Nv ? row : Nv - 1) * D);
-      unsigned char *slot = ring + (k % kRing) * kTileBytes;
-      if (k >= kRing) wait_lds_reads();  // the slot's previous tile has been read
-#pragma unroll
-      for (int j = 0; j < kDma; ++j) load_lds16(src + 16 * grp + 64 * j, slot + 1024 * j);
-    };
-#pragma unroll
-    for (int k = 0; k < kRing; ++k) stage(k);
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
-      // tile k has landed once only the loads of the tiles staged after it remain
-      wait_tiles<kDma>(min(kRing - 1, KT - 1 - k));
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      const unsigned char *slot = ring + (k % kRing) * kTileBytes;
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        Frag<Tag> kf;
-        LdsTile<Tag>::read(kf, slot, c, lane);
-        mfma_slice(acc, qf[c], kf);
-      }
-      if (k + kRing < KT) stage(k + kRing);
-      const bool ok = (wave + NW * k) * 16 + n < Nv;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        S[k][i] = ok ? acc[i] * sh.scale2 : -INFINITY;
-        mr[i] = fmaxf(mr[i], S[k][i]);
-      }
+      for (int i = 0; i < 4; ++i) mr[i] = fmaxf(mr[i], S[k][i]);
     }
-    // lane holds rows grp*4+i of key n: reduce over keys (lanes of equal grp), then waves
+    // lane holds rows grp*4+i of key n: reduce over keys (DPP rows), then waves
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mr[i] = fmaxf(mr[i], __shfl_xor(mr[i], o));
-    }
+    for (int i = 0; i < 4; ++i) mr[i] = row16_max(mr[i]);
     if (n == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wave][grp * 4 + i] = mr[i];
@@ -705,8 +753,7 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
         S[k][i] = ev;
         zr[i] += ev;
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) zr[i] += __shfl_xor(zr[i], o);
+      zr[i] = row16_sum(zr[i]);
     }
     __syncthreads();  // every lane has read rowv
     if (n == 0) {
@@ -723,53 +770,69 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
     float W[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) W[i] = rowv[grp * 4 + i];
+    float *part = ws.part + ((size_t)(lb * sh.Hkv + g) * rt_max + rt) * Nv;
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
       const int ti = wave + NW * k;
       if (ti < nvt) {  // wave-uniform
-        float cs = S[k][0] * W[0] + S[k][1] * W[1] + S[k][2] * W[2] + S[k][3] * W[3];
-        cs += __shfl_xor(cs, 16);
-        cs += __shfl_xor(cs, 32);
+        const float cs = sum_across_rows(S[k][0] * W[0] + S[k][1] * W[1] + S[k][2] * W[2] + S[k][3] * W[3]);
         const int c = ti * 16 + n;
-        if (grp == 0 && c < Nv) colacc[c] += cs;
+        if (grp == 0 && c < Nv) store_coherent(&part[c], cs);
       }
     }
-    __syncthreads();  // red / rowv are reused by the next row tile
-  }
-  if (rt0 < nrt) {
-    float *part = ws.part + ((size_t)u * rt_grid + rt0) * Nv;
-    for (int c = tid; c < Nv; c += kRowsThreads) store_coherent(&part[c], colacc[c]);
-  }
-  wait_all_memory();
-  __syncthreads();
-  if (tid == 0) flag = (counter_add(&ws.cnt_lb[lb], 1u) == (unsigned)(sh.Hkv * rt_grid) - 1);
-  __syncthreads();
-  if (!flag) return;
+    wait_all_memory();
+    __syncthreads();
+    const int u = lb * sh.Hkv + g;
+    float *unit_part = ws.part + (size_t)u * rt_max * Nv;  // row tile 0 slot holds the unit's sum
+    if (nrt > 1) {
+      // last row tile of (l, b, g): add the unit's row-tile partials in order
+      if (tid == 0) flag = (counter_add(&ws.cnt_unit[u], 1u) == (unsigned)nrt - 1);
+      __syncthreads();
+      if (!flag) continue;
+      const auto rp = coherent_rsrc(unit_part, (unsigned)((size_t)nrt * Nv * sizeof(float)));
+      for (int c = tid; c < Nv; c += kRowsThreads) {
+        float v[8];
+        float a = 0.f;
+        for (int t0 = 0; t0 < nrt; t0 += 8) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = load_sc1_f(rp, (unsigned)(((t0 + j) * Nv + c) * sizeof(float)));
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (t0 + j < nrt) a += v[j];
+        }
+        store_coherent(&unit_part[c], a);
+      }
+      wait_all_memory();
+      __syncthreads();
+    }
+    if (tid == 0) flag = (counter_add(&ws.cnt_lb[lb], 1u) == (unsigned)sh.Hkv - 1);
+    __syncthreads();
+    if (!flag) continue;
 
-  // Last workgroup of (l, b): I_v = sum of the row-tile partials over KV heads
-  // and row tiles (ascending), divided by H_q * N_tk.
-  acquire_device();
-  const int nact = min(nrt, rt_grid);
-  const float inv_rows = (ntk > 0) ? 1.f / (float)(sh.Hq * ntk) : 0.f;
-  const int np = sh.Hkv * nact;  // partials per column, summed in (KV head, row tile) order
-  for (int c = tid; c < Nv; c += kRowsThreads) {
-    float a = 0.f;
-    for (int i0 = 0; i0 < np; i0 += 8) {
+    // Last KV head of (l, b): I_v = sum of the heads' sums (ascending) divided
+    // by H_q * N_tk; the ring area holds it for the finisher.
+    float *ivc = reinterpret_cast<float *>(dyn);
+    const float inv_rows = (ntk > 0) ? 1.f / (float)(sh.Hq * ntk) : 0.f;
+    const size_t head_stride = (size_t)rt_max * Nv;
+    const auto rl = coherent_rsrc(ws.part + (size_t)lb * sh.Hkv * head_stride,
+                                  (unsigned)((size_t)sh.Hkv * head_stride * sizeof(float)));
+    for (int c = tid; c < Nv; c += kRowsThreads) {
       float v[8];
+      float a = 0.f;
+      for (int g0 = 0; g0 < sh.Hkv; g0 += 8) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {  // eight independent loads in flight
-        const int i = i0 + j, gg = i / nact, t = i - gg * nact;
-        v[j] = (i < np) ? ws.part[(((size_t)lb * sh.Hkv + gg) * rt_grid + t) * Nv + c] : 0.f;
+        for (int j = 0; j < 8; ++j) v[j] = load_sc1_f(rl, (unsigned)(((g0 + j) * head_stride + c) * sizeof(float)));
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (g0 + j < sh.Hkv) a += v[j];
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) a += v[j];
+      a *= inv_rows;
+      ivc[c] = a;
+      plan.iv[(size_t)lb * Nv + c] = a;
     }
-    a *= inv_rows;
-    colacc[c] = a;
-    plan.iv[(size_t)lb * Nv + c] = a;
+    __syncthreads();
+    finish_layer_sample<kRowsThreads>(sh, plan, ws, lb, ivc);
   }
-  __syncthreads();
-  finish_layer_sample<kRowsThreads>(sh, plan, ws, lb, colacc);
 }
 
 // Block-wide exclusive scan for 1024 threads; returns the exclusive prefix and
@@ -1000,7 +1063,7 @@ struct Config {
 };
 
 // Register budgets of cross_score_rows_kernel instantiations (key tiles per wave).
-constexpr int kRowsKt[] = {4, 8, 16};
+constexpr int kRowsKt[] = {4, 8, 16, 24};
 
 int make_config(const aircache_desc *d, Config *cfg) {
   g_last_error.clear();
@@ -1056,7 +1119,7 @@ int make_config(const aircache_desc *d, Config *cfg) {
     return fail(AIRCACHE_EINVAL, "n_q_heads * max_elite too large (%lld rows); lower max_elite",
                 (long long)s.Hq * s.cap);
   const size_t units = (size_t)s.L * s.B * s.Hkv;
-  const size_t n_cnt = (size_t)s.L * s.B + s.B + 1;
+  const size_t n_cnt = (size_t)s.L * s.B * s.Hkv + (size_t)s.L * s.B + s.B + 1;
   cfg->units = (int)units;
   // Row-complete scoring when the visual keys plus the largest elite window
   // fit in the registers of one 8-wave workgroup.
@@ -1068,12 +1131,15 @@ int make_config(const aircache_desc *d, Config *cfg) {
       break;
     }
   const long long rt_need = ((long long)s.G * s.cap + 15) / 16;
-  cfg->rt_grid = (int)(rt_need < 1 ? 1 : (rt_need > 4 ? 4 : rt_need));
+  cfg->rt_grid = (int)(rt_need < 1 ? 1 : rt_need);  // row tiles of a unit at most
   const size_t tile_bytes = (size_t)16 * s.D * (d->dtype == AIRCACHE_BF16 ? 2 : 4);
-  cfg->rows_lds = (size_t)kRowsWaves * 2 * tile_bytes + ((size_t)s.Nv + s.cap) * sizeof(float);
+  size_t ring = 131072 / (kRowsWaves * tile_bytes);
+  if (ring > 4) ring = 4;
+  cfg->rows_lds = (size_t)kRowsWaves * ring * tile_bytes + (size_t)s.cap * sizeof(int);
+  if ((size_t)s.Nv * sizeof(float) > (size_t)kRowsWaves * ring * tile_bytes) cfg->rows_kt = 0;  // finisher's I_v
   if (cfg->rows_kt && cfg->rows_lds > kMaxLds) cfg->rows_kt = 0;
   if (d->path == AIRCACHE_PATH_ROWS && !cfg->rows_kt)
-    return fail(AIRCACHE_EINVAL, "the rows path needs n_vis <= %d", kRowsWaves * 16 * kRowsKt[2]);
+    return fail(AIRCACHE_EINVAL, "the rows path needs n_vis <= %d", kRowsWaves * 16 * kRowsKt[3]);
   if (d->path == AIRCACHE_PATH_TILED) cfg->rows_kt = 0;
   cfg->off_cnt = 0;
   cfg->off_stats = align_up(n_cnt * sizeof(unsigned));
@@ -1093,7 +1159,8 @@ Ws ws_of(const Config &cfg, void *base) {
   char *p = static_cast<char *>(base);
   const Shape &s = cfg.sh;
   Ws w;
-  w.cnt_lb = reinterpret_cast<unsigned *>(p + cfg.off_cnt);
+  w.cnt_unit = reinterpret_cast<unsigned *>(p + cfg.off_cnt);
+  w.cnt_lb = w.cnt_unit + (size_t)s.L * s.B * s.Hkv;
   w.cnt_b = w.cnt_lb + (size_t)s.L * s.B;
   w.cnt_all = w.cnt_b + s.B;
   w.stats = reinterpret_cast<float2 *>(p + cfg.off_stats);
@@ -1123,15 +1190,39 @@ int mark(hipEvent_t *ev, int i, hipStream_t st) {
   return check_hip(hipEventRecord(ev[i], st), "hipEventRecord");
 }
 
+// Compute units of the current device (cached per device).
+int device_cus(int *cus) {
+  static int cache[64] = {0};
+  int dev = 0;
+  int rc;
+  if ((rc = check_hip(hipGetDevice(&dev), "hipGetDevice"))) return rc;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *cus = cache[dev];
+    return AIRCACHE_OK;
+  }
+  int v = 0;
+  if ((rc = check_hip(hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev), "hipDeviceGetAttribute")))
+    return rc;
+  if (v < 1) v = 1;
+  if (dev >= 0 && dev < 64) cache[dev] = v;
+  *cus = v;
+  return AIRCACHE_OK;
+}
+
 template <typename Tag, int D, int KT>
 int launch_rows(const Config &cfg, const LayerTable &qt, const LayerTable &kt, const PlanPtrs &pp, const Ws &ws,
                 hipStream_t st) {
   const Shape &s = cfg.sh;
   int rc;
   if ((rc = allow_lds(cross_score_rows_kernel<Tag, D, KT>, cfg.rows_lds))) return rc;
-  const unsigned u8 = (unsigned)((cfg.units + 7) / 8 * 8);
-  hipLaunchKernelGGL((cross_score_rows_kernel<Tag, D, KT>), dim3(u8 * cfg.rt_grid), dim3(kRowsThreads), cfg.rows_lds,
-                     st, s, qt, kt, pp, ws, cfg.rt_grid, cfg.units);
+  int cus = 0;
+  if ((rc = device_cus(&cus))) return rc;
+  // persistent: one workgroup per CU (LDS use admits one), never more than the items
+  long long items = (long long)cfg.units * cfg.rt_grid;
+  long long g8 = (items + 7) / 8 * 8;  // a multiple of 8 (item to XCD mapping)
+  const unsigned grid = (unsigned)(g8 < cus ? g8 : (cus / 8) * 8);
+  hipLaunchKernelGGL((cross_score_rows_kernel<Tag, D, KT>), dim3(grid), dim3(kRowsThreads), cfg.rows_lds, st, s, qt,
+                     kt, pp, ws, cfg.rt_grid);
   return check_hip(hipGetLastError(), "cross_score_rows_kernel launch");
 }
 
@@ -1151,7 +1242,8 @@ int launch_plan(const Config &cfg, const LayerTable &qt, const LayerTable &kt, c
     // scoring, statistics and budgets in one launch; the finalize stage is empty
     if (cfg.rows_kt == 4) rc = launch_rows<Tag, D, 4>(cfg, qt, kt, pp, ws, st);
     else if (cfg.rows_kt == 8) rc = launch_rows<Tag, D, 8>(cfg, qt, kt, pp, ws, st);
-    else rc = launch_rows<Tag, D, 16>(cfg, qt, kt, pp, ws, st);
+    else if (cfg.rows_kt == 16) rc = launch_rows<Tag, D, 16>(cfg, qt, kt, pp, ws, st);
+    else rc = launch_rows<Tag, D, 24>(cfg, qt, kt, pp, ws, st);
     if (rc) return rc;
     if ((rc = mark(ev, 2, st))) return rc;
   } else {

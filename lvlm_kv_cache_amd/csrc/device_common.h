@@ -67,22 +67,75 @@ __device__ __forceinline__ void mfma_slice(f32x4_t &acc, const Frag<F32Tag> &a, 
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, acc, 0, 0, 0);
 }
 
+// Cross-lane moves by DPP (no LDS round trip). CTRL: 0xB1 quad_perm
+// [1,0,3,2] (lane ^ 1), 0x4E quad_perm [2,3,0,1] (lane ^ 2), 0x141 row half
+// mirror (lane i of each 8-lane half from lane 7 - i), 0x140 row mirror (lane
+// i of each 16-lane row from lane 15 - i).
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL> __device__ __forceinline__ double dpp_d(double v) {
+  const long long x = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(x >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// Reductions over the 16 lanes of a DPP row; every lane of the row receives
+// the same bits (each step combines a lane with its mirror partner, and the
+// operations are commutative).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  return fmaxf(v, dpp_f<0x140>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  return v + dpp_f<0x140>(v);
+}
+__device__ __forceinline__ double row16_sum_d(double v) {
+  v += dpp_d<0xB1>(v);
+  v += dpp_d<0x4E>(v);
+  v += dpp_d<0x141>(v);
+  return v + dpp_d<0x140>(v);
+}
+
+// Sum over the four 16-lane rows (lanes n, n + 16, n + 32, n + 48) with the
+// gfx950 row-swap permutes; every lane receives (r0 + r1) + (r2 + r3).
+__device__ __forceinline__ float sum_across_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const long long x = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)x, l), hi = __builtin_amdgcn_readlane((int)(x >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// Whole-wave reductions: rows first, then the four row results in a fixed
+// order; the result is wave-uniform.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = row16_max(v);
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v = row16_sum(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
 
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v = row16_sum_d(v);
+  return (readlane_d(v, 0) + readlane_d(v, 16)) + (readlane_d(v, 32) + readlane_d(v, 48));
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
@@ -110,6 +163,23 @@ template <typename T> __device__ __forceinline__ T load_coherent(const T *p) {
 __device__ __forceinline__ unsigned counter_add(unsigned *p, unsigned v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Agent-coherent loads that the compiler may batch like ordinary loads: buffer
+// loads with the sc1 cache policy through a raw buffer resource (gfx9 family
+// resource word 3; out-of-range offsets read as 0). They observe values
+// published with store_coherent without invalidating the L2.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void *base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ float load_sc1_f(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 16));
+}
+__device__ __forceinline__ int load_sc1_i(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+  return (int)__builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 16);
+}
+__device__ __forceinline__ double load_sc1_d(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+  return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, 16));
+}
+
 // Acquire at device scope: after it, ordinary loads observe every value that
 // another workgroup published with store_coherent before its counter update
 // (invalidates this CU's L1 and the XCD's non-coherent L2 lines). Used once
