@@ -135,6 +135,12 @@ size_t aircache_workspace_size(const aircache_desc *desc);
  * worst-case capacity of each k_out[l] / v_out[l] buffer in elements. */
 int64_t aircache_max_compacted_elems(const aircache_desc *desc);
 
+/* The scoring path aircache_plan takes for this descriptor:
+ * AIRCACHE_PATH_TILED or AIRCACHE_PATH_ROWS (desc->path AIRCACHE_PATH_AUTO
+ * resolved), or -1 for an invalid descriptor (aircache_last_error says why).
+ * Host only; no device work. */
+int32_t aircache_resolved_path(const aircache_desc *desc);
+
 /* Scores, statistics, budgets and top-k selection for all layers.
  *   q_txt, k : host arrays of n_layers device pointers (layout above)
  *   plan     : output buffers (see aircache_plan_buf)

@@ -19,6 +19,7 @@ PATH_AUTO, PATH_TILED, PATH_ROWS = 0, 1, 2
 MAX_LAYERS = 128
 
 EXPORTS = ["aircache_abi_version", "aircache_workspace_size", "aircache_max_compacted_elems",
+           "aircache_resolved_path",
            "aircache_plan", "aircache_compress", "aircache_plan_profiled", "aircache_compress_profiled",
            "aircache_strerror", "aircache_last_error"]
 PLAN_KERNELS = ["elite_select", "cross_score", "finalize", "topk_select"]
@@ -60,6 +61,8 @@ def load() -> C.CDLL:
         lib.aircache_workspace_size.argtypes = [C.POINTER(Desc)]
         lib.aircache_max_compacted_elems.restype = C.c_int64
         lib.aircache_max_compacted_elems.argtypes = [C.POINTER(Desc)]
+        lib.aircache_resolved_path.restype = C.c_int32
+        lib.aircache_resolved_path.argtypes = [C.POINTER(Desc)]
         lib.aircache_plan.restype = C.c_int
         lib.aircache_plan.argtypes = [C.POINTER(Desc), P, P, C.POINTER(PlanBuf), P, C.c_size_t, P]
         lib.aircache_compress.restype = C.c_int
@@ -94,6 +97,10 @@ def workspace_size(desc: Desc) -> int:
 
 def max_compacted_elems(desc: Desc) -> int:
     return int(load().aircache_max_compacted_elems(C.byref(desc)))
+
+
+def resolved_path(desc: Desc) -> int:
+    return int(load().aircache_resolved_path(C.byref(desc)))
 
 
 def plan(desc: Desc, q_ptrs, k_ptrs, buf: PlanBuf, ws_ptr: int, ws_bytes: int, stream: int,

@@ -80,6 +80,11 @@ class AirCache:
         self.ws_bytes = ws
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
 
+    @property
+    def scoring_path(self) -> str:
+        """"tiled" or "rows": the scoring path the plan call takes."""
+        return {_lib.PATH_TILED: "tiled", _lib.PATH_ROWS: "rows"}[_lib.resolved_path(self.desc)]
+
     # -- validation ------------------------------------------------------
     def _check_layers(self, ts, shape, name):
         s = self.shape

@@ -1318,6 +1318,12 @@ int64_t aircache_max_compacted_elems(const aircache_desc *desc) {
   return (int64_t)s.B * s.Hkv * (int64_t)(s.Nv + s.Nt) * s.D;
 }
 
+int32_t aircache_resolved_path(const aircache_desc *desc) {
+  Config cfg;
+  if (make_config(desc, &cfg) != AIRCACHE_OK) return -1;
+  return cfg.rows_kt ? AIRCACHE_PATH_ROWS : AIRCACHE_PATH_TILED;
+}
+
 int aircache_plan_profiled(const aircache_desc *desc, const void *const *q_txt, const void *const *k,
                            const aircache_plan_buf *plan, void *workspace, size_t ws_bytes, void *stream,
                            void *const *events, int n_events) {

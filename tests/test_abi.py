@@ -55,6 +55,15 @@ def test_workspace_size(lib):
     assert _lib.max_compacted_elems(desc()) == 1 * 4 * 3008 * 128
 
 
+def test_resolved_path(lib):
+    # rows path while N_v fits 8 waves x 16 keys x 24 tiles (3072 keys), else tiled
+    assert _lib.resolved_path(desc()) == _lib.PATH_ROWS
+    assert _lib.resolved_path(desc(n_vis=3072)) == _lib.PATH_ROWS
+    assert _lib.resolved_path(desc(n_vis=3073)) == _lib.PATH_TILED
+    assert _lib.resolved_path(desc(path=1)) == _lib.PATH_TILED
+    assert _lib.resolved_path(desc(path=2, n_vis=17)) == _lib.PATH_ROWS
+
+
 @pytest.mark.parametrize("bad", [dict(n_layers=0), dict(n_layers=129), dict(batch=0), dict(n_kv_heads=5),
                                  dict(head_dim=96), dict(n_vis=2), dict(n_vis=9000), dict(n_txt=0),
                                  dict(dtype="x"), dict(alpha=1.5), dict(alpha=float("nan")),
@@ -68,6 +77,7 @@ def test_invalid_descriptor(lib, bad):
         d = desc(**bad)
     assert _lib.workspace_size(d) == 0
     assert lib.aircache_last_error().decode()
+    assert _lib.resolved_path(d) == -1
     rc = _lib.plan(d, [1] * max(d.n_layers, 1), [1] * max(d.n_layers, 1), _lib.PlanBuf(), 16, 1 << 40, 0)
     assert rc == _lib.AIRCACHE_EINVAL
 
