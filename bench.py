@@ -225,7 +225,7 @@ def main():
     dom = "cross_score"
     dom_gbps = nbytes[dom] / (kern_us[dom] * 1e-6) / 1e9
     path = ac.scoring_path
-    dom_kernel = "cross_score_rows_kernel" if path == "rows" else "cross_score_kernel"
+    dom_kernel = {"rows": "cross_score_rows_kernel", "chunked": "cross_score_fused_kernel"}.get(path, "cross_score_kernel")
     traffic = measured_traffic(dom_kernel, w.name)
     out = {
         "metric": METRIC,

@@ -80,6 +80,11 @@ typedef enum { AIRCACHE_F32 = 0, AIRCACHE_BF16 = 1 } aircache_dtype;
 /* Device-side condition bits OR-ed into plan->status. */
 #define AIRCACHE_DEV_ELITE_OVERFLOW 1 /* some (layer, sample) had more elite tokens than
                                          desc.max_elite; its results are not valid */
+#define AIRCACHE_DEV_TIMEOUT 2        /* a bounded wait between workgroups of the chunked
+                                         path expired (workspace not zeroed before its
+                                         first use, or the device shared with work that
+                                         kept workgroups from running); results are not
+                                         valid */
 
 typedef struct {
   int32_t n_layers;   /* L, 1 .. AIRCACHE_MAX_LAYERS */
@@ -93,17 +98,22 @@ typedef struct {
   double alpha;       /* elite threshold in [0, 1]; the page uses 0.9 */
   double ratio;       /* r / N_v, the retention ratio in [0, 1] */
   int32_t max_elite;  /* workspace cap on elite tokens per (layer, sample); 0 means n_txt */
-  int32_t path;       /* scoring kernels: AIRCACHE_PATH_AUTO (0), _TILED (1) or _ROWS (2);
-                         every path computes the same results */
+  int32_t path;       /* scoring kernels: AIRCACHE_PATH_AUTO (0), _TILED (1), _ROWS (2)
+                         or _CHUNKED (3); every path computes the same results */
 } aircache_desc;
 
 /* Scoring paths. TILED: column tiles of every (layer, sample, KV head) with
  * the exponentials spilled to the workspace and a separate merge kernel; any
  * size. ROWS: one workgroup per 16 elite-query rows keeps a whole row of
- * logits in registers (n_vis <= 3072). AUTO picks ROWS when it applies. */
+ * logits in registers (n_vis <= 3072). CHUNKED: one persistent launch for
+ * scoring, statistics, budgets and top-k; a workgroup takes a run of visual
+ * keys of every KV head of one (layer, sample) and swaps row maxima and sums
+ * with the other runs (n_kv_heads in {1, 2, 4, 8}). AUTO picks CHUNKED, else
+ * ROWS, else TILED. */
 #define AIRCACHE_PATH_AUTO 0
 #define AIRCACHE_PATH_TILED 1
 #define AIRCACHE_PATH_ROWS 2
+#define AIRCACHE_PATH_CHUNKED 3
 
 /* Outputs of aircache_plan; all device pointers, allocated by the caller with
  * the sizes given, written by the library (row-major, [l][b] means index
@@ -127,8 +137,10 @@ int aircache_abi_version(void);
 
 /* Bytes of device workspace aircache_plan needs for this descriptor, or 0 if
  * the descriptor is invalid (aircache_last_error() says why). The workspace is
- * caller-owned scratch: its content need not be preserved between calls and
- * one workspace must not be used by two calls that can run concurrently. */
+ * caller-owned scratch that must be zero-filled once, before its first use;
+ * the library keeps it valid across calls after that, with this or any other
+ * descriptor it is large enough for. One workspace must not be used by two
+ * calls that can run concurrently. */
 size_t aircache_workspace_size(const aircache_desc *desc);
 
 /* Largest compacted element count per layer (every visual row kept): the
@@ -136,7 +148,7 @@ size_t aircache_workspace_size(const aircache_desc *desc);
 int64_t aircache_max_compacted_elems(const aircache_desc *desc);
 
 /* The scoring path aircache_plan takes for this descriptor:
- * AIRCACHE_PATH_TILED or AIRCACHE_PATH_ROWS (desc->path AIRCACHE_PATH_AUTO
+ * AIRCACHE_PATH_TILED, _ROWS or _CHUNKED (desc->path AIRCACHE_PATH_AUTO
  * resolved), or -1 for an invalid descriptor (aircache_last_error says why).
  * Host only; no device work. */
 int32_t aircache_resolved_path(const aircache_desc *desc);

@@ -15,7 +15,7 @@ from . import _lib
 _DTYPES = {torch.float32: _lib.AIRCACHE_F32, torch.bfloat16: _lib.AIRCACHE_BF16}
 
 
-_PATHS = {"auto": _lib.PATH_AUTO, "tiled": _lib.PATH_TILED, "rows": _lib.PATH_ROWS}
+_PATHS = {"auto": _lib.PATH_AUTO, "tiled": _lib.PATH_TILED, "rows": _lib.PATH_ROWS, "chunked": _lib.PATH_CHUNKED}
 
 
 def make_desc(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt, dtype,
@@ -78,12 +78,14 @@ class AirCache:
         if ws == 0:
             _lib.check(_lib.AIRCACHE_EINVAL)
         self.ws_bytes = ws
-        self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
+        # zero-filled once; the library keeps it valid from call to call
+        self.workspace = torch.zeros(ws, dtype=torch.uint8, device=self.device)
 
     @property
     def scoring_path(self) -> str:
-        """"tiled" or "rows": the scoring path the plan call takes."""
-        return {_lib.PATH_TILED: "tiled", _lib.PATH_ROWS: "rows"}[_lib.resolved_path(self.desc)]
+        """"tiled", "rows" or "chunked": the scoring path the plan call takes."""
+        return {_lib.PATH_TILED: "tiled", _lib.PATH_ROWS: "rows",
+                _lib.PATH_CHUNKED: "chunked"}[_lib.resolved_path(self.desc)]
 
     # -- validation ------------------------------------------------------
     def _check_layers(self, ts, shape, name):

@@ -47,6 +47,7 @@ struct PlanPtrs {
 };
 
 struct Ws {
+  unsigned *epoch;    // [1]   call counter of the workspace (chunked path records carry it)
   unsigned *cnt_unit; // [L*B*Hkv] finished row tiles per (l, b, g)
   unsigned *cnt_lb;   // [L*B] finished scoring tiles (tiled path) or KV heads (rows path) per (l, b)
   unsigned *cnt_b;    // [B]   finished layers per sample
@@ -54,6 +55,8 @@ struct Ws {
   float2 *stats;      // [units][rcap16][ntiles] (tile max, tile sum) per row, base 2
   float *e;           // [units][Nv][row stride] exp2(logit - tile max) of visual keys
   float *part;        // [units][rt_grid][Nv] column sums of one row tile (row-complete path)
+  unsigned *cnt_chunk; // [L*B][chunk_stride] finished row groups per chunk (chunked path), or NULL
+  int chunk_stride;
 };
 
 struct LayerTable {
@@ -93,12 +96,15 @@ __global__ __launch_bounds__(kEliteThreads) void elite_select_kernel(Shape sh, L
 
   // This kernel opens every plan: reset the counters of finalize_kernel.
   for (int g = tid; g < sh.Hkv; g += kEliteThreads) ws.cnt_unit[(size_t)lb * sh.Hkv + g] = 0;
+  if (ws.cnt_chunk)
+    for (int c = tid; c < ws.chunk_stride; c += kEliteThreads) ws.cnt_chunk[(size_t)lb * ws.chunk_stride + c] = 0;
   if (tid == 0) {
     ws.cnt_lb[lb] = 0;
     if (l == 0) ws.cnt_b[b] = 0;
     if (lb == 0) {
       *ws.cnt_all = 0;
       *plan.status = 0;
+      *ws.epoch = *ws.epoch + 1u;
     }
   }
 
@@ -358,7 +364,7 @@ __global__ __launch_bounds__(256) void cross_score_kernel(Shape sh, LayerTable q
 struct BudgetSums {
   double st_sum, mshift, u_sum;
 };
-__device__ BudgetSums budget_sums(int L, const double *st, const double *sk) {
+__device__ __forceinline__ BudgetSums budget_sums(int L, const double *st, const double *sk) {
 #pragma clang fp contract(off)
   BudgetSums r{0.0, 0.0, 0.0};
   for (int l = 0; l < L; ++l) r.st_sum += st[l];
@@ -367,7 +373,7 @@ __device__ BudgetSums budget_sums(int L, const double *st, const double *sk) {
   for (int l = 0; l < L; ++l) r.u_sum += sk[l] - r.mshift;
   return r;
 }
-__device__ void layer_budget(const Shape &sh, const BudgetSums &r, double st, double sk, double *x_out, int *b_out) {
+__device__ __forceinline__ void layer_budget(const Shape &sh, const BudgetSums &r, double st, double sk, double *x_out, int *b_out) {
 #pragma clang fp contract(off)
   const double rr = sh.ratio * (double)sh.Nv;
   const double stn = st * (double)sh.L / r.st_sum;
@@ -835,6 +841,8 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
   }
 }
 
+#include "score_fused.h"
+
 // Block-wide exclusive scan for 1024 threads; returns the exclusive prefix and
 // writes the total to *total.
 __device__ __forceinline__ int block_excl_scan_1024(int v, int *wtot, int *total) {
@@ -1056,11 +1064,20 @@ constexpr size_t kMaxLds = 160 * 1024;
 struct Config {
   Shape sh;
   size_t off_cnt, off_stats, off_e, off_part, ws_bytes;
+  size_t off_xrec, off_mom, off_brec, off_part_rg, off_cnt_chunk;
   size_t elite_lds, score_lds, final_lds, rows_lds;
   int ktw;
   int rows_kt;  // key tiles per wave of cross_score_rows_kernel; 0: the tiled path with spilled exponentials
   int rt_grid, units;
+  bool chunked;        // cross_score_fused_kernel (steps 2-5 in one launch)
+  int fused_kcap_lo;   // smallest key-tile cap per wave a chunked launch can choose
+  int rec_stride, max_chunks, max_rg, wmax;
+  FusedLds flds;
+  int path;            // AIRCACHE_PATH_TILED, _ROWS or _CHUNKED
 };
+
+// Workspace head: the epoch word, then the counters.
+constexpr size_t kEpochBytes = 256;
 
 // Register budgets of cross_score_rows_kernel instantiations (key tiles per wave).
 constexpr int kRowsKt[] = {4, 8, 16, 24};
@@ -1083,7 +1100,8 @@ int make_config(const aircache_desc *d, Config *cfg) {
   if (!(d->ratio >= 0.0 && d->ratio <= 1.0)) return fail(AIRCACHE_EINVAL, "ratio=%g outside [0, 1]", d->ratio);
   if (d->max_elite < 0 || d->max_elite > d->n_txt)
     return fail(AIRCACHE_EINVAL, "max_elite=%d outside [0, n_txt=%d]", d->max_elite, d->n_txt);
-  if (d->path < AIRCACHE_PATH_AUTO || d->path > AIRCACHE_PATH_ROWS) return fail(AIRCACHE_EINVAL, "path=%d unknown", d->path);
+  if (d->path < AIRCACHE_PATH_AUTO || d->path > AIRCACHE_PATH_CHUNKED)
+    return fail(AIRCACHE_EINVAL, "path=%d unknown", d->path);
   Shape &s = cfg->sh;
   s.L = d->n_layers;
   s.B = d->batch;
@@ -1140,10 +1158,62 @@ int make_config(const aircache_desc *d, Config *cfg) {
   if (cfg->rows_kt && cfg->rows_lds > kMaxLds) cfg->rows_kt = 0;
   if (d->path == AIRCACHE_PATH_ROWS && !cfg->rows_kt)
     return fail(AIRCACHE_EINVAL, "the rows path needs n_vis <= %d", kRowsWaves * 16 * kRowsKt[3]);
-  if (d->path == AIRCACHE_PATH_TILED) cfg->rows_kt = 0;
-  cfg->off_cnt = 0;
-  cfg->off_stats = align_up(n_cnt * sizeof(unsigned));
-  if (cfg->rows_kt) {
+  // Chunked path: power-of-two KV head count up to the wave count, its LDS
+  // layout within the limit, and a bounded item count per workgroup on a
+  // 256-CU device.
+  cfg->chunked = false;
+  {
+    const bool heads_ok = (s.Hkv == 1 || s.Hkv == 2 || s.Hkv == 4 || s.Hkv == 8);
+    const int wph = heads_ok ? kFusedWaves / s.Hkv : 1;
+    const int lb = s.L * s.B;
+    cfg->fused_kcap_lo = fused_kcap_min(s.L, s.B, s.Nv, wph);
+    long long rec = 0;
+    int maxc = 1, maxrg = 1, wmax = 16;
+    for (int ntk = 0; ntk <= s.cap; ++ntk) {
+      // the narrowest chunks a launch can choose give the most records
+      const ChunkPlan cp = fused_chunk_plan(ntk, s.G, s.Nv, wph, cfg->fused_kcap_lo);
+      const long long r = (long long)cp.nchunks * s.Hkv * cp.rtg * 16;
+      if (r > rec) rec = r;
+      if (cp.nchunks > maxc) maxc = cp.nchunks;
+      if (cp.nrg > maxrg) maxrg = cp.nrg;
+      // the widest chunk of any cap at or above the smallest
+      const ChunkPlan cw = fused_chunk_plan(ntk, s.G, s.Nv, wph, kFusedSlots);
+      if (cw.width > wmax) wmax = cw.width;
+    }
+    cfg->rec_stride = (int)rec;
+    cfg->max_chunks = maxc;
+    cfg->max_rg = maxrg;
+    cfg->wmax = wmax;
+    const int tb = (int)tile_bytes;
+    cfg->flds = fused_lds_layout(tb, tb <= 4096 ? 3 : 2, s.cap, s.Hkv, s.B);
+    const bool lds_ok = (size_t)cfg->flds.total + 8192 <= kMaxLds &&
+                        (size_t)s.L * maxc * 40 <= (size_t)(cfg->flds.el - cfg->flds.ring);  // finisher's records
+    // the schedule is worked out by one wave: at most 8 (layer, sample) pairs per lane
+    const bool items_ok = lb <= 512 && (long long)lb * maxc * maxrg <= (long long)kFusedMaxItems * kFusedTargetCus &&
+                          maxc <= 64;
+    const bool rec_ok = rec * 16 < (1ll << 31);
+    cfg->chunked = heads_ok && lds_ok && items_ok && rec_ok;
+  }
+  if (d->path == AIRCACHE_PATH_CHUNKED && !cfg->chunked)
+    return fail(AIRCACHE_EINVAL, "the chunked path needs n_kv_heads in {1, 2, 4, 8} and a smaller batch or elite cap");
+  if (d->path == AIRCACHE_PATH_TILED || d->path == AIRCACHE_PATH_ROWS) cfg->chunked = false;
+  if (d->path == AIRCACHE_PATH_TILED || d->path == AIRCACHE_PATH_CHUNKED) cfg->rows_kt = 0;
+  cfg->path = cfg->chunked ? AIRCACHE_PATH_CHUNKED : cfg->rows_kt ? AIRCACHE_PATH_ROWS : AIRCACHE_PATH_TILED;
+  cfg->off_cnt = kEpochBytes;
+  cfg->off_stats = cfg->off_cnt + align_up(n_cnt * sizeof(unsigned));
+  cfg->off_xrec = cfg->off_mom = cfg->off_brec = cfg->off_stats;
+  if (cfg->chunked) {
+    const size_t lbs = (size_t)s.L * s.B;
+    cfg->off_e = cfg->off_part = cfg->off_stats;
+    cfg->off_xrec = cfg->off_stats;
+    cfg->off_mom = cfg->off_xrec + align_up(lbs * (size_t)cfg->rec_stride * 16);
+    cfg->off_brec = cfg->off_mom + align_up(lbs * (size_t)cfg->max_chunks * 32);
+    cfg->off_cnt_chunk = cfg->off_brec + align_up(lbs * 8);
+    cfg->off_part_rg = cfg->off_cnt_chunk + align_up(lbs * (size_t)cfg->max_chunks * sizeof(unsigned));
+    // row-group partial sums only when some elite count can need two row groups
+    const size_t part_rg = cfg->max_rg > 1 ? lbs * (size_t)cfg->max_chunks * cfg->max_rg * cfg->wmax * sizeof(float) : 0;
+    cfg->ws_bytes = cfg->off_part_rg + align_up(part_rg);
+  } else if (cfg->rows_kt) {
     cfg->off_e = cfg->off_stats;
     cfg->off_part = cfg->off_stats;
     cfg->ws_bytes = cfg->off_part + align_up(units * cfg->rt_grid * (size_t)s.Nv * sizeof(float));
@@ -1159,6 +1229,7 @@ Ws ws_of(const Config &cfg, void *base) {
   char *p = static_cast<char *>(base);
   const Shape &s = cfg.sh;
   Ws w;
+  w.epoch = reinterpret_cast<unsigned *>(p);
   w.cnt_unit = reinterpret_cast<unsigned *>(p + cfg.off_cnt);
   w.cnt_lb = w.cnt_unit + (size_t)s.L * s.B * s.Hkv;
   w.cnt_b = w.cnt_lb + (size_t)s.L * s.B;
@@ -1166,6 +1237,8 @@ Ws ws_of(const Config &cfg, void *base) {
   w.stats = reinterpret_cast<float2 *>(p + cfg.off_stats);
   w.e = reinterpret_cast<float *>(p + cfg.off_e);
   w.part = reinterpret_cast<float *>(p + cfg.off_part);
+  w.cnt_chunk = cfg.chunked ? reinterpret_cast<unsigned *>(p + cfg.off_cnt_chunk) : nullptr;
+  w.chunk_stride = cfg.chunked ? cfg.max_chunks : 0;
   return w;
 }
 
@@ -1226,9 +1299,53 @@ int launch_rows(const Config &cfg, const LayerTable &qt, const LayerTable &kt, c
   return check_hip(hipGetLastError(), "cross_score_rows_kernel launch");
 }
 
+template <typename Tag, int D>
+int launch_chunked(const Config &cfg, const LayerTable &qt, const LayerTable &kt, const PlanPtrs &pp, const Ws &ws,
+                   void *ws_base, hipStream_t st) {
+  const Shape &s = cfg.sh;
+  int rc;
+  auto kern = cross_score_fused_kernel<Tag, D>;
+  const size_t lds = (size_t)cfg.flds.total;
+  if ((rc = allow_lds(kern, lds))) return rc;
+  int cus = 0;
+  if ((rc = device_cus(&cus))) return rc;
+  int occ = 0;
+  if ((rc = check_hip(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void *>(kern),
+                                                                   kFusedThreads, lds),
+                      "hipOccupancyMaxActiveBlocksPerMultiprocessor")))
+    return rc;
+  if (occ < 1) return fail(AIRCACHE_EINVAL, "the chunked kernel does not fit a compute unit");
+  const int grid = cus * occ;
+  // every chunk of a (layer, sample) needs a workgroup of its own, and the
+  // item list of a workgroup is bounded
+  if (cfg.max_chunks > grid) return fail(AIRCACHE_EINVAL, "%d chunks per (layer, sample) exceed %d workgroups", cfg.max_chunks, grid);
+  if ((long long)s.L * s.B * cfg.max_chunks > (long long)kFusedMaxItems * grid)
+    return fail(AIRCACHE_EINVAL, "too many work items for %d workgroups", grid);
+  char *p = static_cast<char *>(ws_base);
+  FusedWs fw;
+  fw.epoch = ws.epoch;
+  fw.cnt_b = ws.cnt_b;
+  fw.ticket = ws.cnt_all;
+  fw.xrec = reinterpret_cast<uint64_t *>(p + cfg.off_xrec);
+  fw.mom = reinterpret_cast<double *>(p + cfg.off_mom);
+  fw.brec = reinterpret_cast<uint64_t *>(p + cfg.off_brec);
+  fw.rec_stride = cfg.rec_stride;
+  fw.max_chunks = cfg.max_chunks;
+  fw.max_rg = cfg.max_rg;
+  fw.wmax = cfg.wmax;
+  fw.cnt_chunk = ws.cnt_chunk;
+  fw.part = reinterpret_cast<float *>(p + cfg.off_part_rg);
+  // One workgroup per CU (the LDS use admits no second), so with the device
+  // to itself every workgroup is resident at once, which the waits between
+  // workgroups need; if other work holds CUs, the bounded waits report
+  // AIRCACHE_DEV_TIMEOUT instead of hanging.
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kFusedThreads), lds, st, s, qt, kt, pp, fw, cfg.flds);
+  return check_hip(hipGetLastError(), "cross_score_fused_kernel launch");
+}
+
 template <typename Tag, int D, int KTW>
 int launch_plan(const Config &cfg, const LayerTable &qt, const LayerTable &kt, const PlanPtrs &pp, const Ws &ws,
-                hipStream_t st, hipEvent_t *ev) {
+                void *ws_base, hipStream_t st, hipEvent_t *ev) {
   const Shape &s = cfg.sh;
   int rc;
   if ((rc = allow_lds(elite_select_kernel<Tag, D>, cfg.elite_lds))) return rc;
@@ -1238,6 +1355,13 @@ int launch_plan(const Config &cfg, const LayerTable &qt, const LayerTable &kt, c
                      ws);
   if ((rc = check_hip(hipGetLastError(), "elite_select_kernel launch"))) return rc;
   if ((rc = mark(ev, 1, st))) return rc;
+  if (cfg.chunked) {
+    // scoring, statistics, budgets and top-k in one launch
+    if ((rc = launch_chunked<Tag, D>(cfg, qt, kt, pp, ws, ws_base, st))) return rc;
+    if ((rc = mark(ev, 2, st))) return rc;
+    if ((rc = mark(ev, 3, st))) return rc;
+    return mark(ev, 4, st);
+  }
   if (cfg.rows_kt) {
     // scoring, statistics and budgets in one launch; the finalize stage is empty
     if (cfg.rows_kt == 4) rc = launch_rows<Tag, D, 4>(cfg, qt, kt, pp, ws, st);
@@ -1321,7 +1445,7 @@ int64_t aircache_max_compacted_elems(const aircache_desc *desc) {
 int32_t aircache_resolved_path(const aircache_desc *desc) {
   Config cfg;
   if (make_config(desc, &cfg) != AIRCACHE_OK) return -1;
-  return cfg.rows_kt ? AIRCACHE_PATH_ROWS : AIRCACHE_PATH_TILED;
+  return cfg.path;
 }
 
 int aircache_plan_profiled(const aircache_desc *desc, const void *const *q_txt, const void *const *k,
@@ -1345,10 +1469,10 @@ int aircache_plan_profiled(const aircache_desc *desc, const void *const *q_txt, 
   const Ws ws = ws_of(cfg, workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = desc->dtype == AIRCACHE_BF16;
-  if (bf && cfg.sh.D == 128) return launch_plan<Bf16Tag, 128, 4>(cfg, qt, kt, pp, ws, st, ev);
-  if (bf && cfg.sh.D == 64) return launch_plan<Bf16Tag, 64, 4>(cfg, qt, kt, pp, ws, st, ev);
-  if (!bf && cfg.sh.D == 128) return launch_plan<F32Tag, 128, 2>(cfg, qt, kt, pp, ws, st, ev);
-  return launch_plan<F32Tag, 64, 2>(cfg, qt, kt, pp, ws, st, ev);
+  if (bf && cfg.sh.D == 128) return launch_plan<Bf16Tag, 128, 4>(cfg, qt, kt, pp, ws, workspace, st, ev);
+  if (bf && cfg.sh.D == 64) return launch_plan<Bf16Tag, 64, 4>(cfg, qt, kt, pp, ws, workspace, st, ev);
+  if (!bf && cfg.sh.D == 128) return launch_plan<F32Tag, 128, 2>(cfg, qt, kt, pp, ws, workspace, st, ev);
+  return launch_plan<F32Tag, 64, 2>(cfg, qt, kt, pp, ws, workspace, st, ev);
 }
 
 int aircache_plan(const aircache_desc *desc, const void *const *q_txt, const void *const *k,

@@ -1,0 +1,919 @@
+// Steps 2-5 of the AirCache pass in one persistent launch ("chunked" path),
+// included by aircache.hip inside namespace aircache.
+//
+// Method: paper-notes page "AirCache: Activating Inter-Modal Relevancy KV
+// Cache Compression for Efficient Large Vision-Language Model Inference",
+// "Elite Observation Window" (the A_vtk and I_v equations) and "Layer-wise KV
+// Cache Budget Allocation" (the s_t, s_k and r_hat equations).
+//
+// Work item = (layer, sample, row group, column chunk): a workgroup takes a
+// run of columns (visual keys, then the elite text keys) of every KV head of
+// one (layer, sample) and up to four 16-row tiles of elite-query rows per KV
+// head. Its logits stay in registers. The exact softmax normaliser of a row
+// needs every chunk's contribution, so the chunks of one row group swap
+// per-row (max, sum) pairs through epoch-tagged records (no counter round
+// trip). A chunk's slice of I_v is then final (one row group) or the sum of
+// its row groups' partial column sums (the last row group to finish, a
+// counter election, adds them in order); with it go the slice's moments. The
+// last chunk of a sample (a counter election) combines the moments of all its
+// layers into s_t and s_k and computes the sample's budgets. After its items a
+// workgroup takes top-k tasks from a ticket counter; each waits for its
+// sample's budgets.
+//
+// All workgroups are co-resident (one 512-thread workgroup per CU, the LDS use
+// admitting no second), and a workgroup only waits for items that come no later
+// in the item order than its own or, in the top-k phase, for items every other
+// workgroup finishes before it takes a ticket; so every wait ends. Each wait
+// is also bounded: on expiry the kernel sets AIRCACHE_DEV_TIMEOUT and every
+// other wait of the launch gives up too.
+#pragma once
+
+constexpr int kFusedThreads = 512;
+constexpr int kFusedWaves = kFusedThreads / 64;
+constexpr int kFusedSlots = 24;      // logit registers per wave: key tiles x row tiles (f32x4 each)
+constexpr int kFusedRtMax = 4;       // row tiles per KV head in one item (query fragments in registers)
+constexpr int kFusedMaxItems = 256;  // work items one workgroup can take
+constexpr int kFusedTargetCus = 256; // workgroups the chunk schedule assumes at most
+constexpr int kFusedDigitBits = 5;   // radix digit of the top-k select
+constexpr int kFusedCntStride = 65;  // words per digit row of a wave's top-k counters (64 lanes + 1: no bank conflicts)
+constexpr int kFusedRingMin = kFusedWaves * (1 << kFusedDigitBits) * kFusedCntStride * 4;  // LDS the top-k counters need
+constexpr unsigned kSpinLimit = 1u << 20;  // polls of one wait before it gives up
+
+// Logit slots per wave for an item of rtp row tiles.
+__host__ __device__ constexpr int fused_slots(int rtp) { return kFusedSlots + 0 * rtp; }
+
+// One poll of a bounded wait. True when the wait must end: this one ran out
+// (the timeout bit is set) or another one in the launch already did.
+__device__ __forceinline__ bool spin_expired(unsigned &spins, int *status) {
+  if (++spins > kSpinLimit) {
+    atomicOr(status, AIRCACHE_DEV_TIMEOUT);
+    return true;
+  }
+  if ((spins & 255u) == 0u && (load_coherent(status) & AIRCACHE_DEV_TIMEOUT)) return true;
+  return false;
+}
+
+// Chunking of one (layer, sample) from its elite count and the launch-wide
+// cap kcap on key tiles per wave; the host sizes the workspace with it and
+// the device schedules with it. Columns are the N_v visual keys followed by
+// the N_tk elite text keys (the softmax runs over both); chunk c covers
+// columns [c * width, (c + 1) * width). A (layer, sample) with more elite rows
+// holds fewer key tiles per wave in registers, so it gets narrower chunks, and
+// beyond kFusedRtMax row tiles per KV head its rows split into row groups.
+struct ChunkPlan {
+  int rtg;      // 16-row tiles per KV head (G * N_tk rows), at least 1
+  int nrg;      // row groups
+  int rtp;      // row tiles per KV head in the largest row group
+  int ktw;      // key tiles per wave
+  int width;    // columns per chunk
+  int nchunks;  // chunks of the (layer, sample)
+};
+
+__host__ __device__ inline ChunkPlan fused_chunk_plan(int ntk, int G, int Nv, int wph, int kcap) {
+  ChunkPlan p;
+  const int rows = G * ntk;
+  p.rtg = rows > 0 ? (rows + 15) / 16 : 1;
+  p.nrg = (p.rtg + kFusedRtMax - 1) / kFusedRtMax;
+  p.rtp = p.rtg < kFusedRtMax ? p.rtg : kFusedRtMax;
+  const int ktmax = fused_slots(p.rtp) / p.rtp;
+  int k = kcap < ktmax ? kcap : ktmax;
+  if (k < 1) k = 1;
+  p.ktw = k;
+  p.width = wph * 16 * k;
+  const int cols = Nv + ntk;
+  p.nchunks = (cols + p.width - 1) / p.width;
+  return p;
+}
+
+// Smallest cap on key tiles per wave the launch may choose: with at most
+// kFusedTargetCus workgroups, a smaller cap cannot fit every chunk in one
+// round. The host sizes the workspace for this cap (the most chunks).
+__host__ __device__ inline int fused_kcap_min(int L, int B, int Nv, int wph) {
+  const long long k = (long long)L * B * Nv / ((long long)wph * 16 * kFusedTargetCus);
+  return k < 1 ? 1 : (k > kFusedSlots ? kFusedSlots : (int)k);
+}
+
+// Workspace of the chunked path (the counters are reset by elite_select_kernel,
+// which also advances the epoch; every record carries the epoch it was written
+// in, so stale records of earlier calls never match).
+struct FusedWs {
+  const unsigned *epoch;  // [1]
+  unsigned *cnt_b;        // [B] finished chunks per sample
+  unsigned *ticket;       // [1] top-k tasks handed out
+  unsigned *cnt_chunk;    // [L*B][max_chunks] finished row groups per chunk
+  uint64_t *xrec;         // [L*B][rec_stride][2] (row max | epoch << 32), (row sum | epoch << 32)
+  double *mom;            // [L*B][max_chunks][4] chunk sum, M2, M3, count
+  uint64_t *brec;         // [L*B] (budget | epoch << 32)
+  float *part;            // [L*B][max_chunks][max_rg][wmax] row-group column sums
+  int rec_stride;         // records per (layer, sample)
+  int max_chunks;         // chunks per (layer, sample) at most
+  int max_rg;             // row groups per (layer, sample) at most
+  int wmax;               // columns per chunk at most
+};
+
+// Dynamic LDS of cross_score_fused_kernel (byte offsets, 16-byte aligned).
+struct FusedLds {
+  int ring, el, colsum, red, mloc, wts, ctarget, item_lb, item_rc, total;
+};
+__host__ __device__ inline int fused_align16(int x) { return (x + 15) & ~15; }
+__host__ __device__ inline FusedLds fused_lds_layout(int tile_bytes, int ring_depth, int cap, int Hkv, int B) {
+  FusedLds f;
+  const int wph = kFusedWaves / Hkv;
+  int o = 0;
+  f.ring = o;
+  const int ring = kFusedWaves * ring_depth * tile_bytes;
+  o += fused_align16(ring > kFusedRingMin ? ring : kFusedRingMin);
+  f.el = o;
+  o += fused_align16(cap * 4);
+  f.colsum = o;
+  o += fused_align16(Hkv * wph * 16 * kFusedSlots * 4);
+  f.red = o;
+  o += fused_align16(kFusedWaves * kFusedRtMax * 16 * 4);
+  f.mloc = o;
+  o += fused_align16(Hkv * kFusedRtMax * 16 * 4);
+  f.wts = o;
+  o += fused_align16(Hkv * kFusedRtMax * 16 * 4);
+  f.ctarget = o;
+  o += fused_align16(B * 4);
+  f.item_lb = o;
+  o += fused_align16(kFusedMaxItems * 4);
+  f.item_rc = o;
+  o += fused_align16(kFusedMaxItems * 4);
+  f.total = o;
+  return f;
+}
+
+// The thread index, opaque to the optimiser: values derived from it are
+// recomputed where they are used instead of being hoisted out of the item
+// loop and kept live (and spilled) across the whole kernel.
+__device__ __forceinline__ int opaque_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// A value every lane of the wave holds, moved to a scalar register: buffer
+// resources and addresses built from it are then scalar too (a resource in
+// vector registers costs a loop over the distinct values of the wave).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// 2^x by the hardware instruction. Results below 2^-126 flush to zero, which
+// in a softmax weight (at most 1 against a row sum of at least 1) is far
+// below float32 resolution.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint64_t pack_rec(float v, unsigned epoch) {
+  return ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(v);
+}
+
+// Integer sum over the 64 lanes of a wave (wave-uniform result).
+__device__ __forceinline__ int wave_sum_i(int v) { return (int)wave_sum((float)v); }  // exact below 2^24
+
+// Block-wide exclusive scan over kFusedThreads threads (wtot: kFusedWaves ints).
+__device__ __forceinline__ int fused_block_scan(int v, int *wtot, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int w = 0; w < kFusedWaves; ++w) {
+    const int x = wtot[w];
+    if (w < wave) base += x;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
+}
+
+// Block-wide double sum over kFusedThreads threads in a fixed order.
+__device__ __forceinline__ double fused_block_sum_d(double v, double *red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum_d(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+  for (int w = 0; w < kFusedWaves; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// Everything an item needs to know about itself.
+struct FusedItem {
+  int l, b, plb, r, c, ntk;
+  ChunkPlan cp;
+  const void *q;  // layer's text queries
+  const void *k;  // layer's keys
+};
+
+// One item's row group: RTP row tiles per KV head starting at row tile rt0.
+// Stream the chunk's columns (visual keys, then the elite text keys) with the
+// logits in registers, exchange row (max, sum) with the other chunks of the
+// row group, and leave the column sums of exp2(S - M) / Z over the group's
+// rows, per KV head, in colsum.
+template <typename Tag, int D, int RTP>
+__device__ __forceinline__ void fused_pass(const Shape &sh, const FusedWs &fw, const FusedItem &it, int rt0,
+                                           unsigned char *lds, const FusedLds &lo, unsigned epoch, int *status,
+                                           bool first) {
+  using E = typename Tag::store_t;
+  constexpr int NW = kFusedWaves;
+  constexpr int KTMAX = fused_slots(RTP) / RTP;
+  constexpr int kTileBytes = 16 * D * Tag::kBytes;
+  constexpr int kDma = kTileBytes / 1024;
+  constexpr int kRing = (kTileBytes <= 4096) ? 3 : 2;
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, grp = lane >> 4;
+  const int Hkv = sh.Hkv, G = sh.G, Nv = sh.Nv;
+  const int wph = NW / Hkv;
+  const int g = wave / wph, sub = wave - g * wph;
+  const int ntk = it.ntk, Rg = G * ntk;
+  const int ncols = Nv + ntk;
+  const int ktw = it.cp.ktw, W = it.cp.width, c = it.c;
+  const int *el = reinterpret_cast<const int *>(lds + lo.el);
+  float *colsum = reinterpret_cast<float *>(lds + lo.colsum);
+  float *red = reinterpret_cast<float *>(lds + lo.red);
+  float *mloc = reinterpret_cast<float *>(lds + lo.mloc);
+  float *wts = reinterpret_cast<float *>(lds + lo.wts);
+  unsigned char *ring = lds + lo.ring + (size_t)wave * kRing * kTileBytes;
+  const E *kb = static_cast<const E *>(it.k) + (size_t)(it.b * Hkv + g) * sh.S * D;
+  const E *qb = static_cast<const E *>(it.q);
+
+  // query fragments of this wave's head, RTP tiles of 16 elite-query rows
+  Frag<Tag> qf[RTP][D / 32];
+#pragma unroll
+  for (int rt = 0; rt < RTP; ++rt) {
+    const int r = (rt0 + rt) * 16 + n;
+    if (r < Rg) {
+      const int hl = r / ntk, e = r - hl * ntk;
+      const E *qrow = qb + ((size_t)(it.b * sh.Hq + g * G + hl) * sh.Nt + el[e]) * D;
+#pragma unroll
+      for (int cc = 0; cc < D / 32; ++cc) qf[rt][cc].load(qrow + cc * 32 + grp * 8);
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < D / 32; ++cc) qf[rt][cc].zero();
+    }
+  }
+  // Key tiles of this wave: the contiguous run sub * ktw .. sub * ktw + ktw - 1
+  // of the chunk; column v < N_v is visual key v, N_v <= v < N_v + N_tk the
+  // elite text key el[v - N_v].
+  int vbase = c * W + sub * ktw * 16 + n;  // this lane's column in stage 0
+  asm volatile("" : "+v"(vbase));
+  auto stage = [&](int s) {
+    const int v = vbase + s * 16;
+    int row = v < Nv ? v : (v < ncols ? Nv + el[v - Nv] : Nv - 1);
+    asm volatile("" : "+v"(row));
+    const unsigned char *src = reinterpret_cast<const unsigned char *>(kb + (size_t)row * D);
+    unsigned char *slot = ring + (s % kRing) * kTileBytes;
+    if (s >= kRing) wait_lds_reads();
+#pragma unroll
+    for (int j = 0; j < kDma; ++j) load_lds16(src + 16 * grp + 64 * j, slot + 1024 * j);
+  };
+  f32x4_t S[KTMAX][RTP];
+#pragma unroll
+  for (int s = 0; s < kRing; ++s)
+    if (s < ktw) stage(s);
+#pragma unroll
+  for (int s = 0; s < KTMAX; ++s) {
+    if (s < ktw) {
+      const int ahead = ktw - 1 - s;
+      wait_tiles<kDma>(ahead < kRing - 1 ? ahead : kRing - 1);
+      f32x4_t acc[RTP];
+#pragma unroll
+      for (int rt = 0; rt < RTP; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const unsigned char *slot = ring + (s % kRing) * kTileBytes;
+#pragma unroll
+      for (int cc = 0; cc < D / 32; ++cc) {
+        Frag<Tag> kf;
+        LdsTile<Tag>::read(kf, slot, cc, lane);
+#pragma unroll
+        for (int rt = 0; rt < RTP; ++rt) mfma_slice(acc[rt], qf[rt][cc], kf);
+      }
+      if (s + kRing < ktw) stage(s + kRing);
+      const bool ok = vbase + s * 16 < ncols;
+#pragma unroll
+      for (int rt = 0; rt < RTP; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[s][rt][i] = ok ? acc[rt][i] * sh.scale2 : -INFINITY;
+    }
+  }
+  // chunk-local row maxima: keys of a lane row (DPP), then the head's waves in order
+  constexpr int RW = RTP * 16;  // rows of one head in this pass
+#pragma unroll
+  for (int rt = 0; rt < RTP; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < KTMAX; ++s)
+        if (s < ktw) m = fmaxf(m, S[s][rt][i]);
+      m = row16_max(m);
+      if (n == 0) red[wave * RW + rt * 16 + grp * 4 + i] = m;
+    }
+  __syncthreads();
+  if (tid < Hkv * RW) {
+    const int gg = tid / RW, rr = tid - gg * RW;
+    float m = red[(gg * wph) * RW + rr];
+    for (int w = 1; w < wph; ++w) m = fmaxf(m, red[(gg * wph + w) * RW + rr]);
+    mloc[gg * RW + rr] = m;
+  }
+  __syncthreads();
+  // exponentials in place and chunk-local row sums
+#pragma unroll
+  for (int rt = 0; rt < RTP; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float M = mloc[g * RW + rt * 16 + grp * 4 + i];
+      float z = 0.f;
+#pragma unroll
+      for (int s = 0; s < KTMAX; ++s)
+        if (s < ktw) {
+          const float ev = exp2_fast(S[s][rt][i] - M);
+          S[s][rt][i] = ev;
+          z += ev;
+        }
+      z = row16_sum(z);
+      if (n == 0) red[wave * RW + rt * 16 + grp * 4 + i] = z;
+    }
+  __syncthreads();
+  // publish this chunk's (max, sum) per row, then merge every chunk's pair in
+  // chunk order into the row's normaliser
+  if (tid < Hkv * RW) {
+    const int gg = tid / RW, rr = tid - gg * RW;
+    float z = 0.f;
+    for (int w = 0; w < wph; ++w) z += red[(gg * wph + w) * RW + rr];
+    const float m_own = mloc[gg * RW + rr];
+    const int row = rt0 * 16 + rr;
+    const int rows_h = it.cp.rtg * 16;
+    const size_t rbase = (size_t)it.plb * fw.rec_stride;
+    uint64_t *rec = fw.xrec + 2 * (rbase + ((size_t)c * Hkv + gg) * rows_h + row);
+    store_coherent(rec, pack_rec(m_own, epoch));
+    store_coherent(rec + 1, pack_rec(z, epoch));
+    const auto rsrc = coherent_rsrc(fw.xrec + 2 * rbase, (unsigned)((size_t)fw.rec_stride * 16));
+    float M = -INFINITY, Z = 0.f;
+    const int nch = it.cp.nchunks;
+    constexpr int kXB = 4;  // records in flight per thread
+    for (int c0 = 0; c0 < nch; c0 += kXB) {
+      uint64_t rm[kXB], rz[kXB];
+#pragma unroll
+      for (int j = 0; j < kXB; ++j) {
+        const int cj = c0 + j;
+        const unsigned off = (unsigned)((((size_t)cj * Hkv + gg) * rows_h + row) * 16);
+        if (cj < nch && cj != c) {
+          rm[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rsrc, (int)off, 0, 16));
+          rz[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rsrc, (int)off + 8, 0, 16));
+        } else {
+          rm[j] = pack_rec(m_own, epoch);
+          rz[j] = pack_rec(z, epoch);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kXB; ++j) {
+        const int cj = c0 + j;
+        if (cj >= nch) break;
+        const unsigned off = (unsigned)((((size_t)cj * Hkv + gg) * rows_h + row) * 16);
+        unsigned spins = 0;
+        while ((unsigned)(rm[j] >> 32) != epoch || (unsigned)(rz[j] >> 32) != epoch) {
+          if (spin_expired(spins, status)) break;
+          __builtin_amdgcn_s_sleep(2);
+          rm[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rsrc, (int)off, 0, 16));
+          rz[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rsrc, (int)off + 8, 0, 16));
+        }
+        const float mj = __uint_as_float((unsigned)rm[j]), zj = __uint_as_float((unsigned)rz[j]);
+        if (mj > -INFINITY) {
+          const float mn = fmaxf(M, mj);
+          Z = Z * exp2_fast(M - mn) + zj * exp2_fast(mj - mn);
+          M = mn;
+        }
+      }
+    }
+    wts[gg * RW + rr] = (row < Rg && Z > 0.f) ? exp2_fast(m_own - M) / Z : 0.f;
+  }
+  __syncthreads();
+  // column sums of this pass over the head's rows; one wave owns a column
+  int cbase = g * W + sub * ktw * 16 + n;
+  asm volatile("" : "+v"(cbase));
+  float *cs_lane = colsum + cbase;
+#pragma unroll
+  for (int s = 0; s < KTMAX; ++s) {
+    if (s < ktw) {
+      float v = 0.f;
+#pragma unroll
+      for (int rt = 0; rt < RTP; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v += S[s][rt][i] * wts[g * RW + rt * 16 + grp * 4 + i];
+      v = sum_across_rows(v);
+      // text columns are summed too and never read
+      if (grp == 0) cs_lane[s * 16] = first ? v : cs_lane[s * 16] + v;
+    }
+  }
+  __syncthreads();
+}
+
+// Moments of a run of values, combined pairwise (Chan, Golub and LeVeque's
+// update, extended to the third central moment): count, mean, M2 and M3.
+struct Moments {
+  double n, mean, m2, m3;
+};
+__device__ __forceinline__ Moments combine_moments(const Moments &a, const Moments &b) {
+  if (b.n == 0.0) return a;
+  if (a.n == 0.0) return b;
+  Moments r;
+  const double n = a.n + b.n, inv = 1.0 / n, d = b.mean - a.mean;
+  const double db = d * b.n * inv;  // mean shift
+  r.n = n;
+  r.mean = a.mean + db;
+  r.m2 = a.m2 + b.m2 + d * db * a.n;
+  r.m3 = a.m3 + b.m3 + d * d * db * a.n * (a.n - b.n) * inv + 3.0 * d * (a.n * b.m2 - b.n * a.m2) * inv;
+  return r;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: a scan inside each row of
+// 16 lanes by DPP row shifts, then the row totals added in with readlane.
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  const int lane = threadIdx.x & 63;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  // totals of rows 0, 1 and 2 (read before any row is offset)
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  if (lane >= 16) v += r0;
+  if (lane >= 32) v += r1;
+  if (lane >= 48) v += r2;
+  return v;
+}
+
+// Top-r_hat of one (layer, sample) by the 512 threads of a workgroup: thread
+// t holds the keys of indices t, t + 512, t + 1024, ... in registers (each load
+// instruction reads 64 consecutive scores per wave). I_v >= 0, so the float32
+// bits order like the values. MSB-first radix select finds the key T of the
+// r_hat-th largest score: the bits above the highest bit in which the minimum
+// and maximum keys differ are common to all keys and skipped; each pass counts
+// the next (up to) kFusedDigitBits bits of the keys that match the prefix
+// found so far, every lane into counters of its own in LDS (rows padded to 65
+// words keep lanes on distinct banks), lane d of each wave adds up one digit
+// over its wave, and after one barrier every wave adds the waves' totals,
+// takes a prefix sum over the digits and finds the digit holding the r_hat-th
+// key (all waves reach the same answer, so no second barrier). Kept: every key
+// > T plus the lowest-index keys equal to T up to r_hat, in ascending index
+// order: each 64-index run of a wave is ranked with a ballot and the runs are
+// placed by their counts. Equal scores thus go to the lower index.
+// cnt: kFusedRingMin bytes of LDS (the waves' counters), zero on entry and exit.
+template <int PER>
+__device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, int kbud, int32_t *kept,
+                                           unsigned *cnt) {
+  constexpr int NT = kFusedThreads, NW = kFusedWaves;
+  constexpr int ND = 1 << kFusedDigitBits;
+  constexpr int CS = kFusedCntStride;
+  __shared__ unsigned wdig[2][NW][ND];
+  __shared__ float wmm[2][NW];
+  __shared__ int rowcnt[2][PER][NW];
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int Nv = sh.Nv;
+  if (kbud <= 0) return;
+  if (kbud >= Nv) {
+    for (int i = tid; i < Nv; i += NT) kept[i] = i;
+    return;
+  }
+  const auto riv = coherent_rsrc(iv_l, (unsigned)(Nv * sizeof(float)));
+  unsigned key[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p)
+    key[p] = (p * NT + tid < Nv) ? (unsigned)load_sc1_i(riv, (unsigned)((p * NT + tid) * sizeof(float))) : 0u;
+  unsigned *wc = cnt + (size_t)wave * ND * CS;  // this wave's [digit][lane] counters
+  float fmin = INFINITY, fmax = 0.f;             // keys as floats: same order
+#pragma unroll
+  for (int p = 0; p < PER; ++p)
+    if (p * NT + tid < Nv) {
+      fmin = fminf(fmin, __uint_as_float(key[p]));
+      fmax = fmaxf(fmax, __uint_as_float(key[p]));
+    }
+  fmin = -wave_max(-fmin);
+  fmax = wave_max(fmax);
+  if (lane == 0) {
+    wmm[0][wave] = fmin;
+    wmm[1][wave] = fmax;
+  }
+  __syncthreads();
+  fmin = wmm[0][0];
+  fmax = wmm[1][0];
+  for (int w = 1; w < NW; ++w) {
+    fmin = fminf(fmin, wmm[0][w]);
+    fmax = fmaxf(fmax, wmm[1][w]);
+  }
+  const unsigned kmin = __float_as_uint(fmin), kmax = __float_as_uint(fmax);
+  const unsigned diff = kmin ^ kmax;
+  int hb = diff ? 31 - __clz((int)diff) : -1;  // highest bit in which keys can differ
+  unsigned mask = (hb < 0) ? 0xffffffffu : (hb >= 31) ? 0u : ~((2u << hb) - 1u);
+  unsigned prefix = kmin & mask;
+  int need = kbud;  // keys still to take among those matching the prefix
+  int par = 0;
+  while (hb >= 0) {
+    const int width = min(kFusedDigitBits, hb + 1);
+    const int shift = hb + 1 - width;
+    const unsigned dmask = (1u << width) - 1u;
+#pragma unroll
+    for (int p = 0; p < PER; ++p)
+      if (p * NT + tid < Nv && (key[p] & mask) == prefix)
+        atomicAdd(&wc[((key[p] >> shift) & dmask) * CS + lane], 1u);
+    if (lane < ND) {
+      unsigned *row = wc + lane * CS;  // digit lane of this wave
+      unsigned t = 0;
+#pragma unroll
+      for (int h = 0; h < 64; h += 32) {
+        unsigned v[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) v[j] = row[h + j];  // reads in flight together
+#pragma unroll
+        for (int j = 0; j < 32; ++j) t += v[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 64; ++j) row[j] = 0u;
+      wdig[par][wave][lane] = t;
+    }
+    __syncthreads();
+    // every wave: lane q holds digit ND - 1 - q (descending) summed over waves
+    int c = 0;
+    if (lane < ND)
+      for (int w = 0; w < NW; ++w) c += (int)wdig[par][w][ND - 1 - lane];
+    const int incl = wave_scan_incl(c);
+    const int above = incl - c;  // matching keys with a larger digit
+    const unsigned long long hit = __ballot(lane < ND && above < need && above + c >= need);
+    const int q = hit ? __ffsll((long long)hit) - 1 : 0;
+    prefix |= (unsigned)(ND - 1 - q) << shift;
+    mask |= dmask << shift;
+    need -= __builtin_amdgcn_readlane(above, q);
+    hb -= width;
+    par ^= 1;
+  }
+  const unsigned T = prefix;
+  // per run (p, wave) of 64 indices: keys equal to T, then keys kept
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  unsigned long long meq[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    meq[p] = __ballot(p * NT + tid < Nv && key[p] == T);
+    if (lane == 0) rowcnt[0][p][wave] = __popcll(meq[p]);
+  }
+  __syncthreads();
+  int eq_base = 0;  // keys equal to T at lower indices than this wave's run
+  unsigned long long mk[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    int before = 0, row = 0;
+    for (int w = 0; w < NW; ++w) {
+      const int x = rowcnt[0][p][w];
+      before += (w < wave) ? x : 0;
+      row += x;
+    }
+    const bool valid = p * NT + tid < Nv;
+    const bool eq = (meq[p] >> lane) & 1ull;
+    const int eq_rank = eq_base + before + __popcll(meq[p] & lt);
+    mk[p] = __ballot(valid && (key[p] > T || (eq && eq_rank < need)));
+    if (lane == 0) rowcnt[1][p][wave] = __popcll(mk[p]);
+    eq_base += row;
+  }
+  __syncthreads();
+  int base = 0;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    int before = 0, row = 0;
+    for (int w = 0; w < NW; ++w) {
+      const int x = rowcnt[1][p][w];
+      before += (w < wave) ? x : 0;
+      row += x;
+    }
+    if ((mk[p] >> lane) & 1ull) kept[base + before + __popcll(mk[p] & lt)] = p * NT + tid;
+    base += row;
+  }
+}
+
+// Wait for the budget record of plan index plb; returns the budget.
+__device__ __forceinline__ int fused_wait_budget(const FusedWs &fw, int plb, unsigned epoch, int *status) {
+  const auto rb = coherent_rsrc(fw.brec + plb, 8u);
+  uint64_t v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rb, 0, 0, 16));
+  unsigned spins = 0;
+  while ((unsigned)(v >> 32) != epoch) {
+    if (spin_expired(spins, status)) break;
+    __builtin_amdgcn_s_sleep(8);
+    v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rb, 0, 0, 16));
+  }
+  return (int)(unsigned)v;
+}
+
+template <typename Tag, int D>
+__global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape sh, LayerTable qt, LayerTable kt,
+                                                                          PlanPtrs plan, FusedWs fw, FusedLds lo) {
+  extern __shared__ __attribute__((aligned(16))) float lds_f[];
+  unsigned char *lds = reinterpret_cast<unsigned char *>(lds_f);
+  __shared__ int wtot[kFusedWaves];
+  __shared__ double redd[kFusedWaves];
+  __shared__ double lst[AIRCACHE_MAX_LAYERS], lsk[AIRCACHE_MAX_LAYERS];
+  __shared__ BudgetSums sums;
+  __shared__ int bcast[4];
+  const int tid = threadIdx.x;
+  const int L = sh.L, B = sh.B, Nv = sh.Nv;
+  const int wph = kFusedWaves / sh.Hkv;
+  const unsigned epoch = *fw.epoch;
+  const int P = gridDim.x, me = blockIdx.x;
+  int *ctarget = reinterpret_cast<int *>(lds + lo.ctarget);
+  int *item_lb = reinterpret_cast<int *>(lds + lo.item_lb);
+  int *item_rc = reinterpret_cast<int *>(lds + lo.item_rc);
+  auto elite_count = [&](int plb) {
+    const int t = plan.n_elite[plb];
+    return t < 0 ? 0 : (t > sh.cap ? sh.cap : t);
+  };
+
+  // Schedule, worked out by wave 0 alone (no block barriers): lane q holds
+  // the (b, l) pairs q * per .. q * per + per - 1 in sample-major order.
+  // Cap on key tiles per wave: the smallest (narrowest chunks, most
+  // workgroups busy) whose items all fit one round of the grid, the widest
+  // when none does; a binary search, items being non-increasing in the cap.
+  // Items go in the order (b, l, row group, chunk); this workgroup takes items
+  // me, me + P, me + 2P, ... ctarget[b]: chunks of sample b (the finisher
+  // election's count).
+  __shared__ int sched[2];
+  if (tid < 64) {
+    const int lane = tid;
+    const int LB = L * B;
+    const int per = (LB + 63) / 64;
+    for (int b = lane; b < B; b += 64) ctarget[b] = 0;
+    int ntk[8];  // per <= 8: L * B <= 512
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int s = lane * per + j;
+      ntk[j] = 0;
+      if (j < per && s < LB) {
+        const int b = s / L, l = s - b * L;
+        ntk[j] = elite_count(l * B + b);
+      }
+    }
+    const int P_sched = P < kFusedTargetCus ? P : kFusedTargetCus;
+    int lo_k = fused_kcap_min(L, B, Nv, wph), hi_k = kFusedSlots;
+    while (lo_k < hi_k) {
+      const int mid = (lo_k + hi_k) >> 1;
+      int n = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < per && lane * per + j < LB) {
+          const ChunkPlan cp = fused_chunk_plan(ntk[j], sh.G, Nv, wph, mid);
+          n += cp.nrg * cp.nchunks;
+        }
+      if (wave_sum_i(n) <= P_sched) hi_k = mid;
+      else lo_k = mid + 1;
+    }
+    const int kc = lo_k;
+    int nit[8], nch[8], tot = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      nit[j] = nch[j] = 0;
+      if (j < per && lane * per + j < LB) {
+        const ChunkPlan cp = fused_chunk_plan(ntk[j], sh.G, Nv, wph, kc);
+        nch[j] = cp.nchunks;
+        nit[j] = cp.nrg * cp.nchunks;
+      }
+      tot += nit[j];
+    }
+    const int incl = wave_incl_scan(tot);
+    int start = incl - tot;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int s = lane * per + j;
+      if (j < per && s < LB) {
+        atomicAdd(&ctarget[s / L], nch[j]);
+        int first = me - start;  // first item index >= start congruent to me mod P
+        first = start + ((first % P) + P) % P;
+        for (int i = first; i < start + nit[j]; i += P) {
+          const int k = (i - me) / P;
+          if (k < kFusedMaxItems) {
+            item_lb[k] = s;
+            item_rc[k] = i - start;
+          }
+        }
+        start += nit[j];
+      }
+    }
+    if (lane == 63) {
+      sched[0] = kc;
+      sched[1] = incl;  // items in all
+    }
+  }
+  __syncthreads();
+  const int kcap = uniform(sched[0]);
+  const int run = uniform(sched[1]);
+  int nmine = (me < run) ? (run - me + P - 1) / P : 0;
+  if (nmine > kFusedMaxItems) {
+    if (tid == 0) atomicOr(plan.status, AIRCACHE_DEV_TIMEOUT);
+    nmine = kFusedMaxItems;
+  }
+
+  for (int k = 0; k < nmine; ++k) {
+    const int tid = opaque_tid();
+    FusedItem it;
+    const int s = uniform(item_lb[k]);
+    it.b = s / L;
+    it.l = s - it.b * L;
+    it.plb = it.l * B + it.b;
+    it.ntk = uniform(elite_count(it.plb));
+    it.cp = fused_chunk_plan(it.ntk, sh.G, Nv, wph, kcap);
+    const int local = uniform(item_rc[k]);
+    it.r = local / it.cp.nchunks;
+    it.c = local - it.r * it.cp.nchunks;
+    it.q = qt.p[it.l];
+    it.k = kt.p[it.l];
+    int *el = reinterpret_cast<int *>(lds + lo.el);
+    __syncthreads();  // the previous item is done with the LDS
+    for (int i = tid; i < it.ntk; i += kFusedThreads) el[i] = plan.elite[(size_t)it.plb * sh.Nt + i];
+    __syncthreads();
+    {
+      const int rt0 = it.r * kFusedRtMax, left = it.cp.rtg - rt0;
+      if (left >= 4) fused_pass<Tag, D, 4>(sh, fw, it, rt0, lds, lo, epoch, plan.status, true);
+      else if (left == 3) fused_pass<Tag, D, 3>(sh, fw, it, rt0, lds, lo, epoch, plan.status, true);
+      else if (left == 2) fused_pass<Tag, D, 2>(sh, fw, it, rt0, lds, lo, epoch, plan.status, true);
+      else fused_pass<Tag, D, 1>(sh, fw, it, rt0, lds, lo, epoch, plan.status, true);
+    }
+
+    // Column sums of this item's rows over the KV heads (in order); with one
+    // row group they are the chunk's I_v * H_q * N_tk, else the last row group
+    // of the chunk adds every group's sums in order.
+    const float *colsum = reinterpret_cast<const float *>(lds + lo.colsum);
+    const int W = it.cp.width, c0 = it.c * W;
+    const int ncol = max(0, min(W, Nv - c0));  // visual columns of the chunk
+    float ivv[8];                                // W <= 8 * kFusedThreads
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int col = tid + j * kFusedThreads;
+      float a = 0.f;
+      if (col < ncol)
+        for (int g = 0; g < sh.Hkv; ++g) a += colsum[g * W + col];
+      ivv[j] = a;
+    }
+    if (it.cp.nrg > 1) {
+      const size_t slot = (size_t)it.plb * fw.max_chunks + it.c;
+      float *pr = fw.part + (slot * fw.max_rg + it.r) * fw.wmax;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int col = tid + j * kFusedThreads;
+        if (col < ncol) store_coherent(&pr[col], ivv[j]);
+      }
+      wait_all_memory();
+      __syncthreads();
+      if (tid == 0) bcast[3] = (counter_add(&fw.cnt_chunk[slot], 1u) == (unsigned)it.cp.nrg - 1u);
+      __syncthreads();
+      if (!uniform(bcast[3])) continue;
+      const auto rp = coherent_rsrc(fw.part + slot * fw.max_rg * fw.wmax,
+                                    (unsigned)((size_t)fw.max_rg * fw.wmax * sizeof(float)));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int col = tid + j * kFusedThreads;
+        float a = 0.f;
+        if (col < ncol)
+          for (int r = 0; r < it.cp.nrg; ++r) a += load_sc1_f(rp, (unsigned)((r * fw.wmax + col) * sizeof(float)));
+        ivv[j] = a;
+      }
+    }
+    const float inv_rows = (it.ntk > 0) ? 1.f / (float)(sh.Hq * it.ntk) : 0.f;
+    double sum = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int col = tid + j * kFusedThreads;
+      if (col < ncol) {
+        const float a = ivv[j] * inv_rows;
+        ivv[j] = a;
+        store_coherent(&plan.iv[(size_t)it.plb * Nv + c0 + col], a);
+        sum += (double)a;
+      }
+    }
+    sum = fused_block_sum_d(sum, redd);
+    const double mean = ncol > 0 ? sum / (double)ncol : 0.0;
+    double m2 = 0.0, m3 = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int col = tid + j * kFusedThreads;
+      if (col < ncol) {
+        const double d = (double)ivv[j] - mean;
+        m2 += d * d;
+        m3 += d * d * d;
+      }
+    }
+    m2 = fused_block_sum_d(m2, redd);
+    m3 = fused_block_sum_d(m3, redd);
+    if (tid == 0) {
+      double *mr = fw.mom + ((size_t)it.plb * fw.max_chunks + it.c) * 4;
+      store_coherent(mr + 0, sum);
+      store_coherent(mr + 1, m2);
+      store_coherent(mr + 2, m3);
+      store_coherent(mr + 3, (double)ncol);
+    }
+    wait_all_memory();
+    __syncthreads();
+    if (tid == 0) bcast[0] = (counter_add(&fw.cnt_b[it.b], 1u) == (unsigned)ctarget[it.b] - 1u);
+    __syncthreads();
+    if (!uniform(bcast[0])) continue;
+
+    // Last chunk of sample b: per-layer statistics from the chunks' moments
+    // (pairwise combination in a fixed tree order), then the sample's budgets.
+    const int b = it.b;
+    const int mc = fw.max_chunks;
+    double *momc = reinterpret_cast<double *>(lds + lo.ring);  // [L][mc][5]
+    {
+      const auto rm = coherent_rsrc(fw.mom, (unsigned)((size_t)L * B * mc * 32));
+      for (int i = tid; i < L * mc; i += kFusedThreads) {
+        const int l = i / mc, cc = i - l * mc, plb = l * B + b;
+        const int nch = fused_chunk_plan(elite_count(plb), sh.G, Nv, wph, kcap).nchunks;
+        double v[4] = {0.0, 0.0, 0.0, 0.0};
+        if (cc < nch) {
+          const unsigned off = (unsigned)(((size_t)plb * mc + cc) * 32);
+#pragma unroll
+          for (int f = 0; f < 4; ++f) v[f] = load_sc1_d(rm, off + 8u * f);
+        }
+        // LDS slots: 0 sum, 1 count, 2 mean, 3 M2, 4 M3
+        double *m = momc + (size_t)i * 5;
+        m[0] = v[0];
+        m[1] = v[3];
+        m[2] = v[3] > 0.0 ? v[0] / v[3] : 0.0;
+        m[3] = v[1];
+        m[4] = v[2];
+      }
+    }
+    __syncthreads();
+    // tree: at stride st, chunk cc (a multiple of 2 st) absorbs chunk cc + st
+    for (int st = 1; st < mc; st <<= 1) {
+      for (int i = tid; i < L * mc; i += kFusedThreads) {
+        const int l = i / mc, cc = i - l * mc;
+        if ((cc & (2 * st - 1)) == 0 && cc + st < mc) {
+          double *a = momc + (size_t)i * 5, *bb = momc + (size_t)(i + st) * 5;
+          const Moments m = combine_moments(Moments{a[1], a[2], a[3], a[4]}, Moments{bb[1], bb[2], bb[3], bb[4]});
+          a[0] = a[0] + bb[0];
+          a[1] = m.n;
+          a[2] = m.mean;
+          a[3] = m.m2;
+          a[4] = m.m3;
+        }
+        (void)l;
+      }
+      __syncthreads();
+    }
+    if (tid < L) {
+      const int l = tid, plb = l * B + b;
+      const double *a = momc + (size_t)l * mc * 5;
+      const double st = a[0], M2 = a[3], M3 = a[4];
+      const double sigma = sqrt(M2 / (double)(Nv - 1));
+      const double sk = (sigma > 0.0) ? (M3 / (sigma * sigma * sigma)) *
+                                            ((double)Nv / ((double)(Nv - 1) * (double)(Nv - 2)))
+                                      : 0.0;
+      plan.s_t[plb] = st;
+      plan.s_k[plb] = sk;
+      lst[l] = st;
+      lsk[l] = sk;
+    }
+    __syncthreads();
+    if (tid == 0) sums = budget_sums(L, lst, lsk);
+    __syncthreads();
+    if (tid < L) {
+      const int plb = tid * B + b;
+      double x;
+      int bud;
+      layer_budget(sh, sums, lst[tid], lsk[tid], &x, &bud);
+      if (plan.bx) plan.bx[plb] = x;
+      plan.budget[plb] = bud;
+      store_coherent(&fw.brec[plb], ((uint64_t)epoch << 32) | (uint64_t)(unsigned)bud);
+    }
+  }
+
+  // Top-k tasks, in sample-major order, handed out by ticket.
+  unsigned *cnt = reinterpret_cast<unsigned *>(lds + lo.ring);
+  {
+    const int tid = opaque_tid();
+    __syncthreads();  // every wave is done with the item LDS
+    for (int i = tid; i < kFusedWaves * (1 << kFusedDigitBits) * kFusedCntStride; i += kFusedThreads) cnt[i] = 0u;
+  }
+  for (;;) {
+    const int tid = opaque_tid();
+    __syncthreads();
+    if (tid == 0) bcast[1] = (int)counter_add(fw.ticket, 1u);
+    __syncthreads();
+    const int task = uniform(bcast[1]);
+    if (task >= L * B) break;
+    const int b = task / L, l = task - b * L, plb = l * B + b;
+    if (tid == 0) {
+      bcast[2] = fused_wait_budget(fw, plb, epoch, plan.status);
+      int64_t off = 0;
+      for (int bb = 0; bb < b; ++bb)
+        off += (int64_t)sh.Hkv * (fused_wait_budget(fw, l * B + bb, epoch, plan.status) + sh.Nt) * sh.D;
+      plan.out_off[(size_t)l * (B + 1) + b] = off;
+      if (b == B - 1) plan.out_off[(size_t)l * (B + 1) + B] = off + (int64_t)sh.Hkv * (bcast[2] + sh.Nt) * sh.D;
+      if (plan.n_elite[plb] > sh.cap) atomicOr(plan.status, AIRCACHE_DEV_ELITE_OVERFLOW);
+    }
+    __syncthreads();
+    int kbud = uniform(bcast[2]);
+    if (kbud < 0) kbud = 0;
+    if (kbud > Nv) kbud = Nv;
+    const float *ivl = plan.iv + (size_t)plb * Nv;
+    int32_t *kp = plan.kept + (size_t)plb * Nv;
+    if (Nv <= 2048) block_topk<4>(sh, ivl, kbud, kp, cnt);
+    else if (Nv <= 4096) block_topk<8>(sh, ivl, kbud, kp, cnt);
+    else block_topk<16>(sh, ivl, kbud, kp, cnt);
+  }
+}

@@ -47,11 +47,18 @@ def torch_dtype(w):
     return torch.float32 if w.dtype == wl.F32 else torch.bfloat16
 
 
-def run_gpu(inp: wl.Inputs, alpha=None, ratio=None, max_elite=0, tensors=None, compress=True, path="auto"):
+def make_aircache(w, alpha=None, ratio=None, max_elite=0, path="auto"):
+    return AirCache(w.L, w.B, w.Hq, w.Hkv, w.D, w.Nv, w.Nt, dtype=torch_dtype(w),
+                    alpha=w.alpha if alpha is None else alpha,
+                    ratio=w.ratio if ratio is None else ratio, max_elite=max_elite, path=path)
+
+
+def run_gpu(inp: wl.Inputs, alpha=None, ratio=None, max_elite=0, tensors=None, compress=True, path="auto", ac=None):
+    """Plan (and compress) on the GPU; ac: an AirCache to reuse (its workspace
+    carries state from earlier calls)."""
     w = inp.w
-    ac = AirCache(w.L, w.B, w.Hq, w.Hkv, w.D, w.Nv, w.Nt, dtype=torch_dtype(w),
-                  alpha=w.alpha if alpha is None else alpha,
-                  ratio=w.ratio if ratio is None else ratio, max_elite=max_elite, path=path)
+    if ac is None:
+        ac = make_aircache(w, alpha, ratio, max_elite, path)
     q, k, v = tensors if tensors is not None else to_torch(inp)
     plan = ac.plan(q, k)
     out = {}

@@ -56,18 +56,28 @@ def test_workspace_size(lib):
 
 
 def test_resolved_path(lib):
-    # rows path while N_v fits 8 waves x 16 keys x 24 tiles (3072 keys), else tiled
-    assert _lib.resolved_path(desc()) == _lib.PATH_ROWS
-    assert _lib.resolved_path(desc(n_vis=3072)) == _lib.PATH_ROWS
-    assert _lib.resolved_path(desc(n_vis=3073)) == _lib.PATH_TILED
+    # chunked for 1, 2, 4 or 8 KV heads; else rows while N_v fits 8 waves x 16
+    # keys x 24 tiles (3072 keys); else tiled
+    assert _lib.resolved_path(desc()) == _lib.PATH_CHUNKED
+    assert _lib.resolved_path(desc(n_vis=6272, n_txt=256)) == _lib.PATH_CHUNKED
+    for hkv in (1, 2, 8):
+        assert _lib.resolved_path(desc(n_q_heads=8 * hkv, n_kv_heads=hkv)) == _lib.PATH_CHUNKED
+    assert _lib.resolved_path(desc(n_kv_heads=7)) == _lib.PATH_ROWS
+    assert _lib.resolved_path(desc(n_kv_heads=7, n_vis=3072)) == _lib.PATH_ROWS
+    assert _lib.resolved_path(desc(n_kv_heads=7, n_vis=3073)) == _lib.PATH_TILED
+    assert _lib.resolved_path(desc(n_q_heads=32, n_kv_heads=32)) == _lib.PATH_ROWS
     assert _lib.resolved_path(desc(path=1)) == _lib.PATH_TILED
+    assert _lib.resolved_path(desc(path=2)) == _lib.PATH_ROWS
     assert _lib.resolved_path(desc(path=2, n_vis=17)) == _lib.PATH_ROWS
+    assert _lib.resolved_path(desc(path=3, n_vis=17)) == _lib.PATH_CHUNKED
+    assert _lib.resolved_path(desc(path=3, n_kv_heads=7)) == -1
+    assert _lib.resolved_path(desc(path=2, n_vis=3073)) == -1
 
 
 @pytest.mark.parametrize("bad", [dict(n_layers=0), dict(n_layers=129), dict(batch=0), dict(n_kv_heads=5),
                                  dict(head_dim=96), dict(n_vis=2), dict(n_vis=9000), dict(n_txt=0),
                                  dict(dtype="x"), dict(alpha=1.5), dict(alpha=float("nan")),
-                                 dict(ratio=-0.1), dict(max_elite=129), dict(n_txt=4000), dict(path=3),
+                                 dict(ratio=-0.1), dict(max_elite=129), dict(n_txt=4000), dict(path=4),
                                  dict(path=2, n_vis=4000)])
 def test_invalid_descriptor(lib, bad):
     if bad.get("dtype") == "x":

@@ -1,9 +1,11 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle on the GPU.
 
 Full-size workloads 1-5 (every seed for 1-3, the headline seed for 4-5) in the
-launch configuration the benchmark times, plus small edge shapes: ragged
-tails, one KV head, MHA, head_dim 64, float32 and bfloat16, a single text
-token, alpha and ratio at their extremes, zero queries and several samples.
+launch configuration the benchmark times, each scoring path on the workloads
+it serves, plus small edge shapes: ragged tails, one and eight KV heads, MHA,
+head_dim 64, float32 and bfloat16, a single text token, alpha and ratio at
+their extremes, zero queries (every text token elite, several row passes),
+several samples, and a workspace reused across calls.
 """
 import numpy as np
 import pytest
@@ -38,11 +40,13 @@ def test_workload(cid, seed):
     print(f"[parity] workload {cid} seed {seed}: {rep}", flush=True)
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 5])
-def test_workload_tiled_path(cid):
-    """The general tiled path on the workloads the rows path serves by default."""
+@pytest.mark.parametrize("path,cid", [("tiled", 1), ("tiled", 2), ("tiled", 3), ("tiled", 5),
+                                      ("rows", 1), ("rows", 3), ("rows", 5), ("chunked", 4)])
+def test_workload_other_paths(path, cid):
+    """The scoring paths auto does not pick, on the workloads they can serve."""
+    print(f"[parity] workload {cid} path {path}", flush=True)
     inp = wl.make_inputs(cid, cid)
-    g = run_gpu(inp, max_elite=0 if cid <= 2 else 64, path="tiled")
+    g = run_gpu(inp, max_elite=0 if cid <= 2 else 64, path=path)
     compare(inp, g, reference(inp, g))
 
 
@@ -54,17 +58,45 @@ EDGE = [
     dict(Nv=1000, Nt=20, Hq=14, Hkv=2, D=64, dtype="bf16", L=4, B=2),
     dict(Nv=129, Nt=17, Hq=32, Hkv=1, D=128, dtype="bf16", L=2),   # G = 32 > 16
     dict(Nv=4100, Nt=9, Hq=8, Hkv=2, D=128, dtype="bf16", L=2),
+    dict(Nv=700, Nt=80, Hq=8, Hkv=8, D=128, dtype="bf16", L=3, B=2),   # eight KV heads
+    dict(Nv=333, Nt=24, Hq=8, Hkv=2, D=64, dtype="f32", L=3, B=5),     # several samples
 ]
 
 
 @pytest.mark.parametrize("shape", EDGE, ids=lambda s: "x".join(f"{k}{v}" for k, v in s.items()))
 @pytest.mark.parametrize("seed", [0, 1])
-@pytest.mark.parametrize("path", ["auto", "tiled"])
+@pytest.mark.parametrize("path", ["auto", "tiled", "rows"])
 def test_edge_shapes(shape, seed, path):
+    if path == "rows" and shape["Nv"] > 3072:
+        pytest.skip("the rows path serves N_v <= 3072")
+    print(f"[parity] edge {shape} seed {seed} path {path}", flush=True)
     w = wl.custom(ratio=0.2, **shape)
     inp = wl.make_inputs(w, seed)
     g = run_gpu(inp, path=path)
     compare(inp, g, reference(inp, g))
+
+
+@pytest.mark.parametrize("path", ["auto", "tiled", "rows"])
+def test_all_text_elite_many_rows(path):
+    """Zero queries make every text token elite: G * N_tk = 280 rows per KV head,
+    several row passes of the chunked path, elite text columns spanning chunks."""
+    w = wl.custom(Nv=500, Nt=40, Hq=14, Hkv=2, D=128, dtype="bf16", L=2, B=2, ratio=0.3)
+    inp = wl.make_inputs(w, 6, zero_q=True)
+    g = run_gpu(inp, path=path)
+    assert (g["n_elite"] == 40).all()
+    compare(inp, g, reference(inp, g))
+
+
+def test_workspace_reused_across_calls():
+    """One workspace, three calls with different inputs: each result matches the
+    oracle (records of earlier calls must never be taken for current ones)."""
+    from parity import make_aircache
+    w = wl.custom(Nv=900, Nt=30, Hq=8, Hkv=4, D=128, dtype="bf16", L=3, B=2, ratio=0.2)
+    ac = make_aircache(w)
+    for seed in (21, 22, 21):
+        inp = wl.make_inputs(w, seed)
+        g = run_gpu(inp, ac=ac)
+        compare(inp, g, reference(inp, g))
 
 
 @pytest.mark.parametrize("alpha,ratio", [(0.0, 0.1), (1.0, 0.1), (0.9, 0.0), (0.9, 1.0), (0.5, 0.5)])
