@@ -57,6 +57,8 @@ struct Ws {
   float *part;        // [units][rt_grid][Nv] column sums of one row tile (row-complete path)
   unsigned *cnt_chunk; // [L*B][chunk_stride] finished row groups per chunk (chunked path), or NULL
   int chunk_stride;
+  unsigned *cnt_elite; // [L*B] finished KV heads of the elite stage (reset by the last one)
+  float *pbar_part;    // [L*B*Hkv][N_t] KV-head parts of pbar
 };
 
 struct LayerTable {
@@ -65,153 +67,6 @@ struct LayerTable {
 struct LayerTableOut {
   void *p[AIRCACHE_MAX_LAYERS];
 };
-
-// ----------------------------------------------------------------------------
-// Step 1: elite observation window ("Elite Observation Window", the Att and k
-// equations). One workgroup of 8 waves per (layer, sample). The logits of the
-// last text query of every query head over the N_t text keys of its KV head
-// come from MFMA (16 text keys as the A operand, up to 16 query heads of one KV
-// group as the B operand); the (KV head, head tile, key tile) items are spread
-// over the waves and all H_q x N_t logits land in LDS. Each wave then
-// normalises whole rows (max, sum of exp2), rows are summed into pbar in
-// ascending head order, and elite = { j : pbar_j >= alpha max pbar }, compacted
-// in ascending j by a block scan.
-// ----------------------------------------------------------------------------
-constexpr int kEliteThreads = 512;
-constexpr int kEliteWaves = kEliteThreads / 64;
-
-template <typename Tag, int D>
-__global__ __launch_bounds__(kEliteThreads) void elite_select_kernel(Shape sh, LayerTable qt, LayerTable kt,
-                                                                     PlanPtrs plan, Ws ws) {
-  using E = typename Tag::store_t;
-  extern __shared__ float lds[];  // z[Hq][Nt], pbar[Nt]
-  __shared__ float red[kEliteWaves];
-  __shared__ int wtot[kEliteWaves];
-  const int lb = blockIdx.x, l = lb / sh.B, b = lb % sh.B;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, grp = lane >> 4;
-  const int Nt = sh.Nt, G = sh.G;
-  float *z = lds;
-  float *pbar = lds + (size_t)sh.Hq * Nt;
-
-  // This kernel opens every plan: reset the counters of finalize_kernel.
-  for (int g = tid; g < sh.Hkv; g += kEliteThreads) ws.cnt_unit[(size_t)lb * sh.Hkv + g] = 0;
-  if (ws.cnt_chunk)
-    for (int c = tid; c < ws.chunk_stride; c += kEliteThreads) ws.cnt_chunk[(size_t)lb * ws.chunk_stride + c] = 0;
-  if (tid == 0) {
-    ws.cnt_lb[lb] = 0;
-    if (l == 0) ws.cnt_b[b] = 0;
-    if (lb == 0) {
-      *ws.cnt_all = 0;
-      *plan.status = 0;
-      *ws.epoch = *ws.epoch + 1u;
-    }
-  }
-
-  const E *q = static_cast<const E *>(qt.p[l]);
-  const E *k = static_cast<const E *>(kt.p[l]);
-  const int nkt = (Nt + 15) >> 4;
-  const int nht = (G + 15) >> 4;
-  const int items = sh.Hkv * nht * nkt;
-  // Items (KV head, head tile, key tile) in batches of 4 per wave: all
-  // fragments of a batch are loaded before its MFMAs so the loads overlap.
-  constexpr int kBatch = 4;
-  for (int it0 = wave; it0 < items; it0 += kEliteWaves * kBatch) {
-    Frag<Tag> qf[kBatch][D / 32], kf[kBatch][D / 32];
-#pragma unroll
-    for (int bi = 0; bi < kBatch; ++bi) {
-      const int it = it0 + bi * kEliteWaves;
-      const int kt_ = it % nkt, gh = it / nkt;
-      const int ht = gh % nht, g = gh / nht;
-      const int h0 = ht * 16;
-      const int nh = min(16, G - h0);
-      const int key = kt_ * 16 + n;
-      if (it < items && n < nh) {
-        const E *qrow = q + ((size_t)(b * sh.Hq + g * G + h0 + n) * Nt + (Nt - 1)) * D;
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) qf[bi][c].load(qrow + c * 32 + grp * 8);
-      } else {
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) qf[bi][c].zero();
-      }
-      if (it < items && key < Nt) {
-        const E *krow = k + ((size_t)(b * sh.Hkv + g) * sh.S + sh.Nv + key) * D;
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) kf[bi][c].load(krow + c * 32 + grp * 8);
-      } else {
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) kf[bi][c].zero();
-      }
-    }
-#pragma unroll
-    for (int bi = 0; bi < kBatch; ++bi) {
-      const int it = it0 + bi * kEliteWaves;
-      if (it >= items) break;  // wave-uniform
-      const int kt_ = it % nkt, gh = it / nkt;
-      const int ht = gh % nht, g = gh / nht;
-      const int h0 = ht * 16;
-      const int nh = min(16, G - h0);
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) mfma_slice(acc, kf[bi][c], qf[bi][c]);
-      if (n < nh) {
-        float *zr = z + (size_t)(g * G + h0 + n) * Nt;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kk = kt_ * 16 + grp * 4 + i;
-          if (kk < Nt) zr[kk] = acc[i] * sh.scale2;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  for (int h = wave; h < sh.Hq; h += kEliteWaves) {
-    float *zr = z + (size_t)h * Nt;
-    float m = -INFINITY;
-    for (int j = lane; j < Nt; j += 64) m = fmaxf(m, zr[j]);
-    m = wave_max(m);
-    float s = 0.f;
-    for (int j = lane; j < Nt; j += 64) {
-      const float ev = exp2f(zr[j] - m);
-      zr[j] = ev;
-      s += ev;
-    }
-    s = wave_sum(s);
-    const float inv = 1.f / s;
-    for (int j = lane; j < Nt; j += 64) zr[j] *= inv;
-  }
-  __syncthreads();
-  float m = -INFINITY;
-  for (int j = tid; j < Nt; j += kEliteThreads) {
-    float a = 0.f;
-    for (int h = 0; h < sh.Hq; ++h) a += z[(size_t)h * Nt + j];
-    pbar[j] = a;
-    m = fmaxf(m, a);
-  }
-  m = wave_max(m);
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  m = red[0];
-  for (int w = 1; w < kEliteWaves; ++w) m = fmaxf(m, red[w]);
-  const float thr = sh.alpha * m;
-  const int per = (Nt + kEliteThreads - 1) / kEliteThreads;
-  const int j0 = min(Nt, tid * per), j1 = min(Nt, j0 + per);
-  int cnt = 0;
-  for (int j = j0; j < j1; ++j) cnt += (pbar[j] >= thr) ? 1 : 0;
-  const int incl = wave_incl_scan(cnt);
-  if (lane == 63) wtot[wave] = incl;
-  __syncthreads();
-  int base = 0, total = 0;
-  for (int w = 0; w < kEliteWaves; ++w) {
-    if (w < wave) base += wtot[w];
-    total += wtot[w];
-  }
-  int pos = base + incl - cnt;
-  int32_t *el = plan.elite + (size_t)lb * Nt;
-  for (int j = j0; j < j1; ++j)
-    if (pbar[j] >= thr) el[pos++] = j;
-  if (tid == 0) plan.n_elite[lb] = total;
-}
 
 // ----------------------------------------------------------------------------
 // Step 2a: elite cross-modal logits ("Elite Observation Window", the A_vtk
@@ -843,6 +698,176 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
 
 #include "score_fused.h"
 
+// ----------------------------------------------------------------------------
+// Step 1: elite observation window ("Elite Observation Window", the Att and k
+// equations). One workgroup of 4 waves per (layer, sample, KV head): the
+// logits of the last text query of the head's G query heads over the N_t text
+// keys come from MFMA (16 text keys as the A operand, up to 16 query heads as
+// the B operand) into LDS; each wave normalises whole rows (max, sum of exp2),
+// and the rows are summed in ascending head order into the KV head's part of
+// pbar. The last KV head of a (layer, sample) to finish (a counter election)
+// adds the parts in ascending KV-head order into pbar and keeps
+// { j : pbar_j >= alpha max pbar }, compacted in ascending j by a block scan.
+// The election counter resets itself: the last arriver zeroes it for the next
+// call. (The chunked path computes the elite sets inside its own launch.)
+// ----------------------------------------------------------------------------
+constexpr int kEliteThreads = 256;
+constexpr int kEliteWaves = kEliteThreads / 64;
+
+template <typename Tag, int D>
+__global__ __launch_bounds__(kEliteThreads) void elite_select_kernel(Shape sh, LayerTable qt, LayerTable kt,
+                                                                     PlanPtrs plan, Ws ws) {
+  using E = typename Tag::store_t;
+  extern __shared__ float lds[];  // z[G][Nt]; the last KV head: pbar[Nt]
+  __shared__ float red[kEliteWaves];
+  __shared__ int wtot[kEliteWaves];
+  __shared__ int flag;
+  const int lb = blockIdx.x / sh.Hkv, g = blockIdx.x - lb * sh.Hkv;
+  const int l = lb / sh.B, b = lb % sh.B;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, grp = lane >> 4;
+  const int Nt = sh.Nt, G = sh.G;
+  float *z = lds;
+
+  // This kernel opens every plan: reset the counters of the later kernels.
+  if (g == 0) {
+    for (int u = tid; u < sh.Hkv; u += kEliteThreads) ws.cnt_unit[(size_t)lb * sh.Hkv + u] = 0;
+    if (ws.cnt_chunk)
+      for (int c = tid; c < ws.chunk_stride; c += kEliteThreads) ws.cnt_chunk[(size_t)lb * ws.chunk_stride + c] = 0;
+    if (tid == 0) {
+      ws.cnt_lb[lb] = 0;
+      if (l == 0) ws.cnt_b[b] = 0;
+      if (lb == 0) {
+        *ws.cnt_all = 0;
+        *plan.status = 0;
+        *ws.epoch = *ws.epoch + 1u;
+      }
+    }
+  }
+
+  const E *q = static_cast<const E *>(qt.p[l]);
+  const E *k = static_cast<const E *>(kt.p[l]);
+  const int nkt = (Nt + 15) >> 4;
+  const int nht = (G + 15) >> 4;
+  const int items = nht * nkt;
+  // Items (head tile, key tile) in batches of 4 per wave: all fragments of a
+  // batch are loaded before its MFMAs so the loads overlap.
+  constexpr int kBatch = 4;
+  for (int it0 = wave; it0 < items; it0 += kEliteWaves * kBatch) {
+    Frag<Tag> qf[kBatch][D / 32], kf[kBatch][D / 32];
+#pragma unroll
+    for (int bi = 0; bi < kBatch; ++bi) {
+      const int it = it0 + bi * kEliteWaves;
+      const int kt_ = it % nkt, ht = it / nkt;
+      const int h0 = ht * 16;
+      const int nh = min(16, G - h0);
+      const int key = kt_ * 16 + n;
+      if (it < items && n < nh) {
+        const E *qrow = q + ((size_t)(b * sh.Hq + g * G + h0 + n) * Nt + (Nt - 1)) * D;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) qf[bi][c].load(qrow + c * 32 + grp * 8);
+      } else {
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) qf[bi][c].zero();
+      }
+      if (it < items && key < Nt) {
+        const E *krow = k + ((size_t)(b * sh.Hkv + g) * sh.S + sh.Nv + key) * D;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) kf[bi][c].load(krow + c * 32 + grp * 8);
+      } else {
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) kf[bi][c].zero();
+      }
+    }
+#pragma unroll
+    for (int bi = 0; bi < kBatch; ++bi) {
+      const int it = it0 + bi * kEliteWaves;
+      if (it >= items) break;  // wave-uniform
+      const int kt_ = it % nkt, ht = it / nkt;
+      const int h0 = ht * 16;
+      const int nh = min(16, G - h0);
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) mfma_slice(acc, kf[bi][c], qf[bi][c]);
+      if (n < nh) {
+        float *zr = z + (size_t)(h0 + n) * Nt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = kt_ * 16 + grp * 4 + i;
+          if (kk < Nt) zr[kk] = acc[i] * sh.scale2;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int h = wave; h < G; h += kEliteWaves) {
+    float *zr = z + (size_t)h * Nt;
+    float m = -INFINITY;
+    for (int j = lane; j < Nt; j += 64) m = fmaxf(m, zr[j]);
+    m = wave_max(m);
+    float s = 0.f;
+    for (int j = lane; j < Nt; j += 64) {
+      const float ev = exp2f(zr[j] - m);
+      zr[j] = ev;
+      s += ev;
+    }
+    s = wave_sum(s);
+    const float inv = 1.f / s;
+    for (int j = lane; j < Nt; j += 64) zr[j] *= inv;
+  }
+  __syncthreads();
+  // this KV head's part of pbar, heads in ascending order
+  float *part = ws.pbar_part + (size_t)blockIdx.x * Nt;
+  for (int j = tid; j < Nt; j += kEliteThreads) {
+    float a = 0.f;
+    for (int h = 0; h < G; ++h) a += z[(size_t)h * Nt + j];
+    store_coherent(&part[j], a);
+  }
+  wait_all_memory();
+  __syncthreads();
+  if (tid == 0) {
+    const bool last = counter_add(&ws.cnt_elite[lb], 1u) == (unsigned)sh.Hkv - 1u;
+    if (last) store_coherent(&ws.cnt_elite[lb], 0u);
+    flag = last;
+  }
+  __syncthreads();
+  if (!flag) return;
+
+  // Last KV head of (l, b): pbar = sum of the parts in ascending KV-head order.
+  float *pbar = lds;
+  const auto rp = coherent_rsrc(ws.pbar_part + (size_t)lb * sh.Hkv * Nt, (unsigned)((size_t)sh.Hkv * Nt * sizeof(float)));
+  float m = -INFINITY;
+  for (int j = tid; j < Nt; j += kEliteThreads) {
+    float a = 0.f;
+    for (int gg = 0; gg < sh.Hkv; ++gg) a += load_sc1_f(rp, (unsigned)(((size_t)gg * Nt + j) * sizeof(float)));
+    pbar[j] = a;
+    m = fmaxf(m, a);
+  }
+  m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = red[0];
+  for (int w = 1; w < kEliteWaves; ++w) m = fmaxf(m, red[w]);
+  const float thr = sh.alpha * m;
+  const int per = (Nt + kEliteThreads - 1) / kEliteThreads;
+  const int j0 = min(Nt, tid * per), j1 = min(Nt, j0 + per);
+  int cnt = 0;
+  for (int j = j0; j < j1; ++j) cnt += (pbar[j] >= thr) ? 1 : 0;
+  const int incl = wave_incl_scan(cnt);
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+  for (int w = 0; w < kEliteWaves; ++w) {
+    if (w < wave) base += wtot[w];
+    total += wtot[w];
+  }
+  int pos = base + incl - cnt;
+  int32_t *el = plan.elite + (size_t)lb * Nt;
+  for (int j = j0; j < j1; ++j)
+    if (pbar[j] >= thr) el[pos++] = j;
+  if (tid == 0) plan.n_elite[lb] = total;
+}
+
 // Block-wide exclusive scan for 1024 threads; returns the exclusive prefix and
 // writes the total to *total.
 __device__ __forceinline__ int block_excl_scan_1024(int v, int *wtot, int *total) {
@@ -1065,6 +1090,7 @@ struct Config {
   Shape sh;
   size_t off_cnt, off_stats, off_e, off_part, ws_bytes;
   size_t off_xrec, off_mom, off_brec, off_part_rg, off_cnt_chunk;
+  size_t off_cnt_elite, off_pbar, off_sched;
   size_t elite_lds, score_lds, final_lds, rows_lds;
   int ktw;
   int rows_kt;  // key tiles per wave of cross_score_rows_kernel; 0: the tiled path with spilled exponentials
@@ -1127,12 +1153,12 @@ int make_config(const aircache_desc *d, Config *cfg) {
   s.ratio = d->ratio;
   const int esz = d->dtype == AIRCACHE_BF16 ? 2 : 4;
   (void)esz;
-  cfg->elite_lds = ((size_t)s.Hq + 1) * s.Nt * sizeof(float);
+  cfg->elite_lds = (size_t)(s.G > 1 ? s.G : 1) * s.Nt * sizeof(float);
   cfg->score_lds = (size_t)s.cap * sizeof(int);
   cfg->final_lds = ((size_t)s.Hkv * s.rcap16 + s.Nv) * sizeof(float);
   if (cfg->elite_lds > kMaxLds)
-    return fail(AIRCACHE_EINVAL, "(n_q_heads + 1) * n_txt = %lld too large for the elite stage (max %zu)",
-                ((long long)s.Hq + 1) * s.Nt, kMaxLds / sizeof(float));
+    return fail(AIRCACHE_EINVAL, "(n_q_heads / n_kv_heads) * n_txt = %lld too large for the elite stage (max %zu)",
+                (long long)s.G * s.Nt, kMaxLds / sizeof(float));
   if (cfg->score_lds > kMaxLds || cfg->final_lds > kMaxLds)
     return fail(AIRCACHE_EINVAL, "n_q_heads * max_elite too large (%lld rows); lower max_elite",
                 (long long)s.Hq * s.cap);
@@ -1187,6 +1213,7 @@ int make_config(const aircache_desc *d, Config *cfg) {
     const int tb = (int)tile_bytes;
     cfg->flds = fused_lds_layout(tb, tb <= 4096 ? 3 : 2, s.cap, s.Hkv, s.B);
     const bool lds_ok = (size_t)cfg->flds.total + 8192 <= kMaxLds &&
+                        (size_t)(s.G > 1 ? s.G : 1) * s.Nt * sizeof(float) <= (size_t)cfg->flds.total &&  // phase 0
                         (size_t)s.L * maxc * 40 <= (size_t)(cfg->flds.el - cfg->flds.ring);  // finisher's records
     // the schedule is worked out by one wave: at most 8 (layer, sample) pairs per lane
     const bool items_ok = lb <= 512 && (long long)lb * maxc * maxrg <= (long long)kFusedMaxItems * kFusedTargetCus &&
@@ -1200,7 +1227,12 @@ int make_config(const aircache_desc *d, Config *cfg) {
   if (d->path == AIRCACHE_PATH_TILED || d->path == AIRCACHE_PATH_CHUNKED) cfg->rows_kt = 0;
   cfg->path = cfg->chunked ? AIRCACHE_PATH_CHUNKED : cfg->rows_kt ? AIRCACHE_PATH_ROWS : AIRCACHE_PATH_TILED;
   cfg->off_cnt = kEpochBytes;
-  cfg->off_stats = cfg->off_cnt + align_up(n_cnt * sizeof(unsigned));
+  cfg->off_cnt_elite = cfg->off_cnt + align_up(n_cnt * sizeof(unsigned));
+  cfg->off_pbar = cfg->off_cnt_elite + align_up((size_t)s.L * s.B * sizeof(unsigned));
+  cfg->off_sched = cfg->off_pbar + align_up((size_t)s.L * s.B * s.Hkv * s.Nt * sizeof(float));
+  // elite-set counter of the chunked path
+  const size_t eflags = cfg->chunked ? align_up(sizeof(unsigned)) : 0;
+  cfg->off_stats = cfg->off_sched + eflags;
   cfg->off_xrec = cfg->off_mom = cfg->off_brec = cfg->off_stats;
   if (cfg->chunked) {
     const size_t lbs = (size_t)s.L * s.B;
@@ -1238,6 +1270,8 @@ Ws ws_of(const Config &cfg, void *base) {
   w.e = reinterpret_cast<float *>(p + cfg.off_e);
   w.part = reinterpret_cast<float *>(p + cfg.off_part);
   w.cnt_chunk = cfg.chunked ? reinterpret_cast<unsigned *>(p + cfg.off_cnt_chunk) : nullptr;
+  w.cnt_elite = reinterpret_cast<unsigned *>(p + cfg.off_cnt_elite);
+  w.pbar_part = reinterpret_cast<float *>(p + cfg.off_pbar);
   w.chunk_stride = cfg.chunked ? cfg.max_chunks : 0;
   return w;
 }
@@ -1299,13 +1333,11 @@ int launch_rows(const Config &cfg, const LayerTable &qt, const LayerTable &kt, c
   return check_hip(hipGetLastError(), "cross_score_rows_kernel launch");
 }
 
-template <typename Tag, int D>
-int launch_chunked(const Config &cfg, const LayerTable &qt, const LayerTable &kt, const PlanPtrs &pp, const Ws &ws,
-                   void *ws_base, hipStream_t st) {
-  const Shape &s = cfg.sh;
-  int rc;
+// Workgroups of cross_score_fused_kernel: as many as are resident at once.
+template <typename Tag, int D> int fused_grid(const Config &cfg, int *grid) {
   auto kern = cross_score_fused_kernel<Tag, D>;
   const size_t lds = (size_t)cfg.flds.total;
+  int rc;
   if ((rc = allow_lds(kern, lds))) return rc;
   int cus = 0;
   if ((rc = device_cus(&cus))) return rc;
@@ -1315,7 +1347,16 @@ int launch_chunked(const Config &cfg, const LayerTable &qt, const LayerTable &kt
                       "hipOccupancyMaxActiveBlocksPerMultiprocessor")))
     return rc;
   if (occ < 1) return fail(AIRCACHE_EINVAL, "the chunked kernel does not fit a compute unit");
-  const int grid = cus * occ;
+  *grid = cus * occ;
+  return AIRCACHE_OK;
+}
+
+template <typename Tag, int D>
+int launch_chunked(const Config &cfg, const LayerTable &qt, const LayerTable &kt, const PlanPtrs &pp, const Ws &ws,
+                   void *ws_base, int grid, hipStream_t st) {
+  const Shape &s = cfg.sh;
+  auto kern = cross_score_fused_kernel<Tag, D>;
+  const size_t lds = (size_t)cfg.flds.total;
   // every chunk of a (layer, sample) needs a workgroup of its own, and the
   // item list of a workgroup is bounded
   if (cfg.max_chunks > grid) return fail(AIRCACHE_EINVAL, "%d chunks per (layer, sample) exceed %d workgroups", cfg.max_chunks, grid);
@@ -1335,6 +1376,9 @@ int launch_chunked(const Config &cfg, const LayerTable &qt, const LayerTable &kt
   fw.wmax = cfg.wmax;
   fw.cnt_chunk = ws.cnt_chunk;
   fw.part = reinterpret_cast<float *>(p + cfg.off_part_rg);
+  fw.edone = reinterpret_cast<unsigned *>(p + cfg.off_sched);
+  fw.cnt_elite = ws.cnt_elite;
+  fw.parts = ws.pbar_part;
   // One workgroup per CU (the LDS use admits no second), so with the device
   // to itself every workgroup is resident at once, which the waits between
   // workgroups need; if other work holds CUs, the bounded waits report
@@ -1348,20 +1392,25 @@ int launch_plan(const Config &cfg, const LayerTable &qt, const LayerTable &kt, c
                 void *ws_base, hipStream_t st, hipEvent_t *ev) {
   const Shape &s = cfg.sh;
   int rc;
-  if ((rc = allow_lds(elite_select_kernel<Tag, D>, cfg.elite_lds))) return rc;
   const unsigned nlb = (unsigned)(s.L * s.B);
-  if ((rc = mark(ev, 0, st))) return rc;
-  hipLaunchKernelGGL((elite_select_kernel<Tag, D>), dim3(nlb), dim3(kEliteThreads), cfg.elite_lds, st, s, qt, kt, pp,
-                     ws);
-  if ((rc = check_hip(hipGetLastError(), "elite_select_kernel launch"))) return rc;
-  if ((rc = mark(ev, 1, st))) return rc;
   if (cfg.chunked) {
-    // scoring, statistics, budgets and top-k in one launch
-    if ((rc = launch_chunked<Tag, D>(cfg, qt, kt, pp, ws, ws_base, st))) return rc;
+    // elite sets, scoring, statistics, budgets and top-k in one launch (the
+    // elite interval of the profiled call is empty)
+    int fgrid = 0;
+    if ((rc = fused_grid<Tag, D>(cfg, &fgrid))) return rc;
+    if ((rc = mark(ev, 0, st))) return rc;
+    if ((rc = mark(ev, 1, st))) return rc;
+    if ((rc = launch_chunked<Tag, D>(cfg, qt, kt, pp, ws, ws_base, fgrid, st))) return rc;
     if ((rc = mark(ev, 2, st))) return rc;
     if ((rc = mark(ev, 3, st))) return rc;
     return mark(ev, 4, st);
   }
+  if ((rc = allow_lds(elite_select_kernel<Tag, D>, cfg.elite_lds))) return rc;
+  if ((rc = mark(ev, 0, st))) return rc;
+  hipLaunchKernelGGL((elite_select_kernel<Tag, D>), dim3(nlb * s.Hkv), dim3(kEliteThreads), cfg.elite_lds, st, s, qt,
+                     kt, pp, ws);
+  if ((rc = check_hip(hipGetLastError(), "elite_select_kernel launch"))) return rc;
+  if ((rc = mark(ev, 1, st))) return rc;
   if (cfg.rows_kt) {
     // scoring, statistics and budgets in one launch; the finalize stage is empty
     if (cfg.rows_kt == 4) rc = launch_rows<Tag, D, 4>(cfg, qt, kt, pp, ws, st);

@@ -93,11 +93,15 @@ __host__ __device__ inline int fused_kcap_min(int L, int B, int Nv, int wph) {
   return k < 1 ? 1 : (k > kFusedSlots ? kFusedSlots : (int)k);
 }
 
-// Workspace of the chunked path (the counters are reset by elite_select_kernel,
-// which also advances the epoch; every record carries the epoch it was written
-// in, so stale records of earlier calls never match).
+// Workspace of the chunked path. Every counter is reset by its last arriver
+// and the epoch advances at the end of each call; every record carries the
+// epoch of the call that wrote it, so stale records of earlier calls never
+// match. The workspace must be zero before its first use.
 struct FusedWs {
-  const unsigned *epoch;  // [1]
+  unsigned *epoch;        // [1] calls so far
+  unsigned *edone;        // [1] elite sets published in this call
+  unsigned *cnt_elite;    // [L*B] KV-head parts finished per (layer, sample)
+  float *parts;           // [L*B*Hkv][N_t] KV-head parts of pbar
   unsigned *cnt_b;        // [B] finished chunks per sample
   unsigned *ticket;       // [1] top-k tasks handed out
   unsigned *cnt_chunk;    // [L*B][max_chunks] finished row groups per chunk
@@ -113,7 +117,7 @@ struct FusedWs {
 
 // Dynamic LDS of cross_score_fused_kernel (byte offsets, 16-byte aligned).
 struct FusedLds {
-  int ring, el, colsum, red, mloc, wts, ctarget, item_lb, item_rc, total;
+  int ring, el, colsum, red, mloc, wts, ctarget, items, total;
 };
 __host__ __device__ inline int fused_align16(int x) { return (x + 15) & ~15; }
 __host__ __device__ inline FusedLds fused_lds_layout(int tile_bytes, int ring_depth, int cap, int Hkv, int B) {
@@ -135,9 +139,7 @@ __host__ __device__ inline FusedLds fused_lds_layout(int tile_bytes, int ring_de
   o += fused_align16(Hkv * kFusedRtMax * 16 * 4);
   f.ctarget = o;
   o += fused_align16(B * 4);
-  f.item_lb = o;
-  o += fused_align16(kFusedMaxItems * 4);
-  f.item_rc = o;
+  f.items = o;
   o += fused_align16(kFusedMaxItems * 4);
   f.total = o;
   return f;
@@ -602,6 +604,193 @@ __device__ __forceinline__ int fused_wait_budget(const FusedWs &fw, int plb, uns
   return (int)(unsigned)v;
 }
 
+// Phase 0, one item per (layer, sample, KV head): the part of the elite
+// observation window's pbar that the KV head's G query heads give ("Elite
+// Observation Window", the Att equation). The logits of the last text query
+// of each of the G heads over the N_t text keys come from MFMA (16 text keys
+// as the A operand, up to 16 query heads as the B operand) into LDS; each wave
+// normalises whole rows (max, sum of exp2); the rows are summed in ascending
+// head order into part[j], written with agent-coherent stores.
+// lds: G * N_t floats.
+template <typename Tag, int D>
+__device__ __forceinline__ void fused_elite_part(const Shape &sh, const LayerTable &qt, const LayerTable &kt, int lb,
+                                                 int g, float *part, float *lds) {
+  using E = typename Tag::store_t;
+  constexpr int NW = kFusedWaves, NT = kFusedThreads;
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, grp = lane >> 4;
+  const int l = lb / sh.B, b = lb - (lb / sh.B) * sh.B;
+  const int Nt = sh.Nt, G = sh.G;
+  float *z = lds;
+  const E *q = static_cast<const E *>(qt.p[l]);
+  const E *k = static_cast<const E *>(kt.p[l]);
+  const int nkt = (Nt + 15) >> 4;
+  const int nht = (G + 15) >> 4;
+  const int items = nht * nkt;
+  for (int it = wave; it < items; it += NW) {
+    const int kt_ = it % nkt, ht = it / nkt;
+    const int h0 = ht * 16;
+    const int nh = min(16, G - h0);
+    const int key = kt_ * 16 + n;
+    Frag<Tag> qf[D / 32], kf[D / 32];
+    if (n < nh) {
+      const E *qrow = q + ((size_t)(b * sh.Hq + g * G + h0 + n) * Nt + (Nt - 1)) * D;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) qf[c].load(qrow + c * 32 + grp * 8);
+    } else {
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) qf[c].zero();
+    }
+    if (key < Nt) {
+      const E *krow = k + ((size_t)(b * sh.Hkv + g) * sh.S + sh.Nv + key) * D;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) kf[c].load(krow + c * 32 + grp * 8);
+    } else {
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) kf[c].zero();
+    }
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) mfma_slice(acc, kf[c], qf[c]);
+    if (n < nh) {
+      float *zr = z + (size_t)(h0 + n) * Nt;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kk = kt_ * 16 + grp * 4 + i;
+        if (kk < Nt) zr[kk] = acc[i] * sh.scale2;
+      }
+    }
+  }
+  __syncthreads();
+  for (int h = wave; h < G; h += NW) {
+    float *zr = z + (size_t)h * Nt;
+    float m = -INFINITY;
+    for (int j = lane; j < Nt; j += 64) m = fmaxf(m, zr[j]);
+    m = wave_max(m);
+    float s = 0.f;
+    for (int j = lane; j < Nt; j += 64) {
+      const float ev = exp2f(zr[j] - m);
+      zr[j] = ev;
+      s += ev;
+    }
+    s = wave_sum(s);
+    const float inv = 1.f / s;
+    for (int j = lane; j < Nt; j += 64) zr[j] *= inv;
+  }
+  __syncthreads();
+  for (int j = tid; j < Nt; j += NT) {
+    float a = 0.f;
+    for (int h = 0; h < G; ++h) a += z[(size_t)h * Nt + j];
+    store_coherent(&part[j], a);
+  }
+}
+
+// The last KV head of a (layer, sample) to finish its part: pbar = the sum of
+// the parts in ascending KV-head order, elite = { j : pbar_j >= alpha max pbar },
+// compacted in ascending j by a block scan and written with agent-coherent
+// stores ("Elite Observation Window", the k equation). lds: N_t floats.
+__device__ __forceinline__ void fused_elite_merge(const Shape &sh, const PlanPtrs &plan, const float *parts, int lb,
+                                                  float *lds, int *wtot, float *red) {
+  constexpr int NW = kFusedWaves, NT = kFusedThreads;
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int Nt = sh.Nt;
+  float *pbar = lds;
+  const auto rp = coherent_rsrc(parts, (unsigned)((size_t)sh.Hkv * Nt * sizeof(float)));
+  float m = -INFINITY;
+  for (int j = tid; j < Nt; j += NT) {
+    float a = 0.f;
+    for (int gg = 0; gg < sh.Hkv; ++gg) a += load_sc1_f(rp, (unsigned)(((size_t)gg * Nt + j) * sizeof(float)));
+    pbar[j] = a;
+    m = fmaxf(m, a);
+  }
+  m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = red[0];
+  for (int w = 1; w < NW; ++w) m = fmaxf(m, red[w]);
+  const float thr = sh.alpha * m;
+  const int per = (Nt + NT - 1) / NT;
+  const int j0 = min(Nt, tid * per), j1 = min(Nt, j0 + per);
+  int cnt = 0;
+  for (int j = j0; j < j1; ++j) cnt += (pbar[j] >= thr) ? 1 : 0;
+  int total;
+  int pos = fused_block_scan(cnt, wtot, &total);
+  int32_t *el = plan.elite + (size_t)lb * Nt;
+  for (int j = j0; j < j1; ++j)
+    if (pbar[j] >= thr) store_coherent(&el[pos++], (int32_t)j);
+  if (tid == 0) store_coherent(&plan.n_elite[lb], (int32_t)total);
+}
+
+// Work schedule of this workgroup, worked out by the 64 lanes of wave 0 (no
+// block barriers) from the elite counts: lane q holds the (b, l) pairs
+// q * per .. q * per + per - 1 in sample-major order. The cap on key tiles per
+// wave is the smallest (narrowest chunks, most workgroups busy) whose items
+// all fit one round of the grid, the widest when none does (a binary search,
+// items being non-increasing in the cap). Items go in the order (b, l, row
+// group, chunk); workgroup me takes items me, me + P, ... Writes the items of
+// this workgroup to item[] ((b * L + l) << 16 | index in the (layer, sample)),
+// ctarget[b] (chunks of sample b), hdr[0] = cap and hdr[1] = item count.
+__device__ __forceinline__ void fused_schedule(const Shape &sh, const int (&ntk_of)[8], int me, int P, int *item,
+                                               int *ctarget, int *hdr) {
+  const int lane = threadIdx.x & 63;
+  const int L = sh.L, B = sh.B, Nv = sh.Nv, LB = L * B;
+  const int wph = kFusedWaves / sh.Hkv;
+  const int per = (LB + 63) / 64;
+  for (int b = lane; b < B; b += 64) ctarget[b] = 0;
+  int ntk[8];  // per <= 8: L * B <= 512
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int s = lane * per + j;
+    ntk[j] = (j < per && s < LB) ? ntk_of[j] : 0;
+  }
+  const int P_sched = P < kFusedTargetCus ? P : kFusedTargetCus;
+  int lo_k = fused_kcap_min(L, B, Nv, wph), hi_k = kFusedSlots;
+  while (lo_k < hi_k) {
+    const int mid = (lo_k + hi_k) >> 1;
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < per && lane * per + j < LB) {
+        const ChunkPlan cp = fused_chunk_plan(ntk[j], sh.G, Nv, wph, mid);
+        n += cp.nrg * cp.nchunks;
+      }
+    if (wave_sum_i(n) <= P_sched) hi_k = mid;
+    else lo_k = mid + 1;
+  }
+  const int kc = lo_k;
+  int nit[8], nch[8], tot = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    nit[j] = nch[j] = 0;
+    if (j < per && lane * per + j < LB) {
+      const ChunkPlan cp = fused_chunk_plan(ntk[j], sh.G, Nv, wph, kc);
+      nch[j] = cp.nchunks;
+      nit[j] = cp.nrg * cp.nchunks;
+    }
+    tot += nit[j];
+  }
+  const int incl = wave_incl_scan(tot);
+  int start = incl - tot;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int s = lane * per + j;
+    if (j < per && s < LB) {
+      atomicAdd(&ctarget[s / L], nch[j]);
+      int first = me - start;  // first item index >= start congruent to me mod P
+      first = start + ((first % P) + P) % P;
+      for (int i = first; i < start + nit[j]; i += P) {
+        const int k = (i - me) / P;
+        if (k < kFusedMaxItems) item[k] = (s << 16) | (i - start);
+      }
+      start += nit[j];
+    }
+  }
+  if (lane == 63) {
+    hdr[0] = kc;
+    hdr[1] = incl;  // items in all
+  }
+}
+
 template <typename Tag, int D>
 __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape sh, LayerTable qt, LayerTable kt,
                                                                           PlanPtrs plan, FusedWs fw, FusedLds lo) {
@@ -615,93 +804,67 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
   const int tid = threadIdx.x;
   const int L = sh.L, B = sh.B, Nv = sh.Nv;
   const int wph = kFusedWaves / sh.Hkv;
-  const unsigned epoch = *fw.epoch;
+  const unsigned e0 = *fw.epoch;
+  const unsigned epoch = e0 + 1u;  // tag of every record this call writes
   const int P = gridDim.x, me = blockIdx.x;
   int *ctarget = reinterpret_cast<int *>(lds + lo.ctarget);
-  int *item_lb = reinterpret_cast<int *>(lds + lo.item_lb);
-  int *item_rc = reinterpret_cast<int *>(lds + lo.item_rc);
-  auto elite_count = [&](int plb) {
-    const int t = plan.n_elite[plb];
+  int *item_list = reinterpret_cast<int *>(lds + lo.items);
+  __shared__ float redf[kFusedWaves];
+  __shared__ int hdr[2];
+  auto elite_count = [&](int plb) {  // written in this call: a coherent load
+    const int t = load_coherent(&plan.n_elite[plb]);
     return t < 0 ? 0 : (t > sh.cap ? sh.cap : t);
   };
 
-  // Schedule, worked out by wave 0 alone (no block barriers): lane q holds
-  // the (b, l) pairs q * per .. q * per + per - 1 in sample-major order.
-  // Cap on key tiles per wave: the smallest (narrowest chunks, most
-  // workgroups busy) whose items all fit one round of the grid, the widest
-  // when none does; a binary search, items being non-increasing in the cap.
-  // Items go in the order (b, l, row group, chunk); this workgroup takes items
-  // me, me + P, me + 2P, ... ctarget[b]: chunks of sample b (the finisher
-  // election's count).
-  __shared__ int sched[2];
+  // Phase 0: elite sets. Items (layer, sample, KV head) me, me + P, ...; the
+  // last part of a (layer, sample) (a counter election) merges the parts and
+  // counts the set in edone once it is published. The status word is cleared
+  // before workgroup 0 finishes its first item, so every later status bit is
+  // set after the clear.
+  if (me == 0 && tid == 0) store_coherent(plan.status, 0);
+  for (int t = me; t < L * B * sh.Hkv; t += P) {
+    const int lb = t / sh.Hkv, g = t - lb * sh.Hkv;
+    fused_elite_part<Tag, D>(sh, qt, kt, lb, g, fw.parts + (size_t)t * sh.Nt, lds_f);
+    wait_all_memory();
+    __syncthreads();
+    if (tid == 0) {
+      const bool last = counter_add(&fw.cnt_elite[lb], 1u) == (unsigned)sh.Hkv - 1u;
+      if (last) store_coherent(&fw.cnt_elite[lb], 0u);  // reset for the next call
+      bcast[3] = last;
+    }
+    __syncthreads();
+    if (uniform(bcast[3])) {
+      fused_elite_merge(sh, plan, fw.parts + (size_t)lb * sh.Hkv * sh.Nt, lb, lds_f, wtot, redf);
+      wait_all_memory();
+      __syncthreads();
+      if (tid == 0) counter_add(fw.edone, 1u);
+    }
+    __syncthreads();  // the LDS is free again
+  }
+  // Wave 0: wait until every elite set is out (one lane polls one word, with
+  // sleeps, so the waiting workgroups load the memory system little), then
+  // this workgroup's schedule. edone is reset by the call's last workgroup.
   if (tid < 64) {
-    const int lane = tid;
-    const int LB = L * B;
-    const int per = (LB + 63) / 64;
-    for (int b = lane; b < B; b += 64) ctarget[b] = 0;
-    int ntk[8];  // per <= 8: L * B <= 512
+    const int lane = tid, LB = L * B, per = (LB + 63) / 64;
+    if (lane == 0) {
+      unsigned spins = 0;
+      while (load_coherent(fw.edone) < (unsigned)LB) {
+        if (spin_expired(spins, plan.status)) break;
+        __builtin_amdgcn_s_sleep(10);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    int ntk[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int s = lane * per + j;
-      ntk[j] = 0;
-      if (j < per && s < LB) {
-        const int b = s / L, l = s - b * L;
-        ntk[j] = elite_count(l * B + b);
-      }
+      ntk[j] = (j < per && s < LB) ? elite_count((s % L) * B + s / L) : 0;
     }
-    const int P_sched = P < kFusedTargetCus ? P : kFusedTargetCus;
-    int lo_k = fused_kcap_min(L, B, Nv, wph), hi_k = kFusedSlots;
-    while (lo_k < hi_k) {
-      const int mid = (lo_k + hi_k) >> 1;
-      int n = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < per && lane * per + j < LB) {
-          const ChunkPlan cp = fused_chunk_plan(ntk[j], sh.G, Nv, wph, mid);
-          n += cp.nrg * cp.nchunks;
-        }
-      if (wave_sum_i(n) <= P_sched) hi_k = mid;
-      else lo_k = mid + 1;
-    }
-    const int kc = lo_k;
-    int nit[8], nch[8], tot = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      nit[j] = nch[j] = 0;
-      if (j < per && lane * per + j < LB) {
-        const ChunkPlan cp = fused_chunk_plan(ntk[j], sh.G, Nv, wph, kc);
-        nch[j] = cp.nchunks;
-        nit[j] = cp.nrg * cp.nchunks;
-      }
-      tot += nit[j];
-    }
-    const int incl = wave_incl_scan(tot);
-    int start = incl - tot;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int s = lane * per + j;
-      if (j < per && s < LB) {
-        atomicAdd(&ctarget[s / L], nch[j]);
-        int first = me - start;  // first item index >= start congruent to me mod P
-        first = start + ((first % P) + P) % P;
-        for (int i = first; i < start + nit[j]; i += P) {
-          const int k = (i - me) / P;
-          if (k < kFusedMaxItems) {
-            item_lb[k] = s;
-            item_rc[k] = i - start;
-          }
-        }
-        start += nit[j];
-      }
-    }
-    if (lane == 63) {
-      sched[0] = kc;
-      sched[1] = incl;  // items in all
-    }
+    fused_schedule(sh, ntk, me, P, item_list, ctarget, hdr);
   }
   __syncthreads();
-  const int kcap = uniform(sched[0]);
-  const int run = uniform(sched[1]);
+  const int kcap = uniform(hdr[0]);
+  const int run = uniform(hdr[1]);
   int nmine = (me < run) ? (run - me + P - 1) / P : 0;
   if (nmine > kFusedMaxItems) {
     if (tid == 0) atomicOr(plan.status, AIRCACHE_DEV_TIMEOUT);
@@ -711,20 +874,21 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
   for (int k = 0; k < nmine; ++k) {
     const int tid = opaque_tid();
     FusedItem it;
-    const int s = uniform(item_lb[k]);
+    const int item = uniform(item_list[k]);
+    const int s = item >> 16;
     it.b = s / L;
     it.l = s - it.b * L;
     it.plb = it.l * B + it.b;
     it.ntk = uniform(elite_count(it.plb));
     it.cp = fused_chunk_plan(it.ntk, sh.G, Nv, wph, kcap);
-    const int local = uniform(item_rc[k]);
+    const int local = item & 0xffff;
     it.r = local / it.cp.nchunks;
     it.c = local - it.r * it.cp.nchunks;
     it.q = qt.p[it.l];
     it.k = kt.p[it.l];
     int *el = reinterpret_cast<int *>(lds + lo.el);
     __syncthreads();  // the previous item is done with the LDS
-    for (int i = tid; i < it.ntk; i += kFusedThreads) el[i] = plan.elite[(size_t)it.plb * sh.Nt + i];
+    for (int i = tid; i < it.ntk; i += kFusedThreads) el[i] = load_coherent(&plan.elite[(size_t)it.plb * sh.Nt + i]);
     __syncthreads();
     {
       const int rt0 = it.r * kFusedRtMax, left = it.cp.rtg - rt0;
@@ -759,7 +923,11 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
       }
       wait_all_memory();
       __syncthreads();
-      if (tid == 0) bcast[3] = (counter_add(&fw.cnt_chunk[slot], 1u) == (unsigned)it.cp.nrg - 1u);
+      if (tid == 0) {
+        const bool last = counter_add(&fw.cnt_chunk[slot], 1u) == (unsigned)it.cp.nrg - 1u;
+        if (last) store_coherent(&fw.cnt_chunk[slot], 0u);  // reset for the next call
+        bcast[3] = last;
+      }
       __syncthreads();
       if (!uniform(bcast[3])) continue;
       const auto rp = coherent_rsrc(fw.part + slot * fw.max_rg * fw.wmax,
@@ -808,7 +976,11 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
     }
     wait_all_memory();
     __syncthreads();
-    if (tid == 0) bcast[0] = (counter_add(&fw.cnt_b[it.b], 1u) == (unsigned)ctarget[it.b] - 1u);
+    if (tid == 0) {
+      const bool last = counter_add(&fw.cnt_b[it.b], 1u) == (unsigned)ctarget[it.b] - 1u;
+      if (last) store_coherent(&fw.cnt_b[it.b], 0u);  // reset for the next call
+      bcast[0] = last;
+    }
     __syncthreads();
     if (!uniform(bcast[0])) continue;
 
@@ -892,7 +1064,17 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
   for (;;) {
     const int tid = opaque_tid();
     __syncthreads();
-    if (tid == 0) bcast[1] = (int)counter_add(fw.ticket, 1u);
+    if (tid == 0) {
+      const unsigned t = counter_add(fw.ticket, 1u);
+      // every workgroup takes exactly one ticket past the tasks: the last one
+      // ends the call (counter reset, epoch advanced)
+      if (t == (unsigned)(L * B + P - 1)) {
+        store_coherent(fw.ticket, 0u);
+        store_coherent(fw.edone, 0u);
+        store_coherent(fw.epoch, epoch);
+      }
+      bcast[1] = (int)t;
+    }
     __syncthreads();
     const int task = uniform(bcast[1]);
     if (task >= L * B) break;
@@ -904,7 +1086,7 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
         off += (int64_t)sh.Hkv * (fused_wait_budget(fw, l * B + bb, epoch, plan.status) + sh.Nt) * sh.D;
       plan.out_off[(size_t)l * (B + 1) + b] = off;
       if (b == B - 1) plan.out_off[(size_t)l * (B + 1) + B] = off + (int64_t)sh.Hkv * (bcast[2] + sh.Nt) * sh.D;
-      if (plan.n_elite[plb] > sh.cap) atomicOr(plan.status, AIRCACHE_DEV_ELITE_OVERFLOW);
+      if (load_coherent(&plan.n_elite[plb]) > sh.cap) atomicOr(plan.status, AIRCACHE_DEV_ELITE_OVERFLOW);
     }
     __syncthreads();
     int kbud = uniform(bcast[2]);
