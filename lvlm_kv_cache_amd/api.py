@@ -100,6 +100,17 @@ class AirCache:
             if not t.is_contiguous():
                 raise ValueError(f"{name}[{l}] is not contiguous")
 
+    def _check_outputs(self, k_out, v_out):
+        s = self.shape
+        cap = _lib.max_compacted_elems(self.desc)
+        for name, outs in (("k_out", k_out), ("v_out", v_out)):
+            if len(outs) != s["L"]:
+                raise ValueError(f"{name}: {len(outs)} layers given")
+            for l, t in enumerate(outs):
+                if t.device != self.device or t.dtype != self.dtype or not t.is_contiguous() or t.numel() < cap:
+                    raise ValueError(f"{name}[{l}] must be a contiguous {self.dtype} tensor on "
+                                     f"{self.device} with at least {cap} elements")
+
     def _stream(self, stream):
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
@@ -122,6 +133,11 @@ class AirCache:
                              events=None if events is None else [e.cuda_event for e in events]))
         return out
 
+    def bind(self, q_txt, k, v, plan: PlanOutputs, k_out, v_out, stream=None) -> "BoundPass":
+        """A BoundPass running plan + compress on these tensors with the
+        argument checks and marshalling done once, here."""
+        return BoundPass(self, q_txt, k, v, plan, k_out, v_out, stream)
+
     def alloc_compacted(self):
         """Worst-case (every visual row kept) per-layer output buffers for K and V."""
         n = _lib.max_compacted_elems(self.desc)
@@ -134,15 +150,69 @@ class AirCache:
         shp = (s["B"], s["Hkv"], s["Nv"] + s["Nt"], s["D"])
         self._check_layers(k, shp, "k")
         self._check_layers(v, shp, "v")
-        cap = _lib.max_compacted_elems(self.desc)
-        for name, outs in (("k_out", k_out), ("v_out", v_out)):
-            if len(outs) != s["L"]:
-                raise ValueError(f"{name}: {len(outs)} layers given")
-            for l, t in enumerate(outs):
-                if t.device != self.device or t.dtype != self.dtype or not t.is_contiguous() or t.numel() < cap:
-                    raise ValueError(f"{name}[{l}] must be a contiguous {self.dtype} tensor on "
-                                     f"{self.device} with at least {cap} elements")
+        self._check_outputs(k_out, v_out)
         _lib.check(_lib.compress(self.desc, plan.buf(), [t.data_ptr() for t in k],
                                  [t.data_ptr() for t in v], [t.data_ptr() for t in k_out],
                                  [t.data_ptr() for t in v_out], self._stream(stream),
                                  events=None if events is None else [e.cuda_event for e in events]))
+
+
+class BoundPass:
+    """plan + compress over fixed tensors, validated once.
+
+    Built by AirCache.bind: the pointer arrays and the plan buffer struct are
+    marshalled when it is built, so each call only crosses into the library
+    (the per-call checks and array building of AirCache.plan / .compress cost
+    tens of microseconds of host time, comparable with the pass itself). The
+    tensors must stay alive and keep their storage while it is used.
+    """
+
+    def __init__(self, ac: "AirCache", q_txt, k, v, plan: PlanOutputs, k_out, v_out, stream=None):
+        s = ac.shape
+        ac._check_layers(q_txt, (s["B"], s["Hq"], s["Nt"], s["D"]), "q_txt")
+        shp = (s["B"], s["Hkv"], s["Nv"] + s["Nt"], s["D"])
+        ac._check_layers(k, shp, "k")
+        ac._check_layers(v, shp, "v")
+        ac._check_outputs(k_out, v_out)
+        self.plan_out = plan
+        self._keep = (ac, q_txt, k, v, plan, k_out, v_out)
+        self._lib = _lib.load()
+        self._desc = _lib.C.byref(ac.desc)
+        self._buf = plan.buf()
+        self._pbuf = _lib.C.byref(self._buf)
+        self._q = _lib.ptr_array([t.data_ptr() for t in q_txt])
+        self._k = _lib.ptr_array([t.data_ptr() for t in k])
+        self._v = _lib.ptr_array([t.data_ptr() for t in v])
+        self._ko = _lib.ptr_array([t.data_ptr() for t in k_out])
+        self._vo = _lib.ptr_array([t.data_ptr() for t in v_out])
+        self._ws = _lib.C.c_void_p(ac.workspace.data_ptr())
+        self._ws_bytes = ac.ws_bytes
+        self._st = _lib.C.c_void_p(ac._stream(stream))
+
+    def plan(self, events=None) -> PlanOutputs:
+        if events is None:
+            rc = self._lib.aircache_plan(self._desc, self._q, self._k, self._pbuf, self._ws, self._ws_bytes,
+                                         self._st)
+        else:
+            ev = [e.cuda_event for e in events]
+            rc = self._lib.aircache_plan_profiled(self._desc, self._q, self._k, self._pbuf, self._ws,
+                                                  self._ws_bytes, self._st, _lib.ptr_array(ev), len(ev))
+        if rc:
+            _lib.check(rc)
+        return self.plan_out
+
+    def compress(self, events=None) -> None:
+        if events is None:
+            rc = self._lib.aircache_compress(self._desc, self._pbuf, self._k, self._v, self._ko, self._vo,
+                                             self._st)
+        else:
+            ev = [e.cuda_event for e in events]
+            rc = self._lib.aircache_compress_profiled(self._desc, self._pbuf, self._k, self._v, self._ko,
+                                                      self._vo, self._st, _lib.ptr_array(ev), len(ev))
+        if rc:
+            _lib.check(rc)
+
+    def __call__(self) -> PlanOutputs:
+        self.plan()
+        self.compress()
+        return self.plan_out

@@ -16,7 +16,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "aircache.h"
 #include "device_common.h"
@@ -1283,11 +1285,60 @@ int check_hip(hipError_t e, const char *what) {
   return AIRCACHE_OK;
 }
 
+// Per-device facts about a kernel that host code asks for on every call
+// (dynamic LDS already allowed, resident workgroups per CU), kept so that a
+// call costs no runtime query after the first one.
+struct KernelFacts {
+  int dev;
+  const void *kern;
+  size_t lds_allowed;
+  size_t occ_lds;
+  int occ;
+};
+std::mutex g_facts_mu;
+std::vector<KernelFacts> g_facts;
+
+KernelFacts *kernel_facts(int dev, const void *kern) {  // g_facts_mu held
+  for (auto &f : g_facts)
+    if (f.dev == dev && f.kern == kern) return &f;
+  g_facts.push_back(KernelFacts{dev, kern, 0, 0, 0});
+  return &g_facts.back();
+}
+
 template <typename K> int allow_lds(K kernel, size_t bytes) {
   if (bytes <= 64 * 1024) return AIRCACHE_OK;
-  return check_hip(hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes),
-                   "hipFuncSetAttribute");
+  int dev = 0, rc;
+  if ((rc = check_hip(hipGetDevice(&dev), "hipGetDevice"))) return rc;
+  const void *kp = reinterpret_cast<const void *>(kernel);
+  std::lock_guard<std::mutex> lock(g_facts_mu);
+  KernelFacts *f = kernel_facts(dev, kp);
+  if (f->lds_allowed >= bytes) return AIRCACHE_OK;
+  if ((rc = check_hip(hipFuncSetAttribute(kp, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes),
+                      "hipFuncSetAttribute")))
+    return rc;
+  f->lds_allowed = bytes;
+  return AIRCACHE_OK;
+}
+
+// Resident workgroups per CU of a kernel at this block size and dynamic LDS.
+template <typename K> int occupancy(K kernel, int threads, size_t lds, int *occ) {
+  int dev = 0, rc;
+  if ((rc = check_hip(hipGetDevice(&dev), "hipGetDevice"))) return rc;
+  const void *kp = reinterpret_cast<const void *>(kernel);
+  std::lock_guard<std::mutex> lock(g_facts_mu);
+  KernelFacts *f = kernel_facts(dev, kp);
+  if (f->occ > 0 && f->occ_lds == lds) {
+    *occ = f->occ;
+    return AIRCACHE_OK;
+  }
+  int v = 0;
+  if ((rc = check_hip(hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kp, threads, lds),
+                      "hipOccupancyMaxActiveBlocksPerMultiprocessor")))
+    return rc;
+  f->occ = v;
+  f->occ_lds = lds;
+  *occ = v;
+  return AIRCACHE_OK;
 }
 
 // Optional instrumentation: when ev is non-NULL, ev[i] is recorded on the
@@ -1342,10 +1393,7 @@ template <typename Tag, int D> int fused_grid(const Config &cfg, int *grid) {
   int cus = 0;
   if ((rc = device_cus(&cus))) return rc;
   int occ = 0;
-  if ((rc = check_hip(hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void *>(kern),
-                                                                   kFusedThreads, lds),
-                      "hipOccupancyMaxActiveBlocksPerMultiprocessor")))
-    return rc;
+  if ((rc = occupancy(kern, kFusedThreads, lds, &occ))) return rc;
   if (occ < 1) return fail(AIRCACHE_EINVAL, "the chunked kernel does not fit a compute unit");
   *grid = cus * occ;
   return AIRCACHE_OK;

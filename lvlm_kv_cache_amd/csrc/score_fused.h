@@ -34,9 +34,7 @@ constexpr int kFusedSlots = 24;      // logit registers per wave: key tiles x ro
 constexpr int kFusedRtMax = 4;       // row tiles per KV head in one item (query fragments in registers)
 constexpr int kFusedMaxItems = 256;  // work items one workgroup can take
 constexpr int kFusedTargetCus = 256; // workgroups the chunk schedule assumes at most
-constexpr int kFusedDigitBits = 5;   // radix digit of the top-k select
-constexpr int kFusedCntStride = 65;  // words per digit row of a wave's top-k counters (64 lanes + 1: no bank conflicts)
-constexpr int kFusedRingMin = kFusedWaves * (1 << kFusedDigitBits) * kFusedCntStride * 4;  // LDS the top-k counters need
+constexpr int kFusedRingMin = 16384;  // LDS bytes the top-k select needs (its histogram and candidates)
 constexpr unsigned kSpinLimit = 1u << 20;  // polls of one wait before it gives up
 
 // Logit slots per wave for an item of rtp row tiles.
@@ -449,30 +447,41 @@ __device__ __forceinline__ int wave_scan_incl(int v) {
 // Top-r_hat of one (layer, sample) by the 512 threads of a workgroup: thread
 // t holds the keys of indices t, t + 512, t + 1024, ... in registers (each load
 // instruction reads 64 consecutive scores per wave). I_v >= 0, so the float32
-// bits order like the values. MSB-first radix select finds the key T of the
-// r_hat-th largest score: the bits above the highest bit in which the minimum
-// and maximum keys differ are common to all keys and skipped; each pass counts
-// the next (up to) kFusedDigitBits bits of the keys that match the prefix
-// found so far, every lane into counters of its own in LDS (rows padded to 65
-// words keep lanes on distinct banks), lane d of each wave adds up one digit
-// over its wave, and after one barrier every wave adds the waves' totals,
-// takes a prefix sum over the digits and finds the digit holding the r_hat-th
-// key (all waves reach the same answer, so no second barrier). Kept: every key
-// > T plus the lowest-index keys equal to T up to r_hat, in ascending index
-// order: each 64-index run of a wave is ranked with a ballot and the runs are
-// placed by their counts. Equal scores thus go to the lower index.
-// cnt: kFusedRingMin bytes of LDS (the waves' counters), zero on entry and exit.
+// bits order like the values, and the order that decides the kept set is
+// (key descending, index ascending). The bits above the highest bit in which
+// the minimum and maximum keys differ are common to all keys and skipped.
+// While more than kTopkRankCap keys match the prefix found so far, a radix
+// pass counts the next (up to) kTopkDigitBits bits of the matching keys into
+// one LDS histogram, a block scan over the buckets in descending digit order
+// finds the bucket holding the need-th key, and the prefix grows by that
+// digit (one pass usually leaves a few dozen keys, since 11 bits below the
+// first differing bit resolve the scores to about 1/64 of an octave). The
+// keys left are then copied to LDS and each is ranked against the others
+// directly; the one of rank need - 1 is the threshold T. Kept: every key > T
+// plus the lowest-index keys equal to T up to the count still needed, in
+// ascending index order (each 64-index run of a wave is ranked with a ballot
+// and the runs are placed by their counts).
+// lds: kTopkLdsWords words, the histogram zero on entry (and left zero).
+constexpr int kTopkDigitBits = 11;
+constexpr int kTopkBuckets = 1 << kTopkDigitBits;
+constexpr int kTopkRankCap = 256;
+constexpr int kTopkLdsWords = kTopkBuckets + 2 * kTopkRankCap + 4;
+static_assert(kTopkLdsWords * 4 <= kFusedRingMin, "the top-k select must fit the ring's minimum size");
 template <int PER>
 __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, int kbud, int32_t *kept,
-                                           unsigned *cnt) {
+                                           unsigned *lds) {
   constexpr int NT = kFusedThreads, NW = kFusedWaves;
-  constexpr int ND = 1 << kFusedDigitBits;
-  constexpr int CS = kFusedCntStride;
-  __shared__ unsigned wdig[2][NW][ND];
+  constexpr int BPT = kTopkBuckets / NT;  // buckets per thread in a scan
+  static_assert(BPT * NT == kTopkBuckets, "buckets must split evenly over the threads");
+  __shared__ int wsum[2][NW];
   __shared__ float wmm[2][NW];
+  __shared__ int selv[2][3];
   __shared__ int rowcnt[2][PER][NW];
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
   const int Nv = sh.Nv;
+  unsigned *hist = lds;
+  uint2 *cand = reinterpret_cast<uint2 *>(lds + kTopkBuckets);
+  unsigned *ncand = lds + kTopkBuckets + 2 * kTopkRankCap;
   if (kbud <= 0) return;
   if (kbud >= Nv) {
     for (int i = tid; i < Nv; i += NT) kept[i] = i;
@@ -483,8 +492,7 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, i
 #pragma unroll
   for (int p = 0; p < PER; ++p)
     key[p] = (p * NT + tid < Nv) ? (unsigned)load_sc1_i(riv, (unsigned)((p * NT + tid) * sizeof(float))) : 0u;
-  unsigned *wc = cnt + (size_t)wave * ND * CS;  // this wave's [digit][lane] counters
-  float fmin = INFINITY, fmax = 0.f;             // keys as floats: same order
+  float fmin = INFINITY, fmax = 0.f;  // keys as floats: same order
 #pragma unroll
   for (int p = 0; p < PER; ++p)
     if (p * NT + tid < Nv) {
@@ -497,6 +505,7 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, i
     wmm[0][wave] = fmin;
     wmm[1][wave] = fmax;
   }
+  if (tid == 0) *ncand = 0u;
   __syncthreads();
   fmin = wmm[0][0];
   fmax = wmm[1][0];
@@ -510,46 +519,93 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, i
   unsigned mask = (hb < 0) ? 0xffffffffu : (hb >= 31) ? 0u : ~((2u << hb) - 1u);
   unsigned prefix = kmin & mask;
   int need = kbud;  // keys still to take among those matching the prefix
+  int nmatch = Nv;  // keys matching the prefix
   int par = 0;
-  while (hb >= 0) {
-    const int width = min(kFusedDigitBits, hb + 1);
+  while (hb >= 0 && nmatch > kTopkRankCap) {
+    const int width = min(kTopkDigitBits, hb + 1);
     const int shift = hb + 1 - width;
     const unsigned dmask = (1u << width) - 1u;
+    const int nb = 1 << width;
 #pragma unroll
     for (int p = 0; p < PER; ++p)
-      if (p * NT + tid < Nv && (key[p] & mask) == prefix)
-        atomicAdd(&wc[((key[p] >> shift) & dmask) * CS + lane], 1u);
-    if (lane < ND) {
-      unsigned *row = wc + lane * CS;  // digit lane of this wave
-      unsigned t = 0;
+      if (p * NT + tid < Nv && (key[p] & mask) == prefix) atomicAdd(&hist[(key[p] >> shift) & dmask], 1u);
+    __syncthreads();
+    // thread t: the buckets of descending positions t * BPT .. t * BPT + BPT - 1
+    int c[BPT], ct = 0;
 #pragma unroll
-      for (int h = 0; h < 64; h += 32) {
-        unsigned v[32];
-#pragma unroll
-        for (int j = 0; j < 32; ++j) v[j] = row[h + j];  // reads in flight together
-#pragma unroll
-        for (int j = 0; j < 32; ++j) t += v[j];
+    for (int j = 0; j < BPT; ++j) {
+      const int q = tid * BPT + j;
+      c[j] = 0;
+      if (q < nb) {
+        unsigned *h = &hist[nb - 1 - q];
+        c[j] = (int)*h;
+        *h = 0u;  // zero again for the next pass or call
       }
+      ct += c[j];
+    }
+    const int incl = wave_scan_incl(ct);
+    if (lane == 63) wsum[par][wave] = incl;
+    __syncthreads();
+    int above = incl - ct;
+    for (int w = 0; w < wave; ++w) above += wsum[par][w];
+    if (ct > 0 && above < need && above + ct >= need) {
 #pragma unroll
-      for (int j = 0; j < 64; ++j) row[j] = 0u;
-      wdig[par][wave][lane] = t;
+      for (int j = 0; j < BPT; ++j) {
+        if (above + c[j] >= need) {
+          selv[par][0] = nb - 1 - (tid * BPT + j);
+          selv[par][1] = above;
+          selv[par][2] = c[j];
+          break;
+        }
+        above += c[j];
+      }
     }
     __syncthreads();
-    // every wave: lane q holds digit ND - 1 - q (descending) summed over waves
-    int c = 0;
-    if (lane < ND)
-      for (int w = 0; w < NW; ++w) c += (int)wdig[par][w][ND - 1 - lane];
-    const int incl = wave_scan_incl(c);
-    const int above = incl - c;  // matching keys with a larger digit
-    const unsigned long long hit = __ballot(lane < ND && above < need && above + c >= need);
-    const int q = hit ? __ffsll((long long)hit) - 1 : 0;
-    prefix |= (unsigned)(ND - 1 - q) << shift;
+    const int d = uniform(selv[par][0]);
+    prefix |= (unsigned)d << shift;
     mask |= dmask << shift;
-    need -= __builtin_amdgcn_readlane(above, q);
+    need -= uniform(selv[par][1]);
+    nmatch = uniform(selv[par][2]);
     hb -= width;
     par ^= 1;
   }
-  const unsigned T = prefix;
+  // T and the count of keys equal to T still to take
+  int need_eq = need;
+  unsigned T = prefix;
+  if (hb >= 0) {
+    // the nmatch <= kTopkRankCap keys matching the prefix, ranked directly
+    const unsigned long long lt = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const bool mt = p * NT + tid < Nv && (key[p] & mask) == prefix;
+      const unsigned long long mb = __ballot(mt);
+      if (mb) {
+        unsigned base = 0u;
+        if (lane == 0) base = atomicAdd(ncand, (unsigned)__popcll(mb));
+        base = __shfl(base, 0);
+        if (mt) cand[base + __popcll(mb & lt)] = make_uint2(key[p], (unsigned)(p * NT + tid));
+      }
+    }
+    __syncthreads();
+    nmatch = min(nmatch, kTopkRankCap);
+    if (tid < nmatch) {
+      const uint2 me = cand[tid];
+      int gt = 0, before = 0;
+      for (int i = 0; i < nmatch; ++i) {
+        const uint2 o = cand[i];
+        gt += (o.x > me.x) ? 1 : 0;
+        before += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1 : 0;
+      }
+      if (before == need - 1) {
+        selv[par][0] = (int)me.x;
+        selv[par][1] = need - gt;
+      }
+    }
+    __syncthreads();
+    T = (unsigned)uniform(selv[par][0]);
+    need_eq = uniform(selv[par][1]);
+    if (tid == 0) *ncand = 0u;
+  }
   // per run (p, wave) of 64 indices: keys equal to T, then keys kept
   const unsigned long long lt = (1ull << lane) - 1ull;
   unsigned long long meq[PER];
@@ -572,7 +628,7 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, i
     const bool valid = p * NT + tid < Nv;
     const bool eq = (meq[p] >> lane) & 1ull;
     const int eq_rank = eq_base + before + __popcll(meq[p] & lt);
-    mk[p] = __ballot(valid && (key[p] > T || (eq && eq_rank < need)));
+    mk[p] = __ballot(valid && (key[p] > T || (eq && eq_rank < need_eq)));
     if (lane == 0) rowcnt[1][p][wave] = __popcll(mk[p]);
     eq_base += row;
   }
@@ -1059,7 +1115,7 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
   {
     const int tid = opaque_tid();
     __syncthreads();  // every wave is done with the item LDS
-    for (int i = tid; i < kFusedWaves * (1 << kFusedDigitBits) * kFusedCntStride; i += kFusedThreads) cnt[i] = 0u;
+    for (int i = tid; i < kTopkBuckets; i += kFusedThreads) cnt[i] = 0u;
   }
   for (;;) {
     const int tid = opaque_tid();

@@ -99,6 +99,36 @@ def test_workspace_reused_across_calls():
         compare(inp, g, reference(inp, g))
 
 
+def test_bound_pass_matches_plain_calls():
+    """AirCache.bind (marshalling done once) gives bit-identical results to
+    the per-call plan / compress, over repeated calls."""
+    from parity import make_aircache, to_torch
+    w = wl.custom(Nv=900, Nt=30, Hq=8, Hkv=4, D=128, dtype="bf16", L=3, B=2, ratio=0.2)
+    inp = wl.make_inputs(w, 31)
+    q, k, v = to_torch(inp)
+    ac = make_aircache(w)
+    plain = run_gpu(inp, ac=ac, tensors=(q, k, v))
+    plan = ac.alloc_plan()
+    ko, vo = ac.alloc_compacted()
+    bp = ac.bind(q, k, v, plan, ko, vo)
+    for _ in range(3):
+        bp()
+        torch.cuda.synchronize()
+        for f in ("elite_idx", "n_elite", "iv", "s_t", "s_k", "budget_x", "budget", "out_off", "kept_idx", "status"):
+            a, b = getattr(plan, f).cpu().numpy(), plain[f]
+            if f == "elite_idx":
+                a = np.concatenate([a[l, bb, :plain["n_elite"][l, bb]] for l in range(w.L) for bb in range(w.B)])
+                b = np.concatenate([b[l, bb, :plain["n_elite"][l, bb]] for l in range(w.L) for bb in range(w.B)])
+            if f == "kept_idx":
+                a = np.concatenate([a[l, bb, :plain["budget"][l, bb]] for l in range(w.L) for bb in range(w.B)])
+                b = np.concatenate([b[l, bb, :plain["budget"][l, bb]] for l in range(w.L) for bb in range(w.B)])
+            assert np.array_equal(a, b), f
+        for l in range(w.L):
+            n = int(plain["out_off"][l, w.B])
+            assert torch.equal(ko[l][:n].cpu(), torch.from_numpy(plain["k_out"][l].view(np.int16)).view(ko[l].dtype))
+            assert torch.equal(vo[l][:n].cpu(), torch.from_numpy(plain["v_out"][l].view(np.int16)).view(vo[l].dtype))
+
+
 @pytest.mark.parametrize("alpha,ratio", [(0.0, 0.1), (1.0, 0.1), (0.9, 0.0), (0.9, 1.0), (0.5, 0.5)])
 def test_alpha_ratio_extremes(alpha, ratio):
     w = wl.custom(Nv=200, Nt=24, Hq=6, Hkv=2, D=128, dtype="bf16", L=3, B=2)
