@@ -1091,7 +1091,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 struct Config {
   Shape sh;
   size_t off_cnt, off_stats, off_e, off_part, ws_bytes;
-  size_t off_xrec, off_mom, off_brec, off_part_rg, off_cnt_chunk;
+  size_t off_xrec, off_mom, off_srec, off_part_rg, off_cnt_chunk, off_cnt_lbc;
   size_t off_cnt_elite, off_pbar, off_sched;
   size_t elite_lds, score_lds, final_lds, rows_lds;
   int ktw;
@@ -1213,10 +1213,10 @@ int make_config(const aircache_desc *d, Config *cfg) {
     cfg->max_rg = maxrg;
     cfg->wmax = wmax;
     const int tb = (int)tile_bytes;
-    cfg->flds = fused_lds_layout(tb, tb <= 4096 ? 3 : 2, s.cap, s.Hkv, s.B);
+    cfg->flds = fused_lds_layout(tb, tb <= 4096 ? 3 : 2, s.cap, s.Hkv, lb, s.Nt);
     const bool lds_ok = (size_t)cfg->flds.total + 8192 <= kMaxLds &&
-                        (size_t)(s.G > 1 ? s.G : 1) * s.Nt * sizeof(float) <= (size_t)cfg->flds.total &&  // phase 0
-                        (size_t)s.L * maxc * 40 <= (size_t)(cfg->flds.el - cfg->flds.ring);  // finisher's records
+                        (size_t)(s.G > 1 ? s.G : 1) * s.Nt * sizeof(float) <= (size_t)cfg->flds.total &&  // KV-head parts
+                        (size_t)s.Nt * sizeof(float) <= (size_t)(cfg->flds.el - cfg->flds.ring);       // pbar staging
     // the schedule is worked out by one wave: at most 8 (layer, sample) pairs per lane
     const bool items_ok = lb <= 512 && (long long)lb * maxc * maxrg <= (long long)kFusedMaxItems * kFusedTargetCus &&
                           maxc <= 64;
@@ -1232,18 +1232,19 @@ int make_config(const aircache_desc *d, Config *cfg) {
   cfg->off_cnt_elite = cfg->off_cnt + align_up(n_cnt * sizeof(unsigned));
   cfg->off_pbar = cfg->off_cnt_elite + align_up((size_t)s.L * s.B * sizeof(unsigned));
   cfg->off_sched = cfg->off_pbar + align_up((size_t)s.L * s.B * s.Hkv * s.Nt * sizeof(float));
-  // elite-set counter of the chunked path
-  const size_t eflags = cfg->chunked ? align_up(sizeof(unsigned)) : 0;
+  // part and exit counters of the chunked path
+  const size_t eflags = cfg->chunked ? align_up(2 * sizeof(unsigned)) : 0;
   cfg->off_stats = cfg->off_sched + eflags;
-  cfg->off_xrec = cfg->off_mom = cfg->off_brec = cfg->off_stats;
+  cfg->off_xrec = cfg->off_mom = cfg->off_srec = cfg->off_stats;
   if (cfg->chunked) {
     const size_t lbs = (size_t)s.L * s.B;
     cfg->off_e = cfg->off_part = cfg->off_stats;
     cfg->off_xrec = cfg->off_stats;
     cfg->off_mom = cfg->off_xrec + align_up(lbs * (size_t)cfg->rec_stride * 16);
-    cfg->off_brec = cfg->off_mom + align_up(lbs * (size_t)cfg->max_chunks * 32);
-    cfg->off_cnt_chunk = cfg->off_brec + align_up(lbs * 8);
-    cfg->off_part_rg = cfg->off_cnt_chunk + align_up(lbs * (size_t)cfg->max_chunks * sizeof(unsigned));
+    cfg->off_srec = cfg->off_mom + align_up(lbs * (size_t)cfg->max_chunks * 32);
+    cfg->off_cnt_chunk = cfg->off_srec + align_up(lbs * 32);
+    cfg->off_cnt_lbc = cfg->off_cnt_chunk + align_up(lbs * (size_t)cfg->max_chunks * sizeof(unsigned));
+    cfg->off_part_rg = cfg->off_cnt_lbc + align_up(lbs * sizeof(unsigned));
     // row-group partial sums only when some elite count can need two row groups
     const size_t part_rg = cfg->max_rg > 1 ? lbs * (size_t)cfg->max_chunks * cfg->max_rg * cfg->wmax * sizeof(float) : 0;
     cfg->ws_bytes = cfg->off_part_rg + align_up(part_rg);
@@ -1413,19 +1414,18 @@ int launch_chunked(const Config &cfg, const LayerTable &qt, const LayerTable &kt
   char *p = static_cast<char *>(ws_base);
   FusedWs fw;
   fw.epoch = ws.epoch;
-  fw.cnt_b = ws.cnt_b;
-  fw.ticket = ws.cnt_all;
+  fw.edone = reinterpret_cast<unsigned *>(p + cfg.off_sched);
+  fw.exitc = fw.edone + 1;
   fw.xrec = reinterpret_cast<uint64_t *>(p + cfg.off_xrec);
   fw.mom = reinterpret_cast<double *>(p + cfg.off_mom);
-  fw.brec = reinterpret_cast<uint64_t *>(p + cfg.off_brec);
+  fw.srec = reinterpret_cast<uint64_t *>(p + cfg.off_srec);
+  fw.cnt_lbc = reinterpret_cast<unsigned *>(p + cfg.off_cnt_lbc);
   fw.rec_stride = cfg.rec_stride;
   fw.max_chunks = cfg.max_chunks;
   fw.max_rg = cfg.max_rg;
   fw.wmax = cfg.wmax;
   fw.cnt_chunk = ws.cnt_chunk;
   fw.part = reinterpret_cast<float *>(p + cfg.off_part_rg);
-  fw.edone = reinterpret_cast<unsigned *>(p + cfg.off_sched);
-  fw.cnt_elite = ws.cnt_elite;
   fw.parts = ws.pbar_part;
   // One workgroup per CU (the LDS use admits no second), so with the device
   // to itself every workgroup is resident at once, which the waits between

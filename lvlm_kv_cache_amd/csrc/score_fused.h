@@ -14,18 +14,27 @@
 // per-row (max, sum) pairs through epoch-tagged records (no counter round
 // trip). A chunk's slice of I_v is then final (one row group) or the sum of
 // its row groups' partial column sums (the last row group to finish, a
-// counter election, adds them in order); with it go the slice's moments. The
-// last chunk of a sample (a counter election) combines the moments of all its
-// layers into s_t and s_k and computes the sample's budgets. After its items a
-// workgroup takes top-k tasks from a ticket counter; each waits for its
-// sample's budgets.
+// counter election, adds them in order); with it go the slice's moments.
+//
+// Before the items: one workgroup per (layer, sample, KV head) computes that
+// head's part of the elite observation window's pbar and counts it done;
+// once all are done every workgroup sums the parts of every (layer, sample)
+// itself (no second election and round trip), so each knows all elite sets
+// and works out the same chunk schedule.
+//
+// After the items: the last chunk of a (layer, sample) to finish (a counter
+// election) combines the chunks' moments into s_t and s_k and publishes them
+// in an epoch-tagged record; its workgroup then runs that (layer, sample)'s
+// top-k, whose budget-independent first radix pass overlaps the wait for the
+// records of every layer of the samples up to its own, from which it computes
+// the budgets and the compacted offsets it needs.
 //
 // All workgroups are co-resident (one 512-thread workgroup per CU, the LDS use
-// admitting no second), and a workgroup only waits for items that come no later
-// in the item order than its own or, in the top-k phase, for items every other
-// workgroup finishes before it takes a ticket; so every wait ends. Each wait
-// is also bounded: on expiry the kernel sets AIRCACHE_DEV_TIMEOUT and every
-// other wait of the launch gives up too.
+// admitting no second), and a workgroup only waits for items that come no
+// later in the item order than its own or, after its items, for records that
+// other workgroups publish once their own items are done; so every wait ends.
+// Each wait is also bounded: on expiry the kernel sets AIRCACHE_DEV_TIMEOUT
+// and every other wait of the launch gives up too.
 #pragma once
 
 constexpr int kFusedThreads = 512;
@@ -37,8 +46,11 @@ constexpr int kFusedTargetCus = 256; // workgroups the chunk schedule assumes at
 constexpr int kFusedRingMin = 16384;  // LDS bytes the top-k select needs (its histogram and candidates)
 constexpr unsigned kSpinLimit = 1u << 20;  // polls of one wait before it gives up
 
-// Logit slots per wave for an item of rtp row tiles.
-__host__ __device__ constexpr int fused_slots(int rtp) { return kFusedSlots + 0 * rtp; }
+// Key tiles per wave that the logit registers hold for rtp row tiles
+// (kFusedSlots / rtp, rtp in 1..4).
+__host__ __device__ constexpr int fused_ktmax(int rtp) {
+  return rtp <= 1 ? kFusedSlots : rtp == 2 ? kFusedSlots / 2 : rtp == 3 ? kFusedSlots / 3 : kFusedSlots / 4;
+}
 
 // One poll of a bounded wait. True when the wait must end: this one ran out
 // (the timeout bit is set) or another one in the launch already did.
@@ -73,7 +85,7 @@ __host__ __device__ inline ChunkPlan fused_chunk_plan(int ntk, int G, int Nv, in
   p.rtg = rows > 0 ? (rows + 15) / 16 : 1;
   p.nrg = (p.rtg + kFusedRtMax - 1) / kFusedRtMax;
   p.rtp = p.rtg < kFusedRtMax ? p.rtg : kFusedRtMax;
-  const int ktmax = fused_slots(p.rtp) / p.rtp;
+  const int ktmax = fused_ktmax(p.rtp);
   int k = kcap < ktmax ? kcap : ktmax;
   if (k < 1) k = 1;
   p.ktw = k;
@@ -97,15 +109,14 @@ __host__ __device__ inline int fused_kcap_min(int L, int B, int Nv, int wph) {
 // match. The workspace must be zero before its first use.
 struct FusedWs {
   unsigned *epoch;        // [1] calls so far
-  unsigned *edone;        // [1] elite sets published in this call
-  unsigned *cnt_elite;    // [L*B] KV-head parts finished per (layer, sample)
+  unsigned *edone;        // [1] KV-head parts of pbar finished in this call
+  unsigned *exitc;        // [1] workgroups finished in this call
   float *parts;           // [L*B*Hkv][N_t] KV-head parts of pbar
-  unsigned *cnt_b;        // [B] finished chunks per sample
-  unsigned *ticket;       // [1] top-k tasks handed out
+  unsigned *cnt_lbc;      // [L*B] finished chunks per (layer, sample)
   unsigned *cnt_chunk;    // [L*B][max_chunks] finished row groups per chunk
   uint64_t *xrec;         // [L*B][rec_stride][2] (row max | epoch << 32), (row sum | epoch << 32)
   double *mom;            // [L*B][max_chunks][4] chunk sum, M2, M3, count
-  uint64_t *brec;         // [L*B] (budget | epoch << 32)
+  uint64_t *srec;         // [L*B][4] halves of s_t and s_k, each | epoch << 32
   float *part;            // [L*B][max_chunks][max_rg][wmax] row-group column sums
   int rec_stride;         // records per (layer, sample)
   int max_chunks;         // chunks per (layer, sample) at most
@@ -114,11 +125,18 @@ struct FusedWs {
 };
 
 // Dynamic LDS of cross_score_fused_kernel (byte offsets, 16-byte aligned).
+// ring: the key tiles of the waves, also the staging of pbar before the
+// items and the top-k's histogram after them; ntk / emask: the elite count
+// and the elite set (a bit per text token) of every (layer, sample); sts: the
+// s_t and s_k a budget needs; items / owed: this workgroup's work items and
+// the (layer, sample) pairs whose top-k it owes.
 struct FusedLds {
-  int ring, el, colsum, red, mloc, wts, ctarget, items, total;
+  int ring, el, colsum, red, mloc, wts, items, owed, ntk, emask, sts, total;
 };
 __host__ __device__ inline int fused_align16(int x) { return (x + 15) & ~15; }
-__host__ __device__ inline FusedLds fused_lds_layout(int tile_bytes, int ring_depth, int cap, int Hkv, int B) {
+__host__ __device__ inline int fused_words64(int Nt) { return (Nt + 63) >> 6; }
+__host__ __device__ inline FusedLds fused_lds_layout(int tile_bytes, int ring_depth, int cap, int Hkv, int LB,
+                                                     int Nt) {
   FusedLds f;
   const int wph = kFusedWaves / Hkv;
   int o = 0;
@@ -135,10 +153,16 @@ __host__ __device__ inline FusedLds fused_lds_layout(int tile_bytes, int ring_de
   o += fused_align16(Hkv * kFusedRtMax * 16 * 4);
   f.wts = o;
   o += fused_align16(Hkv * kFusedRtMax * 16 * 4);
-  f.ctarget = o;
-  o += fused_align16(B * 4);
   f.items = o;
   o += fused_align16(kFusedMaxItems * 4);
+  f.owed = o;
+  o += fused_align16(kFusedMaxItems * 4);
+  f.ntk = o;
+  o += fused_align16(LB * 4);
+  f.emask = o;
+  o += fused_align16(LB * fused_words64(Nt) * 8);
+  f.sts = o;
+  o += fused_align16((LB + 8) * 16);  // reads run up to 8 entries past each array
   f.total = o;
   return f;
 }
@@ -217,7 +241,7 @@ __device__ __forceinline__ void fused_pass(const Shape &sh, const FusedWs &fw, c
                                            bool first) {
   using E = typename Tag::store_t;
   constexpr int NW = kFusedWaves;
-  constexpr int KTMAX = fused_slots(RTP) / RTP;
+  constexpr int KTMAX = fused_ktmax(RTP);
   constexpr int kTileBytes = 16 * D * Tag::kBytes;
   constexpr int kDma = kTileBytes / 1024;
   constexpr int kRing = (kTileBytes <= 4096) ? 3 : 2;
@@ -296,17 +320,27 @@ __device__ __forceinline__ void fused_pass(const Shape &sh, const FusedWs &fw, c
         for (int i = 0; i < 4; ++i) S[s][rt][i] = ok ? acc[rt][i] * sh.scale2 : -INFINITY;
     }
   }
-  // chunk-local row maxima: keys of a lane row (DPP), then the head's waves in order
+  // chunk-local row maxima: keys of a lane row (DPP), then the head's waves in
+  // order. The key tiles are the outer loop, so the 4 * RTP row chains
+  // interleave instead of waiting on each other.
   constexpr int RW = RTP * 16;  // rows of one head in this pass
+  float racc[RTP][4];
+#pragma unroll
+  for (int rt = 0; rt < RTP; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) racc[rt][i] = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < KTMAX; ++s)
+    if (s < ktw)
+#pragma unroll
+      for (int rt = 0; rt < RTP; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) racc[rt][i] = fmaxf(racc[rt][i], S[s][rt][i]);
 #pragma unroll
   for (int rt = 0; rt < RTP; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int s = 0; s < KTMAX; ++s)
-        if (s < ktw) m = fmaxf(m, S[s][rt][i]);
-      m = row16_max(m);
+      const float m = row16_max(racc[rt][i]);
       if (n == 0) red[wave * RW + rt * 16 + grp * 4 + i] = m;
     }
   __syncthreads();
@@ -317,21 +351,33 @@ __device__ __forceinline__ void fused_pass(const Shape &sh, const FusedWs &fw, c
     mloc[gg * RW + rr] = m;
   }
   __syncthreads();
-  // exponentials in place and chunk-local row sums
+  // exponentials in place and chunk-local row sums (each row summed in key
+  // order; the rows interleave)
+#pragma unroll
+  for (int rt = 0; rt < RTP; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) racc[rt][i] = 0.f;
+  float Mrow[RTP][4];
+#pragma unroll
+  for (int rt = 0; rt < RTP; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Mrow[rt][i] = mloc[g * RW + rt * 16 + grp * 4 + i];
+#pragma unroll
+  for (int s = 0; s < KTMAX; ++s)
+    if (s < ktw)
+#pragma unroll
+      for (int rt = 0; rt < RTP; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float ev = exp2_fast(S[s][rt][i] - Mrow[rt][i]);
+          S[s][rt][i] = ev;
+          racc[rt][i] += ev;
+        }
 #pragma unroll
   for (int rt = 0; rt < RTP; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float M = mloc[g * RW + rt * 16 + grp * 4 + i];
-      float z = 0.f;
-#pragma unroll
-      for (int s = 0; s < KTMAX; ++s)
-        if (s < ktw) {
-          const float ev = exp2_fast(S[s][rt][i] - M);
-          S[s][rt][i] = ev;
-          z += ev;
-        }
-      z = row16_sum(z);
+      const float z = row16_sum(racc[rt][i]);
       if (n == 0) red[wave * RW + rt * 16 + grp * 4 + i] = z;
     }
   __syncthreads();
@@ -467,9 +513,9 @@ constexpr int kTopkBuckets = 1 << kTopkDigitBits;
 constexpr int kTopkRankCap = 256;
 constexpr int kTopkLdsWords = kTopkBuckets + 2 * kTopkRankCap + 4;
 static_assert(kTopkLdsWords * 4 <= kFusedRingMin, "the top-k select must fit the ring's minimum size");
-template <int PER>
-__device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, int kbud, int32_t *kept,
-                                           unsigned *lds) {
+template <int PER, typename BudgetFn>
+__device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, int32_t *kept, unsigned *lds,
+                                           BudgetFn &&get_budget) {
   constexpr int NT = kFusedThreads, NW = kFusedWaves;
   constexpr int BPT = kTopkBuckets / NT;  // buckets per thread in a scan
   static_assert(BPT * NT == kTopkBuckets, "buckets must split evenly over the threads");
@@ -482,11 +528,6 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, i
   unsigned *hist = lds;
   uint2 *cand = reinterpret_cast<uint2 *>(lds + kTopkBuckets);
   unsigned *ncand = lds + kTopkBuckets + 2 * kTopkRankCap;
-  if (kbud <= 0) return;
-  if (kbud >= Nv) {
-    for (int i = tid; i < Nv; i += NT) kept[i] = i;
-    return;
-  }
   const auto riv = coherent_rsrc(iv_l, (unsigned)(Nv * sizeof(float)));
   unsigned key[PER];
 #pragma unroll
@@ -518,6 +559,27 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, i
   int hb = diff ? 31 - __clz((int)diff) : -1;  // highest bit in which keys can differ
   unsigned mask = (hb < 0) ? 0xffffffffu : (hb >= 31) ? 0u : ~((2u << hb) - 1u);
   unsigned prefix = kmin & mask;
+  // the first radix pass does not depend on the budget: count it before
+  // asking for the budget (whose wait it overlaps)
+  bool counted = hb >= 0 && Nv > kTopkRankCap;
+  if (counted) {
+    const int width = min(kTopkDigitBits, hb + 1);
+    const int shift = hb + 1 - width;
+    const unsigned dmask = (1u << width) - 1u;
+#pragma unroll
+    for (int p = 0; p < PER; ++p)
+      if (p * NT + tid < Nv) atomicAdd(&hist[(key[p] >> shift) & dmask], 1u);
+  }
+  int kbud = get_budget();  // block-wide, with barriers
+  if (kbud < 0) kbud = 0;
+  if (kbud > Nv) kbud = Nv;
+  if (kbud <= 0 || kbud >= Nv) {
+    if (counted)  // leave the histogram zero (the budget's barriers ordered the counts before this)
+      for (int i = tid; i < kTopkBuckets; i += NT) hist[i] = 0u;
+    if (kbud >= Nv)
+      for (int i = tid; i < Nv; i += NT) kept[i] = i;
+    return;
+  }
   int need = kbud;  // keys still to take among those matching the prefix
   int nmatch = Nv;  // keys matching the prefix
   int par = 0;
@@ -526,9 +588,12 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, i
     const int shift = hb + 1 - width;
     const unsigned dmask = (1u << width) - 1u;
     const int nb = 1 << width;
+    if (!counted) {
 #pragma unroll
-    for (int p = 0; p < PER; ++p)
-      if (p * NT + tid < Nv && (key[p] & mask) == prefix) atomicAdd(&hist[(key[p] >> shift) & dmask], 1u);
+      for (int p = 0; p < PER; ++p)
+        if (p * NT + tid < Nv && (key[p] & mask) == prefix) atomicAdd(&hist[(key[p] >> shift) & dmask], 1u);
+    }
+    counted = false;
     __syncthreads();
     // thread t: the buckets of descending positions t * BPT .. t * BPT + BPT - 1
     int c[BPT], ct = 0;
@@ -647,19 +712,6 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, i
   }
 }
 
-// Wait for the budget record of plan index plb; returns the budget.
-__device__ __forceinline__ int fused_wait_budget(const FusedWs &fw, int plb, unsigned epoch, int *status) {
-  const auto rb = coherent_rsrc(fw.brec + plb, 8u);
-  uint64_t v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rb, 0, 0, 16));
-  unsigned spins = 0;
-  while ((unsigned)(v >> 32) != epoch) {
-    if (spin_expired(spins, status)) break;
-    __builtin_amdgcn_s_sleep(8);
-    v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rb, 0, 0, 16));
-  }
-  return (int)(unsigned)v;
-}
-
 // Phase 0, one item per (layer, sample, KV head): the part of the elite
 // observation window's pbar that the KV head's G query heads give ("Elite
 // Observation Window", the Att equation). The logits of the last text query
@@ -741,110 +793,347 @@ __device__ __forceinline__ void fused_elite_part(const Shape &sh, const LayerTab
   }
 }
 
-// The last KV head of a (layer, sample) to finish its part: pbar = the sum of
-// the parts in ascending KV-head order, elite = { j : pbar_j >= alpha max pbar },
-// compacted in ascending j by a block scan and written with agent-coherent
-// stores ("Elite Observation Window", the k equation). lds: N_t floats.
-__device__ __forceinline__ void fused_elite_merge(const Shape &sh, const PlanPtrs &plan, const float *parts, int lb,
-                                                  float *lds, int *wtot, float *red) {
-  constexpr int NW = kFusedWaves, NT = kFusedThreads;
-  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
-  const int Nt = sh.Nt;
-  float *pbar = lds;
-  const auto rp = coherent_rsrc(parts, (unsigned)((size_t)sh.Hkv * Nt * sizeof(float)));
-  float m = -INFINITY;
-  for (int j = tid; j < Nt; j += NT) {
-    float a = 0.f;
-    for (int gg = 0; gg < sh.Hkv; ++gg) a += load_sc1_f(rp, (unsigned)(((size_t)gg * Nt + j) * sizeof(float)));
-    pbar[j] = a;
-    m = fmaxf(m, a);
-  }
-  m = wave_max(m);
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  m = red[0];
-  for (int w = 1; w < NW; ++w) m = fmaxf(m, red[w]);
-  const float thr = sh.alpha * m;
-  const int per = (Nt + NT - 1) / NT;
-  const int j0 = min(Nt, tid * per), j1 = min(Nt, j0 + per);
-  int cnt = 0;
-  for (int j = j0; j < j1; ++j) cnt += (pbar[j] >= thr) ? 1 : 0;
-  int total;
-  int pos = fused_block_scan(cnt, wtot, &total);
-  int32_t *el = plan.elite + (size_t)lb * Nt;
-  for (int j = j0; j < j1; ++j)
-    if (pbar[j] >= thr) store_coherent(&el[pos++], (int32_t)j);
-  if (tid == 0) store_coherent(&plan.n_elite[lb], (int32_t)total);
+// ceil(a / b) for 0 <= a < 2^20 and 1 <= b, without an integer division:
+// the float estimate is within one of floor(a / b) and is corrected exactly.
+__device__ __forceinline__ int ceil_div_small(int a, int b) {
+  int q = (int)((float)a * __builtin_amdgcn_rcpf((float)b));
+  if (q * b > a) --q;
+  if ((q + 1) * b <= a) ++q;
+  return q + (q * b < a ? 1 : 0);
 }
 
-// Work schedule of this workgroup, worked out by the 64 lanes of wave 0 (no
-// block barriers) from the elite counts: lane q holds the (b, l) pairs
-// q * per .. q * per + per - 1 in sample-major order. The cap on key tiles per
-// wave is the smallest (narrowest chunks, most workgroups busy) whose items
-// all fit one round of the grid, the widest when none does (a binary search,
-// items being non-increasing in the cap). Items go in the order (b, l, row
-// group, chunk); workgroup me takes items me, me + P, ... Writes the items of
-// this workgroup to item[] ((b * L + l) << 16 | index in the (layer, sample)),
-// ctarget[b] (chunks of sample b), hdr[0] = cap and hdr[1] = item count.
-__device__ __forceinline__ void fused_schedule(const Shape &sh, const int (&ntk_of)[8], int me, int P, int *item,
-                                               int *ctarget, int *hdr) {
-  const int lane = threadIdx.x & 63;
+// Before the items, every workgroup: pbar of every (layer, sample) as the sum
+// of its KV-head parts in ascending head order (the "Elite Observation
+// Window" Att equation summed over heads), the elite set
+// { j : pbar_j >= alpha max pbar } as a bit mask per 64 text tokens in emask,
+// and its size, clamped to the elite cap, in ntk. Workgroup lb % P also
+// writes the plan's elite list and count of lb and flags an elite set above
+// the cap. stage: LDS for stage_floats floats of pbar (a batch of pairs).
+// HKV = n_kv_heads: every thread keeps 32 part loads in flight.
+template <int HKV>
+__device__ __forceinline__ void fused_elite_sets_h(const Shape &sh, const PlanPtrs &plan, const float *parts, int me,
+                                                   int P, float *stage, int stage_floats, int *ntk,
+                                                   unsigned long long *emask) {
+  constexpr int NT = kFusedThreads, NW = kFusedWaves, R = 32 / HKV, U = 4;
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int Nt = sh.Nt, LB = sh.L * sh.B;
+  const int ntw = fused_words64(Nt);
+  const int batch = max(1, stage_floats / Nt);  // (layer, sample) pairs per batch
+  const auto rp = coherent_rsrc(parts, (unsigned)((size_t)LB * HKV * Nt * sizeof(float)));
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int lb0 = 0; lb0 < LB; lb0 += batch) {
+    const int nlb = min(batch, LB - lb0);
+    const int n = nlb * Nt;
+    for (int e0 = 0; e0 < n; e0 += R * NT) {
+      // every load issued before any is used (an entry past the batch reads
+      // past the buffer's bounds, which returns 0 without a memory access)
+      float part[R][HKV];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int e = e0 + r * NT + tid;
+        const int q = ceil_div_small(e + 1, Nt) - 1, j = e - q * Nt;  // e / Nt, e % Nt
+        const unsigned base = (unsigned)((((size_t)(lb0 + q) * HKV) * Nt + j) * sizeof(float));
+#pragma unroll
+        for (int g = 0; g < HKV; ++g)
+          part[r][g] = load_sc1_f(rp, e < n ? base + (unsigned)(g * Nt * sizeof(float)) : 0xfffffff0u);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int e = e0 + r * NT + tid;
+        float a = 0.f;
+#pragma unroll
+        for (int g = 0; g < HKV; ++g) a += part[r][g];
+        if (e < n) stage[e] = a;
+      }
+    }
+    __syncthreads();
+    // U pairs per wave at a time: their reduction chains interleave
+    for (int q0 = wave * U; q0 < nlb; q0 += NW * U) {
+      float thr[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int q = min(q0 + u, nlb - 1);
+        float m = -INFINITY;
+        for (int j = lane; j < Nt; j += 64) m = fmaxf(m, stage[(size_t)q * Nt + j]);
+        thr[u] = m;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) thr[u] = sh.alpha * wave_max(thr[u]);
+      int cnt[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) cnt[u] = 0;
+      for (int w = 0; w < ntw; ++w) {
+        const int j = w * 64 + lane;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int q = q0 + u;
+          if (q < nlb) {
+            const int lb = lb0 + q;
+            const bool in = j < Nt && stage[(size_t)q * Nt + j] >= thr[u];
+            const unsigned long long mk = __ballot(in);
+            if (lane == 0) emask[(size_t)lb * ntw + w] = mk;
+            cnt[u] += __popcll(mk);
+          }
+        }
+      }
+      if (lane == 0)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int q = q0 + u;
+          if (q < nlb) ntk[lb0 + q] = cnt[u] < sh.cap ? cnt[u] : sh.cap;
+        }
+    }
+    __syncthreads();  // the stage is free again; ntk and emask are complete
+  }
+  // the plan's elite lists and counts of pairs me, me + P, ...: wave w takes
+  // pair me + w P, lane j of word i holds token 64 i + j
+  for (int lb = me + wave * P; lb < LB; lb += NW * P) {
+    int cnt = 0;
+    for (int w = 0; w < ntw; ++w) {
+      const unsigned long long mk = emask[(size_t)lb * ntw + w];
+      if ((mk >> lane) & 1ull) plan.elite[(size_t)lb * Nt + cnt + __popcll(mk & lt)] = w * 64 + lane;
+      cnt += __popcll(mk);
+    }
+    if (lane == 0) {
+      plan.n_elite[lb] = cnt;
+      if (cnt > sh.cap) atomicOr(plan.status, AIRCACHE_DEV_ELITE_OVERFLOW);
+    }
+  }
+}
+__device__ __forceinline__ void fused_elite_sets(const Shape &sh, const PlanPtrs &plan, const float *parts, int me,
+                                                 int P, float *stage, int stage_floats, int *ntk,
+                                                 unsigned long long *emask) {
+  switch (sh.Hkv) {
+    case 1: fused_elite_sets_h<1>(sh, plan, parts, me, P, stage, stage_floats, ntk, emask); break;
+    case 2: fused_elite_sets_h<2>(sh, plan, parts, me, P, stage, stage_floats, ntk, emask); break;
+    case 4: fused_elite_sets_h<4>(sh, plan, parts, me, P, stage, stage_floats, ntk, emask); break;
+    default: fused_elite_sets_h<8>(sh, plan, parts, me, P, stage, stage_floats, ntk, emask); break;
+  }
+}
+
+// Work schedule of this workgroup, block-wide, from the elite counts ntk
+// (LDS, [layer][sample]): thread s takes the pair (b, l) = (s / L, s % L) in
+// sample-major order. The cap on key tiles per wave is the smallest (narrowest
+// chunks, most workgroups busy) whose items all fit one round of the grid, the
+// widest when none does; items are non-increasing in the cap, and
+// items(k) >= (sum of nrg * cols) / (16 wph k), so the search starts at that
+// bound and tries four caps per round. Items go in the order (b, l, row group,
+// chunk); workgroup me takes items me, me + P, ... Writes the items of this
+// workgroup to item[] ((b * L + l) << 16 | index in the (layer, sample)),
+// hdr[0] = cap and hdr[1] = item count. red: 4 * kFusedWaves ints of LDS.
+__device__ __forceinline__ void fused_schedule(const Shape &sh, const int *ntk_lds, int me, int P, int *item,
+                                               int *hdr, int *red) {
+  constexpr int NW = kFusedWaves, C = 4;
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
   const int L = sh.L, B = sh.B, Nv = sh.Nv, LB = L * B;
-  const int wph = kFusedWaves / sh.Hkv;
-  const int per = (LB + 63) / 64;
-  for (int b = lane; b < B; b += 64) ctarget[b] = 0;
-  int ntk[8];  // per <= 8: L * B <= 512
+  const int wph = kFusedWaves / sh.Hkv, W0 = wph * 16;
+  const bool ok = tid < LB;  // LB <= kFusedThreads
+  const int b = ceil_div_small(tid + 1, L) - 1, l = tid - b * L;
+  const int t = ok ? ntk_lds[l * B + b] : 0;
+  const int rows = sh.G * t;
+  const int rtg = rows > 0 ? (rows + 15) >> 4 : 1;
+  const int nrg = ok ? (rtg + kFusedRtMax - 1) / kFusedRtMax : 0;
+  const int km = fused_ktmax(rtg < kFusedRtMax ? rtg : kFusedRtMax);
+  const int cols = Nv + t;
+  auto chunks = [&](int kc) {
+    const int k = kc < km ? kc : km;
+    return ceil_div_small(cols, W0 * (k < 1 ? 1 : k));
+  };
+  // block sums of C values: per wave, then over the waves in order
+  auto block_sums = [&](const int (&v)[C], int (&out)[C]) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int s = lane * per + j;
-    ntk[j] = (j < per && s < LB) ? ntk_of[j] : 0;
-  }
+    for (int c = 0; c < C; ++c) {
+      const int x = wave_sum_i(v[c]);
+      if (lane == 0) red[c * NW + wave] = x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      int x = 0;
+      for (int w = 0; w < NW; ++w) x += red[c * NW + w];
+      out[c] = x;
+    }
+    __syncthreads();
+  };
   const int P_sched = P < kFusedTargetCus ? P : kFusedTargetCus;
-  int lo_k = fused_kcap_min(L, B, Nv, wph), hi_k = kFusedSlots;
-  while (lo_k < hi_k) {
-    const int mid = (lo_k + hi_k) >> 1;
-    int n = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < per && lane * per + j < LB) {
-        const ChunkPlan cp = fused_chunk_plan(ntk[j], sh.G, Nv, wph, mid);
-        n += cp.nrg * cp.nchunks;
-      }
-    if (wave_sum_i(n) <= P_sched) hi_k = mid;
-    else lo_k = mid + 1;
+  int k0;
+  {
+    int v[C] = {nrg * cols, 0, 0, 0}, o[C];
+    block_sums(v, o);
+    const int kb = (int)ceilf((float)o[0] / ((float)W0 * (float)P_sched)) - 1;  // -1: float rounding
+    k0 = max(fused_kcap_min(L, B, Nv, wph), min(kb, kFusedSlots));
   }
-  const int kc = lo_k;
-  int nit[8], nch[8], tot = 0;
+  int kc = kFusedSlots;
+  for (; k0 < kFusedSlots; k0 += C) {
+    int v[C], o[C];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    nit[j] = nch[j] = 0;
-    if (j < per && lane * per + j < LB) {
-      const ChunkPlan cp = fused_chunk_plan(ntk[j], sh.G, Nv, wph, kc);
-      nch[j] = cp.nchunks;
-      nit[j] = cp.nrg * cp.nchunks;
-    }
-    tot += nit[j];
-  }
-  const int incl = wave_incl_scan(tot);
-  int start = incl - tot;
+    for (int c = 0; c < C; ++c) v[c] = (k0 + c <= kFusedSlots) ? nrg * chunks(k0 + c) : 0;
+    block_sums(v, o);
+    int found = -1;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int s = lane * per + j;
-    if (j < per && s < LB) {
-      atomicAdd(&ctarget[s / L], nch[j]);
-      int first = me - start;  // first item index >= start congruent to me mod P
-      first = start + ((first % P) + P) % P;
-      for (int i = first; i < start + nit[j]; i += P) {
-        const int k = (i - me) / P;
-        if (k < kFusedMaxItems) item[k] = (s << 16) | (i - start);
-      }
-      start += nit[j];
+    for (int c = C - 1; c >= 0; --c)
+      if (k0 + c <= kFusedSlots && o[c] <= P_sched) found = k0 + c;
+    if (found >= 0) {
+      kc = found;
+      break;
     }
   }
-  if (lane == 63) {
+  const int nch = nrg > 0 ? chunks(kc) : 0;
+  const int nit = nrg * nch;
+  int total;
+  const int start = fused_block_scan(nit, red, &total);
+  if (nit > 0) {
+    // first item index >= start congruent to me mod P, and its slot k
+    const int d = start - me;
+    int k = d <= 0 ? 0 : ceil_div_small(d, P);
+    for (int i = me + k * P; i < start + nit; i += P, ++k)
+      if (k < kFusedMaxItems) item[k] = (tid << 16) | (i - start);
+  }
+  if (tid == 0) {
     hdr[0] = kc;
-    hdr[1] = incl;  // items in all
+    hdr[1] = total;  // items in all
   }
+}
+
+// Statistics of one (layer, sample) from its chunks' moments, by wave 0:
+// lane c holds chunk c; the chunks combine pairwise in a fixed tree (at
+// stride st, chunk c, a multiple of 2 st, absorbs chunk c + st), so the
+// result does not depend on which workgroup computes it. s_t and s_k
+// ("Layer-wise KV Cache Budget Allocation", the s_t and s_k equations) go to
+// the plan and, tagged with the epoch, to the (layer, sample)'s record.
+__device__ __forceinline__ void fused_layer_stats(const Shape &sh, const PlanPtrs &plan, const FusedWs &fw, int plb,
+                                                  int nch, unsigned epoch) {
+  const int lane = threadIdx.x & 63;
+  const auto rm = coherent_rsrc(fw.mom + (size_t)plb * fw.max_chunks * 4, (unsigned)(fw.max_chunks * 32));
+  double v[4] = {0.0, 0.0, 0.0, 0.0};
+  if (lane < nch)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) v[f] = load_sc1_d(rm, (unsigned)(lane * 32 + 8 * f));
+  double sum = v[0];
+  Moments m{v[3], v[3] > 0.0 ? v[0] / v[3] : 0.0, v[1], v[2]};
+  for (int st = 1; st < nch; st <<= 1) {
+    const int src = lane + st;
+    const double osum = __shfl(sum, src), on = __shfl(m.n, src), omean = __shfl(m.mean, src);
+    const double om2 = __shfl(m.m2, src), om3 = __shfl(m.m3, src);
+    if ((lane & (2 * st - 1)) == 0 && src < nch) {
+      m = combine_moments(m, Moments{on, omean, om2, om3});
+      sum = sum + osum;
+    }
+  }
+  if (lane == 0) {
+    const int Nv = sh.Nv;
+    const double sigma = sqrt(m.m2 / (double)(Nv - 1));
+    const double sk = (sigma > 0.0) ? (m.m3 / (sigma * sigma * sigma)) *
+                                          ((double)Nv / ((double)(Nv - 1) * (double)(Nv - 2)))
+                                    : 0.0;
+    plan.s_t[plb] = sum;
+    plan.s_k[plb] = sk;
+    // each 32-bit half of s_t and s_k in its own word with the epoch: a
+    // reader that sees the epoch in all four words has the values, with no
+    // ordering between the stores needed
+    uint64_t *r = fw.srec + (size_t)plb * 4;
+    const uint64_t a = __builtin_bit_cast(uint64_t, sum), c = __builtin_bit_cast(uint64_t, sk);
+    const uint64_t tag = (uint64_t)epoch << 32;
+    const uint64_t lo32 = 0xffffffffu;
+    store_coherent(r + 0, tag | (a & lo32));
+    store_coherent(r + 1, tag | (a >> 32));
+    store_coherent(r + 2, tag | (c & lo32));
+    store_coherent(r + 3, tag | (c >> 32));
+  }
+}
+
+// budget_sums over LDS with the values read eight at a time ahead of the
+// additions and no branches: the same additions and comparisons in the same
+// order, so the same result (a padded entry adds +0.0 to a non-negative sum,
+// or keeps the minimum).
+__device__ __forceinline__ BudgetSums budget_sums_lds(int L, const double *st, const double *sk) {
+#pragma clang fp contract(off)
+  BudgetSums r{0.0, 0.0, 0.0};
+  for (int l0 = 0; l0 < L; l0 += 8) {
+    double a[8], c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      a[j] = st[l0 + j];
+      c[j] = sk[l0 + j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool in = l0 + j < L;
+      r.st_sum += in ? a[j] : 0.0;
+      r.mshift = (in && c[j] < r.mshift) ? c[j] : r.mshift;
+    }
+  }
+  for (int l0 = 0; l0 < L; l0 += 8) {
+    double c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = sk[l0 + j];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r.u_sum += (l0 + j < L) ? c[j] - r.mshift : 0.0;
+  }
+  return r;
+}
+
+// Budget of (layer l, sample b) for its top-k, block-wide: waits for the
+// statistics records of every layer of samples 0..b, then (wave 0, lane bb
+// for sample bb) the budgets of layer l of those samples ("Layer-wise KV
+// Cache Budget Allocation", the r_hat equation, over the sample's layers in
+// order); writes the plan's budget, budget_x and out_off of (l, b) (and the
+// layer's total after the last sample) and returns the budget.
+// sts: LDS for 2 * (L * (b + 1) + 8) doubles.
+__device__ __forceinline__ int fused_budget(const Shape &sh, const PlanPtrs &plan, const FusedWs &fw, int l, int b,
+                                            unsigned epoch, double *sts, int *bc) {
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int L = sh.L, B = sh.B;
+  const int nrec = L * (b + 1);
+  double *st = sts, *sk = sts + nrec + 8;  // [bb][l]
+  // one resource for all records (a per-lane resource would cost a loop over
+  // the distinct values of the wave)
+  const auto rr = coherent_rsrc(fw.srec, (unsigned)((size_t)L * B * 32));
+  for (int i = tid; i < nrec; i += kFusedThreads) {
+    const int bb = ceil_div_small(i + 1, L) - 1, ll = i - bb * L;
+    const int off = (int)(((size_t)ll * B + bb) * 32);
+    uint64_t w[4];
+    unsigned spins = 0;
+    for (;;) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rr, off + 8 * j, 0, 16));
+      bool ok = true;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ok = ok && (unsigned)(w[j] >> 32) == epoch;
+      if (ok || spin_expired(spins, plan.status)) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    const uint64_t lo32 = 0xffffffffu;
+    st[i] = __builtin_bit_cast(double, (w[0] & lo32) | (w[1] << 32));
+    sk[i] = __builtin_bit_cast(double, (w[2] & lo32) | (w[3] << 32));
+  }
+  __syncthreads();
+  if (wave == 0) {
+    double off = 0.0;  // element offsets, exact in double (below 2^53)
+    for (int bb = lane; bb <= b; bb += 64) {
+      const BudgetSums sums = budget_sums_lds(L, st + (size_t)bb * L, sk + (size_t)bb * L);
+      double x;
+      int bud;
+      layer_budget(sh, sums, st[(size_t)bb * L + l], sk[(size_t)bb * L + l], &x, &bud);
+      const double seg = (double)sh.Hkv * (double)(bud + sh.Nt) * (double)sh.D;
+      if (bb < b) off += seg;
+      else {
+        const int plb = l * B + b;
+        plan.budget[plb] = bud;
+        if (plan.bx) plan.bx[plb] = x;
+        bc[0] = bud;
+        bc[1] = (int)seg;  // below 2^31: one layer's segment of one sample
+      }
+    }
+    off = wave_sum_d(off);
+    if (lane == 0) {
+      plan.out_off[(size_t)l * (B + 1) + b] = (int64_t)off;
+      if (b == B - 1) plan.out_off[(size_t)l * (B + 1) + B] = (int64_t)off + (int64_t)bc[1];
+    }
+  }
+  __syncthreads();
+  return uniform(bc[0]);
 }
 
 template <typename Tag, int D>
@@ -852,72 +1141,45 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
                                                                           PlanPtrs plan, FusedWs fw, FusedLds lo) {
   extern __shared__ __attribute__((aligned(16))) float lds_f[];
   unsigned char *lds = reinterpret_cast<unsigned char *>(lds_f);
-  __shared__ int wtot[kFusedWaves];
+  __shared__ int wtot[4 * kFusedWaves];
   __shared__ double redd[kFusedWaves];
-  __shared__ double lst[AIRCACHE_MAX_LAYERS], lsk[AIRCACHE_MAX_LAYERS];
-  __shared__ BudgetSums sums;
   __shared__ int bcast[4];
+  __shared__ int hdr[2];
   const int tid = threadIdx.x;
-  const int L = sh.L, B = sh.B, Nv = sh.Nv;
+  const int L = sh.L, B = sh.B, Nv = sh.Nv, LB = L * B;
   const int wph = kFusedWaves / sh.Hkv;
+  const int ntw = fused_words64(sh.Nt);
   const unsigned e0 = *fw.epoch;
   const unsigned epoch = e0 + 1u;  // tag of every record this call writes
   const int P = gridDim.x, me = blockIdx.x;
-  int *ctarget = reinterpret_cast<int *>(lds + lo.ctarget);
   int *item_list = reinterpret_cast<int *>(lds + lo.items);
-  __shared__ float redf[kFusedWaves];
-  __shared__ int hdr[2];
-  auto elite_count = [&](int plb) {  // written in this call: a coherent load
-    const int t = load_coherent(&plan.n_elite[plb]);
-    return t < 0 ? 0 : (t > sh.cap ? sh.cap : t);
-  };
+  int *owed = reinterpret_cast<int *>(lds + lo.owed);
+  int *ntk_l = reinterpret_cast<int *>(lds + lo.ntk);
+  unsigned long long *emask = reinterpret_cast<unsigned long long *>(lds + lo.emask);
 
-  // Phase 0: elite sets. Items (layer, sample, KV head) me, me + P, ...; the
-  // last part of a (layer, sample) (a counter election) merges the parts and
-  // counts the set in edone once it is published. The status word is cleared
-  // before workgroup 0 finishes its first item, so every later status bit is
+  // Phase 0: the KV-head parts of pbar, items (layer, sample, KV head) me,
+  // me + P, ...; each is counted in edone once written. The status word is
+  // cleared before workgroup 0's first count, so every later status bit is
   // set after the clear.
   if (me == 0 && tid == 0) store_coherent(plan.status, 0);
-  for (int t = me; t < L * B * sh.Hkv; t += P) {
+  for (int t = me; t < LB * sh.Hkv; t += P) {
     const int lb = t / sh.Hkv, g = t - lb * sh.Hkv;
     fused_elite_part<Tag, D>(sh, qt, kt, lb, g, fw.parts + (size_t)t * sh.Nt, lds_f);
     wait_all_memory();
     __syncthreads();
-    if (tid == 0) {
-      const bool last = counter_add(&fw.cnt_elite[lb], 1u) == (unsigned)sh.Hkv - 1u;
-      if (last) store_coherent(&fw.cnt_elite[lb], 0u);  // reset for the next call
-      bcast[3] = last;
-    }
-    __syncthreads();
-    if (uniform(bcast[3])) {
-      fused_elite_merge(sh, plan, fw.parts + (size_t)lb * sh.Hkv * sh.Nt, lb, lds_f, wtot, redf);
-      wait_all_memory();
-      __syncthreads();
-      if (tid == 0) counter_add(fw.edone, 1u);
-    }
+    if (tid == 0) counter_add(fw.edone, 1u);
     __syncthreads();  // the LDS is free again
   }
-  // Wave 0: wait until every elite set is out (one lane polls one word, with
-  // sleeps, so the waiting workgroups load the memory system little), then
-  // this workgroup's schedule. edone is reset by the call's last workgroup.
-  if (tid < 64) {
-    const int lane = tid, LB = L * B, per = (LB + 63) / 64;
-    if (lane == 0) {
-      unsigned spins = 0;
-      while (load_coherent(fw.edone) < (unsigned)LB) {
-        if (spin_expired(spins, plan.status)) break;
-        __builtin_amdgcn_s_sleep(10);
-      }
+  if (tid == 0) {
+    unsigned spins = 0;
+    while (load_coherent(fw.edone) < (unsigned)(LB * sh.Hkv)) {
+      if (spin_expired(spins, plan.status)) break;
+      __builtin_amdgcn_s_sleep(2);
     }
-    __builtin_amdgcn_wave_barrier();
-    int ntk[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int s = lane * per + j;
-      ntk[j] = (j < per && s < LB) ? elite_count((s % L) * B + s / L) : 0;
-    }
-    fused_schedule(sh, ntk, me, P, item_list, ctarget, hdr);
   }
+  __syncthreads();
+  fused_elite_sets(sh, plan, fw.parts, me, P, lds_f + lo.ring / 4, (lo.el - lo.ring) / 4, ntk_l, emask);
+  fused_schedule(sh, ntk_l, me, P, item_list, hdr, wtot);
   __syncthreads();
   const int kcap = uniform(hdr[0]);
   const int run = uniform(hdr[1]);
@@ -926,16 +1188,17 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
     if (tid == 0) atomicOr(plan.status, AIRCACHE_DEV_TIMEOUT);
     nmine = kFusedMaxItems;
   }
+  int nowed = 0;
 
   for (int k = 0; k < nmine; ++k) {
-    const int tid = opaque_tid();
+    const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
     FusedItem it;
     const int item = uniform(item_list[k]);
     const int s = item >> 16;
     it.b = s / L;
     it.l = s - it.b * L;
     it.plb = it.l * B + it.b;
-    it.ntk = uniform(elite_count(it.plb));
+    it.ntk = uniform(ntk_l[it.plb]);
     it.cp = fused_chunk_plan(it.ntk, sh.G, Nv, wph, kcap);
     const int local = item & 0xffff;
     it.r = local / it.cp.nchunks;
@@ -944,7 +1207,14 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
     it.k = kt.p[it.l];
     int *el = reinterpret_cast<int *>(lds + lo.el);
     __syncthreads();  // the previous item is done with the LDS
-    for (int i = tid; i < it.ntk; i += kFusedThreads) el[i] = load_coherent(&plan.elite[(size_t)it.plb * sh.Nt + i]);
+    // elite list of the item's (layer, sample) from its bit mask, ascending
+    for (int w = wave; w < ntw; w += kFusedWaves) {
+      int base = 0;
+      for (int u = 0; u < w; ++u) base += __popcll(emask[(size_t)it.plb * ntw + u]);
+      const unsigned long long mk = emask[(size_t)it.plb * ntw + w];
+      const int pos = base + __popcll(mk & ((1ull << lane) - 1ull));
+      if (((mk >> lane) & 1ull) && pos < it.ntk) el[pos] = w * 64 + lane;
+    }
     __syncthreads();
     {
       const int rt0 = it.r * kFusedRtMax, left = it.cp.rtg - rt0;
@@ -953,7 +1223,6 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
       else if (left == 2) fused_pass<Tag, D, 2>(sh, fw, it, rt0, lds, lo, epoch, plan.status, true);
       else fused_pass<Tag, D, 1>(sh, fw, it, rt0, lds, lo, epoch, plan.status, true);
     }
-
     // Column sums of this item's rows over the KV heads (in order); with one
     // row group they are the chunk's I_v * H_q * N_tk, else the last row group
     // of the chunk adds every group's sums in order.
@@ -1033,125 +1302,53 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
     wait_all_memory();
     __syncthreads();
     if (tid == 0) {
-      const bool last = counter_add(&fw.cnt_b[it.b], 1u) == (unsigned)ctarget[it.b] - 1u;
-      if (last) store_coherent(&fw.cnt_b[it.b], 0u);  // reset for the next call
+      const bool last = counter_add(&fw.cnt_lbc[it.plb], 1u) == (unsigned)it.cp.nchunks - 1u;
+      if (last) {
+        store_coherent(&fw.cnt_lbc[it.plb], 0u);  // reset for the next call
+        owed[nowed] = it.plb;
+      }
       bcast[0] = last;
     }
     __syncthreads();
-    if (!uniform(bcast[0])) continue;
-
-    // Last chunk of sample b: per-layer statistics from the chunks' moments
-    // (pairwise combination in a fixed tree order), then the sample's budgets.
-    const int b = it.b;
-    const int mc = fw.max_chunks;
-    double *momc = reinterpret_cast<double *>(lds + lo.ring);  // [L][mc][5]
-    {
-      const auto rm = coherent_rsrc(fw.mom, (unsigned)((size_t)L * B * mc * 32));
-      for (int i = tid; i < L * mc; i += kFusedThreads) {
-        const int l = i / mc, cc = i - l * mc, plb = l * B + b;
-        const int nch = fused_chunk_plan(elite_count(plb), sh.G, Nv, wph, kcap).nchunks;
-        double v[4] = {0.0, 0.0, 0.0, 0.0};
-        if (cc < nch) {
-          const unsigned off = (unsigned)(((size_t)plb * mc + cc) * 32);
-#pragma unroll
-          for (int f = 0; f < 4; ++f) v[f] = load_sc1_d(rm, off + 8u * f);
-        }
-        // LDS slots: 0 sum, 1 count, 2 mean, 3 M2, 4 M3
-        double *m = momc + (size_t)i * 5;
-        m[0] = v[0];
-        m[1] = v[3];
-        m[2] = v[3] > 0.0 ? v[0] / v[3] : 0.0;
-        m[3] = v[1];
-        m[4] = v[2];
-      }
-    }
-    __syncthreads();
-    // tree: at stride st, chunk cc (a multiple of 2 st) absorbs chunk cc + st
-    for (int st = 1; st < mc; st <<= 1) {
-      for (int i = tid; i < L * mc; i += kFusedThreads) {
-        const int l = i / mc, cc = i - l * mc;
-        if ((cc & (2 * st - 1)) == 0 && cc + st < mc) {
-          double *a = momc + (size_t)i * 5, *bb = momc + (size_t)(i + st) * 5;
-          const Moments m = combine_moments(Moments{a[1], a[2], a[3], a[4]}, Moments{bb[1], bb[2], bb[3], bb[4]});
-          a[0] = a[0] + bb[0];
-          a[1] = m.n;
-          a[2] = m.mean;
-          a[3] = m.m2;
-          a[4] = m.m3;
-        }
-        (void)l;
-      }
-      __syncthreads();
-    }
-    if (tid < L) {
-      const int l = tid, plb = l * B + b;
-      const double *a = momc + (size_t)l * mc * 5;
-      const double st = a[0], M2 = a[3], M3 = a[4];
-      const double sigma = sqrt(M2 / (double)(Nv - 1));
-      const double sk = (sigma > 0.0) ? (M3 / (sigma * sigma * sigma)) *
-                                            ((double)Nv / ((double)(Nv - 1) * (double)(Nv - 2)))
-                                      : 0.0;
-      plan.s_t[plb] = st;
-      plan.s_k[plb] = sk;
-      lst[l] = st;
-      lsk[l] = sk;
-    }
-    __syncthreads();
-    if (tid == 0) sums = budget_sums(L, lst, lsk);
-    __syncthreads();
-    if (tid < L) {
-      const int plb = tid * B + b;
-      double x;
-      int bud;
-      layer_budget(sh, sums, lst[tid], lsk[tid], &x, &bud);
-      if (plan.bx) plan.bx[plb] = x;
-      plan.budget[plb] = bud;
-      store_coherent(&fw.brec[plb], ((uint64_t)epoch << 32) | (uint64_t)(unsigned)bud);
-    }
+    if (uniform(bcast[0])) ++nowed;
   }
 
-  // Top-k tasks, in sample-major order, handed out by ticket.
-  unsigned *cnt = reinterpret_cast<unsigned *>(lds + lo.ring);
+  // Owed (layer, sample) pairs: first every statistics record (a top-k waits
+  // for records of other pairs, possibly this workgroup's own), then the
+  // top-k tasks with their budgets.
+  for (int o = 0; o < nowed; ++o) {
+    const int plb = uniform(owed[o]);
+    if (threadIdx.x < 64) {
+      const int nch = fused_chunk_plan(ntk_l[plb], sh.G, Nv, wph, kcap).nchunks;
+      fused_layer_stats(sh, plan, fw, plb, nch, epoch);
+    }
+  }
+  unsigned *hist = reinterpret_cast<unsigned *>(lds + lo.ring);
   {
     const int tid = opaque_tid();
     __syncthreads();  // every wave is done with the item LDS
-    for (int i = tid; i < kTopkBuckets; i += kFusedThreads) cnt[i] = 0u;
+    for (int i = tid; i < kTopkBuckets; i += kFusedThreads) hist[i] = 0u;
   }
-  for (;;) {
-    const int tid = opaque_tid();
+  for (int o = 0; o < nowed; ++o) {
     __syncthreads();
-    if (tid == 0) {
-      const unsigned t = counter_add(fw.ticket, 1u);
-      // every workgroup takes exactly one ticket past the tasks: the last one
-      // ends the call (counter reset, epoch advanced)
-      if (t == (unsigned)(L * B + P - 1)) {
-        store_coherent(fw.ticket, 0u);
-        store_coherent(fw.edone, 0u);
-        store_coherent(fw.epoch, epoch);
-      }
-      bcast[1] = (int)t;
-    }
-    __syncthreads();
-    const int task = uniform(bcast[1]);
-    if (task >= L * B) break;
-    const int b = task / L, l = task - b * L, plb = l * B + b;
-    if (tid == 0) {
-      bcast[2] = fused_wait_budget(fw, plb, epoch, plan.status);
-      int64_t off = 0;
-      for (int bb = 0; bb < b; ++bb)
-        off += (int64_t)sh.Hkv * (fused_wait_budget(fw, l * B + bb, epoch, plan.status) + sh.Nt) * sh.D;
-      plan.out_off[(size_t)l * (B + 1) + b] = off;
-      if (b == B - 1) plan.out_off[(size_t)l * (B + 1) + B] = off + (int64_t)sh.Hkv * (bcast[2] + sh.Nt) * sh.D;
-      if (load_coherent(&plan.n_elite[plb]) > sh.cap) atomicOr(plan.status, AIRCACHE_DEV_ELITE_OVERFLOW);
-    }
-    __syncthreads();
-    int kbud = uniform(bcast[2]);
-    if (kbud < 0) kbud = 0;
-    if (kbud > Nv) kbud = Nv;
+    const int plb = uniform(owed[o]);
+    const int l = plb / B, b = plb - l * B;
     const float *ivl = plan.iv + (size_t)plb * Nv;
     int32_t *kp = plan.kept + (size_t)plb * Nv;
-    if (Nv <= 2048) block_topk<4>(sh, ivl, kbud, kp, cnt);
-    else if (Nv <= 4096) block_topk<8>(sh, ivl, kbud, kp, cnt);
-    else block_topk<16>(sh, ivl, kbud, kp, cnt);
+    double *sts = reinterpret_cast<double *>(lds + lo.sts);
+    auto budget = [&]() { return fused_budget(sh, plan, fw, l, b, epoch, sts, bcast); };
+    if (Nv <= 2048) block_topk<4>(sh, ivl, kp, hist, budget);
+    else if (Nv <= 4096) block_topk<8>(sh, ivl, kp, hist, budget);
+    else block_topk<16>(sh, ivl, kp, hist, budget);
+  }
+
+  // The last workgroup to finish ends the call: counters reset, epoch advanced.
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (counter_add(fw.exitc, 1u) == (unsigned)P - 1u) {
+      store_coherent(fw.exitc, 0u);
+      store_coherent(fw.edone, 0u);
+      store_coherent(fw.epoch, epoch);
+    }
   }
 }
