@@ -153,6 +153,12 @@ int64_t aircache_max_compacted_elems(const aircache_desc *desc);
  * Host only; no device work. */
 int32_t aircache_resolved_path(const aircache_desc *desc);
 
+/* Kernel launches aircache_run makes for this descriptor: 1 when the chunked
+ * path compacts inside its launch, more when aircache_run falls back to
+ * aircache_plan then aircache_compress; -1 for an invalid descriptor. Host
+ * only; no device work. */
+int32_t aircache_run_launches(const aircache_desc *desc);
+
 /* Scores, statistics, budgets and top-k selection for all layers.
  *   q_txt, k : host arrays of n_layers device pointers (layout above)
  *   plan     : output buffers (see aircache_plan_buf)
@@ -177,21 +183,42 @@ int aircache_compress(const aircache_desc *desc, const aircache_plan_buf *plan,
                       const void *const *k, const void *const *v, void *const *k_out,
                       void *const *v_out, void *stream);
 
-/* Instrumented variants of aircache_plan / aircache_compress for timing
- * individual kernels. events is a host array of hipEvent_t handles created by
+/* The whole pass in one call: aircache_plan then aircache_compress, with the
+ * same arguments, results and checks as the two calls on the same stream.
+ * Where the chunked path serves the descriptor (aircache_resolved_path) and
+ * 5 * n_layers <= 256, one launch does both: the compaction of a (layer,
+ * sample) starts as soon as its top-k is out, on workgroups that have
+ * finished their scoring work, instead of in a second kernel after the last
+ * top-k. Otherwise the two calls are made in order.
+ *   q_txt, k, v : host arrays of n_layers device pointers (inputs, read-only)
+ *   plan        : output buffers (see aircache_plan_buf), all filled
+ *   k_out, v_out: compacted outputs as for aircache_compress
+ *   workspace   : as for aircache_plan */
+int aircache_run(const aircache_desc *desc, const void *const *q_txt, const void *const *k, const void *const *v,
+                 const aircache_plan_buf *plan, void *const *k_out, void *const *v_out, void *workspace,
+                 size_t ws_bytes, void *stream);
+
+/* Instrumented variants of aircache_plan / aircache_compress / aircache_run for
+ * timing individual kernels. events is a host array of hipEvent_t handles created by
  * the caller: events[i] is recorded on the stream just before the i-th kernel
  * of the call and events[n_events - 1] after the last one. n_events must be
  * AIRCACHE_PLAN_KERNELS + 1 (kernels: elite_select, cross_score, finalize,
- * topk_select) or AIRCACHE_COMPRESS_KERNELS + 1 (kernel: kv_gather); NULL
- * events gives the plain call. Results are identical to the plain calls. */
+ * topk_select), AIRCACHE_COMPRESS_KERNELS + 1 (kernel: kv_gather) or
+ * AIRCACHE_RUN_KERNELS + 1 (the whole pass); NULL events gives the plain call.
+ * Results are identical to the plain calls. */
 #define AIRCACHE_PLAN_KERNELS 4
 #define AIRCACHE_COMPRESS_KERNELS 1
+#define AIRCACHE_RUN_KERNELS 1 /* aircache_run_profiled: events bracket the whole pass */
 int aircache_plan_profiled(const aircache_desc *desc, const void *const *q_txt, const void *const *k,
                            const aircache_plan_buf *plan, void *workspace, size_t ws_bytes, void *stream,
                            void *const *events, int n_events);
 int aircache_compress_profiled(const aircache_desc *desc, const aircache_plan_buf *plan,
                                const void *const *k, const void *const *v, void *const *k_out,
                                void *const *v_out, void *stream, void *const *events, int n_events);
+int aircache_run_profiled(const aircache_desc *desc, const void *const *q_txt, const void *const *k,
+                          const void *const *v, const aircache_plan_buf *plan, void *const *k_out,
+                          void *const *v_out, void *workspace, size_t ws_bytes, void *stream,
+                          void *const *events, int n_events);
 
 /* Text of an aircache_status value. */
 const char *aircache_strerror(int status);

@@ -19,11 +19,12 @@ PATH_AUTO, PATH_TILED, PATH_ROWS, PATH_CHUNKED = 0, 1, 2, 3
 MAX_LAYERS = 128
 
 EXPORTS = ["aircache_abi_version", "aircache_workspace_size", "aircache_max_compacted_elems",
-           "aircache_resolved_path",
-           "aircache_plan", "aircache_compress", "aircache_plan_profiled", "aircache_compress_profiled",
-           "aircache_strerror", "aircache_last_error"]
+           "aircache_resolved_path", "aircache_run_launches",
+           "aircache_plan", "aircache_compress", "aircache_run", "aircache_plan_profiled",
+           "aircache_compress_profiled", "aircache_run_profiled", "aircache_strerror", "aircache_last_error"]
 PLAN_KERNELS = ["elite_select", "cross_score", "finalize", "topk_select"]
 COMPRESS_KERNELS = ["kv_gather"]
+RUN_KERNELS = ["aircache_pass"]
 
 
 class Desc(C.Structure):
@@ -63,6 +64,8 @@ def load() -> C.CDLL:
         lib.aircache_max_compacted_elems.argtypes = [C.POINTER(Desc)]
         lib.aircache_resolved_path.restype = C.c_int32
         lib.aircache_resolved_path.argtypes = [C.POINTER(Desc)]
+        lib.aircache_run_launches.restype = C.c_int32
+        lib.aircache_run_launches.argtypes = [C.POINTER(Desc)]
         lib.aircache_plan.restype = C.c_int
         lib.aircache_plan.argtypes = [C.POINTER(Desc), P, P, C.POINTER(PlanBuf), P, C.c_size_t, P]
         lib.aircache_compress.restype = C.c_int
@@ -72,6 +75,11 @@ def load() -> C.CDLL:
                                                P, C.c_int]
         lib.aircache_compress_profiled.restype = C.c_int
         lib.aircache_compress_profiled.argtypes = [C.POINTER(Desc), C.POINTER(PlanBuf), P, P, P, P, P, P, C.c_int]
+        lib.aircache_run.restype = C.c_int
+        lib.aircache_run.argtypes = [C.POINTER(Desc), P, P, P, C.POINTER(PlanBuf), P, P, P, C.c_size_t, P]
+        lib.aircache_run_profiled.restype = C.c_int
+        lib.aircache_run_profiled.argtypes = [C.POINTER(Desc), P, P, P, C.POINTER(PlanBuf), P, P, P, C.c_size_t, P,
+                                              P, C.c_int]
         lib.aircache_strerror.restype = C.c_char_p
         lib.aircache_strerror.argtypes = [C.c_int]
         lib.aircache_last_error.restype = C.c_char_p
@@ -103,6 +111,10 @@ def resolved_path(desc: Desc) -> int:
     return int(load().aircache_resolved_path(C.byref(desc)))
 
 
+def run_launches(desc: Desc) -> int:
+    return int(load().aircache_run_launches(C.byref(desc)))
+
+
 def plan(desc: Desc, q_ptrs, k_ptrs, buf: PlanBuf, ws_ptr: int, ws_bytes: int, stream: int,
          events=None) -> int:
     q = ptr_array(q_ptrs) if q_ptrs is not None else None
@@ -112,6 +124,16 @@ def plan(desc: Desc, q_ptrs, k_ptrs, buf: PlanBuf, ws_ptr: int, ws_bytes: int, s
                                     C.c_void_p(stream))
     return load().aircache_plan_profiled(C.byref(desc), q, k, C.byref(buf), C.c_void_p(ws_ptr), ws_bytes,
                                          C.c_void_p(stream), ptr_array(events), len(events))
+
+
+def run(desc: Desc, q_ptrs, k_ptrs, v_ptrs, buf: PlanBuf, ko_ptrs, vo_ptrs, ws_ptr: int, ws_bytes: int,
+        stream: int, events=None) -> int:
+    q, k, v, ko, vo = [ptr_array(p) if p is not None else None for p in (q_ptrs, k_ptrs, v_ptrs, ko_ptrs, vo_ptrs)]
+    if events is None:
+        return load().aircache_run(C.byref(desc), q, k, v, C.byref(buf), ko, vo, C.c_void_p(ws_ptr), ws_bytes,
+                                   C.c_void_p(stream))
+    return load().aircache_run_profiled(C.byref(desc), q, k, v, C.byref(buf), ko, vo, C.c_void_p(ws_ptr), ws_bytes,
+                                        C.c_void_p(stream), ptr_array(events), len(events))
 
 
 def compress(desc: Desc, buf: PlanBuf, k_ptrs, v_ptrs, ko_ptrs, vo_ptrs, stream: int, events=None) -> int:

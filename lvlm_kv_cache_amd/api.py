@@ -87,6 +87,12 @@ class AirCache:
         return {_lib.PATH_TILED: "tiled", _lib.PATH_ROWS: "rows",
                 _lib.PATH_CHUNKED: "chunked"}[_lib.resolved_path(self.desc)]
 
+    @property
+    def run_launches(self) -> int:
+        """Kernel launches of run(): 1 when the chunked path compacts inside
+        its launch."""
+        return _lib.run_launches(self.desc)
+
     # -- validation ------------------------------------------------------
     def _check_layers(self, ts, shape, name):
         s = self.shape
@@ -132,6 +138,23 @@ class AirCache:
                              out.buf(), self.workspace.data_ptr(), self.ws_bytes, self._stream(stream),
                              events=None if events is None else [e.cuda_event for e in events]))
         return out
+
+    def run(self, q_txt, k, v, plan: PlanOutputs, k_out, v_out, stream=None, events=None) -> PlanOutputs:
+        """plan + compress in one call (one launch where the chunked path
+        serves the shape); events: optional list of 2 torch.cuda.Event
+        recorded around the whole pass."""
+        s = self.shape
+        self._check_layers(q_txt, (s["B"], s["Hq"], s["Nt"], s["D"]), "q_txt")
+        shp = (s["B"], s["Hkv"], s["Nv"] + s["Nt"], s["D"])
+        self._check_layers(k, shp, "k")
+        self._check_layers(v, shp, "v")
+        self._check_outputs(k_out, v_out)
+        _lib.check(_lib.run(self.desc, [t.data_ptr() for t in q_txt], [t.data_ptr() for t in k],
+                            [t.data_ptr() for t in v], plan.buf(), [t.data_ptr() for t in k_out],
+                            [t.data_ptr() for t in v_out], self.workspace.data_ptr(), self.ws_bytes,
+                            self._stream(stream),
+                            events=None if events is None else [e.cuda_event for e in events]))
+        return plan
 
     def bind(self, q_txt, k, v, plan: PlanOutputs, k_out, v_out, stream=None) -> "BoundPass":
         """A BoundPass running plan + compress on these tensors with the
@@ -212,7 +235,19 @@ class BoundPass:
         if rc:
             _lib.check(rc)
 
-    def __call__(self) -> PlanOutputs:
-        self.plan()
-        self.compress()
+    def run(self, events=None) -> PlanOutputs:
+        """plan + compress in one library call (aircache_run)."""
+        if events is None:
+            rc = self._lib.aircache_run(self._desc, self._q, self._k, self._v, self._pbuf, self._ko, self._vo,
+                                        self._ws, self._ws_bytes, self._st)
+        else:
+            ev = [e.cuda_event for e in events]
+            rc = self._lib.aircache_run_profiled(self._desc, self._q, self._k, self._v, self._pbuf, self._ko,
+                                                 self._vo, self._ws, self._ws_bytes, self._st, _lib.ptr_array(ev),
+                                                 len(ev))
+        if rc:
+            _lib.check(rc)
         return self.plan_out
+
+    def __call__(self) -> PlanOutputs:
+        return self.run()

@@ -1091,7 +1091,9 @@ constexpr size_t kMaxLds = 160 * 1024;
 struct Config {
   Shape sh;
   size_t off_cnt, off_stats, off_e, off_part, ws_bytes;
-  size_t off_xrec, off_mom, off_srec, off_part_rg, off_cnt_chunk, off_cnt_lbc;
+  size_t off_xrec, off_mom, off_srec, off_part_rg, off_cnt_chunk, off_cnt_lbc, off_grec, off_parts64;
+  size_t tile_bytes;   // bytes of one 16-key tile
+  bool run_fused;      // aircache_run compacts inside the chunked launch
   size_t off_cnt_elite, off_pbar, off_sched;
   size_t elite_lds, score_lds, final_lds, rows_lds;
   int ktw;
@@ -1179,6 +1181,7 @@ int make_config(const aircache_desc *d, Config *cfg) {
   const long long rt_need = ((long long)s.G * s.cap + 15) / 16;
   cfg->rt_grid = (int)(rt_need < 1 ? 1 : rt_need);  // row tiles of a unit at most
   const size_t tile_bytes = (size_t)16 * s.D * (d->dtype == AIRCACHE_BF16 ? 2 : 4);
+  cfg->tile_bytes = tile_bytes;
   size_t ring = 131072 / (kRowsWaves * tile_bytes);
   if (ring > 4) ring = 4;
   cfg->rows_lds = (size_t)kRowsWaves * ring * tile_bytes + (size_t)s.cap * sizeof(int);
@@ -1228,11 +1231,15 @@ int make_config(const aircache_desc *d, Config *cfg) {
   if (d->path == AIRCACHE_PATH_TILED || d->path == AIRCACHE_PATH_ROWS) cfg->chunked = false;
   if (d->path == AIRCACHE_PATH_TILED || d->path == AIRCACHE_PATH_CHUNKED) cfg->rows_kt = 0;
   cfg->path = cfg->chunked ? AIRCACHE_PATH_CHUNKED : cfg->rows_kt ? AIRCACHE_PATH_ROWS : AIRCACHE_PATH_TILED;
+  // aircache_run compacts inside the chunked launch when the five pointer
+  // tables fit its table and the kept indices of a pair fit the ring
+  cfg->run_fused = cfg->chunked && 5 * s.L <= kFusedTableSlots &&
+                   (size_t)s.Nv * sizeof(int) <= (size_t)(cfg->flds.el - cfg->flds.ring);
   cfg->off_cnt = kEpochBytes;
   cfg->off_cnt_elite = cfg->off_cnt + align_up(n_cnt * sizeof(unsigned));
   cfg->off_pbar = cfg->off_cnt_elite + align_up((size_t)s.L * s.B * sizeof(unsigned));
   cfg->off_sched = cfg->off_pbar + align_up((size_t)s.L * s.B * s.Hkv * s.Nt * sizeof(float));
-  // part and exit counters of the chunked path
+  // exit and compaction-ticket counters of the chunked path
   const size_t eflags = cfg->chunked ? align_up(2 * sizeof(unsigned)) : 0;
   cfg->off_stats = cfg->off_sched + eflags;
   cfg->off_xrec = cfg->off_mom = cfg->off_srec = cfg->off_stats;
@@ -1244,7 +1251,9 @@ int make_config(const aircache_desc *d, Config *cfg) {
     cfg->off_srec = cfg->off_mom + align_up(lbs * (size_t)cfg->max_chunks * 32);
     cfg->off_cnt_chunk = cfg->off_srec + align_up(lbs * 32);
     cfg->off_cnt_lbc = cfg->off_cnt_chunk + align_up(lbs * (size_t)cfg->max_chunks * sizeof(unsigned));
-    cfg->off_part_rg = cfg->off_cnt_lbc + align_up(lbs * sizeof(unsigned));
+    cfg->off_grec = cfg->off_cnt_lbc + align_up(lbs * sizeof(unsigned));
+    cfg->off_parts64 = cfg->off_grec + align_up(lbs * 32);
+    cfg->off_part_rg = cfg->off_parts64 + align_up(lbs * (size_t)s.Hkv * s.Nt * sizeof(uint64_t));
     // row-group partial sums only when some elite count can need two row groups
     const size_t part_rg = cfg->max_rg > 1 ? lbs * (size_t)cfg->max_chunks * cfg->max_rg * cfg->wmax * sizeof(float) : 0;
     cfg->ws_bytes = cfg->off_part_rg + align_up(part_rg);
@@ -1400,9 +1409,15 @@ template <typename Tag, int D> int fused_grid(const Config &cfg, int *grid) {
   return AIRCACHE_OK;
 }
 
+// Compaction outputs for a chunked launch that also compacts (NULL: plan only).
+struct RunOut {
+  const LayerTable *v;
+  const LayerTable *ko, *vo;
+};
+
 template <typename Tag, int D>
 int launch_chunked(const Config &cfg, const LayerTable &qt, const LayerTable &kt, const PlanPtrs &pp, const Ws &ws,
-                   void *ws_base, int grid, hipStream_t st) {
+                   void *ws_base, int grid, hipStream_t st, const RunOut *out) {
   const Shape &s = cfg.sh;
   auto kern = cross_score_fused_kernel<Tag, D>;
   const size_t lds = (size_t)cfg.flds.total;
@@ -1414,8 +1429,7 @@ int launch_chunked(const Config &cfg, const LayerTable &qt, const LayerTable &kt
   char *p = static_cast<char *>(ws_base);
   FusedWs fw;
   fw.epoch = ws.epoch;
-  fw.edone = reinterpret_cast<unsigned *>(p + cfg.off_sched);
-  fw.exitc = fw.edone + 1;
+  fw.exitc = reinterpret_cast<unsigned *>(p + cfg.off_sched);
   fw.xrec = reinterpret_cast<uint64_t *>(p + cfg.off_xrec);
   fw.mom = reinterpret_cast<double *>(p + cfg.off_mom);
   fw.srec = reinterpret_cast<uint64_t *>(p + cfg.off_srec);
@@ -1426,12 +1440,28 @@ int launch_chunked(const Config &cfg, const LayerTable &qt, const LayerTable &kt
   fw.wmax = cfg.wmax;
   fw.cnt_chunk = ws.cnt_chunk;
   fw.part = reinterpret_cast<float *>(p + cfg.off_part_rg);
-  fw.parts = ws.pbar_part;
+  fw.parts = reinterpret_cast<uint64_t *>(p + cfg.off_parts64);
+  fw.gticket = fw.exitc + 1;
+  fw.grec = reinterpret_cast<uint64_t *>(p + cfg.off_grec);
+  fw.gather = out ? 1 : 0;
+  fw.esize = (int)(cfg.tile_bytes / (16 * s.D));
+  fw.cap_elems = (int64_t)s.B * s.Hkv * (int64_t)s.S * s.D;
+  FusedTables tab;
+  memset(&tab, 0, sizeof(tab));
+  for (int l = 0; l < s.L; ++l) {
+    tab.p[l] = qt.p[l];
+    tab.p[s.L + l] = kt.p[l];
+    if (out) {
+      tab.p[2 * s.L + l] = out->v->p[l];
+      tab.p[3 * s.L + l] = out->ko->p[l];
+      tab.p[4 * s.L + l] = out->vo->p[l];
+    }
+  }
   // One workgroup per CU (the LDS use admits no second), so with the device
   // to itself every workgroup is resident at once, which the waits between
   // workgroups need; if other work holds CUs, the bounded waits report
   // AIRCACHE_DEV_TIMEOUT instead of hanging.
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kFusedThreads), lds, st, s, qt, kt, pp, fw, cfg.flds);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kFusedThreads), lds, st, s, tab, pp, fw, cfg.flds);
   return check_hip(hipGetLastError(), "cross_score_fused_kernel launch");
 }
 
@@ -1448,7 +1478,7 @@ int launch_plan(const Config &cfg, const LayerTable &qt, const LayerTable &kt, c
     if ((rc = fused_grid<Tag, D>(cfg, &fgrid))) return rc;
     if ((rc = mark(ev, 0, st))) return rc;
     if ((rc = mark(ev, 1, st))) return rc;
-    if ((rc = launch_chunked<Tag, D>(cfg, qt, kt, pp, ws, ws_base, fgrid, st))) return rc;
+    if ((rc = launch_chunked<Tag, D>(cfg, qt, kt, pp, ws, ws_base, fgrid, st, nullptr))) return rc;
     if ((rc = mark(ev, 2, st))) return rc;
     if ((rc = mark(ev, 3, st))) return rc;
     return mark(ev, 4, st);
@@ -1518,6 +1548,55 @@ int fill_table(const void *const *src, int L, LayerTable *t, const char *name) {
   return AIRCACHE_OK;
 }
 
+// Compaction tables with the layer-overlap checks of aircache_compress.
+int gather_tables(const Config &cfg, const void *const *k, const void *const *v, void *const *k_out,
+                  void *const *v_out, GatherTables *tb) {
+  const Shape &s = cfg.sh;
+  int rc;
+  if ((rc = fill_table(k, s.L, &tb->k, "k"))) return rc;
+  if ((rc = fill_table(v, s.L, &tb->v, "v"))) return rc;
+  LayerTable ko, vo;
+  if ((rc = fill_table(const_cast<const void *const *>(k_out), s.L, &ko, "k_out"))) return rc;
+  if ((rc = fill_table(const_cast<const void *const *>(v_out), s.L, &vo, "v_out"))) return rc;
+  const int esz = (int)(cfg.tile_bytes / (16 * s.D));
+  const size_t layer_in = (size_t)s.B * s.Hkv * s.S * s.D * esz;
+  const size_t layer_out_max = (size_t)s.B * s.Hkv * s.S * s.D * esz;
+  for (int l = 0; l < s.L; ++l) {
+    tb->ko.p[l] = const_cast<void *>(ko.p[l]);
+    tb->vo.p[l] = const_cast<void *>(vo.p[l]);
+    const char *o[2] = {static_cast<const char *>(ko.p[l]), static_cast<const char *>(vo.p[l])};
+    for (int a = 0; a < 2; ++a) {
+      for (int m = 0; m < s.L; ++m) {
+        const char *in[2] = {static_cast<const char *>(tb->k.p[m]), static_cast<const char *>(tb->v.p[m])};
+        for (int c = 0; c < 2; ++c)
+          if (o[a] < in[c] + layer_in && in[c] < o[a] + layer_out_max)
+            return fail(AIRCACHE_EINVAL, "an output buffer of layer %d may overlap input layer %d", l, m);
+      }
+    }
+  }
+  for (int l = s.L; l < AIRCACHE_MAX_LAYERS; ++l) tb->ko.p[l] = tb->vo.p[l] = nullptr;
+  return AIRCACHE_OK;
+}
+
+int launch_gather(const Config &cfg, const GatherTables &tb, const PlanPtrs &pp, hipStream_t st) {
+  const Shape &s = cfg.sh;
+  const int esz = (int)(cfg.tile_bytes / (16 * s.D));
+  const int units = s.L * s.B * s.Hkv;
+  int nch = (2048 + units - 1) / units;
+  if (nch > 64) nch = 64;
+  if (nch < 1) nch = 1;
+  const int rb = s.D * esz;
+  const int64_t cap = (int64_t)s.B * s.Hkv * s.S * s.D;
+  const dim3 grid((unsigned)(units * nch));
+  if (rb == 128)
+    hipLaunchKernelGGL(kv_gather_kernel<128>, grid, dim3(256), 0, st, s, tb, pp, nch, esz, cap);
+  else if (rb == 256)
+    hipLaunchKernelGGL(kv_gather_kernel<256>, grid, dim3(256), 0, st, s, tb, pp, nch, esz, cap);
+  else
+    hipLaunchKernelGGL(kv_gather_kernel<512>, grid, dim3(256), 0, st, s, tb, pp, nch, esz, cap);
+  return check_hip(hipGetLastError(), "kv_gather_kernel launch");
+}
+
 }  // namespace aircache
 
 using namespace aircache;
@@ -1543,6 +1622,14 @@ int32_t aircache_resolved_path(const aircache_desc *desc) {
   Config cfg;
   if (make_config(desc, &cfg) != AIRCACHE_OK) return -1;
   return cfg.path;
+}
+
+int32_t aircache_run_launches(const aircache_desc *desc) {
+  Config cfg;
+  if (make_config(desc, &cfg) != AIRCACHE_OK) return -1;
+  if (cfg.run_fused) return 1;
+  // aircache_plan's kernels, then kv_gather_kernel
+  return (cfg.chunked ? 1 : cfg.rows_kt ? 3 : 4) + 1;
 }
 
 int aircache_plan_profiled(const aircache_desc *desc, const void *const *q_txt, const void *const *k,
@@ -1587,48 +1674,73 @@ int aircache_compress_profiled(const aircache_desc *desc, const aircache_plan_bu
   int rc;
   if ((rc = make_config(desc, &cfg))) return rc;
   if ((rc = check_plan_buf(plan, true))) return rc;
-  const Shape &s = cfg.sh;
   GatherTables tb;
-  if ((rc = fill_table(k, s.L, &tb.k, "k"))) return rc;
-  if ((rc = fill_table(v, s.L, &tb.v, "v"))) return rc;
-  LayerTable ko, vo;
-  if ((rc = fill_table(const_cast<const void *const *>(k_out), s.L, &ko, "k_out"))) return rc;
-  if ((rc = fill_table(const_cast<const void *const *>(v_out), s.L, &vo, "v_out"))) return rc;
-  const int esz = desc->dtype == AIRCACHE_BF16 ? 2 : 4;
-  const size_t layer_in = (size_t)s.B * s.Hkv * s.S * s.D * esz;
-  const size_t layer_out_max = (size_t)s.B * s.Hkv * s.S * s.D * esz;
-  for (int l = 0; l < s.L; ++l) {
-    tb.ko.p[l] = const_cast<void *>(ko.p[l]);
-    tb.vo.p[l] = const_cast<void *>(vo.p[l]);
-    const char *o[2] = {static_cast<const char *>(ko.p[l]), static_cast<const char *>(vo.p[l])};
-    for (int a = 0; a < 2; ++a) {
-      for (int m = 0; m < s.L; ++m) {
-        const char *in[2] = {static_cast<const char *>(tb.k.p[m]), static_cast<const char *>(tb.v.p[m])};
-        for (int c = 0; c < 2; ++c)
-          if (o[a] < in[c] + layer_in && in[c] < o[a] + layer_out_max)
-            return fail(AIRCACHE_EINVAL, "an output buffer of layer %d may overlap input layer %d", l, m);
-      }
-    }
-  }
-  for (int l = s.L; l < AIRCACHE_MAX_LAYERS; ++l) tb.ko.p[l] = tb.vo.p[l] = nullptr;
+  if ((rc = gather_tables(cfg, k, v, k_out, v_out, &tb))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = mark(ev, 0, st))) return rc;
+  if ((rc = launch_gather(cfg, tb, plan_ptrs(plan), st))) return rc;
+  return mark(ev, 1, st);
+}
+
+int aircache_run_profiled(const aircache_desc *desc, const void *const *q_txt, const void *const *k,
+                          const void *const *v, const aircache_plan_buf *plan, void *const *k_out,
+                          void *const *v_out, void *workspace, size_t ws_bytes, void *stream,
+                          void *const *events, int n_events) {
+  if (events && n_events != AIRCACHE_RUN_KERNELS + 1)
+    return fail(AIRCACHE_EINVAL, "n_events=%d, expected %d", n_events, AIRCACHE_RUN_KERNELS + 1);
+  hipEvent_t *ev = events ? reinterpret_cast<hipEvent_t *>(const_cast<void **>(events)) : nullptr;
+  Config cfg;
+  int rc;
+  if ((rc = make_config(desc, &cfg))) return rc;
+  if ((rc = check_plan_buf(plan, false))) return rc;
+  if (!workspace || ws_bytes < cfg.ws_bytes)
+    return fail(AIRCACHE_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0,
+                cfg.ws_bytes);
+  if (!aligned16(workspace)) return fail(AIRCACHE_EINVAL, "workspace is not 16-byte aligned");
+  LayerTable qt, kt;
+  if ((rc = fill_table(q_txt, cfg.sh.L, &qt, "q_txt"))) return rc;
+  if ((rc = fill_table(k, cfg.sh.L, &kt, "k"))) return rc;
+  GatherTables tb;
+  if ((rc = gather_tables(cfg, k, v, k_out, v_out, &tb))) return rc;
   const PlanPtrs pp = plan_ptrs(plan);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int units = s.L * s.B * s.Hkv;
-  int nch = (2048 + units - 1) / units;
-  if (nch > 64) nch = 64;
-  if (nch < 1) nch = 1;
-  const int rb = s.D * esz;
-  const int64_t cap = (int64_t)s.B * s.Hkv * s.S * s.D;
-  const dim3 grid((unsigned)(units * nch));
+  const bool bf = desc->dtype == AIRCACHE_BF16;
   if ((rc = mark(ev, 0, st))) return rc;
-  if (rb == 128)
-    hipLaunchKernelGGL(kv_gather_kernel<128>, grid, dim3(256), 0, st, s, tb, pp, nch, esz, cap);
-  else if (rb == 256)
-    hipLaunchKernelGGL(kv_gather_kernel<256>, grid, dim3(256), 0, st, s, tb, pp, nch, esz, cap);
-  else
-    hipLaunchKernelGGL(kv_gather_kernel<512>, grid, dim3(256), 0, st, s, tb, pp, nch, esz, cap);
-  if ((rc = check_hip(hipGetLastError(), "kv_gather_kernel launch"))) return rc;
+  if (cfg.run_fused) {
+    LayerTable vt, kot, vot;
+    for (int l = 0; l < cfg.sh.L; ++l) {
+      vt.p[l] = tb.v.p[l];
+      kot.p[l] = tb.ko.p[l];
+      vot.p[l] = tb.vo.p[l];
+    }
+    const RunOut out{&vt, &kot, &vot};
+    const Ws ws = ws_of(cfg, workspace);
+    int fgrid = 0;
+    if (bf && cfg.sh.D == 128) {
+      if (!(rc = fused_grid<Bf16Tag, 128>(cfg, &fgrid)))
+        rc = launch_chunked<Bf16Tag, 128>(cfg, qt, kt, pp, ws, workspace, fgrid, st, &out);
+    } else if (bf) {
+      if (!(rc = fused_grid<Bf16Tag, 64>(cfg, &fgrid)))
+        rc = launch_chunked<Bf16Tag, 64>(cfg, qt, kt, pp, ws, workspace, fgrid, st, &out);
+    } else if (cfg.sh.D == 128) {
+      if (!(rc = fused_grid<F32Tag, 128>(cfg, &fgrid)))
+        rc = launch_chunked<F32Tag, 128>(cfg, qt, kt, pp, ws, workspace, fgrid, st, &out);
+    } else {
+      if (!(rc = fused_grid<F32Tag, 64>(cfg, &fgrid)))
+        rc = launch_chunked<F32Tag, 64>(cfg, qt, kt, pp, ws, workspace, fgrid, st, &out);
+    }
+    if (rc) return rc;
+  } else {
+    if ((rc = aircache_plan(desc, q_txt, k, plan, workspace, ws_bytes, stream))) return rc;
+    if ((rc = launch_gather(cfg, tb, pp, st))) return rc;
+  }
   return mark(ev, 1, st);
+}
+
+int aircache_run(const aircache_desc *desc, const void *const *q_txt, const void *const *k, const void *const *v,
+                 const aircache_plan_buf *plan, void *const *k_out, void *const *v_out, void *workspace,
+                 size_t ws_bytes, void *stream) {
+  return aircache_run_profiled(desc, q_txt, k, v, plan, k_out, v_out, workspace, ws_bytes, stream, nullptr, 0);
 }
 
 int aircache_compress(const aircache_desc *desc, const aircache_plan_buf *plan, const void *const *k,

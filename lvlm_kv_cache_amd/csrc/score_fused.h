@@ -109,9 +109,8 @@ __host__ __device__ inline int fused_kcap_min(int L, int B, int Nv, int wph) {
 // match. The workspace must be zero before its first use.
 struct FusedWs {
   unsigned *epoch;        // [1] calls so far
-  unsigned *edone;        // [1] KV-head parts of pbar finished in this call
   unsigned *exitc;        // [1] workgroups finished in this call
-  float *parts;           // [L*B*Hkv][N_t] KV-head parts of pbar
+  uint64_t *parts;        // [L*B*Hkv][N_t] KV-head parts of pbar, (value | epoch << 32)
   unsigned *cnt_lbc;      // [L*B] finished chunks per (layer, sample)
   unsigned *cnt_chunk;    // [L*B][max_chunks] finished row groups per chunk
   uint64_t *xrec;         // [L*B][rec_stride][2] (row max | epoch << 32), (row sum | epoch << 32)
@@ -122,6 +121,12 @@ struct FusedWs {
   int max_chunks;         // chunks per (layer, sample) at most
   int max_rg;             // row groups per (layer, sample) at most
   int wmax;               // columns per chunk at most
+  // compaction in the same launch (gather != 0)
+  int gather;
+  int esize;              // bytes per element
+  int64_t cap_elems;      // elements of each compacted layer buffer
+  unsigned *gticket;      // [1] copy units handed out
+  uint64_t *grec;         // [L*B][4] budget, out_off halves, each | epoch << 32
 };
 
 // Dynamic LDS of cross_score_fused_kernel (byte offsets, 16-byte aligned).
@@ -221,6 +226,15 @@ __device__ __forceinline__ double fused_block_sum_d(double v, double *red) {
   __syncthreads();
   return t;
 }
+
+// Layer pointers of one launch of the chunked kernel, L entries each: text
+// queries at [0, L), keys at [L, 2L) and, when the launch also compacts,
+// values at [2L, 3L), compacted keys at [3L, 4L) and compacted values at
+// [4L, 5L).
+constexpr int kFusedTableSlots = 256;
+struct FusedTables {
+  const void *p[kFusedTableSlots];
+};
 
 // Everything an item needs to know about itself.
 struct FusedItem {
@@ -577,7 +591,7 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, i
     if (counted)  // leave the histogram zero (the budget's barriers ordered the counts before this)
       for (int i = tid; i < kTopkBuckets; i += NT) hist[i] = 0u;
     if (kbud >= Nv)
-      for (int i = tid; i < Nv; i += NT) kept[i] = i;
+      for (int i = tid; i < Nv; i += NT) store_coherent(&kept[i], (int32_t)i);
     return;
   }
   int need = kbud;  // keys still to take among those matching the prefix
@@ -707,7 +721,7 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, i
       before += (w < wave) ? x : 0;
       row += x;
     }
-    if ((mk[p] >> lane) & 1ull) kept[base + before + __popcll(mk[p] & lt)] = p * NT + tid;
+    if ((mk[p] >> lane) & 1ull) store_coherent(&kept[base + before + __popcll(mk[p] & lt)], (int32_t)(p * NT + tid));
     base += row;
   }
 }
@@ -718,11 +732,12 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, i
 // of each of the G heads over the N_t text keys come from MFMA (16 text keys
 // as the A operand, up to 16 query heads as the B operand) into LDS; each wave
 // normalises whole rows (max, sum of exp2); the rows are summed in ascending
-// head order into part[j], written with agent-coherent stores.
+// head order into part[j], written with agent-coherent stores as
+// (value | epoch << 32) words, so a reader that sees the epoch has the value.
 // lds: G * N_t floats.
 template <typename Tag, int D>
-__device__ __forceinline__ void fused_elite_part(const Shape &sh, const LayerTable &qt, const LayerTable &kt, int lb,
-                                                 int g, float *part, float *lds) {
+__device__ __forceinline__ void fused_elite_part(const Shape &sh, const FusedTables &tab, int lb,
+                                                 int g, uint64_t *part, unsigned epoch, float *lds) {
   using E = typename Tag::store_t;
   constexpr int NW = kFusedWaves, NT = kFusedThreads;
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
@@ -730,8 +745,8 @@ __device__ __forceinline__ void fused_elite_part(const Shape &sh, const LayerTab
   const int l = lb / sh.B, b = lb - (lb / sh.B) * sh.B;
   const int Nt = sh.Nt, G = sh.G;
   float *z = lds;
-  const E *q = static_cast<const E *>(qt.p[l]);
-  const E *k = static_cast<const E *>(kt.p[l]);
+  const E *q = static_cast<const E *>(tab.p[l]);
+  const E *k = static_cast<const E *>(tab.p[sh.L + l]);
   const int nkt = (Nt + 15) >> 4;
   const int nht = (G + 15) >> 4;
   const int items = nht * nkt;
@@ -789,7 +804,7 @@ __device__ __forceinline__ void fused_elite_part(const Shape &sh, const LayerTab
   for (int j = tid; j < Nt; j += NT) {
     float a = 0.f;
     for (int h = 0; h < G; ++h) a += z[(size_t)h * Nt + j];
-    store_coherent(&part[j], a);
+    store_coherent(&part[j], pack_rec(a, epoch));
   }
 }
 
@@ -811,7 +826,8 @@ __device__ __forceinline__ int ceil_div_small(int a, int b) {
 // the cap. stage: LDS for stage_floats floats of pbar (a batch of pairs).
 // HKV = n_kv_heads: every thread keeps 32 part loads in flight.
 template <int HKV>
-__device__ __forceinline__ void fused_elite_sets_h(const Shape &sh, const PlanPtrs &plan, const float *parts, int me,
+__device__ __forceinline__ void fused_elite_sets_h(const Shape &sh, const PlanPtrs &plan, const uint64_t *parts,
+                                                   unsigned epoch, int me,
                                                    int P, float *stage, int stage_floats, int *ntk,
                                                    unsigned long long *emask) {
   constexpr int NT = kFusedThreads, NW = kFusedWaves, R = 32 / HKV, U = 4;
@@ -819,30 +835,50 @@ __device__ __forceinline__ void fused_elite_sets_h(const Shape &sh, const PlanPt
   const int Nt = sh.Nt, LB = sh.L * sh.B;
   const int ntw = fused_words64(Nt);
   const int batch = max(1, stage_floats / Nt);  // (layer, sample) pairs per batch
-  const auto rp = coherent_rsrc(parts, (unsigned)((size_t)LB * HKV * Nt * sizeof(float)));
+  const auto rp = coherent_rsrc(parts, (unsigned)((size_t)LB * HKV * Nt * sizeof(uint64_t)));
   const unsigned long long lt = (1ull << lane) - 1ull;
   for (int lb0 = 0; lb0 < LB; lb0 += batch) {
     const int nlb = min(batch, LB - lb0);
     const int n = nlb * Nt;
     for (int e0 = 0; e0 < n; e0 += R * NT) {
       // every load issued before any is used (an entry past the batch reads
-      // past the buffer's bounds, which returns 0 without a memory access)
-      float part[R][HKV];
+      // past the buffer's bounds, which returns 0 without a memory access);
+      // a word not yet tagged with this call's epoch is read again
+      unsigned off[R][HKV];
+      uint64_t part[R][HKV];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int e = e0 + r * NT + tid;
         const int q = ceil_div_small(e + 1, Nt) - 1, j = e - q * Nt;  // e / Nt, e % Nt
-        const unsigned base = (unsigned)((((size_t)(lb0 + q) * HKV) * Nt + j) * sizeof(float));
+        const unsigned base = (unsigned)((((size_t)(lb0 + q) * HKV) * Nt + j) * sizeof(uint64_t));
 #pragma unroll
-        for (int g = 0; g < HKV; ++g)
-          part[r][g] = load_sc1_f(rp, e < n ? base + (unsigned)(g * Nt * sizeof(float)) : 0xfffffff0u);
+        for (int g = 0; g < HKV; ++g) {
+          off[r][g] = e < n ? base + (unsigned)(g * Nt * sizeof(uint64_t)) : 0xfffffff0u;
+          part[r][g] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rp, (int)off[r][g], 0, 16));
+        }
+      }
+      unsigned spins = 0;
+      for (;;) {
+        bool ok = true;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int g = 0; g < HKV; ++g) ok = ok && (off[r][g] == 0xfffffff0u || (unsigned)(part[r][g] >> 32) == epoch);
+        if (ok || spin_expired(spins, plan.status)) break;
+        __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int g = 0; g < HKV; ++g)
+            if (off[r][g] != 0xfffffff0u && (unsigned)(part[r][g] >> 32) != epoch)
+              part[r][g] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rp, (int)off[r][g], 0, 16));
       }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int e = e0 + r * NT + tid;
         float a = 0.f;
 #pragma unroll
-        for (int g = 0; g < HKV; ++g) a += part[r][g];
+        for (int g = 0; g < HKV; ++g) a += __uint_as_float((unsigned)part[r][g]);
         if (e < n) stage[e] = a;
       }
     }
@@ -900,14 +936,14 @@ __device__ __forceinline__ void fused_elite_sets_h(const Shape &sh, const PlanPt
     }
   }
 }
-__device__ __forceinline__ void fused_elite_sets(const Shape &sh, const PlanPtrs &plan, const float *parts, int me,
-                                                 int P, float *stage, int stage_floats, int *ntk,
-                                                 unsigned long long *emask) {
+__device__ __forceinline__ void fused_elite_sets(const Shape &sh, const PlanPtrs &plan, const uint64_t *parts,
+                                                 unsigned epoch, int me, int P, float *stage, int stage_floats,
+                                                 int *ntk, unsigned long long *emask) {
   switch (sh.Hkv) {
-    case 1: fused_elite_sets_h<1>(sh, plan, parts, me, P, stage, stage_floats, ntk, emask); break;
-    case 2: fused_elite_sets_h<2>(sh, plan, parts, me, P, stage, stage_floats, ntk, emask); break;
-    case 4: fused_elite_sets_h<4>(sh, plan, parts, me, P, stage, stage_floats, ntk, emask); break;
-    default: fused_elite_sets_h<8>(sh, plan, parts, me, P, stage, stage_floats, ntk, emask); break;
+    case 1: fused_elite_sets_h<1>(sh, plan, parts, epoch, me, P, stage, stage_floats, ntk, emask); break;
+    case 2: fused_elite_sets_h<2>(sh, plan, parts, epoch, me, P, stage, stage_floats, ntk, emask); break;
+    case 4: fused_elite_sets_h<4>(sh, plan, parts, epoch, me, P, stage, stage_floats, ntk, emask); break;
+    default: fused_elite_sets_h<8>(sh, plan, parts, epoch, me, P, stage, stage_floats, ntk, emask); break;
   }
 }
 
@@ -1078,7 +1114,8 @@ __device__ __forceinline__ BudgetSums budget_sums_lds(int L, const double *st, c
 // for sample bb) the budgets of layer l of those samples ("Layer-wise KV
 // Cache Budget Allocation", the r_hat equation, over the sample's layers in
 // order); writes the plan's budget, budget_x and out_off of (l, b) (and the
-// layer's total after the last sample) and returns the budget.
+// layer's total after the last sample), leaves the budget in bc[0] and the
+// offset's 32-bit halves in bc[2], bc[3], and returns the budget.
 // sts: LDS for 2 * (L * (b + 1) + 8) doubles.
 __device__ __forceinline__ int fused_budget(const Shape &sh, const PlanPtrs &plan, const FusedWs &fw, int l, int b,
                                             unsigned epoch, double *sts, int *bc) {
@@ -1129,6 +1166,8 @@ __device__ __forceinline__ int fused_budget(const Shape &sh, const PlanPtrs &pla
     off = wave_sum_d(off);
     if (lane == 0) {
       plan.out_off[(size_t)l * (B + 1) + b] = (int64_t)off;
+      bc[2] = (int)((uint64_t)(int64_t)off & 0xffffffffu);
+      bc[3] = (int)((uint64_t)(int64_t)off >> 32);
       if (b == B - 1) plan.out_off[(size_t)l * (B + 1) + B] = (int64_t)off + (int64_t)bc[1];
     }
   }
@@ -1136,9 +1175,49 @@ __device__ __forceinline__ int fused_budget(const Shape &sh, const PlanPtrs &pla
   return uniform(bc[0]);
 }
 
+// One compaction unit ("compress" of the training-free procedure): the kept
+// visual rows (ascending) and then all N_t text rows of one (layer, sample, KV
+// head) of K or V, copied to the sample's segment of the compacted layer
+// buffer at element offset off, as 16-byte pieces, sixteen per thread in
+// flight. A budget or offset outside the buffer is skipped, as in
+// kv_gather_kernel. kidx: LDS for N_v ints.
+__device__ __forceinline__ void fused_gather_unit(const Shape &sh, const PlanPtrs &plan, const FusedWs &fw,
+                                                  const char *src_l, char *dst_l, int b, int g, int plb, int bud,
+                                                  int64_t off, int *kidx) {
+  constexpr int NT = kFusedThreads, J = 16;
+  const int tid = opaque_tid();
+  const int Nv = sh.Nv, n = bud + sh.Nt;
+  const int rb = sh.D * fw.esize;  // bytes per row: 128, 256 or 512
+  if (bud < 0 || bud > Nv || off < 0 || off + (int64_t)sh.Hkv * n * sh.D > fw.cap_elems) return;
+  const auto rk = coherent_rsrc(plan.kept + (size_t)plb * Nv, (unsigned)(Nv * sizeof(int32_t)));
+  for (int i = tid; i < bud; i += NT) kidx[i] = load_sc1_i(rk, (unsigned)(i * sizeof(int32_t)));
+  __syncthreads();
+  const int cs = rb == 128 ? 3 : rb == 256 ? 4 : 5;  // log2 of 16-byte pieces per row
+  const int nq = n << cs;
+  const char *src = src_l + (size_t)(b * sh.Hkv + g) * sh.S * rb;
+  char *dst = dst_l + (size_t)off * fw.esize + (size_t)g * n * rb;
+  for (int q0 = 0; q0 < nq; q0 += J * NT) {
+    u32x4_t v[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int q = min(q0 + j * NT + tid, nq - 1);  // past the end: reload the last piece, not stored
+      const int i = q >> cs, c = q & ((1 << cs) - 1);
+      int row = i < bud ? kidx[i] : Nv + (i - bud);
+      row = min(max(row, 0), sh.S - 1);  // a kept index is below N_v; never read outside the layer
+      v[j] = *reinterpret_cast<const u32x4_t *>(src + (size_t)row * rb + 16 * c);
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int q = q0 + j * NT + tid;
+      if (q < nq) *reinterpret_cast<u32x4_t *>(dst + ((size_t)(q >> cs) * rb + 16 * (q & ((1 << cs) - 1)))) = v[j];
+    }
+  }
+  __syncthreads();  // kidx is reused by the next unit
+}
+
 template <typename Tag, int D>
-__global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape sh, LayerTable qt, LayerTable kt,
-                                                                          PlanPtrs plan, FusedWs fw, FusedLds lo) {
+__global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape sh, FusedTables tab, PlanPtrs plan,
+                                                                          FusedWs fw, FusedLds lo) {
   extern __shared__ __attribute__((aligned(16))) float lds_f[];
   unsigned char *lds = reinterpret_cast<unsigned char *>(lds_f);
   __shared__ int wtot[4 * kFusedWaves];
@@ -1158,27 +1237,20 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
   unsigned long long *emask = reinterpret_cast<unsigned long long *>(lds + lo.emask);
 
   // Phase 0: the KV-head parts of pbar, items (layer, sample, KV head) me,
-  // me + P, ...; each is counted in edone once written. The status word is
-  // cleared before workgroup 0's first count, so every later status bit is
-  // set after the clear.
-  if (me == 0 && tid == 0) store_coherent(plan.status, 0);
+  // me + P, ..., published as epoch-tagged words (no counter: the readers
+  // check the tags). The status word is cleared before workgroup 0 writes
+  // its first part; every status bit is set after some workgroup has seen
+  // all parts, so after the clear.
+  if (me == 0 && tid == 0) {
+    store_coherent(plan.status, 0);
+    wait_all_memory();
+  }
   for (int t = me; t < LB * sh.Hkv; t += P) {
     const int lb = t / sh.Hkv, g = t - lb * sh.Hkv;
-    fused_elite_part<Tag, D>(sh, qt, kt, lb, g, fw.parts + (size_t)t * sh.Nt, lds_f);
-    wait_all_memory();
-    __syncthreads();
-    if (tid == 0) counter_add(fw.edone, 1u);
+    fused_elite_part<Tag, D>(sh, tab, lb, g, fw.parts + (size_t)t * sh.Nt, epoch, lds_f);
     __syncthreads();  // the LDS is free again
   }
-  if (tid == 0) {
-    unsigned spins = 0;
-    while (load_coherent(fw.edone) < (unsigned)(LB * sh.Hkv)) {
-      if (spin_expired(spins, plan.status)) break;
-      __builtin_amdgcn_s_sleep(2);
-    }
-  }
-  __syncthreads();
-  fused_elite_sets(sh, plan, fw.parts, me, P, lds_f + lo.ring / 4, (lo.el - lo.ring) / 4, ntk_l, emask);
+  fused_elite_sets(sh, plan, fw.parts, epoch, me, P, lds_f + lo.ring / 4, (lo.el - lo.ring) / 4, ntk_l, emask);
   fused_schedule(sh, ntk_l, me, P, item_list, hdr, wtot);
   __syncthreads();
   const int kcap = uniform(hdr[0]);
@@ -1203,8 +1275,8 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
     const int local = item & 0xffff;
     it.r = local / it.cp.nchunks;
     it.c = local - it.r * it.cp.nchunks;
-    it.q = qt.p[it.l];
-    it.k = kt.p[it.l];
+    it.q = tab.p[it.l];
+    it.k = tab.p[L + it.l];
     int *el = reinterpret_cast<int *>(lds + lo.el);
     __syncthreads();  // the previous item is done with the LDS
     // elite list of the item's (layer, sample) from its bit mask, ascending
@@ -1340,6 +1412,58 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
     if (Nv <= 2048) block_topk<4>(sh, ivl, kp, hist, budget);
     else if (Nv <= 4096) block_topk<8>(sh, ivl, kp, hist, budget);
     else block_topk<16>(sh, ivl, kp, hist, budget);
+    if (fw.gather) {
+      // kept indices out: publish the (layer, sample) for compaction
+      wait_all_memory();
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const uint64_t tag = (uint64_t)epoch << 32;
+        uint64_t *r = fw.grec + (size_t)plb * 4;
+        store_coherent(r + 0, tag | (uint64_t)(unsigned)bcast[0]);
+        store_coherent(r + 1, tag | (uint64_t)(unsigned)bcast[2]);
+        store_coherent(r + 2, tag | (uint64_t)(unsigned)bcast[3]);
+      }
+    }
+  }
+
+  // Compaction units (layer, sample, KV head, K or V) by ticket, in
+  // sample-major order; each waits for its (layer, sample)'s record.
+  if (fw.gather) {
+    int *kidx = reinterpret_cast<int *>(lds + lo.ring);
+    const int nunits = LB * sh.Hkv * 2;
+    const auto rg = coherent_rsrc(fw.grec, (unsigned)((size_t)LB * 32));
+    for (;;) {
+      __syncthreads();
+      if (threadIdx.x == 0) bcast[1] = (int)counter_add(fw.gticket, 1u);
+      __syncthreads();
+      const int u = uniform(bcast[1]);
+      if (u >= nunits) break;
+      const int kv = u & 1, ug = u >> 1;
+      const int s2 = ug / sh.Hkv, g = ug - s2 * sh.Hkv;
+      const int b = s2 / L, l = s2 - b * L, plb = l * B + b;
+      if (threadIdx.x == 0) {
+        uint64_t w[3];
+        unsigned spins = 0;
+        for (;;) {
+#pragma unroll
+          for (int j = 0; j < 3; ++j)
+            w[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rg, plb * 32 + 8 * j, 0, 16));
+          if (((unsigned)(w[0] >> 32) == epoch && (unsigned)(w[1] >> 32) == epoch && (unsigned)(w[2] >> 32) == epoch) ||
+              spin_expired(spins, plan.status))
+            break;
+          __builtin_amdgcn_s_sleep(2);
+        }
+        bcast[0] = (int)(unsigned)w[0];
+        bcast[2] = (int)(unsigned)w[1];
+        bcast[3] = (int)(unsigned)w[2];
+      }
+      __syncthreads();
+      const int bud = uniform(bcast[0]);
+      const int64_t off = (int64_t)(((uint64_t)(unsigned)uniform(bcast[3]) << 32) | (uint64_t)(unsigned)uniform(bcast[2]));
+      const char *src = static_cast<const char *>(tab.p[(1 + kv) * L + l]);  // k or v
+      char *dst = static_cast<char *>(const_cast<void *>(tab.p[(3 + kv) * L + l]));  // k_out or v_out
+      fused_gather_unit(sh, plan, fw, src, dst, b, g, plb, bud, off, kidx);
+    }
   }
 
   // The last workgroup to finish ends the call: counters reset, epoch advanced.
@@ -1347,7 +1471,7 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
   if (threadIdx.x == 0) {
     if (counter_add(fw.exitc, 1u) == (unsigned)P - 1u) {
       store_coherent(fw.exitc, 0u);
-      store_coherent(fw.edone, 0u);
+      if (fw.gather) store_coherent(fw.gticket, 0u);
       store_coherent(fw.epoch, epoch);
     }
   }

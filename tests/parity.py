@@ -53,16 +53,24 @@ def make_aircache(w, alpha=None, ratio=None, max_elite=0, path="auto"):
                     ratio=w.ratio if ratio is None else ratio, max_elite=max_elite, path=path)
 
 
-def run_gpu(inp: wl.Inputs, alpha=None, ratio=None, max_elite=0, tensors=None, compress=True, path="auto", ac=None):
+def run_gpu(inp: wl.Inputs, alpha=None, ratio=None, max_elite=0, tensors=None, compress=True, path="auto", ac=None,
+            run=False):
     """Plan (and compress) on the GPU; ac: an AirCache to reuse (its workspace
-    carries state from earlier calls)."""
+    carries state from earlier calls); run: one aircache_run call instead of
+    aircache_plan then aircache_compress."""
     w = inp.w
     if ac is None:
         ac = make_aircache(w, alpha, ratio, max_elite, path)
     q, k, v = tensors if tensors is not None else to_torch(inp)
-    plan = ac.plan(q, k)
     out = {}
-    if compress:
+    if run:
+        plan = ac.alloc_plan()
+        ko, vo = ac.alloc_compacted()
+        ac.run(q, k, v, plan, ko, vo)
+        compress = True
+    else:
+        plan = ac.plan(q, k)
+    if compress and not run:
         ko, vo = ac.alloc_compacted()
         ac.compress(plan, k, v, ko, vo)
     torch.cuda.synchronize()

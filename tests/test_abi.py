@@ -74,6 +74,17 @@ def test_resolved_path(lib):
     assert _lib.resolved_path(desc(path=2, n_vis=3073)) == -1
 
 
+def test_run_launches(lib):
+    # one launch where the chunked path also compacts (5 * n_layers pointers
+    # fit its table), else the plan call's kernels and kv_gather_kernel
+    assert _lib.run_launches(desc()) == 1
+    assert _lib.run_launches(desc(n_layers=51)) == 1
+    assert _lib.run_launches(desc(n_layers=52)) == 2
+    assert _lib.run_launches(desc(path=2)) == 4
+    assert _lib.run_launches(desc(path=1)) == 5
+    assert _lib.run_launches(desc(n_layers=0)) == -1
+
+
 @pytest.mark.parametrize("bad", [dict(n_layers=0), dict(n_layers=129), dict(batch=0), dict(n_kv_heads=5),
                                  dict(head_dim=96), dict(n_vis=2), dict(n_vis=9000), dict(n_txt=0),
                                  dict(dtype="x"), dict(alpha=1.5), dict(alpha=float("nan")),

@@ -40,6 +40,16 @@ def test_workload(cid, seed):
     print(f"[parity] workload {cid} seed {seed}: {rep}", flush=True)
 
 
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_workload_run(cid):
+    """aircache_run (plan and compaction in one call, one launch on the chunked
+    path) on the full-size workloads."""
+    print(f"[parity] workload {cid} run", flush=True)
+    inp = wl.make_inputs(cid, cid)
+    g = run_gpu(inp, max_elite=0 if cid <= 2 else 64, run=True)
+    compare(inp, g, reference(inp, g))
+
+
 @pytest.mark.parametrize("path,cid", [("tiled", 1), ("tiled", 2), ("tiled", 3), ("tiled", 5),
                                       ("rows", 1), ("rows", 3), ("rows", 5), ("chunked", 4)])
 def test_workload_other_paths(path, cid):
@@ -65,24 +75,24 @@ EDGE = [
 
 @pytest.mark.parametrize("shape", EDGE, ids=lambda s: "x".join(f"{k}{v}" for k, v in s.items()))
 @pytest.mark.parametrize("seed", [0, 1])
-@pytest.mark.parametrize("path", ["auto", "tiled", "rows"])
+@pytest.mark.parametrize("path", ["auto", "auto-run", "tiled", "rows"])
 def test_edge_shapes(shape, seed, path):
     if path == "rows" and shape["Nv"] > 3072:
         pytest.skip("the rows path serves N_v <= 3072")
     print(f"[parity] edge {shape} seed {seed} path {path}", flush=True)
     w = wl.custom(ratio=0.2, **shape)
     inp = wl.make_inputs(w, seed)
-    g = run_gpu(inp, path=path)
+    g = run_gpu(inp, path=path.split("-")[0], run=path.endswith("-run"))
     compare(inp, g, reference(inp, g))
 
 
-@pytest.mark.parametrize("path", ["auto", "tiled", "rows"])
+@pytest.mark.parametrize("path", ["auto", "auto-run", "tiled", "rows"])
 def test_all_text_elite_many_rows(path):
     """Zero queries make every text token elite: G * N_tk = 280 rows per KV head,
     several row passes of the chunked path, elite text columns spanning chunks."""
     w = wl.custom(Nv=500, Nt=40, Hq=14, Hkv=2, D=128, dtype="bf16", L=2, B=2, ratio=0.3)
     inp = wl.make_inputs(w, 6, zero_q=True)
-    g = run_gpu(inp, path=path)
+    g = run_gpu(inp, path=path.split("-")[0], run=path.endswith("-run"))
     assert (g["n_elite"] == 40).all()
     compare(inp, g, reference(inp, g))
 
@@ -93,9 +103,9 @@ def test_workspace_reused_across_calls():
     from parity import make_aircache
     w = wl.custom(Nv=900, Nt=30, Hq=8, Hkv=4, D=128, dtype="bf16", L=3, B=2, ratio=0.2)
     ac = make_aircache(w)
-    for seed in (21, 22, 21):
+    for seed, run in ((21, False), (22, True), (21, True), (23, False)):
         inp = wl.make_inputs(w, seed)
-        g = run_gpu(inp, ac=ac)
+        g = run_gpu(inp, ac=ac, run=run)
         compare(inp, g, reference(inp, g))
 
 
