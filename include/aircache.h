@@ -137,10 +137,11 @@ int aircache_abi_version(void);
 
 /* Bytes of device workspace aircache_plan needs for this descriptor, or 0 if
  * the descriptor is invalid (aircache_last_error() says why). The workspace is
- * caller-owned scratch that must be zero-filled once, before its first use;
- * the library keeps it valid across calls after that, with this or any other
- * descriptor it is large enough for. One workspace must not be used by two
- * calls that can run concurrently. */
+ * caller-owned scratch that must be zero-filled before its first use with a
+ * descriptor; the library keeps it valid across calls with that descriptor
+ * (its counters end every call at zero and its records carry a call count).
+ * Zero it again before using it with a different descriptor. One workspace
+ * must not be used by two calls that can run concurrently. */
 size_t aircache_workspace_size(const aircache_desc *desc);
 
 /* Largest compacted element count per layer (every visual row kept): the
