@@ -543,10 +543,10 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, i
   uint2 *cand = reinterpret_cast<uint2 *>(lds + kTopkBuckets);
   unsigned *ncand = lds + kTopkBuckets + 2 * kTopkRankCap;
   const auto riv = coherent_rsrc(iv_l, (unsigned)(Nv * sizeof(float)));
+  // an index past N_v reads past the buffer, which returns 0
   unsigned key[PER];
 #pragma unroll
-  for (int p = 0; p < PER; ++p)
-    key[p] = (p * NT + tid < Nv) ? (unsigned)load_sc1_i(riv, (unsigned)((p * NT + tid) * sizeof(float))) : 0u;
+  for (int p = 0; p < PER; ++p) key[p] = (unsigned)load_sc1_i(riv, (unsigned)((p * NT + tid) * sizeof(float)));
   float fmin = INFINITY, fmax = 0.f;  // keys as floats: same order
 #pragma unroll
   for (int p = 0; p < PER; ++p)
@@ -648,8 +648,9 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, i
     hb -= width;
     par ^= 1;
   }
-  // T and the count of keys equal to T still to take
+  // T, the count of keys equal to T still to take, and of all keys equal to T
   int need_eq = need;
+  int n_eq = nmatch;  // with every bit resolved, the keys matching the prefix all equal T
   unsigned T = prefix;
   if (hb >= 0) {
     // the nmatch <= kTopkRankCap keys matching the prefix, ranked directly
@@ -669,47 +670,60 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, i
     nmatch = min(nmatch, kTopkRankCap);
     if (tid < nmatch) {
       const uint2 me = cand[tid];
-      int gt = 0, before = 0;
+      int gt = 0, before = 0, eq = 0;
       for (int i = 0; i < nmatch; ++i) {
         const uint2 o = cand[i];
         gt += (o.x > me.x) ? 1 : 0;
+        eq += (o.x == me.x) ? 1 : 0;
         before += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1 : 0;
       }
       if (before == need - 1) {
         selv[par][0] = (int)me.x;
         selv[par][1] = need - gt;
+        selv[par][2] = eq;  // every key equal to T matches the prefix
       }
     }
     __syncthreads();
     T = (unsigned)uniform(selv[par][0]);
     need_eq = uniform(selv[par][1]);
+    n_eq = uniform(selv[par][2]);
     if (tid == 0) *ncand = 0u;
   }
-  // per run (p, wave) of 64 indices: keys equal to T, then keys kept
+  // per run (p, wave) of 64 indices: the kept keys. When every key equal to T
+  // is kept (the usual case) that is key >= T; otherwise the keys equal to T
+  // are ranked by index first.
   const unsigned long long lt = (1ull << lane) - 1ull;
-  unsigned long long meq[PER];
-#pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    meq[p] = __ballot(p * NT + tid < Nv && key[p] == T);
-    if (lane == 0) rowcnt[0][p][wave] = __popcll(meq[p]);
-  }
-  __syncthreads();
-  int eq_base = 0;  // keys equal to T at lower indices than this wave's run
   unsigned long long mk[PER];
+  if (n_eq == need_eq) {
 #pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    int before = 0, row = 0;
-    for (int w = 0; w < NW; ++w) {
-      const int x = rowcnt[0][p][w];
-      before += (w < wave) ? x : 0;
-      row += x;
+    for (int p = 0; p < PER; ++p) {
+      mk[p] = __ballot(p * NT + tid < Nv && key[p] >= T);
+      if (lane == 0) rowcnt[1][p][wave] = __popcll(mk[p]);
     }
-    const bool valid = p * NT + tid < Nv;
-    const bool eq = (meq[p] >> lane) & 1ull;
-    const int eq_rank = eq_base + before + __popcll(meq[p] & lt);
-    mk[p] = __ballot(valid && (key[p] > T || (eq && eq_rank < need_eq)));
-    if (lane == 0) rowcnt[1][p][wave] = __popcll(mk[p]);
-    eq_base += row;
+  } else {
+    unsigned long long meq[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      meq[p] = __ballot(p * NT + tid < Nv && key[p] == T);
+      if (lane == 0) rowcnt[0][p][wave] = __popcll(meq[p]);
+    }
+    __syncthreads();
+    int eq_base = 0;  // keys equal to T at lower indices than this wave's run
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      int before = 0, row = 0;
+      for (int w = 0; w < NW; ++w) {
+        const int x = rowcnt[0][p][w];
+        before += (w < wave) ? x : 0;
+        row += x;
+      }
+      const bool valid = p * NT + tid < Nv;
+      const bool eq = (meq[p] >> lane) & 1ull;
+      const int eq_rank = eq_base + before + __popcll(meq[p] & lt);
+      mk[p] = __ballot(valid && (key[p] > T || (eq && eq_rank < need_eq)));
+      if (lane == 0) rowcnt[1][p][wave] = __popcll(mk[p]);
+      eq_base += row;
+    }
   }
   __syncthreads();
   int base = 0;
@@ -1385,16 +1399,15 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
     if (uniform(bcast[0])) ++nowed;
   }
 
-  // Owed (layer, sample) pairs: first every statistics record (a top-k waits
-  // for records of other pairs, possibly this workgroup's own), then the
-  // top-k tasks with their budgets.
-  for (int o = 0; o < nowed; ++o) {
-    const int plb = uniform(owed[o]);
-    if (threadIdx.x < 64) {
+  // Owed (layer, sample) pairs: first every statistics record (every top-k
+  // waits for the records of whole samples, possibly this workgroup's own),
+  // then the top-k tasks with their budgets.
+  if (threadIdx.x < 64)
+    for (int o = 0; o < nowed; ++o) {
+      const int plb = uniform(owed[o]);
       const int nch = fused_chunk_plan(ntk_l[plb], sh.G, Nv, wph, kcap).nchunks;
       fused_layer_stats(sh, plan, fw, plb, nch, epoch);
     }
-  }
   unsigned *hist = reinterpret_cast<unsigned *>(lds + lo.ring);
   {
     const int tid = opaque_tid();
