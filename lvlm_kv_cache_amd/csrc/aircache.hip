@@ -1091,7 +1091,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 struct Config {
   Shape sh;
   size_t off_cnt, off_stats, off_e, off_part, ws_bytes;
-  size_t off_xrec, off_mom, off_srec, off_part_rg, off_cnt_chunk, off_cnt_lbc, off_grec, off_parts64;
+  size_t off_xrec, off_mom, off_srec, off_part_rg, off_cnt_chunk, off_ivrec, off_keptrec, off_grec, off_parts64;
   size_t tile_bytes;   // bytes of one 16-key tile
   bool run_fused;      // aircache_run compacts inside the chunked launch
   size_t off_cnt_elite, off_pbar, off_sched;
@@ -1248,10 +1248,11 @@ int make_config(const aircache_desc *d, Config *cfg) {
     cfg->off_e = cfg->off_part = cfg->off_stats;
     cfg->off_xrec = cfg->off_stats;
     cfg->off_mom = cfg->off_xrec + align_up(lbs * (size_t)cfg->rec_stride * 16);
-    cfg->off_srec = cfg->off_mom + align_up(lbs * (size_t)cfg->max_chunks * 32);
+    cfg->off_srec = cfg->off_mom + align_up(lbs * (size_t)cfg->max_chunks * 64);
     cfg->off_cnt_chunk = cfg->off_srec + align_up(lbs * 32);
-    cfg->off_cnt_lbc = cfg->off_cnt_chunk + align_up(lbs * (size_t)cfg->max_chunks * sizeof(unsigned));
-    cfg->off_grec = cfg->off_cnt_lbc + align_up(lbs * sizeof(unsigned));
+    cfg->off_ivrec = cfg->off_cnt_chunk + align_up(lbs * (size_t)cfg->max_chunks * sizeof(unsigned));
+    cfg->off_keptrec = cfg->off_ivrec + align_up(lbs * (size_t)s.Nv * sizeof(uint64_t));
+    cfg->off_grec = cfg->off_keptrec + align_up(lbs * (size_t)s.Nv * sizeof(uint64_t));
     cfg->off_parts64 = cfg->off_grec + align_up(lbs * 32);
     cfg->off_part_rg = cfg->off_parts64 + align_up(lbs * (size_t)s.Hkv * s.Nt * sizeof(uint64_t));
     // row-group partial sums only when some elite count can need two row groups
@@ -1431,9 +1432,10 @@ int launch_chunked(const Config &cfg, const LayerTable &qt, const LayerTable &kt
   fw.epoch = ws.epoch;
   fw.exitc = reinterpret_cast<unsigned *>(p + cfg.off_sched);
   fw.xrec = reinterpret_cast<uint64_t *>(p + cfg.off_xrec);
-  fw.mom = reinterpret_cast<double *>(p + cfg.off_mom);
+  fw.mom = reinterpret_cast<uint64_t *>(p + cfg.off_mom);
+  fw.ivrec = reinterpret_cast<uint64_t *>(p + cfg.off_ivrec);
+  fw.keptrec = reinterpret_cast<uint64_t *>(p + cfg.off_keptrec);
   fw.srec = reinterpret_cast<uint64_t *>(p + cfg.off_srec);
-  fw.cnt_lbc = reinterpret_cast<unsigned *>(p + cfg.off_cnt_lbc);
   fw.rec_stride = cfg.rec_stride;
   fw.max_chunks = cfg.max_chunks;
   fw.max_rg = cfg.max_rg;

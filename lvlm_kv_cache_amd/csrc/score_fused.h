@@ -111,10 +111,11 @@ struct FusedWs {
   unsigned *epoch;        // [1] calls so far
   unsigned *exitc;        // [1] workgroups finished in this call
   uint64_t *parts;        // [L*B*Hkv][N_t] KV-head parts of pbar, (value | epoch << 32)
-  unsigned *cnt_lbc;      // [L*B] finished chunks per (layer, sample)
   unsigned *cnt_chunk;    // [L*B][max_chunks] finished row groups per chunk
   uint64_t *xrec;         // [L*B][rec_stride][2] (row max | epoch << 32), (row sum | epoch << 32)
-  double *mom;            // [L*B][max_chunks][4] chunk sum, M2, M3, count
+  uint64_t *mom;          // [L*B][max_chunks][8] halves of chunk sum, M2, M3, count, each | epoch << 32
+  uint64_t *ivrec;        // [L*B][N_v] I_v | epoch << 32
+  uint64_t *keptrec;      // [L*B][N_v] kept index | epoch << 32
   uint64_t *srec;         // [L*B][4] halves of s_t and s_k, each | epoch << 32
   float *part;            // [L*B][max_chunks][max_rg][wmax] row-group column sums
   int rec_stride;         // records per (layer, sample)
@@ -528,8 +529,8 @@ constexpr int kTopkRankCap = 256;
 constexpr int kTopkLdsWords = kTopkBuckets + 2 * kTopkRankCap + 4;
 static_assert(kTopkLdsWords * 4 <= kFusedRingMin, "the top-k select must fit the ring's minimum size");
 template <int PER, typename BudgetFn>
-__device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, int32_t *kept, unsigned *lds,
-                                           BudgetFn &&get_budget) {
+__device__ __forceinline__ void block_topk(const Shape &sh, const uint64_t *iv_l, int32_t *kept, uint64_t *kept_rec,
+                                           unsigned epoch, int *status, unsigned *lds, BudgetFn &&get_budget) {
   constexpr int NT = kFusedThreads, NW = kFusedWaves;
   constexpr int BPT = kTopkBuckets / NT;  // buckets per thread in a scan
   static_assert(BPT * NT == kTopkBuckets, "buckets must split evenly over the threads");
@@ -542,11 +543,30 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, i
   unsigned *hist = lds;
   uint2 *cand = reinterpret_cast<uint2 *>(lds + kTopkBuckets);
   unsigned *ncand = lds + kTopkBuckets + 2 * kTopkRankCap;
-  const auto riv = coherent_rsrc(iv_l, (unsigned)(Nv * sizeof(float)));
-  // an index past N_v reads past the buffer, which returns 0
+  // the scores as epoch-tagged words, read again until every word carries
+  // this call's epoch (an index past N_v reads past the buffer: 0, not used)
+  const auto riv = coherent_rsrc(iv_l, (unsigned)(Nv * sizeof(uint64_t)));
+  uint64_t kw[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p)
+    kw[p] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(riv, (p * NT + tid) * 8, 0, 16));
+  {
+    unsigned spins = 0;
+    for (;;) {
+      bool ok = true;
+#pragma unroll
+      for (int p = 0; p < PER; ++p) ok = ok && (p * NT + tid >= Nv || (unsigned)(kw[p] >> 32) == epoch);
+      if (ok || spin_expired(spins, status)) break;
+      __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+      for (int p = 0; p < PER; ++p)
+        if (p * NT + tid < Nv && (unsigned)(kw[p] >> 32) != epoch)
+          kw[p] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(riv, (p * NT + tid) * 8, 0, 16));
+    }
+  }
   unsigned key[PER];
 #pragma unroll
-  for (int p = 0; p < PER; ++p) key[p] = (unsigned)load_sc1_i(riv, (unsigned)((p * NT + tid) * sizeof(float)));
+  for (int p = 0; p < PER; ++p) key[p] = (unsigned)kw[p];
   float fmin = INFINITY, fmax = 0.f;  // keys as floats: same order
 #pragma unroll
   for (int p = 0; p < PER; ++p)
@@ -591,7 +611,10 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, i
     if (counted)  // leave the histogram zero (the budget's barriers ordered the counts before this)
       for (int i = tid; i < kTopkBuckets; i += NT) hist[i] = 0u;
     if (kbud >= Nv)
-      for (int i = tid; i < Nv; i += NT) store_coherent(&kept[i], (int32_t)i);
+      for (int i = tid; i < Nv; i += NT) {
+        kept[i] = i;
+        store_coherent(&kept_rec[i], ((uint64_t)epoch << 32) | (uint64_t)(unsigned)i);
+      }
     return;
   }
   int need = kbud;  // keys still to take among those matching the prefix
@@ -735,7 +758,11 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const float *iv_l, i
       before += (w < wave) ? x : 0;
       row += x;
     }
-    if ((mk[p] >> lane) & 1ull) store_coherent(&kept[base + before + __popcll(mk[p] & lt)], (int32_t)(p * NT + tid));
+    if ((mk[p] >> lane) & 1ull) {
+      const int pos = base + before + __popcll(mk[p] & lt), idx = p * NT + tid;
+      kept[pos] = idx;
+      store_coherent(&kept_rec[pos], ((uint64_t)epoch << 32) | (uint64_t)(unsigned)idx);
+    }
     base += row;
   }
 }
@@ -1054,11 +1081,26 @@ __device__ __forceinline__ void fused_schedule(const Shape &sh, const int *ntk_l
 __device__ __forceinline__ void fused_layer_stats(const Shape &sh, const PlanPtrs &plan, const FusedWs &fw, int plb,
                                                   int nch, unsigned epoch) {
   const int lane = threadIdx.x & 63;
-  const auto rm = coherent_rsrc(fw.mom + (size_t)plb * fw.max_chunks * 4, (unsigned)(fw.max_chunks * 32));
+  const auto rm = coherent_rsrc(fw.mom + (size_t)plb * fw.max_chunks * 8, (unsigned)(fw.max_chunks * 64));
   double v[4] = {0.0, 0.0, 0.0, 0.0};
-  if (lane < nch)
+  if (lane < nch) {
+    // wait for chunk lane's record: eight words tagged with this call's epoch
+    uint64_t w[8];
+    unsigned spins = 0;
+    for (;;) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) v[f] = load_sc1_d(rm, (unsigned)(lane * 32 + 8 * f));
+      for (int f = 0; f < 8; ++f)
+        w[f] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rm, lane * 64 + 8 * f, 0, 16));
+      bool ok = true;
+#pragma unroll
+      for (int f = 0; f < 8; ++f) ok = ok && (unsigned)(w[f] >> 32) == epoch;
+      if (ok || spin_expired(spins, plan.status)) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      v[f] = __builtin_bit_cast(double, (w[2 * f] & 0xffffffffu) | (w[2 * f + 1] << 32));
+  }
   double sum = v[0];
   Moments m{v[3], v[3] > 0.0 ? v[0] / v[3] : 0.0, v[1], v[2]};
   for (int st = 1; st < nch; st <<= 1) {
@@ -1189,43 +1231,71 @@ __device__ __forceinline__ int fused_budget(const Shape &sh, const PlanPtrs &pla
   return uniform(bc[0]);
 }
 
-// One compaction unit ("compress" of the training-free procedure): the kept
-// visual rows (ascending) and then all N_t text rows of one (layer, sample, KV
-// head) of K or V, copied to the sample's segment of the compacted layer
-// buffer at element offset off, as 16-byte pieces, sixteen per thread in
-// flight. A budget or offset outside the buffer is skipped, as in
-// kv_gather_kernel. kidx: LDS for N_v ints.
-__device__ __forceinline__ void fused_gather_unit(const Shape &sh, const PlanPtrs &plan, const FusedWs &fw,
-                                                  const char *src_l, char *dst_l, int b, int g, int plb, int bud,
-                                                  int64_t off, int *kidx) {
+// Copy of rows [r0, r1) of one compaction unit, 16-byte pieces, sixteen per
+// thread in flight: row i is source row src_row(i) and destination row i.
+template <typename RowFn>
+__device__ __forceinline__ void fused_copy_rows(const char *src, char *dst, int rb, int cs, int r0, int r1, int S,
+                                                RowFn &&src_row) {
   constexpr int NT = kFusedThreads, J = 16;
   const int tid = opaque_tid();
-  const int Nv = sh.Nv, n = bud + sh.Nt;
-  const int rb = sh.D * fw.esize;  // bytes per row: 128, 256 or 512
-  if (bud < 0 || bud > Nv || off < 0 || off + (int64_t)sh.Hkv * n * sh.D > fw.cap_elems) return;
-  const auto rk = coherent_rsrc(plan.kept + (size_t)plb * Nv, (unsigned)(Nv * sizeof(int32_t)));
-  for (int i = tid; i < bud; i += NT) kidx[i] = load_sc1_i(rk, (unsigned)(i * sizeof(int32_t)));
-  __syncthreads();
-  const int cs = rb == 128 ? 3 : rb == 256 ? 4 : 5;  // log2 of 16-byte pieces per row
-  const int nq = n << cs;
-  const char *src = src_l + (size_t)(b * sh.Hkv + g) * sh.S * rb;
-  char *dst = dst_l + (size_t)off * fw.esize + (size_t)g * n * rb;
-  for (int q0 = 0; q0 < nq; q0 += J * NT) {
+  const int q_begin = r0 << cs, q_end = r1 << cs;
+  for (int q0 = q_begin; q0 < q_end; q0 += J * NT) {
     u32x4_t v[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int q = min(q0 + j * NT + tid, nq - 1);  // past the end: reload the last piece, not stored
+      const int q = min(q0 + j * NT + tid, q_end - 1);  // past the end: reload the last piece, not stored
       const int i = q >> cs, c = q & ((1 << cs) - 1);
-      int row = i < bud ? kidx[i] : Nv + (i - bud);
-      row = min(max(row, 0), sh.S - 1);  // a kept index is below N_v; never read outside the layer
+      const int row = min(max(src_row(i), 0), S - 1);  // never read outside the layer
       v[j] = *reinterpret_cast<const u32x4_t *>(src + (size_t)row * rb + 16 * c);
     }
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int q = q0 + j * NT + tid;
-      if (q < nq) *reinterpret_cast<u32x4_t *>(dst + ((size_t)(q >> cs) * rb + 16 * (q & ((1 << cs) - 1)))) = v[j];
+      if (q < q_end) *reinterpret_cast<u32x4_t *>(dst + ((size_t)(q >> cs) * rb + 16 * (q & ((1 << cs) - 1)))) = v[j];
     }
   }
+}
+
+// One compaction unit ("compress" of the training-free procedure): the kept
+// visual rows (ascending) and then all N_t text rows of one (layer, sample, KV
+// head) of K or V, copied to the sample's segment of the compacted layer
+// buffer at element offset off. The text rows go first, while the kept
+// indices (epoch-tagged words the top-k writes) are still arriving. A budget
+// or offset outside the buffer is skipped, as in kv_gather_kernel.
+// kidx: LDS for N_v ints.
+__device__ __forceinline__ void fused_gather_unit(const Shape &sh, const PlanPtrs &plan, const FusedWs &fw,
+                                                  const char *src_l, char *dst_l, int b, int g, int plb, int bud,
+                                                  int64_t off, unsigned epoch, int *kidx) {
+  constexpr int NT = kFusedThreads, KW = 16;  // N_v <= KW * NT
+  const int tid = opaque_tid();
+  const int Nv = sh.Nv, n = bud + sh.Nt;
+  const int rb = sh.D * fw.esize;  // bytes per row: 128, 256 or 512
+  if (bud < 0 || bud > Nv || off < 0 || off + (int64_t)sh.Hkv * n * sh.D > fw.cap_elems) return;
+  const int cs = rb == 128 ? 3 : rb == 256 ? 4 : 5;  // log2 of 16-byte pieces per row
+  const char *src = src_l + (size_t)(b * sh.Hkv + g) * sh.S * rb;
+  char *dst = dst_l + (size_t)off * fw.esize + (size_t)g * n * rb;
+  const auto rk = coherent_rsrc(fw.keptrec + (size_t)plb * Nv, (unsigned)(Nv * sizeof(uint64_t)));
+  uint64_t kw[KW];
+#pragma unroll
+  for (int j = 0; j < KW; ++j)
+    kw[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rk, (tid + j * NT) * 8, 0, 16));
+  fused_copy_rows(src, dst, rb, cs, bud, n, sh.S, [&](int i) { return Nv + (i - bud); });
+  unsigned spins = 0;
+  for (;;) {
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < KW; ++j) ok = ok && (tid + j * NT >= bud || (unsigned)(kw[j] >> 32) == epoch);
+    if (ok || spin_expired(spins, plan.status)) break;
+    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int j = 0; j < KW; ++j)
+      kw[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rk, (tid + j * NT) * 8, 0, 16));
+  }
+#pragma unroll
+  for (int j = 0; j < KW; ++j)
+    if (tid + j * NT < bud) kidx[tid + j * NT] = (int)(unsigned)kw[j];
+  __syncthreads();
+  fused_copy_rows(src, dst, rb, cs, 0, bud, sh.S, [&](int i) { return kidx[i]; });
   __syncthreads();  // kidx is reused by the next unit
 }
 
@@ -1309,6 +1379,13 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
       else if (left == 2) fused_pass<Tag, D, 2>(sh, fw, it, rt0, lds, lo, epoch, plan.status, true);
       else fused_pass<Tag, D, 1>(sh, fw, it, rt0, lds, lo, epoch, plan.status, true);
     }
+    // The workgroup of a pair's first item (row group 0, chunk 0) owns its
+    // statistics and top-k, which it runs after its items.
+    if (it.r == 0 && it.c == 0) {
+      if (tid == 0) owed[nowed] = it.plb;
+      ++nowed;
+    }
+
     // Column sums of this item's rows over the KV heads (in order); with one
     // row group they are the chunk's I_v * H_q * N_tk, else the last row group
     // of the chunk adds every group's sums in order.
@@ -1360,7 +1437,8 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
       if (col < ncol) {
         const float a = ivv[j] * inv_rows;
         ivv[j] = a;
-        store_coherent(&plan.iv[(size_t)it.plb * Nv + c0 + col], a);
+        plan.iv[(size_t)it.plb * Nv + c0 + col] = a;
+        store_coherent(&fw.ivrec[(size_t)it.plb * Nv + c0 + col], pack_rec(a, epoch));
         sum += (double)a;
       }
     }
@@ -1378,25 +1456,14 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
     }
     m2 = fused_block_sum_d(m2, redd);
     m3 = fused_block_sum_d(m3, redd);
-    if (tid == 0) {
-      double *mr = fw.mom + ((size_t)it.plb * fw.max_chunks + it.c) * 4;
-      store_coherent(mr + 0, sum);
-      store_coherent(mr + 1, m2);
-      store_coherent(mr + 2, m3);
-      store_coherent(mr + 3, (double)ncol);
+    if (tid < 4) {
+      // the chunk's moments as epoch-tagged 32-bit halves (no ordering needed)
+      const double v = tid == 0 ? sum : tid == 1 ? m2 : tid == 2 ? m3 : (double)ncol;
+      const uint64_t u = __builtin_bit_cast(uint64_t, v), tag = (uint64_t)epoch << 32;
+      uint64_t *mr = fw.mom + ((size_t)it.plb * fw.max_chunks + it.c) * 8 + 2 * tid;
+      store_coherent(mr, tag | (u & 0xffffffffu));
+      store_coherent(mr + 1, tag | (u >> 32));
     }
-    wait_all_memory();
-    __syncthreads();
-    if (tid == 0) {
-      const bool last = counter_add(&fw.cnt_lbc[it.plb], 1u) == (unsigned)it.cp.nchunks - 1u;
-      if (last) {
-        store_coherent(&fw.cnt_lbc[it.plb], 0u);  // reset for the next call
-        owed[nowed] = it.plb;
-      }
-      bcast[0] = last;
-    }
-    __syncthreads();
-    if (uniform(bcast[0])) ++nowed;
   }
 
   // Owed (layer, sample) pairs: first every statistics record (every top-k
@@ -1418,25 +1485,25 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
     __syncthreads();
     const int plb = uniform(owed[o]);
     const int l = plb / B, b = plb - l * B;
-    const float *ivl = plan.iv + (size_t)plb * Nv;
+    const uint64_t *ivl = fw.ivrec + (size_t)plb * Nv;
     int32_t *kp = plan.kept + (size_t)plb * Nv;
+    uint64_t *kr = fw.keptrec + (size_t)plb * Nv;
     double *sts = reinterpret_cast<double *>(lds + lo.sts);
-    auto budget = [&]() { return fused_budget(sh, plan, fw, l, b, epoch, sts, bcast); };
-    if (Nv <= 2048) block_topk<4>(sh, ivl, kp, hist, budget);
-    else if (Nv <= 4096) block_topk<8>(sh, ivl, kp, hist, budget);
-    else block_topk<16>(sh, ivl, kp, hist, budget);
-    if (fw.gather) {
-      // kept indices out: publish the (layer, sample) for compaction
-      wait_all_memory();
-      __syncthreads();
-      if (threadIdx.x == 0) {
+    auto budget = [&]() {
+      const int bud = fused_budget(sh, plan, fw, l, b, epoch, sts, bcast);
+      if (fw.gather && threadIdx.x == 0) {
+        // budget and offset out: compaction of the text rows can start
         const uint64_t tag = (uint64_t)epoch << 32;
         uint64_t *r = fw.grec + (size_t)plb * 4;
         store_coherent(r + 0, tag | (uint64_t)(unsigned)bcast[0]);
         store_coherent(r + 1, tag | (uint64_t)(unsigned)bcast[2]);
         store_coherent(r + 2, tag | (uint64_t)(unsigned)bcast[3]);
       }
-    }
+      return bud;
+    };
+    if (Nv <= 2048) block_topk<4>(sh, ivl, kp, kr, epoch, plan.status, hist, budget);
+    else if (Nv <= 4096) block_topk<8>(sh, ivl, kp, kr, epoch, plan.status, hist, budget);
+    else block_topk<16>(sh, ivl, kp, kr, epoch, plan.status, hist, budget);
   }
 
   // Compaction units (layer, sample, KV head, K or V) by ticket, in
@@ -1475,7 +1542,7 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
       const int64_t off = (int64_t)(((uint64_t)(unsigned)uniform(bcast[3]) << 32) | (uint64_t)(unsigned)uniform(bcast[2]));
       const char *src = static_cast<const char *>(tab.p[(1 + kv) * L + l]);  // k or v
       char *dst = static_cast<char *>(const_cast<void *>(tab.p[(3 + kv) * L + l]));  // k_out or v_out
-      fused_gather_unit(sh, plan, fw, src, dst, b, g, plb, bud, off, kidx);
+      fused_gather_unit(sh, plan, fw, src, dst, b, g, plb, bud, off, epoch, kidx);
     }
   }
 
