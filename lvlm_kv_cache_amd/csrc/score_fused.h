@@ -228,6 +228,27 @@ __device__ __forceinline__ double fused_block_sum_d(double v, double *red) {
   return t;
 }
 
+// Two block-wide double sums at once, each in the order of fused_block_sum_d.
+// red: 2 * kFusedWaves doubles.
+__device__ __forceinline__ void fused_block_sum_d2(double &a, double &b, double *red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  a = wave_sum_d(a);
+  b = wave_sum_d(b);
+  if (lane == 0) {
+    red[wave] = a;
+    red[kFusedWaves + wave] = b;
+  }
+  __syncthreads();
+  double ta = 0.0, tb = 0.0;
+  for (int w = 0; w < kFusedWaves; ++w) {
+    ta += red[w];
+    tb += red[kFusedWaves + w];
+  }
+  __syncthreads();
+  a = ta;
+  b = tb;
+}
+
 // Layer pointers of one launch of the chunked kernel, L entries each: text
 // queries at [0, L), keys at [L, 2L) and, when the launch also compacts,
 // values at [2L, 3L), compacted keys at [3L, 4L) and compacted values at
@@ -252,8 +273,7 @@ struct FusedItem {
 // rows, per KV head, in colsum.
 template <typename Tag, int D, int RTP>
 __device__ __forceinline__ void fused_pass(const Shape &sh, const FusedWs &fw, const FusedItem &it, int rt0,
-                                           unsigned char *lds, const FusedLds &lo, unsigned epoch, int *status,
-                                           bool first) {
+                                           unsigned char *lds, const FusedLds &lo, unsigned epoch, int *status) {
   using E = typename Tag::store_t;
   constexpr int NW = kFusedWaves;
   constexpr int KTMAX = fused_ktmax(RTP);
@@ -450,7 +470,14 @@ __device__ __forceinline__ void fused_pass(const Shape &sh, const FusedWs &fw, c
     wts[gg * RW + rr] = (row < Rg && Z > 0.f) ? exp2_fast(m_own - M) / Z : 0.f;
   }
   __syncthreads();
-  // column sums of this pass over the head's rows; one wave owns a column
+  // column sums of this pass over the head's rows; one wave owns a column.
+  // The row weights go to registers first (the compiler cannot tell that the
+  // column-sum stores leave them alone, so it would read them again per tile).
+  float wrow[RTP][4];
+#pragma unroll
+  for (int rt = 0; rt < RTP; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wrow[rt][i] = wts[g * RW + rt * 16 + grp * 4 + i];
   int cbase = g * W + sub * ktw * 16 + n;
   asm volatile("" : "+v"(cbase));
   float *cs_lane = colsum + cbase;
@@ -461,10 +488,10 @@ __device__ __forceinline__ void fused_pass(const Shape &sh, const FusedWs &fw, c
 #pragma unroll
       for (int rt = 0; rt < RTP; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v += S[s][rt][i] * wts[g * RW + rt * 16 + grp * 4 + i];
+        for (int i = 0; i < 4; ++i) v += S[s][rt][i] * wrow[rt][i];
       v = sum_across_rows(v);
       // text columns are summed too and never read
-      if (grp == 0) cs_lane[s * 16] = first ? v : cs_lane[s * 16] + v;
+      if (grp == 0) cs_lane[s * 16] = v;
     }
   }
   __syncthreads();
@@ -516,7 +543,8 @@ __device__ __forceinline__ int wave_scan_incl(int v) {
 // one LDS histogram, a block scan over the buckets in descending digit order
 // finds the bucket holding the need-th key, and the prefix grows by that
 // digit (one pass usually leaves a few dozen keys, since 11 bits below the
-// first differing bit resolve the scores to about 1/64 of an octave). The
+// first differing bit resolve the scores to about 1/64 of an octave); the
+// first pass's counts and their scan come before the budget is known. The
 // keys left are then copied to LDS and each is ranked against the others
 // directly; the one of rank need - 1 is the threshold T. Kept: every key > T
 // plus the lowest-index keys equal to T up to the count still needed, in
@@ -593,23 +621,42 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const uint64_t *iv_l
   int hb = diff ? 31 - __clz((int)diff) : -1;  // highest bit in which keys can differ
   unsigned mask = (hb < 0) ? 0xffffffffu : (hb >= 31) ? 0u : ~((2u << hb) - 1u);
   unsigned prefix = kmin & mask;
-  // the first radix pass does not depend on the budget: count it before
-  // asking for the budget (whose wait it overlaps)
-  bool counted = hb >= 0 && Nv > kTopkRankCap;
-  if (counted) {
+  // The first radix pass does not depend on the budget: its counts and their
+  // scan over the buckets (descending digits) are done before asking for the
+  // budget, whose wait they overlap; only the choice of bucket waits for it.
+  // Thread t: the buckets of descending positions t * BPT .. t * BPT + BPT - 1.
+  const bool first = hb >= 0 && Nv > kTopkRankCap;
+  int c0[BPT], ct0 = 0, above0 = 0;
+  if (first) {
     const int width = min(kTopkDigitBits, hb + 1);
     const int shift = hb + 1 - width;
     const unsigned dmask = (1u << width) - 1u;
+    const int nb = 1 << width;
 #pragma unroll
     for (int p = 0; p < PER; ++p)
       if (p * NT + tid < Nv) atomicAdd(&hist[(key[p] >> shift) & dmask], 1u);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int q = tid * BPT + j;
+      c0[j] = 0;
+      if (q < nb) {
+        unsigned *h = &hist[nb - 1 - q];
+        c0[j] = (int)*h;
+        *h = 0u;  // zero again for the next pass or call
+      }
+      ct0 += c0[j];
+    }
+    const int incl = wave_scan_incl(ct0);
+    if (lane == 63) wsum[0][wave] = incl;
+    __syncthreads();
+    above0 = incl - ct0;
+    for (int w = 0; w < wave; ++w) above0 += wsum[0][w];
   }
   int kbud = get_budget();  // block-wide, with barriers
   if (kbud < 0) kbud = 0;
   if (kbud > Nv) kbud = Nv;
   if (kbud <= 0 || kbud >= Nv) {
-    if (counted)  // leave the histogram zero (the budget's barriers ordered the counts before this)
-      for (int i = tid; i < kTopkBuckets; i += NT) hist[i] = 0u;
     if (kbud >= Nv)
       for (int i = tid; i < Nv; i += NT) {
         kept[i] = i;
@@ -620,19 +667,41 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const uint64_t *iv_l
   int need = kbud;  // keys still to take among those matching the prefix
   int nmatch = Nv;  // keys matching the prefix
   int par = 0;
+  if (first) {
+    const int width = min(kTopkDigitBits, hb + 1);
+    const int shift = hb + 1 - width;
+    const unsigned dmask = (1u << width) - 1u;
+    const int nb = 1 << width;
+    if (ct0 > 0 && above0 < need && above0 + ct0 >= need) {
+      int above = above0;
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) {
+        if (above + c0[j] >= need) {
+          selv[0][0] = nb - 1 - (tid * BPT + j);
+          selv[0][1] = above;
+          selv[0][2] = c0[j];
+          break;
+        }
+        above += c0[j];
+      }
+    }
+    __syncthreads();
+    prefix |= (unsigned)uniform(selv[0][0]) << shift;
+    mask |= dmask << shift;
+    need -= uniform(selv[0][1]);
+    nmatch = uniform(selv[0][2]);
+    hb -= width;
+    par = 1;
+  }
   while (hb >= 0 && nmatch > kTopkRankCap) {
     const int width = min(kTopkDigitBits, hb + 1);
     const int shift = hb + 1 - width;
     const unsigned dmask = (1u << width) - 1u;
     const int nb = 1 << width;
-    if (!counted) {
 #pragma unroll
-      for (int p = 0; p < PER; ++p)
-        if (p * NT + tid < Nv && (key[p] & mask) == prefix) atomicAdd(&hist[(key[p] >> shift) & dmask], 1u);
-    }
-    counted = false;
+    for (int p = 0; p < PER; ++p)
+      if (p * NT + tid < Nv && (key[p] & mask) == prefix) atomicAdd(&hist[(key[p] >> shift) & dmask], 1u);
     __syncthreads();
-    // thread t: the buckets of descending positions t * BPT .. t * BPT + BPT - 1
     int c[BPT], ct = 0;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
@@ -941,14 +1010,16 @@ __device__ __forceinline__ void fused_elite_sets_h(const Shape &sh, const PlanPt
       for (int u = 0; u < U; ++u) cnt[u] = 0;
       for (int w = 0; w < ntw; ++w) {
         const int j = w * 64 + lane;
+        // the U values first: an LDS store in between would hold up each load
+        float x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = stage[(size_t)min(q0 + u, nlb - 1) * Nt + min(j, Nt - 1)];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int q = q0 + u;
           if (q < nlb) {
-            const int lb = lb0 + q;
-            const bool in = j < Nt && stage[(size_t)q * Nt + j] >= thr[u];
-            const unsigned long long mk = __ballot(in);
-            if (lane == 0) emask[(size_t)lb * ntw + w] = mk;
+            const unsigned long long mk = __ballot(j < Nt && x[u] >= thr[u]);
+            if (lane == 0) emask[(size_t)(lb0 + q) * ntw + w] = mk;
             cnt[u] += __popcll(mk);
           }
         }
@@ -1286,7 +1357,6 @@ __device__ __forceinline__ void fused_gather_unit(const Shape &sh, const PlanPtr
 #pragma unroll
     for (int j = 0; j < KW; ++j) ok = ok && (tid + j * NT >= bud || (unsigned)(kw[j] >> 32) == epoch);
     if (ok || spin_expired(spins, plan.status)) break;
-    __builtin_amdgcn_s_sleep(2);
 #pragma unroll
     for (int j = 0; j < KW; ++j)
       kw[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rk, (tid + j * NT) * 8, 0, 16));
@@ -1305,7 +1375,7 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
   extern __shared__ __attribute__((aligned(16))) float lds_f[];
   unsigned char *lds = reinterpret_cast<unsigned char *>(lds_f);
   __shared__ int wtot[4 * kFusedWaves];
-  __shared__ double redd[kFusedWaves];
+  __shared__ double redd[2 * kFusedWaves];
   __shared__ int bcast[4];
   __shared__ int hdr[2];
   const int tid = threadIdx.x;
@@ -1374,10 +1444,10 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
     __syncthreads();
     {
       const int rt0 = it.r * kFusedRtMax, left = it.cp.rtg - rt0;
-      if (left >= 4) fused_pass<Tag, D, 4>(sh, fw, it, rt0, lds, lo, epoch, plan.status, true);
-      else if (left == 3) fused_pass<Tag, D, 3>(sh, fw, it, rt0, lds, lo, epoch, plan.status, true);
-      else if (left == 2) fused_pass<Tag, D, 2>(sh, fw, it, rt0, lds, lo, epoch, plan.status, true);
-      else fused_pass<Tag, D, 1>(sh, fw, it, rt0, lds, lo, epoch, plan.status, true);
+      if (left >= 4) fused_pass<Tag, D, 4>(sh, fw, it, rt0, lds, lo, epoch, plan.status);
+      else if (left == 3) fused_pass<Tag, D, 3>(sh, fw, it, rt0, lds, lo, epoch, plan.status);
+      else if (left == 2) fused_pass<Tag, D, 2>(sh, fw, it, rt0, lds, lo, epoch, plan.status);
+      else fused_pass<Tag, D, 1>(sh, fw, it, rt0, lds, lo, epoch, plan.status);
     }
     // The workgroup of a pair's first item (row group 0, chunk 0) owns its
     // statistics and top-k, which it runs after its items.
@@ -1454,8 +1524,7 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
         m3 += d * d * d;
       }
     }
-    m2 = fused_block_sum_d(m2, redd);
-    m3 = fused_block_sum_d(m3, redd);
+    fused_block_sum_d2(m2, m3, redd);
     if (tid < 4) {
       // the chunk's moments as epoch-tagged 32-bit halves (no ordering needed)
       const double v = tid == 0 ? sum : tid == 1 ? m2 : tid == 2 ? m3 : (double)ncol;
