@@ -96,6 +96,26 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "dispatches": 5}))
 
 
+def copy_ceiling_gbps(mib=512, reps=10):
+    """Bandwidth of a plain device-to-device copy (read + write bytes per
+    second): the practical ceiling the pass is also compared with."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    return 2 * n / t / 1e9
+
+
 def algorithmic_bytes(w, n_elite, budget):
     """Bytes the method must move in one pass (reads and writes), from the
     measured elite counts and budgets. Dropped visual V rows are never read."""
@@ -220,7 +240,9 @@ def main():
         for i in range(a.steps):
             bound[i % ncopy].run(events=ev[i])
         torch.cuda.synchronize()
-        kern_us = {names[0]: 1e3 * sum(e[0].elapsed_time(e[1]) for e in ev) / a.steps}
+        per_step = [1e3 * e[0].elapsed_time(e[1]) for e in ev]
+        kern_us = {names[0]: sum(per_step) / a.steps}
+        launch_pct = {q: float(np.percentile(per_step, q)) for q in (10, 50, 90)}
     else:
         names = _lib.PLAN_KERNELS + _lib.COMPRESS_KERNELS
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(_lib.PLAN_KERNELS) + 1)] +
@@ -241,6 +263,17 @@ def main():
                 kern[n] += p[j].elapsed_time(p[j + 1])
             kern["kv_gather"] += c[0].elapsed_time(c[1])
         kern_us = {n: 1e3 * t / a.steps for n, t in kern.items()}
+        launch_pct = None
+
+    # Hot: the same steps on one input copy only (K partly cache-resident).
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(a.steps):
+        bound[0].run() if fused else step(0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_hot = e0.elapsed_time(e1) / a.steps
+    copy_gbps = copy_ceiling_gbps()
 
     tokens = w.L * w.B * w.Nv
     value = tokens / (ms * 1e-3)
@@ -275,8 +308,14 @@ def main():
                      "unit": "GB/s", "frac": dom_gbps / PEAK_HBM_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": kern_us[dom]},
         "kernel_us": kern_us,
+        "launch_us_p10_p50_p90": None if launch_pct is None else [launch_pct[10], launch_pct[50], launch_pct[90]],
+        "hot_ms_per_step": ms_hot,
+        "copy_ceiling_gbps": copy_gbps,
+        "pass_frac_of_copy_ceiling": gbps / copy_gbps,
         "elite_mean": float(n_elite.mean()),
+        "elite_hist": {int(k): int(v) for k, v in zip(*np.unique(n_elite, return_counts=True))},
         "budget_sum": int(budget.sum()),
+        "budget_min_mean_max": [int(budget.min()), float(budget.mean()), int(budget.max())],
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, a.cpu_seconds)
