@@ -214,7 +214,11 @@ template <int PER> __device__ __forceinline__ void wait_tiles(int t) {
     case 0: wait_vmcnt<0>(); break;
     case 1: wait_vmcnt<PER>(); break;
     case 2: wait_vmcnt<2 * PER>(); break;
-    default: wait_vmcnt<3 * PER>(); break;
+    case 3: wait_vmcnt<3 * PER>(); break;
+    case 4: wait_vmcnt<(4 * PER < 63 ? 4 * PER : 63)>(); break;
+    case 5: wait_vmcnt<(5 * PER < 63 ? 5 * PER : 63)>(); break;
+    case 6: wait_vmcnt<(6 * PER < 63 ? 6 * PER : 63)>(); break;
+    default: wait_vmcnt<(7 * PER < 63 ? 7 * PER : 63)>(); break;
   }
 }
 

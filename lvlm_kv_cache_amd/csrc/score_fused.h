@@ -111,6 +111,8 @@ struct FusedWs {
   unsigned *epoch;        // [1] calls so far
   unsigned *exitc;        // [1] workgroups finished in this call
   uint64_t *parts;        // [L*B*Hkv][N_t] KV-head parts of pbar, (value | epoch << 32)
+  uint64_t *erec;         // [L*B][erec_stride] elite size, mask halves, each | epoch << 32
+  int erec_stride;        // words per elite record: 1 + 2 * ceil(N_t / 64)
   unsigned *cnt_chunk;    // [L*B][max_chunks] finished row groups per chunk
   uint64_t *xrec;         // [L*B][rec_stride][2] (row max | epoch << 32), (row sum | epoch << 32)
   uint64_t *mom;          // [L*B][max_chunks][8] halves of chunk sum, M2, M3, count, each | epoch << 32
@@ -130,14 +132,21 @@ struct FusedWs {
   uint64_t *grec;         // [L*B][4] budget, out_off halves, each | epoch << 32
 };
 
+// Key tiles in flight per wave: about 128 KB of LDS ring per workgroup. The
+// stream of a CU is bound by the bytes it has in flight over the load
+// latency, and this is the most the LDS leaves room for.
+__host__ __device__ constexpr int fused_ring_depth(int tile_bytes) {
+  return tile_bytes >= 8192 ? 2 : tile_bytes >= 4096 ? 4 : 8;
+}
+
 // Dynamic LDS of cross_score_fused_kernel (byte offsets, 16-byte aligned).
 // ring: the key tiles of the waves, also the staging of pbar before the
-// items and the top-k's histogram after them; ntk / emask: the elite count
-// and the elite set (a bit per text token) of every (layer, sample); sts: the
+// items and the top-k's histogram after them; ntk: the elite count of every
+// (layer, sample); sts: the
 // s_t and s_k a budget needs; items / owed: this workgroup's work items and
 // the (layer, sample) pairs whose top-k it owes.
 struct FusedLds {
-  int ring, el, colsum, red, mloc, wts, items, owed, ntk, emask, sts, total;
+  int ring, el, colsum, red, mloc, wts, items, owed, ntk, sts, total;
 };
 __host__ __device__ inline int fused_align16(int x) { return (x + 15) & ~15; }
 __host__ __device__ inline int fused_words64(int Nt) { return (Nt + 63) >> 6; }
@@ -165,8 +174,6 @@ __host__ __device__ inline FusedLds fused_lds_layout(int tile_bytes, int ring_de
   o += fused_align16(kFusedMaxItems * 4);
   f.ntk = o;
   o += fused_align16(LB * 4);
-  f.emask = o;
-  o += fused_align16(LB * fused_words64(Nt) * 8);
   f.sts = o;
   o += fused_align16((LB + 8) * 16);  // reads run up to 8 entries past each array
   f.total = o;
@@ -279,7 +286,7 @@ __device__ __forceinline__ void fused_pass(const Shape &sh, const FusedWs &fw, c
   constexpr int KTMAX = fused_ktmax(RTP);
   constexpr int kTileBytes = 16 * D * Tag::kBytes;
   constexpr int kDma = kTileBytes / 1024;
-  constexpr int kRing = (kTileBytes <= 4096) ? 3 : 2;
+  constexpr int kRing = fused_ring_depth(kTileBytes);
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, grp = lane >> 4;
   const int Hkv = sh.Hkv, G = sh.G, Nv = sh.Nv;
@@ -927,135 +934,151 @@ __device__ __forceinline__ int ceil_div_small(int a, int b) {
   return q + (q * b < a ? 1 : 0);
 }
 
-// Before the items, every workgroup: pbar of every (layer, sample) as the sum
-// of its KV-head parts in ascending head order (the "Elite Observation
-// Window" Att equation summed over heads), the elite set
-// { j : pbar_j >= alpha max pbar } as a bit mask per 64 text tokens in emask,
-// and its size, clamped to the elite cap, in ntk. Workgroup lb % P also
-// writes the plan's elite list and count of lb and flags an elite set above
-// the cap. stage: LDS for stage_floats floats of pbar (a batch of pairs).
-// HKV = n_kv_heads: every thread keeps 32 part loads in flight.
-template <int HKV>
-__device__ __forceinline__ void fused_elite_sets_h(const Shape &sh, const PlanPtrs &plan, const uint64_t *parts,
-                                                   unsigned epoch, int me,
-                                                   int P, float *stage, int stage_floats, int *ntk,
-                                                   unsigned long long *emask) {
-  constexpr int NT = kFusedThreads, NW = kFusedWaves, R = 32 / HKV, U = 4;
+// Elite set of one (layer, sample) lb, block-wide, by the workgroup that
+// computed its first KV-head part: pbar = the sum of the KV-head parts in
+// ascending head order (the "Elite Observation Window" Att equation summed
+// over heads; the parts are epoch-tagged words, read again until all carry
+// this call's epoch), the set { j : pbar_j >= alpha max pbar } (the k
+// equation) as a bit mask per 64 text tokens, and its size. Published as
+// epoch-tagged words: erec[lb] = [size, then each mask word as two 32-bit
+// halves]; also the plan's elite list and count, and the overflow flag when
+// the set exceeds the elite cap. N_t <= 1024 (two entries per thread).
+__device__ __forceinline__ void fused_elite_merge(const Shape &sh, const PlanPtrs &plan, const FusedWs &fw, int lb,
+                                                  unsigned epoch, int *wtot, float *red) {
+  constexpr int NT = kFusedThreads, NW = kFusedWaves, E = 2;
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
-  const int Nt = sh.Nt, LB = sh.L * sh.B;
+  const int Nt = sh.Nt, Hkv = sh.Hkv;
+  const auto rp = coherent_rsrc(fw.parts + (size_t)lb * Hkv * Nt, (unsigned)((size_t)Hkv * Nt * sizeof(uint64_t)));
+  // entry j = tid + e * NT: every load issued before any is checked
+  uint64_t w[E][8];
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const int j = tid + e * NT;
+      const unsigned off = (j < Nt && g < Hkv) ? (unsigned)(((size_t)g * Nt + j) * sizeof(uint64_t)) : 0xfffffff0u;
+      w[e][g] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rp, (int)off, 0, 16));
+    }
+  unsigned spins = 0;
+  for (;;) {
+    bool ok = true;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int g = 0; g < 8; ++g) ok = ok && (tid + e * NT >= Nt || g >= Hkv || (unsigned)(w[e][g] >> 32) == epoch);
+    if (ok || spin_expired(spins, plan.status)) break;
+    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const int j = tid + e * NT;
+        const unsigned off = (j < Nt && g < Hkv) ? (unsigned)(((size_t)g * Nt + j) * sizeof(uint64_t)) : 0xfffffff0u;
+        w[e][g] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rp, (int)off, 0, 16));
+      }
+  }
+  float pb[E];
+  float m = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float a = 0.f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+      if (g < Hkv) a += __uint_as_float((unsigned)w[e][g]);
+    pb[e] = a;
+    if (tid + e * NT < Nt) m = fmaxf(m, a);
+  }
+  m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = red[0];
+  for (int u = 1; u < NW; ++u) m = fmaxf(m, red[u]);
+  const float thr = sh.alpha * m;
+  // word e * NW + wave holds tokens 64 (e * NW + wave) + lane
+  unsigned long long mk[E];
+  int cnt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    mk[e] = __ballot(tid + e * NT < Nt && pb[e] >= thr);
+    cnt += __popcll(mk[e]);
+  }
+  // words before this wave's, in token order: word (e, wave) comes after all
+  // words of pass e' < e and the words (e, wave' < wave)
+  if (lane == 0)
+#pragma unroll
+    for (int e = 0; e < E; ++e) wtot[e * NW + wave] = __popcll(mk[e]);
+  __syncthreads();
   const int ntw = fused_words64(Nt);
-  const int batch = max(1, stage_floats / Nt);  // (layer, sample) pairs per batch
-  const auto rp = coherent_rsrc(parts, (unsigned)((size_t)LB * HKV * Nt * sizeof(uint64_t)));
+  uint64_t *rec = fw.erec + (size_t)lb * fw.erec_stride;
+  const uint64_t tag = (uint64_t)epoch << 32;
+  int total = 0;
+  for (int u = 0; u < E * NW; ++u) total += wtot[u];
   const unsigned long long lt = (1ull << lane) - 1ull;
-  for (int lb0 = 0; lb0 < LB; lb0 += batch) {
-    const int nlb = min(batch, LB - lb0);
-    const int n = nlb * Nt;
-    for (int e0 = 0; e0 < n; e0 += R * NT) {
-      // every load issued before any is used (an entry past the batch reads
-      // past the buffer's bounds, which returns 0 without a memory access);
-      // a word not yet tagged with this call's epoch is read again
-      unsigned off[R][HKV];
-      uint64_t part[R][HKV];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int e = e0 + r * NT + tid;
-        const int q = ceil_div_small(e + 1, Nt) - 1, j = e - q * Nt;  // e / Nt, e % Nt
-        const unsigned base = (unsigned)((((size_t)(lb0 + q) * HKV) * Nt + j) * sizeof(uint64_t));
-#pragma unroll
-        for (int g = 0; g < HKV; ++g) {
-          off[r][g] = e < n ? base + (unsigned)(g * Nt * sizeof(uint64_t)) : 0xfffffff0u;
-          part[r][g] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rp, (int)off[r][g], 0, 16));
-        }
-      }
-      unsigned spins = 0;
-      for (;;) {
-        bool ok = true;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int g = 0; g < HKV; ++g) ok = ok && (off[r][g] == 0xfffffff0u || (unsigned)(part[r][g] >> 32) == epoch);
-        if (ok || spin_expired(spins, plan.status)) break;
-        __builtin_amdgcn_s_sleep(2);
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int g = 0; g < HKV; ++g)
-            if (off[r][g] != 0xfffffff0u && (unsigned)(part[r][g] >> 32) != epoch)
-              part[r][g] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rp, (int)off[r][g], 0, 16));
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int e = e0 + r * NT + tid;
-        float a = 0.f;
-#pragma unroll
-        for (int g = 0; g < HKV; ++g) a += __uint_as_float((unsigned)part[r][g]);
-        if (e < n) stage[e] = a;
-      }
-    }
-    __syncthreads();
-    // U pairs per wave at a time: their reduction chains interleave
-    for (int q0 = wave * U; q0 < nlb; q0 += NW * U) {
-      float thr[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int q = min(q0 + u, nlb - 1);
-        float m = -INFINITY;
-        for (int j = lane; j < Nt; j += 64) m = fmaxf(m, stage[(size_t)q * Nt + j]);
-        thr[u] = m;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) thr[u] = sh.alpha * wave_max(thr[u]);
-      int cnt[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) cnt[u] = 0;
-      for (int w = 0; w < ntw; ++w) {
-        const int j = w * 64 + lane;
-        // the U values first: an LDS store in between would hold up each load
-        float x[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) x[u] = stage[(size_t)min(q0 + u, nlb - 1) * Nt + min(j, Nt - 1)];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int q = q0 + u;
-          if (q < nlb) {
-            const unsigned long long mk = __ballot(j < Nt && x[u] >= thr[u]);
-            if (lane == 0) emask[(size_t)(lb0 + q) * ntw + w] = mk;
-            cnt[u] += __popcll(mk);
-          }
-        }
-      }
-      if (lane == 0)
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int q = q0 + u;
-          if (q < nlb) ntk[lb0 + q] = cnt[u] < sh.cap ? cnt[u] : sh.cap;
-        }
-    }
-    __syncthreads();  // the stage is free again; ntk and emask are complete
-  }
-  // the plan's elite lists and counts of pairs me, me + P, ...: wave w takes
-  // pair me + w P, lane j of word i holds token 64 i + j
-  for (int lb = me + wave * P; lb < LB; lb += NW * P) {
-    int cnt = 0;
-    for (int w = 0; w < ntw; ++w) {
-      const unsigned long long mk = emask[(size_t)lb * ntw + w];
-      if ((mk >> lane) & 1ull) plan.elite[(size_t)lb * Nt + cnt + __popcll(mk & lt)] = w * 64 + lane;
-      cnt += __popcll(mk);
-    }
-    if (lane == 0) {
-      plan.n_elite[lb] = cnt;
-      if (cnt > sh.cap) atomicOr(plan.status, AIRCACHE_DEV_ELITE_OVERFLOW);
+  for (int e = 0; e < E; ++e) {
+    const int word = e * NW + wave;
+    int before = 0;
+    for (int u = 0; u < word; ++u) before += wtot[u];
+    if ((mk[e] >> lane) & 1ull) plan.elite[(size_t)lb * Nt + before + __popcll(mk[e] & lt)] = word * 64 + lane;
+    if (word < ntw && lane < 2) {
+      const unsigned half = lane == 0 ? (unsigned)mk[e] : (unsigned)(mk[e] >> 32);
+      store_coherent(&rec[1 + 2 * word + lane], tag | (uint64_t)half);
     }
   }
+  if (tid == 0) {
+    store_coherent(&rec[0], tag | (uint64_t)(unsigned)total);
+    plan.n_elite[lb] = total;
+    if (total > sh.cap) atomicOr(plan.status, AIRCACHE_DEV_ELITE_OVERFLOW);
+  }
+  __syncthreads();  // wtot and red are free again
 }
-__device__ __forceinline__ void fused_elite_sets(const Shape &sh, const PlanPtrs &plan, const uint64_t *parts,
-                                                 unsigned epoch, int me, int P, float *stage, int stage_floats,
-                                                 int *ntk, unsigned long long *emask) {
-  switch (sh.Hkv) {
-    case 1: fused_elite_sets_h<1>(sh, plan, parts, epoch, me, P, stage, stage_floats, ntk, emask); break;
-    case 2: fused_elite_sets_h<2>(sh, plan, parts, epoch, me, P, stage, stage_floats, ntk, emask); break;
-    case 4: fused_elite_sets_h<4>(sh, plan, parts, epoch, me, P, stage, stage_floats, ntk, emask); break;
-    default: fused_elite_sets_h<8>(sh, plan, parts, epoch, me, P, stage, stage_floats, ntk, emask); break;
+
+// Every workgroup: the elite count of every (layer, sample), clamped to the
+// elite cap, into ntk (LDS), from the merges' epoch-tagged records.
+__device__ __forceinline__ void fused_elite_counts(const Shape &sh, const FusedWs &fw, unsigned epoch, int *status,
+                                                   int *ntk) {
+  const int LB = sh.L * sh.B;
+  const auto rr = coherent_rsrc(fw.erec, (unsigned)((size_t)LB * fw.erec_stride * sizeof(uint64_t)));
+  for (int lb = opaque_tid(); lb < LB; lb += kFusedThreads) {
+    const int off = (int)((size_t)lb * fw.erec_stride * sizeof(uint64_t));
+    uint64_t v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, 16));
+    unsigned spins = 0;
+    while ((unsigned)(v >> 32) != epoch) {
+      if (spin_expired(spins, status)) break;
+      __builtin_amdgcn_s_sleep(2);
+      v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, 16));
+    }
+    const int t = (int)(unsigned)v;
+    ntk[lb] = t < sh.cap ? t : sh.cap;
+  }
+  __syncthreads();
+}
+
+// The elite list of lb, ascending, into el (LDS, ntk entries) from the
+// merge's mask words. scr: LDS for N_t / 64 mask words.
+__device__ __forceinline__ void fused_elite_list(const Shape &sh, const FusedWs &fw, int lb, int ntk, unsigned epoch,
+                                                 int *status, int *el, unsigned long long *scr) {
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int ntw = fused_words64(sh.Nt);
+  const auto rr = coherent_rsrc(fw.erec + (size_t)lb * fw.erec_stride, (unsigned)(fw.erec_stride * sizeof(uint64_t)));
+  if (tid < 2 * ntw) {
+    const int off = (1 + tid) * (int)sizeof(uint64_t);
+    uint64_t v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, 16));
+    unsigned spins = 0;
+    while ((unsigned)(v >> 32) != epoch) {
+      if (spin_expired(spins, status)) break;
+      __builtin_amdgcn_s_sleep(2);
+      v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, 16));
+    }
+    reinterpret_cast<unsigned *>(scr)[tid] = (unsigned)v;  // little-endian: halves form the word
+  }
+  __syncthreads();
+  for (int w = wave; w < ntw; w += kFusedWaves) {
+    int base = 0;
+    for (int u = 0; u < w; ++u) base += __popcll(scr[u]);
+    const unsigned long long mk = scr[w];
+    const int pos = base + __popcll(mk & ((1ull << lane) - 1ull));
+    if (((mk >> lane) & 1ull) && pos < ntk) el[pos] = w * 64 + lane;
   }
 }
 
@@ -1376,6 +1399,7 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
   unsigned char *lds = reinterpret_cast<unsigned char *>(lds_f);
   __shared__ int wtot[4 * kFusedWaves];
   __shared__ double redd[2 * kFusedWaves];
+  __shared__ float redf[kFusedWaves];
   __shared__ int bcast[4];
   __shared__ int hdr[2];
   const int tid = threadIdx.x;
@@ -1388,7 +1412,6 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
   int *item_list = reinterpret_cast<int *>(lds + lo.items);
   int *owed = reinterpret_cast<int *>(lds + lo.owed);
   int *ntk_l = reinterpret_cast<int *>(lds + lo.ntk);
-  unsigned long long *emask = reinterpret_cast<unsigned long long *>(lds + lo.emask);
 
   // Phase 0: the KV-head parts of pbar, items (layer, sample, KV head) me,
   // me + P, ..., published as epoch-tagged words (no counter: the readers
@@ -1404,7 +1427,13 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
     fused_elite_part<Tag, D>(sh, tab, lb, g, fw.parts + (size_t)t * sh.Nt, epoch, lds_f);
     __syncthreads();  // the LDS is free again
   }
-  fused_elite_sets(sh, plan, fw.parts, epoch, me, P, lds_f + lo.ring / 4, (lo.el - lo.ring) / 4, ntk_l, emask);
+  // merges of the pairs whose first KV-head part this workgroup computed, then
+  // every pair's elite count
+  for (int t = me; t < LB * sh.Hkv; t += P) {
+    const int lb = t / sh.Hkv;
+    if (t == lb * sh.Hkv) fused_elite_merge(sh, plan, fw, lb, epoch, wtot, redf);
+  }
+  fused_elite_counts(sh, fw, epoch, plan.status, ntk_l);
   fused_schedule(sh, ntk_l, me, P, item_list, hdr, wtot);
   __syncthreads();
   const int kcap = uniform(hdr[0]);
@@ -1433,14 +1462,9 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
     it.k = tab.p[L + it.l];
     int *el = reinterpret_cast<int *>(lds + lo.el);
     __syncthreads();  // the previous item is done with the LDS
-    // elite list of the item's (layer, sample) from its bit mask, ascending
-    for (int w = wave; w < ntw; w += kFusedWaves) {
-      int base = 0;
-      for (int u = 0; u < w; ++u) base += __popcll(emask[(size_t)it.plb * ntw + u]);
-      const unsigned long long mk = emask[(size_t)it.plb * ntw + w];
-      const int pos = base + __popcll(mk & ((1ull << lane) - 1ull));
-      if (((mk >> lane) & 1ull) && pos < it.ntk) el[pos] = w * 64 + lane;
-    }
+    // elite list of the item's (layer, sample), ascending
+    fused_elite_list(sh, fw, it.plb, it.ntk, epoch, plan.status, el,
+                     reinterpret_cast<unsigned long long *>(lds + lo.mloc));
     __syncthreads();
     {
       const int rt0 = it.r * kFusedRtMax, left = it.cp.rtg - rt0;
