@@ -770,7 +770,19 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const uint64_t *iv_l
     if (tid < nmatch) {
       const uint2 me = cand[tid];
       int gt = 0, before = 0, eq = 0;
-      for (int i = 0; i < nmatch; ++i) {
+      int i = 0;
+      for (; i + 4 <= nmatch; i += 4) {
+        uint2 o[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[u] = cand[i + u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          gt += (o[u].x > me.x) ? 1 : 0;
+          eq += (o[u].x == me.x) ? 1 : 0;
+          before += (o[u].x > me.x || (o[u].x == me.x && o[u].y < me.y)) ? 1 : 0;
+        }
+      }
+      for (; i < nmatch; ++i) {
         const uint2 o = cand[i];
         gt += (o.x > me.x) ? 1 : 0;
         eq += (o.x == me.x) ? 1 : 0;
