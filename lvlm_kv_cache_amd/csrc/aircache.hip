@@ -1091,8 +1091,8 @@ constexpr size_t kMaxLds = 160 * 1024;
 struct Config {
   Shape sh;
   size_t off_cnt, off_stats, off_e, off_part, ws_bytes;
-  size_t off_xrec, off_mom, off_srec, off_part_rg, off_cnt_chunk, off_ivrec, off_keptrec, off_grec, off_parts64,
-      off_erec;
+  size_t off_xrec, off_mom, off_srec, off_part_rg, off_cnt_chunk, off_ivrec, off_keptrec, off_grec,
+      off_parts64, off_erec, off_hint;
   size_t tile_bytes;   // bytes of one 16-key tile
   bool run_fused;      // aircache_run compacts inside the chunked launch
   size_t off_cnt_elite, off_pbar, off_sched;
@@ -1220,8 +1220,7 @@ int make_config(const aircache_desc *d, Config *cfg) {
     cfg->flds = fused_lds_layout(tb, fused_ring_depth(tb), s.cap, s.Hkv, lb, s.Nt);
     // 4 KB for the kernel's static LDS (2.5 KB)
     const bool lds_ok = (size_t)cfg->flds.total + 4096 <= kMaxLds &&
-                        (size_t)(s.G > 1 ? s.G : 1) * s.Nt * sizeof(float) <= (size_t)cfg->flds.total &&  // KV-head parts
-                        (size_t)s.Nt * sizeof(float) <= (size_t)(cfg->flds.el - cfg->flds.ring);       // pbar staging
+                        (size_t)(s.G > 1 ? s.G : 1) * s.Nt * sizeof(float) <= (size_t)cfg->flds.total;  // one head's logits
     // the schedule is worked out by one wave: at most 8 (layer, sample) pairs per lane
     const bool items_ok = lb <= 512 && (long long)lb * maxc * maxrg <= (long long)kFusedMaxItems * kFusedTargetCus &&
                           maxc <= 64;
@@ -1257,9 +1256,11 @@ int make_config(const aircache_desc *d, Config *cfg) {
     cfg->off_ivrec = cfg->off_cnt_chunk + align_up(lbs * (size_t)cfg->max_chunks * sizeof(unsigned));
     cfg->off_keptrec = cfg->off_ivrec + align_up(lbs * (size_t)s.Nv * sizeof(uint64_t));
     cfg->off_grec = cfg->off_keptrec + align_up(lbs * (size_t)s.Nv * sizeof(uint64_t));
+    // elite-window parts: up to one per KV head (the launch picks how many)
     cfg->off_parts64 = cfg->off_grec + align_up(lbs * 32);
     cfg->off_erec = cfg->off_parts64 + align_up(lbs * (size_t)s.Hkv * s.Nt * sizeof(uint64_t));
-    cfg->off_part_rg = cfg->off_erec + align_up(lbs * (size_t)(1 + 2 * fused_words64(s.Nt)) * sizeof(uint64_t));
+    cfg->off_hint = cfg->off_erec + align_up(lbs * (size_t)(1 + 2 * fused_words64(s.Nt)) * sizeof(uint64_t));
+    cfg->off_part_rg = cfg->off_hint + align_up((size_t)kFusedHintSlots * sizeof(uint64_t));
     // row-group partial sums only when some elite count can need two row groups
     const size_t part_rg = cfg->max_rg > 1 ? lbs * (size_t)cfg->max_chunks * cfg->max_rg * cfg->wmax * sizeof(float) : 0;
     cfg->ws_bytes = cfg->off_part_rg + align_up(part_rg);
@@ -1448,7 +1449,13 @@ int launch_chunked(const Config &cfg, const LayerTable &qt, const LayerTable &kt
   fw.cnt_chunk = ws.cnt_chunk;
   fw.part = reinterpret_cast<float *>(p + cfg.off_part_rg);
   fw.parts = reinterpret_cast<uint64_t *>(p + cfg.off_parts64);
+  // parts per (layer, sample): the most KV-head groups (a divisor of H_kv)
+  // that still give every part a workgroup of its own; the parts of one
+  // (layer, sample) are loaded by as many CUs
+  fw.npp = 1;
+  while (fw.npp < s.Hkv && (long long)s.L * s.B * fw.npp * 2 <= grid) fw.npp *= 2;
   fw.erec = reinterpret_cast<uint64_t *>(p + cfg.off_erec);
+  fw.hint = reinterpret_cast<uint64_t *>(p + cfg.off_hint);
   fw.erec_stride = 1 + 2 * fused_words64(s.Nt);
   fw.gticket = fw.exitc + 1;
   fw.grec = reinterpret_cast<uint64_t *>(p + cfg.off_grec);

@@ -6,28 +6,35 @@
 // "Elite Observation Window" (the A_vtk and I_v equations) and "Layer-wise KV
 // Cache Budget Allocation" (the s_t, s_k and r_hat equations).
 //
+// Before the items: one workgroup per (layer, sample) forms its elite set
+// and publishes the size and bit mask; every workgroup reads every size and
+// works out the same chunk schedule by itself. Meanwhile each wave loads the
+// first key tiles of the item it took in the previous call into its LDS ring
+// (used only if it gets that item again).
+//
 // Work item = (layer, sample, row group, column chunk): a workgroup takes a
 // run of columns (visual keys, then the elite text keys) of every KV head of
 // one (layer, sample) and up to four 16-row tiles of elite-query rows per KV
 // head. Its logits stay in registers. The exact softmax normaliser of a row
 // needs every chunk's contribution, so the chunks of one row group swap
-// per-row (max, sum) pairs through epoch-tagged records (no counter round
-// trip). A chunk's slice of I_v is then final (one row group) or the sum of
-// its row groups' partial column sums (the last row group to finish, a
-// counter election, adds them in order); with it go the slice's moments.
+// per-row (max, sum) pairs through epoch-tagged records. A chunk's slice of
+// I_v is then final (one row group) or the sum of its row groups' partial
+// column sums (the last row group to finish, a counter election, adds them in
+// order); the slice and its moments are published as tagged records.
 //
-// Before the items: one workgroup per (layer, sample, KV head) computes that
-// head's part of the elite observation window's pbar and counts it done;
-// once all are done every workgroup sums the parts of every (layer, sample)
-// itself (no second election and round trip), so each knows all elite sets
-// and works out the same chunk schedule.
+// After the items: the workgroup of a (layer, sample)'s first item combines
+// the chunks' moments into s_t and s_k, publishes them, then runs its top-k,
+// whose first radix pass overlaps the wait for the records of every layer of
+// the samples up to its own, from which it computes the budget and the
+// compacted offsets it needs; those and the kept indices are published as
+// tagged records. Workgroups with nothing left take compaction units (the
+// text rows, then the kept rows, of one layer, sample and KV head) from a
+// ticket counter.
 //
-// After the items: the last chunk of a (layer, sample) to finish (a counter
-// election) combines the chunks' moments into s_t and s_k and publishes them
-// in an epoch-tagged record; its workgroup then runs that (layer, sample)'s
-// top-k, whose budget-independent first radix pass overlaps the wait for the
-// records of every layer of the samples up to its own, from which it computes
-// the budgets and the compacted offsets it needs.
+// Records: every cross-workgroup value is written as (32-bit payload | epoch
+// << 32) words with agent-coherent stores, so a reader that sees the call's
+// epoch has the value; the epoch advances once per call and the last
+// workgroup to finish resets the few counters.
 //
 // All workgroups are co-resident (one 512-thread workgroup per CU, the LDS use
 // admitting no second), and a workgroup only waits for items that come no
@@ -110,7 +117,8 @@ __host__ __device__ inline int fused_kcap_min(int L, int B, int Nv, int wph) {
 struct FusedWs {
   unsigned *epoch;        // [1] calls so far
   unsigned *exitc;        // [1] workgroups finished in this call
-  uint64_t *parts;        // [L*B*Hkv][N_t] KV-head parts of pbar, (value | epoch << 32)
+  uint64_t *parts;        // [L*B][npp][N_t] elite-window parts 1.. of pbar, (value | epoch << 32)
+  int npp;                // parts per (layer, sample): a divisor of H_kv
   uint64_t *erec;         // [L*B][erec_stride] elite size, mask halves, each | epoch << 32
   int erec_stride;        // words per elite record: 1 + 2 * ceil(N_t / 64)
   unsigned *cnt_chunk;    // [L*B][max_chunks] finished row groups per chunk
@@ -125,6 +133,7 @@ struct FusedWs {
   int max_rg;             // row groups per (layer, sample) at most
   int wmax;               // columns per chunk at most
   // compaction in the same launch (gather != 0)
+  uint64_t *hint;         // [kFusedHintSlots] first item of each workgroup in the last call
   int gather;
   int esize;              // bytes per element
   int64_t cap_elems;      // elements of each compacted layer buffer
@@ -273,6 +282,46 @@ struct FusedItem {
   const void *k;  // layer's keys
 };
 
+// A workgroup's guess of its first item, kept from the previous call: the
+// (layer, sample), the column chunk and the key tiles per wave.
+constexpr int kFusedHintSlots = 1024;
+__host__ __device__ inline uint64_t fused_hint(int plb, int c, int ktw) {
+  return 1ull | ((uint64_t)(unsigned)plb << 1) | ((uint64_t)(unsigned)c << 24) | ((uint64_t)(unsigned)ktw << 48);
+}
+
+// While the elite sets are formed the HBM is idle: each wave loads the first
+// tiles of its key run in the item the hint guesses into its ring slots, as
+// fused_pass would stage them. fused_pass uses them only if the item is that
+// one (and they are visual keys), else it stages over them.
+template <typename Tag, int D>
+__device__ __forceinline__ void fused_prestage(const Shape &sh, const FusedTables &tab, uint64_t hint,
+                                               unsigned char *lds, const FusedLds &lo) {
+  using E = typename Tag::store_t;
+  constexpr int kTileBytes = 16 * D * Tag::kBytes;
+  constexpr int kDma = kTileBytes / 1024;
+  constexpr int kRing = fused_ring_depth(kTileBytes);
+  if (!(hint & 1ull)) return;
+  const int plb = (int)((hint >> 1) & 0x7fffff), c = (int)((hint >> 24) & 0xffffff), ktw = (int)(hint >> 48);
+  const int L = sh.L, B = sh.B, Hkv = sh.Hkv, Nv = sh.Nv;
+  if (plb >= L * B || ktw < 1 || ktw > kFusedSlots) return;
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, grp = lane >> 4;
+  const int wph = kFusedWaves / Hkv;
+  const int g = wave / wph, sub = wave - g * wph;
+  const int W = wph * 16 * ktw;
+  const int v0 = c * W + sub * ktw * 16;
+  const int nt = ktw < kRing ? ktw : kRing;
+  if (v0 + nt * 16 > Nv) return;  // only visual keys (text keys need the elite list)
+  const int l = plb / B, b = plb - l * B;
+  const E *kb = static_cast<const E *>(tab.p[L + l]) + (size_t)(b * Hkv + g) * sh.S * D;
+  unsigned char *ring = lds + lo.ring + (size_t)wave * kRing * kTileBytes;
+  for (int s = 0; s < nt; ++s) {
+    const unsigned char *src = reinterpret_cast<const unsigned char *>(kb + (size_t)(v0 + s * 16 + n) * D);
+#pragma unroll
+    for (int j = 0; j < kDma; ++j) load_lds16(src + 16 * grp + 64 * j, ring + s * kTileBytes + 1024 * j);
+  }
+}
+
 // One item's row group: RTP row tiles per KV head starting at row tile rt0.
 // Stream the chunk's columns (visual keys, then the elite text keys) with the
 // logits in registers, exchange row (max, sum) with the other chunks of the
@@ -280,7 +329,8 @@ struct FusedItem {
 // rows, per KV head, in colsum.
 template <typename Tag, int D, int RTP>
 __device__ __forceinline__ void fused_pass(const Shape &sh, const FusedWs &fw, const FusedItem &it, int rt0,
-                                           unsigned char *lds, const FusedLds &lo, unsigned epoch, int *status) {
+                                           unsigned char *lds, const FusedLds &lo, unsigned epoch, int *status,
+                                           uint64_t hint) {
   using E = typename Tag::store_t;
   constexpr int NW = kFusedWaves;
   constexpr int KTMAX = fused_ktmax(RTP);
@@ -335,9 +385,14 @@ __device__ __forceinline__ void fused_pass(const Shape &sh, const FusedWs &fw, c
     for (int j = 0; j < kDma; ++j) load_lds16(src + 16 * grp + 64 * j, slot + 1024 * j);
   };
   f32x4_t S[KTMAX][RTP];
+  // first tiles already in this wave's ring (fused_prestage) when the item is
+  // the one the hint guessed and those tiles are visual keys
+  const bool staged = hint == fused_hint(it.plb, c, ktw) &&
+                      c * W + sub * ktw * 16 + (ktw < kRing ? ktw : kRing) * 16 <= Nv;
+  if (!staged)
 #pragma unroll
-  for (int s = 0; s < kRing; ++s)
-    if (s < ktw) stage(s);
+    for (int s = 0; s < kRing; ++s)
+      if (s < ktw) stage(s);
 #pragma unroll
   for (int s = 0; s < KTMAX; ++s) {
     if (s < ktw) {
@@ -855,88 +910,6 @@ __device__ __forceinline__ void block_topk(const Shape &sh, const uint64_t *iv_l
   }
 }
 
-// Phase 0, one item per (layer, sample, KV head): the part of the elite
-// observation window's pbar that the KV head's G query heads give ("Elite
-// Observation Window", the Att equation). The logits of the last text query
-// of each of the G heads over the N_t text keys come from MFMA (16 text keys
-// as the A operand, up to 16 query heads as the B operand) into LDS; each wave
-// normalises whole rows (max, sum of exp2); the rows are summed in ascending
-// head order into part[j], written with agent-coherent stores as
-// (value | epoch << 32) words, so a reader that sees the epoch has the value.
-// lds: G * N_t floats.
-template <typename Tag, int D>
-__device__ __forceinline__ void fused_elite_part(const Shape &sh, const FusedTables &tab, int lb,
-                                                 int g, uint64_t *part, unsigned epoch, float *lds) {
-  using E = typename Tag::store_t;
-  constexpr int NW = kFusedWaves, NT = kFusedThreads;
-  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, grp = lane >> 4;
-  const int l = lb / sh.B, b = lb - (lb / sh.B) * sh.B;
-  const int Nt = sh.Nt, G = sh.G;
-  float *z = lds;
-  const E *q = static_cast<const E *>(tab.p[l]);
-  const E *k = static_cast<const E *>(tab.p[sh.L + l]);
-  const int nkt = (Nt + 15) >> 4;
-  const int nht = (G + 15) >> 4;
-  const int items = nht * nkt;
-  for (int it = wave; it < items; it += NW) {
-    const int kt_ = it % nkt, ht = it / nkt;
-    const int h0 = ht * 16;
-    const int nh = min(16, G - h0);
-    const int key = kt_ * 16 + n;
-    Frag<Tag> qf[D / 32], kf[D / 32];
-    if (n < nh) {
-      const E *qrow = q + ((size_t)(b * sh.Hq + g * G + h0 + n) * Nt + (Nt - 1)) * D;
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) qf[c].load(qrow + c * 32 + grp * 8);
-    } else {
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) qf[c].zero();
-    }
-    if (key < Nt) {
-      const E *krow = k + ((size_t)(b * sh.Hkv + g) * sh.S + sh.Nv + key) * D;
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) kf[c].load(krow + c * 32 + grp * 8);
-    } else {
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) kf[c].zero();
-    }
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) mfma_slice(acc, kf[c], qf[c]);
-    if (n < nh) {
-      float *zr = z + (size_t)(h0 + n) * Nt;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = kt_ * 16 + grp * 4 + i;
-        if (kk < Nt) zr[kk] = acc[i] * sh.scale2;
-      }
-    }
-  }
-  __syncthreads();
-  for (int h = wave; h < G; h += NW) {
-    float *zr = z + (size_t)h * Nt;
-    float m = -INFINITY;
-    for (int j = lane; j < Nt; j += 64) m = fmaxf(m, zr[j]);
-    m = wave_max(m);
-    float s = 0.f;
-    for (int j = lane; j < Nt; j += 64) {
-      const float ev = exp2f(zr[j] - m);
-      zr[j] = ev;
-      s += ev;
-    }
-    s = wave_sum(s);
-    const float inv = 1.f / s;
-    for (int j = lane; j < Nt; j += 64) zr[j] *= inv;
-  }
-  __syncthreads();
-  for (int j = tid; j < Nt; j += NT) {
-    float a = 0.f;
-    for (int h = 0; h < G; ++h) a += z[(size_t)h * Nt + j];
-    store_coherent(&part[j], pack_rec(a, epoch));
-  }
-}
-
 // ceil(a / b) for 0 <= a < 2^20 and 1 <= b, without an integer division:
 // the float estimate is within one of floor(a / b) and is corrected exactly.
 __device__ __forceinline__ int ceil_div_small(int a, int b) {
@@ -946,60 +919,183 @@ __device__ __forceinline__ int ceil_div_small(int a, int b) {
   return q + (q * b < a ? 1 : 0);
 }
 
-// Elite set of one (layer, sample) lb, block-wide, by the workgroup that
-// computed its first KV-head part: pbar = the sum of the KV-head parts in
-// ascending head order (the "Elite Observation Window" Att equation summed
-// over heads; the parts are epoch-tagged words, read again until all carry
-// this call's epoch), the set { j : pbar_j >= alpha max pbar } (the k
-// equation) as a bit mask per 64 text tokens, and its size. Published as
-// epoch-tagged words: erec[lb] = [size, then each mask word as two 32-bit
-// halves]; also the plan's elite list and count, and the overflow flag when
-// the set exceeds the elite cap. N_t <= 1024 (two entries per thread).
-__device__ __forceinline__ void fused_elite_merge(const Shape &sh, const PlanPtrs &plan, const FusedWs &fw, int lb,
-                                                  unsigned epoch, int *wtot, float *red) {
-  constexpr int NT = kFusedThreads, NW = kFusedWaves, E = 2;
+// Logits of the last text query of every query head of KV heads g0.. over
+// the text keys, scaled, into z (rows of N_t floats, G rows per KV head):
+// items (KV head, query-head tile, key tile) wave, wave + NW, ..., U at a
+// time per wave, every load of the U items issued before the first product.
+// Items past the end repeat the wave's first of the batch, not stored.
+template <typename Tag, int D, int U>
+__device__ __forceinline__ void fused_elite_logits(const Shape &sh, const typename Tag::store_t *q,
+                                                   const typename Tag::store_t *k, int b, int g0, int items,
+                                                   int per_head, int nkt, float *z, int head_floats) {
+  using E = typename Tag::store_t;
+  constexpr int NW = kFusedWaves;
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
-  const int Nt = sh.Nt, Hkv = sh.Hkv;
-  const auto rp = coherent_rsrc(fw.parts + (size_t)lb * Hkv * Nt, (unsigned)((size_t)Hkv * Nt * sizeof(uint64_t)));
-  // entry j = tid + e * NT: every load issued before any is checked
-  uint64_t w[E][8];
+  const int n = lane & 15, grp = lane >> 4;
+  const int Nt = sh.Nt, G = sh.G, Hkv = sh.Hkv;
+  for (int it0 = wave; it0 < items; it0 += NW * U) {
+    // the loads of U items before any product; rows past the ends read a
+    // valid row whose results are never stored
+    Frag<Tag> qf[U][D / 32], kf[U][D / 32];
 #pragma unroll
-  for (int e = 0; e < E; ++e)
+    for (int u = 0; u < U; ++u) {
+      const int it = it0 + u * NW < items ? it0 + u * NW : it0;  // past the end: the wave's first again
+      const int gl = it / per_head, r = it - gl * per_head;
+      const int ht = r / nkt, kt_ = r - ht * nkt;
+      const int g = g0 + gl;
+      const int h = min(ht * 16 + n, G - 1), key = min(kt_ * 16 + n, Nt - 1);
+      const E *qrow = q + ((size_t)(b * sh.Hq + g * G + h) * Nt + (Nt - 1)) * D;
+      const E *krow = k + ((size_t)(b * Hkv + g) * sh.S + sh.Nv + key) * D;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int j = tid + e * NT;
-      const unsigned off = (j < Nt && g < Hkv) ? (unsigned)(((size_t)g * Nt + j) * sizeof(uint64_t)) : 0xfffffff0u;
-      w[e][g] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rp, (int)off, 0, 16));
-    }
-  unsigned spins = 0;
-  for (;;) {
-    bool ok = true;
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-#pragma unroll
-      for (int g = 0; g < 8; ++g) ok = ok && (tid + e * NT >= Nt || g >= Hkv || (unsigned)(w[e][g] >> 32) == epoch);
-    if (ok || spin_expired(spins, plan.status)) break;
-    __builtin_amdgcn_s_sleep(2);
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-#pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        const int j = tid + e * NT;
-        const unsigned off = (j < Nt && g < Hkv) ? (unsigned)(((size_t)g * Nt + j) * sizeof(uint64_t)) : 0xfffffff0u;
-        w[e][g] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rp, (int)off, 0, 16));
+      for (int c = 0; c < D / 32; ++c) {
+        qf[u][c].load(qrow + c * 32 + grp * 8);
+        kf[u][c].load(krow + c * 32 + grp * 8);
       }
+    }
+    // every load in flight before the first product (the scheduler would
+    // otherwise issue each item's loads after the previous item's products)
+    __builtin_amdgcn_sched_barrier(0);
+    // products of every item, including the repeats past the end: a product
+    // under a branch would have its loads moved after the previous item's
+    f32x4_t acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) mfma_slice(acc[u], kf[u][c], qf[u][c]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int it = it0 + u * NW;
+      if (it < items) {
+        const int gl = it / per_head, r = it - gl * per_head;
+        const int ht = r / nkt, kt_ = r - ht * nkt;
+        if (ht * 16 + n < G) {
+          float *zr = z + (size_t)gl * head_floats + (size_t)(ht * 16 + n) * Nt;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kk = kt_ * 16 + grp * 4 + i;
+            if (kk < Nt) zr[kk] = acc[u][i] * sh.scale2;
+          }
+        }
+      }
+    }
   }
-  float pb[E];
+}
+
+// Phase 0, elite sets ("Elite Observation Window", the Att and k equations).
+// A (layer, sample) lb is split into npp parts of H_kv / npp KV heads, one
+// workgroup each. For every KV head g of the part and each of its G query
+// heads, the logits of the last text query over the N_t text keys come from
+// MFMA (16 text keys as the A operand, up to 16 query heads as the B operand)
+// into LDS; each wave normalises whole rows (max, sum of exp2); the part's
+// pbar_j is the sum over its KV heads in ascending order of the sums over
+// their query heads in ascending order. KV heads are taken in groups whose
+// logits fit the LDS (G * N_t floats per head; the host keeps one head within
+// it). Parts 1.. are published as epoch-tagged words; the workgroup of part 0
+// adds them to its own in ascending part order, forms the set
+// { j : pbar_j >= alpha max pbar } as one bit mask per 64 text tokens, and
+// publishes it with agent-coherent stores: erec[lb] = [size, then each mask
+// word as two 32-bit halves]; also the plan's elite list and count, and the
+// overflow flag when the set exceeds the elite cap. N_t <= 1024 (two entries
+// per thread).
+template <typename Tag, int D>
+__device__ __forceinline__ void fused_elite_part(const Shape &sh, const FusedTables &tab, const PlanPtrs &plan,
+                                                 const FusedWs &fw, int lb, int pi, unsigned epoch, float *z,
+                                                 int lds_bytes, int *wtot, float *red) {
+  using E = typename Tag::store_t;
+  constexpr int NT = kFusedThreads, NW = kFusedWaves, EP = 2;
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int l = lb / sh.B, b = lb - (lb / sh.B) * sh.B;
+  const int Nt = sh.Nt, G = sh.G, Hkv = sh.Hkv, npp = fw.npp;
+  const int hg = Hkv / npp, gbeg = pi * hg, gend = gbeg + hg;
+  const E *q = static_cast<const E *>(tab.p[l]);
+  const E *k = static_cast<const E *>(tab.p[sh.L + l]);
+  const int nkt = (Nt + 15) >> 4, nht = (G + 15) >> 4;
+  const int per_head = nht * nkt;
+  const int head_floats = G * Nt;
+  int gh = lds_bytes / (head_floats * (int)sizeof(float));
+  gh = gh < 1 ? 1 : (gh > hg ? hg : gh);
+  float pb[EP] = {0.f, 0.f};
+  for (int g0 = gbeg; g0 < gend; g0 += gh) {
+    const int ng = gend - g0 < gh ? gend - g0 : gh;
+    const int items = ng * per_head;
+    // U items per wave at a time, U no more than a wave has
+    const int per_wave = (items + NW - 1) / NW;
+    if (per_wave >= 4) fused_elite_logits<Tag, D, 4>(sh, q, k, b, g0, items, per_head, nkt, z, head_floats);
+    else if (per_wave >= 2) fused_elite_logits<Tag, D, 2>(sh, q, k, b, g0, items, per_head, nkt, z, head_floats);
+    else fused_elite_logits<Tag, D, 1>(sh, q, k, b, g0, items, per_head, nkt, z, head_floats);
+    __syncthreads();
+    for (int h = wave; h < ng * G; h += NW) {
+      float *zr = z + (size_t)h * Nt;
+      float m = -INFINITY;
+      for (int j = lane; j < Nt; j += 64) m = fmaxf(m, zr[j]);
+      m = wave_max(m);
+      float s = 0.f;
+      for (int j = lane; j < Nt; j += 64) {
+        const float ev = exp2f(zr[j] - m);
+        zr[j] = ev;
+        s += ev;
+      }
+      s = wave_sum(s);
+      const float inv = 1.f / s;
+      for (int j = lane; j < Nt; j += 64) zr[j] *= inv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EP; ++e) {
+      const int j = tid + e * NT;
+      if (j < Nt)
+        for (int gl = 0; gl < ng; ++gl) {
+          float a = 0.f;
+          for (int h = 0; h < G; ++h) a += z[(size_t)(gl * G + h) * Nt + j];
+          pb[e] += a;
+        }
+    }
+    __syncthreads();  // z is free again
+  }
+  if (pi > 0) {
+    uint64_t *part = fw.parts + ((size_t)lb * npp + pi) * Nt;
+#pragma unroll
+    for (int e = 0; e < EP; ++e)
+      if (tid + e * NT < Nt) store_coherent(&part[tid + e * NT], pack_rec(pb[e], epoch));
+    return;
+  }
+  if (npp > 1) {
+    // the other parts, every load issued before any is checked
+    constexpr int PM = 7;  // npp <= 8
+    const auto rp = coherent_rsrc(fw.parts + (size_t)lb * npp * Nt, (unsigned)((size_t)npp * Nt * sizeof(uint64_t)));
+    uint64_t w[EP][PM];
+    unsigned spins = 0;
+    for (;;) {
+#pragma unroll
+      for (int e = 0; e < EP; ++e)
+#pragma unroll
+        for (int p = 0; p < PM; ++p) {
+          const int j = tid + e * NT;
+          const unsigned off =
+              (j < Nt && p + 1 < npp) ? (unsigned)(((size_t)(p + 1) * Nt + j) * sizeof(uint64_t)) : 0xfffffff0u;
+          w[e][p] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rp, (int)off, 0, 16));
+        }
+      bool ok = true;
+#pragma unroll
+      for (int e = 0; e < EP; ++e)
+#pragma unroll
+        for (int p = 0; p < PM; ++p)
+          ok = ok && (tid + e * NT >= Nt || p + 1 >= npp || (unsigned)(w[e][p] >> 32) == epoch);
+      if (ok || spin_expired(spins, plan.status)) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+#pragma unroll
+    for (int e = 0; e < EP; ++e)
+#pragma unroll
+      for (int p = 0; p < PM; ++p)
+        if (p + 1 < npp) pb[e] += __uint_as_float((unsigned)w[e][p]);
+  }
   float m = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    float a = 0.f;
-#pragma unroll
-    for (int g = 0; g < 8; ++g)
-      if (g < Hkv) a += __uint_as_float((unsigned)w[e][g]);
-    pb[e] = a;
-    if (tid + e * NT < Nt) m = fmaxf(m, a);
-  }
+  for (int e = 0; e < EP; ++e)
+    if (tid + e * NT < Nt) m = fmaxf(m, pb[e]);
   m = wave_max(m);
   if (lane == 0) red[wave] = m;
   __syncthreads();
@@ -1007,10 +1103,10 @@ __device__ __forceinline__ void fused_elite_merge(const Shape &sh, const PlanPtr
   for (int u = 1; u < NW; ++u) m = fmaxf(m, red[u]);
   const float thr = sh.alpha * m;
   // word e * NW + wave holds tokens 64 (e * NW + wave) + lane
-  unsigned long long mk[E];
+  unsigned long long mk[EP];
   int cnt = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
+  for (int e = 0; e < EP; ++e) {
     mk[e] = __ballot(tid + e * NT < Nt && pb[e] >= thr);
     cnt += __popcll(mk[e]);
   }
@@ -1018,16 +1114,16 @@ __device__ __forceinline__ void fused_elite_merge(const Shape &sh, const PlanPtr
   // words of pass e' < e and the words (e, wave' < wave)
   if (lane == 0)
 #pragma unroll
-    for (int e = 0; e < E; ++e) wtot[e * NW + wave] = __popcll(mk[e]);
+    for (int e = 0; e < EP; ++e) wtot[e * NW + wave] = __popcll(mk[e]);
   __syncthreads();
   const int ntw = fused_words64(Nt);
   uint64_t *rec = fw.erec + (size_t)lb * fw.erec_stride;
   const uint64_t tag = (uint64_t)epoch << 32;
   int total = 0;
-  for (int u = 0; u < E * NW; ++u) total += wtot[u];
+  for (int u = 0; u < EP * NW; ++u) total += wtot[u];
   const unsigned long long lt = (1ull << lane) - 1ull;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
+  for (int e = 0; e < EP; ++e) {
     const int word = e * NW + wave;
     int before = 0;
     for (int u = 0; u < word; ++u) before += wtot[u];
@@ -1425,27 +1521,31 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
   int *owed = reinterpret_cast<int *>(lds + lo.owed);
   int *ntk_l = reinterpret_cast<int *>(lds + lo.ntk);
 
-  // Phase 0: the KV-head parts of pbar, items (layer, sample, KV head) me,
-  // me + P, ..., published as epoch-tagged words (no counter: the readers
-  // check the tags). The status word is cleared before workgroup 0 writes
-  // its first part; every status bit is set after some workgroup has seen
-  // all parts, so after the clear.
+  // Phase 0: the elite set of (layer, sample) me, me + P, ... (no counter: the
+  // readers check the records' tags). The status word is cleared before
+  // workgroup 0 publishes its first set; every status bit is set after some
+  // workgroup has seen all sets, so after the clear.
   if (me == 0 && tid == 0) {
     store_coherent(plan.status, 0);
     wait_all_memory();
   }
-  for (int t = me; t < LB * sh.Hkv; t += P) {
-    const int lb = t / sh.Hkv, g = t - lb * sh.Hkv;
-    fused_elite_part<Tag, D>(sh, tab, lb, g, fw.parts + (size_t)t * sh.Nt, epoch, lds_f);
-    __syncthreads();  // the LDS is free again
+  // A wave's loads complete in order, so a wave that polls a record waits for
+  // its prestage loads too; a part's own loads are bound by what one CU has in
+  // flight. A wave prestages once it has no part left and no poll before the
+  // schedule: workgroups without a part at once, the others after their
+  // parts, the waves that read the elite counts after those.
+  const uint64_t hint = me < kFusedHintSlots ? fw.hint[me] : 0ull;
+  const int nparts = LB * fw.npp;
+  const bool former = me < nparts;
+  const bool count_wave = (tid >> 6) * 64 < (LB < kFusedThreads ? LB : kFusedThreads);
+  if (!former && !count_wave) fused_prestage<Tag, D>(sh, tab, hint, lds, lo);
+  for (int t = me; t < nparts; t += P) {
+    const int lb = t / fw.npp;
+    fused_elite_part<Tag, D>(sh, tab, plan, fw, lb, t - lb * fw.npp, epoch, lds_f, lo.total, wtot, redf);
   }
-  // merges of the pairs whose first KV-head part this workgroup computed, then
-  // every pair's elite count
-  for (int t = me; t < LB * sh.Hkv; t += P) {
-    const int lb = t / sh.Hkv;
-    if (t == lb * sh.Hkv) fused_elite_merge(sh, plan, fw, lb, epoch, wtot, redf);
-  }
+  if (former && !count_wave) fused_prestage<Tag, D>(sh, tab, hint, lds, lo);
   fused_elite_counts(sh, fw, epoch, plan.status, ntk_l);
+  if (count_wave) fused_prestage<Tag, D>(sh, tab, hint, lds, lo);
   fused_schedule(sh, ntk_l, me, P, item_list, hdr, wtot);
   __syncthreads();
   const int kcap = uniform(hdr[0]);
@@ -1480,10 +1580,16 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
     __syncthreads();
     {
       const int rt0 = it.r * kFusedRtMax, left = it.cp.rtg - rt0;
-      if (left >= 4) fused_pass<Tag, D, 4>(sh, fw, it, rt0, lds, lo, epoch, plan.status);
-      else if (left == 3) fused_pass<Tag, D, 3>(sh, fw, it, rt0, lds, lo, epoch, plan.status);
-      else if (left == 2) fused_pass<Tag, D, 2>(sh, fw, it, rt0, lds, lo, epoch, plan.status);
-      else fused_pass<Tag, D, 1>(sh, fw, it, rt0, lds, lo, epoch, plan.status);
+      uint64_t h = 0ull;  // the prestaged tiles serve the first item only
+      if (k == 0) {
+        wait_all_memory();  // this wave's prestage loads are in its ring
+        h = hint;
+        if (tid == 0 && me < kFusedHintSlots) fw.hint[me] = fused_hint(it.plb, it.c, it.cp.ktw);
+      }
+      if (left >= 4) fused_pass<Tag, D, 4>(sh, fw, it, rt0, lds, lo, epoch, plan.status, h);
+      else if (left == 3) fused_pass<Tag, D, 3>(sh, fw, it, rt0, lds, lo, epoch, plan.status, h);
+      else if (left == 2) fused_pass<Tag, D, 2>(sh, fw, it, rt0, lds, lo, epoch, plan.status, h);
+      else fused_pass<Tag, D, 1>(sh, fw, it, rt0, lds, lo, epoch, plan.status, h);
     }
     // The workgroup of a pair's first item (row group 0, chunk 0) owns its
     // statistics and top-k, which it runs after its items.
