@@ -1454,6 +1454,7 @@ int launch_chunked(const Config &cfg, const LayerTable &qt, const LayerTable &kt
   // (layer, sample) are loaded by as many CUs
   fw.npp = 1;
   while (fw.npp < s.Hkv && (long long)s.L * s.B * fw.npp * 2 <= grid) fw.npp *= 2;
+  fw.kcap_lo = cfg.fused_kcap_lo;
   fw.erec = reinterpret_cast<uint64_t *>(p + cfg.off_erec);
   fw.hint = reinterpret_cast<uint64_t *>(p + cfg.off_hint);
   fw.erec_stride = 1 + 2 * fused_words64(s.Nt);

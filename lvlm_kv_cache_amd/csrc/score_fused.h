@@ -119,6 +119,7 @@ struct FusedWs {
   unsigned *exitc;        // [1] workgroups finished in this call
   uint64_t *parts;        // [L*B][npp][N_t] elite-window parts 1.. of pbar, (value | epoch << 32)
   int npp;                // parts per (layer, sample): a divisor of H_kv
+  int kcap_lo;            // smallest key-tile cap per wave the schedule may choose (fused_kcap_min)
   uint64_t *erec;         // [L*B][erec_stride] elite size, mask halves, each | epoch << 32
   int erec_stride;        // words per elite record: 1 + 2 * ceil(N_t / 64)
   unsigned *cnt_chunk;    // [L*B][max_chunks] finished row groups per chunk
@@ -289,13 +290,14 @@ __host__ __device__ inline uint64_t fused_hint(int plb, int c, int ktw) {
   return 1ull | ((uint64_t)(unsigned)plb << 1) | ((uint64_t)(unsigned)c << 24) | ((uint64_t)(unsigned)ktw << 48);
 }
 
-// While the elite sets are formed the HBM is idle: each wave loads the first
-// tiles of its key run in the item the hint guesses into its ring slots, as
-// fused_pass would stage them. fused_pass uses them only if the item is that
-// one (and they are visual keys), else it stages over them.
+// While the elite sets are formed the HBM is idle: the first tiles of wave
+// `wave`'s key run in the item the hint guesses go into that wave's ring
+// slots, as fused_pass would stage them (the calling wave issues the loads).
+// fused_pass uses them only if the item is that one (and they are visual
+// keys), else it stages over them.
 template <typename Tag, int D>
 __device__ __forceinline__ void fused_prestage(const Shape &sh, const FusedTables &tab, uint64_t hint,
-                                               unsigned char *lds, const FusedLds &lo) {
+                                               unsigned char *lds, const FusedLds &lo, int wave) {
   using E = typename Tag::store_t;
   constexpr int kTileBytes = 16 * D * Tag::kBytes;
   constexpr int kDma = kTileBytes / 1024;
@@ -304,7 +306,7 @@ __device__ __forceinline__ void fused_prestage(const Shape &sh, const FusedTable
   const int plb = (int)((hint >> 1) & 0x7fffff), c = (int)((hint >> 24) & 0xffffff), ktw = (int)(hint >> 48);
   const int L = sh.L, B = sh.B, Hkv = sh.Hkv, Nv = sh.Nv;
   if (plb >= L * B || ktw < 1 || ktw > kFusedSlots) return;
-  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int lane = opaque_tid() & 63;
   const int n = lane & 15, grp = lane >> 4;
   const int wph = kFusedWaves / Hkv;
   const int g = wave / wph, sub = wave - g * wph;
@@ -1191,86 +1193,85 @@ __device__ __forceinline__ void fused_elite_list(const Shape &sh, const FusedWs 
 }
 
 // Work schedule of this workgroup, block-wide, from the elite counts ntk
-// (LDS, [layer][sample]): thread s takes the pair (b, l) = (s / L, s % L) in
-// sample-major order. The cap on key tiles per wave is the smallest (narrowest
-// chunks, most workgroups busy) whose items all fit one round of the grid, the
-// widest when none does; items are non-increasing in the cap, and
-// items(k) >= (sum of nrg * cols) / (16 wph k), so the search starts at that
-// bound and tries four caps per round. Items go in the order (b, l, row group,
-// chunk); workgroup me takes items me, me + P, ... Writes the items of this
-// workgroup to item[] ((b * L + l) << 16 | index in the (layer, sample)),
-// hdr[0] = cap and hdr[1] = item count. red: 4 * kFusedWaves ints of LDS.
-__device__ __forceinline__ void fused_schedule(const Shape &sh, const int *ntk_lds, int me, int P, int *item,
-                                               int *hdr, int *red) {
-  constexpr int NW = kFusedWaves, C = 4;
+// (LDS, [layer][sample]); pair p = (b, l) = (p / L, p % L) in sample-major
+// order is held by lane p % 64 of a wave (up to eight per lane, L * B <=
+// 512). The cap on key tiles per wave is the smallest (narrowest chunks, most
+// workgroups busy) whose items all fit one round of the grid, the widest when
+// none does: items are non-increasing in the cap, and no cap below
+// fw.kcap_lo fits, so wave w counts the items of cap kcap_lo + w (eight caps
+// per round, one barrier each). Items go in the order (b, l, row group,
+// chunk); workgroup me takes items me, me + P, ...; wave 0 writes those of
+// this workgroup to item[] ((b * L + l) << 16 | index in the (layer,
+// sample)), hdr[0] = cap and hdr[1] = item count. Sums are exact integer wave
+// scans. One wave issues an instruction every four cycles at best and this
+// runs on every call, so each wave's share is kept short.
+__device__ __forceinline__ void fused_schedule(const Shape &sh, const FusedWs &fw, const int *ntk_lds, int me, int P,
+                                               int *item, int *hdr, int *red) {
+  constexpr int NW = kFusedWaves;
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
   const int L = sh.L, B = sh.B, Nv = sh.Nv, LB = L * B;
   const int wph = kFusedWaves / sh.Hkv, W0 = wph * 16;
-  const bool ok = tid < LB;  // LB <= kFusedThreads
-  const int b = ceil_div_small(tid + 1, L) - 1, l = tid - b * L;
-  const int t = ok ? ntk_lds[l * B + b] : 0;
-  const int rows = sh.G * t;
-  const int rtg = rows > 0 ? (rows + 15) >> 4 : 1;
-  const int nrg = ok ? (rtg + kFusedRtMax - 1) / kFusedRtMax : 0;
-  const int km = fused_ktmax(rtg < kFusedRtMax ? rtg : kFusedRtMax);
-  const int cols = Nv + t;
-  auto chunks = [&](int kc) {
-    const int k = kc < km ? kc : km;
-    return ceil_div_small(cols, W0 * (k < 1 ? 1 : k));
+  const int nj = (LB + 63) >> 6;  // pairs per lane at most
+  // pair p: row groups, key-tile cap of its row tiles, columns
+  auto pair = [&](int p, int &nrg, int &km, int &cols) {
+    const int b = ceil_div_small(p + 1, L) - 1, l = p - b * L;
+    const int t = p < LB ? ntk_lds[l * B + b] : 0;
+    const int rtg = t > 0 ? (sh.G * t + 15) >> 4 : 1;
+    nrg = p < LB ? (rtg + kFusedRtMax - 1) / kFusedRtMax : 0;
+    km = fused_ktmax(rtg < kFusedRtMax ? rtg : kFusedRtMax);
+    cols = Nv + t;
   };
-  // block sums of C values: per wave, then over the waves in order
-  auto block_sums = [&](const int (&v)[C], int (&out)[C]) {
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int x = wave_sum_i(v[c]);
-      if (lane == 0) red[c * NW + wave] = x;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      int x = 0;
-      for (int w = 0; w < NW; ++w) x += red[c * NW + w];
-      out[c] = x;
-    }
-    __syncthreads();
+  auto chunks = [&](int km, int cols, int kc) {
+    const int k = kc < km ? kc : km;
+    return ceil_div_small(cols, W0 * k);
   };
   const int P_sched = P < kFusedTargetCus ? P : kFusedTargetCus;
-  int k0;
-  {
-    int v[C] = {nrg * cols, 0, 0, 0}, o[C];
-    block_sums(v, o);
-    const int kb = (int)ceilf((float)o[0] / ((float)W0 * (float)P_sched)) - 1;  // -1: float rounding
-    k0 = max(fused_kcap_min(L, B, Nv, wph), min(kb, kFusedSlots));
-  }
   int kc = kFusedSlots;
-  for (; k0 < kFusedSlots; k0 += C) {
-    int v[C], o[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) v[c] = (k0 + c <= kFusedSlots) ? nrg * chunks(k0 + c) : 0;
-    block_sums(v, o);
+#pragma unroll 1
+  for (int k0 = fw.kcap_lo; k0 < kFusedSlots; k0 += NW) {
+    const int mine = k0 + wave;  // this wave's candidate
+    int v = 0;
+#pragma unroll 1
+    for (int j = 0; j < nj; ++j) {
+      int nrg, km, cols;
+      pair(lane + 64 * j, nrg, km, cols);
+      v += nrg * chunks(km, cols, mine);
+    }
+    v = __builtin_amdgcn_readlane(wave_scan_incl(v), 63);
+    if (lane == 0) red[wave] = (mine <= kFusedSlots && v <= P_sched) ? 1 : 0;
+    __syncthreads();
     int found = -1;
-#pragma unroll
-    for (int c = C - 1; c >= 0; --c)
-      if (k0 + c <= kFusedSlots && o[c] <= P_sched) found = k0 + c;
+    for (int w = NW - 1; w >= 0; --w)
+      if (red[w]) found = k0 + w;
+    __syncthreads();  // red is read before the next round writes it
     if (found >= 0) {
       kc = found;
       break;
     }
   }
-  const int nch = nrg > 0 ? chunks(kc) : 0;
-  const int nit = nrg * nch;
-  int total;
-  const int start = fused_block_scan(nit, red, &total);
-  if (nit > 0) {
-    // first item index >= start congruent to me mod P, and its slot k
-    const int d = start - me;
-    int k = d <= 0 ? 0 : ceil_div_small(d, P);
-    for (int i = me + k * P; i < start + nit; i += P, ++k)
-      if (k < kFusedMaxItems) item[k] = (tid << 16) | (i - start);
+  if (wave != 0) return;
+  // exclusive prefix of the item counts in pair order, and this workgroup's items
+  int base = 0;
+#pragma unroll 1
+  for (int j = 0; j < nj; ++j) {
+    const int p = lane + 64 * j;
+    int nrg, km, cols;
+    pair(p, nrg, km, cols);
+    const int nit = nrg > 0 ? nrg * chunks(km, cols, kc) : 0;
+    const int incl = wave_scan_incl(nit);
+    const int start = base + incl - nit;
+    base += __builtin_amdgcn_readlane(incl, 63);
+    if (nit > 0) {
+      // first item index >= start congruent to me mod P, and its slot k
+      const int d = start - me;
+      int k = d <= 0 ? 0 : ceil_div_small(d, P);
+      for (int i = me + k * P; i < start + nit; i += P, ++k)
+        if (k < kFusedMaxItems) item[k] = (p << 16) | (i - start);
+    }
   }
-  if (tid == 0) {
+  if (lane == 0) {
     hdr[0] = kc;
-    hdr[1] = total;  // items in all
+    hdr[1] = base;  // items in all
   }
 }
 
@@ -1529,24 +1530,32 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
     store_coherent(plan.status, 0);
     wait_all_memory();
   }
-  // A wave's loads complete in order, so a wave that polls a record waits for
-  // its prestage loads too; a part's own loads are bound by what one CU has in
-  // flight. A wave prestages once it has no part left and no poll before the
-  // schedule: workgroups without a part at once, the others after their
-  // parts, the waves that read the elite counts after those.
+  // A wave's loads complete in order and a barrier waits for them, so a
+  // prestage only pays where the workgroup would wait anyway: not in the
+  // waves that read the elite counts (their tiles are loaded by wave ncw +
+  // their index, when there is one) and not in the workgroups that merge a
+  // set (they finish last); at once in workgroups without a part (a part's
+  // own loads are bound by what one CU has in flight), after it in those
+  // with a part to publish.
   const uint64_t hint = me < kFusedHintSlots ? fw.hint[me] : 0ull;
   const int nparts = LB * fw.npp;
   const bool former = me < nparts;
-  const bool count_wave = (tid >> 6) * 64 < (LB < kFusedThreads ? LB : kFusedThreads);
-  if (!former && !count_wave) fused_prestage<Tag, D>(sh, tab, hint, lds, lo);
+  const bool merger = former && me % fw.npp == 0;
+  const int ncw = ((LB < kFusedThreads ? LB : kFusedThreads) + 63) >> 6;  // waves that read the counts
+  const int wave_id = tid >> 6;
+  auto prestage = [&]() {
+    if (wave_id < ncw) return;
+    fused_prestage<Tag, D>(sh, tab, hint, lds, lo, wave_id);
+    if (wave_id - ncw < ncw) fused_prestage<Tag, D>(sh, tab, hint, lds, lo, wave_id - ncw);
+  };
+  if (!former) prestage();
   for (int t = me; t < nparts; t += P) {
     const int lb = t / fw.npp;
     fused_elite_part<Tag, D>(sh, tab, plan, fw, lb, t - lb * fw.npp, epoch, lds_f, lo.total, wtot, redf);
   }
-  if (former && !count_wave) fused_prestage<Tag, D>(sh, tab, hint, lds, lo);
+  if (former && !merger) prestage();
   fused_elite_counts(sh, fw, epoch, plan.status, ntk_l);
-  if (count_wave) fused_prestage<Tag, D>(sh, tab, hint, lds, lo);
-  fused_schedule(sh, ntk_l, me, P, item_list, hdr, wtot);
+  fused_schedule(sh, fw, ntk_l, me, P, item_list, hdr, wtot);
   __syncthreads();
   const int kcap = uniform(hdr[0]);
   const int run = uniform(hdr[1]);
@@ -1577,13 +1586,15 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
     // elite list of the item's (layer, sample), ascending
     fused_elite_list(sh, fw, it.plb, it.ntk, epoch, plan.status, el,
                      reinterpret_cast<unsigned long long *>(lds + lo.mloc));
+    if (k == 0) wait_all_memory();  // the prestage loads are in the ring before the barrier
     __syncthreads();
     {
       const int rt0 = it.r * kFusedRtMax, left = it.cp.rtg - rt0;
       uint64_t h = 0ull;  // the prestaged tiles serve the first item only
       if (k == 0) {
-        wait_all_memory();  // this wave's prestage loads are in its ring
-        h = hint;
+        // a wave's tiles were prestaged unless its workgroup merged a set, or
+        // it reads the counts and no wave was left to load them
+        if (!merger && (wave >= ncw || wave + ncw < kFusedWaves)) h = hint;
         if (tid == 0 && me < kFusedHintSlots) fw.hint[me] = fused_hint(it.plb, it.c, it.cp.ktw);
       }
       if (left >= 4) fused_pass<Tag, D, 4>(sh, fw, it, rt0, lds, lo, epoch, plan.status, h);
