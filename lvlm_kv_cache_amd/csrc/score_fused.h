@@ -185,7 +185,7 @@ __host__ __device__ inline FusedLds fused_lds_layout(int tile_bytes, int ring_de
   f.ntk = o;
   o += fused_align16(LB * 4);
   f.sts = o;
-  o += fused_align16((LB + 8) * 16);  // reads run up to 8 entries past each array
+  o += fused_align16((LB + 16) * 16);  // reads run up to 15 entries past each array
   f.total = o;
   return f;
 }
@@ -1337,34 +1337,87 @@ __device__ __forceinline__ void fused_layer_stats(const Shape &sh, const PlanPtr
   }
 }
 
-// budget_sums over LDS with the values read eight at a time ahead of the
-// additions and no branches: the same additions and comparisons in the same
-// order, so the same result (a padded entry adds +0.0 to a non-negative sum,
-// or keeps the minimum).
+// budget_sums over LDS with the values read sixteen at a time, every read of
+// a batch issued before the first addition (one LDS round trip per batch), and
+// no branches. The two sums take the same additions in the same order, so the
+// same result (a padded entry adds +0.0 to a non-negative sum). The shift is a
+// minimum, exact in any order: four interleaved chains of v_min_f64 instead of
+// one compare-and-select chain, then +0.0 unless some s_k is negative (which
+// is what the serial form keeps: it starts at +0.0 and takes only values below
+// it). Reads run up to 15 entries past L (the LDS arrays are padded).
 __device__ __forceinline__ BudgetSums budget_sums_lds(int L, const double *st, const double *sk) {
 #pragma clang fp contract(off)
+  constexpr int U = 16;
   BudgetSums r{0.0, 0.0, 0.0};
-  for (int l0 = 0; l0 < L; l0 += 8) {
-    double a[8], c[8];
+  double m[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int l0 = 0; l0 < L; l0 += U) {
+    double a[U], c[U];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < U; ++j) {
       a[j] = st[l0 + j];
       c[j] = sk[l0 + j];
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < U; ++j) {
       const bool in = l0 + j < L;
       r.st_sum += in ? a[j] : 0.0;
-      r.mshift = (in && c[j] < r.mshift) ? c[j] : r.mshift;
+      m[j & 3] = in ? fmin(m[j & 3], c[j]) : m[j & 3];
     }
   }
-  for (int l0 = 0; l0 < L; l0 += 8) {
-    double c[8];
+  const double mn = fmin(fmin(m[0], m[1]), fmin(m[2], m[3]));
+  r.mshift = mn < 0.0 ? mn : 0.0;
+  for (int l0 = 0; l0 < L; l0 += U) {
+    double c[U];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) c[j] = sk[l0 + j];
+    for (int j = 0; j < U; ++j) c[j] = sk[l0 + j];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) r.u_sum += (l0 + j < L) ? c[j] - r.mshift : 0.0;
+    for (int j = 0; j < U; ++j) r.u_sum += (l0 + j < L) ? c[j] - r.mshift : 0.0;
   }
+  return r;
+}
+
+// budget_sums of one sample with its layers across the lanes of a wave (L <=
+// 64; every lane gets the result): the shift is a minimum, exact in any order
+// (a DPP reduction; lanes past L hold 0.0, which min(0, ...) already has),
+// +0.0 unless some s_k is negative, as the serial form keeps; the shifted
+// values are formed in every lane at once; the two sums then take the same
+// additions in the same order as the serial form, four lanes' values read
+// ahead of their additions.
+// One wave issues an instruction every four cycles at best, so the serial
+// part is kept to the additions.
+__device__ __forceinline__ BudgetSums budget_sums_wave(int L, const double *st, const double *sk) {
+#pragma clang fp contract(off)
+  const int lane = opaque_tid() & 63;
+  const double a = lane < L ? st[lane] : 0.0;
+  const double c = lane < L ? sk[lane] : 0.0;
+  double mn = c;
+  mn = fmin(mn, dpp_d<0xB1>(mn));
+  mn = fmin(mn, dpp_d<0x4E>(mn));
+  mn = fmin(mn, dpp_d<0x141>(mn));
+  mn = fmin(mn, dpp_d<0x140>(mn));
+  mn = fmin(fmin(readlane_d(mn, 0), readlane_d(mn, 16)), fmin(readlane_d(mn, 32), readlane_d(mn, 48)));
+  BudgetSums r;
+  r.mshift = mn < 0.0 ? mn : 0.0;
+  // lanes past L add +0.0, which leaves these non-negative sums unchanged
+  const double u = lane < L ? c - r.mshift : 0.0;
+  double s1 = 0.0, s2 = 0.0;
+  for (int l0 = 0; l0 < L; l0 += 4) {
+    double a4[4], u4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a4[j] = readlane_d(a, l0 + j);
+      u4[j] = readlane_d(u, l0 + j);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      s1 += a4[j];
+      s2 += u4[j];
+    }
+  }
+  r.st_sum = s1;
+  r.u_sum = s2;
   return r;
 }
 
@@ -1375,13 +1428,13 @@ __device__ __forceinline__ BudgetSums budget_sums_lds(int L, const double *st, c
 // order); writes the plan's budget, budget_x and out_off of (l, b) (and the
 // layer's total after the last sample), leaves the budget in bc[0] and the
 // offset's 32-bit halves in bc[2], bc[3], and returns the budget.
-// sts: LDS for 2 * (L * (b + 1) + 8) doubles.
+// sts: LDS for 2 * (L * (b + 1) + 16) doubles.
 __device__ __forceinline__ int fused_budget(const Shape &sh, const PlanPtrs &plan, const FusedWs &fw, int l, int b,
                                             unsigned epoch, double *sts, int *bc) {
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
   const int L = sh.L, B = sh.B;
   const int nrec = L * (b + 1);
-  double *st = sts, *sk = sts + nrec + 8;  // [bb][l]
+  double *st = sts, *sk = sts + nrec + 16;  // [bb][l], each with 16 entries of padding
   // one resource for all records (a per-lane resource would cost a loop over
   // the distinct values of the wave)
   const auto rr = coherent_rsrc(fw.srec, (unsigned)((size_t)L * B * 32));
@@ -1407,8 +1460,12 @@ __device__ __forceinline__ int fused_budget(const Shape &sh, const PlanPtrs &pla
   __syncthreads();
   if (wave == 0) {
     double off = 0.0;  // element offsets, exact in double (below 2^53)
-    for (int bb = lane; bb <= b; bb += 64) {
-      const BudgetSums sums = budget_sums_lds(L, st + (size_t)bb * L, sk + (size_t)bb * L);
+    // one sample: its layers across the lanes; several: one sample per lane
+    const bool across = b == 0 && L <= 64;
+    BudgetSums sums0;
+    if (across) sums0 = budget_sums_wave(L, st, sk);
+    for (int bb = across ? 0 : lane; bb <= b && (!across || lane == 0); bb += 64) {
+      const BudgetSums sums = across ? sums0 : budget_sums_lds(L, st + (size_t)bb * L, sk + (size_t)bb * L);
       double x;
       int bud;
       layer_budget(sh, sums, st[(size_t)bb * L + l], sk[(size_t)bb * L + l], &x, &bud);
