@@ -998,9 +998,9 @@ __device__ __forceinline__ void fused_elite_logits(const Shape &sh, const typena
 // adds them to its own in ascending part order, forms the set
 // { j : pbar_j >= alpha max pbar } as one bit mask per 64 text tokens, and
 // publishes it with agent-coherent stores: erec[lb] = [size, then each mask
-// word as two 32-bit halves]; also the plan's elite list and count, and the
-// overflow flag when the set exceeds the elite cap. N_t <= 1024 (two entries
-// per thread).
+// word as two 32-bit halves]; also the plan's elite list and count (the
+// overflow flag is set from the counts). N_t <= 1024 (two entries per
+// thread).
 template <typename Tag, int D>
 __device__ __forceinline__ void fused_elite_part(const Shape &sh, const FusedTables &tab, const PlanPtrs &plan,
                                                  const FusedWs &fw, int lb, int pi, unsigned epoch, float *z,
@@ -1138,15 +1138,15 @@ __device__ __forceinline__ void fused_elite_part(const Shape &sh, const FusedTab
   if (tid == 0) {
     store_coherent(&rec[0], tag | (uint64_t)(unsigned)total);
     plan.n_elite[lb] = total;
-    if (total > sh.cap) atomicOr(plan.status, AIRCACHE_DEV_ELITE_OVERFLOW);
   }
   __syncthreads();  // wtot and red are free again
 }
 
 // Every workgroup: the elite count of every (layer, sample), clamped to the
-// elite cap, into ntk (LDS), from the merges' epoch-tagged records.
+// elite cap, into ntk (LDS), from the merges' epoch-tagged records; with
+// flag_overflow, counts above the cap set the overflow status bit.
 __device__ __forceinline__ void fused_elite_counts(const Shape &sh, const FusedWs &fw, unsigned epoch, int *status,
-                                                   int *ntk) {
+                                                   int *ntk, bool flag_overflow) {
   const int LB = sh.L * sh.B;
   const auto rr = coherent_rsrc(fw.erec, (unsigned)((size_t)LB * fw.erec_stride * sizeof(uint64_t)));
   for (int lb = opaque_tid(); lb < LB; lb += kFusedThreads) {
@@ -1160,6 +1160,7 @@ __device__ __forceinline__ void fused_elite_counts(const Shape &sh, const FusedW
     }
     const int t = (int)(unsigned)v;
     ntk[lb] = t < sh.cap ? t : sh.cap;
+    if (flag_overflow && t > sh.cap) atomicOr(status, AIRCACHE_DEV_ELITE_OVERFLOW);
   }
   __syncthreads();
 }
@@ -1579,25 +1580,30 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
   int *owed = reinterpret_cast<int *>(lds + lo.owed);
   int *ntk_l = reinterpret_cast<int *>(lds + lo.ntk);
 
-  // Phase 0: the elite set of (layer, sample) me, me + P, ... (no counter: the
-  // readers check the records' tags). The status word is cleared before
-  // workgroup 0 publishes its first set; every status bit is set after some
-  // workgroup has seen all sets, so after the clear.
+  // Phase 0: the elite sets (no counter: the readers check the records'
+  // tags). Pair lb's part 0, with its merge, runs on workgroup P - 1 - lb
+  // (mod P), its parts 1.. from workgroup 0 up, so the merges, which finish
+  // last, land on the workgroups that get no item when there are fewer items
+  // than workgroups. The status word is cleared by workgroup 0 before it
+  // reads the counts, and its bits are set later: the overflow bit by
+  // workgroup 0 from the counts, the timeout bit after a wait has run out.
   if (me == 0 && tid == 0) {
     store_coherent(plan.status, 0);
     wait_all_memory();
   }
-  // A wave's loads complete in order and a barrier waits for them, so a
-  // prestage only pays where the workgroup would wait anyway: not in the
-  // waves that read the elite counts (their tiles are loaded by wave ncw +
-  // their index, when there is one) and not in the workgroups that merge a
-  // set (they finish last); at once in workgroups without a part (a part's
-  // own loads are bound by what one CU has in flight), after it in those
-  // with a part to publish.
+  // A wave's loads complete in order and a barrier waits for them, so the
+  // waves that read the elite counts issue no prestage loads (their tiles
+  // are loaded by wave ncw + their index, when there is one); the others
+  // prestage at once in workgroups without a part (a part's own loads are
+  // bound by what one CU has in flight), after their parts in the others
+  // (a merging workgroup then reads the counts late, but streams its first
+  // item's chunk as fast as the rest).
   const uint64_t hint = me < kFusedHintSlots ? fw.hint[me] : 0ull;
-  const int nparts = LB * fw.npp;
-  const bool former = me < nparts;
-  const bool merger = former && me % fw.npp == 0;
+  const int npp = fw.npp;
+  const int nother = LB * (npp - 1);  // parts 1.. in all (LB * npp <= P when npp > 1)
+  const bool merger = P - 1 - me < LB;
+  const bool other = me < nother;
+  const bool former = merger || other;
   const int ncw = ((LB < kFusedThreads ? LB : kFusedThreads) + 63) >> 6;  // waves that read the counts
   const int wave_id = tid >> 6;
   auto prestage = [&]() {
@@ -1606,12 +1612,14 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
     if (wave_id - ncw < ncw) fused_prestage<Tag, D>(sh, tab, hint, lds, lo, wave_id - ncw);
   };
   if (!former) prestage();
-  for (int t = me; t < nparts; t += P) {
-    const int lb = t / fw.npp;
-    fused_elite_part<Tag, D>(sh, tab, plan, fw, lb, t - lb * fw.npp, epoch, lds_f, lo.total, wtot, redf);
+  if (other) {
+    const int lb = me / (npp - 1);
+    fused_elite_part<Tag, D>(sh, tab, plan, fw, lb, me - lb * (npp - 1) + 1, epoch, lds_f, lo.total, wtot, redf);
   }
-  if (former && !merger) prestage();
-  fused_elite_counts(sh, fw, epoch, plan.status, ntk_l);
+  for (int lb = P - 1 - me; lb < LB; lb += P)
+    fused_elite_part<Tag, D>(sh, tab, plan, fw, lb, 0, epoch, lds_f, lo.total, wtot, redf);
+  if (former) prestage();
+  fused_elite_counts(sh, fw, epoch, plan.status, ntk_l, me == 0);
   fused_schedule(sh, fw, ntk_l, me, P, item_list, hdr, wtot);
   __syncthreads();
   const int kcap = uniform(hdr[0]);
@@ -1649,9 +1657,9 @@ __global__ __launch_bounds__(kFusedThreads) void cross_score_fused_kernel(Shape 
       const int rt0 = it.r * kFusedRtMax, left = it.cp.rtg - rt0;
       uint64_t h = 0ull;  // the prestaged tiles serve the first item only
       if (k == 0) {
-        // a wave's tiles were prestaged unless its workgroup merged a set, or
-        // it reads the counts and no wave was left to load them
-        if (!merger && (wave >= ncw || wave + ncw < kFusedWaves)) h = hint;
+        // a wave's tiles were prestaged unless it reads the counts and no
+        // wave was left to load them
+        if (wave >= ncw || wave + ncw < kFusedWaves) h = hint;
         if (tid == 0 && me < kFusedHintSlots) fw.hint[me] = fused_hint(it.plb, it.c, it.cp.ktw);
       }
       if (left >= 4) fused_pass<Tag, D, 4>(sh, fw, it, rt0, lds, lo, epoch, plan.status, h);
