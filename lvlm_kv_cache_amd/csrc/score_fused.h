@@ -496,34 +496,40 @@ __device__ __forceinline__ void fused_pass(const Shape &sh, const FusedWs &fw, c
     const auto rsrc = coherent_rsrc(fw.xrec + 2 * rbase, (unsigned)((size_t)fw.rec_stride * 16));
     float M = -INFINITY, Z = 0.f;
     const int nch = it.cp.nchunks;
-    constexpr int kXB = 4;  // records in flight per thread
+    constexpr int kXB = 8;  // chunks' records in flight per thread (one 16-byte load each)
     for (int c0 = 0; c0 < nch; c0 += kXB) {
-      uint64_t rm[kXB], rz[kXB];
+      // every record of the batch loaded, then the batch polled as a whole
+      // (unconditional reloads) and merged in chunk order
+      u32x4_t rw[kXB];
+      auto load_batch = [&]() {
 #pragma unroll
-      for (int j = 0; j < kXB; ++j) {
-        const int cj = c0 + j;
-        const unsigned off = (unsigned)((((size_t)cj * Hkv + gg) * rows_h + row) * 16);
-        if (cj < nch && cj != c) {
-          rm[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rsrc, (int)off, 0, 16));
-          rz[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rsrc, (int)off + 8, 0, 16));
-        } else {
-          rm[j] = pack_rec(m_own, epoch);
-          rz[j] = pack_rec(z, epoch);
+        for (int j = 0; j < kXB; ++j) {
+          const int cj = c0 + j;
+          const unsigned off = (cj < nch && cj != c)
+                                   ? (unsigned)((((size_t)cj * Hkv + gg) * rows_h + row) * 16)
+                                   : 0xfffffff0u;  // past the end: reads zeros, not used
+          rw[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 16));
         }
+      };
+      load_batch();
+      unsigned spins = 0;
+      for (;;) {
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < kXB; ++j) {
+          const int cj = c0 + j;
+          ok = ok && (cj >= nch || cj == c || (rw[j][1] == epoch && rw[j][3] == epoch));
+        }
+        if (ok || spin_expired(spins, status)) break;
+        __builtin_amdgcn_s_sleep(2);
+        load_batch();
       }
 #pragma unroll
       for (int j = 0; j < kXB; ++j) {
         const int cj = c0 + j;
         if (cj >= nch) break;
-        const unsigned off = (unsigned)((((size_t)cj * Hkv + gg) * rows_h + row) * 16);
-        unsigned spins = 0;
-        while ((unsigned)(rm[j] >> 32) != epoch || (unsigned)(rz[j] >> 32) != epoch) {
-          if (spin_expired(spins, status)) break;
-          __builtin_amdgcn_s_sleep(2);
-          rm[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rsrc, (int)off, 0, 16));
-          rz[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rsrc, (int)off + 8, 0, 16));
-        }
-        const float mj = __uint_as_float((unsigned)rm[j]), zj = __uint_as_float((unsigned)rz[j]);
+        const float mj = cj == c ? m_own : __uint_as_float(rw[j][0]);
+        const float zj = cj == c ? z : __uint_as_float(rw[j][2]);
         if (mj > -INFINITY) {
           const float mn = fmaxf(M, mj);
           Z = Z * exp2_fast(M - mn) + zj * exp2_fast(mj - mn);
