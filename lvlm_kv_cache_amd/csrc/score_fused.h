@@ -311,9 +311,12 @@ __device__ __forceinline__ void fused_prestage(const Shape &sh, const FusedTable
   const int wph = kFusedWaves / Hkv;
   const int g = wave / wph, sub = wave - g * wph;
   const int W = wph * 16 * ktw;
-  const int v0 = c * W + sub * ktw * 16;
   const int nt = ktw < kRing ? ktw : kRing;
-  if (v0 + nt * 16 > Nv) return;  // only visual keys (text keys need the elite list)
+  // only visual keys (text keys need the elite list); 64-bit, so that no hint
+  // value can wrap the row index
+  const long long v0l = (long long)c * W + (long long)sub * ktw * 16;
+  if (v0l + nt * 16 > Nv) return;
+  const int v0 = (int)v0l;
   const int l = plb / B, b = plb - l * B;
   const E *kb = static_cast<const E *>(tab.p[L + l]) + (size_t)(b * Hkv + g) * sh.S * D;
   unsigned char *ring = lds + lo.ring + (size_t)wave * kRing * kTileBytes;
