@@ -1031,9 +1031,11 @@ __device__ __forceinline__ void fused_elite_part(const Shape &sh, const FusedTab
   for (int g0 = gbeg; g0 < gend; g0 += gh) {
     const int ng = gend - g0 < gh ? gend - g0 : gh;
     const int items = ng * per_head;
-    // U items per wave at a time, U no more than a wave has
+    // U items per wave at a time, U no more than a wave has (float32
+    // fragments are twice as wide: at most two items, or the operands spill)
     const int per_wave = (items + NW - 1) / NW;
-    if (per_wave >= 4) fused_elite_logits<Tag, D, 4>(sh, q, k, b, g0, items, per_head, nkt, z, head_floats);
+    constexpr int UMAX = Tag::kBytes == 4 ? 2 : 4;
+    if (per_wave >= 4) fused_elite_logits<Tag, D, UMAX>(sh, q, k, b, g0, items, per_head, nkt, z, head_floats);
     else if (per_wave >= 2) fused_elite_logits<Tag, D, 2>(sh, q, k, b, g0, items, per_head, nkt, z, head_floats);
     else fused_elite_logits<Tag, D, 1>(sh, q, k, b, g0, items, per_head, nkt, z, head_floats);
     __syncthreads();
