@@ -5,7 +5,8 @@ launch configuration the benchmark times, each scoring path on the workloads
 it serves, plus small edge shapes: ragged tails, one and eight KV heads, MHA,
 head_dim 64, float32 and bfloat16, a single text token, alpha and ratio at
 their extremes, zero queries (every text token elite, several row passes),
-several samples, and a workspace reused across calls.
+several samples, a workspace reused across calls, and workload 3 with flat
+attention (every text token elite).
 """
 import numpy as np
 import pytest
@@ -47,6 +48,20 @@ def test_workload_run(cid):
     print(f"[parity] workload {cid} run", flush=True)
     inp = wl.make_inputs(cid, cid)
     g = run_gpu(inp, max_elite=0 if cid <= 2 else 64, run=True)
+    compare(inp, g, reference(inp, g))
+
+
+def test_workload_3_flat_attention_stress():
+    """Workload 3 at full size with the N(0,1)/sqrt(D) base (the stress run
+    behind bench.py --base-scale inv_sqrt_d): attention is flat, so every text
+    token is elite (N_tk = 128, 56 row tiles per KV head, many row groups);
+    no elite cap, one launch."""
+    import dataclasses
+    w = dataclasses.replace(wl.CONFIGS[3], base="inv_sqrt_d")
+    print("[parity] workload 3 flat-attention stress", flush=True)
+    inp = wl.make_inputs(w, 3)
+    g = run_gpu(inp, max_elite=0, run=True)
+    assert (g["n_elite"] == w.Nt).all()
     compare(inp, g, reference(inp, g))
 
 
