@@ -423,15 +423,16 @@ __global__ __launch_bounds__(256) void finalize_kernel(Shape sh, PlanPtrs plan, 
 // ----------------------------------------------------------------------------
 // Steps 2 + 3 + 4 in one launch when a whole row of logits fits in registers
 // (N_v <= 8 waves x 16 x KT). A persistent grid of one 8-wave workgroup per
-// CU walks the work items (layer-sample, KV head, row tile of 16 elite-query
-// rows) in order; the item count of each (layer, sample) follows from its
-// elite count. Per item: the elite queries are the MFMA A operand and 16 keys
-// at a time the B operand; wave w owns visual key tiles w, w + 8, ..., which
+// CU walks the work items (layer-sample, KV head, group of RT row tiles of 16
+// elite-query rows) in order; the item count of each (layer, sample) follows
+// from its elite count. Per item: the elite queries are the MFMA A operand
+// and 16 keys at a time the B operand (each key tile read from LDS once for
+// the item's RT row tiles, so K is streamed once per RT tiles); wave w owns visual key tiles w, w + 8, ..., which
 // stream through a per-wave LDS ring by DMA and whose logits stay in
 // registers; the few elite text keys enter the row max and row sum through an
 // online update. Exact row max and sum come from DPP row reductions, then a
 // fixed-order sum over the waves. Each wave writes the column sums of
-// exp2(S - M) / Z over the tile's rows for its key tiles as this item's partial
+// exp2(S - M) / Z over the item's rows for its key tiles as this item's partial
 // I_v; the last item of a (layer, sample) adds the partials in a fixed order
 // and runs the statistics and budget finisher.
 // ----------------------------------------------------------------------------
@@ -443,18 +444,27 @@ template <typename Tag, int D> constexpr int rows_ring() {
   return (131072 / (kRowsWaves * 16 * D * Tag::kBytes)) < 4 ? (131072 / (kRowsWaves * 16 * D * Tag::kBytes)) : 4;
 }
 
+// Row tiles per item of the rows kernel: 4, 2 or 1, as many as keep one
+// lane's query fragments and logits of the item (per row tile: D / 32
+// fragments and KT f32x4) within 112 registers.
+template <typename Tag, int D, int KT> constexpr int rows_rt() {
+  constexpr int per = (D / 32) * (Tag::kBytes == 4 ? 8 : 4) + 4 * KT;
+  return 4 * per <= 112 ? 4 : 2 * per <= 112 ? 2 : 1;
+}
+
 template <typename Tag, int D, int KT>
 __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh, LayerTable qt, LayerTable kt,
                                                                         PlanPtrs plan, Ws ws, int rt_max) {
   using E = typename Tag::store_t;
   constexpr int NW = kRowsWaves;
+  constexpr int RT = rows_rt<Tag, D, KT>();
   constexpr int kTileBytes = 16 * D * Tag::kBytes;  // one 16-key tile
   constexpr int kDma = kTileBytes / 1024;           // 16-byte DMA loads per lane per tile
   constexpr int kRing = rows_ring<Tag, D>();        // tiles in flight per wave
   static_assert(KT >= kRing, "ring deeper than the tile count");
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];  // ring[NW][kRing][tile] | el[cap]
-  __shared__ float red[NW][16];
-  __shared__ float rowv[16];
+  __shared__ float red[NW][16 * RT];
+  __shared__ float rowv[16 * RT];
   __shared__ int flag;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, grp = lane >> 4;
@@ -465,7 +475,8 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
     int t = plan.n_elite[x];
     return t < 0 ? 0 : (t > sh.cap ? sh.cap : t);
   };
-  auto item_count = [&](int x) { return sh.Hkv * ((sh.G * elite_count(x) + 15) >> 4); };
+  // items of a (layer, sample): KV heads x groups of RT row tiles
+  auto item_count = [&](int x) { return sh.Hkv * ((((sh.G * elite_count(x) + 15) >> 4) + RT - 1) / RT); };
   int lb = 0, base = 0, cnt = item_count(0);
   // Pass p covers items [p * grid, (p + 1) * grid); XCD x (blocks x, x + 8, ...
   // under round-robin dispatch) takes a contiguous eighth of each pass, so the
@@ -478,8 +489,8 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
       if (++lb < LB) cnt = item_count(lb);
     }
     if (lb >= LB) break;
-    const int nrt = cnt / sh.Hkv;
-    const int local = item - base, g = local / nrt, rt = local - g * nrt;
+    const int ngrp = cnt / sh.Hkv;  // row-tile groups of a KV head
+    const int local = item - base, g = local / ngrp, rg = local - g * ngrp;
     const int l = lb / sh.B, b = lb % sh.B;
     const int ntk = elite_count(lb);
     const int R = sh.G * ntk;
@@ -491,16 +502,19 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
     const E *kb = static_cast<const E *>(kt.p[l]) + (size_t)(b * sh.Hkv + g) * sh.S * D;
     const int nvt = (Nv + 15) >> 4;
     const int nxt = (ntk + 15) >> 4;
-    const int r = rt * 16 + n;
-    Frag<Tag> qf[D / 32];
-    if (r < R) {
-      const int hl = r / ntk, e = r - hl * ntk;
-      const E *qrow = q + ((size_t)(b * sh.Hq + g * sh.G + hl) * sh.Nt + el[e]) * D;
+    Frag<Tag> qf[RT][D / 32];
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) qf[c].load(qrow + c * 32 + grp * 8);
-    } else {
+    for (int j = 0; j < RT; ++j) {
+      const int r = (rg * RT + j) * 16 + n;
+      if (r < R) {
+        const int hl = r / ntk, e = r - hl * ntk;
+        const E *qrow = q + ((size_t)(b * sh.Hq + g * sh.G + hl) * sh.Nt + el[e]) * D;
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) qf[c].zero();
+        for (int c = 0; c < D / 32; ++c) qf[j][c].load(qrow + c * 32 + grp * 8);
+      } else {
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) qf[j][c].zero();
+      }
     }
     // Visual key tiles through the LDS ring. Loads are issued for every slot
     // (an empty slot rereads the last visual row and is ignored) so the count
@@ -510,9 +524,15 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
     // visual tiles w, w + NW, .... Tiles stream through a per-wave LDS ring by
     // DMA; loads are issued for every slot (an empty slot rereads a valid row
     // and is ignored) so the count of loads in flight is static.
-    f32x4_t S[KT];
-    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    float zx[4] = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t S[RT][KT];
+    float mx[RT][4], zx[RT][4];
+#pragma unroll
+    for (int j = 0; j < RT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mx[j][i] = -INFINITY;
+        zx[j][i] = 0.f;
+      }
     auto stage = [&](int t) {
       int row;
       if (t == 0) {
@@ -537,27 +557,34 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
     for (int t = 0; t <= KT; ++t) {
       // tile t has landed once only the loads of the tiles staged after it remain
       wait_tiles<kDma>(min(kRing - 1, KT - t));
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t acc[RT];
+#pragma unroll
+      for (int j = 0; j < RT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const unsigned char *slot = ring + (t % kRing) * kTileBytes;
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) {
         Frag<Tag> kf;
         LdsTile<Tag>::read(kf, slot, c, lane);
-        mfma_slice(acc, qf[c], kf);
+#pragma unroll
+        for (int j = 0; j < RT; ++j) mfma_slice(acc[j], qf[j][c], kf);
       }
       if (t + kRing <= KT) stage(t + kRing);
       if (t == 0) {
         if (wave < nxt && wave * 16 + n < ntk) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            mx[i] = acc[i] * sh.scale2;
-            zx[i] = 1.f;
-          }
+          for (int j = 0; j < RT; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              mx[j][i] = acc[j][i] * sh.scale2;
+              zx[j][i] = 1.f;
+            }
         }
       } else {
         const bool ok = (wave + NW * (t - 1)) * 16 + n < Nv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[t - 1][i] = ok ? acc[i] * sh.scale2 : -INFINITY;
+        for (int j = 0; j < RT; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[j][t - 1][i] = ok ? acc[j][i] * sh.scale2 : -INFINITY;
       }
     }
     // Elite text tiles beyond one per wave (elite windows over 16 x NW tokens).
@@ -572,73 +599,91 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) kf[c].zero();
       }
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) mfma_slice(acc, qf[c], kf[c]);
-      if (e < ntk) {
+      for (int j = 0; j < RT; ++j) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = acc[i] * sh.scale2;
-          const float mn = fmaxf(mx[i], v);
-          zx[i] = zx[i] * exp2f(mx[i] - mn) + exp2f(v - mn);
-          mx[i] = mn;
+        for (int c = 0; c < D / 32; ++c) mfma_slice(acc, qf[j][c], kf[c]);
+        if (e < ntk) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = acc[i] * sh.scale2;
+            const float mn = fmaxf(mx[j][i], v);
+            zx[j][i] = zx[j][i] * exp2f(mx[j][i] - mn) + exp2f(v - mn);
+            mx[j][i] = mn;
+          }
         }
       }
     }
-    float mr[4] = {mx[0], mx[1], mx[2], mx[3]};
+    // lane holds rows grp*4+i of row tile j and key n: reduce over keys (DPP
+    // rows), then waves
 #pragma unroll
-    for (int k = 0; k < KT; ++k) {
+    for (int j = 0; j < RT; ++j) {
+      float mr[4] = {mx[j][0], mx[j][1], mx[j][2], mx[j][3]};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mr[i] = fmaxf(mr[i], S[k][i]);
-    }
-    // lane holds rows grp*4+i of key n: reduce over keys (DPP rows), then waves
+      for (int k = 0; k < KT; ++k) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mr[i] = row16_max(mr[i]);
-    if (n == 0) {
+        for (int i = 0; i < 4; ++i) mr[i] = fmaxf(mr[i], S[j][k][i]);
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][grp * 4 + i] = mr[i];
+      for (int i = 0; i < 4; ++i) mr[i] = row16_max(mr[i]);
+      if (n == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][j * 16 + grp * 4 + i] = mr[i];
+      }
     }
     __syncthreads();
-    if (tid < 16) {
+    if (tid < 16 * RT) {
       float m = red[0][tid];
       for (int w = 1; w < NW; ++w) m = fmaxf(m, red[w][tid]);
       rowv[tid] = m;
     }
     __syncthreads();
-    float zr[4];
+    float zr[RT][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float M = rowv[grp * 4 + i];
-      zr[i] = (mx[i] > -INFINITY) ? zx[i] * exp2f(mx[i] - M) : 0.f;
+    for (int j = 0; j < RT; ++j)
 #pragma unroll
-      for (int k = 0; k < KT; ++k) {
-        const float ev = exp2f(S[k][i] - M);
-        S[k][i] = ev;
-        zr[i] += ev;
+      for (int i = 0; i < 4; ++i) {
+        const float M = rowv[j * 16 + grp * 4 + i];
+        zr[j][i] = (mx[j][i] > -INFINITY) ? zx[j][i] * exp2f(mx[j][i] - M) : 0.f;
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+          const float ev = exp2f(S[j][k][i] - M);
+          S[j][k][i] = ev;
+          zr[j][i] += ev;
+        }
+        zr[j][i] = row16_sum(zr[j][i]);
       }
-      zr[i] = row16_sum(zr[i]);
-    }
     __syncthreads();  // every lane has read rowv
     if (n == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][grp * 4 + i] = zr[i];
+      for (int j = 0; j < RT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][j * 16 + grp * 4 + i] = zr[j][i];
     }
     __syncthreads();
-    if (tid < 16) {
+    if (tid < 16 * RT) {
       float z = 0.f;
       for (int w = 0; w < NW; ++w) z += red[w][tid];
-      rowv[tid] = (rt * 16 + tid < R) ? 1.f / z : 0.f;
+      rowv[tid] = (rg * RT * 16 + tid < R) ? 1.f / z : 0.f;
     }
     __syncthreads();
-    float W[4];
+    float W[RT][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) W[i] = rowv[grp * 4 + i];
-    float *part = ws.part + ((size_t)(lb * sh.Hkv + g) * rt_max + rt) * Nv;
+    for (int j = 0; j < RT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) W[j][i] = rowv[j * 16 + grp * 4 + i];
+    float *part = ws.part + ((size_t)(lb * sh.Hkv + g) * rt_max + rg) * Nv;
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
       const int ti = wave + NW * k;
       if (ti < nvt) {  // wave-uniform
-        const float cs = sum_across_rows(S[k][0] * W[0] + S[k][1] * W[1] + S[k][2] * W[2] + S[k][3] * W[3]);
+        // the item's row tiles in order, each its four rows in order
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < RT; ++j)
+          a += S[j][k][0] * W[j][0] + S[j][k][1] * W[j][1] + S[j][k][2] * W[j][2] + S[j][k][3] * W[j][3];
+        const float cs = sum_across_rows(a);
         const int c = ti * 16 + n;
         if (grp == 0 && c < Nv) store_coherent(&part[c], cs);
       }
@@ -646,22 +691,22 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
     wait_all_memory();
     __syncthreads();
     const int u = lb * sh.Hkv + g;
-    float *unit_part = ws.part + (size_t)u * rt_max * Nv;  // row tile 0 slot holds the unit's sum
-    if (nrt > 1) {
-      // last row tile of (l, b, g): add the unit's row-tile partials in order
-      if (tid == 0) flag = (counter_add(&ws.cnt_unit[u], 1u) == (unsigned)nrt - 1);
+    float *unit_part = ws.part + (size_t)u * rt_max * Nv;  // group 0's slot holds the unit's sum
+    if (ngrp > 1) {
+      // last row-tile group of (l, b, g): add the unit's group partials in order
+      if (tid == 0) flag = (counter_add(&ws.cnt_unit[u], 1u) == (unsigned)ngrp - 1);
       __syncthreads();
       if (!flag) continue;
-      const auto rp = coherent_rsrc(unit_part, (unsigned)((size_t)nrt * Nv * sizeof(float)));
+      const auto rp = coherent_rsrc(unit_part, (unsigned)((size_t)ngrp * Nv * sizeof(float)));
       for (int c = tid; c < Nv; c += kRowsThreads) {
         float v[8];
         float a = 0.f;
-        for (int t0 = 0; t0 < nrt; t0 += 8) {
+        for (int t0 = 0; t0 < ngrp; t0 += 8) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) v[j] = load_sc1_f(rp, (unsigned)(((t0 + j) * Nv + c) * sizeof(float)));
 #pragma unroll
           for (int j = 0; j < 8; ++j)
-            if (t0 + j < nrt) a += v[j];
+            if (t0 + j < ngrp) a += v[j];
         }
         store_coherent(&unit_part[c], a);
       }
