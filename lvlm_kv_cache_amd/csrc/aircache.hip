@@ -446,10 +446,11 @@ template <typename Tag, int D> constexpr int rows_ring() {
 
 // Row tiles per item of the rows kernel: 4, 2 or 1, as many as keep one
 // lane's query fragments and logits of the item (per row tile: D / 32
-// fragments and KT f32x4) within 112 registers.
+// fragments and KT f32x4) within what the kernel has left without spilling
+// (found by compiling: 128 registers for four tiles, 112 for two).
 template <typename Tag, int D, int KT> constexpr int rows_rt() {
   constexpr int per = (D / 32) * (Tag::kBytes == 4 ? 8 : 4) + 4 * KT;
-  return 4 * per <= 112 ? 4 : 2 * per <= 112 ? 2 : 1;
+  return 4 * per <= 128 ? 4 : 2 * per <= 112 ? 2 : 1;
 }
 
 template <typename Tag, int D, int KT>
@@ -1156,7 +1157,8 @@ struct Config {
 constexpr size_t kEpochBytes = 256;
 
 // Register budgets of cross_score_rows_kernel instantiations (key tiles per wave).
-constexpr int kRowsKt[] = {4, 8, 16, 24};
+constexpr int kRowsKt[] = {4, 5, 8, 16, 24};
+constexpr int kRowsKtMax = 24;
 
 int make_config(const aircache_desc *d, Config *cfg) {
   g_last_error.clear();
@@ -1234,7 +1236,7 @@ int make_config(const aircache_desc *d, Config *cfg) {
   if ((size_t)s.Nv * sizeof(float) > (size_t)kRowsWaves * ring * tile_bytes) cfg->rows_kt = 0;  // finisher's I_v
   if (cfg->rows_kt && cfg->rows_lds > kMaxLds) cfg->rows_kt = 0;
   if (d->path == AIRCACHE_PATH_ROWS && !cfg->rows_kt)
-    return fail(AIRCACHE_EINVAL, "the rows path needs n_vis <= %d", kRowsWaves * 16 * kRowsKt[3]);
+    return fail(AIRCACHE_EINVAL, "the rows path needs n_vis <= %d", kRowsWaves * 16 * kRowsKtMax);
   // Chunked path: power-of-two KV head count up to the wave count, its LDS
   // layout within the limit, and a bounded item count per workgroup on a
   // 256-CU device.
@@ -1554,6 +1556,7 @@ int launch_plan(const Config &cfg, const LayerTable &qt, const LayerTable &kt, c
   if (cfg.rows_kt) {
     // scoring, statistics and budgets in one launch; the finalize stage is empty
     if (cfg.rows_kt == 4) rc = launch_rows<Tag, D, 4>(cfg, qt, kt, pp, ws, st);
+    else if (cfg.rows_kt == 5) rc = launch_rows<Tag, D, 5>(cfg, qt, kt, pp, ws, st);
     else if (cfg.rows_kt == 8) rc = launch_rows<Tag, D, 8>(cfg, qt, kt, pp, ws, st);
     else if (cfg.rows_kt == 16) rc = launch_rows<Tag, D, 16>(cfg, qt, kt, pp, ws, st);
     else rc = launch_rows<Tag, D, 24>(cfg, qt, kt, pp, ws, st);
