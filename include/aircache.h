@@ -104,8 +104,9 @@ typedef struct {
 
 /* Scoring paths. TILED: column tiles of every (layer, sample, KV head) with
  * the exponentials spilled to the workspace and a separate merge kernel; any
- * size. ROWS: one workgroup per 16 elite-query rows keeps a whole row of
- * logits in registers (n_vis <= 3072). CHUNKED: one persistent launch for
+ * size. ROWS: a workgroup per group of up to four 16-row tiles of elite
+ * queries keeps their whole rows of logits in registers (n_vis <= 3072).
+ * CHUNKED: one persistent launch for
  * scoring, statistics, budgets and top-k; a workgroup takes a run of visual
  * keys of every KV head of one (layer, sample) and swaps row maxima and sums
  * with the other runs (n_kv_heads in {1, 2, 4, 8}). AUTO picks CHUNKED, else

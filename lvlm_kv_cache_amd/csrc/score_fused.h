@@ -1547,10 +1547,17 @@ __device__ __forceinline__ void fused_gather_unit(const Shape &sh, const PlanPtr
   const char *src = src_l + (size_t)(b * sh.Hkv + g) * sh.S * rb;
   char *dst = dst_l + (size_t)off * fw.esize + (size_t)g * n * rb;
   const auto rk = coherent_rsrc(fw.keptrec + (size_t)plb * Nv, (unsigned)(Nv * sizeof(uint64_t)));
+  // only the bud kept words are read (past them: the out-of-range offset,
+  // zeros without a memory access), so a poll round moves bud words
   uint64_t kw[KW];
+  auto load_kept = [&]() {
 #pragma unroll
-  for (int j = 0; j < KW; ++j)
-    kw[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rk, (tid + j * NT) * 8, 0, 16));
+    for (int j = 0; j < KW; ++j) {
+      const unsigned o = tid + j * NT < bud ? (unsigned)((tid + j * NT) * 8) : 0xfffffff0u;
+      kw[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rk, (int)o, 0, 16));
+    }
+  };
+  load_kept();
   fused_copy_rows(src, dst, rb, cs, bud, n, sh.S, [&](int i) { return Nv + (i - bud); });
   unsigned spins = 0;
   for (;;) {
@@ -1558,9 +1565,7 @@ __device__ __forceinline__ void fused_gather_unit(const Shape &sh, const PlanPtr
 #pragma unroll
     for (int j = 0; j < KW; ++j) ok = ok && (tid + j * NT >= bud || (unsigned)(kw[j] >> 32) == epoch);
     if (ok || spin_expired(spins, plan.status)) break;
-#pragma unroll
-    for (int j = 0; j < KW; ++j)
-      kw[j] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rk, (tid + j * NT) * 8, 0, 16));
+    load_kept();
   }
 #pragma unroll
   for (int j = 0; j < KW; ++j)
