@@ -154,6 +154,38 @@ def test_bound_pass_matches_plain_calls():
             assert torch.equal(vo[l][:n].cpu(), torch.from_numpy(plain["v_out"][l].view(np.int16)).view(vo[l].dtype))
 
 
+def _random_shapes(n, seed=2024):
+    """Seeded small shapes over the knobs the launch configuration depends on:
+    layers x samples (how many elite-set parts and merges, and on which
+    workgroups), KV heads and group size, ragged N_v and N_t, dtype, alpha and
+    ratio."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 3, 7]))
+        out.append(dict(L=int(rng.integers(1, 9)), B=int(rng.integers(1, 4)), Hkv=hkv, Hq=hkv * G,
+                        D=int(rng.choice([64, 128])), Nv=int(rng.integers(3, 1500)), Nt=int(rng.integers(1, 150)),
+                        dtype=str(rng.choice(["bf16", "f32"])), alpha=float(rng.choice([0.5, 0.9, 1.0])),
+                        ratio=float(rng.choice([0.05, 0.2, 0.5]))))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_shapes(20), ids=lambda s: "x".join(f"{k}{v}" for k, v in s.items()))
+@pytest.mark.parametrize("path", ["auto-run", "rows"])
+def test_random_shapes(shape, path):
+    """Seeded random small shapes on the one-launch pass and the rows path."""
+    if path == "rows" and shape["Nv"] > 3072:
+        pytest.skip("the rows path serves N_v <= 3072")
+    print(f"[parity] random {shape} path {path}", flush=True)
+    kw = dict(shape)
+    alpha, ratio = kw.pop("alpha"), kw.pop("ratio")
+    w = wl.custom(alpha=alpha, ratio=ratio, **kw)
+    inp = wl.make_inputs(w, 11)
+    g = run_gpu(inp, path=path.split("-")[0], run=path.endswith("-run"))
+    compare(inp, g, reference(inp, g, alpha=alpha, ratio=ratio), ratio=ratio)
+
+
 @pytest.mark.parametrize("alpha,ratio", [(0.0, 0.1), (1.0, 0.1), (0.9, 0.0), (0.9, 1.0), (0.5, 0.5)])
 def test_alpha_ratio_extremes(alpha, ratio):
     w = wl.custom(Nv=200, Nt=24, Hq=6, Hkv=2, D=128, dtype="bf16", L=3, B=2)
