@@ -50,7 +50,7 @@ def lib():
         l.orc_cross_score.restype = None
         l.orc_layer_stats.argtypes = [P, C.c_int, P, P]
         l.orc_layer_stats.restype = None
-        l.orc_budget.argtypes = [P, P, C.c_int, C.c_double, C.c_int, P, P]
+        l.orc_budget.argtypes = [P, P, C.c_int, C.c_double, C.c_int, C.c_int, P, P]
         l.orc_budget.restype = None
         l.orc_topk.argtypes = [P, C.c_int, C.c_int, P]
         l.orc_topk.restype = None
@@ -111,14 +111,16 @@ def layer_stats(iv) -> tuple[float, float]:
     return st.value, sk.value
 
 
-def budget(s_t, s_k, ratio: float, Nv: int):
-    """Step 4 for one sample: (x[L], budget[L])."""
+def budget(s_t, s_k, ratio: float, Nv: int, mode: int = 0):
+    """Step 4 for one sample: (x[L], budget[L]). mode: 0 the page's rule
+    (strength and skewness), 1 uniform, 2 strength only, 3 skewness only (the
+    allocation ablation's variants, see orc_budget)."""
     st = np.ascontiguousarray(s_t, dtype=np.float64)
     sk = np.ascontiguousarray(s_k, dtype=np.float64)
     L = len(st)
     x = np.zeros(L, np.float64)
     r = np.zeros(L, np.int32)
-    lib().orc_budget(_ptr(st), _ptr(sk), L, float(ratio), int(Nv), _ptr(x), _ptr(r))
+    lib().orc_budget(_ptr(st), _ptr(sk), L, float(ratio), int(Nv), int(mode), _ptr(x), _ptr(r))
     return x, r
 
 

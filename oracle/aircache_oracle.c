@@ -175,8 +175,13 @@ void orc_layer_stats(const double *iv, int n, double *s_t, double *s_k) {
  * s't = s_t * L / sum(s_t); shift m = min(0, min s_k), u = s_k - m,
  * s'k = u * L / sum(u) (1 for every layer when sum(u) = 0);
  * x = 0.5 * (s't + s'k) * (ratio * N_v); budget = clamp(floor(x), 0, N_v).
+ * mode picks the allocation rule: 0 the page's (strength and skewness,
+ * "Layer-wise KV Cache Budget Allocation", the r_hat equation); the variants
+ * of that section's allocation ablation table, read as the same equation with
+ * one term: 1 uniform, x = ratio * N_v; 2 strength only, x = s't * ratio *
+ * N_v; 3 skewness only, x = s'k * ratio * N_v.
  */
-void orc_budget(const double *s_t, const double *s_k, int L, double ratio, int Nv,
+void orc_budget(const double *s_t, const double *s_k, int L, double ratio, int Nv, int mode,
                 double *x, int32_t *budget) {
   double st_sum = 0.0, m = 0.0, u_sum = 0.0;
   for (int l = 0; l < L; ++l) st_sum += s_t[l];
@@ -187,7 +192,7 @@ void orc_budget(const double *s_t, const double *s_k, int L, double ratio, int N
   for (int l = 0; l < L; ++l) {
     double stn = s_t[l] * (double)L / st_sum;
     double skn = (u_sum > 0.0) ? (s_k[l] - m) * (double)L / u_sum : 1.0;
-    x[l] = 0.5 * (stn + skn) * r;
+    x[l] = mode == 1 ? r : mode == 2 ? stn * r : mode == 3 ? skn * r : 0.5 * (stn + skn) * r;
     double f = floor(x[l]);
     if (!(f > 0.0)) f = 0.0; /* also maps NaN to 0 */
     if (f > (double)Nv) f = (double)Nv;
@@ -287,7 +292,7 @@ int orc_run(const orc_desc *w, const void *const *q, const void *const *k,
       st[l] = s_t[(size_t)l * B + b];
       sk[l] = s_k[(size_t)l * B + b];
     }
-    orc_budget(st, sk, L, w->ratio, w->Nv, xx, bb);
+    orc_budget(st, sk, L, w->ratio, w->Nv, 0, xx, bb);
     for (int l = 0; l < L; ++l) {
       x[(size_t)l * B + b] = xx[l];
       budget[(size_t)l * B + b] = bb[l];

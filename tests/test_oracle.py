@@ -267,6 +267,48 @@ def test_budget_mean_is_r_and_single_layer():
     assert abs(x[0] - 57.6) < 1e-12 and r[0] == 57
 
 
+# Allocation variants of the page's ablation ("Layer-wise KV Cache Budget
+# Allocation", the allocation table), read as the r_hat equation with one
+# term (or none): 1 uniform, 2 strength only, 3 skewness only.
+#  a) uniform: every layer floor(ratio * N_v), whatever the statistics
+#  b) strength only, s_t=[1,3] (L=2): s't=[0.5,1.5], r=0.125*64=8 -> x=[4,12]
+#  c) skewness only, s_k=[-1,1]: m=-1, u=[0,2], s'k=[0,2], r=8 -> x=[0,16]
+#  d) skewness only with sum(u)=0 (s_k all equal): s'k=1 -> x=r
+@pytest.mark.parametrize("L", [1, 3, 28])
+def test_budget_uniform_variant(L):
+    rng = np.random.default_rng(L)
+    st, sk = rng.uniform(0.1, 2.0, L), rng.normal(0.0, 3.0, L)
+    x, r = oracle.budget(st, sk, 0.1, 2880, mode=1)
+    assert np.all(x == 0.1 * 2880) and list(r) == [288] * L
+
+
+def test_budget_single_term_variants():
+    x, r = oracle.budget([1.0, 3.0], [5.0, -7.0], 0.125, 64, mode=2)
+    assert np.allclose(x, [4.0, 12.0], rtol=0, atol=1e-12) and list(r) == [4, 12]
+    x, r = oracle.budget([9.0, 0.1], [-1.0, 1.0], 0.125, 64, mode=3)
+    assert np.allclose(x, [0.0, 16.0], rtol=0, atol=1e-12) and list(r) == [0, 16]
+    x, r = oracle.budget([9.0, 0.1, 4.0], [-2.5, -2.5, -2.5], 0.125, 64, mode=3)
+    assert np.all(x == 8.0) and list(r) == [8, 8, 8]
+
+
+def test_budget_rule_is_mean_of_single_terms():
+    """The page's x is the mean of the strength-only and skewness-only x, up to
+    rounding; the budgets of the single-term variants also sum to L * r."""
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        L = int(rng.integers(1, 40))
+        st, sk = rng.uniform(0.5, 1.0, L), rng.normal(1.0, 2.0, L)
+        ratio, nv = float(rng.uniform(0.01, 0.3)), int(rng.integers(3, 7000))
+        x0, _ = oracle.budget(st, sk, ratio, nv)
+        x2, r2 = oracle.budget(st, sk, ratio, nv, mode=2)
+        x3, r3 = oracle.budget(st, sk, ratio, nv, mode=3)
+        assert np.allclose(x0, 0.5 * (x2 + x3), rtol=1e-12, atol=1e-9)
+        for x in (x2, x3):
+            assert abs(x.sum() - L * ratio * nv) <= 1e-9 * L * ratio * nv
+        for x, r in ((x2, r2), (x3, r3)):
+            assert np.array_equal(r, np.clip(np.floor(x), 0, nv).astype(int))
+
+
 # ---------------------------------------------------------------- step 5 ----
 
 def check_topk(scores, k, kept):
