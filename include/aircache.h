@@ -100,7 +100,20 @@ typedef struct {
   int32_t max_elite;  /* workspace cap on elite tokens per (layer, sample); 0 means n_txt */
   int32_t path;       /* scoring kernels: AIRCACHE_PATH_AUTO (0), _TILED (1), _ROWS (2)
                          or _CHUNKED (3); every path computes the same results */
+  int32_t budget_mode; /* layer allocation rule, AIRCACHE_BUDGET_*; 0 is the method's */
 } aircache_desc;
+
+/* Layer budget allocation rules. AIRCACHE (0): the method's, r_hat =
+ * 0.5 * (s'_t + s'_k) * r ("Layer-wise KV Cache Budget Allocation", the r_hat
+ * equation). The others are the variants that section's allocation ablation
+ * compares, read as the same equation with one term or none: UNIFORM (1)
+ * r_hat = r, STRENGTH (2) r_hat = s'_t * r, SKEWNESS (3) r_hat = s'_k * r; each
+ * floored and clamped to [0, N_v] as the method's. (The ablation's pyramid rule
+ * has no formula on the page and is not offered.) */
+#define AIRCACHE_BUDGET_AIRCACHE 0
+#define AIRCACHE_BUDGET_UNIFORM 1
+#define AIRCACHE_BUDGET_STRENGTH 2
+#define AIRCACHE_BUDGET_SKEWNESS 3
 
 /* Scoring paths. TILED: column tiles of every (layer, sample, KV head) with
  * the exponentials spilled to the workspace and a separate merge kernel; any

@@ -16,16 +16,19 @@ _DTYPES = {torch.float32: _lib.AIRCACHE_F32, torch.bfloat16: _lib.AIRCACHE_BF16}
 
 
 _PATHS = {"auto": _lib.PATH_AUTO, "tiled": _lib.PATH_TILED, "rows": _lib.PATH_ROWS, "chunked": _lib.PATH_CHUNKED}
+# layer budget rules: the method's, then its allocation ablation's variants
+_BUDGETS = {"aircache": 0, "uniform": 1, "strength": 2, "skewness": 3}
 
 
 def make_desc(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt, dtype,
-              alpha=0.9, ratio=0.1, max_elite=0, path="auto") -> _lib.Desc:
+              alpha=0.9, ratio=0.1, max_elite=0, path="auto", budget_mode=0) -> _lib.Desc:
     if isinstance(dtype, torch.dtype):
         dtype = _DTYPES[dtype]
     elif isinstance(dtype, str):
         dtype = {"f32": _lib.AIRCACHE_F32, "bf16": _lib.AIRCACHE_BF16}[dtype]
     return _lib.Desc(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt, dtype,
-                     float(alpha), float(ratio), int(max_elite), _PATHS[path] if isinstance(path, str) else int(path))
+                     float(alpha), float(ratio), int(max_elite), _PATHS[path] if isinstance(path, str) else int(path),
+                     _BUDGETS[budget_mode] if isinstance(budget_mode, str) else int(budget_mode))
 
 
 @dataclasses.dataclass
@@ -65,7 +68,8 @@ class AirCache:
     """
 
     def __init__(self, n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt,
-                 dtype=torch.bfloat16, alpha=0.9, ratio=0.1, max_elite=0, device="cuda", path="auto"):
+                 dtype=torch.bfloat16, alpha=0.9, ratio=0.1, max_elite=0, device="cuda", path="auto",
+                 budget_mode="aircache"):
         self.shape = dict(L=n_layers, B=batch, Hq=n_q_heads, Hkv=n_kv_heads, D=head_dim,
                           Nv=n_vis, Nt=n_txt)
         self.dtype = dtype
@@ -73,7 +77,7 @@ class AirCache:
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
         self.desc = make_desc(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt,
-                              dtype, alpha, ratio, max_elite, path)
+                              dtype, alpha, ratio, max_elite, path, budget_mode)
         ws = _lib.workspace_size(self.desc)
         if ws == 0:
             _lib.check(_lib.AIRCACHE_EINVAL)

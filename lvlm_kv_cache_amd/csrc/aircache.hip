@@ -37,6 +37,7 @@ struct Shape {
   float alpha;
   float scale2;  // log2(e) / sqrt(D): logits are kept in the base-2 domain
   double ratio;
+  int budget_mode;  // AIRCACHE_BUDGET_*
 };
 
 struct PlanPtrs {
@@ -235,7 +236,12 @@ __device__ __forceinline__ void layer_budget(const Shape &sh, const BudgetSums &
   const double rr = sh.ratio * (double)sh.Nv;
   const double stn = st * (double)sh.L / r.st_sum;
   const double skn = (r.u_sum > 0.0) ? (sk - r.mshift) * (double)sh.L / r.u_sum : 1.0;
-  const double x = 0.5 * (stn + skn) * rr;
+  // the method's rule, or one of its allocation ablation's variants
+  const int mode = sh.budget_mode;
+  const double x = mode == AIRCACHE_BUDGET_UNIFORM    ? rr
+                   : mode == AIRCACHE_BUDGET_STRENGTH ? stn * rr
+                   : mode == AIRCACHE_BUDGET_SKEWNESS ? skn * rr
+                                                      : 0.5 * (stn + skn) * rr;
   double f = floor(x);
   if (!(f > 0.0)) f = 0.0;
   if (f > (double)sh.Nv) f = (double)sh.Nv;
@@ -1180,6 +1186,8 @@ int make_config(const aircache_desc *d, Config *cfg) {
     return fail(AIRCACHE_EINVAL, "max_elite=%d outside [0, n_txt=%d]", d->max_elite, d->n_txt);
   if (d->path < AIRCACHE_PATH_AUTO || d->path > AIRCACHE_PATH_CHUNKED)
     return fail(AIRCACHE_EINVAL, "path=%d unknown", d->path);
+  if (d->budget_mode < AIRCACHE_BUDGET_AIRCACHE || d->budget_mode > AIRCACHE_BUDGET_SKEWNESS)
+    return fail(AIRCACHE_EINVAL, "budget_mode=%d unknown", d->budget_mode);
   Shape &s = cfg->sh;
   s.L = d->n_layers;
   s.B = d->batch;
@@ -1203,6 +1211,7 @@ int make_config(const aircache_desc *d, Config *cfg) {
   s.alpha = (float)d->alpha;
   s.scale2 = (float)(1.4426950408889634 / sqrt((double)s.D));
   s.ratio = d->ratio;
+  s.budget_mode = d->budget_mode;
   const int esz = d->dtype == AIRCACHE_BF16 ? 2 : 4;
   (void)esz;
   cfg->elite_lds = (size_t)(s.G > 1 ? s.G : 1) * s.Nt * sizeof(float);

@@ -47,20 +47,21 @@ def torch_dtype(w):
     return torch.float32 if w.dtype == wl.F32 else torch.bfloat16
 
 
-def make_aircache(w, alpha=None, ratio=None, max_elite=0, path="auto"):
+def make_aircache(w, alpha=None, ratio=None, max_elite=0, path="auto", budget_mode=0):
     return AirCache(w.L, w.B, w.Hq, w.Hkv, w.D, w.Nv, w.Nt, dtype=torch_dtype(w),
                     alpha=w.alpha if alpha is None else alpha,
-                    ratio=w.ratio if ratio is None else ratio, max_elite=max_elite, path=path)
+                    ratio=w.ratio if ratio is None else ratio, max_elite=max_elite, path=path,
+                    budget_mode=budget_mode)
 
 
 def run_gpu(inp: wl.Inputs, alpha=None, ratio=None, max_elite=0, tensors=None, compress=True, path="auto", ac=None,
-            run=False):
+            run=False, budget_mode=0):
     """Plan (and compress) on the GPU; ac: an AirCache to reuse (its workspace
     carries state from earlier calls); run: one aircache_run call instead of
     aircache_plan then aircache_compress."""
     w = inp.w
     if ac is None:
-        ac = make_aircache(w, alpha, ratio, max_elite, path)
+        ac = make_aircache(w, alpha, ratio, max_elite, path, budget_mode)
     q, k, v = tensors if tensors is not None else to_torch(inp)
     out = {}
     if run:
@@ -88,7 +89,7 @@ def run_gpu(inp: wl.Inputs, alpha=None, ratio=None, max_elite=0, tensors=None, c
     return out
 
 
-def reference(inp: wl.Inputs, gpu: dict, alpha=None, ratio=None):
+def reference(inp: wl.Inputs, gpu: dict, alpha=None, ratio=None, budget_mode=0):
     """Oracle values for every (l, b), conditional on the GPU's elite sets where
     they differ only in threshold-ambiguous tokens."""
     w = inp.w
@@ -123,7 +124,9 @@ def reference(inp: wl.Inputs, gpu: dict, alpha=None, ratio=None):
     ref["x"] = np.zeros((L, B))
     ref["budget"] = np.zeros((L, B), np.int32)
     for b in range(B):
-        ref["x"][:, b], ref["budget"][:, b] = oracle.budget(ref["s_t"][:, b], ref["s_k"][:, b], ratio, w.Nv)
+        ref["x"][:, b], ref["budget"][:, b] = oracle.budget(ref["s_t"][:, b], ref["s_k"][:, b], ratio, w.Nv,
+                                                            budget_mode)
+    ref["budget_mode"] = budget_mode
     return ref
 
 
@@ -151,7 +154,7 @@ def compare(inp: wl.Inputs, gpu: dict, ref: dict, ratio=None, check_compacted=Tr
             assert abs(sk - gpu["s_k"][l, b]) <= 1e-7 * max(1.0, abs(sk))
     # budgets: conditional (exact) and end to end
     for b in range(B):
-        x, r = oracle.budget(gpu["s_t"][:, b], gpu["s_k"][:, b], ratio, w.Nv)
+        x, r = oracle.budget(gpu["s_t"][:, b], gpu["s_k"][:, b], ratio, w.Nv, ref.get("budget_mode", 0))
         assert np.array_equal(x, gpu["budget_x"][:, b]), f"budget_x differs for sample {b}"
         assert np.array_equal(r, gpu["budget"][:, b]), f"budget differs for sample {b}: {r} vs {gpu['budget'][:, b]}"
     for l in range(L):

@@ -186,6 +186,33 @@ def test_random_shapes(shape, path):
     compare(inp, g, reference(inp, g, alpha=alpha, ratio=ratio), ratio=ratio)
 
 
+_BUDGET_MODES = {"uniform": 1, "strength": 2, "skewness": 3}
+
+
+@pytest.mark.parametrize("mode", list(_BUDGET_MODES))
+@pytest.mark.parametrize("path", ["auto-run", "rows", "tiled"])
+def test_budget_variants(mode, path):
+    """The allocation ablation's variants (uniform, strength only, skewness
+    only) on every scoring path."""
+    print(f"[parity] budget {mode} path {path}", flush=True)
+    w = wl.custom(Nv=700, Nt=40, Hq=12, Hkv=4, D=128, dtype="bf16", L=6, B=2, ratio=0.2)
+    inp = wl.make_inputs(w, 9)
+    m = _BUDGET_MODES[mode]
+    g = run_gpu(inp, path=path.split("-")[0], run=path.endswith("-run"), budget_mode=m)
+    compare(inp, g, reference(inp, g, budget_mode=m))
+    if mode == "uniform":
+        assert (g["budget"] == int(0.2 * 700)).all()
+
+
+@pytest.mark.parametrize("mode", list(_BUDGET_MODES))
+def test_workload_3_budget_variants(mode):
+    print(f"[parity] workload 3 budget {mode}", flush=True)
+    inp = wl.make_inputs(3, 3)
+    m = _BUDGET_MODES[mode]
+    g = run_gpu(inp, max_elite=64, run=True, budget_mode=m)
+    compare(inp, g, reference(inp, g, budget_mode=m))
+
+
 @pytest.mark.parametrize("alpha,ratio", [(0.0, 0.1), (1.0, 0.1), (0.9, 0.0), (0.9, 1.0), (0.5, 0.5)])
 def test_alpha_ratio_extremes(alpha, ratio):
     w = wl.custom(Nv=200, Nt=24, Hq=6, Hkv=2, D=128, dtype="bf16", L=3, B=2)
