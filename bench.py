@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--path", default="auto", choices=["auto", "chunked", "tiled", "rows"])
     ap.add_argument("--budget-mode", default="aircache", choices=["aircache", "uniform", "strength", "skewness"],
                     help="layer budget rule: the method's (default) or one of its allocation ablation's variants")
+    ap.add_argument("--obs-window", type=int, default=0,
+                    help="0: the elite observation window (default); k > 0: the last k text tokens instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -202,7 +204,7 @@ def main():
 
     ac = AirCache(w.L, w.B, w.Hq, w.Hkv, w.D, w.Nv, w.Nt, dtype=tdtype, alpha=w.alpha, ratio=w.ratio,
                   max_elite=min(a.max_elite, w.Nt) if a.max_elite > 0 else 0, device=dev, path=a.path,
-                  budget_mode=a.budget_mode)
+                  budget_mode=a.budget_mode, obs_window=a.obs_window)
     plan = ac.alloc_plan()
     k_out, v_out = ac.alloc_compacted()
     stream = torch.cuda.current_stream(dev)
@@ -299,7 +301,8 @@ def main():
     dom_kernel = {"rows": "cross_score_rows_kernel", "chunked": "cross_score_fused_kernel"}.get(path, "cross_score_kernel")
     # counters are taken on the workload as defined (its own base distribution)
     traffic = (measured_traffic(dom_kernel, w.name)
-               if w.base == wl.CONFIGS[a.workload].base and a.budget_mode == "aircache" else None)
+               if w.base == wl.CONFIGS[a.workload].base and a.budget_mode == "aircache" and a.obs_window == 0
+               else None)
     out = {
         "metric": METRIC,
         "value": value,
@@ -313,7 +316,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == wl.BF16 else "f32",
         "data": "synthetic",
-        "config": dict(w.describe(), base=w.base, budget_mode=a.budget_mode, seed=seed, input_copies=ncopy, cache="hot" if a.hot else "rotated",
+        "config": dict(w.describe(), base=w.base, budget_mode=a.budget_mode, obs_window=a.obs_window, seed=seed, input_copies=ncopy, cache="hot" if a.hot else "rotated",
                        path=path, launches_per_step=ac.run_launches),
         "samples_per_s": w.B / (ms * 1e-3),
         "hbm": {"algorithmic_bytes_per_step": nbytes["total"], "achieved_gbps": gbps,

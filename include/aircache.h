@@ -101,6 +101,9 @@ typedef struct {
   int32_t path;       /* scoring kernels: AIRCACHE_PATH_AUTO (0), _TILED (1), _ROWS (2)
                          or _CHUNKED (3); every path computes the same results */
   int32_t budget_mode; /* layer allocation rule, AIRCACHE_BUDGET_*; 0 is the method's */
+  int32_t obs_window;  /* observation window: 0 the method's elite window; k > 0 the last
+                          min(k, n_txt) text tokens instead (the window ablation of the
+                          "Elite Observation Window" section: 16, 32, or all text tokens) */
 } aircache_desc;
 
 /* Layer budget allocation rules. AIRCACHE (0): the method's, r_hat =

@@ -32,7 +32,7 @@ class Desc(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("n_vis", C.c_int32),
                 ("n_txt", C.c_int32), ("dtype", C.c_int32), ("alpha", C.c_double),
                 ("ratio", C.c_double), ("max_elite", C.c_int32), ("path", C.c_int32),
-                ("budget_mode", C.c_int32)]
+                ("budget_mode", C.c_int32), ("obs_window", C.c_int32)]
 
 
 class PlanBuf(C.Structure):

@@ -21,14 +21,14 @@ _BUDGETS = {"aircache": 0, "uniform": 1, "strength": 2, "skewness": 3}
 
 
 def make_desc(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt, dtype,
-              alpha=0.9, ratio=0.1, max_elite=0, path="auto", budget_mode=0) -> _lib.Desc:
+              alpha=0.9, ratio=0.1, max_elite=0, path="auto", budget_mode=0, obs_window=0) -> _lib.Desc:
     if isinstance(dtype, torch.dtype):
         dtype = _DTYPES[dtype]
     elif isinstance(dtype, str):
         dtype = {"f32": _lib.AIRCACHE_F32, "bf16": _lib.AIRCACHE_BF16}[dtype]
     return _lib.Desc(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt, dtype,
                      float(alpha), float(ratio), int(max_elite), _PATHS[path] if isinstance(path, str) else int(path),
-                     _BUDGETS[budget_mode] if isinstance(budget_mode, str) else int(budget_mode))
+                     _BUDGETS[budget_mode] if isinstance(budget_mode, str) else int(budget_mode), int(obs_window))
 
 
 @dataclasses.dataclass
@@ -69,7 +69,7 @@ class AirCache:
 
     def __init__(self, n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt,
                  dtype=torch.bfloat16, alpha=0.9, ratio=0.1, max_elite=0, device="cuda", path="auto",
-                 budget_mode="aircache"):
+                 budget_mode="aircache", obs_window=0):
         self.shape = dict(L=n_layers, B=batch, Hq=n_q_heads, Hkv=n_kv_heads, D=head_dim,
                           Nv=n_vis, Nt=n_txt)
         self.dtype = dtype
@@ -77,7 +77,7 @@ class AirCache:
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
         self.desc = make_desc(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt,
-                              dtype, alpha, ratio, max_elite, path, budget_mode)
+                              dtype, alpha, ratio, max_elite, path, budget_mode, obs_window)
         ws = _lib.workspace_size(self.desc)
         if ws == 0:
             _lib.check(_lib.AIRCACHE_EINVAL)

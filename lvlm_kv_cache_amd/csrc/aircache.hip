@@ -38,6 +38,7 @@ struct Shape {
   float scale2;  // log2(e) / sqrt(D): logits are kept in the base-2 domain
   double ratio;
   int budget_mode;  // AIRCACHE_BUDGET_*
+  int window;       // 0: the elite window; k > 0: the last k text tokens (k <= N_t)
 };
 
 struct PlanPtrs {
@@ -903,10 +904,12 @@ __global__ __launch_bounds__(kEliteThreads) void elite_select_kernel(Shape sh, L
   m = red[0];
   for (int w = 1; w < kEliteWaves; ++w) m = fmaxf(m, red[w]);
   const float thr = sh.alpha * m;
+  // the elite set, or the contiguous window of the last sh.window text tokens
+  auto keep = [&](int j) { return sh.window > 0 ? j >= Nt - sh.window : pbar[j] >= thr; };
   const int per = (Nt + kEliteThreads - 1) / kEliteThreads;
   const int j0 = min(Nt, tid * per), j1 = min(Nt, j0 + per);
   int cnt = 0;
-  for (int j = j0; j < j1; ++j) cnt += (pbar[j] >= thr) ? 1 : 0;
+  for (int j = j0; j < j1; ++j) cnt += keep(j) ? 1 : 0;
   const int incl = wave_incl_scan(cnt);
   if (lane == 63) wtot[wave] = incl;
   __syncthreads();
@@ -918,7 +921,7 @@ __global__ __launch_bounds__(kEliteThreads) void elite_select_kernel(Shape sh, L
   int pos = base + incl - cnt;
   int32_t *el = plan.elite + (size_t)lb * Nt;
   for (int j = j0; j < j1; ++j)
-    if (pbar[j] >= thr) el[pos++] = j;
+    if (keep(j)) el[pos++] = j;
   if (tid == 0) plan.n_elite[lb] = total;
 }
 
@@ -1188,6 +1191,7 @@ int make_config(const aircache_desc *d, Config *cfg) {
     return fail(AIRCACHE_EINVAL, "path=%d unknown", d->path);
   if (d->budget_mode < AIRCACHE_BUDGET_AIRCACHE || d->budget_mode > AIRCACHE_BUDGET_SKEWNESS)
     return fail(AIRCACHE_EINVAL, "budget_mode=%d unknown", d->budget_mode);
+  if (d->obs_window < 0) return fail(AIRCACHE_EINVAL, "obs_window=%d < 0", d->obs_window);
   Shape &s = cfg->sh;
   s.L = d->n_layers;
   s.B = d->batch;
@@ -1212,6 +1216,7 @@ int make_config(const aircache_desc *d, Config *cfg) {
   s.scale2 = (float)(1.4426950408889634 / sqrt((double)s.D));
   s.ratio = d->ratio;
   s.budget_mode = d->budget_mode;
+  s.window = d->obs_window < d->n_txt ? d->obs_window : d->n_txt;
   const int esz = d->dtype == AIRCACHE_BF16 ? 2 : 4;
   (void)esz;
   cfg->elite_lds = (size_t)(s.G > 1 ? s.G : 1) * s.Nt * sizeof(float);

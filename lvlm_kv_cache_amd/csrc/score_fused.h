@@ -1120,7 +1120,9 @@ __device__ __forceinline__ void fused_elite_part(const Shape &sh, const FusedTab
   int cnt = 0;
 #pragma unroll
   for (int e = 0; e < EP; ++e) {
-    mk[e] = __ballot(tid + e * NT < Nt && pb[e] >= thr);
+    // the elite set, or the contiguous window of the last sh.window text tokens
+    const int j = tid + e * NT;
+    mk[e] = __ballot(j < Nt && (sh.window > 0 ? j >= Nt - sh.window : pb[e] >= thr));
     cnt += __popcll(mk[e]);
   }
   // words before this wave's, in token order: word (e, wave) comes after all

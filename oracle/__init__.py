@@ -93,6 +93,14 @@ def elite_select(w, q_l: np.ndarray, k_l: np.ndarray, b: int, alpha=None):
     return el[:n].copy(), pbar
 
 
+def window_select(Nt: int, k: int) -> np.ndarray:
+    """Step 1 with a contiguous observation window instead of the elite one
+    (the window ablation of "Elite Observation Window": the last 16 or 32 text
+    tokens, or all of them): the last min(k, N_t) text tokens, ascending."""
+    k = min(int(k), int(Nt))
+    return np.arange(Nt - k, Nt, dtype=np.int32)
+
+
 def cross_score(w, q_l, k_l, b: int, elite) -> np.ndarray:
     """Step 2: I_v[N_v] (float64) for the given elite set."""
     _check_inputs(w, q_l, k_l)

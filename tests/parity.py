@@ -47,21 +47,21 @@ def torch_dtype(w):
     return torch.float32 if w.dtype == wl.F32 else torch.bfloat16
 
 
-def make_aircache(w, alpha=None, ratio=None, max_elite=0, path="auto", budget_mode=0):
+def make_aircache(w, alpha=None, ratio=None, max_elite=0, path="auto", budget_mode=0, obs_window=0):
     return AirCache(w.L, w.B, w.Hq, w.Hkv, w.D, w.Nv, w.Nt, dtype=torch_dtype(w),
                     alpha=w.alpha if alpha is None else alpha,
                     ratio=w.ratio if ratio is None else ratio, max_elite=max_elite, path=path,
-                    budget_mode=budget_mode)
+                    budget_mode=budget_mode, obs_window=obs_window)
 
 
 def run_gpu(inp: wl.Inputs, alpha=None, ratio=None, max_elite=0, tensors=None, compress=True, path="auto", ac=None,
-            run=False, budget_mode=0):
+            run=False, budget_mode=0, obs_window=0):
     """Plan (and compress) on the GPU; ac: an AirCache to reuse (its workspace
     carries state from earlier calls); run: one aircache_run call instead of
     aircache_plan then aircache_compress."""
     w = inp.w
     if ac is None:
-        ac = make_aircache(w, alpha, ratio, max_elite, path, budget_mode)
+        ac = make_aircache(w, alpha, ratio, max_elite, path, budget_mode, obs_window)
     q, k, v = tensors if tensors is not None else to_torch(inp)
     out = {}
     if run:
@@ -89,7 +89,7 @@ def run_gpu(inp: wl.Inputs, alpha=None, ratio=None, max_elite=0, tensors=None, c
     return out
 
 
-def reference(inp: wl.Inputs, gpu: dict, alpha=None, ratio=None, budget_mode=0):
+def reference(inp: wl.Inputs, gpu: dict, alpha=None, ratio=None, budget_mode=0, obs_window=0):
     """Oracle values for every (l, b), conditional on the GPU's elite sets where
     they differ only in threshold-ambiguous tokens."""
     w = inp.w
@@ -101,8 +101,13 @@ def reference(inp: wl.Inputs, gpu: dict, alpha=None, ratio=None, budget_mode=0):
 
     def one(lb):
         l, b = lb
-        el, pbar = oracle.elite_select(w, inp.q[l], inp.k[l], b, alpha=alpha)
         gel = gpu["elite_idx"][l, b, :gpu["n_elite"][l, b]]
+        if obs_window > 0:
+            # a contiguous window: one exact answer
+            el = oracle.window_select(w.Nt, obs_window)
+            assert np.array_equal(el, gel), f"(l={l}, b={b}) window differs"
+        else:
+            el, pbar = oracle.elite_select(w, inp.q[l], inp.k[l], b, alpha=alpha)
         use = el
         if not np.array_equal(el, gel):
             diff = set(el.tolist()) ^ set(gel.tolist())

@@ -35,19 +35,20 @@ def test_exports_every_declared_function(lib):
 
 
 def test_struct_layouts():
-    # eight int32, two doubles, three int32, padded to the doubles' alignment
-    assert C.sizeof(_lib.Desc) == 8 * 4 + 2 * 8 + 3 * 4 + 4
+    # eight int32, two doubles, four int32
+    assert C.sizeof(_lib.Desc) == 8 * 4 + 2 * 8 + 4 * 4
     assert _lib.Desc.budget_mode.offset == 8 * 4 + 2 * 8 + 2 * 4
+    assert _lib.Desc.obs_window.offset == 8 * 4 + 2 * 8 + 3 * 4
     assert C.sizeof(_lib.PlanBuf) == 10 * 8
 
 
 def desc(**kw):
     base = dict(n_layers=28, batch=1, n_q_heads=28, n_kv_heads=4, head_dim=128, n_vis=2880,
-                n_txt=128, dtype="bf16", alpha=0.9, ratio=0.1, max_elite=0, path=0, budget_mode=0)
+                n_txt=128, dtype="bf16", alpha=0.9, ratio=0.1, max_elite=0, path=0, budget_mode=0, obs_window=0)
     base.update(kw)
     return make_desc(*[base[k] for k in ("n_layers", "batch", "n_q_heads", "n_kv_heads", "head_dim",
                                          "n_vis", "n_txt", "dtype", "alpha", "ratio", "max_elite", "path",
-                                         "budget_mode")])
+                                         "budget_mode", "obs_window")])
 
 
 def test_workspace_size(lib):
@@ -92,7 +93,8 @@ def test_run_launches(lib):
                                  dict(head_dim=96), dict(n_vis=2), dict(n_vis=9000), dict(n_txt=0),
                                  dict(dtype="x"), dict(alpha=1.5), dict(alpha=float("nan")),
                                  dict(ratio=-0.1), dict(max_elite=129), dict(n_txt=4000), dict(path=4),
-                                 dict(path=2, n_vis=4000), dict(budget_mode=4), dict(budget_mode=-1)])
+                                 dict(path=2, n_vis=4000), dict(budget_mode=4), dict(budget_mode=-1),
+                                 dict(obs_window=-1)])
 def test_invalid_descriptor(lib, bad):
     if bad.get("dtype") == "x":
         d = desc()

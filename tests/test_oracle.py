@@ -309,6 +309,14 @@ def test_budget_rule_is_mean_of_single_terms():
             assert np.array_equal(r, np.clip(np.floor(x), 0, nv).astype(int))
 
 
+def test_window_select():
+    # the window ablation's contiguous windows: the last k text tokens
+    assert list(oracle.window_select(128, 16)) == list(range(112, 128))
+    assert list(oracle.window_select(128, 32)) == list(range(96, 128))
+    assert list(oracle.window_select(40, 128)) == list(range(40))   # all text tokens
+    assert list(oracle.window_select(7, 1)) == [6]
+
+
 # ---------------------------------------------------------------- step 5 ----
 
 def check_topk(scores, k, kept):

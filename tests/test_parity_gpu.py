@@ -213,6 +213,26 @@ def test_workload_3_budget_variants(mode):
     compare(inp, g, reference(inp, g, budget_mode=m))
 
 
+@pytest.mark.parametrize("window", [16, 32, 40])
+@pytest.mark.parametrize("path", ["auto-run", "rows", "tiled"])
+def test_observation_windows(window, path):
+    """The window ablation's contiguous windows (the last 16 or 32 text
+    tokens, or all 40) in place of the elite window, on every scoring path."""
+    print(f"[parity] window {window} path {path}", flush=True)
+    w = wl.custom(Nv=700, Nt=40, Hq=12, Hkv=4, D=128, dtype="bf16", L=6, B=2, ratio=0.2)
+    inp = wl.make_inputs(w, 10)
+    g = run_gpu(inp, path=path.split("-")[0], run=path.endswith("-run"), obs_window=window)
+    assert (g["n_elite"] == min(window, w.Nt)).all()
+    compare(inp, g, reference(inp, g, obs_window=window))
+
+
+def test_workload_3_window_16():
+    print("[parity] workload 3 window 16", flush=True)
+    inp = wl.make_inputs(3, 3)
+    g = run_gpu(inp, max_elite=64, run=True, obs_window=16)
+    compare(inp, g, reference(inp, g, obs_window=16))
+
+
 @pytest.mark.parametrize("alpha,ratio", [(0.0, 0.1), (1.0, 0.1), (0.9, 0.0), (0.9, 1.0), (0.5, 0.5)])
 def test_alpha_ratio_extremes(alpha, ratio):
     w = wl.custom(Nv=200, Nt=24, Hq=6, Hkv=2, D=128, dtype="bf16", L=3, B=2)
