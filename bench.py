@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense, MI355X (fp32: the vector peak)
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "lvlm_kv_cache_amd", "csrc")
 SOURCES = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith((".hip", ".h"))] + \
@@ -143,6 +144,14 @@ def algorithmic_bytes(w, n_elite, budget):
                 elite_select=L * B * w.Hkv * w.Nt * D * e + L * B * w.Hq * D * e)
 
 
+def algorithmic_flops(w, n_elite):
+    """Multiply-adds x 2 the method needs in one pass: the last text query
+    against every text key, and every elite query against the visual and
+    elite text keys, for every query head."""
+    ntk = n_elite.astype("int64")
+    return int((2 * w.Hq * w.D * (w.Nt + ntk * (w.Nv + ntk))).sum())
+
+
 def cpu_baseline(inp, target_s):
     import oracle
     w = inp.w
@@ -231,6 +240,9 @@ def main():
     n_elite = plan.n_elite.cpu().numpy()
     budget = plan.budget.cpu().numpy()
     nbytes = algorithmic_bytes(w, n_elite, budget)
+    nflops = algorithmic_flops(w, n_elite)
+    dt = "bf16" if w.dtype == wl.BF16 else "f32"
+    t_roof_us = max(nbytes["total"] / (PEAK_HBM_GBPS * 1e9), nflops / (PEAK_MFMA_TFLOPS[dt] * 1e12)) * 1e6
 
     # Headline: K whole passes between two events, no instrumentation inside.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -319,6 +331,11 @@ def main():
         "config": dict(w.describe(), base=w.base, budget_mode=a.budget_mode, obs_window=a.obs_window, seed=seed, input_copies=ncopy, cache="hot" if a.hot else "rotated",
                        path=path, launches_per_step=ac.run_launches),
         "samples_per_s": w.B / (ms * 1e-3),
+        "visual_tokens_per_s": w.B * w.Nv / (ms * 1e-3),  # B * N_v per step (all layers in it)
+        # the pass's own bound: t_roof = max(bytes at the HBM peak, flops at the
+        # MFMA peak of the dtype), and t_roof / t_step
+        "t_roof_us": t_roof_us,
+        "roof_frac": t_roof_us / (ms * 1e3),
         "hbm": {"algorithmic_bytes_per_step": nbytes["total"], "achieved_gbps": gbps,
                 "peak_gbps": PEAK_HBM_GBPS, "frac_of_peak": gbps / PEAK_HBM_GBPS},
         "roofline": {"bound": "hbm", "kernel": dom_kernel, "achieved": dom_gbps, "peak": PEAK_HBM_GBPS,
