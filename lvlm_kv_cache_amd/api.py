@@ -63,8 +63,16 @@ class AirCache:
     """One compression pass configuration with its workspace.
 
     plan(q_txt, k) scores, budgets and selects; compress(...) writes the
-    compacted per-layer K/V. Both run on the current stream of the device and
+    compacted per-layer K/V; run(...) does both (one launch where the chunked
+    path serves the shape). All run on the current stream of the device and
     return without synchronising.
+
+    alpha: the elite threshold; ratio: r / N_v; max_elite: workspace cap on
+    elite tokens (0: N_t); path: "auto", "chunked", "rows" or "tiled";
+    budget_mode: "aircache" (the method's layer allocation) or one of its
+    allocation ablation's variants, "uniform", "strength", "skewness";
+    obs_window: 0 for the elite observation window, k > 0 for the last k
+    text tokens instead (the window ablation's contiguous windows).
     """
 
     def __init__(self, n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt,
