@@ -54,6 +54,9 @@ def parse():
                     help="layer budget rule: the method's (default) or one of its allocation ablation's variants")
     ap.add_argument("--obs-window", type=int, default=0,
                     help="0: the elite observation window (default); k > 0: the last k text tokens instead")
+    ap.add_argument("--skip-hot", action="store_true",
+                    help="leave out the cache-warm loop (one input copy every step), so that every launch of the "
+                         "run reads rotated inputs (profiles of the headline conditions)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -94,38 +97,96 @@ def measured_traffic(kernel, workload):
 
 
 def copy_calibration(mib):
-    """Plain copies of a known size: their FETCH_SIZE / WRITE_SIZE per dispatch
-    against mib MiB gives the scale of the counters."""
+    """Plain copies of a known size with the hand-written copy kernel of
+    libhbmprobe.so: their FETCH_SIZE / WRITE_SIZE per dispatch against mib MiB
+    gives the scale of the counters. The three buffers rotate, so no copy
+    finds its source in the last-level cache."""
+    import ctypes as C
     import torch
+    from lvlm_kv_cache_amd import build as lb
+    lib = C.CDLL(lb.PROBE_OUT)
+    lib.hbm_probe_grid.restype = C.c_int
+    lib.hbm_probe_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_void_p]
     n = mib << 20
-    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-    dst = torch.empty_like(src)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    for _ in range(5):
-        flush.fill_(0)          # evict src / dst from the last-level cache
-        dst.copy_(src)
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda").fill_(i + 1) for i in range(3)]
+    grid = lib.hbm_probe_grid(8)
+    sp = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for i in range(5):
+        a, b = bufs[i % 3], bufs[(i + 1) % 3]
+        assert lib.hbm_probe_copy(C.c_void_p(a.data_ptr()), C.c_void_p(b.data_ptr()), n, grid, sp) == 0
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes": n, "dispatches": 5}))
+    print(json.dumps({"copy_calibration_bytes": n, "dispatches": 5, "kernel": "copy_kernel"}))
 
 
-def copy_ceiling_gbps(mib=512, reps=10):
-    """Bandwidth of a plain device-to-device copy (read + write bytes per
-    second): the practical ceiling the pass is also compared with."""
+def hbm_ceilings(mib=1024, reps=10):
+    """What plain hand-written kernels reach on this device (libhbmprobe.so):
+    a read-only stream and a copy of `mib` MiB (rotated over three buffers so
+    none is in the last-level cache when it is read), in GB/s of bytes read
+    plus written, and the interval between two back-to-back launches of an
+    empty kernel on one stream, in microseconds."""
+    import ctypes as C
     import torch
+    from lvlm_kv_cache_amd import build as lb
+    lib = C.CDLL(lb.PROBE_OUT)
+    lib.hbm_probe_grid.restype = C.c_int
+    lib.hbm_probe_sink_words.restype = C.c_size_t
+    lib.hbm_probe_sink_words.argtypes = [C.c_int]
+    lib.hbm_probe_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
+    lib.hbm_probe_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_void_p]
+    lib.hbm_probe_empty.argtypes = [C.c_void_p]
     n = mib << 20
-    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) * 1e-3 / reps
-    del src, dst
-    return 2 * n / t / 1e9
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda").fill_(i + 1) for i in range(3)]
+    grid = lib.hbm_probe_grid(8)
+    sink = torch.empty(int(lib.hbm_probe_sink_words(grid)), dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    sp = C.c_void_p(st.cuda_stream)
+
+    def timed(fn, k):
+        for i in range(2):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for i in range(k):
+            fn(i)
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / k
+
+    def rd(i):
+        assert lib.hbm_probe_read(C.c_void_p(bufs[i % 3].data_ptr()), n, C.c_void_p(sink.data_ptr()), grid, sp) == 0
+
+    def cp(i):
+        a, b = bufs[i % 3], bufs[(i + 1) % 3]
+        assert lib.hbm_probe_copy(C.c_void_p(a.data_ptr()), C.c_void_p(b.data_ptr()), n, grid, sp) == 0
+
+    def em(i):
+        assert lib.hbm_probe_empty(sp) == 0
+
+    t_read = timed(rd, reps)
+    t_copy = timed(cp, reps)
+    t_empty = timed(em, 200)
+    del bufs, sink
+    return {"read_gbps": n / t_read / 1e9, "copy_gbps": 2 * n / t_copy / 1e9, "empty_launch_us": t_empty * 1e6,
+            "bytes_per_launch": n, "grid": grid}
+
+
+def host_cpu():
+    """The host CPU's model name and the logical CPUs this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count()
+    return model, n
 
 
 def algorithmic_bytes(w, n_elite, budget):
@@ -162,8 +223,9 @@ def cpu_baseline(inp, target_s):
         el = time.perf_counter() - t0
         if el >= target_s or reps >= 30:
             break
+    model, ncpu = host_cpu()
     return {"value": w.L * w.B * w.Nv * reps / el, "unit": "visual KV token-layers/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "nproc": ncpu,
             "sample": f"the full pass of workload {w.name} (all {w.L} layers, batch {w.B}) on the same "
                       f"inputs, {reps} repetition(s), {el:.1f} s, single-threaded C in double precision"}
 
@@ -194,7 +256,6 @@ def main():
     if a.base_scale is not None and a.base_scale != w.base:
         w = dataclasses.replace(w, base=a.base_scale)
     seed = a.workload if a.seed is None else a.seed
-    inp = wl.make_inputs(w, seed)
     tdtype = torch.float32 if w.dtype == wl.F32 else torch.bfloat16
 
     def dev_layers(arr):
@@ -206,10 +267,16 @@ def main():
             out.append(t.to(dev))
         return out
 
-    base = (dev_layers(inp.q), dev_layers(inp.k), dev_layers(inp.v))
-    per_copy = sum(t.numel() * t.element_size() for ts in base for t in ts)
+    # input copies, each drawn from its own seed (seed, seed + 1, ...), so
+    # consecutive steps see different elite sets, budgets and schedules
+    inp = wl.make_inputs(w, seed)
+    copies = [(dev_layers(inp.q), dev_layers(inp.k), dev_layers(inp.v))]
+    per_copy = sum(t.numel() * t.element_size() for ts in copies[0] for t in ts)
     ncopy = 1 if a.hot else max(1, math.ceil((1 << 30) / per_copy))
-    copies = [base] + [tuple([t.clone() for t in ts] for ts in base) for _ in range(ncopy - 1)]
+    for i in range(1, ncopy):
+        ci = wl.make_inputs(w, seed + i)
+        copies.append((dev_layers(ci.q), dev_layers(ci.k), dev_layers(ci.v)))
+        del ci
 
     ac = AirCache(w.L, w.B, w.Hq, w.Hkv, w.D, w.Nv, w.Nt, dtype=tdtype, alpha=w.alpha, ratio=w.ratio,
                   max_elite=min(a.max_elite, w.Nt) if a.max_elite > 0 else 0, device=dev, path=a.path,
@@ -221,26 +288,46 @@ def main():
     # one bound pass per input copy: argument checks and marshalling happen
     # here, outside the timed loops
     bound = [ac.bind(q, k, v, plan, k_out, v_out, stream=stream) for (q, k, v) in copies]
-
     fused = ac.run_launches == 1  # plan and compaction in one launch
 
-    def step(i, pev=None, cev=None):
-        bp = bound[i % ncopy]
+    # every timed call writes its device status to a word of its own, all
+    # checked after the loops (a call clears and sets only its own word)
+    n_calls = 3 * a.steps
+    status_words = torch.zeros(n_calls, dtype=torch.int32, device=dev)
+    sbound = [bound[i % ncopy].with_status(status_words[i].data_ptr()) for i in range(n_calls)]
+
+    def check_status(what, st):
+        bad = torch.nonzero(st).flatten().tolist()
+        if bad:
+            raise RuntimeError(f"device status {int(st[bad[0]])} in {len(bad)} call(s) of the {what} loop "
+                               "(raise --max-elite)")
+
+    def step(i, pev=None, cev=None, bp=None):
+        bp = bp if bp is not None else bound[i % ncopy]
         if pev is None and cev is None:
             bp.run()                   # aircache_run: the whole pass in one call
         else:
             bp.plan(events=pev)
             bp.compress(events=cev)
 
+    # warm-up, then one call per input copy to read what each copy needs
     for i in range(a.warmup):
         step(i)
-    torch.cuda.synchronize()
-    if int(plan.status.item()) != 0:
-        raise RuntimeError(f"device status {int(plan.status.item())} (raise --max-elite)")
-    n_elite = plan.n_elite.cpu().numpy()
-    budget = plan.budget.cpu().numpy()
-    nbytes = algorithmic_bytes(w, n_elite, budget)
-    nflops = algorithmic_flops(w, n_elite)
+    n_elite, budget = [], []
+    for i in range(ncopy):
+        step(i)
+        torch.cuda.synchronize()
+        if int(plan.status.item()) != 0:
+            raise RuntimeError(f"device status {int(plan.status.item())} on input copy {i} (raise --max-elite)")
+        n_elite.append(plan.n_elite.cpu().numpy())
+        budget.append(plan.budget.cpu().numpy())
+    # algorithmic bytes and flops of a step: the mean over the copies the
+    # steps rotate through (each copy is used equally often, up to one step)
+    nb = [algorithmic_bytes(w, n, r) for n, r in zip(n_elite, budget)]
+    nbytes = {k: sum(d[k] for d in nb) / ncopy for k in nb[0]}
+    nflops = sum(algorithmic_flops(w, n) for n in n_elite) / ncopy
+    n_elite_all = np.concatenate([n.ravel() for n in n_elite])
+    budget_all = np.concatenate([r.ravel() for r in budget])
     dt = "bf16" if w.dtype == wl.BF16 else "f32"
     t_roof_us = max(nbytes["total"] / (PEAK_HBM_GBPS * 1e9), nflops / (PEAK_MFMA_TFLOPS[dt] * 1e12)) * 1e6
 
@@ -249,10 +336,11 @@ def main():
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(a.steps):
-        step(i)
+        step(i, bp=sbound[i])
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / a.steps
+    check_status("headline", status_words[:a.steps])
 
     # Per-kernel durations: the same K passes with events around each kernel
     # (the one launch of the whole pass where the chunked path compacts in it).
@@ -264,7 +352,7 @@ def main():
                 e.record(stream)
         torch.cuda.synchronize()
         for i in range(a.steps):
-            bound[i % ncopy].run(events=ev[i])
+            sbound[a.steps + i].run(events=ev[i])
         torch.cuda.synchronize()
         per_step = [1e3 * e[0].elapsed_time(e[1]) for e in ev]
         kern_us = {names[0]: sum(per_step) / a.steps}
@@ -280,7 +368,7 @@ def main():
                 e.record(stream)
         torch.cuda.synchronize()
         for i in range(a.steps):
-            step(i, pev=ev[i][:np_], cev=ev[i][np_:])
+            step(i, pev=ev[i][:np_], cev=ev[i][np_:], bp=sbound[a.steps + i])
         torch.cuda.synchronize()
         kern = {n: 0.0 for n in names}
         for i in range(a.steps):
@@ -290,16 +378,21 @@ def main():
             kern["kv_gather"] += c[0].elapsed_time(c[1])
         kern_us = {n: 1e3 * t / a.steps for n, t in kern.items()}
         launch_pct = None
+    check_status("per-launch", status_words[a.steps:2 * a.steps])
 
     # Hot: the same steps on one input copy only (K partly cache-resident).
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(a.steps):
-        bound[0].run() if fused else step(0)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_hot = e0.elapsed_time(e1) / a.steps
-    copy_gbps = copy_ceiling_gbps()
+    ms_hot = None
+    if not a.skip_hot:
+        hot = [bound[0].with_status(status_words[2 * a.steps + i].data_ptr()) for i in range(a.steps)]
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(a.steps):
+            step(0, bp=hot[i])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_hot = e0.elapsed_time(e1) / a.steps
+        check_status("hot", status_words[2 * a.steps:])
+    ceil = hbm_ceilings()
 
     tokens = w.L * w.B * w.Nv
     value = tokens / (ms * 1e-3)
@@ -344,12 +437,14 @@ def main():
         "kernel_us": kern_us,
         "launch_us_p10_p50_p90": None if launch_pct is None else [launch_pct[10], launch_pct[50], launch_pct[90]],
         "hot_ms_per_step": ms_hot,
-        "copy_ceiling_gbps": copy_gbps,
-        "pass_frac_of_copy_ceiling": gbps / copy_gbps,
-        "elite_mean": float(n_elite.mean()),
-        "elite_hist": {int(k): int(v) for k, v in zip(*np.unique(n_elite, return_counts=True))},
-        "budget_sum": int(budget.sum()),
-        "budget_min_mean_max": [int(budget.min()), float(budget.mean()), int(budget.max())],
+        # what plain hand-written kernels reach on the same device
+        "ceilings": ceil,
+        "pass_frac_of_copy_ceiling": gbps / ceil["copy_gbps"],
+        "pass_frac_of_read_ceiling": gbps / ceil["read_gbps"],
+        "elite_mean": float(n_elite_all.mean()),
+        "elite_hist": {int(k): int(v) for k, v in zip(*np.unique(n_elite_all, return_counts=True))},
+        "budget_sum_per_step": float(budget_all.sum() / ncopy),
+        "budget_min_mean_max": [int(budget_all.min()), float(budget_all.mean()), int(budget_all.max())],
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, a.cpu_seconds)

@@ -177,7 +177,16 @@ int32_t aircache_resolved_path(const aircache_desc *desc);
  * only; no device work. */
 int32_t aircache_run_launches(const aircache_desc *desc);
 
-/* Scores, statistics, budgets and top-k selection for all layers.
+/* Scores, statistics, budgets and top-k selection for all layers: the first
+ * four steps of the pass on the AirCache paper-notes page.
+ *   - elite set and I_v: "Elite Observation Window" (the Att, k, A_vtk and
+ *     I_v equations);
+ *   - s_t, s_k and the budget r_hat: "Layer-wise KV Cache Budget Allocation"
+ *     (the s_t, s_k and r_hat equations, normalised across layers);
+ *   - the top-r_hat selection per layer and the rule that budgets are set
+ *     once, after prefill, for all layers together: the training-free
+ *     procedure (the section on losses and training strategy).
+ * Arguments:
  *   q_txt, k : host arrays of n_layers device pointers (layout above)
  *   plan     : output buffers (see aircache_plan_buf)
  *   workspace: device scratch of ws_bytes >= aircache_workspace_size(desc)
@@ -188,9 +197,12 @@ int32_t aircache_run_launches(const aircache_desc *desc);
 int aircache_plan(const aircache_desc *desc, const void *const *q_txt, const void *const *k,
                   const aircache_plan_buf *plan, void *workspace, size_t ws_bytes, void *stream);
 
-/* Compaction (the page's compress step): for every (layer, sample, KV head)
- * copy the kept visual rows (plan->kept_idx, ascending) and then all text rows
- * of K and V into k_out[l] / v_out[l] at plan->out_off[l][b]. Bit-exact copies.
+/* Compaction: the compress step of the training-free procedure on the
+ * AirCache paper-notes page (the section on losses and training strategy:
+ * after the budgets are set, each layer keeps its selected visual KV and all
+ * text KV for decoding). For every (layer, sample, KV head) copy the kept
+ * visual rows (plan->kept_idx, ascending) and then all text rows of K and V
+ * into k_out[l] / v_out[l] at plan->out_off[l][b]. Bit-exact copies.
  *   k, v        : host arrays of n_layers device pointers (inputs, read-only)
  *   k_out, v_out: host arrays of n_layers device pointers to buffers of at
  *                 least out_off[l][B] elements (aircache_max_compacted_elems is

@@ -224,6 +224,18 @@ class BoundPass:
         self._ws_bytes = ac.ws_bytes
         self._st = _lib.C.c_void_p(ac._stream(stream))
 
+    def with_status(self, ptr: int) -> "BoundPass":
+        """A copy of this bound pass whose calls write their device status word
+        to ptr (an int32 in device memory) instead of the plan's: a caller
+        that makes many calls can then read every call's status afterwards."""
+        import copy
+        other = copy.copy(self)
+        buf = _lib.PlanBuf.from_buffer_copy(self._buf)
+        buf.status = ptr
+        other._buf = buf
+        other._pbuf = _lib.C.byref(buf)
+        return other
+
     def plan(self, events=None) -> PlanOutputs:
         if events is None:
             rc = self._lib.aircache_plan(self._desc, self._q, self._k, self._pbuf, self._ws, self._ws_bytes,

@@ -18,7 +18,6 @@
 
 #include <mutex>
 #include <string>
-#include <vector>
 
 #include "aircache.h"
 #include "device_common.h"
@@ -1374,13 +1373,18 @@ struct KernelFacts {
   int occ;
 };
 std::mutex g_facts_mu;
-std::vector<KernelFacts> g_facts;
+constexpr int kMaxFacts = 512;  // (device, kernel) pairs: far more than the kernels times the devices
+KernelFacts g_facts[kMaxFacts];
+int g_nfacts = 0;
 
-KernelFacts *kernel_facts(int dev, const void *kern) {  // g_facts_mu held
-  for (auto &f : g_facts)
-    if (f.dev == dev && f.kern == kern) return &f;
-  g_facts.push_back(KernelFacts{dev, kern, 0, 0, 0});
-  return &g_facts.back();
+// The facts entry of (dev, kern), created on first use; NULL if the table is
+// full (the caller then queries the runtime every time). g_facts_mu held.
+KernelFacts *kernel_facts(int dev, const void *kern) {
+  for (int i = 0; i < g_nfacts; ++i)
+    if (g_facts[i].dev == dev && g_facts[i].kern == kern) return &g_facts[i];
+  if (g_nfacts == kMaxFacts) return nullptr;
+  g_facts[g_nfacts] = KernelFacts{dev, kern, 0, 0, 0};
+  return &g_facts[g_nfacts++];
 }
 
 template <typename K> int allow_lds(K kernel, size_t bytes) {
@@ -1390,11 +1394,11 @@ template <typename K> int allow_lds(K kernel, size_t bytes) {
   const void *kp = reinterpret_cast<const void *>(kernel);
   std::lock_guard<std::mutex> lock(g_facts_mu);
   KernelFacts *f = kernel_facts(dev, kp);
-  if (f->lds_allowed >= bytes) return AIRCACHE_OK;
+  if (f && f->lds_allowed >= bytes) return AIRCACHE_OK;
   if ((rc = check_hip(hipFuncSetAttribute(kp, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes),
                       "hipFuncSetAttribute")))
     return rc;
-  f->lds_allowed = bytes;
+  if (f) f->lds_allowed = bytes;
   return AIRCACHE_OK;
 }
 
@@ -1405,7 +1409,7 @@ template <typename K> int occupancy(K kernel, int threads, size_t lds, int *occ)
   const void *kp = reinterpret_cast<const void *>(kernel);
   std::lock_guard<std::mutex> lock(g_facts_mu);
   KernelFacts *f = kernel_facts(dev, kp);
-  if (f->occ > 0 && f->occ_lds == lds) {
+  if (f && f->occ > 0 && f->occ_lds == lds) {
     *occ = f->occ;
     return AIRCACHE_OK;
   }
@@ -1413,8 +1417,10 @@ template <typename K> int occupancy(K kernel, int threads, size_t lds, int *occ)
   if ((rc = check_hip(hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kp, threads, lds),
                       "hipOccupancyMaxActiveBlocksPerMultiprocessor")))
     return rc;
-  f->occ = v;
-  f->occ_lds = lds;
+  if (f) {
+    f->occ = v;
+    f->occ_lds = lds;
+  }
   *occ = v;
   return AIRCACHE_OK;
 }
@@ -1676,6 +1682,56 @@ int launch_gather(const Config &cfg, const GatherTables &tb, const PlanPtrs &pp,
   return check_hip(hipGetLastError(), "kv_gather_kernel launch");
 }
 
+// The whole pass (aircache_run): one chunked launch that also compacts where
+// the descriptor allows it, else the plan launches then the gather.
+int run_pass(const Config &cfg, const aircache_desc *desc, const void *const *q_txt, const void *const *k,
+             const void *const *v, const aircache_plan_buf *plan, void *const *k_out, void *const *v_out,
+             void *workspace, size_t ws_bytes, hipStream_t st, hipEvent_t *ev) {
+  int rc;
+  if ((rc = check_plan_buf(plan, false))) return rc;
+  if (!workspace || ws_bytes < cfg.ws_bytes)
+    return fail(AIRCACHE_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0,
+                cfg.ws_bytes);
+  if (!aligned16(workspace)) return fail(AIRCACHE_EINVAL, "workspace is not 16-byte aligned");
+  LayerTable qt, kt;
+  if ((rc = fill_table(q_txt, cfg.sh.L, &qt, "q_txt"))) return rc;
+  if ((rc = fill_table(k, cfg.sh.L, &kt, "k"))) return rc;
+  GatherTables tb;
+  if ((rc = gather_tables(cfg, k, v, k_out, v_out, &tb))) return rc;
+  const PlanPtrs pp = plan_ptrs(plan);
+  const bool bf = desc->dtype == AIRCACHE_BF16;
+  if ((rc = mark(ev, 0, st))) return rc;
+  if (cfg.run_fused) {
+    LayerTable vt, kot, vot;
+    for (int l = 0; l < cfg.sh.L; ++l) {
+      vt.p[l] = tb.v.p[l];
+      kot.p[l] = tb.ko.p[l];
+      vot.p[l] = tb.vo.p[l];
+    }
+    const RunOut out{&vt, &kot, &vot};
+    const Ws ws = ws_of(cfg, workspace);
+    int fgrid = 0;
+    if (bf && cfg.sh.D == 128) {
+      if (!(rc = fused_grid<Bf16Tag, 128>(cfg, &fgrid)))
+        rc = launch_chunked<Bf16Tag, 128>(cfg, qt, kt, pp, ws, workspace, fgrid, st, &out);
+    } else if (bf) {
+      if (!(rc = fused_grid<Bf16Tag, 64>(cfg, &fgrid)))
+        rc = launch_chunked<Bf16Tag, 64>(cfg, qt, kt, pp, ws, workspace, fgrid, st, &out);
+    } else if (cfg.sh.D == 128) {
+      if (!(rc = fused_grid<F32Tag, 128>(cfg, &fgrid)))
+        rc = launch_chunked<F32Tag, 128>(cfg, qt, kt, pp, ws, workspace, fgrid, st, &out);
+    } else {
+      if (!(rc = fused_grid<F32Tag, 64>(cfg, &fgrid)))
+        rc = launch_chunked<F32Tag, 64>(cfg, qt, kt, pp, ws, workspace, fgrid, st, &out);
+    }
+    if (rc) return rc;
+  } else {
+    if ((rc = aircache_plan(desc, q_txt, k, plan, workspace, ws_bytes, st))) return rc;
+    if ((rc = launch_gather(cfg, tb, pp, st))) return rc;
+  }
+  return mark(ev, 1, st);
+}
+
 }  // namespace aircache
 
 using namespace aircache;
@@ -1771,49 +1827,8 @@ int aircache_run_profiled(const aircache_desc *desc, const void *const *q_txt, c
   Config cfg;
   int rc;
   if ((rc = make_config(desc, &cfg))) return rc;
-  if ((rc = check_plan_buf(plan, false))) return rc;
-  if (!workspace || ws_bytes < cfg.ws_bytes)
-    return fail(AIRCACHE_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0,
-                cfg.ws_bytes);
-  if (!aligned16(workspace)) return fail(AIRCACHE_EINVAL, "workspace is not 16-byte aligned");
-  LayerTable qt, kt;
-  if ((rc = fill_table(q_txt, cfg.sh.L, &qt, "q_txt"))) return rc;
-  if ((rc = fill_table(k, cfg.sh.L, &kt, "k"))) return rc;
-  GatherTables tb;
-  if ((rc = gather_tables(cfg, k, v, k_out, v_out, &tb))) return rc;
-  const PlanPtrs pp = plan_ptrs(plan);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool bf = desc->dtype == AIRCACHE_BF16;
-  if ((rc = mark(ev, 0, st))) return rc;
-  if (cfg.run_fused) {
-    LayerTable vt, kot, vot;
-    for (int l = 0; l < cfg.sh.L; ++l) {
-      vt.p[l] = tb.v.p[l];
-      kot.p[l] = tb.ko.p[l];
-      vot.p[l] = tb.vo.p[l];
-    }
-    const RunOut out{&vt, &kot, &vot};
-    const Ws ws = ws_of(cfg, workspace);
-    int fgrid = 0;
-    if (bf && cfg.sh.D == 128) {
-      if (!(rc = fused_grid<Bf16Tag, 128>(cfg, &fgrid)))
-        rc = launch_chunked<Bf16Tag, 128>(cfg, qt, kt, pp, ws, workspace, fgrid, st, &out);
-    } else if (bf) {
-      if (!(rc = fused_grid<Bf16Tag, 64>(cfg, &fgrid)))
-        rc = launch_chunked<Bf16Tag, 64>(cfg, qt, kt, pp, ws, workspace, fgrid, st, &out);
-    } else if (cfg.sh.D == 128) {
-      if (!(rc = fused_grid<F32Tag, 128>(cfg, &fgrid)))
-        rc = launch_chunked<F32Tag, 128>(cfg, qt, kt, pp, ws, workspace, fgrid, st, &out);
-    } else {
-      if (!(rc = fused_grid<F32Tag, 64>(cfg, &fgrid)))
-        rc = launch_chunked<F32Tag, 64>(cfg, qt, kt, pp, ws, workspace, fgrid, st, &out);
-    }
-    if (rc) return rc;
-  } else {
-    if ((rc = aircache_plan(desc, q_txt, k, plan, workspace, ws_bytes, stream))) return rc;
-    if ((rc = launch_gather(cfg, tb, pp, st))) return rc;
-  }
-  return mark(ev, 1, st);
+  return run_pass(cfg, desc, q_txt, k, v, plan, k_out, v_out, workspace, ws_bytes, static_cast<hipStream_t>(stream),
+                  ev);
 }
 
 int aircache_run(const aircache_desc *desc, const void *const *q_txt, const void *const *k, const void *const *v,

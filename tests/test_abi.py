@@ -140,3 +140,4 @@ def test_compress_argument_errors(lib):
 def test_strerror(lib):
     assert lib.aircache_strerror(0) == b"ok"
     assert lib.aircache_strerror(2) == b"workspace too small"
+

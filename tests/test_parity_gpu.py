@@ -1,7 +1,8 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle on the GPU.
 
-Full-size workloads 1-5 (every seed for 1-3, the headline seed for 4-5) in the
-launch configuration the benchmark times, each scoring path on the workloads
+Full-size workloads 1-5 (every parity seed) in the launch configuration the
+benchmark times, and 4-5 also with no elite cap (max_elite = 0, the library's
+default), each scoring path on the workloads
 it serves, plus small edge shapes: ragged tails, one and eight KV heads, MHA,
 head_dim 64, float32 and bfloat16, a single text token, alpha and ratio at
 their extremes, zero queries (every text token elite, several row passes),
@@ -27,8 +28,7 @@ def gpu():
     torch.cuda.set_device(0)
 
 
-CASES = [(1, s) for s in wl.parity_seeds(1)] + [(2, s) for s in wl.parity_seeds(2)] + \
-        [(3, s) for s in wl.parity_seeds(3)] + [(4, 4), (5, 5)]
+CASES = [(c, s) for c in (1, 2, 3, 4, 5) for s in wl.parity_seeds(c)]
 
 
 @pytest.mark.parametrize("cid,seed", CASES)
@@ -48,6 +48,16 @@ def test_workload_run(cid):
     print(f"[parity] workload {cid} run", flush=True)
     inp = wl.make_inputs(cid, cid)
     g = run_gpu(inp, max_elite=0 if cid <= 2 else 64, run=True)
+    compare(inp, g, reference(inp, g))
+
+
+@pytest.mark.parametrize("cid", [4, 5])
+def test_workload_run_no_elite_cap(cid):
+    """aircache_run on workloads 4 and 5 at full size with max_elite = 0 (the
+    elite cap is N_t, the library's default), whatever path that resolves to."""
+    print(f"[parity] workload {cid} run, no elite cap", flush=True)
+    inp = wl.make_inputs(cid, cid)
+    g = run_gpu(inp, max_elite=0, run=True)
     compare(inp, g, reference(inp, g))
 
 
@@ -109,6 +119,19 @@ def test_all_text_elite_many_rows(path):
     inp = wl.make_inputs(w, 6, zero_q=True)
     g = run_gpu(inp, path=path.split("-")[0], run=path.endswith("-run"))
     assert (g["n_elite"] == 40).all()
+    compare(inp, g, reference(inp, g))
+
+
+@pytest.mark.parametrize("path", ["rows", "tiled"])
+def test_more_than_128_elite_tokens(path):
+    """Zero queries with N_t = 200 make all 200 text tokens elite: the rows
+    path then has more elite text tiles than waves (16 x 8 = 128 tokens), and
+    seven MHA KV heads keep the shape off the chunked path."""
+    w = wl.custom(Nv=300, Nt=200, Hq=7, Hkv=7, D=128, dtype="bf16", L=2, B=1, ratio=0.2)
+    print(f"[parity] 200 elite tokens, path {path}", flush=True)
+    inp = wl.make_inputs(w, 12, zero_q=True)
+    g = run_gpu(inp, path=path)
+    assert (g["n_elite"] == 200).all()
     compare(inp, g, reference(inp, g))
 
 
@@ -278,5 +301,26 @@ def test_deterministic_rerun():
     for key in a:
         if isinstance(a[key], list):
             assert all(np.array_equal(x, y) for x, y in zip(a[key], b[key])), key
+        else:
+            assert np.array_equal(a[key], b[key]), key
+
+
+def test_deterministic_rerun_one_launch():
+    """aircache_run (the one launch the benchmark times) twice on workload 3
+    with one workspace: bit-identical plans and compacted caches."""
+    from parity import make_aircache, to_torch
+    inp = wl.make_inputs(3, 3)
+    t = to_torch(inp)
+    ac = make_aircache(inp.w, max_elite=64)
+    a = run_gpu(inp, tensors=t, ac=ac, run=True)
+    b = run_gpu(inp, tensors=t, ac=ac, run=True)
+    for key in a:
+        if isinstance(a[key], list):
+            assert all(np.array_equal(x, y) for x, y in zip(a[key], b[key])), key
+        elif key in ("elite_idx", "kept_idx"):
+            n = a["n_elite"] if key == "elite_idx" else a["budget"]
+            for l in range(inp.w.L):
+                for bb in range(inp.w.B):
+                    assert np.array_equal(a[key][l, bb, :n[l, bb]], b[key][l, bb, :n[l, bb]]), key
         else:
             assert np.array_equal(a[key], b[key]), key
