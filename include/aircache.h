@@ -228,6 +228,27 @@ int aircache_run(const aircache_desc *desc, const void *const *q_txt, const void
                  const aircache_plan_buf *plan, void *const *k_out, void *const *v_out, void *workspace,
                  size_t ws_bytes, void *stream);
 
+/* aircache_run for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same pass, results and checks as aircache_run, with the library's own
+ * scratch in place of the caller's workspace. The scratch is a static device
+ * array of AIRCACHE_NOALLOC_SCRATCH_BYTES per GPU, held from the library's
+ * first use on that GPU until the process ends; this call allocates nothing
+ * (no hipMalloc, no allocating library routine). A descriptor whose
+ * aircache_workspace_size exceeds that size is rejected with
+ * AIRCACHE_EINVAL before anything is enqueued. On a GPU's first call, and on
+ * every call whose descriptor differs from the previous call's on that GPU,
+ * the part of the scratch the descriptor uses is zeroed first by a kernel on
+ * the same stream; otherwise the scratch keeps what the last call left, as a
+ * workspace does across aircache_run calls. Every call on one GPU shares that
+ * GPU's scratch: calls that can overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller. The remaining arguments
+ * are those of aircache_run. */
+#define AIRCACHE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int aircache_run_noalloc(const aircache_desc *desc, const void *const *q_txt, const void *const *k,
+                         const void *const *v, const aircache_plan_buf *plan, void *const *k_out,
+                         void *const *v_out, void *stream);
+
 /* Instrumented variants of aircache_plan / aircache_compress / aircache_run for
  * timing individual kernels. events is a host array of hipEvent_t handles created by
  * the caller: events[i] is recorded on the stream just before the i-th kernel

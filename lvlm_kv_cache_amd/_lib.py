@@ -21,7 +21,9 @@ MAX_LAYERS = 128
 EXPORTS = ["aircache_abi_version", "aircache_workspace_size", "aircache_max_compacted_elems",
            "aircache_resolved_path", "aircache_run_launches",
            "aircache_plan", "aircache_compress", "aircache_run", "aircache_plan_profiled",
-           "aircache_compress_profiled", "aircache_run_profiled", "aircache_strerror", "aircache_last_error"]
+           "aircache_compress_profiled", "aircache_run_profiled", "aircache_run_noalloc", "aircache_strerror",
+           "aircache_last_error"]
+NOALLOC_SCRATCH_BYTES = 64 << 20  # AIRCACHE_NOALLOC_SCRATCH_BYTES
 PLAN_KERNELS = ["elite_select", "cross_score", "finalize", "topk_select"]
 COMPRESS_KERNELS = ["kv_gather"]
 RUN_KERNELS = ["aircache_pass"]
@@ -81,6 +83,8 @@ def load() -> C.CDLL:
         lib.aircache_run_profiled.restype = C.c_int
         lib.aircache_run_profiled.argtypes = [C.POINTER(Desc), P, P, P, C.POINTER(PlanBuf), P, P, P, C.c_size_t, P,
                                               P, C.c_int]
+        lib.aircache_run_noalloc.restype = C.c_int
+        lib.aircache_run_noalloc.argtypes = [C.POINTER(Desc), P, P, P, C.POINTER(PlanBuf), P, P, P]
         lib.aircache_strerror.restype = C.c_char_p
         lib.aircache_strerror.argtypes = [C.c_int]
         lib.aircache_last_error.restype = C.c_char_p
@@ -135,6 +139,12 @@ def run(desc: Desc, q_ptrs, k_ptrs, v_ptrs, buf: PlanBuf, ko_ptrs, vo_ptrs, ws_p
                                    C.c_void_p(stream))
     return load().aircache_run_profiled(C.byref(desc), q, k, v, C.byref(buf), ko, vo, C.c_void_p(ws_ptr), ws_bytes,
                                         C.c_void_p(stream), ptr_array(events), len(events))
+
+
+def run_noalloc(desc: Desc, q_ptrs, k_ptrs, v_ptrs, buf: PlanBuf, ko_ptrs, vo_ptrs, stream: int) -> int:
+    """aircache_run_noalloc: the whole pass on the library's static scratch."""
+    q, k, v, ko, vo = [ptr_array(p) if p is not None else None for p in (q_ptrs, k_ptrs, v_ptrs, ko_ptrs, vo_ptrs)]
+    return load().aircache_run_noalloc(C.byref(desc), q, k, v, C.byref(buf), ko, vo, C.c_void_p(stream))
 
 
 def compress(desc: Desc, buf: PlanBuf, k_ptrs, v_ptrs, ko_ptrs, vo_ptrs, stream: int, events=None) -> int:

@@ -1732,6 +1732,57 @@ int run_pass(const Config &cfg, const aircache_desc *desc, const void *const *q_
   return mark(ev, 1, st);
 }
 
+// ----------------------------------------------------------------------------
+// Library-owned scratch for aircache_run_noalloc: one array per device (each
+// GPU the library runs on holds its own copy until the process ends), used in
+// place of a caller workspace. In host code `scratch` names a host-side
+// stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+// ----------------------------------------------------------------------------
+constexpr size_t kScratchBytes = AIRCACHE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  void *ptr;             // device address of this device's scratch, NULL until looked up
+  bool have_desc;        // desc holds the descriptor the scratch is laid out for
+  aircache_desc desc;
+};
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[kMaxDevices];
+
+bool same_desc(const aircache_desc &a, const aircache_desc &b) {
+  return a.n_layers == b.n_layers && a.batch == b.batch && a.n_q_heads == b.n_q_heads &&
+         a.n_kv_heads == b.n_kv_heads && a.head_dim == b.head_dim && a.n_vis == b.n_vis &&
+         a.n_txt == b.n_txt && a.dtype == b.dtype && a.alpha == b.alpha && a.ratio == b.ratio &&
+         a.max_elite == b.max_elite && a.path == b.path && a.budget_mode == b.budget_mode &&
+         a.obs_window == b.obs_window;
+}
+
+// Zero n16 16-byte words (a kernel, not hipMemsetAsync, so a captured graph
+// replays it like any other kernel).
+__global__ __launch_bounds__(256) void zero_fill_kernel(u32x4_t *p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = u32x4_t{0u, 0u, 0u, 0u};
+}
+
+// The current device's scratch slot, with its address looked up on the
+// device's first use. g_scratch_mu held.
+int scratch_slot(ScratchSlot **slot) {
+  int dev = 0, rc;
+  if ((rc = check_hip(hipGetDevice(&dev), "hipGetDevice"))) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return fail(AIRCACHE_EINVAL, "device %d beyond the %d the scratch serves", dev, kMaxDevices);
+  ScratchSlot &s = g_scratch[dev];
+  if (!s.ptr) {
+    void *p = nullptr;
+    if ((rc = check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"))) return rc;
+    if (!p) return fail(AIRCACHE_EHIP, "hipGetSymbolAddress(scratch) gave NULL");
+    s.ptr = p;
+  }
+  *slot = &s;
+  return AIRCACHE_OK;
+}
+
 }  // namespace aircache
 
 using namespace aircache;
@@ -1829,6 +1880,48 @@ int aircache_run_profiled(const aircache_desc *desc, const void *const *q_txt, c
   if ((rc = make_config(desc, &cfg))) return rc;
   return run_pass(cfg, desc, q_txt, k, v, plan, k_out, v_out, workspace, ws_bytes, static_cast<hipStream_t>(stream),
                   ev);
+}
+
+int aircache_run_noalloc(const aircache_desc *desc, const void *const *q_txt, const void *const *k,
+                         const void *const *v, const aircache_plan_buf *plan, void *const *k_out,
+                         void *const *v_out, void *stream) {
+  Config cfg;
+  int rc;
+  if ((rc = make_config(desc, &cfg))) return rc;
+  if (cfg.ws_bytes > kScratchBytes)
+    return fail(AIRCACHE_EINVAL, "this descriptor needs %zu bytes of scratch; aircache_run_noalloc holds %zu "
+                "(use aircache_run with a workspace)", cfg.ws_bytes, kScratchBytes);
+  // validate everything before the scratch is touched, so a rejected call
+  // leaves it as the last accepted call left it
+  if ((rc = check_plan_buf(plan, false))) return rc;
+  {
+    LayerTable t;
+    GatherTables tb;
+    if ((rc = fill_table(q_txt, cfg.sh.L, &t, "q_txt"))) return rc;
+    if ((rc = gather_tables(cfg, k, v, k_out, v_out, &tb))) return rc;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchSlot *slot = nullptr;
+  if ((rc = scratch_slot(&slot))) return rc;
+  // the records of the pass are valid across calls with one descriptor only:
+  // on a device's first call, or after a call with another descriptor, the
+  // part of the scratch this descriptor uses is zeroed first
+  if (!slot->have_desc || !same_desc(slot->desc, *desc)) {
+    slot->have_desc = false;
+    const size_t n16 = cfg.ws_bytes / 16;  // ws_bytes is a multiple of 256
+    if (n16 > 0) {
+      const size_t want = (n16 + 255) / 256;
+      const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
+      hipLaunchKernelGGL(zero_fill_kernel, dim3(grid), dim3(256), 0, st, static_cast<u32x4_t *>(slot->ptr), n16);
+      if ((rc = check_hip(hipGetLastError(), "zero_fill_kernel launch"))) return rc;
+    }
+    slot->desc = *desc;
+    slot->have_desc = true;
+  }
+  rc = run_pass(cfg, desc, q_txt, k, v, plan, k_out, v_out, slot->ptr, kScratchBytes, st, nullptr);
+  if (rc == AIRCACHE_EHIP) slot->have_desc = false;  // a launch failed: zero again on the next call
+  return rc;
 }
 
 int aircache_run(const aircache_desc *desc, const void *const *q_txt, const void *const *k, const void *const *v,

@@ -141,3 +141,25 @@ def test_strerror(lib):
     assert lib.aircache_strerror(0) == b"ok"
     assert lib.aircache_strerror(2) == b"workspace too small"
 
+
+def test_noalloc_argument_errors(lib):
+    """aircache_run_noalloc rejects, on the host and before anything touches
+    the scratch, a descriptor whose workspace exceeds the static scratch and
+    the argument errors aircache_run rejects."""
+    big = desc(path=1, n_layers=28, batch=8, n_vis=3072, n_txt=1024)  # tiled: gigabytes of workspace
+    assert _lib.workspace_size(big) > _lib.NOALLOC_SCRATCH_BYTES
+    ptrs = [4096] * 28
+    rc = _lib.run_noalloc(big, ptrs, ptrs, ptrs, fake_buf(), ptrs, ptrs, 0)
+    assert rc == _lib.AIRCACHE_EINVAL
+    assert "scratch" in lib.aircache_last_error().decode()
+    d = desc(n_layers=2, n_vis=64, n_txt=16)
+    assert _lib.workspace_size(d) <= _lib.NOALLOC_SCRATCH_BYTES
+    ok = [1 << 20, 2 << 20]
+    assert _lib.run_noalloc(d, ok, ok, ok, _lib.PlanBuf(), [3 << 20, 4 << 20], [5 << 20, 6 << 20], 0) == \
+        _lib.AIRCACHE_EINVAL                                                              # NULL plan outputs
+    assert _lib.run_noalloc(d, None, ok, ok, fake_buf(), [3 << 20, 4 << 20], [5 << 20, 6 << 20], 0) == \
+        _lib.AIRCACHE_EINVAL                                                              # no queries
+    assert _lib.run_noalloc(d, ok, ok, ok, fake_buf(), [(1 << 20) + 64, 4 << 20], [5 << 20, 6 << 20], 0) == \
+        _lib.AIRCACHE_EINVAL                                                              # output overlaps input
+    d.n_layers = 0
+    assert _lib.run_noalloc(d, ok, ok, ok, fake_buf(), ok, ok, 0) == _lib.AIRCACHE_EINVAL
