@@ -750,7 +750,7 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
   }
 }
 
-#include "score_fused.h"
+#include "pass_chunked.h"
 
 // ----------------------------------------------------------------------------
 // Step 1: elite observation window ("Elite Observation Window", the Att and k
@@ -1145,8 +1145,6 @@ constexpr size_t kMaxLds = 160 * 1024;
 struct Config {
   Shape sh;
   size_t off_cnt, off_stats, off_e, off_part, ws_bytes;
-  size_t off_xrec, off_mom, off_srec, off_part_rg, off_cnt_chunk, off_ivrec, off_keptrec, off_grec,
-      off_parts64, off_erec, off_hint;
   size_t tile_bytes;   // bytes of one 16-key tile
   bool run_fused;      // aircache_run compacts inside the chunked launch
   size_t off_cnt_elite, off_pbar, off_sched;
@@ -1154,11 +1152,13 @@ struct Config {
   int ktw;
   int rows_kt;  // key tiles per wave of cross_score_rows_kernel; 0: the tiled path with spilled exponentials
   int rt_grid, units;
-  bool chunked;        // cross_score_fused_kernel (steps 2-5 in one launch)
-  int fused_kcap_lo;   // smallest key-tile cap per wave a chunked launch can choose
-  int rec_stride, max_chunks, max_rg, wmax;
-  FusedLds flds;
+  bool chunked;        // aircache_pass_kernel: the whole pass in one launch
   int path;            // AIRCACHE_PATH_TILED, _ROWS or _CHUNKED
+  // chunked path: schedule facts fixed by the shape, workspace offsets, LDS
+  int hgs, nhg, wph, width, nch, rows;
+  size_t off_pass_head, off_parts, off_erec, off_xrec, off_mom, off_ivrec, off_brec;
+  int erec_stride;
+  PassLds plds;
 };
 
 // Workspace head: the epoch word, then the counters.
@@ -1250,80 +1250,59 @@ int make_config(const aircache_desc *d, Config *cfg) {
   if (cfg->rows_kt && cfg->rows_lds > kMaxLds) cfg->rows_kt = 0;
   if (d->path == AIRCACHE_PATH_ROWS && !cfg->rows_kt)
     return fail(AIRCACHE_EINVAL, "the rows path needs n_vis <= %d", kRowsWaves * 16 * kRowsKtMax);
-  // Chunked path: power-of-two KV head count up to the wave count, its LDS
-  // layout within the limit, and a bounded item count per workgroup on a
-  // 256-CU device.
+  // Chunked path: a head group is the largest power of two up to eight that
+  // divides H_kv; the chunk width fills the LDS ring (wph * 16 * KT keys); a
+  // (layer, sample) has at most 64 chunks, its passes stay within the record
+  // tags, the elite window within the elite parts' limits, and the LDS layout
+  // within a CU.
   cfg->chunked = false;
   {
-    const bool heads_ok = (s.Hkv == 1 || s.Hkv == 2 || s.Hkv == 4 || s.Hkv == 8);
-    const int wph = heads_ok ? kFusedWaves / s.Hkv : 1;
-    const int lb = s.L * s.B;
-    cfg->fused_kcap_lo = fused_kcap_min(s.L, s.B, s.Nv, wph);
-    long long rec = 0;
-    int maxc = 1, maxrg = 1, wmax = 16;
-    for (int ntk = 0; ntk <= s.cap; ++ntk) {
-      // the narrowest chunks a launch can choose give the most records
-      const ChunkPlan cp = fused_chunk_plan(ntk, s.G, s.Nv, wph, cfg->fused_kcap_lo);
-      const long long r = (long long)cp.nchunks * s.Hkv * cp.rtg * 16;
-      if (r > rec) rec = r;
-      if (cp.nchunks > maxc) maxc = cp.nchunks;
-      if (cp.nrg > maxrg) maxrg = cp.nrg;
-      // the widest chunk of any cap at or above the smallest
-      const ChunkPlan cw = fused_chunk_plan(ntk, s.G, s.Nv, wph, kFusedSlots);
-      if (cw.width > wmax) wmax = cw.width;
-    }
-    cfg->rec_stride = (int)rec;
-    cfg->max_chunks = maxc;
-    cfg->max_rg = maxrg;
-    cfg->wmax = wmax;
-    const int tb = (int)tile_bytes;
-    cfg->flds = fused_lds_layout(tb, fused_ring_depth(tb), s.cap, s.Hkv, lb, s.Nt);
-    // 4 KB for the kernel's static LDS (2.5 KB)
-    const bool lds_ok = (size_t)cfg->flds.total + 4096 <= kMaxLds &&
-                        (size_t)(s.G > 1 ? s.G : 1) * s.Nt * sizeof(float) <= (size_t)cfg->flds.total;  // one head's logits
-    // the schedule is worked out by one wave: at most 8 (layer, sample) pairs per lane
-    const bool items_ok = lb <= 512 && (long long)lb * maxc * maxrg <= (long long)kFusedMaxItems * kFusedTargetCus &&
-                          maxc <= 64;
-    const bool rec_ok = rec * 16 < (1ll << 31);
-    // the elite merge holds two text tokens per thread
-    const bool txt_ok = s.Nt <= 2 * kFusedThreads;
-    cfg->chunked = heads_ok && lds_ok && items_ok && rec_ok && txt_ok;
+    const int esize = d->dtype == AIRCACHE_BF16 ? 2 : 4;
+    int hgs = 1;
+    while (hgs < 8 && s.Hkv % (hgs * 2) == 0) hgs *= 2;
+    cfg->hgs = hgs;
+    cfg->nhg = s.Hkv / hgs;
+    cfg->wph = kPassWaves / hgs;
+    cfg->width = cfg->wph * 16 * pass_kt(s.D, esize);
+    cfg->nch = (s.Nv + cfg->width - 1) / cfg->width;
+    cfg->rows = pass_rtp(s.D, esize) * 16;
+    cfg->erec_stride = 1 + 2 * pass_words64(s.Nt);
+    cfg->plds = pass_lds_layout(s.D, esize, hgs, cfg->width, s.G, s.Nt, s.Nv, s.L);
+    const long long rtg_max = ((long long)s.G * s.cap + 15) / 16;
+    const long long npass_max = (long long)cfg->nhg * ((rtg_max + pass_rtp(s.D, esize) - 1) / pass_rtp(s.D, esize));
+    const bool lds_ok = (size_t)cfg->plds.total + 4096 <= kMaxLds &&
+                        (long long)(s.G > 1 ? s.G : 1) * s.Nt * 4 <= cfg->plds.z_bytes &&
+                        (size_t)(kTopkLdsWords * 4 + 16) + (size_t)s.Nv * 4 + (size_t)(s.L + 16) * 28 <= (size_t)kRingBytes;
+    const bool ok = lds_ok && cfg->nch <= 64 && npass_max < kPassMaxPass && s.Nt <= 2 * kPassThreads;
+    cfg->chunked = ok;
   }
   if (d->path == AIRCACHE_PATH_CHUNKED && !cfg->chunked)
-    return fail(AIRCACHE_EINVAL, "the chunked path needs n_kv_heads in {1, 2, 4, 8} and a smaller batch or elite cap");
+    return fail(AIRCACHE_EINVAL, "the chunked path needs n_txt <= 1024, at most 64 chunks of visual keys and a "
+                "smaller elite cap or head group");
   if (d->path == AIRCACHE_PATH_TILED || d->path == AIRCACHE_PATH_ROWS) cfg->chunked = false;
   if (d->path == AIRCACHE_PATH_TILED || d->path == AIRCACHE_PATH_CHUNKED) cfg->rows_kt = 0;
   cfg->path = cfg->chunked ? AIRCACHE_PATH_CHUNKED : cfg->rows_kt ? AIRCACHE_PATH_ROWS : AIRCACHE_PATH_TILED;
   // aircache_run compacts inside the chunked launch when the five pointer
-  // tables fit its table and the kept indices of a pair fit the ring
-  cfg->run_fused = cfg->chunked && 5 * s.L <= kFusedTableSlots &&
-                   (size_t)s.Nv * sizeof(int) <= (size_t)(cfg->flds.el - cfg->flds.ring);
+  // tables fit its table
+  cfg->run_fused = cfg->chunked && 5 * s.L <= kPassTableSlots;
   cfg->off_cnt = kEpochBytes;
   cfg->off_cnt_elite = cfg->off_cnt + align_up(n_cnt * sizeof(unsigned));
   cfg->off_pbar = cfg->off_cnt_elite + align_up((size_t)s.L * s.B * sizeof(unsigned));
   cfg->off_sched = cfg->off_pbar + align_up((size_t)s.L * s.B * s.Hkv * s.Nt * sizeof(float));
-  // exit and compaction-ticket counters of the chunked path
-  const size_t eflags = cfg->chunked ? align_up(2 * sizeof(unsigned)) : 0;
-  cfg->off_stats = cfg->off_sched + eflags;
-  cfg->off_xrec = cfg->off_mom = cfg->off_srec = cfg->off_stats;
+  cfg->off_stats = cfg->off_sched;
   if (cfg->chunked) {
+    // head at offset 0: the call count (epoch), exit counter, flags, wrap
+    // counter; then the records (the other paths' counters are not used)
     const size_t lbs = (size_t)s.L * s.B;
+    cfg->off_pass_head = 0;
+    cfg->off_parts = cfg->off_pass_head + kEpochBytes;
+    cfg->off_erec = cfg->off_parts + align_up(lbs * (size_t)s.Hkv * s.Nt * sizeof(uint64_t));
+    cfg->off_xrec = cfg->off_erec + align_up(lbs * (size_t)cfg->erec_stride * sizeof(uint64_t));
+    cfg->off_mom = cfg->off_xrec + align_up(lbs * 2 * (size_t)cfg->nch * cfg->hgs * cfg->rows * 16);
+    cfg->off_ivrec = cfg->off_mom + align_up(lbs * (size_t)cfg->nch * 64);
+    cfg->off_brec = cfg->off_ivrec + align_up(lbs * (size_t)s.Nv * sizeof(uint64_t));
+    cfg->ws_bytes = cfg->off_brec + align_up(lbs * sizeof(uint64_t));
     cfg->off_e = cfg->off_part = cfg->off_stats;
-    cfg->off_xrec = cfg->off_stats;
-    cfg->off_mom = cfg->off_xrec + align_up(lbs * (size_t)cfg->rec_stride * 16);
-    cfg->off_srec = cfg->off_mom + align_up(lbs * (size_t)cfg->max_chunks * 64);
-    cfg->off_cnt_chunk = cfg->off_srec + align_up(lbs * 32);
-    cfg->off_ivrec = cfg->off_cnt_chunk + align_up(lbs * (size_t)cfg->max_chunks * sizeof(unsigned));
-    cfg->off_keptrec = cfg->off_ivrec + align_up(lbs * (size_t)s.Nv * sizeof(uint64_t));
-    cfg->off_grec = cfg->off_keptrec + align_up(lbs * (size_t)s.Nv * sizeof(uint64_t));
-    // elite-window parts: up to one per KV head (the launch picks how many)
-    cfg->off_parts64 = cfg->off_grec + align_up(lbs * 32);
-    cfg->off_erec = cfg->off_parts64 + align_up(lbs * (size_t)s.Hkv * s.Nt * sizeof(uint64_t));
-    cfg->off_hint = cfg->off_erec + align_up(lbs * (size_t)(1 + 2 * fused_words64(s.Nt)) * sizeof(uint64_t));
-    cfg->off_part_rg = cfg->off_hint + align_up((size_t)kFusedHintSlots * sizeof(uint64_t));
-    // row-group partial sums only when some elite count can need two row groups
-    const size_t part_rg = cfg->max_rg > 1 ? lbs * (size_t)cfg->max_chunks * cfg->max_rg * cfg->wmax * sizeof(float) : 0;
-    cfg->ws_bytes = cfg->off_part_rg + align_up(part_rg);
   } else if (cfg->rows_kt) {
     cfg->off_e = cfg->off_stats;
     cfg->off_part = cfg->off_stats;
@@ -1348,10 +1327,10 @@ Ws ws_of(const Config &cfg, void *base) {
   w.stats = reinterpret_cast<float2 *>(p + cfg.off_stats);
   w.e = reinterpret_cast<float *>(p + cfg.off_e);
   w.part = reinterpret_cast<float *>(p + cfg.off_part);
-  w.cnt_chunk = cfg.chunked ? reinterpret_cast<unsigned *>(p + cfg.off_cnt_chunk) : nullptr;
+  w.cnt_chunk = nullptr;
   w.cnt_elite = reinterpret_cast<unsigned *>(p + cfg.off_cnt_elite);
   w.pbar_part = reinterpret_cast<float *>(p + cfg.off_pbar);
-  w.chunk_stride = cfg.chunked ? cfg.max_chunks : 0;
+  w.chunk_stride = 0;
   return w;
 }
 
@@ -1468,69 +1447,79 @@ int launch_rows(const Config &cfg, const LayerTable &qt, const LayerTable &kt, c
   return check_hip(hipGetLastError(), "cross_score_rows_kernel launch");
 }
 
-// Workgroups of cross_score_fused_kernel: as many as are resident at once.
-template <typename Tag, int D> int fused_grid(const Config &cfg, int *grid) {
-  auto kern = cross_score_fused_kernel<Tag, D>;
-  const size_t lds = (size_t)cfg.flds.total;
+// Workgroups of aircache_pass_kernel: as many as are resident at once (one
+// per CU: the LDS use admits no second).
+template <typename Tag, int D> int pass_grid(const Config &cfg, int *grid) {
+  auto kern = aircache_pass_kernel<Tag, D>;
+  const size_t lds = (size_t)cfg.plds.total;
   int rc;
   if ((rc = allow_lds(kern, lds))) return rc;
   int cus = 0;
   if ((rc = device_cus(&cus))) return rc;
   int occ = 0;
-  if ((rc = occupancy(kern, kFusedThreads, lds, &occ))) return rc;
+  if ((rc = occupancy(kern, kPassThreads, lds, &occ))) return rc;
   if (occ < 1) return fail(AIRCACHE_EINVAL, "the chunked kernel does not fit a compute unit");
   *grid = cus * occ;
   return AIRCACHE_OK;
 }
 
-// Compaction outputs for a chunked launch that also compacts (NULL: plan only).
+// Compaction operands of a chunked launch that also compacts (NULL: plan only).
 struct RunOut {
   const LayerTable *v;
   const LayerTable *ko, *vo;
 };
 
+// The schedule of one chunked launch on `grid` workgroups: elite parts per
+// (layer, sample) (the most KV-head groups, a divisor of H_kv, that still
+// leave half the grid to round 0), elite workgroups, pairs per round.
+int pass_schedule(const Config &cfg, int grid, PassWs *pw) {
+  const Shape &s = cfg.sh;
+  const long long LB = (long long)s.L * s.B;
+  if (cfg.nch > grid) return fail(AIRCACHE_EINVAL, "%d chunks per (layer, sample) exceed %d workgroups", cfg.nch, grid);
+  int npp = 1;
+  while (npp < s.Hkv && npp < 8 && s.Hkv % (npp * 2) == 0 && LB * npp * 2 * 2 <= grid) npp *= 2;
+  pw->npp = npp;
+  pw->E = (int)(LB * npp < grid ? LB * npp : grid);
+  pw->ppr0 = (grid - pw->E) / cfg.nch;
+  pw->ppr = grid / cfg.nch;
+  return AIRCACHE_OK;
+}
+
 template <typename Tag, int D>
-int launch_chunked(const Config &cfg, const LayerTable &qt, const LayerTable &kt, const PlanPtrs &pp, const Ws &ws,
+int launch_chunked(const Config &cfg, const LayerTable &qt, const LayerTable &kt, const PlanPtrs &pp,
                    void *ws_base, int grid, hipStream_t st, const RunOut *out) {
   const Shape &s = cfg.sh;
-  auto kern = cross_score_fused_kernel<Tag, D>;
-  const size_t lds = (size_t)cfg.flds.total;
-  // every chunk of a (layer, sample) needs a workgroup of its own, and the
-  // item list of a workgroup is bounded
-  if (cfg.max_chunks > grid) return fail(AIRCACHE_EINVAL, "%d chunks per (layer, sample) exceed %d workgroups", cfg.max_chunks, grid);
-  if ((long long)s.L * s.B * cfg.max_chunks > (long long)kFusedMaxItems * grid)
-    return fail(AIRCACHE_EINVAL, "too many work items for %d workgroups", grid);
+  auto kern = aircache_pass_kernel<Tag, D>;
+  const size_t lds = (size_t)cfg.plds.total;
   char *p = static_cast<char *>(ws_base);
-  FusedWs fw;
-  fw.epoch = ws.epoch;
-  fw.exitc = reinterpret_cast<unsigned *>(p + cfg.off_sched);
-  fw.xrec = reinterpret_cast<uint64_t *>(p + cfg.off_xrec);
-  fw.mom = reinterpret_cast<uint64_t *>(p + cfg.off_mom);
-  fw.ivrec = reinterpret_cast<uint64_t *>(p + cfg.off_ivrec);
-  fw.keptrec = reinterpret_cast<uint64_t *>(p + cfg.off_keptrec);
-  fw.srec = reinterpret_cast<uint64_t *>(p + cfg.off_srec);
-  fw.rec_stride = cfg.rec_stride;
-  fw.max_chunks = cfg.max_chunks;
-  fw.max_rg = cfg.max_rg;
-  fw.wmax = cfg.wmax;
-  fw.cnt_chunk = ws.cnt_chunk;
-  fw.part = reinterpret_cast<float *>(p + cfg.off_part_rg);
-  fw.parts = reinterpret_cast<uint64_t *>(p + cfg.off_parts64);
-  // parts per (layer, sample): the most KV-head groups (a divisor of H_kv)
-  // that still give every part a workgroup of its own; the parts of one
-  // (layer, sample) are loaded by as many CUs
-  fw.npp = 1;
-  while (fw.npp < s.Hkv && (long long)s.L * s.B * fw.npp * 2 <= grid) fw.npp *= 2;
-  fw.kcap_lo = cfg.fused_kcap_lo;
-  fw.erec = reinterpret_cast<uint64_t *>(p + cfg.off_erec);
-  fw.hint = reinterpret_cast<uint64_t *>(p + cfg.off_hint);
-  fw.erec_stride = 1 + 2 * fused_words64(s.Nt);
-  fw.gticket = fw.exitc + 1;
-  fw.grec = reinterpret_cast<uint64_t *>(p + cfg.off_grec);
-  fw.gather = out ? 1 : 0;
-  fw.esize = (int)(cfg.tile_bytes / (16 * s.D));
-  fw.cap_elems = (int64_t)s.B * s.Hkv * (int64_t)s.S * s.D;
-  FusedTables tab;
+  PassWs pw;
+  int rc;
+  if ((rc = pass_schedule(cfg, grid, &pw))) return rc;
+  unsigned *head = reinterpret_cast<unsigned *>(p + cfg.off_pass_head);
+  pw.epoch = head;
+  pw.exitc = head + 1;
+  pw.flags = reinterpret_cast<int *>(head + 2);
+  pw.wrapc = head + 3;
+  pw.recs = reinterpret_cast<u32x4_t *>(p + cfg.off_parts);
+  pw.rec_words = (cfg.ws_bytes - cfg.off_parts) / 16;
+  pw.parts = reinterpret_cast<uint64_t *>(p + cfg.off_parts);
+  pw.erec = reinterpret_cast<uint64_t *>(p + cfg.off_erec);
+  pw.xrec = reinterpret_cast<uint64_t *>(p + cfg.off_xrec);
+  pw.mom = reinterpret_cast<uint64_t *>(p + cfg.off_mom);
+  pw.ivrec = reinterpret_cast<uint64_t *>(p + cfg.off_ivrec);
+  pw.brec = reinterpret_cast<uint64_t *>(p + cfg.off_brec);
+  pw.erec_stride = cfg.erec_stride;
+  pw.hgs = cfg.hgs;
+  pw.nhg = cfg.nhg;
+  pw.wph = cfg.wph;
+  pw.width = cfg.width;
+  pw.nch = cfg.nch;
+  pw.rows = cfg.rows;
+  pw.gather = out ? 1 : 0;
+  pw.units = (int)((long long)s.L * s.B * (out ? s.Hkv * 2 : 1));
+  pw.esize = (int)(cfg.tile_bytes / (16 * s.D));
+  pw.cap_elems = (int64_t)s.B * s.Hkv * (int64_t)s.S * s.D;
+  PassTables tab;
   memset(&tab, 0, sizeof(tab));
   for (int l = 0; l < s.L; ++l) {
     tab.p[l] = qt.p[l];
@@ -1541,12 +1530,11 @@ int launch_chunked(const Config &cfg, const LayerTable &qt, const LayerTable &kt
       tab.p[4 * s.L + l] = out->vo->p[l];
     }
   }
-  // One workgroup per CU (the LDS use admits no second), so with the device
-  // to itself every workgroup is resident at once, which the waits between
-  // workgroups need; if other work holds CUs, the bounded waits report
-  // AIRCACHE_DEV_TIMEOUT instead of hanging.
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kFusedThreads), lds, st, s, tab, pp, fw, cfg.flds);
-  return check_hip(hipGetLastError(), "cross_score_fused_kernel launch");
+  // every workgroup resident at once, which the waits between workgroups
+  // need; if other work holds CUs, the bounded waits report
+  // AIRCACHE_DEV_TIMEOUT instead of hanging
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kPassThreads), lds, st, s, tab, pp, pw, cfg.plds);
+  return check_hip(hipGetLastError(), "aircache_pass_kernel launch");
 }
 
 template <typename Tag, int D, int KTW>
@@ -1559,10 +1547,10 @@ int launch_plan(const Config &cfg, const LayerTable &qt, const LayerTable &kt, c
     // elite sets, scoring, statistics, budgets and top-k in one launch (the
     // elite interval of the profiled call is empty)
     int fgrid = 0;
-    if ((rc = fused_grid<Tag, D>(cfg, &fgrid))) return rc;
+    if ((rc = pass_grid<Tag, D>(cfg, &fgrid))) return rc;
     if ((rc = mark(ev, 0, st))) return rc;
     if ((rc = mark(ev, 1, st))) return rc;
-    if ((rc = launch_chunked<Tag, D>(cfg, qt, kt, pp, ws, ws_base, fgrid, st, nullptr))) return rc;
+    if ((rc = launch_chunked<Tag, D>(cfg, qt, kt, pp, ws_base, fgrid, st, nullptr))) return rc;
     if ((rc = mark(ev, 2, st))) return rc;
     if ((rc = mark(ev, 3, st))) return rc;
     return mark(ev, 4, st);
@@ -1709,20 +1697,19 @@ int run_pass(const Config &cfg, const aircache_desc *desc, const void *const *q_
       vot.p[l] = tb.vo.p[l];
     }
     const RunOut out{&vt, &kot, &vot};
-    const Ws ws = ws_of(cfg, workspace);
     int fgrid = 0;
     if (bf && cfg.sh.D == 128) {
-      if (!(rc = fused_grid<Bf16Tag, 128>(cfg, &fgrid)))
-        rc = launch_chunked<Bf16Tag, 128>(cfg, qt, kt, pp, ws, workspace, fgrid, st, &out);
+      if (!(rc = pass_grid<Bf16Tag, 128>(cfg, &fgrid)))
+        rc = launch_chunked<Bf16Tag, 128>(cfg, qt, kt, pp, workspace, fgrid, st, &out);
     } else if (bf) {
-      if (!(rc = fused_grid<Bf16Tag, 64>(cfg, &fgrid)))
-        rc = launch_chunked<Bf16Tag, 64>(cfg, qt, kt, pp, ws, workspace, fgrid, st, &out);
+      if (!(rc = pass_grid<Bf16Tag, 64>(cfg, &fgrid)))
+        rc = launch_chunked<Bf16Tag, 64>(cfg, qt, kt, pp, workspace, fgrid, st, &out);
     } else if (cfg.sh.D == 128) {
-      if (!(rc = fused_grid<F32Tag, 128>(cfg, &fgrid)))
-        rc = launch_chunked<F32Tag, 128>(cfg, qt, kt, pp, ws, workspace, fgrid, st, &out);
+      if (!(rc = pass_grid<F32Tag, 128>(cfg, &fgrid)))
+        rc = launch_chunked<F32Tag, 128>(cfg, qt, kt, pp, workspace, fgrid, st, &out);
     } else {
-      if (!(rc = fused_grid<F32Tag, 64>(cfg, &fgrid)))
-        rc = launch_chunked<F32Tag, 64>(cfg, qt, kt, pp, ws, workspace, fgrid, st, &out);
+      if (!(rc = pass_grid<F32Tag, 64>(cfg, &fgrid)))
+        rc = launch_chunked<F32Tag, 64>(cfg, qt, kt, pp, workspace, fgrid, st, &out);
     }
     if (rc) return rc;
   } else {

@@ -60,22 +60,38 @@ def test_workspace_size(lib):
 
 
 def test_resolved_path(lib):
-    # chunked for 1, 2, 4 or 8 KV heads; else rows while N_v fits 8 waves x 16
-    # keys x 24 tiles (3072 keys); else tiled
+    # chunked (one launch) whenever the shape fits it: any number of KV heads
+    # (head groups of up to eight), N_t <= 1024, at most 64 chunks of visual
+    # keys; else rows while N_v fits 8 waves x 16 keys x 24 tiles (3072 keys);
+    # else tiled
     assert _lib.resolved_path(desc()) == _lib.PATH_CHUNKED
     assert _lib.resolved_path(desc(n_vis=6272, n_txt=256)) == _lib.PATH_CHUNKED
-    for hkv in (1, 2, 8):
+    for hkv in (1, 2, 3, 7, 8, 32):
         assert _lib.resolved_path(desc(n_q_heads=8 * hkv, n_kv_heads=hkv)) == _lib.PATH_CHUNKED
-    assert _lib.resolved_path(desc(n_kv_heads=7)) == _lib.PATH_ROWS
-    assert _lib.resolved_path(desc(n_kv_heads=7, n_vis=3072)) == _lib.PATH_ROWS
-    assert _lib.resolved_path(desc(n_kv_heads=7, n_vis=3073)) == _lib.PATH_TILED
-    assert _lib.resolved_path(desc(n_q_heads=32, n_kv_heads=32)) == _lib.PATH_ROWS
+    assert _lib.resolved_path(desc(n_q_heads=32, n_kv_heads=32)) == _lib.PATH_CHUNKED
+    assert _lib.resolved_path(desc(n_txt=1100)) == _lib.PATH_ROWS            # N_t beyond the elite parts
+    # float32 with D = 128: 64-key chunks, so N_v > 4096 is more than 64 chunks
+    assert _lib.resolved_path(desc(dtype="f32", n_vis=4096)) == _lib.PATH_CHUNKED
+    assert _lib.resolved_path(desc(dtype="f32", n_vis=4097)) == _lib.PATH_TILED
     assert _lib.resolved_path(desc(path=1)) == _lib.PATH_TILED
     assert _lib.resolved_path(desc(path=2)) == _lib.PATH_ROWS
     assert _lib.resolved_path(desc(path=2, n_vis=17)) == _lib.PATH_ROWS
     assert _lib.resolved_path(desc(path=3, n_vis=17)) == _lib.PATH_CHUNKED
-    assert _lib.resolved_path(desc(path=3, n_kv_heads=7)) == -1
+    assert _lib.resolved_path(desc(path=3, n_kv_heads=7)) == _lib.PATH_CHUNKED
+    assert _lib.resolved_path(desc(path=3, n_txt=1100)) == -1
     assert _lib.resolved_path(desc(path=2, n_vis=3073)) == -1
+
+
+def test_chunked_workspace_does_not_depend_on_the_elite_cap(lib):
+    """The one-launch path's records are sized by the shape alone (row
+    normaliser slots are reused pass after pass), so the default max_elite = 0
+    (cap N_t) costs no more workspace than a small cap, and the five workloads
+    stay on the one-launch path with workspaces of tens of megabytes."""
+    for kw in (dict(), dict(n_vis=6272, n_txt=256, batch=4), dict(n_vis=3072, n_txt=1024, batch=8)):
+        a = _lib.workspace_size(desc(max_elite=0, **kw))
+        assert a == _lib.workspace_size(desc(max_elite=8, **kw))
+        assert 0 < a < 128 << 20
+        assert _lib.resolved_path(desc(max_elite=0, **kw)) == _lib.PATH_CHUNKED
 
 
 def test_run_launches(lib):

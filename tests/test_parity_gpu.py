@@ -324,3 +324,55 @@ def test_deterministic_rerun_one_launch():
                     assert np.array_equal(a[key][l, bb, :n[l, bb]], b[key][l, bb, :n[l, bb]]), key
         else:
             assert np.array_equal(a[key], b[key]), key
+
+
+def _set_word(ac, index, value):
+    """Set 32-bit word `index` of the pass's workspace (the one-launch path
+    keeps its call count at word 0 and its condition flags at word 2)."""
+    import struct
+    ac.workspace[4 * index:4 * index + 4] = torch.tensor(np.frombuffer(struct.pack("<I", value & 0xFFFFFFFF),
+                                                                       np.uint8).copy(), device=ac.workspace.device)
+
+
+@pytest.mark.parametrize("start", [(1 << 21) - 1, 0xFFFFFFFF])
+def test_epoch_wrap(start):
+    """Call counts at the edges of the record tags: a call whose epoch is a
+    multiple of 2^21 first zeroes every record and waits for the whole grid;
+    the count wrapping past 2^32 skips epoch 0 (the tag of a zeroed record).
+    Both that call and the next match the oracle."""
+    from parity import make_aircache
+    w = wl.custom(L=3, B=2, Hq=8, Hkv=2, D=128, Nv=500, Nt=30, dtype="bf16", ratio=0.2)
+    ac = make_aircache(w)
+    assert ac.scoring_path == "chunked"
+    if start != 0xFFFFFFFF:
+        inp = wl.make_inputs(w, 60)
+        compare(inp, g := run_gpu(inp, ac=ac, run=True), reference(inp, g))
+    torch.cuda.synchronize()
+    _set_word(ac, 0, start)
+    for seed in (61, 62):
+        print(f"[parity] epoch wrap from {start:#x}, seed {seed}", flush=True)
+        inp = wl.make_inputs(w, seed)
+        g = run_gpu(inp, ac=ac, run=True)
+        compare(inp, g, reference(inp, g))
+
+
+def test_forced_timeout_is_flagged_then_cleared():
+    """The bounded waits of the one-launch pass, forced from the host: with the
+    workspace's flags word set to AIRCACHE_DEV_TIMEOUT before a call, every wait
+    gives up after its first 256 polls; the kernel still ends, reports the bit
+    in the status word and clears the flags, and the next call is exact."""
+    from parity import make_aircache
+    w = wl.custom(L=3, B=2, Hq=8, Hkv=2, D=128, Nv=500, Nt=30, dtype="bf16", ratio=0.2)
+    ac = make_aircache(w)
+    assert ac.scoring_path == "chunked"
+    inp = wl.make_inputs(w, 70)
+    g = run_gpu(inp, ac=ac, run=True)
+    compare(inp, g, reference(inp, g))
+    torch.cuda.synchronize()
+    _set_word(ac, 2, 2)  # AIRCACHE_DEV_TIMEOUT
+    print("[parity] forced timeout", flush=True)
+    g = run_gpu(wl.make_inputs(w, 71), ac=ac, run=True)
+    assert g["status"][0] & 2
+    inp = wl.make_inputs(w, 72)
+    g = run_gpu(inp, ac=ac, run=True)
+    compare(inp, g, reference(inp, g))
