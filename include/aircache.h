@@ -122,11 +122,14 @@ typedef struct {
  * the exponentials spilled to the workspace and a separate merge kernel; any
  * size. ROWS: a workgroup per group of up to four 16-row tiles of elite
  * queries keeps their whole rows of logits in registers (n_vis <= 3072).
- * CHUNKED: one persistent launch for
- * scoring, statistics, budgets and top-k; a workgroup takes a run of visual
- * keys of every KV head of one (layer, sample) and swaps row maxima and sums
- * with the other runs (n_kv_heads in {1, 2, 4, 8}). AUTO picks CHUNKED, else
- * ROWS, else TILED. */
+ * CHUNKED: one persistent launch for the elite sets, scoring, statistics,
+ * budgets and top-k (and, from aircache_run, the compaction): once every
+ * elite set size is known, each workgroup takes a chunk of the keys (visual,
+ * then elite text) of one (layer, sample) for every KV head, chunks narrower
+ * where there are more elite rows, and swaps row maxima and sums with the
+ * other chunks of its (layer, sample); any n_kv_heads; n_txt <= 1024,
+ * n_layers * batch <= 2048 and the per-layer statistics within a CU's LDS.
+ * AUTO picks CHUNKED, else ROWS, else TILED. */
 #define AIRCACHE_PATH_AUTO 0
 #define AIRCACHE_PATH_TILED 1
 #define AIRCACHE_PATH_ROWS 2

@@ -1155,9 +1155,8 @@ struct Config {
   bool chunked;        // aircache_pass_kernel: the whole pass in one launch
   int path;            // AIRCACHE_PATH_TILED, _ROWS or _CHUNKED
   // chunked path: schedule facts fixed by the shape, workspace offsets, LDS
-  int hgs, nhg, wph, width, nch, rows;
-  size_t off_pass_head, off_parts, off_erec, off_xrec, off_mom, off_ivrec, off_brec;
-  int erec_stride;
+  int hgs, nhg, wph, rows, mnch, kcap_lo, nmw;
+  size_t off_pass_head, off_parts, off_ecnt, off_emask, off_xrec, off_mom, off_ivrec, off_brec;
   PassLds plds;
 };
 
@@ -1251,34 +1250,37 @@ int make_config(const aircache_desc *d, Config *cfg) {
   if (d->path == AIRCACHE_PATH_ROWS && !cfg->rows_kt)
     return fail(AIRCACHE_EINVAL, "the rows path needs n_vis <= %d", kRowsWaves * 16 * kRowsKtMax);
   // Chunked path: a head group is the largest power of two up to eight that
-  // divides H_kv; the chunk width fills the LDS ring (wph * 16 * KT keys); a
-  // (layer, sample) has at most 64 chunks, its passes stay within the record
-  // tags, the elite window within the elite parts' limits, and the LDS layout
-  // within a CU.
+  // divides H_kv (a wave group per KV head); the records are sized for the
+  // most chunks a pair can have (the elite cap, the smallest key-tile cap);
+  // the passes of an item stay within the record tags, the elite window
+  // within the elite parts' limits, and the LDS layout within a CU.
   cfg->chunked = false;
   {
     const int esize = d->dtype == AIRCACHE_BF16 ? 2 : 4;
+    const int rtpm = pass_rtp(s.D, esize);
     int hgs = 1;
     while (hgs < 8 && s.Hkv % (hgs * 2) == 0) hgs *= 2;
     cfg->hgs = hgs;
     cfg->nhg = s.Hkv / hgs;
     cfg->wph = kPassWaves / hgs;
-    cfg->width = cfg->wph * 16 * pass_kt(s.D, esize);
-    cfg->nch = (s.Nv + cfg->width - 1) / cfg->width;
-    cfg->rows = pass_rtp(s.D, esize) * 16;
-    cfg->erec_stride = 1 + 2 * pass_words64(s.Nt);
-    cfg->plds = pass_lds_layout(s.D, esize, hgs, cfg->width, s.G, s.Nt, s.Nv, s.L);
+    cfg->rows = rtpm * 16;
+    cfg->nmw = 2 * pass_words64(s.Nt);
+    cfg->kcap_lo = pass_kcap_min(s.L, s.B, s.Nv, cfg->wph);
+    cfg->mnch = item_plan(s.cap, s.G, s.Nv, cfg->wph, cfg->kcap_lo, s.D, esize).nch;
+    const long long LB = (long long)s.L * s.B;
+    const bool lb_ok = LB <= 2048;
+    cfg->plds = pass_lds_layout(s.D, esize, hgs, lb_ok ? (int)LB : 0, s.Nt, s.Nv);
     const long long rtg_max = ((long long)s.G * s.cap + 15) / 16;
-    const long long npass_max = (long long)cfg->nhg * ((rtg_max + pass_rtp(s.D, esize) - 1) / pass_rtp(s.D, esize));
+    const long long npass_max = (long long)cfg->nhg * ((rtg_max + rtpm - 1) / rtpm);
     const bool lds_ok = (size_t)cfg->plds.total + 4096 <= kMaxLds &&
                         (long long)(s.G > 1 ? s.G : 1) * s.Nt * 4 <= cfg->plds.z_bytes &&
-                        (size_t)(kTopkLdsWords * 4 + 16) + (size_t)s.Nv * 4 + (size_t)(s.L + 16) * 28 <= (size_t)kRingBytes;
-    const bool ok = lds_ok && cfg->nch <= 64 && npass_max < kPassMaxPass && s.Nt <= 2 * kPassThreads;
+                        (long long)cfg->plds.sts + pass_sts_bytes(s.L, cfg->mnch) <= (long long)kRingBytes;
+    const bool ok = lb_ok && lds_ok && npass_max < kPassMaxPass && s.Nt <= 2 * kPassThreads;
     cfg->chunked = ok;
   }
   if (d->path == AIRCACHE_PATH_CHUNKED && !cfg->chunked)
-    return fail(AIRCACHE_EINVAL, "the chunked path needs n_txt <= 1024, at most 64 chunks of visual keys and a "
-                "smaller elite cap or head group");
+    return fail(AIRCACHE_EINVAL, "the chunked path needs n_txt <= 1024, n_layers * batch <= 2048 and an elite cap, "
+                "n_vis and layer count whose records and statistics fit its LDS");
   if (d->path == AIRCACHE_PATH_TILED || d->path == AIRCACHE_PATH_ROWS) cfg->chunked = false;
   if (d->path == AIRCACHE_PATH_TILED || d->path == AIRCACHE_PATH_CHUNKED) cfg->rows_kt = 0;
   cfg->path = cfg->chunked ? AIRCACHE_PATH_CHUNKED : cfg->rows_kt ? AIRCACHE_PATH_ROWS : AIRCACHE_PATH_TILED;
@@ -1296,10 +1298,11 @@ int make_config(const aircache_desc *d, Config *cfg) {
     const size_t lbs = (size_t)s.L * s.B;
     cfg->off_pass_head = 0;
     cfg->off_parts = cfg->off_pass_head + kEpochBytes;
-    cfg->off_erec = cfg->off_parts + align_up(lbs * (size_t)s.Hkv * s.Nt * sizeof(uint64_t));
-    cfg->off_xrec = cfg->off_erec + align_up(lbs * (size_t)cfg->erec_stride * sizeof(uint64_t));
-    cfg->off_mom = cfg->off_xrec + align_up(lbs * 2 * (size_t)cfg->nch * cfg->hgs * cfg->rows * 16);
-    cfg->off_ivrec = cfg->off_mom + align_up(lbs * (size_t)cfg->nch * 64);
+    cfg->off_ecnt = cfg->off_parts + align_up(lbs * (size_t)s.Hkv * s.Nt * sizeof(uint64_t));
+    cfg->off_emask = cfg->off_ecnt + align_up(lbs * sizeof(uint64_t));
+    cfg->off_xrec = cfg->off_emask + align_up(lbs * (size_t)cfg->nmw * sizeof(uint64_t));
+    cfg->off_mom = cfg->off_xrec + align_up(lbs * 2 * (size_t)cfg->mnch * cfg->hgs * cfg->rows * 16);
+    cfg->off_ivrec = cfg->off_mom + align_up(lbs * (size_t)cfg->mnch * 64);
     cfg->off_brec = cfg->off_ivrec + align_up(lbs * (size_t)s.Nv * sizeof(uint64_t));
     cfg->ws_bytes = cfg->off_brec + align_up(lbs * sizeof(uint64_t));
     cfg->off_e = cfg->off_part = cfg->off_stats;
@@ -1469,19 +1472,21 @@ struct RunOut {
   const LayerTable *ko, *vo;
 };
 
-// The schedule of one chunked launch on `grid` workgroups: elite parts per
-// (layer, sample) (the most KV-head groups, a divisor of H_kv, that still
-// leave half the grid to round 0), elite workgroups, pairs per round.
+// The host's part of a chunked launch on `grid` workgroups: elite parts per
+// (layer, sample) and elite workgroups; the chunks of a pair must fit the grid
+// at the widest chunks (the kernel schedules the rest).
 int pass_schedule(const Config &cfg, int grid, PassWs *pw) {
   const Shape &s = cfg.sh;
   const long long LB = (long long)s.L * s.B;
-  if (cfg.nch > grid) return fail(AIRCACHE_EINVAL, "%d chunks per (layer, sample) exceed %d workgroups", cfg.nch, grid);
+  const int esize = (int)(cfg.tile_bytes / (16 * s.D));
+  const int widest = item_plan(s.cap, s.G, s.Nv, cfg.wph, kKtwMax, s.D, esize).nch;
+  if (widest > grid) return fail(AIRCACHE_EINVAL, "%d chunks per (layer, sample) exceed %d workgroups", widest, grid);
+  // parts per (layer, sample): the most KV-head groups (a power of two up to
+  // eight dividing H_kv) with every part on a workgroup of its own
   int npp = 1;
-  while (npp < s.Hkv && npp < 8 && s.Hkv % (npp * 2) == 0 && LB * npp * 2 * 2 <= grid) npp *= 2;
+  while (npp < s.Hkv && npp < 8 && s.Hkv % (npp * 2) == 0 && LB * npp * 2 <= grid) npp *= 2;
   pw->npp = npp;
-  pw->E = (int)(LB * npp < grid ? LB * npp : grid);
-  pw->ppr0 = (grid - pw->E) / cfg.nch;
-  pw->ppr = grid / cfg.nch;
+  pw->EW = (int)(LB * npp < grid ? LB * npp : grid);
   return AIRCACHE_OK;
 }
 
@@ -1503,18 +1508,19 @@ int launch_chunked(const Config &cfg, const LayerTable &qt, const LayerTable &kt
   pw.recs = reinterpret_cast<u32x4_t *>(p + cfg.off_parts);
   pw.rec_words = (cfg.ws_bytes - cfg.off_parts) / 16;
   pw.parts = reinterpret_cast<uint64_t *>(p + cfg.off_parts);
-  pw.erec = reinterpret_cast<uint64_t *>(p + cfg.off_erec);
+  pw.ecnt = reinterpret_cast<uint64_t *>(p + cfg.off_ecnt);
+  pw.emask = reinterpret_cast<uint64_t *>(p + cfg.off_emask);
   pw.xrec = reinterpret_cast<uint64_t *>(p + cfg.off_xrec);
   pw.mom = reinterpret_cast<uint64_t *>(p + cfg.off_mom);
   pw.ivrec = reinterpret_cast<uint64_t *>(p + cfg.off_ivrec);
   pw.brec = reinterpret_cast<uint64_t *>(p + cfg.off_brec);
-  pw.erec_stride = cfg.erec_stride;
+  pw.nmw = cfg.nmw;
   pw.hgs = cfg.hgs;
   pw.nhg = cfg.nhg;
   pw.wph = cfg.wph;
-  pw.width = cfg.width;
-  pw.nch = cfg.nch;
   pw.rows = cfg.rows;
+  pw.mnch = cfg.mnch;
+  pw.kcap_lo = cfg.kcap_lo;
   pw.gather = out ? 1 : 0;
   pw.units = (int)((long long)s.L * s.B * (out ? s.Hkv * 2 : 1));
   pw.esize = (int)(cfg.tile_bytes / (16 * s.D));

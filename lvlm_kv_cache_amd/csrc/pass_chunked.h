@@ -8,32 +8,33 @@
 // and the training-free procedure (budgets for all layers at once after
 // prefill, then compression).
 //
-// Schedule. Everything a workgroup does is fixed by the shape alone, so no
-// step waits for a schedule worked out from the elite counts, and the key
-// tiles of a workgroup's first item are loaded into its LDS at launch:
-//   - elite workgroups [0, E): one part of the elite window each (the text
-//     softmax rows of the last text query of a group of KV heads of one
-//     (layer, sample)); the workgroup of part 0 adds the others' parts and
-//     publishes the elite set (size and one bit mask per 64 text tokens);
-//   - items: (layer, sample, chunk of `width` visual keys), every KV head of
-//     it. Round 0 runs on workgroups [E, P) while the elite sets form, rounds
-//     1, 2, ... on all workgroups; every chunk of a (layer, sample) falls in
-//     the same round on a workgroup of its own, so the chunks of a pair run
-//     together. An item streams its keys a head group (up to eight KV heads,
-//     one per wave group) at a time and, per head group, takes the elite
-//     query rows in passes of up to RTP 16-row tiles; the keys stay in LDS
-//     across the passes of one head group. Logits stay in registers. The
-//     exact softmax normaliser of a row needs every chunk of the row's
-//     (layer, sample): each pass publishes the chunk's (max, sum) per row and
-//     merges every chunk's pair in chunk order. The elite text keys enter the
-//     rows' normalisers through chunk 0 and never the column sums. The
-//     chunk's I_v and its moments (sum, M2, M3, count) go out as records;
-//   - consumer units (layer, sample, KV head, K or V), a contiguous range per
-//     workgroup: each combines the chunk moments of every layer of its sample
-//     into s_t and s_k, computes the budgets, selects its layer's top-r_hat
-//     from the published I_v and copies its rows (the kept visual rows, then
-//     the text rows) into the compacted cache. Without compaction a unit is a
-//     (layer, sample).
+// Phases of one launch, every workgroup resident at once (one per CU):
+//   1. Elite sets. Workgroup pt < L * B * npp forms part pt % npp (a group of
+//      KV heads) of the elite window of (layer, sample) pt / npp: the text
+//      softmax rows of the last text query; the workgroup of part 0 adds the
+//      other parts and publishes the elite set (size and one bit mask per 64
+//      text tokens). No key is loaded meanwhile, so these few dependent round
+//      trips see an idle memory system.
+//   2. Schedule. Every workgroup reads every elite record (one round trip)
+//      and works out the same schedule: items (layer, sample, chunk) with a
+//      chunk width per (layer, sample) that keeps its logits in registers
+//      (fewer key tiles per wave for more elite rows), the widest for which
+//      every chunk fits one round of the grid, item i on workgroup i mod P.
+//   3. Items. A chunk's columns are N_v visual keys then the N_tk elite text
+//      keys (the softmax runs over both). Per head group (up to eight KV
+//      heads, a wave group each) and per pass of up to RTP 16-row tiles of
+//      elite query rows, the chunk's keys stream through an LDS ring into
+//      MFMA with the logits in registers; the exact softmax normaliser of a
+//      row needs every chunk of its (layer, sample), so each pass publishes
+//      the chunk's (max, sum) per row and merges every chunk's pair (fixed
+//      groups of eight chunks, merged in chunk order). The chunk's I_v and its
+//      moments (sum, M2, M3, count) go out as records.
+//   4. Consumer units (layer, sample, KV head, K or V), a contiguous range per
+//      workgroup: each combines the chunk moments of every layer of its sample
+//      into s_t and s_k, computes the budgets, selects its layer's top-r_hat
+//      from the published I_v and copies the kept visual rows, then the text
+//      rows, into the compacted cache. Without compaction a unit is a
+//      (layer, sample).
 //
 // Records: every cross-workgroup value is a 64-bit word (32-bit payload | tag
 // << 32) written with an agent-coherent store; a reader that sees the
@@ -48,29 +49,24 @@
 // then a barrier over the grid). The last workgroup to finish writes the
 // call's status, resets the counters and advances the epoch.
 //
-// Progress: all workgroups are resident at once (one per CU). Items wait only
-// for items of their own round (which every workgroup reaches, rounds being
-// taken in order) and for elite sets (published by elite workgroups before
-// any item of theirs); consumer units wait only for item records and for the
-// budgets of earlier samples, which the first unit of each sample publishes
-// before its own top-k. Every wait is also bounded: on expiry the kernel
-// flags AIRCACHE_DEV_TIMEOUT and every other wait of the launch gives up.
-//
-// LDS-DMA and polling: a wave's vector-memory operations complete in issue
-// order, so a poll issued behind a wave's key-tile loads would wait for them.
-// Waves 0 and 1 (the poll waves) therefore issue no tile loads: waves 2 and 3
-// load their ring slots besides their own, and every poll of a record is made
-// by wave 0 or 1.
+// Progress: elite parts wait for nothing; merges wait for parts; the schedule
+// waits for merges; an item waits for the items of its own (layer, sample),
+// which are consecutive in item order and at most P, so by induction on the
+// lowest unfinished item every wait ends; consumer units wait only for item
+// records and for the budgets of earlier samples, which the first unit of
+// each sample publishes before its own top-k. Every wait is also bounded: on
+// expiry the kernel flags AIRCACHE_DEV_TIMEOUT and every other wait gives up.
 #pragma once
 
 constexpr int kPassThreads = 512;
 constexpr int kPassWaves = kPassThreads / 64;
-constexpr int kPollWaves = 2;              // waves 0 and 1: polls, no LDS-DMA
-constexpr int kPollThreads = kPollWaves * 64;
 constexpr unsigned kSpinLimit = 1u << 20;  // polls of one wait before it gives up
 constexpr int kPassTableSlots = 256;       // layer pointers of one launch
 constexpr int kPassMaxPass = 1024;         // passes of one item at most (tag space)
 constexpr int kRingBytes = 131072;         // key tiles in LDS per workgroup
+constexpr int kKtwMax = 12;                // key tiles per wave of one chunk at most
+constexpr int kMaskWords = 2048;           // elite mask words (32 tokens each) preloaded in LDS at most
+constexpr int kTargetCus = 256;            // workgroups the chunk widths are sized for at least
 constexpr unsigned kTagEpochMask = (1u << 21) - 1u;  // epoch bits in the row normaliser tags
 
 // Tag of the row normaliser records of pass p in the call with this epoch.
@@ -78,11 +74,49 @@ __device__ __forceinline__ unsigned xrec_tag(unsigned epoch, int p) {
   return ((epoch & kTagEpochMask) + 1u) * (unsigned)kPassMaxPass + (unsigned)p;
 }
 
-// Key tiles per wave in the ring (a wave's share of one head group of an
-// item) and row tiles per pass (register budget of the logits and the query
-// fragments), per element size and head dimension.
-__host__ __device__ constexpr int pass_kt(int D, int esize) { return kRingBytes / (kPassWaves * 16 * D * esize); }
+// Per element size and head dimension: ring slots per wave (one 16-key tile
+// each), row tiles per pass at most, and logit tiles a wave keeps in
+// registers (key tiles x row tiles, four registers each; fewer where the
+// query fragments take more registers); key tiles per wave for rtp row tiles.
+__host__ __device__ constexpr int pass_ring(int D, int esize) { return kRingBytes / (kPassWaves * 16 * D * esize); }
 __host__ __device__ constexpr int pass_rtp(int D, int esize) { return (esize == 2 && D == 128) ? 6 : 4; }
+__host__ __device__ constexpr int pass_slots(int D, int esize) { return (esize == 4 && D == 128) ? 16 : 24; }
+__host__ __device__ constexpr int pass_ktmax(int rtp, int D, int esize) {
+  return pass_slots(D, esize) / rtp < kKtwMax ? pass_slots(D, esize) / rtp : kKtwMax;
+}
+
+// Chunking of one (layer, sample) from its elite count and the launch's cap
+// kcap on key tiles per wave. Columns are the N_v visual keys then the N_tk
+// elite text keys; chunk c covers columns [c * width, (c + 1) * width).
+struct ItemPlan {
+  int rtg;    // 16-row tiles of elite query rows per KV head (G * N_tk rows), at least 1
+  int nrg;    // row passes per head group
+  int ktw;    // key tiles per wave
+  int width;  // columns per chunk
+  int nch;    // chunks
+};
+__host__ __device__ inline ItemPlan item_plan(int ntk, int G, int Nv, int wph, int kcap, int D, int esize) {
+  ItemPlan p;
+  const int rtpm = pass_rtp(D, esize);
+  const int rows = G * ntk;
+  p.rtg = rows > 0 ? (rows + 15) / 16 : 1;
+  p.nrg = (p.rtg + rtpm - 1) / rtpm;
+  const int rtp0 = p.rtg < rtpm ? p.rtg : rtpm;
+  const int km = pass_ktmax(rtp0, D, esize);
+  int k = kcap < km ? kcap : km;
+  p.ktw = k < 1 ? 1 : k;
+  p.width = wph * 16 * p.ktw;
+  p.nch = (Nv + ntk + p.width - 1) / p.width;
+  return p;
+}
+
+// Smallest key-tile cap a launch may choose (with at most kTargetCus
+// workgroups a smaller one cannot fit every chunk in one round); the host
+// sizes the records for it.
+__host__ __device__ inline int pass_kcap_min(int L, int B, int Nv, int wph) {
+  const long long k = (long long)L * B * Nv / ((long long)wph * 16 * kTargetCus);
+  return k < 1 ? 1 : (k > kKtwMax ? kKtwMax : (int)k);
+}
 
 // One poll of a bounded wait. True when the wait must end: this one ran out
 // (the timeout bit is set) or another one in the launch already did.
@@ -93,6 +127,15 @@ __device__ __forceinline__ bool spin_expired(unsigned &spins, int *flags) {
   }
   if ((spins & 255u) == 0u && (load_coherent(flags) & AIRCACHE_DEV_TIMEOUT)) return true;
   return false;
+}
+
+// Pause between two polls of a wait: about 0.05 us, growing to about 0.2 us
+// after the first polls. A poll re-reads only the records still missing
+// (tens of bytes per thread), far below what would slow the streams that
+// run meanwhile; a longer pause would only delay the waiter.
+__device__ __forceinline__ void poll_pause(unsigned spins) {
+  __builtin_amdgcn_s_sleep(2);
+  if (spins > 4u) __builtin_amdgcn_s_sleep(6);
 }
 
 // The thread index, opaque to the optimiser: values derived from it are
@@ -149,6 +192,7 @@ __device__ __forceinline__ void block_sum_d2(double &a, double &b, double *red) 
   b = tb;
 }
 
+
 // Layer pointers of one launch, L entries each: text queries at [0, L), keys
 // at [L, 2L) and, when the launch also compacts, values at [2L, 3L),
 // compacted keys at [3L, 4L) and compacted values at [4L, 5L).
@@ -156,7 +200,8 @@ struct PassTables {
   const void *p[kPassTableSlots];
 };
 
-// Workspace of the chunked path and the launch's schedule.
+// Workspace of the chunked path and the launch's fixed facts. Pairs are
+// (layer, sample), plb = l * B + b in the records.
 struct PassWs {
   unsigned *epoch;   // [1] calls so far (the last call's epoch)
   unsigned *exitc;   // [1] workgroups finished in this call
@@ -165,22 +210,21 @@ struct PassWs {
   u32x4_t *recs;     // the records (parts .. brec), zeroed by those calls
   size_t rec_words;  // 16-byte words of the records
   uint64_t *parts;   // [L*B][npp][N_t] elite-window parts 1.. (pbar sums | epoch << 32)
-  uint64_t *erec;    // [L*B][erec_stride] elite size, then mask halves, each | epoch << 32
-  uint64_t *xrec;    // [L*B][2][nch][hgs][rows][2] row (max, sum) | tag << 32
-  uint64_t *mom;     // [L*B][nch][8] halves of chunk sum, M2, M3, count | epoch << 32
+  uint64_t *ecnt;    // [L*B] elite set size | epoch << 32
+  uint64_t *emask;   // [L*B][nmw] elite set mask, 32-bit halves | epoch << 32
+  uint64_t *xrec;    // [L*B][2][mnch][hgs][rows][2] row (max, sum) | tag << 32
+  uint64_t *mom;     // [L*B][mnch][8] halves of chunk sum, M2, M3, count | epoch << 32
   uint64_t *ivrec;   // [L*B][N_v] I_v | epoch << 32
   uint64_t *brec;    // [L*B] budget | epoch << 32
-  int npp;           // elite-window parts per (layer, sample): a divisor of H_kv
-  int erec_stride;   // 1 + 2 * ceil(N_t / 64)
+  int npp;           // elite-window parts per pair: a divisor of H_kv
+  int EW;            // workgroups [0, EW) form the elite-window parts
+  int nmw;           // mask halves per pair, 2 * ceil(N_t / 64)
   int hgs;           // KV heads per head group (1, 2, 4 or 8; divides H_kv)
   int nhg;           // head groups, H_kv / hgs
   int wph;           // waves per KV head, kPassWaves / hgs
-  int width;         // visual keys per chunk, wph * 16 * KT
-  int nch;           // chunks per (layer, sample)
-  int rows;          // rows per record slot and head, RTP * 16
-  int E;             // elite workgroups
-  int ppr0;          // (layer, sample) pairs in round 0
-  int ppr;           // pairs per later round
+  int rows;          // rows per record slot and head, RTPM * 16
+  int mnch;          // chunks of one pair at most (record stride)
+  int kcap_lo;       // smallest key-tile cap the schedule may choose
   int units;         // consumer units
   int gather;        // 1: the launch also compacts
   int esize;         // bytes per element
@@ -189,32 +233,37 @@ struct PassWs {
 
 // Dynamic LDS of aircache_pass_kernel (byte offsets, 16-byte aligned). ring:
 // the key tiles (kRingBytes), reused by the consumer units (top-k histogram
-// and candidates, kept indices, statistics). misc: the elite list and the row
-// arrays of the items. The elite parts' text logits take ring and misc (an
-// elite workgroup stages no keys before its parts are done).
+// and candidates, kept indices, statistics). misc: the schedule (item starts
+// per pair) and the item arrays. The elite parts' text logits take ring and
+// misc (no schedule exists yet, no key is staged).
 struct PassLds {
-  int ring, misc;                             // regions
-  int el, scr, colsum, red, mloc, zloc, wts, tmax, tsum;  // item arrays inside misc
-  int z_bytes;                                // bytes of misc the elite parts may use
-  int kidx, hist, sts;                        // consumer arrays inside ring
+  int ring, misc;                                     // regions
+  int start, masks, el, colsum, red, mloc, zloc, wts;  // inside misc
+  int nmask;                                          // mask words preloaded (0: none)
+  int z_bytes;                                        // bytes the elite parts may use
+  int kidx, hist, sts;                                // consumer arrays inside ring
   int total;
 };
 
-__host__ __device__ inline PassLds pass_lds_layout(int D, int esize, int hgs, int width, int G, int Nt, int Nv,
-                                                   int L) {
+__host__ __device__ inline PassLds pass_lds_layout(int D, int esize, int hgs, int LB, int Nt, int Nv) {
   PassLds f;
+  const int nmw = 2 * pass_words64(Nt);
+  f.nmask = LB * nmw <= kMaskWords ? LB * nmw : 0;
   const int rows = pass_rtp(D, esize) * 16;
+  const int wmax = (kPassWaves / hgs) * 16 * kKtwMax;  // columns of a chunk at most
   int o = 0;
   f.ring = o;
   o += kRingBytes;
   f.misc = o;
   int m = 0;
+  f.start = o + m;
+  m += pass_align16((LB + 1) * 4);
+  f.masks = o + m;
+  m += pass_align16(f.nmask * 4);
   f.el = o + m;
   m += pass_align16(Nt * 4);
-  f.scr = o + m;
-  m += pass_align16((2 + 2 * pass_words64(Nt)) * 4);
   f.colsum = o + m;
-  m += pass_align16(hgs * width * 4);
+  m += pass_align16(hgs * wmax * 4);
   f.red = o + m;
   m += pass_align16(kPassWaves * rows * 4);
   f.mloc = o + m;
@@ -223,21 +272,23 @@ __host__ __device__ inline PassLds pass_lds_layout(int D, int esize, int hgs, in
   m += pass_align16(hgs * rows * 4);
   f.wts = o + m;
   m += pass_align16(hgs * rows * 4);
-  f.tmax = o + m;
-  m += pass_align16(hgs * rows * 4);
-  f.tsum = o + m;
-  m += pass_align16(hgs * rows * 4);
   o += pass_align16(m);
   f.total = o;
-  f.z_bytes = o - f.ring;  // the elite parts' text logits: ring and misc
+  f.z_bytes = o - f.ring;
   // consumer arrays in the ring
   int r = 0;
   f.hist = r;
   r += pass_align16((2048 + 2 * 256 + 4) * 4);  // kTopkLdsWords
   f.kidx = r;
   r += pass_align16(Nv * 4);
-  f.sts = r;  // st, sk, bx: L + 16 doubles each; budgets: L + 16 ints
+  f.sts = r;  // st, sk, bx: L + 16 doubles each; chunk moments; budgets
   return f;
+}
+
+// Bytes of the consumer arrays in the ring from sts on: st, sk, bx, the
+// chunk moments [L][mnch][4] doubles and the budgets (L + 16 ints).
+__host__ __device__ inline long long pass_sts_bytes(int L, int mnch) {
+  return (long long)(L + 16) * 8 * 3 + (long long)L * mnch * 32 + (long long)(L + 16) * 4;
 }
 
 // ---------------------------------------------------------------------------
@@ -302,6 +353,7 @@ __device__ __forceinline__ void elite_logits(const Shape &sh, const typename Tag
   }
 }
 
+
 // One part of the elite window of (layer, sample) lb: KV heads
 // [pi * H_kv / npp, (pi + 1) * H_kv / npp). For every KV head of the part and
 // each of its G query heads, the softmax row of the last text query over the
@@ -310,9 +362,10 @@ __device__ __forceinline__ void elite_logits(const Shape &sh, const typename Tag
 // over their query heads in ascending order. Parts 1.. are published as
 // epoch-tagged words; the workgroup of part 0 adds them in ascending part
 // order, keeps { j : pbar_j >= alpha max pbar } (or the last `window` text
-// tokens for the window variants) and publishes it: erec[lb] = [size, then
-// each mask word as two 32-bit halves]; also the plan's elite list and count,
-// and the overflow bit when the size exceeds the elite cap. N_t <= 1024.
+// tokens for the window variants) and publishes it: its size (ecnt[lb]) and
+// its bit mask as 32-bit halves (emask[lb], tokens 32 h .. 32 h + 31 in half
+// h); also the plan's elite list and count, and the overflow bit when the
+// size exceeds the elite cap. N_t <= 1024.
 template <typename Tag, int D>
 __device__ __forceinline__ void elite_part(const Shape &sh, const PassTables &tab, const PlanPtrs &plan,
                                            const PassWs &pw, int lb, int pi, unsigned epoch, float *z,
@@ -398,7 +451,7 @@ __device__ __forceinline__ void elite_part(const Shape &sh, const PassTables &ta
         for (int p = 0; p < PM; ++p)
           ok = ok && (tid + e * NT >= Nt || p + 1 >= npp || (unsigned)(w[e][p] >> 32) == epoch);
       if (ok || spin_expired(spins, pw.flags)) break;
-      __builtin_amdgcn_s_sleep(2);
+      poll_pause(spins);
     }
 #pragma unroll
     for (int e = 0; e < EP; ++e)
@@ -428,7 +481,7 @@ __device__ __forceinline__ void elite_part(const Shape &sh, const PassTables &ta
     for (int e = 0; e < EP; ++e) wtot[e * NW + wave] = __popcll(mk[e]);
   __syncthreads();
   const int ntw = pass_words64(Nt);
-  uint64_t *rec = pw.erec + (size_t)lb * pw.erec_stride;
+  uint64_t *mrec = pw.emask + (size_t)lb * pw.nmw;
   const uint64_t tag = (uint64_t)epoch << 32;
   int total = 0;
   for (int u = 0; u < EP * NW; ++u) total += wtot[u];
@@ -441,11 +494,11 @@ __device__ __forceinline__ void elite_part(const Shape &sh, const PassTables &ta
     if ((mk[e] >> lane) & 1ull) plan.elite[(size_t)lb * Nt + before + __popcll(mk[e] & lt)] = word * 64 + lane;
     if (word < ntw && lane < 2) {
       const unsigned half = lane == 0 ? (unsigned)mk[e] : (unsigned)(mk[e] >> 32);
-      store_coherent(&rec[1 + 2 * word + lane], tag | (uint64_t)half);
+      store_coherent(&mrec[2 * word + lane], tag | (uint64_t)half);
     }
   }
   if (tid == 0) {
-    store_coherent(&rec[0], tag | (uint64_t)(unsigned)total);
+    store_coherent(&pw.ecnt[lb], tag | (uint64_t)(unsigned)total);
     plan.n_elite[lb] = total;
     if (total > sh.cap) __hip_atomic_fetch_or(pw.flags, AIRCACHE_DEV_ELITE_OVERFLOW, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
@@ -453,141 +506,216 @@ __device__ __forceinline__ void elite_part(const Shape &sh, const PassTables &ta
   __syncthreads();  // wtot and red are free again
 }
 
-// The elite list of pair plb, ascending, into el (LDS, at most the elite cap
-// entries) from its merge's record; wave 0 (a poll wave) polls the size and
-// mask words into scr. Returns the clamped count (block-wide).
-__device__ __forceinline__ int pass_elite_list(const Shape &sh, const PassWs &pw, int plb, unsigned epoch, int *el,
-                                               unsigned *scr) {
+
+// ---------------------------------------------------------------------------
+// Schedule and items: cross-modal scores of one chunk ("Elite Observation
+// Window", the A_vtk and I_v equations).
+// ---------------------------------------------------------------------------
+
+// Integer sum over a wave (exact in any order).
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// The launch's schedule, computed alike by every workgroup from the elite
+// set sizes of all pairs: the key-tile cap kcap (the smallest in
+// [kcap_lo, kKtwMax] for which every chunk of every pair has a workgroup of
+// its own, else kKtwMax) and start[q] = the first item of pair q (q = b L + l,
+// sample-major: a sample's layers finish first), start[L B] = the items. With
+// preload, the elite masks of every pair go to masks (LDS, nmw words per
+// pair, plb-major) in the same round trip. Returns kcap (block-wide).
+template <int D, int ESIZE>
+__device__ __forceinline__ int pass_schedule(const Shape &sh, const PassWs &pw, unsigned epoch, int *start,
+                                             unsigned *masks, bool preload) {
+  __shared__ int ktot[kKtwMax + 1];
+  __shared__ int ksel;
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
-  const int ntw = pass_words64(sh.Nt), nword = 1 + 2 * ntw;  // <= 33
-  if (wave == 0 && lane < nword) {
-    const auto rr = coherent_rsrc(pw.erec + (size_t)plb * pw.erec_stride,
-                                  (unsigned)(pw.erec_stride * sizeof(uint64_t)));
-    const int off = lane * (int)sizeof(uint64_t);
-    uint64_t v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, 16));
-    unsigned spins = 0;
-    while ((unsigned)(v >> 32) != epoch) {
-      if (spin_expired(spins, pw.flags)) break;
-      __builtin_amdgcn_s_sleep(1);
-      v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rr, off, 0, 16));
+  const int L = sh.L, LB = sh.L * sh.B, P = gridDim.x;
+  const int klo = pw.kcap_lo, nk = kKtwMax - klo + 1;
+  if (tid <= kKtwMax) ktot[tid] = 0;
+  // counts (thread q < LB) and, with preload, mask words: every load issued
+  // before any is checked; short pauses (nothing streams yet)
+  {
+    const auto rc = coherent_rsrc(pw.ecnt, (unsigned)(LB * sizeof(uint64_t)));
+    const int nmw = pw.nmw, nmask = preload ? LB * nmw : 0;
+    const auto rm = coherent_rsrc(pw.emask, (unsigned)((size_t)nmask * sizeof(uint64_t)));
+    for (int j0 = 0; j0 < LB || j0 < nmask; j0 += kPassThreads) {
+      const int j = j0 + tid;
+      int q = j, plb = 0;
+      if (j < LB) {
+        const int b = q / L, l = q - b * L;
+        plb = l * sh.B + b;
+      }
+      uint64_t wc = 0, wm = 0;
+      auto load = [&]() {
+        if (j < LB) wc = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rc, plb * 8, 0, 16));
+        if (j < nmask) wm = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rm, j * 8, 0, 16));
+      };
+      load();
+      unsigned spins = 0;
+      while ((j < LB && (unsigned)(wc >> 32) != epoch) || (j < nmask && (unsigned)(wm >> 32) != epoch)) {
+        if (spin_expired(spins, pw.flags)) break;
+        __builtin_amdgcn_s_sleep(2);
+        load();
+      }
+      if (j < LB) {
+        int ntk = (int)(unsigned)wc;
+        start[q + 1] = ntk < 0 ? 0 : (ntk > sh.cap ? sh.cap : ntk);
+      }
+      if (j < nmask) {
+        // tokens 32 h .. 32 h + 31 of the pair in half h; bits past N_t cleared
+        const int h = j - (j / nmw) * nmw, valid = sh.Nt - 32 * h;
+        const unsigned keep = valid >= 32 ? 0xffffffffu : (valid <= 0 ? 0u : ((1u << valid) - 1u));
+        masks[j] = (unsigned)wm & keep;
+      }
     }
-    // the size at scr[0]; mask word i as the halves scr[2 + 2i], scr[3 + 2i]
-    scr[lane == 0 ? 0 : lane + 1] = (unsigned)v;
   }
   __syncthreads();
-  // the list holds the mask's tokens below N_t; the count is the record's,
-  // clamped to the elite cap and to the tokens the list holds (the two agree
-  // unless a wait gave up, and then no index may leave its range)
-  const unsigned long long *mw = reinterpret_cast<const unsigned long long *>(scr + 2);
-  const int tail = sh.Nt - (ntw - 1) * 64;  // tokens in the last mask word, 1..64
-  const unsigned long long last = tail >= 64 ? ~0ull : ((1ull << tail) - 1ull);
-  int held = 0;
-  for (int u = 0; u < ntw; ++u) held += __popcll(mw[u] & (u == ntw - 1 ? last : ~0ull));
-  int ntk = (int)scr[0];
-  ntk = ntk < sh.cap ? ntk : sh.cap;
-  ntk = ntk < held ? ntk : held;
-  ntk = ntk > 0 ? ntk : 0;
-  for (int w = wave; w < ntw; w += kPassWaves) {
-    int base = 0;
-    for (int u = 0; u < w; ++u) base += __popcll(mw[u]);
-    const unsigned long long mk = mw[w] & (w == ntw - 1 ? last : ~0ull);
-    const int pos = base + __popcll(mk & ((1ull << lane) - 1ull));
-    if (((mk >> lane) & 1ull) && pos < ntk) el[pos] = w * 64 + lane;
+  // chunks of every pair for every candidate cap, (pair, cap) combinations
+  // spread over the threads; integer sums, exact in any order
+  for (int x = tid; x < LB * nk; x += kPassThreads) {
+    const int q = x / nk, k = klo + (x - q * nk);
+    atomicAdd(&ktot[k], item_plan(start[q + 1], sh.G, sh.Nv, pw.wph, k, D, ESIZE).nch);
   }
   __syncthreads();
-  return uniform(ntk);
-}
-
-// ---------------------------------------------------------------------------
-// Items: cross-modal scores of one chunk ("Elite Observation Window", the
-// A_vtk and I_v equations).
-// ---------------------------------------------------------------------------
-
-// LDS-DMA of one wave's share of a head group's keys of an item: KT tiles of
-// 16 visual keys of KV head g from column c0 + sub * KT * 16 on, into the
-// wave's ring slots (staged as LdsTile reads them); keys past N_v read the
-// last visual key, masked later.
-template <typename Tag, int D>
-__device__ __forceinline__ void pass_issue(const Shape &sh, const void *k_layer, int b, int g, int c0, int sub,
-                                           unsigned char *slots) {
-  using E = typename Tag::store_t;
-  constexpr int KT = pass_kt(D, Tag::kBytes);
-  constexpr int kTile = 16 * D * Tag::kBytes;
-  constexpr int kDma = kTile / 1024;
-  const int lane = opaque_tid() & 63, n = lane & 15, grp = lane >> 4;
-  const E *kb = static_cast<const E *>(k_layer) + (size_t)(b * sh.Hkv + g) * sh.S * D;
-#pragma unroll
-  for (int s = 0; s < KT; ++s) {
-    const int v = c0 + (sub * KT + s) * 16 + n;
-    const int row = v < sh.Nv ? v : sh.Nv - 1;
-    const unsigned char *src = reinterpret_cast<const unsigned char *>(kb + (size_t)row * D);
-#pragma unroll
-    for (int j = 0; j < kDma; ++j) load_lds16(src + 16 * grp + 64 * j, slots + s * kTile + 1024 * j);
+  if (tid == 0) {
+    int sel = kKtwMax;
+    for (int k = klo; k <= kKtwMax; ++k)
+      if (ktot[k] <= P) {
+        sel = k;
+        break;
+      }
+    ksel = sel;
   }
+  __syncthreads();
+  const int kcap = uniform(ksel);
+  for (int q = tid; q < LB; q += kPassThreads)
+    start[q + 1] = item_plan(start[q + 1], sh.G, sh.Nv, pw.wph, kcap, D, ESIZE).nch;
+  __syncthreads();
+  if (wave == 0) {
+    int carry = 0;
+    for (int q0 = 0; q0 < LB; q0 += 64) {
+      const int q = q0 + lane;
+      const int v = q < LB ? start[q + 1] : 0;
+      const int incl = wave_incl_scan(v) + carry;
+      if (q < LB) start[q + 1] = incl;
+      carry = __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (lane == 0) start[0] = 0;
+  }
+  __syncthreads();
+  return kcap;
 }
 
-// The keys of head group hg of the item (pair q, chunk c) into the ring, by
-// the loader waves: wave w >= kPollWaves loads its own slots and, for
-// w < 2 * kPollWaves, those of poll wave w - kPollWaves.
-template <typename Tag, int D>
-__device__ __forceinline__ void pass_stage(const Shape &sh, const PassWs &pw, const PassTables &tab, int q, int c,
-                                           int hg, unsigned char *ring) {
-  constexpr int KT = pass_kt(D, Tag::kBytes);
-  constexpr int kTile = 16 * D * Tag::kBytes;
-  const int wave = uniform(opaque_tid() >> 6);
-  if (wave < kPollWaves) return;
-  const int b = q / sh.L, l = q - b * sh.L;
-  const void *kl = tab.p[sh.L + l];
-  const int c0 = c * pw.width;
-  auto one = [&](int ow) {
-    const int gl = ow / pw.wph, sub = ow - gl * pw.wph;
-    pass_issue<Tag, D>(sh, kl, b, hg * pw.hgs + gl, c0, sub, ring + (size_t)ow * KT * kTile);
-  };
-  one(wave);
-  if (wave < 2 * kPollWaves) one(wave - kPollWaves);
+// The pair of item i: the last q with start[q] <= i (wave-uniform).
+__device__ __forceinline__ int pass_pair_of(const int *start, int LB, int i) {
+  int lo = 0, hi = LB - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (start[mid] <= i) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// The elite list of pair plb into el (LDS, ascending, at most the elite cap
+// entries), from its mask (preloaded in LDS, else read from its records);
+// returns its size (block-wide).
+__device__ __forceinline__ int pass_elite_list(const Shape &sh, const PassWs &pw, int plb, unsigned epoch,
+                                               const unsigned *masks, bool preloaded, int *el) {
+  __shared__ unsigned mw[32];
+  __shared__ int pre[33];
+  const int tid = opaque_tid();
+  const int Nt = sh.Nt, nmw = pw.nmw;
+  if (tid < nmw) {
+    unsigned v;
+    if (preloaded) {
+      v = masks[(size_t)plb * nmw + tid];
+    } else {
+      const auto rm = coherent_rsrc(pw.emask + (size_t)plb * nmw, (unsigned)(nmw * sizeof(uint64_t)));
+      uint64_t w = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rm, tid * 8, 0, 16));
+      unsigned spins = 0;
+      while ((unsigned)(w >> 32) != epoch) {
+        if (spin_expired(spins, pw.flags)) break;
+        poll_pause(spins);
+        w = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rm, tid * 8, 0, 16));
+      }
+      // tokens 32 tid .. 32 tid + 31; bits past N_t cleared
+      const int valid = Nt - 32 * tid;
+      const unsigned keep = valid >= 32 ? 0xffffffffu : (valid <= 0 ? 0u : ((1u << valid) - 1u));
+      v = (unsigned)w & keep;
+    }
+    mw[tid] = v;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int s = 0;
+    for (int h = 0; h < nmw; ++h) {
+      pre[h] = s;
+      s += __popc(mw[h]);
+    }
+    pre[nmw] = s;
+  }
+  __syncthreads();
+  const int cap = sh.cap;
+  for (int j = tid; j < Nt; j += kPassThreads) {
+    const int h = j >> 5, bit = j & 31;
+    const unsigned m = mw[h];
+    if ((m >> bit) & 1u) {
+      const int pos = pre[h] + __popc(m & ((1u << bit) - 1u));
+      if (pos < cap) el[pos] = j;
+    }
+  }
+  const int total = pre[nmw];
+  __syncthreads();
+  return uniform(total < cap ? total : cap);
 }
 
 struct PassItem {
-  int l, b, plb, c, c0, ncol, ntk, rtg, nrg;
-  const void *q, *k;
+  int l, b, plb, q, c, c0, ncolv, ntk, rtg, nrg, ktw, width, nchq;
+  const void *q_l, *k_l;
 };
 
 // One pass of an item: RTP row tiles (rows rg * RTPM * 16 ..) of the elite
-// query rows of every KV head of head group hg, against the chunk's keys in
-// the ring. Leaves the pass's column sums of the softmax rows added to colacc
-// (a wave's key tiles; one value per column, in every lane of its row). When
-// the pass is the last over these tiles, stage_next() loads the next ones as
-// soon as every wave has read them.
-template <typename Tag, int D, int RTP, typename NextFn>
+// query rows of every KV head of head group hg, against the chunk's keys:
+// columns c0 .. c0 + width - 1 of N_v visual keys followed by the N_tk elite
+// text keys. Wave (head gl, sub) takes key tiles sub * ktw .. of its head's
+// chunk; they stream through its ring slots (R tiles in flight, refilled as
+// they are read), the logits stay in registers. The pass's column sums of the
+// softmax rows go to colsum (set when first, else added).
+template <typename Tag, int D, int RTP>
 __device__ __forceinline__ void pass_rows(const Shape &sh, const PassWs &pw, const PassItem &it, int hg, int rg,
-                                          int pidx, bool last_of_tiles, unsigned char *lds, const PassLds &lo,
-                                          unsigned epoch, float (&colacc)[pass_kt(D, Tag::kBytes)],
-                                          NextFn &&stage_next) {
+                                          int pidx, bool first, unsigned char *lds, const PassLds &lo,
+                                          unsigned epoch) {
   using E = typename Tag::store_t;
-  constexpr int NW = kPassWaves;
-  constexpr int KT = pass_kt(D, Tag::kBytes);
+  constexpr int NT = kPassThreads;
   constexpr int RTPM = pass_rtp(D, Tag::kBytes);
+  constexpr int R = pass_ring(D, Tag::kBytes);
+  constexpr int KM = pass_ktmax(RTP, D, Tag::kBytes);  // key tiles per wave at most with RTP row tiles
   constexpr int kTile = 16 * D * Tag::kBytes;
+  constexpr int kDma = kTile / 1024;
   constexpr int RW = RTP * 16;  // rows of one head in this pass
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, grp = lane >> 4;
   const int hgs = pw.hgs, wph = pw.wph, ROWS = pw.rows;
   const int gl = wave / wph, sub = wave - gl * wph;
   const int g = hg * hgs + gl;
-  const int ntk = it.ntk, Rg = sh.G * ntk, Nv = sh.Nv;
+  const int ntk = it.ntk, Rg = sh.G * ntk, Nv = sh.Nv, ktw = it.ktw, W = it.width;
   const int rt0 = rg * RTPM;
   const int *el = reinterpret_cast<const int *>(lds + lo.el);
   float *red = reinterpret_cast<float *>(lds + lo.red);
   float *mloc = reinterpret_cast<float *>(lds + lo.mloc);
   float *zloc = reinterpret_cast<float *>(lds + lo.zloc);
   float *wts = reinterpret_cast<float *>(lds + lo.wts);
-  float *tmax = reinterpret_cast<float *>(lds + lo.tmax);
-  float *tsum = reinterpret_cast<float *>(lds + lo.tsum);
-  const unsigned char *slots = lds + lo.ring + (size_t)wave * KT * kTile;
-  const E *qb = static_cast<const E *>(it.q);
-  const E *kb = static_cast<const E *>(it.k) + (size_t)(it.b * sh.Hkv + g) * sh.S * D;
+  float *colsum = reinterpret_cast<float *>(lds + lo.colsum);
+  unsigned char *slots = lds + lo.ring + (size_t)wave * R * kTile;
+  const E *qb = static_cast<const E *>(it.q_l);
+  const E *kb = static_cast<const E *>(it.k_l) + (size_t)(it.b * sh.Hkv + g) * sh.S * D;
 
-  // query fragments: RTP tiles of 16 elite query rows of this wave's head
+  // query fragments first (the waits for them then cover no key tile): RTP
+  // tiles of 16 elite query rows of this wave's head
   Frag<Tag> qf[RTP][D / 32];
 #pragma unroll
   for (int rt = 0; rt < RTP; ++rt) {
@@ -603,119 +731,68 @@ __device__ __forceinline__ void pass_rows(const Shape &sh, const PassWs &pw, con
     }
   }
 
-  // Chunk 0 also carries the elite text keys: per row, their (max, sum of
-  // exp2(logit - max)) into tmax / tsum, from fragments read straight from
-  // global memory (two passes over them, the second recomputing the logits).
-  // They enter the rows' normalisers, never the column sums.
-  const int ntt = it.c == 0 ? (ntk + 15) >> 4 : 0;
-  auto text_logits = [&](int t, f32x4_t (&st)[RTP]) {
-    const int e = t * 16 + n;
-    const E *kr = kb + (size_t)(Nv + el[e < ntk ? e : ntk - 1]) * D;
-    Frag<Tag> kf[D / 32];
+  // column of this lane in key tile s: col0 + 16 s
+  int col0 = it.c0 + sub * ktw * 16 + n;
+  asm volatile("" : "+v"(col0));
+  const int ncols = Nv + ntk;
+  // LDS-DMA of key tile s into slot s % R: visual key col, or elite text key
+  // el[col - N_v]; columns past the keys read the last visual key (masked)
+  auto issue = [&](int s) {
+    const int v = col0 + s * 16;
+    int row;
+    if (v < Nv) row = v;
+    else if (v < ncols) row = Nv + el[v - Nv];
+    else row = Nv - 1;
+    const unsigned char *src = reinterpret_cast<const unsigned char *>(kb + (size_t)row * D);
+    unsigned char *dst = slots + (s % R) * kTile;
 #pragma unroll
-    for (int cc = 0; cc < D / 32; ++cc) kf[cc].load(kr + cc * 32 + grp * 8);
-#pragma unroll
-    for (int rt = 0; rt < RTP; ++rt) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int cc = 0; cc < D / 32; ++cc) mfma_slice(acc, qf[rt][cc], kf[cc]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st[rt][i] = e < ntk ? acc[i] * sh.scale2 : -INFINITY;
-    }
+    for (int j = 0; j < kDma; ++j) load_lds16(src + 16 * grp + 64 * j, dst + 1024 * j);
   };
-  float racc[RTP][4];
-  if (ntt > 0) {
 #pragma unroll
-    for (int rt = 0; rt < RTP; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) racc[rt][i] = -INFINITY;
-    for (int t = sub; t < ntt; t += wph) {
-      f32x4_t st[RTP];
-      text_logits(t, st);
-#pragma unroll
-      for (int rt = 0; rt < RTP; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) racc[rt][i] = fmaxf(racc[rt][i], st[rt][i]);
-    }
-#pragma unroll
-    for (int rt = 0; rt < RTP; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float m = row16_max(racc[rt][i]);
-        if (n == 0) red[wave * RW + rt * 16 + grp * 4 + i] = m;
-      }
-    __syncthreads();
-    if (tid < hgs * RW) {
-      const int gg = tid / RW, rr = tid - gg * RW;
-      float m = red[(gg * wph) * RW + rr];
-      for (int w = 1; w < wph; ++w) m = fmaxf(m, red[(gg * wph + w) * RW + rr]);
-      tmax[gg * RW + rr] = m;
-    }
-    __syncthreads();
-    float Tm[RTP][4];
-#pragma unroll
-    for (int rt = 0; rt < RTP; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        Tm[rt][i] = tmax[gl * RW + rt * 16 + grp * 4 + i];
-        racc[rt][i] = 0.f;
-      }
-    for (int t = sub; t < ntt; t += wph) {
-      f32x4_t st[RTP];
-      text_logits(t, st);
-#pragma unroll
-      for (int rt = 0; rt < RTP; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) racc[rt][i] += st[rt][i] > -INFINITY ? exp2_fast(st[rt][i] - Tm[rt][i]) : 0.f;
-    }
-#pragma unroll
-    for (int rt = 0; rt < RTP; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float z = row16_sum(racc[rt][i]);
-        if (n == 0) red[wave * RW + rt * 16 + grp * 4 + i] = z;
-      }
-    __syncthreads();
-    if (tid < hgs * RW) {
-      const int gg = tid / RW, rr = tid - gg * RW;
-      float z = 0.f;
-      for (int w = 0; w < wph; ++w) z += red[(gg * wph + w) * RW + rr];
-      tsum[gg * RW + rr] = z;
-    }
-    __syncthreads();  // red is written again by the visual row maxima
-  }
+  for (int s = 0; s < R; ++s)
+    if (s < ktw) issue(s);
 
-  // logits of the visual keys, from the ring
-  f32x4_t S[KT][RTP];
-  int vbase = it.c0 + sub * KT * 16 + n;  // this lane's column in tile 0
-  asm volatile("" : "+v"(vbase));
+  f32x4_t S[KM][RTP];
 #pragma unroll
-  for (int s = 0; s < KT; ++s) {
-    f32x4_t acc[RTP];
+  for (int s = 0; s < KM; ++s) {
+    if (s < ktw) {
+      // tiles s + 1 .. min(s + R, ktw) - 1 may stay in flight
+      const int ahead = (s + R < ktw ? s + R : ktw) - 1 - s;
+      wait_tiles<kDma>(ahead);
+      f32x4_t acc[RTP];
 #pragma unroll
-    for (int rt = 0; rt < RTP; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const unsigned char *slot = slots + s * kTile;
+      for (int rt = 0; rt < RTP; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const unsigned char *slot = slots + (s % R) * kTile;
 #pragma unroll
-    for (int cc = 0; cc < D / 32; ++cc) {
-      Frag<Tag> kf;
-      LdsTile<Tag>::read(kf, slot, cc, lane);
+      for (int cc = 0; cc < D / 32; ++cc) {
+        Frag<Tag> kf;
+        LdsTile<Tag>::read(kf, slot, cc, lane);
 #pragma unroll
-      for (int rt = 0; rt < RTP; ++rt) mfma_slice(acc[rt], qf[rt][cc], kf);
+        for (int rt = 0; rt < RTP; ++rt) mfma_slice(acc[rt], qf[rt][cc], kf);
+      }
+      if (s + R < ktw) {
+        wait_lds_reads();  // the slot's reads are done before the DMA overwrites it
+        issue(s + R);
+      }
+      const bool ok = col0 + s * 16 < ncols;
+#pragma unroll
+      for (int rt = 0; rt < RTP; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[s][rt][i] = ok ? acc[rt][i] * sh.scale2 : -INFINITY;
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < RTP; ++rt) S[s][rt] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
-    const bool ok = vbase + s * 16 < Nv;
-#pragma unroll
-    for (int rt = 0; rt < RTP; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[s][rt][i] = ok ? acc[rt][i] * sh.scale2 : -INFINITY;
   }
-  // chunk-local row maxima (visual keys and, in chunk 0, the text keys): keys
-  // of a lane row by DPP, then the head's waves in order
+  // chunk-local row maxima: keys of a lane row by DPP, then the head's waves
+  // in order
+  float racc[RTP][4];
 #pragma unroll
   for (int rt = 0; rt < RTP; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) racc[rt][i] = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < KT; ++s)
+  for (int s = 0; s < KM; ++s)
 #pragma unroll
     for (int rt = 0; rt < RTP; ++rt)
 #pragma unroll
@@ -728,15 +805,11 @@ __device__ __forceinline__ void pass_rows(const Shape &sh, const PassWs &pw, con
       if (n == 0) red[wave * RW + rt * 16 + grp * 4 + i] = m;
     }
   __syncthreads();
-  // every read of this pass's tiles is done (their values entered S before
-  // the barrier): the loader waves may stage the next tiles now
-  if (last_of_tiles) stage_next();
-  if (tid < hgs * RW) {
-    const int gg = tid / RW, rr = tid - gg * RW;
+  for (int qr = tid; qr < hgs * RW; qr += NT) {
+    const int gg = qr / RW, rr = qr - gg * RW;
     float m = red[(gg * wph) * RW + rr];
     for (int w = 1; w < wph; ++w) m = fmaxf(m, red[(gg * wph + w) * RW + rr]);
-    if (ntt > 0) m = fmaxf(m, tmax[gg * RW + rr]);
-    mloc[gg * RW + rr] = m;
+    mloc[qr] = m;
   }
   __syncthreads();
   // exponentials in place and chunk-local row sums
@@ -749,12 +822,13 @@ __device__ __forceinline__ void pass_rows(const Shape &sh, const PassWs &pw, con
       racc[rt][i] = 0.f;
     }
 #pragma unroll
-  for (int s = 0; s < KT; ++s)
+  for (int s = 0; s < KM; ++s)
 #pragma unroll
     for (int rt = 0; rt < RTP; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float ev = exp2_fast(S[s][rt][i] - Mrow[rt][i]);
+        // a row with no key in this chunk has maximum -inf: its weights are 0
+        const float ev = Mrow[rt][i] > -INFINITY ? exp2_fast(S[s][rt][i] - Mrow[rt][i]) : 0.f;
         S[s][rt][i] = ev;
         racc[rt][i] += ev;
       }
@@ -766,72 +840,72 @@ __device__ __forceinline__ void pass_rows(const Shape &sh, const PassWs &pw, con
       if (n == 0) red[wave * RW + rt * 16 + grp * 4 + i] = z;
     }
   __syncthreads();
-  if (tid < hgs * RW) {
-    const int gg = tid / RW, rr = tid - gg * RW;
+  for (int qr = tid; qr < hgs * RW; qr += NT) {
+    const int gg = qr / RW, rr = qr - gg * RW;
     float z = 0.f;
     for (int w = 0; w < wph; ++w) z += red[(gg * wph + w) * RW + rr];
-    if (ntt > 0) {
-      const float tm = tmax[gg * RW + rr];
-      if (tm > -INFINITY) z += tsum[gg * RW + rr] * exp2_fast(tm - mloc[gg * RW + rr]);
-    }
-    zloc[gg * RW + rr] = z;
+    zloc[qr] = z;
   }
   __syncthreads();
-  // the poll waves publish this chunk's (max, sum) per row and merge every
-  // chunk's pair in chunk order into each row's normaliser
-  if (tid < kPollThreads) {
+  // publish this chunk's (max, sum) per row and merge every chunk's pair in
+  // chunk order into each row's normaliser
+  {
     const unsigned tag = xrec_tag(epoch, pidx);
-    const int nch = pw.nch, c = it.c;
-    const size_t sbase = ((size_t)it.plb * 2 + (pidx & 1)) * nch;  // (pair, slot) block, in chunks
+    const int nch = it.nchq, c = it.c, mnch = pw.mnch;
+    const size_t sbase = ((size_t)it.plb * 2 + (pidx & 1)) * mnch;  // (pair, slot) block, in chunks
     uint64_t *blk = pw.xrec + 2 * sbase * hgs * ROWS;
-    const auto rsrc = coherent_rsrc(blk, (unsigned)((size_t)nch * hgs * ROWS * 16));
-    for (int qr = tid; qr < hgs * RW; qr += kPollThreads) {
+    const auto rsrc = coherent_rsrc(blk, (unsigned)((size_t)mnch * hgs * ROWS * 16));
+    for (int qr = tid; qr < hgs * RW; qr += NT) {
       const int gg = qr / RW, rr = qr - gg * RW;
-      const float m_own = mloc[gg * RW + rr], z_own = zloc[gg * RW + rr];
+      const float m_own = mloc[qr], z_own = zloc[qr];
       uint64_t *rec = blk + 2 * (((size_t)c * hgs + gg) * ROWS + rr);
       store_coherent(rec, pack_rec(m_own, tag));
       store_coherent(rec + 1, pack_rec(z_own, tag));
       float M = -INFINITY, Z = 0.f;
       constexpr int kXB = 8;  // chunks' records in flight per row (one 16-byte load each)
-      for (int c0 = 0; c0 < nch; c0 += kXB) {
+      for (int cb = 0; cb < nch; cb += kXB) {
         u32x4_t rw[kXB];
-        auto load_batch = [&]() {
 #pragma unroll
-          for (int j = 0; j < kXB; ++j) {
-            const int cj = c0 + j;
-            const unsigned off = (cj < nch && cj != c) ? (unsigned)((((size_t)cj * hgs + gg) * ROWS + rr) * 16)
-                                                       : 0xfffffff0u;  // past the end: zeros, not used
-            rw[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 16));
-          }
-        };
-        load_batch();
+        for (int j = 0; j < kXB; ++j) {
+          const int cj = cb + j;
+          const unsigned off = (cj < nch && cj != c) ? (unsigned)((((size_t)cj * hgs + gg) * ROWS + rr) * 16)
+                                                     : 0xfffffff0u;  // past the end: zeros, not used
+          rw[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)off, 0, 16));
+        }
         unsigned spins = 0;
         for (;;) {
           bool ok = true;
 #pragma unroll
           for (int j = 0; j < kXB; ++j) {
-            const int cj = c0 + j;
+            const int cj = cb + j;
             ok = ok && (cj >= nch || cj == c || (rw[j][1] == tag && rw[j][3] == tag));
           }
           if (ok || spin_expired(spins, pw.flags)) break;
-          __builtin_amdgcn_s_sleep(1);
-          load_batch();
+          poll_pause(spins);
+#pragma unroll
+          for (int j = 0; j < kXB; ++j) {
+            const int cj = cb + j;
+            if (cj < nch && cj != c && !(rw[j][1] == tag && rw[j][3] == tag))
+              rw[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rsrc, (int)((((size_t)cj * hgs + gg) * ROWS + rr) * 16), 0, 16));
+          }
         }
 #pragma unroll
         for (int j = 0; j < kXB; ++j) {
-          const int cj = c0 + j;
-          if (cj >= nch) break;
-          const float mj = cj == c ? m_own : __uint_as_float(rw[j][0]);
-          const float zj = cj == c ? z_own : __uint_as_float(rw[j][2]);
-          if (mj > -INFINITY) {
-            const float mn = fmaxf(M, mj);
-            Z = Z * exp2_fast(M - mn) + zj * exp2_fast(mj - mn);
-            M = mn;
+          const int cj = cb + j;
+          if (cj < nch) {
+            const float mj = cj == c ? m_own : __uint_as_float(rw[j][0]);
+            const float zj = cj == c ? z_own : __uint_as_float(rw[j][2]);
+            if (mj > -INFINITY) {
+              const float mn = fmaxf(M, mj);
+              Z = Z * exp2_fast(M - mn) + zj * exp2_fast(mj - mn);
+              M = mn;
+            }
           }
         }
       }
       const int row = rt0 * 16 + rr;
-      wts[gg * RW + rr] = (row < Rg && Z > 0.f) ? exp2_fast(m_own - M) / Z : 0.f;
+      wts[qr] = (row < Rg && Z > 0.f && m_own > -INFINITY) ? exp2_fast(m_own - M) / Z : 0.f;
     }
   }
   __syncthreads();
@@ -842,16 +916,20 @@ __device__ __forceinline__ void pass_rows(const Shape &sh, const PassWs &pw, con
   for (int rt = 0; rt < RTP; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) wrow[rt][i] = wts[gl * RW + rt * 16 + grp * 4 + i];
+  float *cs = colsum + gl * W + sub * ktw * 16 + n;
 #pragma unroll
-  for (int s = 0; s < KT; ++s) {
-    float v = 0.f;
+  for (int s = 0; s < KM; ++s) {
+    if (s < ktw) {
+      float v = 0.f;
 #pragma unroll
-    for (int rt = 0; rt < RTP; ++rt)
+      for (int rt = 0; rt < RTP; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v += S[s][rt][i] * wrow[rt][i];
-    colacc[s] += sum_across_rows(v);
+        for (int i = 0; i < 4; ++i) v += S[s][rt][i] * wrow[rt][i];
+      v = sum_across_rows(v);
+      if (grp == 0) cs[s * 16] = first ? v : cs[s * 16] + v;
+    }
   }
-  __syncthreads();  // red, mloc, zloc, wts, tmax, tsum are reused by the next pass
+  __syncthreads();  // red, mloc, zloc, wts are reused by the next pass
 }
 
 // ---------------------------------------------------------------------------
@@ -859,70 +937,108 @@ __device__ __forceinline__ void pass_rows(const Shape &sh, const PassWs &pw, con
 // training-free procedure).
 // ---------------------------------------------------------------------------
 
-// Moments of a run of values, combined pairwise (Chan, Golub and LeVeque's
-// update, extended to the third central moment): count, mean, M2 and M3.
-struct Moments {
-  double n, mean, m2, m3;
-};
-__device__ __forceinline__ Moments combine_moments(const Moments &a, const Moments &b) {
-  if (b.n == 0.0) return a;
-  if (a.n == 0.0) return b;
-  Moments r;
-  const double n = a.n + b.n, inv = 1.0 / n, d = b.mean - a.mean;
-  const double db = d * b.n * inv;  // mean shift
-  r.n = n;
-  r.mean = a.mean + db;
-  r.m2 = a.m2 + b.m2 + d * db * a.n;
-  r.m3 = a.m3 + b.m3 + d * d * db * a.n * (a.n - b.n) * inv + 3.0 * d * (a.n * b.m2 - b.n * a.m2) * inv;
-  return r;
-}
-
-// s_t and s_k of (layer, sample) plb ("Layer-wise KV Cache Budget
-// Allocation", the s_t and s_k equations) from its chunks' moment records, by
-// one wave: lane c holds chunks c, c + 64, ... (combined in that order), then
-// the lanes combine pairwise in a fixed tree (at stride st, lane c, a
-// multiple of 2 st, absorbs lane c + st), so every unit that computes it gets
-// the same bits. The wave's lane 0 returns the values.
-__device__ __forceinline__ void chunk_stats(const Shape &sh, const PassWs &pw, int plb, unsigned epoch, double *st_out,
-                                            double *sk_out) {
-  const int lane = threadIdx.x & 63;
-  const int nch = pw.nch;
-  const auto rm = coherent_rsrc(pw.mom + (size_t)plb * nch * 8, (unsigned)(nch * 64));
-  double sum = 0.0;
-  Moments m{0.0, 0.0, 0.0, 0.0};
-  for (int c = lane; c < nch; c += 64) {
-    uint64_t w[8];
-    unsigned spins = 0;
-    for (;;) {
+// The moment records of every chunk of every layer of sample b into LDS
+// (mb: [L][mnch][4] doubles: sum, M2, M3, count; layer l has the chunks of
+// pair q = b L + l, start[q + 1] - start[q] of them), block-wide: each thread
+// takes record slots tid, tid + 512, ..., up to four at a time with every
+// load in flight before any is checked, and polls until all carry the epoch.
+__device__ __forceinline__ void load_sample_moments(const Shape &sh, const PassWs &pw, int b, unsigned epoch,
+                                                    const int *start, double *mb) {
+  constexpr int U = 4;
+  const int tid = opaque_tid();
+  const int mnch = pw.mnch, nrec = sh.L * mnch;
+  // one resource for every record (a per-lane resource would cost a loop
+  // over the distinct values of the wave); past the end reads zeros
+  const auto rm = coherent_rsrc(pw.mom, (unsigned)((size_t)sh.L * sh.B * mnch * 64));
+  auto used = [&](int i) {
+    if (i >= nrec) return false;
+    const int l = i / mnch, c = i - (i / mnch) * mnch, q = b * sh.L + l;
+    return c < start[q + 1] - start[q];
+  };
+  auto base_of = [&](int i) {
+    const int l = i / mnch, c = i - (i / mnch) * mnch;
+    return (unsigned)(((size_t)(l * sh.B + b) * mnch + c) * 64);
+  };
+  for (int i0 = tid; i0 < nrec; i0 += U * kPassThreads) {
+    uint64_t w[U][8];
+    bool use[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kPassThreads;
+      use[u] = used(i);
+      const unsigned base = use[u] ? base_of(i) : 0xffffff00u;  // past the end: zeros, not used
 #pragma unroll
       for (int f = 0; f < 8; ++f)
-        w[f] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rm, c * 64 + 8 * f, 0, 16));
+        w[u][f] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rm, (int)(base + 8 * f), 0, 16));
+    }
+    unsigned spins = 0;
+    for (;;) {
       bool ok = true;
 #pragma unroll
-      for (int f = 0; f < 8; ++f) ok = ok && (unsigned)(w[f] >> 32) == epoch;
-      if (ok || spin_expired(spins, pw.flags)) break;
-      __builtin_amdgcn_s_sleep(1);
-    }
-    double v[4];
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int f = 0; f < 4; ++f) v[f] = __builtin_bit_cast(double, (w[2 * f] & 0xffffffffu) | (w[2 * f + 1] << 32));
-    sum = sum + v[0];
-    m = combine_moments(m, Moments{v[3], v[3] > 0.0 ? v[0] / v[3] : 0.0, v[1], v[2]});
-  }
-  const int nl = nch < 64 ? nch : 64;
-  for (int st = 1; st < nl; st <<= 1) {
-    const int src = lane + st;
-    const double osum = __shfl(sum, src), on = __shfl(m.n, src), omean = __shfl(m.mean, src);
-    const double om2 = __shfl(m.m2, src), om3 = __shfl(m.m3, src);
-    if ((lane & (2 * st - 1)) == 0 && src < nl) {
-      m = combine_moments(m, Moments{on, omean, om2, om3});
-      sum = sum + osum;
+        for (int f = 0; f < 8; ++f) ok = ok && (!use[u] || (unsigned)(w[u][f] >> 32) == epoch);
+      if (ok || spin_expired(spins, pw.flags)) break;
+      poll_pause(spins);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        bool rec_ok = true;
+#pragma unroll
+        for (int f = 0; f < 8; ++f) rec_ok = rec_ok && (unsigned)(w[u][f] >> 32) == epoch;
+        if (use[u] && !rec_ok) {
+          const unsigned base = base_of(i0 + u * kPassThreads);
+#pragma unroll
+          for (int f = 0; f < 8; ++f)
+            w[u][f] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rm, (int)(base + 8 * f), 0, 16));
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kPassThreads;
+      if (use[u])
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          mb[(size_t)i * 4 + f] = __builtin_bit_cast(double, (w[u][2 * f] & 0xffffffffu) | (w[u][2 * f + 1] << 32));
     }
   }
+}
+
+// s_t and s_k of layer l ("Layer-wise KV Cache Budget Allocation", the s_t
+// and s_k equations) from its chunks' moments in LDS (m4: [nch][4] = sum,
+// M2, M3, count), by the 16 lanes of one DPP row: s_t = the sum of the chunk
+// sums; the central moments about the layer mean mu follow exactly from the
+// chunks' (with d_c = mean_c - mu): M2 = sum_c M2_c + n_c d_c^2 and
+// M3 = sum_c M3_c + 3 d_c M2_c + n_c d_c^3. Lane i of the row takes chunks
+// i, i + 16, ... in that order, then fixed-order row sums, so every unit that
+// computes it gets the same bits. Every lane of the row returns the values.
+__device__ __forceinline__ void chunk_stats(const Shape &sh, int nch, const double *m4, double *st_out,
+                                            double *sk_out) {
+  const int i16 = threadIdx.x & 15;
+  double sum = 0.0, cnt = 0.0;
+  for (int c = i16; c < nch; c += 16) {
+    sum += m4[(size_t)c * 4];
+    cnt += m4[(size_t)c * 4 + 3];
+  }
+  sum = row16_sum_d(sum);
+  cnt = row16_sum_d(cnt);  // whole numbers: exact
+  const double mu = cnt > 0.0 ? sum / cnt : 0.0;
+  double m2 = 0.0, m3 = 0.0;
+  for (int c = i16; c < nch; c += 16) {
+    const double *v = m4 + (size_t)c * 4;
+    const double n = v[3];
+    if (n > 0.0) {
+      const double d = v[0] / n - mu;
+      m2 += v[1] + n * d * d;
+      m3 += v[2] + 3.0 * d * v[1] + n * d * d * d;
+    }
+  }
+  m2 = row16_sum_d(m2);
+  m3 = row16_sum_d(m3);
   const int Nv = sh.Nv;
-  const double sigma = sqrt(m.m2 / (double)(Nv - 1));
+  const double sigma = sqrt(m2 / (double)(Nv - 1));
   const double sk =
-      (sigma > 0.0) ? (m.m3 / (sigma * sigma * sigma)) * ((double)Nv / ((double)(Nv - 1) * (double)(Nv - 2))) : 0.0;
+      (sigma > 0.0) ? (m3 / (sigma * sigma * sigma)) * ((double)Nv / ((double)(Nv - 1) * (double)(Nv - 2))) : 0.0;
   *st_out = sum;
   *sk_out = sk;
 }
@@ -971,7 +1087,8 @@ __device__ __forceinline__ BudgetSums budget_sums_lds(int L, const double *st, c
 // 64; every lane gets the result): the shift is a minimum, exact in any order
 // (a DPP reduction; lanes past L hold 0.0, which min(0, ...) already has),
 // +0.0 unless some s_k is negative; the two sums take the same additions in
-// the same order as the serial form, four lanes' values read ahead.
+// the same order as the serial form (ascending layers, as the host's budget
+// rule), four lanes' values read ahead.
 __device__ __forceinline__ BudgetSums budget_sums_wave(int L, const double *st, const double *sk) {
 #pragma clang fp contract(off)
   const int lane = opaque_tid() & 63;
@@ -1006,21 +1123,27 @@ __device__ __forceinline__ BudgetSums budget_sums_wave(int L, const double *st, 
 }
 
 // Statistics and budgets of every layer of sample b, block-wide, into LDS
-// (st, sk, bx: L + 16 doubles each, bud: L + 16 ints): each wave combines the
+// (st, sk, bx: L + 16 doubles each, bud: L + 16 ints; start: the launch's
+// item starts per pair): each wave combines the
 // chunk moments of layers wave, wave + 8, ...; then wave 0 forms the budgets
 // ("Layer-wise KV Cache Budget Allocation", the r_hat equation over the
 // sample's layers, in double precision and the oracle's order). With publish,
 // the plan's s_t, s_k, budget and budget_x of the sample and its budget
 // records (read by the units of later samples for their offsets) go out.
 __device__ __forceinline__ void sample_budgets(const Shape &sh, const PlanPtrs &plan, const PassWs &pw, int b,
-                                               unsigned epoch, bool publish, double *st, double *sk, double *bx,
-                                               int *bud) {
+                                               unsigned epoch, bool publish, const int *start, double *st, double *sk,
+                                               double *bx, int *bud, double *mb) {
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
   const int L = sh.L, B = sh.B;
-  for (int l = wave; l < L; l += kPassWaves) {
+  load_sample_moments(sh, pw, b, epoch, start, mb);
+  __syncthreads();
+  // layer l on DPP row l % 4 of wave (l / 4) % 8: 32 layers at a time
+  for (int l0 = 4 * wave; l0 < L; l0 += 4 * kPassWaves) {
+    const int l = l0 + (lane >> 4);
+    const int q = b * L + (l < L ? l : L - 1);
     double a, c;
-    chunk_stats(sh, pw, l * B + b, epoch, &a, &c);
-    if (lane == 0) {
+    chunk_stats(sh, l < L ? start[q + 1] - start[q] : 0, mb + (size_t)(l < L ? l : 0) * pw.mnch * 4, &a, &c);
+    if ((lane & 15) == 0 && l < L) {
       st[l] = a;
       sk[l] = c;
     }
@@ -1117,7 +1240,7 @@ __device__ __forceinline__ int block_topk(const Shape &sh, const uint64_t *iv_l,
 #pragma unroll
       for (int p = 0; p < PER; ++p) ok = ok && (p * NT + tid >= Nv || (unsigned)(kw[p] >> 32) == epoch);
       if (ok || spin_expired(spins, flags)) break;
-      __builtin_amdgcn_s_sleep(1);
+      poll_pause(spins);
 #pragma unroll
       for (int p = 0; p < PER; ++p)
         if (p * NT + tid < Nv && (unsigned)(kw[p] >> 32) != epoch)
@@ -1377,6 +1500,7 @@ __device__ __forceinline__ int block_topk(const Shape &sh, const uint64_t *iv_l,
 
 // Copy of rows [r0, r1) of one compaction unit, 16-byte pieces, sixteen per
 // thread in flight: row i is source row src_row(i) and destination row i.
+// Non-temporal stores: the compacted cache is not read again in this launch.
 template <typename RowFn>
 __device__ __forceinline__ void copy_rows(const char *src, char *dst, int rb, int cs, int r0, int r1, int S,
                                           RowFn &&src_row) {
@@ -1395,29 +1519,27 @@ __device__ __forceinline__ void copy_rows(const char *src, char *dst, int rb, in
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int q = q0 + j * NT + tid;
-      if (q < q_end) *reinterpret_cast<u32x4_t *>(dst + ((size_t)(q >> cs) * rb + 16 * (q & ((1 << cs) - 1)))) = v[j];
+      if (q < q_end) store_nt(reinterpret_cast<u32x4_t *>(dst + ((size_t)(q >> cs) * rb + 16 * (q & ((1 << cs) - 1)))), v[j]);
     }
   }
 }
+
 
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
 
-// Item (round r) of workgroup me: pair q (sample-major, q = b * L + l) and
-// chunk c; false when the workgroup has none in that round.
-__device__ __forceinline__ bool pass_item_of(const PassWs &pw, int LB, int me, int r, int *q, int *c) {
-  if (r == 0) {
-    const int s = me - pw.E;
-    if (s < 0 || s >= pw.ppr0 * pw.nch) return false;
-    *q = s / pw.nch;
-    *c = s - (s / pw.nch) * pw.nch;
-    return *q < LB;
-  }
-  if (me >= pw.ppr * pw.nch) return false;
-  *q = pw.ppr0 + (r - 1) * pw.ppr + me / pw.nch;
-  *c = me - (me / pw.nch) * pw.nch;
-  return *q < LB;
+template <typename Tag, int D>
+__device__ __forceinline__ void pass_rows_dispatch(int rtp, const Shape &sh, const PassWs &pw, const PassItem &it,
+                                                   int hg, int rg, int pidx, bool first, unsigned char *lds,
+                                                   const PassLds &lo, unsigned epoch) {
+  constexpr int RTPM = pass_rtp(D, Tag::kBytes);
+  if (RTPM >= 6 && rtp >= 6) pass_rows<Tag, D, (RTPM >= 6 ? 6 : 1)>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
+  else if (RTPM >= 5 && rtp == 5) pass_rows<Tag, D, (RTPM >= 5 ? 5 : 1)>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
+  else if (rtp == 4) pass_rows<Tag, D, 4>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
+  else if (rtp == 3) pass_rows<Tag, D, 3>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
+  else if (rtp == 2) pass_rows<Tag, D, 2>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
+  else pass_rows<Tag, D, 1>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
 }
 
 template <typename Tag, int D>
@@ -1428,7 +1550,6 @@ __global__ __launch_bounds__(kPassThreads) void aircache_pass_kernel(Shape sh, P
   __shared__ int wtot[4 * kPassWaves];
   __shared__ double redd[2 * kPassWaves];
   __shared__ float redf[kPassWaves];
-  constexpr int KT = pass_kt(D, Tag::kBytes);
   constexpr int RTPM = pass_rtp(D, Tag::kBytes);
   const int L = sh.L, B = sh.B, Nv = sh.Nv, LB = L * B;
   const unsigned e0 = *pw.epoch + 1u;
@@ -1449,104 +1570,64 @@ __global__ __launch_bounds__(kPassThreads) void aircache_pass_kernel(Shape sh, P
       unsigned spins = 0;
       while (load_coherent(pw.wrapc) < (unsigned)P) {
         if (spin_expired(spins, pw.flags)) break;
-        __builtin_amdgcn_s_sleep(2);
+        poll_pause(spins);
       }
     }
     __syncthreads();
   }
 
-  // The first item's keys load while the elite sets form (workgroups that
-  // form elite sets have no round-0 item; they stage theirs after their
-  // parts, and so do workgroups whose first item is in round 1).
-  int q0, cfirst;
-  const bool staged0 = pass_item_of(pw, LB, me, 0, &q0, &cfirst);
-  if (staged0) pass_stage<Tag, D>(sh, pw, tab, q0, cfirst, 0, ring);
-
-  // Elite sets: parts 1.. on workgroups [0, LB * (npp - 1)), part 0 and the
-  // merge on [LB * (npp - 1), E).
-  if (me < pw.E) {
-    const int npp = pw.npp, nother = LB * (npp - 1);
-    float *z = reinterpret_cast<float *>(ring);  // no round-0 item: the ring is free until the stage below
-    if (me < nother) {
-      const int lb = me / (npp - 1);
-      elite_part<Tag, D>(sh, tab, plan, pw, lb, me - lb * (npp - 1) + 1, epoch, z, lo.z_bytes, wtot, redf);
-    } else {
-      for (int lb = me - nother; lb < LB; lb += pw.E - nother)
-        elite_part<Tag, D>(sh, tab, plan, pw, lb, 0, epoch, z, lo.z_bytes, wtot, redf);
+  // 1. Elite-window parts: part pt of pair pt / npp on workgroup pt mod EW.
+  if (me < pw.EW) {
+    float *z = reinterpret_cast<float *>(ring);
+    for (int pt = me; pt < LB * pw.npp; pt += pw.EW) {
+      const int lb = pt / pw.npp;
+      elite_part<Tag, D>(sh, tab, plan, pw, lb, pt - lb * pw.npp, epoch, z, lo.z_bytes, wtot, redf);
     }
-    __syncthreads();
   }
-  // (a workgroup's rounds 1, 2, ... are consecutive, so its first item is in
-  // round 0 or round 1)
-  if (!staged0 && pass_item_of(pw, LB, me, 1, &q0, &cfirst)) pass_stage<Tag, D>(sh, pw, tab, q0, cfirst, 0, ring);
+  __syncthreads();
 
-  // Items, round by round.
-  const int rounds = 1 + (LB > pw.ppr0 ? (LB - pw.ppr0 + pw.ppr - 1) / pw.ppr : 0);
-  for (int r = 0; r < rounds; ++r) {
-    int q, c;
-    if (!pass_item_of(pw, LB, me, r, &q, &c)) {
-      if (r == 0) continue;
-      break;
-    }
+  // 2. The schedule, alike in every workgroup.
+  int *start = reinterpret_cast<int *>(lds + lo.start);
+  unsigned *masks = reinterpret_cast<unsigned *>(lds + lo.masks);
+  const bool preload = lo.nmask > 0;
+  const int kcap = pass_schedule<D, Tag::kBytes>(sh, pw, epoch, start, masks, preload);
+  const int n_items = uniform(start[LB]);
+
+  // 3. Items i = me, me + P, ...
+  for (int i = me; i < n_items; i += P) {
     const int tid = opaque_tid();
     PassItem it;
-    it.b = q / L;
-    it.l = q - it.b * L;
+    it.q = pass_pair_of(start, LB, i);
+    it.c = i - start[it.q];
+    it.nchq = start[it.q + 1] - start[it.q];
+    it.b = it.q / L;
+    it.l = it.q - it.b * L;
     it.plb = it.l * B + it.b;
-    it.c = c;
-    it.c0 = c * pw.width;
-    it.ncol = min(pw.width, Nv - it.c0);
-    it.q = tab.p[it.l];
-    it.k = tab.p[L + it.l];
-    int *el = reinterpret_cast<int *>(lds + lo.el);
-    it.ntk = pass_elite_list(sh, pw, it.plb, epoch, el, reinterpret_cast<unsigned *>(lds + lo.scr));
-    const int rows = sh.G * it.ntk;
-    it.rtg = rows > 0 ? (rows + 15) >> 4 : 1;
-    it.nrg = (it.rtg + RTPM - 1) / RTPM;
-    float colacc[KT];
-#pragma unroll
-    for (int s = 0; s < KT; ++s) colacc[s] = 0.f;
-    float ivacc[2] = {0.f, 0.f};  // columns tid and tid + 512
+    it.q_l = tab.p[it.l];
+    it.k_l = tab.p[L + it.l];
+    it.ntk = pass_elite_list(sh, pw, it.plb, epoch, masks, preload, reinterpret_cast<int *>(lds + lo.el));
+    const ItemPlan ip = item_plan(it.ntk, sh.G, Nv, pw.wph, kcap, D, Tag::kBytes);
+    it.rtg = ip.rtg;
+    it.nrg = ip.nrg;
+    it.ktw = ip.ktw;
+    it.width = ip.width;
+    it.c0 = it.c * ip.width;
+    {
+      const int left = Nv - it.c0;
+      it.ncolv = left < 0 ? 0 : (left > ip.width ? ip.width : left);
+    }
+    const int W = ip.width;
     float *colsum = reinterpret_cast<float *>(lds + lo.colsum);
-    const int W = pw.width;
+    float ivacc[3] = {0.f, 0.f, 0.f};  // columns tid, tid + 512, tid + 1024
     for (int hg = 0; hg < pw.nhg; ++hg) {
-      // this head group's tiles were staged by the previous pass or item (or
-      // at launch): the loader waves wait for their loads
-      if ((opaque_tid() >> 6) >= kPollWaves) wait_all_memory();
-      __syncthreads();
       for (int rg = 0; rg < it.nrg; ++rg) {
-        const int pidx = hg * it.nrg + rg;
         const int rtp = min(RTPM, it.rtg - rg * RTPM);
-        const bool last = rg == it.nrg - 1;
-        auto stage_next = [&]() {
-          if (hg + 1 < pw.nhg) {
-            pass_stage<Tag, D>(sh, pw, tab, q, c, hg + 1, ring);
-          } else {
-            int qn, cn;
-            if (pass_item_of(pw, LB, me, r + 1, &qn, &cn)) pass_stage<Tag, D>(sh, pw, tab, qn, cn, 0, ring);
-          }
-        };
-        if (rtp >= 6 && RTPM >= 6) pass_rows<Tag, D, (RTPM >= 6 ? 6 : 1)>(sh, pw, it, hg, rg, pidx, last, lds, lo, epoch, colacc, stage_next);
-        else if (rtp == 5 && RTPM >= 5) pass_rows<Tag, D, (RTPM >= 5 ? 5 : 1)>(sh, pw, it, hg, rg, pidx, last, lds, lo, epoch, colacc, stage_next);
-        else if (rtp == 4) pass_rows<Tag, D, 4>(sh, pw, it, hg, rg, pidx, last, lds, lo, epoch, colacc, stage_next);
-        else if (rtp == 3) pass_rows<Tag, D, 3>(sh, pw, it, hg, rg, pidx, last, lds, lo, epoch, colacc, stage_next);
-        else if (rtp == 2) pass_rows<Tag, D, 2>(sh, pw, it, hg, rg, pidx, last, lds, lo, epoch, colacc, stage_next);
-        else pass_rows<Tag, D, 1>(sh, pw, it, hg, rg, pidx, last, lds, lo, epoch, colacc, stage_next);
+        pass_rows_dispatch<Tag, D>(rtp, sh, pw, it, hg, rg, hg * it.nrg + rg, rg == 0, lds, lo, epoch);
       }
-      // the head group's column sums, per head, then added over its heads in
-      // ascending order (KV heads in ascending order overall)
-      {
-        const int lane = tid & 63, wave = tid >> 6;
-        const int gl = wave / pw.wph, sub = wave - gl * pw.wph;
-        if ((lane >> 4) == 0)
+      // the head group's column sums, added over its heads in ascending order
+      // (KV heads in ascending order overall)
 #pragma unroll
-          for (int s = 0; s < KT; ++s) colsum[gl * W + (sub * KT + s) * 16 + lane] = colacc[s];
-#pragma unroll
-        for (int s = 0; s < KT; ++s) colacc[s] = 0.f;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < 3; ++j) {
         const int col = tid + j * kPassThreads;
         if (col < W)
           for (int gg = 0; gg < pw.hgs; ++gg) ivacc[j] += colsum[gg * W + col];
@@ -1557,9 +1638,9 @@ __global__ __launch_bounds__(kPassThreads) void aircache_pass_kernel(Shape sh, P
     const float inv_rows = (it.ntk > 0) ? 1.f / (float)(sh.Hq * it.ntk) : 0.f;
     double sum = 0.0;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 3; ++j) {
       const int col = tid + j * kPassThreads;
-      if (col < it.ncol) {
+      if (col < it.ncolv) {
         const float a = ivacc[j] * inv_rows;
         ivacc[j] = a;
         plan.iv[(size_t)it.plb * Nv + it.c0 + col] = a;
@@ -1568,12 +1649,12 @@ __global__ __launch_bounds__(kPassThreads) void aircache_pass_kernel(Shape sh, P
       }
     }
     sum = block_sum_d(sum, redd);
-    const double mean = it.ncol > 0 ? sum / (double)it.ncol : 0.0;
+    const double mean = it.ncolv > 0 ? sum / (double)it.ncolv : 0.0;
     double m2 = 0.0, m3 = 0.0;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 3; ++j) {
       const int col = tid + j * kPassThreads;
-      if (col < it.ncol) {
+      if (col < it.ncolv) {
         const double d = (double)ivacc[j] - mean;
         m2 += d * d;
         m3 += d * d * d;
@@ -1581,15 +1662,15 @@ __global__ __launch_bounds__(kPassThreads) void aircache_pass_kernel(Shape sh, P
     }
     block_sum_d2(m2, m3, redd);
     if (tid < 4) {
-      const double v = tid == 0 ? sum : tid == 1 ? m2 : tid == 2 ? m3 : (double)it.ncol;
+      const double v = tid == 0 ? sum : tid == 1 ? m2 : tid == 2 ? m3 : (double)it.ncolv;
       const uint64_t u = __builtin_bit_cast(uint64_t, v), tag = (uint64_t)epoch << 32;
-      uint64_t *mr = pw.mom + ((size_t)it.plb * pw.nch + it.c) * 8 + 2 * tid;
+      uint64_t *mr = pw.mom + ((size_t)it.plb * pw.mnch + it.c) * 8 + 2 * tid;
       store_coherent(mr, tag | (u & 0xffffffffu));
       store_coherent(mr + 1, tag | (u >> 32));
     }
   }
 
-  // Consumer units: a contiguous range per workgroup. A unit is (sample,
+  // 4. Consumer units: a contiguous range per workgroup. A unit is (sample,
   // layer, KV head, K or V) with compaction, (sample, layer) without.
   {
     const int per = pw.gather ? sh.Hkv * 2 : 1;
@@ -1599,7 +1680,8 @@ __global__ __launch_bounds__(kPassThreads) void aircache_pass_kernel(Shape sh, P
     double *st = reinterpret_cast<double *>(ring + lo.sts);
     double *sk = st + (L + 16);
     double *bx = sk + (L + 16);
-    int *bud = reinterpret_cast<int *>(bx + (L + 16));
+    double *mb = bx + (L + 16);                          // [L][mnch][4] chunk moments
+    int *bud = reinterpret_cast<int *>(mb + (size_t)L * pw.mnch * 4);
     __shared__ int bc[4];
     {
       const int tid = opaque_tid();
@@ -1617,7 +1699,7 @@ __global__ __launch_bounds__(kPassThreads) void aircache_pass_kernel(Shape sh, P
       auto budget = [&]() {
         if (have_b != b) {
           // the sample's first unit publishes its statistics and budgets
-          sample_budgets(sh, plan, pw, b, epoch, u == b * L * per, st, sk, bx, bud);
+          sample_budgets(sh, plan, pw, b, epoch, u == b * L * per, start, st, sk, bx, bud, mb);
           have_b = b;
         }
         // offset of (l, b) in the layer's compacted buffer: the budgets of
@@ -1630,7 +1712,7 @@ __global__ __launch_bounds__(kPassThreads) void aircache_pass_kernel(Shape sh, P
             unsigned spins = 0;
             while ((unsigned)(v >> 32) != epoch) {
               if (spin_expired(spins, pw.flags)) break;
-              __builtin_amdgcn_s_sleep(1);
+              poll_pause(spins);
               v = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rb, b2 * 8, 0, 16));
             }
             off += (long long)sh.Hkv * ((long long)(int)(unsigned)v + sh.Nt) * sh.D;

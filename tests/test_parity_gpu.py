@@ -122,15 +122,16 @@ def test_all_text_elite_many_rows(path):
     compare(inp, g, reference(inp, g))
 
 
-@pytest.mark.parametrize("path", ["rows", "tiled"])
+@pytest.mark.parametrize("path", ["rows", "tiled", "auto-run"])
 def test_more_than_128_elite_tokens(path):
     """Zero queries with N_t = 200 make all 200 text tokens elite: the rows
-    path then has more elite text tiles than waves (16 x 8 = 128 tokens), and
-    seven MHA KV heads keep the shape off the chunked path."""
+    path then has more elite text tiles than waves (16 x 8 = 128 tokens); the
+    one-launch pass takes seven MHA KV heads one per head group, 200 elite
+    rows in three row passes and 200 elite text columns in its last chunks."""
     w = wl.custom(Nv=300, Nt=200, Hq=7, Hkv=7, D=128, dtype="bf16", L=2, B=1, ratio=0.2)
     print(f"[parity] 200 elite tokens, path {path}", flush=True)
     inp = wl.make_inputs(w, 12, zero_q=True)
-    g = run_gpu(inp, path=path)
+    g = run_gpu(inp, path=path.split("-")[0], run=path.endswith("-run"))
     assert (g["n_elite"] == 200).all()
     compare(inp, g, reference(inp, g))
 
