@@ -365,11 +365,12 @@ __device__ __forceinline__ void elite_logits(const Shape &sh, const typename Tag
 // tokens for the window variants) and publishes it: its size (ecnt[lb]) and
 // its bit mask as 32-bit halves (emask[lb], tokens 32 h .. 32 h + 31 in half
 // h); also the plan's elite list and count, and the overflow bit when the
-// size exceeds the elite cap. N_t <= 1024.
-template <typename Tag, int D>
+// size exceeds the elite cap. before_store() runs before its first record
+// store. N_t <= 1024.
+template <typename Tag, int D, typename BeforeStoreFn>
 __device__ __forceinline__ void elite_part(const Shape &sh, const PassTables &tab, const PlanPtrs &plan,
                                            const PassWs &pw, int lb, int pi, unsigned epoch, float *z,
-                                           int lds_bytes, int *wtot, float *red) {
+                                           int lds_bytes, int *wtot, float *red, BeforeStoreFn &&before_store) {
   using E = typename Tag::store_t;
   constexpr int NT = kPassThreads, NW = kPassWaves, EP = 2;
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
@@ -421,6 +422,7 @@ __device__ __forceinline__ void elite_part(const Shape &sh, const PassTables &ta
     }
     __syncthreads();  // z is free again
   }
+  before_store();
   if (pi > 0) {
     uint64_t *part = pw.parts + ((size_t)lb * npp + pi) * Nt;
 #pragma unroll
@@ -748,9 +750,11 @@ __device__ __forceinline__ void pass_rows(const Shape &sh, const PassWs &pw, con
 #pragma unroll
     for (int j = 0; j < kDma; ++j) load_lds16(src + 16 * grp + 64 * j, dst + 1024 * j);
   };
+  // a later pass over a chunk whose tiles all fit the ring finds them there
+  const bool resident = rg > 0 && ktw <= R;
 #pragma unroll
   for (int s = 0; s < R; ++s)
-    if (s < ktw) issue(s);
+    if (s < ktw && !resident) issue(s);
 
   f32x4_t S[KM][RTP];
 #pragma unroll
@@ -758,7 +762,7 @@ __device__ __forceinline__ void pass_rows(const Shape &sh, const PassWs &pw, con
     if (s < ktw) {
       // tiles s + 1 .. min(s + R, ktw) - 1 may stay in flight
       const int ahead = (s + R < ktw ? s + R : ktw) - 1 - s;
-      wait_tiles<kDma>(ahead);
+      if (!resident) wait_tiles<kDma>(ahead);
       f32x4_t acc[RTP];
 #pragma unroll
       for (int rt = 0; rt < RTP; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1534,8 +1538,10 @@ __device__ __forceinline__ void pass_rows_dispatch(int rtp, const Shape &sh, con
                                                    int hg, int rg, int pidx, bool first, unsigned char *lds,
                                                    const PassLds &lo, unsigned epoch) {
   constexpr int RTPM = pass_rtp(D, Tag::kBytes);
-  if (RTPM >= 6 && rtp >= 6) pass_rows<Tag, D, (RTPM >= 6 ? 6 : 1)>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
-  else if (RTPM >= 5 && rtp == 5) pass_rows<Tag, D, (RTPM >= 5 ? 5 : 1)>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
+  if (RTPM >= 6 && rtp >= 6)
+    pass_rows<Tag, D, (RTPM >= 6 ? 6 : 1)>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
+  else if (RTPM >= 5 && rtp == 5)
+    pass_rows<Tag, D, (RTPM >= 5 ? 5 : 1)>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
   else if (rtp == 4) pass_rows<Tag, D, 4>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
   else if (rtp == 3) pass_rows<Tag, D, 3>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
   else if (rtp == 2) pass_rows<Tag, D, 2>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
@@ -1557,8 +1563,15 @@ __global__ __launch_bounds__(kPassThreads) void aircache_pass_kernel(Shape sh, P
   const int P = gridDim.x, me = blockIdx.x;
   unsigned char *ring = lds + lo.ring;
 
-  // Every 2^21 calls: zero every record, then wait for the whole grid.
-  if ((epoch & kTagEpochMask) == 0u) {
+  // Every 2^21 calls: zero every record, then wait for the whole grid. Run
+  // once per workgroup before its first record store (an elite workgroup
+  // after its first part's logits, the others before the schedule), so that
+  // no load waits for the epoch before the elite windows' first loads.
+  bool wrapped = false;
+  auto wrap_once = [&]() {
+    if (wrapped) return;
+    wrapped = true;
+    if ((epoch & kTagEpochMask) != 0u) return;
     // agent-coherent stores, so that every XCD's coherent reads see the zeros
     uint64_t *r64 = reinterpret_cast<uint64_t *>(pw.recs);
     for (size_t i = (size_t)me * kPassThreads + threadIdx.x; i < 2 * pw.rec_words; i += (size_t)P * kPassThreads)
@@ -1574,16 +1587,17 @@ __global__ __launch_bounds__(kPassThreads) void aircache_pass_kernel(Shape sh, P
       }
     }
     __syncthreads();
-  }
+  };
 
   // 1. Elite-window parts: part pt of pair pt / npp on workgroup pt mod EW.
   if (me < pw.EW) {
     float *z = reinterpret_cast<float *>(ring);
     for (int pt = me; pt < LB * pw.npp; pt += pw.EW) {
       const int lb = pt / pw.npp;
-      elite_part<Tag, D>(sh, tab, plan, pw, lb, pt - lb * pw.npp, epoch, z, lo.z_bytes, wtot, redf);
+      elite_part<Tag, D>(sh, tab, plan, pw, lb, pt - lb * pw.npp, epoch, z, lo.z_bytes, wtot, redf, wrap_once);
     }
   }
+  wrap_once();
   __syncthreads();
 
   // 2. The schedule, alike in every workgroup.
@@ -1688,7 +1702,9 @@ __global__ __launch_bounds__(kPassThreads) void aircache_pass_kernel(Shape sh, P
       __syncthreads();  // the ring is free: every item of this workgroup is done
       for (int i = tid; i < kTopkBuckets; i += kPassThreads) hist[i] = 0u;
     }
-    int have_b = -1;  // the sample whose budgets st / sk / bx / bud hold
+    int have_b = -1;    // the sample whose budgets st / sk / bx / bud hold
+    int have_plb = -1;  // the (layer, sample) whose kept list kidx and offset bc hold
+    int have_kb = 0;
     for (int u = u0; u < u1; ++u) {
       const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
       const int qq = u / per, rem = u - qq * per;
@@ -1736,10 +1752,16 @@ __global__ __launch_bounds__(kPassThreads) void aircache_pass_kernel(Shape sh, P
       };
       const uint64_t *ivl = pw.ivrec + (size_t)plb * Nv;
       int32_t *kout = lead ? plan.kept + (size_t)plb * Nv : nullptr;
-      int rb_;
-      if (Nv <= 2048) rb_ = block_topk<4>(sh, ivl, kidx, kout, epoch, pw.flags, hist, budget);
-      else if (Nv <= 4096) rb_ = block_topk<8>(sh, ivl, kidx, kout, epoch, pw.flags, hist, budget);
-      else rb_ = block_topk<16>(sh, ivl, kidx, kout, epoch, pw.flags, hist, budget);
+      // the units of one (layer, sample) are consecutive: its top-k once per
+      // workgroup
+      int rb_ = have_kb;
+      if (plb != have_plb) {
+        if (Nv <= 2048) rb_ = block_topk<4>(sh, ivl, kidx, kout, epoch, pw.flags, hist, budget);
+        else if (Nv <= 4096) rb_ = block_topk<8>(sh, ivl, kidx, kout, epoch, pw.flags, hist, budget);
+        else rb_ = block_topk<16>(sh, ivl, kidx, kout, epoch, pw.flags, hist, budget);
+        have_plb = plb;
+        have_kb = uniform(rb_);
+      }
       if (!pw.gather) continue;
       const int kb = uniform(rb_);
       const long long off =
