@@ -56,6 +56,8 @@ def lib():
         l.orc_topk.restype = None
         l.orc_gather.argtypes = [C.POINTER(Desc), P, C.c_int, P, C.c_int, P]
         l.orc_gather.restype = None
+        l.orc_decode_attention.argtypes = [C.POINTER(Desc), P, P, C.c_int, P, P]
+        l.orc_decode_attention.restype = None
         l.orc_run.argtypes = [C.POINTER(Desc)] + [P] * 15
         l.orc_run.restype = C.c_int
         _lib = l
@@ -147,6 +149,32 @@ def gather(w, src_l: np.ndarray, b: int, kept) -> np.ndarray:
     out = np.zeros((w.Hkv, len(kept) + w.Nt, w.D), dtype=src_l.dtype)
     lib().orc_gather(C.byref(d), _ptr(src_l), b, _ptr(kept), len(kept), _ptr(out))
     return out
+
+
+def decode_attention_segment(w, k_seg, v_seg, n: int, q) -> np.ndarray:
+    """Decode attention over one (layer, sample) segment [H_kv][n][D] of the
+    compacted cache for the new queries q [H_q][D]: o [H_q][D] (float64)."""
+    store = np.float32 if w.dtype == "f32" else np.uint16
+    k_seg = np.ascontiguousarray(k_seg, dtype=store).ravel()
+    v_seg = np.ascontiguousarray(v_seg, dtype=store).ravel()
+    q = np.ascontiguousarray(q, dtype=store)
+    assert k_seg.size == v_seg.size == w.Hkv * n * w.D and q.shape == (w.Hq, w.D)
+    o = np.zeros((w.Hq, w.D), np.float64)
+    lib().orc_decode_attention(C.byref(desc_of(w)), _ptr(k_seg), _ptr(v_seg), int(n), _ptr(q), _ptr(o))
+    return o
+
+
+def decode_attention(w, k_out_l, v_out_l, out_off_l, budget_l, q_l) -> np.ndarray:
+    """Decode attention over layer l's compacted cache (k_out_l / v_out_l flat,
+    out_off_l [B+1], budget_l [B]) for the new queries q_l [B][H_q][D]:
+    o [B][H_q][D] (float64)."""
+    o = np.zeros((w.B, w.Hq, w.D), np.float64)
+    for b in range(w.B):
+        n = int(budget_l[b]) + w.Nt
+        off = int(out_off_l[b])
+        size = w.Hkv * n * w.D
+        o[b] = decode_attention_segment(w, k_out_l[off:off + size], v_out_l[off:off + size], n, q_l[b])
+    return o
 
 
 # ---- the whole pass ---------------------------------------------------------

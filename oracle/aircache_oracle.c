@@ -257,6 +257,39 @@ void orc_gather(const orc_desc *w, const void *src_l, int b, const int32_t *kept
 }
 
 /*
+ * Decode attention over one compacted (layer, sample) segment, the consumer
+ * of the compacted cache: the KV-cache primer page (devpress.csdn.net),
+ * section 2.1 "到底缓存什么？", the o_t equation, with one new query per head
+ * and no mask (the incremental step sees only cached positions, section 2.2).
+ * For each query head h, with KV head g = h / (H_q / H_kv):
+ *   o_h = softmax(q_h . K_g^T / sqrt(D)) V_g
+ * over the n rows of head g in the segment, laid out [H_kv][n][D] as
+ * orc_gather writes it. q: [H_q][D] in the descriptor's dtype; o: [H_q][D].
+ */
+void orc_decode_attention(const orc_desc *w, const void *k_seg, const void *v_seg, int n, const void *q,
+                          double *o) {
+  const int G = w->Hq / w->Hkv, D = w->D;
+  const double scale = sqrt((double)D);
+  double *z = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  for (int h = 0; h < w->Hq; ++h) {
+    const int g = h / G;
+    for (int j = 0; j < n; ++j) {
+      double acc = 0.0;
+      for (int d = 0; d < D; ++d)
+        acc += elem(q, (size_t)h * D + d, w->dtype) * elem(k_seg, ((size_t)g * n + j) * D + d, w->dtype);
+      z[j] = acc / scale;
+    }
+    softmax(z, n);
+    for (int d = 0; d < D; ++d) {
+      double acc = 0.0;
+      for (int j = 0; j < n; ++j) acc += z[j] * elem(v_seg, ((size_t)g * n + j) * D + d, w->dtype);
+      o[(size_t)h * D + d] = acc;
+    }
+  }
+  free(z);
+}
+
+/*
  * The whole pass. Arrays indexed [l][b] are row-major with B columns.
  *   elite [L][B][N_t] (first n_elite valid), pbar [L][B][N_t],
  *   iv [L][B][N_v], s_t, s_k, x [L][B], budget [L][B],

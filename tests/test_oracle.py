@@ -415,3 +415,92 @@ def test_config2_generator_reading_elite_is_all_text():
     inp = wl.make_inputs(small, 2)
     o = oracle.run(inp, compact=False, threads=4)
     assert (o["n_elite"] == w.Nt).all()
+
+
+# ------------------------------------------------- decode attention (f2) ----
+# The consumer of the compacted cache: o_h = softmax(q_h K_g^T / sqrt(D)) V_g
+# (the KV-cache primer page, section 2.1, the o_t equation).
+
+def _seg(w, rng, n, scale=1.0):
+    k = (rng.standard_normal((w.Hkv, n, w.D)) * scale).astype(np.float32)
+    v = rng.standard_normal((w.Hkv, n, w.D)).astype(np.float32)
+    q = rng.standard_normal((w.Hq, w.D)).astype(np.float32)
+    if w.dtype == "bf16":
+        k, v, q = wl.f32_to_bf16_bits(k), wl.f32_to_bf16_bits(v), wl.f32_to_bf16_bits(q)
+    return k, v, q
+
+
+def _f64(w, a):
+    return (a if w.dtype == "f32" else wl.bf16_bits_to_f32(a)).astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_single_row_returns_its_value(dtype):
+    w = wl.custom(Nv=8, Nt=2, Hq=6, Hkv=2, D=16, dtype=dtype)
+    k, v, q = _seg(w, np.random.default_rng(1), 1)
+    o = oracle.decode_attention_segment(w, k, v, 1, q)
+    for h in range(w.Hq):
+        assert np.array_equal(o[h], _f64(w, v)[h // 3, 0])
+
+
+@pytest.mark.parametrize("n", [2, 7, 40])
+def test_decode_uniform_keys_give_the_mean_value(n):
+    w = wl.custom(Nv=8, Nt=2, Hq=4, Hkv=2, D=32)
+    k, v, q = _seg(w, np.random.default_rng(n), n)
+    k[:] = k[:, :1]  # every row of a head's keys equal: uniform weights
+    o = oracle.decode_attention_segment(w, k, v, n, q)
+    for h in range(w.Hq):
+        np.testing.assert_allclose(o[h], _f64(w, v)[h // 2].mean(axis=0), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("shape", [dict(Hq=1, Hkv=1), dict(Hq=6, Hkv=2), dict(Hq=4, Hkv=4, dtype="bf16")])
+def test_decode_matches_library_softmax(seed, shape):
+    """Brute force with scipy's softmax, query head h on KV head h // G."""
+    w = wl.custom(Nv=8, Nt=2, D=24, **shape)
+    n = 5 + seed
+    k, v, q = _seg(w, np.random.default_rng(10 + seed), n, scale=2.0)
+    o = oracle.decode_attention_segment(w, k, v, n, q)
+    K, V, Q = _f64(w, k), _f64(w, v), _f64(w, q)
+    G = w.Hq // w.Hkv
+    for h in range(w.Hq):
+        p = scipy.special.softmax(K[h // G] @ Q[h] / math.sqrt(w.D))
+        np.testing.assert_allclose(o[h], p @ V[h // G], rtol=1e-12, atol=1e-13)
+
+
+def test_decode_is_invariant_to_row_order():
+    w = wl.custom(Nv=8, Nt=2, Hq=4, Hkv=2, D=16)
+    n = 9
+    k, v, q = _seg(w, np.random.default_rng(3), n)
+    perm = np.random.default_rng(4).permutation(n)
+    a = oracle.decode_attention_segment(w, k, v, n, q)
+    b = oracle.decode_attention_segment(w, np.ascontiguousarray(k[:, perm]), np.ascontiguousarray(v[:, perm]), n, q)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
+def test_decode_dominant_key_selects_its_value():
+    w = wl.custom(Nv=8, Nt=2, Hq=2, Hkv=1, D=16)
+    rng = np.random.default_rng(5)
+    n = 6
+    k, v, q = _seg(w, rng, n, scale=0.01)
+    k[0, 4] = 40.0 * q[0] / np.linalg.norm(q[0])  # a key along query 0
+    o = oracle.decode_attention_segment(w, k, v, n, q)
+    np.testing.assert_allclose(o[0], v[0, 4], atol=1e-6)
+
+
+def test_decode_over_the_compacted_layer_uses_offsets_and_budgets():
+    """Layer-level wrapper on the oracle's own compacted output: each sample's
+    segment is found at out_off with budget + N_t rows per KV head."""
+    w = wl.custom(Nv=12, Nt=3, Hq=4, Hkv=2, D=8, B=2, L=1, ratio=0.4)
+    inp = wl.make_inputs(w, 2)
+    out = oracle.run(inp)
+    q = np.random.default_rng(6).standard_normal((w.B, w.Hq, w.D)).astype(np.float32)
+    o = oracle.decode_attention(w, out["k_out"][0], out["v_out"][0], out["out_off"][0], out["budget"][0], q)
+    for b in range(w.B):
+        kept = out["kept"][0, b, :out["budget"][0, b]]
+        rows = np.concatenate([kept, np.arange(w.Nv, w.Nv + w.Nt)])
+        K = inp.k[0, b][:, rows].astype(np.float64)
+        V = inp.v[0, b][:, rows].astype(np.float64)
+        for h in range(w.Hq):
+            p = scipy.special.softmax(K[h // 2] @ q[b, h].astype(np.float64) / math.sqrt(w.D))
+            np.testing.assert_allclose(o[b, h], p @ V[h // 2], rtol=1e-12, atol=1e-13)
