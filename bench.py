@@ -58,6 +58,7 @@ def parse():
                     help="leave out the cache-warm loop (one input copy every step), so that every launch of the "
                          "run reads rotated inputs (profiles of the headline conditions)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-decode", action="store_true", help="do not time decode attention over the compacted cache")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (the reference kernel that scales "
@@ -392,6 +393,36 @@ def main():
         torch.cuda.synchronize()
         ms_hot = e0.elapsed_time(e1) / a.steps
         check_status("hot", status_words[2 * a.steps:])
+    # Decode attention over the compacted cache the last step wrote
+    # (aircache_decode), new queries of the workload's dtype; K timed calls.
+    dec = None
+    if not a.skip_decode:
+        torch.cuda.synchronize()
+        budget_now = plan.budget.cpu().numpy()
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        qd = [(torch.randn(w.B, w.Hq, w.D, device=dev, generator=g) * (4.0 / math.sqrt(w.D))).to(tdtype)
+              for _ in range(w.L)]
+        od = [torch.empty(w.B, w.Hq, w.D, dtype=torch.float32, device=dev) for _ in range(w.L)]
+        bdec = ac.bind_decode(qd, plan, k_out, v_out, od, stream=stream)
+        for _ in range(3):
+            bdec()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(a.steps):
+            bdec()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dec_us = 1e3 * e0.elapsed_time(e1) / a.steps
+        esz = 2 if w.dtype == wl.BF16 else 4
+        # K and V rows of every segment once, the new queries, the outputs
+        dec_bytes = (2.0 * w.Hkv * w.D * esz * float((budget_now + w.Nt).sum()) +
+                     w.L * w.B * w.Hq * w.D * (esz + 4))
+        dec_gbps = dec_bytes / (dec_us * 1e-6) / 1e9
+        dec = {"kernels": ["decode_partial_kernel", "decode_combine_kernel"], "us_per_call": dec_us,
+               "algorithmic_bytes": dec_bytes, "achieved_gbps": dec_gbps, "peak_gbps": PEAK_HBM_GBPS,
+               "frac": dec_gbps / PEAK_HBM_GBPS, "dense_cache_bytes": 2.0 * w.L * w.B * w.Hkv * w.S * w.D * esz,
+               "retained_row_frac": float((budget_now + w.Nt).sum()) / (w.L * w.B * (w.Nv + w.Nt))}
     ceil = hbm_ceilings()
 
     tokens = w.L * w.B * w.Nv
@@ -403,7 +434,7 @@ def main():
     else:
         dom, dom_bytes = "cross_score", nbytes["cross_score"]
     dom_gbps = dom_bytes / (kern_us[dom] * 1e-6) / 1e9
-    dom_kernel = {"rows": "cross_score_rows_kernel", "chunked": "cross_score_fused_kernel"}.get(path, "cross_score_kernel")
+    dom_kernel = {"rows": "cross_score_rows_kernel", "chunked": "aircache_pass_kernel"}.get(path, "cross_score_kernel")
     # counters are taken on the workload as defined (its own base distribution)
     traffic = (measured_traffic(dom_kernel, w.name)
                if w.base == wl.CONFIGS[a.workload].base and a.budget_mode == "aircache" and a.obs_window == 0
@@ -445,6 +476,9 @@ def main():
         "elite_hist": {int(k): int(v) for k, v in zip(*np.unique(n_elite_all, return_counts=True))},
         "budget_sum_per_step": float(budget_all.sum() / ncopy),
         "budget_min_mean_max": [int(budget_all.min()), float(budget_all.mean()), int(budget_all.max())],
+        # decode attention over the compacted cache (a consumer of the pass,
+        # timed after the pass, not part of its step)
+        "decode_attention": dec,
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, a.cpu_seconds)

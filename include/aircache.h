@@ -252,6 +252,35 @@ int aircache_run_noalloc(const aircache_desc *desc, const void *const *q_txt, co
                          const void *const *v, const aircache_plan_buf *plan, void *const *k_out,
                          void *const *v_out, void *stream);
 
+/* Decode attention over the compacted cache, the consumer of the compacted
+ * per-layer cache: the KV-cache primer page (devpress.csdn.net), section 2.1
+ * "到底缓存什么？", the o_t equation, with one new query per query head and no
+ * mask. For every layer l, sample b and query head h, with KV head
+ * g = h / (n_q_heads / n_kv_heads) and the n = budget[l][b] + n_txt rows of
+ * head g in the (l, b) segment that aircache_compress / aircache_run wrote
+ * ([n_kv_heads][n][head_dim] at out_off[l][b]):
+ *   o[l][b][h] = softmax(q_dec[l][b][h] . K^T / sqrt(head_dim)) V
+ * in float32 arithmetic.
+ *   q_dec       : host array of n_layers device pointers, each [B][H_q][D] in
+ *                 the descriptor's dtype (read-only)
+ *   plan        : only budget and out_off are read (device), as aircache_plan
+ *                 or aircache_run left them on the same stream
+ *   k_out, v_out: the compacted buffers (read-only)
+ *   o           : host array of n_layers device pointers, each [B][H_q][D]
+ *                 float32 (written)
+ *   workspace   : device scratch of ws_bytes >= aircache_decode_workspace_size
+ *                 (no zeroing needed; every word read is written first)
+ * All device pointers 16-byte aligned. A workgroup's threads own eight
+ * output elements of one query head each: at most 32 query heads per KV head
+ * for head_dim 128, 64 for head_dim 64 (AIRCACHE_EINVAL beyond). A segment
+ * whose budget or offset is
+ * out of range (a plan not written by this library) gives NaN rows instead
+ * of reading outside the buffers. */
+size_t aircache_decode_workspace_size(const aircache_desc *desc);
+int aircache_decode(const aircache_desc *desc, const void *const *q_dec, const aircache_plan_buf *plan,
+                    const void *const *k_out, const void *const *v_out, float *const *o, void *workspace,
+                    size_t ws_bytes, void *stream);
+
 /* Instrumented variants of aircache_plan / aircache_compress / aircache_run for
  * timing individual kernels. events is a host array of hipEvent_t handles created by
  * the caller: events[i] is recorded on the stream just before the i-th kernel

@@ -22,7 +22,7 @@ EXPORTS = ["aircache_abi_version", "aircache_workspace_size", "aircache_max_comp
            "aircache_resolved_path", "aircache_run_launches",
            "aircache_plan", "aircache_compress", "aircache_run", "aircache_plan_profiled",
            "aircache_compress_profiled", "aircache_run_profiled", "aircache_run_noalloc", "aircache_strerror",
-           "aircache_last_error"]
+           "aircache_last_error", "aircache_decode_workspace_size", "aircache_decode"]
 NOALLOC_SCRATCH_BYTES = 64 << 20  # AIRCACHE_NOALLOC_SCRATCH_BYTES
 PLAN_KERNELS = ["elite_select", "cross_score", "finalize", "topk_select"]
 COMPRESS_KERNELS = ["kv_gather"]
@@ -85,6 +85,10 @@ def load() -> C.CDLL:
                                               P, C.c_int]
         lib.aircache_run_noalloc.restype = C.c_int
         lib.aircache_run_noalloc.argtypes = [C.POINTER(Desc), P, P, P, C.POINTER(PlanBuf), P, P, P]
+        lib.aircache_decode_workspace_size.restype = C.c_size_t
+        lib.aircache_decode_workspace_size.argtypes = [C.POINTER(Desc)]
+        lib.aircache_decode.restype = C.c_int
+        lib.aircache_decode.argtypes = [C.POINTER(Desc), P, C.POINTER(PlanBuf), P, P, P, P, C.c_size_t, P]
         lib.aircache_strerror.restype = C.c_char_p
         lib.aircache_strerror.argtypes = [C.c_int]
         lib.aircache_last_error.restype = C.c_char_p
@@ -153,3 +157,15 @@ def compress(desc: Desc, buf: PlanBuf, k_ptrs, v_ptrs, ko_ptrs, vo_ptrs, stream:
         return load().aircache_compress(C.byref(desc), C.byref(buf), *arrs, C.c_void_p(stream))
     return load().aircache_compress_profiled(C.byref(desc), C.byref(buf), *arrs, C.c_void_p(stream),
                                              ptr_array(events), len(events))
+
+
+def decode_workspace_size(desc: Desc) -> int:
+    return int(load().aircache_decode_workspace_size(C.byref(desc)))
+
+
+def decode(desc: Desc, q_ptrs, buf: PlanBuf, ko_ptrs, vo_ptrs, o_ptrs, ws_ptr: int, ws_bytes: int,
+           stream: int) -> int:
+    """aircache_decode: decode attention over the compacted cache."""
+    q, ko, vo, o = [ptr_array(p) if p is not None else None for p in (q_ptrs, ko_ptrs, vo_ptrs, o_ptrs)]
+    return load().aircache_decode(C.byref(desc), q, C.byref(buf), ko, vo, o, C.c_void_p(ws_ptr), ws_bytes,
+                                  C.c_void_p(stream))

@@ -180,6 +180,36 @@ class AirCache:
         mk = lambda: [torch.empty(n, dtype=self.dtype, device=self.device) for _ in range(L)]
         return mk(), mk()
 
+    def decode(self, q_dec, plan: PlanOutputs, k_out, v_out, o=None, stream=None):
+        """Decode attention over the compacted cache (aircache_decode): for
+        every layer, q_dec[l] [B][H_q][D] (the pass's dtype) against the rows
+        that run / compress wrote for plan; returns o, per layer [B][H_q][D]
+        float32 (allocated when not given). The decode workspace is kept on
+        the object."""
+        s = self.shape
+        self._check_layers(q_dec, (s["B"], s["Hq"], s["D"]), "q_dec")
+        self._check_outputs(k_out, v_out)
+        if o is None:
+            o = [torch.empty(s["B"], s["Hq"], s["D"], dtype=torch.float32, device=self.device)
+                 for _ in range(s["L"])]
+        for l, t in enumerate(o):
+            if t.device != self.device or t.dtype != torch.float32 or not t.is_contiguous() or \
+                    tuple(t.shape) != (s["B"], s["Hq"], s["D"]):
+                raise ValueError(f"o[{l}] must be a contiguous float32 [B, H_q, D] tensor on {self.device}")
+        need = _lib.decode_workspace_size(self.desc)
+        if getattr(self, "dec_workspace", None) is None or self.dec_workspace.numel() < need:
+            self.dec_workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+        _lib.check(_lib.decode(self.desc, [t.data_ptr() for t in q_dec], plan.buf(),
+                               [t.data_ptr() for t in k_out], [t.data_ptr() for t in v_out],
+                               [t.data_ptr() for t in o], self.dec_workspace.data_ptr(), need,
+                               self._stream(stream)))
+        return o
+
+    def bind_decode(self, q_dec, plan: PlanOutputs, k_out, v_out, o, stream=None) -> "BoundDecode":
+        """A BoundDecode running decode() on these tensors with the checks and
+        marshalling done once, here."""
+        return BoundDecode(self, q_dec, plan, k_out, v_out, o, stream)
+
     def compress(self, plan: PlanOutputs, k, v, k_out, v_out, stream=None, events=None) -> None:
         s = self.shape
         shp = (s["B"], s["Hkv"], s["Nv"] + s["Nt"], s["D"])
@@ -275,3 +305,39 @@ class BoundPass:
 
     def __call__(self) -> PlanOutputs:
         return self.run()
+
+
+class BoundDecode:
+    """AirCache.decode over fixed tensors, validated and marshalled once (as
+    BoundPass does for the pass). The tensors must stay alive while it is used."""
+
+    def __init__(self, ac: "AirCache", q_dec, plan: PlanOutputs, k_out, v_out, o, stream=None):
+        s = ac.shape
+        ac._check_layers(q_dec, (s["B"], s["Hq"], s["D"]), "q_dec")
+        ac._check_outputs(k_out, v_out)
+        for l, t in enumerate(o):
+            if t.device != ac.device or t.dtype != torch.float32 or not t.is_contiguous() or \
+                    tuple(t.shape) != (s["B"], s["Hq"], s["D"]):
+                raise ValueError(f"o[{l}] must be a contiguous float32 [B, H_q, D] tensor on {ac.device}")
+        need = _lib.decode_workspace_size(ac.desc)
+        self.workspace = torch.empty(need, dtype=torch.uint8, device=ac.device)
+        self.out = o
+        self._keep = (ac, q_dec, plan, k_out, v_out, o)
+        self._lib = _lib.load()
+        self._desc = _lib.C.byref(ac.desc)
+        self._buf = plan.buf()
+        self._pbuf = _lib.C.byref(self._buf)
+        self._q = _lib.ptr_array([t.data_ptr() for t in q_dec])
+        self._ko = _lib.ptr_array([t.data_ptr() for t in k_out])
+        self._vo = _lib.ptr_array([t.data_ptr() for t in v_out])
+        self._o = _lib.ptr_array([t.data_ptr() for t in o])
+        self._ws = _lib.C.c_void_p(self.workspace.data_ptr())
+        self._ws_bytes = need
+        self._st = _lib.C.c_void_p(ac._stream(stream))
+
+    def __call__(self):
+        rc = self._lib.aircache_decode(self._desc, self._q, self._pbuf, self._ko, self._vo, self._o, self._ws,
+                                       self._ws_bytes, self._st)
+        if rc:
+            _lib.check(rc)
+        return self.out

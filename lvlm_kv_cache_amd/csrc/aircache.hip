@@ -751,6 +751,7 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
 }
 
 #include "pass_chunked.h"
+#include "decode.h"
 
 // ----------------------------------------------------------------------------
 // Step 1: elite observation window ("Elite Observation Window", the Att and k
@@ -1780,6 +1781,35 @@ int scratch_slot(ScratchSlot **slot) {
 
 using namespace aircache;
 
+// ----------------------------------------------------------------------------
+// Decode attention over the compacted cache (decode.h).
+// ----------------------------------------------------------------------------
+
+size_t decode_ws_bytes(const Shape &s) {
+  const size_t units = (size_t)s.L * s.B * s.Hq * decode_splits(s.L, s.B, s.Hkv, kDecTargetCus);
+  return align_up(units * sizeof(float2)) + align_up(units * (size_t)s.D * sizeof(float));
+}
+
+template <typename Tag, int D>
+int launch_decode(const Shape &s, const DecodeTables &tb, const aircache_plan_buf *plan, void *ws, hipStream_t st) {
+  const int smax = decode_splits(s.L, s.B, s.Hkv, kDecTargetCus);
+  const size_t units = (size_t)s.L * s.B * s.Hq * smax;
+  float2 *ml = static_cast<float2 *>(ws);
+  float *acc = reinterpret_cast<float *>(static_cast<char *>(ws) + align_up(units * sizeof(float2)));
+  const int64_t cap = (int64_t)s.B * s.Hkv * (int64_t)s.S * s.D;
+  const size_t lds = (size_t)decode_lds_bytes(s.G, D, Tag::kBytes);
+  const long long grid = (long long)s.L * s.B * s.Hkv * smax;
+  if (grid > INT32_MAX) return fail(AIRCACHE_EINVAL, "decode grid of %lld workgroups too large", grid);
+  int rc;
+  if ((rc = allow_lds(decode_partial_kernel<Tag, D>, lds))) return rc;
+  hipLaunchKernelGGL((decode_partial_kernel<Tag, D>), dim3((unsigned)grid), dim3(kDecThreads), lds, st, s, tb,
+                     plan->budget, plan->out_off, cap, smax, ml, acc);
+  if ((rc = check_hip(hipGetLastError(), "decode_partial_kernel launch"))) return rc;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(s.L * s.B * s.Hq)), dim3(D), 0, st, s, tb,
+                     plan->budget, plan->out_off, cap, smax, ml, acc);
+  return check_hip(hipGetLastError(), "decode_combine_kernel launch");
+}
+
 extern "C" {
 
 int aircache_abi_version(void) { return AIRCACHE_ABI_VERSION; }
@@ -1926,6 +1956,43 @@ int aircache_run(const aircache_desc *desc, const void *const *q_txt, const void
 int aircache_compress(const aircache_desc *desc, const aircache_plan_buf *plan, const void *const *k,
                       const void *const *v, void *const *k_out, void *const *v_out, void *stream) {
   return aircache_compress_profiled(desc, plan, k, v, k_out, v_out, stream, nullptr, 0);
+}
+
+size_t aircache_decode_workspace_size(const aircache_desc *desc) {
+  Config cfg;
+  if (make_config(desc, &cfg)) return 0;
+  return decode_ws_bytes(cfg.sh);
+}
+
+int aircache_decode(const aircache_desc *desc, const void *const *q_dec, const aircache_plan_buf *plan,
+                    const void *const *k_out, const void *const *v_out, float *const *o, void *workspace,
+                    size_t ws_bytes, void *stream) {
+  Config cfg;
+  int rc;
+  if ((rc = make_config(desc, &cfg))) return rc;
+  const Shape &s = cfg.sh;
+  if (!plan || !plan->budget || !plan->out_off) return fail(AIRCACHE_EINVAL, "plan, plan->budget or plan->out_off is NULL");
+  if (!aligned16(plan->out_off)) return fail(AIRCACHE_EINVAL, "plan->out_off is not 16-byte aligned");
+  const int esize = desc->dtype == AIRCACHE_BF16 ? 2 : 4;
+  if ((long long)s.G * s.D / 8 > kDecThreads || decode_lds_bytes(s.G, s.D, esize) > kDecMaxLds)
+    return fail(AIRCACHE_EINVAL, "decode holds %d query heads per KV head at most for head_dim %d",
+                kDecThreads * 8 / s.D, s.D);
+  DecodeTables tb;
+  if ((rc = fill_table(q_dec, s.L, &tb.q, "q_dec"))) return rc;
+  if ((rc = fill_table(k_out, s.L, &tb.k, "k_out"))) return rc;
+  if ((rc = fill_table(v_out, s.L, &tb.v, "v_out"))) return rc;
+  LayerTable ot;
+  if ((rc = fill_table(reinterpret_cast<const void *const *>(o), s.L, &ot, "o"))) return rc;
+  for (int l = 0; l < AIRCACHE_MAX_LAYERS; ++l) tb.o.p[l] = const_cast<void *>(ot.p[l]);
+  if (!workspace || ws_bytes < decode_ws_bytes(s))
+    return fail(AIRCACHE_EWORKSPACE, "decode workspace of %zu bytes, %zu needed", ws_bytes, decode_ws_bytes(s));
+  if (!aligned16(workspace)) return fail(AIRCACHE_EINVAL, "workspace is not 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = desc->dtype == AIRCACHE_BF16;
+  if (bf && s.D == 128) return launch_decode<Bf16Tag, 128>(s, tb, plan, workspace, st);
+  if (bf) return launch_decode<Bf16Tag, 64>(s, tb, plan, workspace, st);
+  if (s.D == 128) return launch_decode<F32Tag, 128>(s, tb, plan, workspace, st);
+  return launch_decode<F32Tag, 64>(s, tb, plan, workspace, st);
 }
 
 const char *aircache_strerror(int status) {

@@ -1,0 +1,261 @@
+// Decode attention over the compacted cache, included by aircache.hip inside
+// namespace aircache.
+//
+// The consumer of the compacted per-layer cache: the KV-cache primer page
+// (devpress.csdn.net), section 2.1 "到底缓存什么？", the o_t equation, with
+// one new query per query head and no mask (the incremental step only sees
+// cached positions, section 2.2). For layer l, sample b and query head h with
+// KV head g = h / G, over the n = r_hat[l][b] + N_t rows of head g in the
+// (l, b) segment of the compacted buffers ([H_kv][n][D] at out_off[l][b]):
+//   o[l][b][h] = softmax(q[l][b][h] . K^T / sqrt(D)) V.
+//
+// Split-row decoding: the rows of each (l, b, g) are split evenly over S
+// workgroups (S fixed by the shape, for two workgroups per CU); a workgroup
+// takes its rows in chunks of kDecRows for all G query heads of g at once
+// (every K and V row is read once from HBM), keeping per head a running
+// maximum, sum of exponentials and unnormalised output row (rescaled when the
+// maximum grows). decode_combine_kernel merges the splits of each (l, b, h)
+// in split order. The pass is a stream of K and V
+// rows (HBM-bound; the contraction per row is G x D multiply-adds), so the
+// arithmetic is plain fp32 on the vector units.
+#pragma once
+
+constexpr int kDecThreads = 512;                  // 8 waves, 16 rows each
+constexpr int kDecRows = 16 * (kDecThreads / 64);  // rows of one split
+constexpr int kDecMaxLds = 160 * 1024;  // a CU's LDS (the kernel has no static LDS)
+constexpr int kDecTargetCus = 256;      // the splits are sized for this many CUs
+
+// Widening of stored elements to float (bf16: the 16 bits are the top half).
+template <typename Tag> __device__ __forceinline__ float to_f32(typename Tag::store_t x);
+template <> __device__ __forceinline__ float to_f32<Bf16Tag>(uint16_t x) { return __uint_as_float((unsigned)x << 16); }
+template <> __device__ __forceinline__ float to_f32<F32Tag>(float x) { return x; }
+
+// Eight or four stored elements from one 16-byte piece, widened.
+__device__ __forceinline__ void widen(const u32x4_t &w, float *out, Bf16Tag) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void widen(const u32x4_t &w, float *out, F32Tag) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
+}
+
+struct DecodeTables {
+  LayerTable q, k, v;
+  LayerTableOut o;
+};
+
+// Splits per (l, b, g): enough workgroups for two per CU, whatever the
+// budgets (rows split evenly, each split's rows in chunks of kDecRows).
+__host__ __device__ inline int decode_splits(int L, int B, int Hkv, int cus) {
+  const long long units = (long long)L * B * Hkv;
+  const long long s = (2LL * cus + units - 1) / units;
+  return (int)(s < 1 ? 1 : (s > 64 ? 64 : s));
+}
+
+// Threads per (query head, 8 output elements) of the accumulation: the rows
+// of a chunk are split over them.
+__host__ __device__ inline int decode_parts(int G, int D) {
+  int p = kDecThreads / (G * D / 8);
+  int q = 1;
+  while (q * 2 <= p && q < 16) q *= 2;
+  return q;
+}
+
+// Dynamic LDS of decode_partial_kernel: q of the G heads [G][D] floats,
+// logits then weights [G][kDecRows] floats, per-head running (max, sum,
+// rescale) [G][4] floats, the chunk's V rows, and the parts' accumulators
+// [parts][G][D] floats at the end (over the V rows and weights).
+__host__ __device__ inline int decode_lds_bytes(int G, int D, int esize) {
+  const int main = G * D * 4 + G * kDecRows * 4 + G * 16 + kDecRows * D * esize;
+  const int red = G * D * 4 * decode_parts(G, D) + G * D * 4 + G * 16;
+  return main > red ? main : red;
+}
+
+template <typename Tag, int D>
+__global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(Shape sh, DecodeTables tb,
+                                                                     const int32_t *budget, const int64_t *out_off,
+                                                                     int64_t cap_elems, int S, float2 *part_ml,
+                                                                     float *part_acc) {
+  using E = typename Tag::store_t;
+  constexpr int NT = kDecThreads;
+  constexpr int kPiece = 16 / Tag::kBytes;     // elements per 16-byte piece
+  extern __shared__ __attribute__((aligned(16))) float dec_lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n16 = lane & 15, grp = lane >> 4;
+  const int G = sh.G, Hkv = sh.Hkv, B = sh.B;
+  int rest = blockIdx.x;
+  const int s = rest % S;
+  rest /= S;
+  const int g = rest % Hkv;
+  rest /= Hkv;
+  const int b = rest % B, l = rest / B;
+  const int lb = l * B + b;
+  const int r = budget[lb];
+  const int64_t off = out_off[(size_t)l * (B + 1) + b];
+  const bool ok = r >= 0 && r <= sh.Nv && off >= 0 && off + (int64_t)Hkv * (r + sh.Nt) * D <= cap_elems;
+  const int n = ok ? r + sh.Nt : 0;
+  // this split's rows [lo, hi), an even share of the n rows
+  const int lo = (int)((long long)n * s / S), hi = (int)((long long)n * (s + 1) / S);
+  E *qs = reinterpret_cast<E *>(dec_lds);            // [G][D] as stored (room for floats)
+  float *zp = dec_lds + G * D;                       // [G][kDecRows]
+  float *run = zp + G * kDecRows;                    // [G][4]: max, sum, rescale
+  E *vs = reinterpret_cast<E *>(run + G * 4);        // [kDecRows][D]
+  const E *kseg = static_cast<const E *>(tb.k.p[l]) + (ok ? off + (int64_t)g * n * D : 0);
+  const E *vseg = static_cast<const E *>(tb.v.p[l]) + (ok ? off + (int64_t)g * n * D : 0);
+  const E *qb = static_cast<const E *>(tb.q.p[l]) + ((size_t)b * sh.Hq + (size_t)g * G) * D;
+  // the G query rows into LDS, as stored
+  for (int p = tid; p < G * D / kPiece; p += NT)
+    reinterpret_cast<u32x4_t *>(qs)[p] = reinterpret_cast<const u32x4_t *>(qb)[p];
+  for (int h = tid; h < G; h += NT) {
+    run[h * 4 + 0] = -INFINITY;
+    run[h * 4 + 1] = 0.f;
+  }
+  // accumulation layout: thread (h, e8, part) owns output elements
+  // [8 e8, 8 e8 + 8) of head h over the chunk rows j = part, part + P, ...
+  const int P = decode_parts(G, D);
+  const int oh = tid / (D / 8 * P), orem = tid - oh * (D / 8 * P);
+  const int oe = orem / P, opart = orem - oe * P;
+  const bool owner = oh < G;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  __syncthreads();
+
+  for (int c0 = lo; c0 < hi; c0 += kDecRows) {
+    const int nr = min(kDecRows, hi - c0);
+    // this lane's quarter of key row c0 + 16 wave + n16, and the chunk's V rows
+    const int row = wave * 16 + n16;
+    const bool rv = row < nr;
+    // key fragments of this wave's 16 rows (MFMA A operand: row n16, slice
+    // part grp) and the chunk's V rows; every load issued before the first
+    // is used
+    Frag<Tag> kf[D / 32];
+    {
+      constexpr int VP = kDecRows * D / kPiece / NT;  // V pieces per thread
+      const E *kp = kseg + (size_t)(c0 + (rv ? row : 0)) * D + grp * 8;
+      const u32x4_t *vp = reinterpret_cast<const u32x4_t *>(vseg + (size_t)c0 * D);
+      const int pieces = nr * D / kPiece;
+      u32x4_t vw[VP];
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        if (rv) kf[c].load(kp + c * 32);
+        else kf[c].zero();
+      }
+#pragma unroll
+      for (int i = 0; i < VP; ++i) vw[i] = tid + i * NT < pieces ? vp[tid + i * NT] : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < VP; ++i)
+        if (tid + i * NT < pieces) reinterpret_cast<u32x4_t *>(vs)[tid + i * NT] = vw[i];
+    }
+    // logits (log2 domain) by MFMA, 16 query heads at a time (B operand:
+    // head n16): acc[i] is row 4 grp + i of the wave's 16 against head n16
+    for (int h0 = 0; h0 < G; h0 += 16) {
+      const int hq = min(h0 + n16, G - 1);
+      f32x4_t acc4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        Frag<Tag> qf;
+        qf.load(qs + (size_t)hq * D + c * 32 + grp * 8);
+        mfma_slice(acc4, kf[c], qf);
+      }
+      if (h0 + n16 < G)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rw = wave * 16 + grp * 4 + i;
+          zp[(h0 + n16) * kDecRows + rw] = rw < nr ? acc4[i] * sh.scale2 : -INFINITY;
+        }
+    }
+    __syncthreads();
+    // per head: the running maximum, the chunk's weights, the running sum
+    for (int h = wave; h < G; h += NT / 64) {
+      float *z = zp + h * kDecRows;
+      float m = -INFINITY;
+      for (int j = lane; j < kDecRows; j += 64) m = fmaxf(m, z[j]);
+      m = wave_max(m);
+      const float m_old = run[h * 4 + 0];
+      const float m_new = fmaxf(m_old, m);
+      float t = 0.f;
+      for (int j = lane; j < kDecRows; j += 64) {
+        const float p = z[j] > -INFINITY ? exp2f(z[j] - m_new) : 0.f;
+        z[j] = p;
+        t += p;
+      }
+      t = wave_sum(t);
+      if (lane == 0) {
+        const float sc = m_old > -INFINITY ? exp2f(m_old - m_new) : 0.f;
+        run[h * 4 + 0] = m_new;
+        run[h * 4 + 1] = run[h * 4 + 1] * sc + t;
+        run[h * 4 + 2] = sc;
+      }
+    }
+    __syncthreads();
+    // accumulators rescaled to the new maximum, then weight x V over the
+    // thread's rows of the chunk (one 16-byte V read gives 8 elements)
+    if (owner) {
+      const float sc = run[oh * 4 + 2];
+      const float *p = zp + oh * kDecRows;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= sc;
+      for (int j = opart; j < nr; j += P) {
+        float vv[8];
+        const E *vr = vs + j * D + 8 * oe;
+        if (Tag::kBytes == 2) {
+          widen(*reinterpret_cast<const u32x4_t *>(vr), vv, Tag{});
+        } else {
+          widen(*reinterpret_cast<const u32x4_t *>(vr), vv, Tag{});
+          widen(*reinterpret_cast<const u32x4_t *>(vr + 4), vv + 4, Tag{});
+        }
+        const float pj = p[j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += pj * vv[i];
+      }
+    }
+    __syncthreads();  // vs, zp and the rescale factors are rewritten by the next chunk
+  }
+  // the split's running (max, sum) out, then the parts' accumulators added
+  // in part order (over q, the weights and the V rows, all read by now)
+  for (int h = tid; h < G; h += NT)
+    part_ml[((size_t)lb * sh.Hq + (size_t)g * G + h) * S + s] = make_float2(run[h * 4 + 0], run[h * 4 + 1]);
+  __syncthreads();
+  float *red = dec_lds;  // [P][G][D]
+  if (owner)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[((size_t)opart * G + oh) * D + 8 * oe + i] = acc[i];
+  __syncthreads();
+  for (int i = tid; i < G * D; i += NT) {
+    const int h = i / D, d = i - h * D;
+    float a = 0.f;
+    for (int q = 0; q < P; ++q) a += red[((size_t)q * G + h) * D + d];
+    part_acc[(((size_t)lb * sh.Hq + (size_t)g * G + h) * S + s) * D + d] = a;
+  }
+}
+
+// o[l][b][h] from the splits of (l, b, KV head h / G), merged in split order.
+template <int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(Shape sh, DecodeTables tb, const int32_t *budget,
+                                                           const int64_t *out_off, int64_t cap_elems, int S,
+                                                           const float2 *part_ml, const float *part_acc) {
+  const int d = threadIdx.x;
+  const int h = blockIdx.x % sh.Hq, lb0 = blockIdx.x / sh.Hq;
+  const int B = sh.B, b = lb0 % B, l = lb0 / B, lb = l * B + b;
+  const int r = budget[lb];
+  const int64_t off = out_off[(size_t)l * (B + 1) + b];
+  const bool ok = r >= 0 && r <= sh.Nv && off >= 0 && off + (int64_t)sh.Hkv * (r + sh.Nt) * D <= cap_elems;
+  const int ns = ok ? S : 0;
+  const size_t base = ((size_t)lb * sh.Hq + h) * S;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, part_ml[base + s].x);
+  float Z = 0.f, a = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float2 ml = part_ml[base + s];
+    const float e = ml.x > -INFINITY ? exp2f(ml.x - M) : 0.f;
+    Z += ml.y * e;
+    a += part_acc[(base + s) * D + d] * e;
+  }
+  float *o = static_cast<float *>(tb.o.p[l]) + ((size_t)b * sh.Hq + h) * D;
+  o[d] = a / Z;  // (an invalid segment: 0 / 0)
+}

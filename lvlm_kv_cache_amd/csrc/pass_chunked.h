@@ -354,6 +354,57 @@ __device__ __forceinline__ void elite_logits(const Shape &sh, const typename Tag
 }
 
 
+// The same logits for long text (a wave's U key tiles of one head per batch):
+// for each KV head of g0.. and each query-head tile, the wave loads the query
+// fragments once and key tiles wave, wave + NW, ... U at a time, every load
+// of a batch issued before the first product, so twice the keys of
+// elite_logits are in flight per wave.
+template <typename Tag, int D, int U>
+__device__ __forceinline__ void elite_logits_long(const Shape &sh, const typename Tag::store_t *q,
+                                                  const typename Tag::store_t *k, int b, int g0, int ng, int nht,
+                                                  int nkt, float *z, int head_floats) {
+  using E = typename Tag::store_t;
+  constexpr int NW = kPassWaves;
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, grp = lane >> 4;
+  const int Nt = sh.Nt, G = sh.G, Hkv = sh.Hkv;
+  for (int gl = 0; gl < ng; ++gl)
+    for (int ht = 0; ht < nht; ++ht) {
+      const int g = g0 + gl;
+      const int h = min(ht * 16 + n, G - 1);
+      const E *qrow = q + ((size_t)(b * sh.Hq + g * G + h) * Nt + (Nt - 1)) * D;
+      const E *kbase = k + ((size_t)(b * Hkv + g) * sh.S + sh.Nv) * D;
+      for (int kt0 = wave; kt0 < nkt; kt0 += NW * U) {
+        Frag<Tag> qf[D / 32], kf[U][D / 32];
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) qf[c].load(qrow + c * 32 + grp * 8);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int kt = kt0 + u * NW < nkt ? kt0 + u * NW : kt0;
+          const E *krow = kbase + (size_t)min(kt * 16 + n, Nt - 1) * D;
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c) kf[u][c].load(krow + c * 32 + grp * 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c) mfma_slice(acc, kf[u][c], qf[c]);
+          const int kt = kt0 + u * NW;
+          if (kt < nkt && ht * 16 + n < G) {
+            float *zr = z + (size_t)gl * head_floats + (size_t)(ht * 16 + n) * Nt;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int kk = kt * 16 + grp * 4 + i;
+              if (kk < Nt) zr[kk] = acc[i] * sh.scale2;
+            }
+          }
+        }
+      }
+    }
+}
+
 // One part of the elite window of (layer, sample) lb: KV heads
 // [pi * H_kv / npp, (pi + 1) * H_kv / npp). For every KV head of the part and
 // each of its G query heads, the softmax row of the last text query over the
@@ -390,7 +441,9 @@ __device__ __forceinline__ void elite_part(const Shape &sh, const PassTables &ta
     const int items = ng * per_head;
     const int per_wave = (items + NW - 1) / NW;
     constexpr int UMAX = Tag::kBytes == 4 ? 2 : 4;
-    if (per_wave >= 4) elite_logits<Tag, D, UMAX>(sh, q, k, b, g0, items, per_head, nkt, z, head_floats);
+    if (Tag::kBytes == 2 && nkt >= 8 * NW)
+      elite_logits_long<Tag, D, (Tag::kBytes == 2 ? 8 : 1)>(sh, q, k, b, g0, ng, nht, nkt, z, head_floats);
+    else if (per_wave >= 4) elite_logits<Tag, D, UMAX>(sh, q, k, b, g0, items, per_head, nkt, z, head_floats);
     else if (per_wave >= 2) elite_logits<Tag, D, 2>(sh, q, k, b, g0, items, per_head, nkt, z, head_floats);
     else elite_logits<Tag, D, 1>(sh, q, k, b, g0, items, per_head, nkt, z, head_floats);
     __syncthreads();

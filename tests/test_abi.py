@@ -183,3 +183,23 @@ def test_noalloc_argument_errors(lib):
         _lib.AIRCACHE_EINVAL                                                              # output overlaps input
     d.n_layers = 0
     assert _lib.run_noalloc(d, ok, ok, ok, fake_buf(), ok, ok, 0) == _lib.AIRCACHE_EINVAL
+
+
+def test_decode_workspace_and_argument_errors(lib):
+    """aircache_decode's host-side checks (nothing reaches the device)."""
+    d = desc()
+    assert _lib.decode_workspace_size(d) > 0
+    assert _lib.decode_workspace_size(desc(n_layers=0)) == 0
+    buf = _lib.PlanBuf()
+    fake = [16 * (i + 1) for i in range(28)]
+    # no plan buffers
+    assert _lib.decode(d, fake, buf, fake, fake, fake, 16, 1 << 30, 0) == _lib.AIRCACHE_EINVAL
+    # too many query heads per KV head for one workgroup's LDS
+    big = desc(n_q_heads=66, n_kv_heads=2)
+    buf.budget = 16
+    buf.out_off = 32
+    assert _lib.decode(big, fake, buf, fake, fake, fake, 16, 1 << 30, 0) == _lib.AIRCACHE_EINVAL
+    # workspace too small
+    assert _lib.decode(d, fake, buf, fake, fake, fake, 16, 8, 0) == _lib.AIRCACHE_EWORKSPACE
+    # a NULL layer pointer
+    assert _lib.decode(d, fake[:-1] + [0], buf, fake, fake, fake, 16, 1 << 30, 0) == _lib.AIRCACHE_EINVAL

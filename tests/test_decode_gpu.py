@@ -1,0 +1,141 @@
+"""Decode attention over the compacted cache (aircache_decode) against the
+oracle's decode_attention, on the GPU's own compacted output.
+
+The comparison is conditional on the GPU's plan (budgets, offsets) and
+compacted rows, which the pass's own parity tests check bit for bit; here the
+GPU's float32 decode is held to the oracle's float64 one per element:
+|gpu - ref| <= 2e-4 |ref| + 2e-4 max|ref row|. float32 sums over up to
+N_v + N_t rows of weights in [0, 1] against float64 keep a relative error of
+a few 1e-6 on these inputs; the bound leaves room for the worst-case growth
+of a long sum (n 2^-24 with n up to ~7000 rows).
+"""
+from __future__ import annotations
+
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from parity import make_aircache, to_torch
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 2e-4
+
+
+def _decode_case(w, seed, max_elite=0, layers=None):
+    inp = wl.make_inputs(w, seed)
+    ac = make_aircache(w, max_elite=max_elite)
+    q, k, v = to_torch(inp)
+    plan = ac.alloc_plan()
+    ko, vo = ac.alloc_compacted()
+    ac.run(q, k, v, plan, ko, vo)
+    rng = np.random.default_rng(1000 + seed)
+    qd32 = [(rng.standard_normal((w.B, w.Hq, w.D)) / np.sqrt(w.D) * 4.0).astype(np.float32) for _ in range(w.L)]
+    if w.dtype == wl.BF16:
+        qd_host = [wl.f32_to_bf16_bits(a) for a in qd32]
+        qd = [torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for a in qd_host]
+    else:
+        qd_host = qd32
+        qd = [torch.from_numpy(a).cuda() for a in qd32]
+    print(f"[decode] {w.name} seed {seed} L={w.L} B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} Nv={w.Nv} Nt={w.Nt}",
+          flush=True)
+    o = ac.decode(qd, plan, ko, vo)
+    torch.cuda.synchronize()
+    assert int(plan.status.item()) == 0
+    budget = plan.budget.cpu().numpy()
+    out_off = plan.out_off.cpu().numpy()
+    store = np.float32 if w.dtype == wl.F32 else np.uint16
+
+    def host(t, n):
+        a = t[:n].cpu()
+        if w.dtype == wl.BF16:
+            a = a.view(torch.int16)
+        return a.numpy().view(store)
+
+    layers = range(w.L) if layers is None else layers
+
+    def check(l):
+        n = int(out_off[l, w.B])
+        ref = oracle.decode_attention(w, host(ko[l], n), host(vo[l], n), out_off[l], budget[l], qd_host[l])
+        got = o[l].cpu().numpy().astype(np.float64)
+        scale = np.abs(ref).max(axis=-1, keepdims=True)
+        err = np.abs(got - ref)
+        bad = err > RTOL * np.abs(ref) + RTOL * scale
+        assert not bad.any(), (f"layer {l}: {int(bad.sum())} elements off, max err "
+                               f"{float((err / np.maximum(scale, 1e-30)).max()):.3g} of the row scale")
+        return float((err / np.maximum(scale, 1e-30)).max())
+
+    with ThreadPoolExecutor(8) as ex:
+        worst = max(ex.map(check, layers))
+    print(f"[decode] worst error {worst:.3g} of the row scale", flush=True)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3])
+def test_decode_workload(cid):
+    _decode_case(wl.CONFIGS[cid], wl.parity_seeds(cid)[0])
+
+
+@pytest.mark.parametrize("cid", [4, 5])
+def test_decode_workload_large(cid):
+    """The default elite cap (N_t), full size; every layer checked."""
+    _decode_case(wl.CONFIGS[cid], wl.parity_seeds(cid)[0])
+
+
+EDGE = [
+    dict(Nv=17, Nt=3, Hq=1, Hkv=1, D=64, dtype="f32"),
+    dict(Nv=300, Nt=40, Hq=7, Hkv=1, D=128, dtype="bf16", B=3, L=3),
+    dict(Nv=257, Nt=33, Hq=4, Hkv=4, D=128, dtype="f32", L=2),
+    dict(Nv=129, Nt=17, Hq=32, Hkv=1, D=128, dtype="bf16", L=2),   # G = 32
+    dict(Nv=700, Nt=80, Hq=14, Hkv=7, D=64, dtype="bf16", L=2, B=2),
+    dict(Nv=333, Nt=24, Hq=8, Hkv=2, D=64, dtype="f32", L=3, B=5),
+]
+
+
+@pytest.mark.parametrize("shape", EDGE, ids=lambda s: "x".join(f"{k}{v}" for k, v in s.items()))
+@pytest.mark.parametrize("ratio", [0.0, 0.2, 1.0])
+def test_decode_edge_shapes(shape, ratio):
+    """Budgets of 0 (text rows only), partial and every visual row."""
+    _decode_case(wl.custom(ratio=ratio, **shape), 4)
+
+
+def test_decode_out_of_range_plan_gives_nan_not_a_fault():
+    """A plan whose budget or offset lies outside the buffers (not one this
+    library wrote) makes the kernels' own range checks give NaN rows."""
+    w = wl.custom(Nv=64, Nt=16, Hq=4, Hkv=2, D=64, dtype="bf16", L=2, B=2, ratio=0.25)
+    inp = wl.make_inputs(w, 3)
+    ac = make_aircache(w)
+    q, k, v = to_torch(inp)
+    plan = ac.alloc_plan()
+    ko, vo = ac.alloc_compacted()
+    ac.run(q, k, v, plan, ko, vo)
+    torch.cuda.synchronize()
+    plan.budget[0, 1] = w.Nv + 5          # budget out of range
+    plan.out_off[1, 0] = 1 << 40           # offset past the buffer
+    qd = [torch.randn(w.B, w.Hq, w.D, device="cuda").to(torch.bfloat16) for _ in range(w.L)]
+    o = ac.decode(qd, plan, ko, vo)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[0][1]).all() and torch.isnan(o[1][0]).all()
+    assert torch.isfinite(o[0][0]).all() and torch.isfinite(o[1][1]).all()
+
+
+def test_bound_decode_matches_plain_call():
+    w = wl.custom(Nv=300, Nt=40, Hq=8, Hkv=2, D=128, dtype="bf16", L=2, B=2, ratio=0.2)
+    inp = wl.make_inputs(w, 5)
+    ac = make_aircache(w)
+    q, k, v = to_torch(inp)
+    plan = ac.alloc_plan()
+    ko, vo = ac.alloc_compacted()
+    ac.run(q, k, v, plan, ko, vo)
+    qd = [torch.randn(w.B, w.Hq, w.D, device="cuda").to(torch.bfloat16) for _ in range(w.L)]
+    a = ac.decode(qd, plan, ko, vo)
+    o = [torch.full((w.B, w.Hq, w.D), float("nan"), device="cuda") for _ in range(w.L)]
+    bd = ac.bind_decode(qd, plan, ko, vo, o)
+    b = bd()
+    b = bd()  # twice: the workspace needs no zeroing between calls
+    torch.cuda.synchronize()
+    for l in range(w.L):
+        assert torch.equal(a[l], b[l])
