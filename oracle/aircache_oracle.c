@@ -179,7 +179,11 @@ void orc_layer_stats(const double *iv, int n, double *s_t, double *s_k) {
  * "Layer-wise KV Cache Budget Allocation", the r_hat equation); the variants
  * of that section's allocation ablation table, read as the same equation with
  * one term: 1 uniform, x = ratio * N_v; 2 strength only, x = s't * ratio *
- * N_v; 3 skewness only, x = s'k * ratio * N_v.
+ * N_v; 3 skewness only, x = s'k * ratio * N_v; 4 the pyramid allocation the
+ * table names (budgets falling with depth; the page gives no formula), read
+ * as the plainest linear pyramid with the same mean, x = r 2 (L - l) / (L + 1)
+ * for layer l = 0 .. L - 1 (the sum over layers is L r, the first layer gets
+ * 2 L r / (L + 1), the last 2 r / (L + 1)).
  */
 void orc_budget(const double *s_t, const double *s_k, int L, double ratio, int Nv, int mode,
                 double *x, int32_t *budget) {
@@ -192,7 +196,11 @@ void orc_budget(const double *s_t, const double *s_k, int L, double ratio, int N
   for (int l = 0; l < L; ++l) {
     double stn = s_t[l] * (double)L / st_sum;
     double skn = (u_sum > 0.0) ? (s_k[l] - m) * (double)L / u_sum : 1.0;
-    x[l] = mode == 1 ? r : mode == 2 ? stn * r : mode == 3 ? skn * r : 0.5 * (stn + skn) * r;
+    x[l] = mode == 1   ? r
+           : mode == 2 ? stn * r
+           : mode == 3 ? skn * r
+           : mode == 4 ? r * (double)(2 * (L - l)) / (double)(L + 1)
+                       : 0.5 * (stn + skn) * r;
     double f = floor(x[l]);
     if (!(f > 0.0)) f = 0.0; /* also maps NaN to 0 */
     if (f > (double)Nv) f = (double)Nv;

@@ -309,6 +309,27 @@ def test_budget_rule_is_mean_of_single_terms():
             assert np.array_equal(r, np.clip(np.floor(x), 0, nv).astype(int))
 
 
+# e) pyramid (mode 4, the table's PyramidKV allocation read as a linear
+#    pyramid with the method's mean): L=3, r=0.125*64=8 -> x = 8*2*(3-l)/4 =
+#    [12, 8, 4]; L=1 -> x = r; whatever the statistics; sum L*r; falling with depth
+def test_budget_pyramid_variant():
+    x, r = oracle.budget([1.0, 3.0, 0.5], [5.0, -7.0, 0.0], 0.125, 64, mode=4)
+    assert np.allclose(x, [12.0, 8.0, 4.0], rtol=0, atol=1e-12) and list(r) == [12, 8, 4]
+    x, r = oracle.budget([2.0], [1.0], 0.1, 2880, mode=4)
+    assert np.allclose(x, [288.0], rtol=0, atol=1e-12) and list(r) == [288]
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        L = int(rng.integers(2, 40))
+        ratio, nv = float(rng.uniform(0.01, 0.3)), int(rng.integers(3, 7000))
+        a, ra = oracle.budget(rng.uniform(0.5, 1.0, L), rng.normal(1.0, 2.0, L), ratio, nv, mode=4)
+        b, rb = oracle.budget(rng.uniform(0.5, 1.0, L), rng.normal(1.0, 2.0, L), ratio, nv, mode=4)
+        assert np.array_equal(a, b) and np.array_equal(ra, rb)      # statistics play no part
+        assert abs(a.sum() - L * ratio * nv) <= 1e-9 * L * ratio * nv
+        assert np.all(np.diff(a) < 0)                                 # deeper layers get less
+        r = ratio * nv
+        assert np.allclose(a[[0, -1]], [2 * L * r / (L + 1), 2 * r / (L + 1)], rtol=1e-12)
+
+
 def test_window_select():
     # the window ablation's contiguous windows: the last k text tokens
     assert list(oracle.window_select(128, 16)) == list(range(112, 128))
