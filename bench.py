@@ -50,7 +50,7 @@ def parse():
                          "workloads 3-5 is a stress run with many elite text tokens, not a headline figure)")
     ap.add_argument("--max-elite", type=int, default=64)
     ap.add_argument("--path", default="auto", choices=["auto", "chunked", "tiled", "rows"])
-    ap.add_argument("--budget-mode", default="aircache", choices=["aircache", "uniform", "strength", "skewness"],
+    ap.add_argument("--budget-mode", default="aircache", choices=["aircache", "uniform", "strength", "skewness", "pyramid"],
                     help="layer budget rule: the method's (default) or one of its allocation ablation's variants")
     ap.add_argument("--obs-window", type=int, default=0,
                     help="0: the elite observation window (default); k > 0: the last k text tokens instead")

@@ -110,13 +110,16 @@ typedef struct {
  * 0.5 * (s'_t + s'_k) * r ("Layer-wise KV Cache Budget Allocation", the r_hat
  * equation). The others are the variants that section's allocation ablation
  * compares, read as the same equation with one term or none: UNIFORM (1)
- * r_hat = r, STRENGTH (2) r_hat = s'_t * r, SKEWNESS (3) r_hat = s'_k * r; each
- * floored and clamped to [0, N_v] as the method's. (The ablation's pyramid rule
- * has no formula on the page and is not offered.) */
+ * r_hat = r, STRENGTH (2) r_hat = s'_t * r, SKEWNESS (3) r_hat = s'_k * r, and
+ * PYRAMID (4), the table's pyramid allocation (budgets falling with depth, no
+ * formula on the page), read as the linear pyramid with the method's mean
+ * budget, r_hat = r * 2 (L - l) / (L + 1) for layer l = 0 .. L - 1; each
+ * floored and clamped to [0, N_v] as the method's. */
 #define AIRCACHE_BUDGET_AIRCACHE 0
 #define AIRCACHE_BUDGET_UNIFORM 1
 #define AIRCACHE_BUDGET_STRENGTH 2
 #define AIRCACHE_BUDGET_SKEWNESS 3
+#define AIRCACHE_BUDGET_PYRAMID 4
 
 /* Scoring paths. TILED: column tiles of every (layer, sample, KV head) with
  * the exponentials spilled to the workspace and a separate merge kernel; any
@@ -247,7 +250,7 @@ int aircache_run(const aircache_desc *desc, const void *const *q_txt, const void
  * GPU's scratch: calls that can overlap on one GPU (other streams, other host
  * threads) race and must be serialised by the caller. The remaining arguments
  * are those of aircache_run. */
-#define AIRCACHE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define AIRCACHE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 int aircache_run_noalloc(const aircache_desc *desc, const void *const *q_txt, const void *const *k,
                          const void *const *v, const aircache_plan_buf *plan, void *const *k_out,
                          void *const *v_out, void *stream);

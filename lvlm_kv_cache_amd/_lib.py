@@ -23,7 +23,7 @@ EXPORTS = ["aircache_abi_version", "aircache_workspace_size", "aircache_max_comp
            "aircache_plan", "aircache_compress", "aircache_run", "aircache_plan_profiled",
            "aircache_compress_profiled", "aircache_run_profiled", "aircache_run_noalloc", "aircache_strerror",
            "aircache_last_error", "aircache_decode_workspace_size", "aircache_decode"]
-NOALLOC_SCRATCH_BYTES = 64 << 20  # AIRCACHE_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 128 << 20  # AIRCACHE_NOALLOC_SCRATCH_BYTES
 PLAN_KERNELS = ["elite_select", "cross_score", "finalize", "topk_select"]
 COMPRESS_KERNELS = ["kv_gather"]
 RUN_KERNELS = ["aircache_pass"]

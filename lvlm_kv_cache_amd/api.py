@@ -17,7 +17,7 @@ _DTYPES = {torch.float32: _lib.AIRCACHE_F32, torch.bfloat16: _lib.AIRCACHE_BF16}
 
 _PATHS = {"auto": _lib.PATH_AUTO, "tiled": _lib.PATH_TILED, "rows": _lib.PATH_ROWS, "chunked": _lib.PATH_CHUNKED}
 # layer budget rules: the method's, then its allocation ablation's variants
-_BUDGETS = {"aircache": 0, "uniform": 1, "strength": 2, "skewness": 3}
+_BUDGETS = {"aircache": 0, "uniform": 1, "strength": 2, "skewness": 3, "pyramid": 4}
 
 
 def make_desc(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt, dtype,
@@ -70,7 +70,8 @@ class AirCache:
     alpha: the elite threshold; ratio: r / N_v; max_elite: workspace cap on
     elite tokens (0: N_t); path: "auto", "chunked", "rows" or "tiled";
     budget_mode: "aircache" (the method's layer allocation) or one of its
-    allocation ablation's variants, "uniform", "strength", "skewness";
+    allocation ablation's variants, "uniform", "strength", "skewness",
+    "pyramid";
     obs_window: 0 for the elite observation window, k > 0 for the last k
     text tokens instead (the window ablation's contiguous windows).
     """

@@ -231,7 +231,8 @@ __device__ __forceinline__ BudgetSums budget_sums(int L, const double *st, const
   for (int l = 0; l < L; ++l) r.u_sum += sk[l] - r.mshift;
   return r;
 }
-__device__ __forceinline__ void layer_budget(const Shape &sh, const BudgetSums &r, double st, double sk, double *x_out, int *b_out) {
+__device__ __forceinline__ void layer_budget(const Shape &sh, const BudgetSums &r, int l, double st, double sk,
+                                             double *x_out, int *b_out) {
 #pragma clang fp contract(off)
   const double rr = sh.ratio * (double)sh.Nv;
   const double stn = st * (double)sh.L / r.st_sum;
@@ -241,6 +242,7 @@ __device__ __forceinline__ void layer_budget(const Shape &sh, const BudgetSums &
   const double x = mode == AIRCACHE_BUDGET_UNIFORM    ? rr
                    : mode == AIRCACHE_BUDGET_STRENGTH ? stn * rr
                    : mode == AIRCACHE_BUDGET_SKEWNESS ? skn * rr
+                   : mode == AIRCACHE_BUDGET_PYRAMID  ? rr * (double)(2 * (sh.L - l)) / (double)(sh.L + 1)
                                                       : 0.5 * (stn + skn) * rr;
   double f = floor(x);
   if (!(f > 0.0)) f = 0.0;
@@ -320,7 +322,7 @@ __device__ void finish_layer_sample(const Shape &sh, const PlanPtrs &plan, const
   for (int l = tid; l < L; l += NT) {
     double x;
     int bud;
-    layer_budget(sh, sums, lst[l], lsk[l], &x, &bud);
+    layer_budget(sh, sums, l, lst[l], lsk[l], &x, &bud);
     if (plan.bx) store_coherent(&plan.bx[l * B + b], x);
     store_coherent(&plan.budget[l * B + b], (int32_t)bud);
   }
@@ -1188,7 +1190,7 @@ int make_config(const aircache_desc *d, Config *cfg) {
     return fail(AIRCACHE_EINVAL, "max_elite=%d outside [0, n_txt=%d]", d->max_elite, d->n_txt);
   if (d->path < AIRCACHE_PATH_AUTO || d->path > AIRCACHE_PATH_CHUNKED)
     return fail(AIRCACHE_EINVAL, "path=%d unknown", d->path);
-  if (d->budget_mode < AIRCACHE_BUDGET_AIRCACHE || d->budget_mode > AIRCACHE_BUDGET_SKEWNESS)
+  if (d->budget_mode < AIRCACHE_BUDGET_AIRCACHE || d->budget_mode > AIRCACHE_BUDGET_PYRAMID)
     return fail(AIRCACHE_EINVAL, "budget_mode=%d unknown", d->budget_mode);
   if (d->obs_window < 0) return fail(AIRCACHE_EINVAL, "obs_window=%d < 0", d->obs_window);
   Shape &s = cfg->sh;

@@ -1215,7 +1215,7 @@ __device__ __forceinline__ void sample_budgets(const Shape &sh, const PlanPtrs &
     for (int l = lane; l < L; l += 64) {
       double x;
       int r;
-      layer_budget(sh, sums, st[l], sk[l], &x, &r);
+      layer_budget(sh, sums, l, st[l], sk[l], &x, &r);
       bx[l] = x;
       bud[l] = r;
       if (publish) {

@@ -113,7 +113,7 @@ def test_run_launches(lib):
                                  dict(head_dim=96), dict(n_vis=2), dict(n_vis=9000), dict(n_txt=0),
                                  dict(dtype="x"), dict(alpha=1.5), dict(alpha=float("nan")),
                                  dict(ratio=-0.1), dict(max_elite=129), dict(n_txt=4000), dict(path=4),
-                                 dict(path=2, n_vis=4000), dict(budget_mode=4), dict(budget_mode=-1),
+                                 dict(path=2, n_vis=4000), dict(budget_mode=5), dict(budget_mode=-1),
                                  dict(obs_window=-1)])
 def test_invalid_descriptor(lib, bad):
     if bad.get("dtype") == "x":

@@ -210,7 +210,7 @@ def test_random_shapes(shape, path):
     compare(inp, g, reference(inp, g, alpha=alpha, ratio=ratio), ratio=ratio)
 
 
-_BUDGET_MODES = {"uniform": 1, "strength": 2, "skewness": 3}
+_BUDGET_MODES = {"uniform": 1, "strength": 2, "skewness": 3, "pyramid": 4}
 
 
 @pytest.mark.parametrize("mode", list(_BUDGET_MODES))
