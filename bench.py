@@ -49,7 +49,7 @@ def parse():
                     help="base distribution of the drawn Q/K/V (default: the workload's own; inv_sqrt_d on "
                          "workloads 3-5 is a stress run with many elite text tokens, not a headline figure)")
     ap.add_argument("--max-elite", type=int, default=64)
-    ap.add_argument("--path", default="auto", choices=["auto", "chunked", "tiled", "rows"])
+    ap.add_argument("--path", default="auto", choices=["auto", "small", "chunked", "tiled", "rows"])
     ap.add_argument("--budget-mode", default="aircache", choices=["aircache", "uniform", "strength", "skewness", "pyramid"],
                     help="layer budget rule: the method's (default) or one of its allocation ablation's variants")
     ap.add_argument("--obs-window", type=int, default=0,
@@ -434,7 +434,8 @@ def main():
     else:
         dom, dom_bytes = "cross_score", nbytes["cross_score"]
     dom_gbps = dom_bytes / (kern_us[dom] * 1e-6) / 1e9
-    dom_kernel = {"rows": "cross_score_rows_kernel", "chunked": "aircache_pass_kernel"}.get(path, "cross_score_kernel")
+    dom_kernel = {"rows": "cross_score_rows_kernel", "chunked": "aircache_pass_kernel",
+                  "small": "aircache_small_kernel"}.get(path, "cross_score_kernel")
     # counters are taken on the workload as defined (its own base distribution)
     traffic = (measured_traffic(dom_kernel, w.name)
                if w.base == wl.CONFIGS[a.workload].base and a.budget_mode == "aircache" and a.obs_window == 0

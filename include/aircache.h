@@ -99,7 +99,7 @@ typedef struct {
   double ratio;       /* r / N_v, the retention ratio in [0, 1] */
   int32_t max_elite;  /* workspace cap on elite tokens per (layer, sample); 0 means n_txt */
   int32_t path;       /* scoring kernels: AIRCACHE_PATH_AUTO (0), _TILED (1), _ROWS (2)
-                         or _CHUNKED (3); every path computes the same results */
+                         _CHUNKED (3) or _SMALL (4); every path computes the same results */
   int32_t budget_mode; /* layer allocation rule, AIRCACHE_BUDGET_*; 0 is the method's */
   int32_t obs_window;  /* observation window: 0 the method's elite window; k > 0 the last
                           min(k, n_txt) text tokens instead (the window ablation of the
@@ -132,11 +132,17 @@ typedef struct {
  * where there are more elite rows, and swaps row maxima and sums with the
  * other chunks of its (layer, sample); any n_kv_heads; n_txt <= 1024,
  * n_layers * batch <= 2048 and the per-layer statistics within a CU's LDS.
- * AUTO picks CHUNKED, else ROWS, else TILED. */
+ * SMALL: one workgroup runs the whole pass (and, from aircache_run, the
+ * compaction) sample after sample, for shapes whose keys and text queries of
+ * one sample over all layers fit its LDS with the per-wave buffers
+ * (n_vis <= 512, n_q_heads * n_txt <= 8192, n_layers <= 51): no waits
+ * between workgroups.
+ * AUTO picks SMALL, else CHUNKED, else ROWS, else TILED. */
 #define AIRCACHE_PATH_AUTO 0
 #define AIRCACHE_PATH_TILED 1
 #define AIRCACHE_PATH_ROWS 2
 #define AIRCACHE_PATH_CHUNKED 3
+#define AIRCACHE_PATH_SMALL 4
 
 /* Outputs of aircache_plan; all device pointers, allocated by the caller with
  * the sizes given, written by the library (row-major, [l][b] means index
@@ -172,7 +178,7 @@ size_t aircache_workspace_size(const aircache_desc *desc);
 int64_t aircache_max_compacted_elems(const aircache_desc *desc);
 
 /* The scoring path aircache_plan takes for this descriptor:
- * AIRCACHE_PATH_TILED, _ROWS or _CHUNKED (desc->path AIRCACHE_PATH_AUTO
+ * AIRCACHE_PATH_TILED, _ROWS, _CHUNKED or _SMALL (desc->path AIRCACHE_PATH_AUTO
  * resolved), or -1 for an invalid descriptor (aircache_last_error says why).
  * Host only; no device work. */
 int32_t aircache_resolved_path(const aircache_desc *desc);

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "_build", "libaircache.so")
 AIRCACHE_OK, AIRCACHE_EINVAL, AIRCACHE_EWORKSPACE, AIRCACHE_EHIP = 0, 1, 2, 3
 AIRCACHE_F32, AIRCACHE_BF16 = 0, 1
 AIRCACHE_DEV_ELITE_OVERFLOW, AIRCACHE_DEV_TIMEOUT = 1, 2
-PATH_AUTO, PATH_TILED, PATH_ROWS, PATH_CHUNKED = 0, 1, 2, 3
+PATH_AUTO, PATH_TILED, PATH_ROWS, PATH_CHUNKED, PATH_SMALL = 0, 1, 2, 3, 4
 MAX_LAYERS = 128
 
 EXPORTS = ["aircache_abi_version", "aircache_workspace_size", "aircache_max_compacted_elems",

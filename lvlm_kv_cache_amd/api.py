@@ -15,7 +15,8 @@ from . import _lib
 _DTYPES = {torch.float32: _lib.AIRCACHE_F32, torch.bfloat16: _lib.AIRCACHE_BF16}
 
 
-_PATHS = {"auto": _lib.PATH_AUTO, "tiled": _lib.PATH_TILED, "rows": _lib.PATH_ROWS, "chunked": _lib.PATH_CHUNKED}
+_PATHS = {"auto": _lib.PATH_AUTO, "tiled": _lib.PATH_TILED, "rows": _lib.PATH_ROWS, "chunked": _lib.PATH_CHUNKED,
+          "small": _lib.PATH_SMALL}
 # layer budget rules: the method's, then its allocation ablation's variants
 _BUDGETS = {"aircache": 0, "uniform": 1, "strength": 2, "skewness": 3, "pyramid": 4}
 
@@ -68,7 +69,7 @@ class AirCache:
     return without synchronising.
 
     alpha: the elite threshold; ratio: r / N_v; max_elite: workspace cap on
-    elite tokens (0: N_t); path: "auto", "chunked", "rows" or "tiled";
+    elite tokens (0: N_t); path: "auto", "small", "chunked", "rows" or "tiled";
     budget_mode: "aircache" (the method's layer allocation) or one of its
     allocation ablation's variants, "uniform", "strength", "skewness",
     "pyramid";
@@ -96,9 +97,9 @@ class AirCache:
 
     @property
     def scoring_path(self) -> str:
-        """"tiled", "rows" or "chunked": the scoring path the plan call takes."""
+        """"tiled", "rows", "chunked" or "small": the scoring path the plan call takes."""
         return {_lib.PATH_TILED: "tiled", _lib.PATH_ROWS: "rows",
-                _lib.PATH_CHUNKED: "chunked"}[_lib.resolved_path(self.desc)]
+                _lib.PATH_CHUNKED: "chunked", _lib.PATH_SMALL: "small"}[_lib.resolved_path(self.desc)]
 
     @property
     def run_launches(self) -> int:

@@ -753,6 +753,7 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
 }
 
 #include "pass_chunked.h"
+#include "small.h"
 #include "decode.h"
 
 // ----------------------------------------------------------------------------
@@ -1156,7 +1157,9 @@ struct Config {
   int rows_kt;  // key tiles per wave of cross_score_rows_kernel; 0: the tiled path with spilled exponentials
   int rt_grid, units;
   bool chunked;        // aircache_pass_kernel: the whole pass in one launch
-  int path;            // AIRCACHE_PATH_TILED, _ROWS or _CHUNKED
+  bool small;          // aircache_small_kernel: the whole pass in one workgroup
+  SmallLds slds;
+  int path;            // AIRCACHE_PATH_TILED, _ROWS, _CHUNKED or _SMALL
   // chunked path: schedule facts fixed by the shape, workspace offsets, LDS
   int hgs, nhg, wph, rows, mnch, kcap_lo, nmw;
   size_t off_pass_head, off_parts, off_ecnt, off_emask, off_xrec, off_mom, off_ivrec, off_brec;
@@ -1188,7 +1191,7 @@ int make_config(const aircache_desc *d, Config *cfg) {
   if (!(d->ratio >= 0.0 && d->ratio <= 1.0)) return fail(AIRCACHE_EINVAL, "ratio=%g outside [0, 1]", d->ratio);
   if (d->max_elite < 0 || d->max_elite > d->n_txt)
     return fail(AIRCACHE_EINVAL, "max_elite=%d outside [0, n_txt=%d]", d->max_elite, d->n_txt);
-  if (d->path < AIRCACHE_PATH_AUTO || d->path > AIRCACHE_PATH_CHUNKED)
+  if (d->path < AIRCACHE_PATH_AUTO || d->path > AIRCACHE_PATH_SMALL)
     return fail(AIRCACHE_EINVAL, "path=%d unknown", d->path);
   if (d->budget_mode < AIRCACHE_BUDGET_AIRCACHE || d->budget_mode > AIRCACHE_BUDGET_PYRAMID)
     return fail(AIRCACHE_EINVAL, "budget_mode=%d unknown", d->budget_mode);
@@ -1284,18 +1287,44 @@ int make_config(const aircache_desc *d, Config *cfg) {
   if (d->path == AIRCACHE_PATH_CHUNKED && !cfg->chunked)
     return fail(AIRCACHE_EINVAL, "the chunked path needs n_txt <= 1024, n_layers * batch <= 2048 and an elite cap, "
                 "n_vis and layer count whose records and statistics fit its LDS");
+  // Small path: one sample's keys and text queries of every layer, with the
+  // per-wave buffers, within the one workgroup's LDS; AUTO takes it first.
+  // Waves with layer work: up to eight, fewer when their buffers do not fit.
+  {
+    const int esize = d->dtype == AIRCACHE_BF16 ? 2 : 4;
+    cfg->small = false;
+    if (s.Nv <= kSmallMaxNv && (long long)s.Hq * s.Nt <= kSmallMaxZ && s.L <= kSmallMaxLayers &&
+        5 * s.L <= kPassTableSlots)
+      for (int w = s.L < kSmallWaves ? s.L : kSmallWaves; w >= 1 && !cfg->small; --w) {
+        cfg->slds = small_lds_layout(s.L, s.Hq, s.Hkv, s.D, s.Nv, s.Nt, esize, w);
+        cfg->small = (size_t)cfg->slds.total + 1024 <= kMaxLds;
+      }
+  }
+  if (d->path == AIRCACHE_PATH_SMALL && !cfg->small)
+    return fail(AIRCACHE_EINVAL, "the small path needs one sample's keys and text queries of every layer in LDS, "
+                "n_vis <= %d, n_q_heads * n_txt <= %d and n_layers <= %d", kSmallMaxNv, kSmallMaxZ,
+                kSmallMaxLayers);
+  if (d->path != AIRCACHE_PATH_AUTO && d->path != AIRCACHE_PATH_SMALL) cfg->small = false;
   if (d->path == AIRCACHE_PATH_TILED || d->path == AIRCACHE_PATH_ROWS) cfg->chunked = false;
   if (d->path == AIRCACHE_PATH_TILED || d->path == AIRCACHE_PATH_CHUNKED) cfg->rows_kt = 0;
-  cfg->path = cfg->chunked ? AIRCACHE_PATH_CHUNKED : cfg->rows_kt ? AIRCACHE_PATH_ROWS : AIRCACHE_PATH_TILED;
+  if (cfg->small) cfg->chunked = false, cfg->rows_kt = 0;
+  cfg->path = cfg->small ? AIRCACHE_PATH_SMALL
+              : cfg->chunked ? AIRCACHE_PATH_CHUNKED
+              : cfg->rows_kt ? AIRCACHE_PATH_ROWS
+                             : AIRCACHE_PATH_TILED;
   // aircache_run compacts inside the chunked launch when the five pointer
   // tables fit its table
-  cfg->run_fused = cfg->chunked && 5 * s.L <= kPassTableSlots;
+  cfg->run_fused = (cfg->chunked || cfg->small) && 5 * s.L <= kPassTableSlots;
   cfg->off_cnt = kEpochBytes;
   cfg->off_cnt_elite = cfg->off_cnt + align_up(n_cnt * sizeof(unsigned));
   cfg->off_pbar = cfg->off_cnt_elite + align_up((size_t)s.L * s.B * sizeof(unsigned));
   cfg->off_sched = cfg->off_pbar + align_up((size_t)s.L * s.B * s.Hkv * s.Nt * sizeof(float));
   cfg->off_stats = cfg->off_sched;
-  if (cfg->chunked) {
+  if (cfg->small) {
+    // one workgroup keeps everything in LDS: no workspace beyond the head
+    cfg->ws_bytes = kEpochBytes;
+    cfg->off_e = cfg->off_part = cfg->off_stats = 0;
+  } else if (cfg->chunked) {
     // head at offset 0: the call count (epoch), exit counter, flags, wrap
     // counter; then the records (the other paths' counters are not used)
     const size_t lbs = (size_t)s.L * s.B;
@@ -1546,12 +1575,47 @@ int launch_chunked(const Config &cfg, const LayerTable &qt, const LayerTable &kt
   return check_hip(hipGetLastError(), "aircache_pass_kernel launch");
 }
 
+// The small path: one workgroup, the tables of aircache_pass_kernel (values
+// and compacted outputs only when out is given).
+template <typename Tag, int D>
+int launch_small(const Config &cfg, const LayerTable &qt, const LayerTable &kt, const PlanPtrs &pp, hipStream_t st,
+                 const RunOut *out) {
+  const Shape &s = cfg.sh;
+  auto kern = aircache_small_kernel<Tag, D>;
+  const size_t lds = (size_t)cfg.slds.total;
+  int rc;
+  if ((rc = allow_lds(kern, lds))) return rc;
+  PassTables tab;
+  memset(&tab, 0, sizeof(tab));
+  for (int l = 0; l < s.L; ++l) {
+    tab.p[l] = qt.p[l];
+    tab.p[s.L + l] = kt.p[l];
+    if (out) {
+      tab.p[2 * s.L + l] = out->v->p[l];
+      tab.p[3 * s.L + l] = out->ko->p[l];
+      tab.p[4 * s.L + l] = out->vo->p[l];
+    }
+  }
+  const int64_t cap = (int64_t)s.B * s.Hkv * (int64_t)s.S * s.D;
+  hipLaunchKernelGGL(kern, dim3(1), dim3(kSmallThreads), lds, st, s, tab, pp, out ? 1 : 0, cap, cfg.slds);
+  return check_hip(hipGetLastError(), "aircache_small_kernel launch");
+}
+
 template <typename Tag, int D, int KTW>
 int launch_plan(const Config &cfg, const LayerTable &qt, const LayerTable &kt, const PlanPtrs &pp, const Ws &ws,
                 void *ws_base, hipStream_t st, hipEvent_t *ev) {
   const Shape &s = cfg.sh;
   int rc;
   const unsigned nlb = (unsigned)(s.L * s.B);
+  if (cfg.small) {
+    // the whole plan in one workgroup (the profiled call's other intervals are empty)
+    if ((rc = mark(ev, 0, st))) return rc;
+    if ((rc = mark(ev, 1, st))) return rc;
+    if ((rc = launch_small<Tag, D>(cfg, qt, kt, pp, st, nullptr))) return rc;
+    if ((rc = mark(ev, 2, st))) return rc;
+    if ((rc = mark(ev, 3, st))) return rc;
+    return mark(ev, 4, st);
+  }
   if (cfg.chunked) {
     // elite sets, scoring, statistics, budgets and top-k in one launch (the
     // elite interval of the profiled call is empty)
@@ -1707,7 +1771,12 @@ int run_pass(const Config &cfg, const aircache_desc *desc, const void *const *q_
     }
     const RunOut out{&vt, &kot, &vot};
     int fgrid = 0;
-    if (bf && cfg.sh.D == 128) {
+    if (cfg.small) {
+      if (bf && cfg.sh.D == 128) rc = launch_small<Bf16Tag, 128>(cfg, qt, kt, pp, st, &out);
+      else if (bf) rc = launch_small<Bf16Tag, 64>(cfg, qt, kt, pp, st, &out);
+      else if (cfg.sh.D == 128) rc = launch_small<F32Tag, 128>(cfg, qt, kt, pp, st, &out);
+      else rc = launch_small<F32Tag, 64>(cfg, qt, kt, pp, st, &out);
+    } else if (bf && cfg.sh.D == 128) {
       if (!(rc = pass_grid<Bf16Tag, 128>(cfg, &fgrid)))
         rc = launch_chunked<Bf16Tag, 128>(cfg, qt, kt, pp, workspace, fgrid, st, &out);
     } else if (bf) {
@@ -1840,7 +1909,7 @@ int32_t aircache_run_launches(const aircache_desc *desc) {
   if (make_config(desc, &cfg) != AIRCACHE_OK) return -1;
   if (cfg.run_fused) return 1;
   // aircache_plan's kernels, then kv_gather_kernel
-  return (cfg.chunked ? 1 : cfg.rows_kt ? 3 : 4) + 1;
+  return (cfg.chunked || cfg.small ? 1 : cfg.rows_kt ? 3 : 4) + 1;
 }
 
 int aircache_plan_profiled(const aircache_desc *desc, const void *const *q_txt, const void *const *k,

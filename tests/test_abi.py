@@ -83,6 +83,14 @@ def test_resolved_path(lib):
     assert _lib.resolved_path(desc(path=3, n_kv_heads=7)) == _lib.PATH_CHUNKED
     assert _lib.resolved_path(desc(path=3, n_txt=1100)) == -1
     assert _lib.resolved_path(desc(path=2, n_vis=3073)) == -1
+    # tiny shapes: one workgroup for the whole pass
+    tiny = dict(n_layers=2, n_q_heads=2, n_kv_heads=2, head_dim=64, n_vis=64, n_txt=16, dtype="f32")
+    assert _lib.resolved_path(desc(**tiny)) == _lib.PATH_SMALL
+    assert _lib.resolved_path(desc(path=3, **tiny)) == _lib.PATH_CHUNKED
+    assert _lib.resolved_path(desc(path=4, **tiny)) == _lib.PATH_SMALL
+    assert _lib.run_launches(desc(**tiny)) == 1
+    assert 0 < _lib.workspace_size(desc(**tiny)) <= 256
+    assert _lib.resolved_path(desc(path=4)) == -1           # workload 3 is far beyond 256 KB of keys
 
 
 def test_chunked_workspace_sizes(lib):

@@ -76,12 +76,13 @@ def test_workload_3_flat_attention_stress():
 
 
 @pytest.mark.parametrize("path,cid", [("tiled", 1), ("tiled", 2), ("tiled", 3), ("tiled", 5),
-                                      ("rows", 1), ("rows", 3), ("rows", 5), ("chunked", 4)])
+                                      ("rows", 1), ("rows", 3), ("rows", 5), ("chunked", 4), ("chunked", 1),
+                                      ("chunked-run", 1)])
 def test_workload_other_paths(path, cid):
     """The scoring paths auto does not pick, on the workloads they can serve."""
     print(f"[parity] workload {cid} path {path}", flush=True)
     inp = wl.make_inputs(cid, cid)
-    g = run_gpu(inp, max_elite=0 if cid <= 2 else 64, path=path)
+    g = run_gpu(inp, max_elite=0 if cid <= 2 else 64, path=path.split("-")[0], run=path.endswith("-run"))
     compare(inp, g, reference(inp, g))
 
 
@@ -98,17 +99,79 @@ EDGE = [
 ]
 
 
+def _small_ok(w):
+    from lvlm_kv_cache_amd import _lib, make_desc
+    d = make_desc(w.L, w.B, w.Hq, w.Hkv, w.D, w.Nv, w.Nt, w.dtype, path="small")
+    return _lib.resolved_path(d) == _lib.PATH_SMALL
+
+
 @pytest.mark.parametrize("shape", EDGE, ids=lambda s: "x".join(f"{k}{v}" for k, v in s.items()))
 @pytest.mark.parametrize("seed", [0, 1])
-@pytest.mark.parametrize("path", ["auto", "auto-run", "tiled", "rows"])
+@pytest.mark.parametrize("path", ["auto", "auto-run", "chunked-run", "small", "small-run", "tiled", "rows"])
 def test_edge_shapes(shape, seed, path):
     if path == "rows" and shape["Nv"] > 3072:
         pytest.skip("the rows path serves N_v <= 3072")
+    if path.startswith("small") and not _small_ok(wl.custom(ratio=0.2, **shape)):
+        pytest.skip("the small path serves shapes whose keys and text queries fit its LDS")
     print(f"[parity] edge {shape} seed {seed} path {path}", flush=True)
     w = wl.custom(ratio=0.2, **shape)
     inp = wl.make_inputs(w, seed)
     g = run_gpu(inp, path=path.split("-")[0], run=path.endswith("-run"))
     compare(inp, g, reference(inp, g))
+
+
+SMALL_EDGE = [
+    dict(Nv=40, Nt=8, Hq=2, Hkv=1, D=64, dtype="bf16", L=12, B=2),     # more layers than waves
+    dict(Nv=200, Nt=90, Hq=2, Hkv=1, D=64, dtype="bf16", L=2, B=2),    # N_t over one 64-lane block
+    dict(Nv=500, Nt=12, Hq=4, Hkv=1, D=64, dtype="bf16", L=1, B=3),    # N_v near the rank's limit, G = 4
+    dict(Nv=150, Nt=10, Hq=2, Hkv=1, D=128, dtype="f32", L=1, B=2),
+    dict(Nv=65, Nt=33, Hq=6, Hkv=3, D=128, dtype="bf16", L=1, B=2),    # ragged N_v, three KV heads
+    dict(Nv=3, Nt=1, Hq=1, Hkv=1, D=64, dtype="f32", L=5, B=4),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL_EDGE, ids=lambda s: "x".join(f"{k}{v}" for k, v in s.items()))
+@pytest.mark.parametrize("path", ["small", "small-run", "auto-run"])
+def test_small_shapes(shape, path):
+    """Shapes of the one-workgroup path: layers shared by waves, N_t over a
+    lane block, N_v up to the direct rank's limit, several samples."""
+    w = wl.custom(ratio=0.3, **shape)
+    assert _small_ok(w)
+    print(f"[parity] small {shape} path {path}", flush=True)
+    inp = wl.make_inputs(w, 21)
+    g = run_gpu(inp, path=path.split("-")[0], run=path.endswith("-run"))
+    compare(inp, g, reference(inp, g))
+
+
+@pytest.mark.parametrize("mode", [1, 2, 3, 4])
+def test_small_budget_variants(mode):
+    w = wl.custom(Nv=90, Nt=20, Hq=4, Hkv=2, D=64, dtype="bf16", L=3, B=2, ratio=0.25)
+    assert _small_ok(w)
+    inp = wl.make_inputs(w, 22)
+    g = run_gpu(inp, path="small", run=True, budget_mode=mode)
+    compare(inp, g, reference(inp, g, budget_mode=mode))
+
+
+@pytest.mark.parametrize("window", [4, 20])
+def test_small_observation_windows(window):
+    w = wl.custom(Nv=90, Nt=20, Hq=4, Hkv=2, D=64, dtype="bf16", L=3, B=2, ratio=0.25)
+    inp = wl.make_inputs(w, 23)
+    g = run_gpu(inp, path="small", run=True, obs_window=window)
+    assert (g["n_elite"] == window).all()
+    compare(inp, g, reference(inp, g, obs_window=window))
+
+
+def test_small_all_text_elite_and_overflow():
+    """Zero queries: every text token elite (N_t = 70, over one lane block);
+    then an elite cap below N_t flags the overflow."""
+    w = wl.custom(Nv=120, Nt=70, Hq=2, Hkv=1, D=64, dtype="bf16", L=3, B=2, ratio=0.2)
+    assert _small_ok(w)
+    inp = wl.make_inputs(w, 24, zero_q=True)
+    g = run_gpu(inp, path="small", run=True)
+    assert (g["n_elite"] == 70).all()
+    compare(inp, g, reference(inp, g))
+    g = run_gpu(inp, path="small", max_elite=16, compress=False)
+    assert g["status"][0] == 1
 
 
 @pytest.mark.parametrize("path", ["auto", "auto-run", "tiled", "rows"])
@@ -196,9 +259,10 @@ def _random_shapes(n, seed=2024):
 
 
 @pytest.mark.parametrize("shape", _random_shapes(20), ids=lambda s: "x".join(f"{k}{v}" for k, v in s.items()))
-@pytest.mark.parametrize("path", ["auto-run", "rows"])
+@pytest.mark.parametrize("path", ["auto-run", "chunked-run", "rows"])
 def test_random_shapes(shape, path):
-    """Seeded random small shapes on the one-launch pass and the rows path."""
+    """Seeded random small shapes on the automatic path (small or one-launch),
+    the one-launch pass and the rows path."""
     if path == "rows" and shape["Nv"] > 3072:
         pytest.skip("the rows path serves N_v <= 3072")
     print(f"[parity] random {shape} path {path}", flush=True)
