@@ -56,6 +56,12 @@ def lib():
         l.orc_topk.restype = None
         l.orc_gather.argtypes = [C.POINTER(Desc), P, C.c_int, P, C.c_int, P]
         l.orc_gather.restype = None
+        l.orc_cross_score_groups.argtypes = [C.POINTER(Desc), P, P, C.c_int, P, C.c_int, P]
+        l.orc_cross_score_groups.restype = None
+        l.orc_gather_groups.argtypes = [C.POINTER(Desc), P, C.c_int, P, C.c_int, C.c_int, P]
+        l.orc_gather_groups.restype = None
+        l.orc_quantize_i8.argtypes = [P, C.c_int, C.c_size_t, P, P]
+        l.orc_quantize_i8.restype = None
         l.orc_decode_attention.argtypes = [C.POINTER(Desc), P, P, C.c_int, P, P]
         l.orc_decode_attention.restype = None
         l.orc_run.argtypes = [C.POINTER(Desc)] + [P] * 15
@@ -113,6 +119,16 @@ def cross_score(w, q_l, k_l, b: int, elite) -> np.ndarray:
     return iv
 
 
+def cross_score_groups(w, q_l, k_l, b: int, elite) -> np.ndarray:
+    """Step 2 per KV head (group-wise selection): I_v^g as [H_kv][N_v] float64."""
+    _check_inputs(w, q_l, k_l)
+    d = desc_of(w)
+    el = np.ascontiguousarray(elite, dtype=np.int32)
+    iv = np.zeros((w.Hkv, w.Nv), np.float64)
+    lib().orc_cross_score_groups(C.byref(d), _ptr(q_l), _ptr(k_l), b, _ptr(el), len(el), _ptr(iv))
+    return iv
+
+
 def layer_stats(iv) -> tuple[float, float]:
     """Step 3: (s_t, s_k) of one I_v vector."""
     a = np.ascontiguousarray(iv, dtype=np.float64)
@@ -149,6 +165,26 @@ def gather(w, src_l: np.ndarray, b: int, kept) -> np.ndarray:
     out = np.zeros((w.Hkv, len(kept) + w.Nt, w.D), dtype=src_l.dtype)
     lib().orc_gather(C.byref(d), _ptr(src_l), b, _ptr(kept), len(kept), _ptr(out))
     return out
+
+
+def gather_groups(w, src_l: np.ndarray, b: int, kept_g) -> np.ndarray:
+    """Step 6 with per-KV-head kept lists kept_g [H_kv][k]: [H_kv][k + N_t][D]."""
+    kept_g = np.ascontiguousarray(kept_g, dtype=np.int32).reshape(w.Hkv, -1)
+    k = kept_g.shape[1]
+    d = desc_of(w)
+    out = np.zeros((w.Hkv, k + w.Nt, w.D), dtype=src_l.dtype)
+    lib().orc_gather_groups(C.byref(d), _ptr(src_l), b, _ptr(kept_g), max(k, 0), k, _ptr(out))
+    return out
+
+
+def quantize_i8(seg, dtype: str):
+    """int8 quantisation of one head's kept cache: (codes int8[n], scale).
+    seg holds float32 values (dtype "f32") or bfloat16 bit patterns ("bf16")."""
+    a = np.ascontiguousarray(seg)
+    codes = np.zeros(max(a.size, 1), np.int8)
+    sc = C.c_float()
+    lib().orc_quantize_i8(_ptr(a), 0 if dtype == "f32" else 1, a.size, _ptr(codes), C.addressof(sc))
+    return codes[:a.size].reshape(a.shape), sc.value
 
 
 def decode_attention_segment(w, k_seg, v_seg, n: int, q) -> np.ndarray:

@@ -33,7 +33,13 @@
  *  - top-r selection by I_v, equal scores go to the lower index, kept indices
  *    are emitted in ascending order;
  *  - compacted layout per (layer, sample, KV head): kept visual rows in
- *    ascending order, then all text rows, samples packed one after another.
+ *    ascending order, then all text rows, samples packed one after another;
+ *  - the per-KV-head selection (group-wise top-K) keeps each KV head's own
+ *    top-r_hat by the I_v of its query heads, with the layer's budget r_hat
+ *    set from the I_v over all query heads as in the shared selection;
+ *  - int8 quantisation of the kept cache: symmetric range [-127, 127], one
+ *    scale per (layer, sample, KV head) for K and one for V, codes rounded
+ *    half to even in float32.
  */
 #include <math.h>
 #include <stdint.h>
@@ -137,6 +143,35 @@ void orc_cross_score(const orc_desc *w, const void *q_l, const void *k_l, int b,
     }
   }
   for (int i = 0; i < w->Nv; ++i) iv[i] /= (double)w->Hq * (double)ntk;
+  free(z);
+}
+
+/*
+ * Step 2 with one selection per KV head (the group-wise top-K of the
+ * edge-device survey page, section 10.1 on GQA/MQA: the query heads that
+ * share a KV head decide together). For KV head g, I_v^g[i] is the mean,
+ * over the G query heads h with h / G = g and the elite rows j, of the
+ * probability at visual column i of the same row softmax as orc_cross_score.
+ * iv_g: [H_kv][N_v].
+ */
+void orc_cross_score_groups(const orc_desc *w, const void *q_l, const void *k_l, int b,
+                            const int32_t *elite, int ntk, double *iv_g) {
+  const int G = w->Hq / w->Hkv;
+  const int ncol = w->Nv + ntk;
+  double *z = (double *)malloc(sizeof(double) * (size_t)ncol);
+  for (int i = 0; i < w->Hkv * w->Nv; ++i) iv_g[i] = 0.0;
+  for (int h = 0; h < w->Hq; ++h) {
+    int g = h / G;
+    double *row_sum = iv_g + (size_t)g * w->Nv;
+    for (int e = 0; e < ntk; ++e) {
+      int jq = elite[e];
+      for (int c = 0; c < w->Nv; ++c) z[c] = logit(w, q_l, k_l, b, h, jq, g, c);
+      for (int e2 = 0; e2 < ntk; ++e2) z[w->Nv + e2] = logit(w, q_l, k_l, b, h, jq, g, w->Nv + elite[e2]);
+      softmax(z, ncol);
+      for (int i = 0; i < w->Nv; ++i) row_sum[i] += z[i];
+    }
+  }
+  for (int i = 0; i < w->Hkv * w->Nv; ++i) iv_g[i] /= (double)G * (double)ntk;
   free(z);
 }
 
@@ -262,6 +297,62 @@ void orc_gather(const orc_desc *w, const void *src_l, int b, const int32_t *kept
       dst += row;
     }
   }
+}
+
+/*
+ * Step 6 with one selection per KV head: as orc_gather, with head g's kept
+ * visual rows read from kept_g + g * kept_stride (k of them, in the order
+ * given).
+ */
+void orc_gather_groups(const orc_desc *w, const void *src_l, int b, const int32_t *kept_g, int kept_stride,
+                       int k, void *out_seg) {
+  const size_t esz = (w->dtype == 0) ? 4 : 2;
+  const size_t row = (size_t)w->D * esz;
+  const char *src = (const char *)src_l;
+  char *dst = (char *)out_seg;
+  for (int g = 0; g < w->Hkv; ++g) {
+    const int32_t *kept = kept_g + (size_t)g * kept_stride;
+    for (int i = 0; i < k; ++i) {
+      memcpy(dst, src + k_index(w, b, g, kept[i]) * esz, row);
+      dst += row;
+    }
+    for (int j = 0; j < w->Nt; ++j) {
+      memcpy(dst, src + k_index(w, b, g, w->Nv + j) * esz, row);
+      dst += row;
+    }
+  }
+}
+
+/*
+ * int8 quantisation of one head's kept cache, after the token compression
+ * (the UniCache blog, section 6.3 on stacking quantisation with compression:
+ * compress first, then quantise; one scale per head, the head's largest
+ * absolute value over the quantisation range). The page fixes neither the
+ * range nor the rounding; read as the symmetric range [-127, 127], scale
+ * s = max|x| / 127 and code q = round-half-to-even(x / s), with s = 0 and
+ * every code 0 for an all-zero head. The quantised code is an integer
+ * decided by floating point, so it is decided in float32 (the inputs are
+ * float32, or bfloat16, which widens to float32 exactly): one float32
+ * division per element, correctly rounded, then rintf.
+ * seg: n elements in the descriptor's dtype; codes: n int8; *scale: s.
+ */
+void orc_quantize_i8(const void *seg, int dtype, size_t n, int8_t *codes, float *scale) {
+  float m = 0.0f;
+  for (size_t i = 0; i < n; ++i) {
+    const float x = (float)elem(seg, i, dtype);
+    const float a = x < 0.0f ? -x : x;
+    if (a > m) m = a;
+  }
+  const float s = m / 127.0f;
+  for (size_t i = 0; i < n; ++i) {
+    const float x = (float)elem(seg, i, dtype);
+    float q = 0.0f;
+    if (s > 0.0f) q = rintf(x / s);
+    if (q > 127.0f) q = 127.0f;
+    if (q < -127.0f) q = -127.0f;
+    codes[i] = (int8_t)q;
+  }
+  *scale = s;
 }
 
 /*

@@ -170,6 +170,58 @@ def test_cross_score_only_elite_text_columns_in_denominator():
     assert np.array_equal(iv0, iv2)
 
 
+# ---------------------------------------------- step 2, per KV head (f4) ----
+
+def library_iv_groups(w, inp, b, elite):
+    """I_v per KV head from numpy matrix products and scipy's softmax: the
+    rows of the G query heads that share KV head g, averaged."""
+    G = w.Hq // w.Hkv
+    out = np.zeros((w.Hkv, w.Nv))
+    for g in range(w.Hkv):
+        K = inp.as_f32("k")[0, b, g].astype(np.float64)
+        cols = np.concatenate([K[:w.Nv], K[w.Nv + np.asarray(elite, int)]])
+        for h in range(g * G, (g + 1) * G):
+            Qe = inp.as_f32("q")[0, b, h][np.asarray(elite, int)].astype(np.float64)
+            P = scipy.special.softmax(Qe @ cols.T / math.sqrt(w.D), axis=1)
+            out[g] += P[:, :w.Nv].sum(0)
+    return out / (G * len(elite))
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("shape", [dict(Hq=6, Hkv=2), dict(Hq=4, Hkv=4, dtype="bf16"), dict(Hq=8, Hkv=2)])
+def test_cross_score_groups_matches_library_softmax(seed, shape):
+    w, inp = tiny(seed, Nv=15, Nt=7, D=32, B=2, **shape)
+    for b in range(2):
+        el, _ = oracle.elite_select(w, inp.q[0], inp.k[0], b, alpha=0.5)
+        ivg = oracle.cross_score_groups(w, inp.q[0], inp.k[0], b, el)
+        assert np.allclose(ivg, library_iv_groups(w, inp, b, el), rtol=1e-12, atol=0)
+        # the heads' scores differ (the selection is per head for a reason)
+        assert not np.allclose(ivg[0], ivg[1])
+
+
+def test_cross_score_groups_one_kv_head_is_the_shared_score():
+    w, inp = tiny(3, Nv=20, Nt=6, D=16, Hq=5, Hkv=1)
+    el, _ = oracle.elite_select(w, inp.q[0], inp.k[0], 0, alpha=0.3)
+    ivg = oracle.cross_score_groups(w, inp.q[0], inp.k[0], 0, el)
+    assert np.array_equal(ivg[0], oracle.cross_score(w, inp.q[0], inp.k[0], 0, el))
+
+
+def test_cross_score_groups_average_to_the_shared_score():
+    # equal head groups: the mean over KV heads of I_v^g is I_v
+    w, inp = tiny(4, Nv=11, Nt=5, D=16, Hq=6, Hkv=3, B=1)
+    el = np.array([1, 4], np.int32)
+    ivg = oracle.cross_score_groups(w, inp.q[0], inp.k[0], 0, el)
+    iv = oracle.cross_score(w, inp.q[0], inp.k[0], 0, el)
+    assert np.allclose(ivg.mean(0), iv, rtol=1e-13, atol=0)
+
+
+def test_cross_score_groups_uniform_when_queries_are_zero():
+    w = wl.custom(Nv=10, Nt=4, Hq=4, Hkv=2, D=16)
+    inp = wl.make_inputs(w, 1, zero_q=True)
+    ivg = oracle.cross_score_groups(w, inp.q[0], inp.k[0], 0, np.arange(4, dtype=np.int32))
+    assert np.allclose(ivg, 1.0 / 14, rtol=1e-14, atol=0)
+
+
 # ---------------------------------------------------------------- step 3 ----
 
 @pytest.mark.parametrize("n", [3, 4, 64, 576, 2880])
@@ -402,6 +454,67 @@ def test_gather_layout_and_text_rows():
                 assert np.array_equal(seg[g, :r], inp.k[l, b, g, kept])
                 assert np.array_equal(seg[g, r:], inp.k[l, b, g, 12:])
         assert out["out_off"][l, 2] == sum(2 * (int(out["budget"][l, b]) + 3) * 8 for b in range(2))
+
+
+def test_gather_groups_layout_per_head():
+    w = wl.custom(Nv=10, Nt=3, Hq=4, Hkv=2, D=8, B=2)
+    inp = wl.make_inputs(w, 12)
+    kept = np.array([[1, 4, 9], [0, 2, 3]], np.int32)
+    for b in range(2):
+        seg = oracle.gather_groups(w, inp.k[0], b, kept)
+        for g in range(2):
+            assert np.array_equal(seg[g, :3], inp.k[0, b, g, kept[g]])
+            assert np.array_equal(seg[g, 3:], inp.k[0, b, g, 10:])
+    # one list for every head: the shared gather
+    same = np.array([[2, 5], [2, 5]], np.int32)
+    assert np.array_equal(oracle.gather_groups(w, inp.v[0], 1, same), oracle.gather(w, inp.v[0], 1, same[0]))
+    # no visual row kept: the text rows only
+    assert np.array_equal(oracle.gather_groups(w, inp.k[0], 0, np.zeros((2, 0), np.int32)), inp.k[0, 0, :, 10:])
+
+
+# -------------------------------------------- int8 quantisation (f4) ----
+
+def test_quantize_exact_multiples_of_the_scale():
+    # max |x| = 127 / 8, so s = 1/8 exactly and x = k / 8 has code k
+    k = np.arange(-127, 128, dtype=np.float64)
+    x = (k / 8.0).astype(np.float32)
+    codes, s = oracle.quantize_i8(x, "f32")
+    assert s == 0.125
+    assert np.array_equal(codes.astype(np.int64), k.astype(np.int64))
+
+
+def test_quantize_ties_round_half_to_even():
+    x = np.array([127, 2.5, 3.5, -2.5, 0.5, -0.5, 1.5, -1.5, 126.5], np.float64) / 8.0
+    codes, s = oracle.quantize_i8(x.astype(np.float32), "f32")
+    assert s == 0.125
+    assert codes.tolist() == [127, 2, 4, -2, 0, 0, 2, -2, 126]
+
+
+def test_quantize_all_zero_head():
+    codes, s = oracle.quantize_i8(np.zeros(40, np.float32), "f32")
+    assert s == 0.0 and not codes.any()
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_quantize_error_bound_and_extremes(seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(3000) * rng.uniform(0.1, 10)).astype(np.float32)
+    codes, s = oracle.quantize_i8(x, "f32")
+    i = int(np.argmax(np.abs(x)))
+    assert abs(int(codes[i])) == 127 and np.sign(codes[i]) == np.sign(x[i])
+    assert np.isclose(s, np.abs(x).max() / 127, rtol=1e-7)
+    assert codes.min() >= -127 and codes.max() <= 127
+    err = np.abs(codes.astype(np.float64) * s - x.astype(np.float64))
+    assert err.max() <= s * (0.5 + 1e-5)
+
+
+def test_quantize_bf16_is_its_float32_value():
+    rng = np.random.default_rng(9)
+    bits = wl.f32_to_bf16_bits(rng.standard_normal(500).astype(np.float32))
+    as_f32 = (bits.astype(np.uint32) << 16).view(np.float32)
+    c16, s16 = oracle.quantize_i8(bits, "bf16")
+    c32, s32 = oracle.quantize_i8(as_f32, "f32")
+    assert s16 == s32 and np.array_equal(c16, c32)
 
 
 # ------------------------------------------------------------ end to end ----
