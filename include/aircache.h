@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define AIRCACHE_ABI_VERSION 1
+#define AIRCACHE_ABI_VERSION 2
 #define AIRCACHE_MAX_LAYERS 128
 
 typedef enum {
@@ -104,7 +104,22 @@ typedef struct {
   int32_t obs_window;  /* observation window: 0 the method's elite window; k > 0 the last
                           min(k, n_txt) text tokens instead (the window ablation of the
                           "Elite Observation Window" section: 16, 32, or all text tokens) */
+  int32_t select_mode; /* AIRCACHE_SELECT_*: one selection per (layer, sample), the method's
+                          (0), or one per KV head (1) */
 } aircache_desc;
+
+/* Visual-token selection granularity. SHARED (0): the method's, one top-r_hat
+ * per (layer, sample) by I_v over all query heads. PER_KV_HEAD (1): the
+ * group-wise top-K of the edge-device survey page (section 10.1 on GQA/MQA,
+ * the query heads that share a KV head decide together): KV head g keeps its
+ * own top-r_hat by I_v^g, the mean over its G query heads and the elite rows
+ * of the same row softmax; the budget r_hat is still set from the I_v over all
+ * query heads (plan->iv, s_t, s_k as in SHARED), so every KV head of a
+ * (layer, sample) keeps the same number of rows and the compacted layout is
+ * unchanged. Served by the TILED and SMALL paths (AUTO picks between them);
+ * ROWS and CHUNKED reject it. */
+#define AIRCACHE_SELECT_SHARED 0
+#define AIRCACHE_SELECT_PER_KV_HEAD 1
 
 /* Layer budget allocation rules. AIRCACHE (0): the method's, r_hat =
  * 0.5 * (s'_t + s'_k) * r ("Layer-wise KV Cache Budget Allocation", the r_hat
@@ -157,8 +172,11 @@ typedef struct {
   int32_t *budget;    /* [L][B] r_hat, in [0, N_v] */
   int64_t *out_off;   /* [L][B+1] element offset of each sample's segment in the layer's
                          compacted buffer; out_off[l][B] is the layer's total element count */
-  int32_t *kept_idx;  /* [L][B][N_v] kept visual indices, ascending; first budget valid */
+  int32_t *kept_idx;  /* [L][B][N_v] kept visual indices, ascending; first budget valid;
+                         [L][B][H_kv][N_v] with select_mode PER_KV_HEAD */
   int32_t *status;    /* [1] AIRCACHE_DEV_* bits, reset by every aircache_plan call */
+  float *iv_head;     /* [L][B][H_kv][N_v] I_v^g per KV head; written (and required) with
+                         select_mode PER_KV_HEAD, not read otherwise (may be NULL) */
 } aircache_plan_buf;
 
 /* Library version (AIRCACHE_ABI_VERSION). */
@@ -239,6 +257,27 @@ int aircache_compress(const aircache_desc *desc, const aircache_plan_buf *plan,
 int aircache_run(const aircache_desc *desc, const void *const *q_txt, const void *const *k, const void *const *v,
                  const aircache_plan_buf *plan, void *const *k_out, void *const *v_out, void *workspace,
                  size_t ws_bytes, void *stream);
+
+/* int8 quantisation of the compacted cache, one scale per (layer, sample, KV
+ * head) for K and one for V, after the token compression (the UniCache blog,
+ * section 6.3 on stacking quantisation with compression: compress first,
+ * then quantise; a per-head scale, the head's largest absolute value over the
+ * quantisation range). Read as the symmetric range [-127, 127]: per head
+ * segment x (its r_hat + n_txt rows of the compacted layout), s = max|x| / 127
+ * and code = round-half-to-even(x / s), both in float32 (one correctly
+ * rounded division each), s = 0 and every code 0 for an all-zero segment;
+ * the value is code * s.
+ *   plan        : budget and out_off as written by aircache_plan
+ *   k_out, v_out: the compacted buffers of aircache_compress / aircache_run
+ *   kq, vq      : host arrays of n_layers device pointers to int8 buffers of
+ *                 out_off[l][B] bytes, the same layout as k_out / v_out
+ *                 (16-byte aligned)
+ *   k_scale, v_scale: device float buffers [L][B][H_kv]
+ * Segments whose budget or offset lie outside the buffers (a plan this
+ * library did not write) are skipped. */
+int aircache_quantize_i8(const aircache_desc *desc, const aircache_plan_buf *plan, const void *const *k_out,
+                         const void *const *v_out, int8_t *const *kq, int8_t *const *vq, float *k_scale,
+                         float *v_scale, void *stream);
 
 /* aircache_run for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the

@@ -16,13 +16,14 @@ AIRCACHE_OK, AIRCACHE_EINVAL, AIRCACHE_EWORKSPACE, AIRCACHE_EHIP = 0, 1, 2, 3
 AIRCACHE_F32, AIRCACHE_BF16 = 0, 1
 AIRCACHE_DEV_ELITE_OVERFLOW, AIRCACHE_DEV_TIMEOUT = 1, 2
 PATH_AUTO, PATH_TILED, PATH_ROWS, PATH_CHUNKED, PATH_SMALL = 0, 1, 2, 3, 4
+SELECT_SHARED, SELECT_PER_KV_HEAD = 0, 1
 MAX_LAYERS = 128
 
 EXPORTS = ["aircache_abi_version", "aircache_workspace_size", "aircache_max_compacted_elems",
            "aircache_resolved_path", "aircache_run_launches",
            "aircache_plan", "aircache_compress", "aircache_run", "aircache_plan_profiled",
            "aircache_compress_profiled", "aircache_run_profiled", "aircache_run_noalloc", "aircache_strerror",
-           "aircache_last_error", "aircache_decode_workspace_size", "aircache_decode"]
+           "aircache_last_error", "aircache_decode_workspace_size", "aircache_decode", "aircache_quantize_i8"]
 NOALLOC_SCRATCH_BYTES = 128 << 20  # AIRCACHE_NOALLOC_SCRATCH_BYTES
 PLAN_KERNELS = ["elite_select", "cross_score", "finalize", "topk_select"]
 COMPRESS_KERNELS = ["kv_gather"]
@@ -34,12 +35,12 @@ class Desc(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("n_vis", C.c_int32),
                 ("n_txt", C.c_int32), ("dtype", C.c_int32), ("alpha", C.c_double),
                 ("ratio", C.c_double), ("max_elite", C.c_int32), ("path", C.c_int32),
-                ("budget_mode", C.c_int32), ("obs_window", C.c_int32)]
+                ("budget_mode", C.c_int32), ("obs_window", C.c_int32), ("select_mode", C.c_int32)]
 
 
 class PlanBuf(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("elite_idx", "n_elite", "iv", "s_t", "s_k", "budget_x",
-                                          "budget", "out_off", "kept_idx", "status")]
+                                          "budget", "out_off", "kept_idx", "status", "iv_head")]
 
 
 class AirCacheError(RuntimeError):
@@ -89,6 +90,8 @@ def load() -> C.CDLL:
         lib.aircache_decode_workspace_size.argtypes = [C.POINTER(Desc)]
         lib.aircache_decode.restype = C.c_int
         lib.aircache_decode.argtypes = [C.POINTER(Desc), P, C.POINTER(PlanBuf), P, P, P, P, C.c_size_t, P]
+        lib.aircache_quantize_i8.restype = C.c_int
+        lib.aircache_quantize_i8.argtypes = [C.POINTER(Desc), C.POINTER(PlanBuf), P, P, P, P, P, P, P]
         lib.aircache_strerror.restype = C.c_char_p
         lib.aircache_strerror.argtypes = [C.c_int]
         lib.aircache_last_error.restype = C.c_char_p
@@ -169,3 +172,10 @@ def decode(desc: Desc, q_ptrs, buf: PlanBuf, ko_ptrs, vo_ptrs, o_ptrs, ws_ptr: i
     q, ko, vo, o = [ptr_array(p) if p is not None else None for p in (q_ptrs, ko_ptrs, vo_ptrs, o_ptrs)]
     return load().aircache_decode(C.byref(desc), q, C.byref(buf), ko, vo, o, C.c_void_p(ws_ptr), ws_bytes,
                                   C.c_void_p(stream))
+
+
+def quantize_i8(desc: Desc, buf: PlanBuf, ko_ptrs, vo_ptrs, kq_ptrs, vq_ptrs, k_scale: int, v_scale: int,
+                stream: int) -> int:
+    ko, vo, kq, vq = [ptr_array(p) for p in (ko_ptrs, vo_ptrs, kq_ptrs, vq_ptrs)]
+    return load().aircache_quantize_i8(C.byref(desc), C.byref(buf), ko, vo, kq, vq, C.c_void_p(k_scale),
+                                       C.c_void_p(v_scale), C.c_void_p(stream))

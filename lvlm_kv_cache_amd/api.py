@@ -19,17 +19,21 @@ _PATHS = {"auto": _lib.PATH_AUTO, "tiled": _lib.PATH_TILED, "rows": _lib.PATH_RO
           "small": _lib.PATH_SMALL}
 # layer budget rules: the method's, then its allocation ablation's variants
 _BUDGETS = {"aircache": 0, "uniform": 1, "strength": 2, "skewness": 3, "pyramid": 4}
+# visual-token selection: one per (layer, sample), the method's, or one per KV head
+_SELECT = {"shared": _lib.SELECT_SHARED, "per_kv_head": _lib.SELECT_PER_KV_HEAD}
 
 
 def make_desc(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt, dtype,
-              alpha=0.9, ratio=0.1, max_elite=0, path="auto", budget_mode=0, obs_window=0) -> _lib.Desc:
+              alpha=0.9, ratio=0.1, max_elite=0, path="auto", budget_mode=0, obs_window=0,
+              select="shared") -> _lib.Desc:
     if isinstance(dtype, torch.dtype):
         dtype = _DTYPES[dtype]
     elif isinstance(dtype, str):
         dtype = {"f32": _lib.AIRCACHE_F32, "bf16": _lib.AIRCACHE_BF16}[dtype]
     return _lib.Desc(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt, dtype,
                      float(alpha), float(ratio), int(max_elite), _PATHS[path] if isinstance(path, str) else int(path),
-                     _BUDGETS[budget_mode] if isinstance(budget_mode, str) else int(budget_mode), int(obs_window))
+                     _BUDGETS[budget_mode] if isinstance(budget_mode, str) else int(budget_mode), int(obs_window),
+                     _SELECT[select] if isinstance(select, str) else int(select))
 
 
 @dataclasses.dataclass
@@ -42,22 +46,28 @@ class PlanOutputs:
     budget_x: torch.Tensor   # float64 [L, B]
     budget: torch.Tensor     # int32 [L, B]
     out_off: torch.Tensor    # int64 [L, B + 1]
-    kept_idx: torch.Tensor   # int32 [L, B, N_v]
+    kept_idx: torch.Tensor   # int32 [L, B, N_v], or [L, B, H_kv, N_v] with one selection per KV head
     status: torch.Tensor     # int32 [1]
+    iv_head: torch.Tensor | None = None  # float32 [L, B, H_kv, N_v] with one selection per KV head
 
     @classmethod
-    def empty(cls, L, B, Nv, Nt, device) -> "PlanOutputs":
+    def empty(cls, L, B, Nv, Nt, device, per_kv_head: int = 0) -> "PlanOutputs":
+        """per_kv_head: H_kv for one selection per KV head, else 0."""
         i32 = dict(dtype=torch.int32, device=device)
         f64 = dict(dtype=torch.float64, device=device)
+        sel = (per_kv_head,) if per_kv_head else ()
         return cls(elite_idx=torch.empty(L, B, Nt, **i32), n_elite=torch.empty(L, B, **i32),
                    iv=torch.empty(L, B, Nv, dtype=torch.float32, device=device),
                    s_t=torch.empty(L, B, **f64), s_k=torch.empty(L, B, **f64),
                    budget_x=torch.empty(L, B, **f64), budget=torch.empty(L, B, **i32),
                    out_off=torch.empty(L, B + 1, dtype=torch.int64, device=device),
-                   kept_idx=torch.empty(L, B, Nv, **i32), status=torch.zeros(1, **i32))
+                   kept_idx=torch.empty(L, B, *sel, Nv, **i32), status=torch.zeros(1, **i32),
+                   iv_head=torch.empty(L, B, per_kv_head, Nv, dtype=torch.float32, device=device)
+                   if per_kv_head else None)
 
     def buf(self) -> _lib.PlanBuf:
-        return _lib.PlanBuf(*[getattr(self, f.name).data_ptr() for f in dataclasses.fields(self)])
+        ptr = lambda t: 0 if t is None else t.data_ptr()
+        return _lib.PlanBuf(*[ptr(getattr(self, f.name)) for f in dataclasses.fields(self)])
 
 
 class AirCache:
@@ -74,12 +84,14 @@ class AirCache:
     allocation ablation's variants, "uniform", "strength", "skewness",
     "pyramid";
     obs_window: 0 for the elite observation window, k > 0 for the last k
-    text tokens instead (the window ablation's contiguous windows).
+    text tokens instead (the window ablation's contiguous windows);
+    select: "shared" (one selection per layer and sample, the method's) or
+    "per_kv_head" (each KV head its own top-r_hat, the group-wise top-K).
     """
 
     def __init__(self, n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt,
                  dtype=torch.bfloat16, alpha=0.9, ratio=0.1, max_elite=0, device="cuda", path="auto",
-                 budget_mode="aircache", obs_window=0):
+                 budget_mode="aircache", obs_window=0, select="shared"):
         self.shape = dict(L=n_layers, B=batch, Hq=n_q_heads, Hkv=n_kv_heads, D=head_dim,
                           Nv=n_vis, Nt=n_txt)
         self.dtype = dtype
@@ -87,7 +99,8 @@ class AirCache:
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
         self.desc = make_desc(n_layers, batch, n_q_heads, n_kv_heads, head_dim, n_vis, n_txt,
-                              dtype, alpha, ratio, max_elite, path, budget_mode, obs_window)
+                              dtype, alpha, ratio, max_elite, path, budget_mode, obs_window, select)
+        self.per_kv_head = self.desc.select_mode == _lib.SELECT_PER_KV_HEAD
         ws = _lib.workspace_size(self.desc)
         if ws == 0:
             _lib.check(_lib.AIRCACHE_EINVAL)
@@ -139,7 +152,8 @@ class AirCache:
     # -- calls -------------------------------------------------------------
     def alloc_plan(self) -> PlanOutputs:
         s = self.shape
-        return PlanOutputs.empty(s["L"], s["B"], s["Nv"], s["Nt"], self.device)
+        return PlanOutputs.empty(s["L"], s["B"], s["Nv"], s["Nt"], self.device,
+                                 s["Hkv"] if self.per_kv_head else 0)
 
     def plan(self, q_txt, k, out: PlanOutputs | None = None, stream=None, events=None) -> PlanOutputs:
         """events: optional list of 5 torch.cuda.Event (timing=True) recorded
@@ -206,6 +220,38 @@ class AirCache:
                                [t.data_ptr() for t in o], self.dec_workspace.data_ptr(), need,
                                self._stream(stream)))
         return o
+
+    def quantize_i8(self, plan: PlanOutputs, k_out, v_out, kq=None, vq=None, k_scale=None, v_scale=None,
+                    stream=None):
+        """int8 codes of the compacted cache with one float32 scale per
+        (layer, sample, KV head) for K and for V (aircache_quantize_i8).
+        Returns (kq, vq, k_scale, v_scale); kq / vq per layer int8 with the
+        compacted layout, scales [L, B, H_kv]; allocated when not given."""
+        s = self.shape
+        self._check_outputs(k_out, v_out)
+        cap = _lib.max_compacted_elems(self.desc)
+        if kq is None:
+            kq = [torch.empty(cap, dtype=torch.int8, device=self.device) for _ in range(s["L"])]
+        if vq is None:
+            vq = [torch.empty(cap, dtype=torch.int8, device=self.device) for _ in range(s["L"])]
+        for name, ts in (("kq", kq), ("vq", vq)):
+            if len(ts) != s["L"] or any(t.dtype != torch.int8 or t.device != self.device or not t.is_contiguous()
+                                        or t.numel() < cap for t in ts):
+                raise ValueError(f"{name}: {s['L']} contiguous int8 tensors on {self.device} of at least "
+                                 f"{cap} elements expected")
+        if k_scale is None:
+            k_scale = torch.empty(s["L"], s["B"], s["Hkv"], dtype=torch.float32, device=self.device)
+        if v_scale is None:
+            v_scale = torch.empty(s["L"], s["B"], s["Hkv"], dtype=torch.float32, device=self.device)
+        for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if t.dtype != torch.float32 or t.device != self.device or not t.is_contiguous() or \
+                    t.numel() != s["L"] * s["B"] * s["Hkv"]:
+                raise ValueError(f"{name} must be a contiguous float32 [L, B, H_kv] tensor on {self.device}")
+        _lib.check(_lib.quantize_i8(self.desc, plan.buf(), [t.data_ptr() for t in k_out],
+                                    [t.data_ptr() for t in v_out], [t.data_ptr() for t in kq],
+                                    [t.data_ptr() for t in vq], k_scale.data_ptr(), v_scale.data_ptr(),
+                                    self._stream(stream)))
+        return kq, vq, k_scale, v_scale
 
     def bind_decode(self, q_dec, plan: PlanOutputs, k_out, v_out, o, stream=None) -> "BoundDecode":
         """A BoundDecode running decode() on these tensors with the checks and

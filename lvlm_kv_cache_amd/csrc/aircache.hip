@@ -38,6 +38,8 @@ struct Shape {
   double ratio;
   int budget_mode;  // AIRCACHE_BUDGET_*
   int window;       // 0: the elite window; k > 0: the last k text tokens (k <= N_t)
+  int nsel;         // selections per (layer, sample): 1, or H_kv (one per KV head)
+  int per_head;     // one selection per KV head (I_v^g written to plan.iv_head)
 };
 
 struct PlanPtrs {
@@ -47,6 +49,7 @@ struct PlanPtrs {
   int32_t *budget;
   int64_t *out_off;
   int32_t *kept, *status;
+  float *iv_head;  // [L][B][H_kv][N_v] I_v per KV head when nsel == H_kv
 };
 
 struct Ws {
@@ -393,12 +396,15 @@ __global__ __launch_bounds__(256) void finalize_kernel(Shape sh, PlanPtrs plan, 
   __syncthreads();
   const float inv_rows = (ntk > 0) ? 1.f / (float)(sh.Hq * ntk) : 0.f;
   const int c0 = t * sh.T, c1 = min(sh.Nv, c0 + sh.T);
+  // one selection per KV head: I_v^g over the G query heads of KV head g
+  const float inv_grp = (ntk > 0) ? 1.f / (float)(sh.G * ntk) : 0.f;
   for (int c = c0 + tid; c < c1; c += 256) {
     float acc = 0.f;
     for (int g = 0; g < sh.Hkv; ++g) {
       const f32x4_t *e4 =
           reinterpret_cast<const f32x4_t *>(ws.e + (size_t)(lb * sh.Hkv + g) * sh.Nv * sh.rcap16 + (size_t)c * RP);
       const f32x4_t *w4 = reinterpret_cast<const f32x4_t *>(wl + g * RP);
+      float ag = 0.f;
       for (int r0 = 0; r0 < RP / 4; r0 += 4) {  // RP is a multiple of 16
         f32x4_t ev[4];
 #pragma unroll
@@ -406,12 +412,14 @@ __global__ __launch_bounds__(256) void finalize_kernel(Shape sh, PlanPtrs plan, 
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const f32x4_t wv = w4[r0 + j];
-          acc += ev[j].x * wv.x;
-          acc += ev[j].y * wv.y;
-          acc += ev[j].z * wv.z;
-          acc += ev[j].w * wv.w;
+          ag += ev[j].x * wv.x;
+          ag += ev[j].y * wv.y;
+          ag += ev[j].z * wv.z;
+          ag += ev[j].w * wv.w;
         }
       }
+      if (sh.per_head) plan.iv_head[((size_t)lb * sh.Hkv + g) * sh.Nv + c] = ag * inv_grp;
+      acc += ag;
     }
     store_coherent(&plan.iv[(size_t)lb * sh.Nv + c], acc * inv_rows);
   }
@@ -968,11 +976,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(Shape sh, Pla
   __shared__ unsigned wmin[kTopkWaves], wmax[kTopkWaves];
   __shared__ unsigned sel_digit, sel_above;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lb = blockIdx.x;
+  // one workgroup per (layer, sample), or per (layer, sample, KV head) with
+  // one selection per KV head (scores I_v^g, the same budget)
+  const int lb = blockIdx.x / sh.nsel, gsel = blockIdx.x - lb * sh.nsel;
   const int Nv = sh.Nv;
-  if (tid == 0 && plan.n_elite[lb] > sh.cap) atomicOr(plan.status, AIRCACHE_DEV_ELITE_OVERFLOW);
+  if (tid == 0 && gsel == 0 && plan.n_elite[lb] > sh.cap) atomicOr(plan.status, AIRCACHE_DEV_ELITE_OVERFLOW);
   const int kbud = plan.budget[lb];
-  int32_t *kept = plan.kept + (size_t)lb * Nv;
+  int32_t *kept = plan.kept + (size_t)blockIdx.x * Nv;
+  const float *scores = sh.per_head ? plan.iv_head + (size_t)blockIdx.x * Nv : plan.iv + (size_t)lb * Nv;
   const int per = (Nv + kTopkThreads - 1) / kTopkThreads;
   const int i0 = min(Nv, tid * per), i1 = min(Nv, i0 + per);
   if (kbud <= 0) return;
@@ -985,7 +996,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(Shape sh, Pla
 #pragma unroll
   for (int p = 0; p < kTopkPer; ++p) {
     const int i = i0 + p;
-    key[p] = (i < i1) ? __float_as_uint(plan.iv[(size_t)lb * Nv + i]) : 0u;
+    key[p] = (i < i1) ? __float_as_uint(scores[i]) : 0u;
     if (i < i1) {
       kmin = min(kmin, key[p]);
       kmax = max(kmax, key[p]);
@@ -1115,7 +1126,7 @@ __global__ __launch_bounds__(256) void kv_gather_kernel(Shape sh, GatherTables t
   const char *vs = static_cast<const char *>(tb.v.p[l]) + src_base;
   char *kd = static_cast<char *>(tb.ko.p[l]) + dst_base;
   char *vd = static_cast<char *>(tb.vo.p[l]) + dst_base;
-  const int32_t *kept = plan.kept + (size_t)lb * sh.Nv;
+  const int32_t *kept = plan.kept + ((size_t)lb * sh.nsel + (sh.nsel > 1 ? g : 0)) * sh.Nv;
   const int sub = tid % LPR;
   for (int p = r0 + tid / LPR; p < r1; p += RPI) {
     const int srow = (p < bud) ? kept[p] : sh.Nv + (p - bud);
@@ -1124,6 +1135,91 @@ __global__ __launch_bounds__(256) void kv_gather_kernel(Shape sh, GatherTables t
     const u32x4_t vv = reinterpret_cast<const u32x4_t *>(vs + (size_t)srow * RB)[sub];
     store_nt(reinterpret_cast<u32x4_t *>(kd + (size_t)p * RB) + sub, kv);
     store_nt(reinterpret_cast<u32x4_t *>(vd + (size_t)p * RB) + sub, vv);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// int8 quantisation of the compacted cache (the UniCache blog, section 6.3:
+// compress first, then quantise, one scale per head). One workgroup per
+// (layer, sample, KV head, K or V) segment of the compacted layout: the
+// segment's largest absolute value, s = max / 127, then codes
+// rint(x / s) clamped to [-127, 127], both divisions correctly rounded in
+// float32. 16 elements per thread step: one 16-byte store of codes.
+// ----------------------------------------------------------------------------
+struct QuantTables {
+  LayerTable ko, vo;
+  LayerTableOut kq, vq;
+};
+
+template <typename Tag>
+__device__ __forceinline__ void load16_as_f32(const typename Tag::store_t *p, float (&x)[16]);
+template <> __device__ __forceinline__ void load16_as_f32<F32Tag>(const float *p, float (&x)[16]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x4_t v = reinterpret_cast<const f32x4_t *>(p)[j];
+    x[4 * j] = v.x;
+    x[4 * j + 1] = v.y;
+    x[4 * j + 2] = v.z;
+    x[4 * j + 3] = v.w;
+  }
+}
+template <> __device__ __forceinline__ void load16_as_f32<Bf16Tag>(const uint16_t *p, float (&x)[16]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const u32x4_t v = reinterpret_cast<const u32x4_t *>(p)[j];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[8 * j + 2 * e] = __uint_as_float(v[e] << 16);
+      x[8 * j + 2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+    }
+  }
+}
+
+template <typename Tag>
+__global__ __launch_bounds__(256) void quantize_i8_kernel(Shape sh, QuantTables tb, PlanPtrs plan, float *k_scale,
+                                                          float *v_scale, int64_t cap_elems) {
+  using E = typename Tag::store_t;
+  __shared__ float wmax[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kv = blockIdx.x & 1, u = blockIdx.x >> 1;
+  const int g = u % sh.Hkv, lb = u / sh.Hkv, l = lb / sh.B, b = lb - (lb / sh.B) * sh.B;
+  const int bud = plan.budget[lb];
+  if (bud < 0 || bud > sh.Nv) return;  // not a budget written by aircache_plan
+  const int n = bud + sh.Nt;
+  const int64_t seg0 = plan.out_off[(size_t)l * (sh.B + 1) + b];
+  if (seg0 < 0 || seg0 + (int64_t)sh.Hkv * n * sh.D > cap_elems) return;
+  const size_t base = (size_t)seg0 + (size_t)g * n * sh.D, cnt16 = (size_t)n * sh.D / 16;
+  const E *src = static_cast<const E *>(kv ? tb.vo.p[l] : tb.ko.p[l]) + base;
+  int8_t *dst = static_cast<int8_t *>(kv ? tb.vq.p[l] : tb.kq.p[l]) + base;
+  float m = 0.f;
+  for (size_t p = tid; p < cnt16; p += 256) {
+    float x[16];
+    load16_as_f32<Tag>(src + 16 * p, x);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(x[j]));
+  }
+  m = wave_max(m);
+  if (lane == 0) wmax[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float sc = __fdiv_rn(m, 127.0f);
+  if (tid == 0) (kv ? v_scale : k_scale)[(size_t)lb * sh.Hkv + g] = sc;
+  for (size_t p = tid; p < cnt16; p += 256) {
+    float x[16];
+    load16_as_f32<Tag>(src + 16 * p, x);
+    u32x4_t out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      unsigned word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float q = sc > 0.f ? rintf(__fdiv_rn(x[4 * w + j], sc)) : 0.f;
+        q = fminf(fmaxf(q, -127.f), 127.f);
+        word |= ((unsigned)(int)q & 0xffu) << (8 * j);
+      }
+      out[w] = word;
+    }
+    store_nt(reinterpret_cast<u32x4_t *>(dst + 16 * p), out);
   }
 }
 
@@ -1196,6 +1292,11 @@ int make_config(const aircache_desc *d, Config *cfg) {
   if (d->budget_mode < AIRCACHE_BUDGET_AIRCACHE || d->budget_mode > AIRCACHE_BUDGET_PYRAMID)
     return fail(AIRCACHE_EINVAL, "budget_mode=%d unknown", d->budget_mode);
   if (d->obs_window < 0) return fail(AIRCACHE_EINVAL, "obs_window=%d < 0", d->obs_window);
+  if (d->select_mode != AIRCACHE_SELECT_SHARED && d->select_mode != AIRCACHE_SELECT_PER_KV_HEAD)
+    return fail(AIRCACHE_EINVAL, "select_mode=%d unknown", d->select_mode);
+  const bool per_head = d->select_mode == AIRCACHE_SELECT_PER_KV_HEAD;
+  if (per_head && (d->path == AIRCACHE_PATH_ROWS || d->path == AIRCACHE_PATH_CHUNKED))
+    return fail(AIRCACHE_EINVAL, "one selection per KV head is served by the tiled and small paths");
   Shape &s = cfg->sh;
   s.L = d->n_layers;
   s.B = d->batch;
@@ -1221,6 +1322,8 @@ int make_config(const aircache_desc *d, Config *cfg) {
   s.ratio = d->ratio;
   s.budget_mode = d->budget_mode;
   s.window = d->obs_window < d->n_txt ? d->obs_window : d->n_txt;
+  s.nsel = per_head ? s.Hkv : 1;
+  s.per_head = per_head ? 1 : 0;
   const int esz = d->dtype == AIRCACHE_BF16 ? 2 : 4;
   (void)esz;
   cfg->elite_lds = (size_t)(s.G > 1 ? s.G : 1) * s.Nt * sizeof(float);
@@ -1296,7 +1399,7 @@ int make_config(const aircache_desc *d, Config *cfg) {
     if (s.Nv <= kSmallMaxNv && (long long)s.Hq * s.Nt <= kSmallMaxZ && s.L <= kSmallMaxLayers &&
         5 * s.L <= kPassTableSlots)
       for (int w = s.L < kSmallWaves ? s.L : kSmallWaves; w >= 1 && !cfg->small; --w) {
-        cfg->slds = small_lds_layout(s.L, s.Hq, s.Hkv, s.D, s.Nv, s.Nt, esize, w);
+        cfg->slds = small_lds_layout(s.L, s.Hq, s.Hkv, s.D, s.Nv, s.Nt, esize, w, s.nsel);
         cfg->small = (size_t)cfg->slds.total + 1024 <= kMaxLds;
       }
   }
@@ -1305,6 +1408,7 @@ int make_config(const aircache_desc *d, Config *cfg) {
                 "n_vis <= %d, n_q_heads * n_txt <= %d and n_layers <= %d", kSmallMaxNv, kSmallMaxZ,
                 kSmallMaxLayers);
   if (d->path != AIRCACHE_PATH_AUTO && d->path != AIRCACHE_PATH_SMALL) cfg->small = false;
+  if (per_head) cfg->chunked = false, cfg->rows_kt = 0;
   if (d->path == AIRCACHE_PATH_TILED || d->path == AIRCACHE_PATH_ROWS) cfg->chunked = false;
   if (d->path == AIRCACHE_PATH_TILED || d->path == AIRCACHE_PATH_CHUNKED) cfg->rows_kt = 0;
   if (cfg->small) cfg->chunked = false, cfg->rows_kt = 0;
@@ -1654,7 +1758,7 @@ int launch_plan(const Config &cfg, const LayerTable &qt, const LayerTable &kt, c
     if ((rc = check_hip(hipGetLastError(), "finalize_kernel launch"))) return rc;
   }
   if ((rc = mark(ev, 3, st))) return rc;
-  hipLaunchKernelGGL(topk_select_kernel, dim3(nlb), dim3(kTopkThreads), 0, st, s, pp);
+  hipLaunchKernelGGL(topk_select_kernel, dim3(nlb * (unsigned)s.nsel), dim3(kTopkThreads), 0, st, s, pp);
   if ((rc = check_hip(hipGetLastError(), "topk_select_kernel launch"))) return rc;
   return mark(ev, 4, st);
 }
@@ -1671,15 +1775,18 @@ PlanPtrs plan_ptrs(const aircache_plan_buf *p) {
   q.out_off = p->out_off;
   q.kept = p->kept_idx;
   q.status = p->status;
+  q.iv_head = p->iv_head;
   return q;
 }
 
-int check_plan_buf(const aircache_plan_buf *p, bool for_compress) {
+int check_plan_buf(const aircache_plan_buf *p, bool for_compress, const Config &cfg) {
   if (!p) return fail(AIRCACHE_EINVAL, "plan is NULL");
   if (!p->budget || !p->out_off || !p->kept_idx) return fail(AIRCACHE_EINVAL, "plan budget/out_off/kept_idx NULL");
   if (for_compress) return AIRCACHE_OK;
   if (!p->elite_idx || !p->n_elite || !p->iv || !p->s_t || !p->s_k || !p->status)
     return fail(AIRCACHE_EINVAL, "a required plan output pointer is NULL");
+  if (cfg.sh.per_head && !p->iv_head)
+    return fail(AIRCACHE_EINVAL, "plan iv_head is NULL (one selection per KV head writes it)");
   return AIRCACHE_OK;
 }
 
@@ -1749,7 +1856,7 @@ int run_pass(const Config &cfg, const aircache_desc *desc, const void *const *q_
              const void *const *v, const aircache_plan_buf *plan, void *const *k_out, void *const *v_out,
              void *workspace, size_t ws_bytes, hipStream_t st, hipEvent_t *ev) {
   int rc;
-  if ((rc = check_plan_buf(plan, false))) return rc;
+  if ((rc = check_plan_buf(plan, false, cfg))) return rc;
   if (!workspace || ws_bytes < cfg.ws_bytes)
     return fail(AIRCACHE_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0,
                 cfg.ws_bytes);
@@ -1921,7 +2028,7 @@ int aircache_plan_profiled(const aircache_desc *desc, const void *const *q_txt, 
   Config cfg;
   int rc;
   if ((rc = make_config(desc, &cfg))) return rc;
-  if ((rc = check_plan_buf(plan, false))) return rc;
+  if ((rc = check_plan_buf(plan, false, cfg))) return rc;
   if (!workspace || ws_bytes < cfg.ws_bytes)
     return fail(AIRCACHE_EWORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? ws_bytes : 0,
                 cfg.ws_bytes);
@@ -1953,7 +2060,7 @@ int aircache_compress_profiled(const aircache_desc *desc, const aircache_plan_bu
   Config cfg;
   int rc;
   if ((rc = make_config(desc, &cfg))) return rc;
-  if ((rc = check_plan_buf(plan, true))) return rc;
+  if ((rc = check_plan_buf(plan, true, cfg))) return rc;
   GatherTables tb;
   if ((rc = gather_tables(cfg, k, v, k_out, v_out, &tb))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -1987,7 +2094,7 @@ int aircache_run_noalloc(const aircache_desc *desc, const void *const *q_txt, co
                 "(use aircache_run with a workspace)", cfg.ws_bytes, kScratchBytes);
   // validate everything before the scratch is touched, so a rejected call
   // leaves it as the last accepted call left it
-  if ((rc = check_plan_buf(plan, false))) return rc;
+  if ((rc = check_plan_buf(plan, false, cfg))) return rc;
   {
     LayerTable t;
     GatherTables tb;
@@ -2064,6 +2171,37 @@ int aircache_decode(const aircache_desc *desc, const void *const *q_dec, const a
   if (bf) return launch_decode<Bf16Tag, 64>(s, tb, plan, workspace, st);
   if (s.D == 128) return launch_decode<F32Tag, 128>(s, tb, plan, workspace, st);
   return launch_decode<F32Tag, 64>(s, tb, plan, workspace, st);
+}
+
+int aircache_quantize_i8(const aircache_desc *desc, const aircache_plan_buf *plan, const void *const *k_out,
+                         const void *const *v_out, int8_t *const *kq, int8_t *const *vq, float *k_scale,
+                         float *v_scale, void *stream) {
+  Config cfg;
+  int rc;
+  if ((rc = make_config(desc, &cfg))) return rc;
+  const Shape &s = cfg.sh;
+  if (!plan || !plan->budget || !plan->out_off) return fail(AIRCACHE_EINVAL, "plan, plan->budget or plan->out_off is NULL");
+  if (!k_scale || !v_scale) return fail(AIRCACHE_EINVAL, "k_scale or v_scale is NULL");
+  QuantTables tb;
+  if ((rc = fill_table(k_out, s.L, &tb.ko, "k_out"))) return rc;
+  if ((rc = fill_table(v_out, s.L, &tb.vo, "v_out"))) return rc;
+  LayerTable a, c;
+  if ((rc = fill_table(reinterpret_cast<const void *const *>(kq), s.L, &a, "kq"))) return rc;
+  if ((rc = fill_table(reinterpret_cast<const void *const *>(vq), s.L, &c, "vq"))) return rc;
+  for (int l = 0; l < AIRCACHE_MAX_LAYERS; ++l) {
+    tb.kq.p[l] = const_cast<void *>(a.p[l]);
+    tb.vq.p[l] = const_cast<void *>(c.p[l]);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t cap = (int64_t)s.B * s.Hkv * s.S * s.D;
+  const dim3 grid((unsigned)(2 * s.L * s.B * s.Hkv));
+  if (desc->dtype == AIRCACHE_BF16)
+    hipLaunchKernelGGL(quantize_i8_kernel<Bf16Tag>, grid, dim3(256), 0, st, s, tb, plan_ptrs(plan), k_scale,
+                       v_scale, cap);
+  else
+    hipLaunchKernelGGL(quantize_i8_kernel<F32Tag>, grid, dim3(256), 0, st, s, tb, plan_ptrs(plan), k_scale,
+                       v_scale, cap);
+  return check_hip(hipGetLastError(), "quantize_i8_kernel launch");
 }
 
 const char *aircache_strerror(int status) {

@@ -32,7 +32,8 @@ constexpr int kSmallMaxLayers = 51;
 // (whole LDS-DMA instructions); after the scoring the same bytes hold the
 // waves' rank keys [W][N_v rounded up to 64]. Per wave: elite logits
 // [H_q][N_t], head maxima and inverse sums [2][H_q], the elite list [N_t].
-// Then I_v [L][N_v] (then the kept indices), statistics [L + 16] doubles x 2,
+// Then I_v [L][nsel][N_v] (per KV head with one selection per KV head; then
+// the kept indices), statistics [L + 16] doubles x 2,
 // budgets [L + 16], layer offsets [L] and the five layer pointer tables
 // [5 L].
 struct SmallLds {
@@ -41,7 +42,7 @@ struct SmallLds {
   int kall, qall, keys, z, hm, el, ivl, st, bud, off, ptr, total;
 };
 __host__ __device__ inline SmallLds small_lds_layout(int L, int Hq, int Hkv, int D, int Nv, int Nt, int esize,
-                                                     int W) {
+                                                     int W, int nsel) {
   SmallLds f;
   long long o = 0;
   auto take = [&](long long bytes) {
@@ -61,7 +62,7 @@ __host__ __device__ inline SmallLds small_lds_layout(int L, int Hq, int Hkv, int
   f.z = take((long long)W * Hq * Nt * 4);
   f.hm = take((long long)W * Hq * 8);
   f.el = take((long long)W * Nt * 4);
-  f.ivl = take((long long)L * Nv * 4);
+  f.ivl = take((long long)L * nsel * Nv * 4);
   f.st = take((L + 16) * 8 * 2);
   f.bud = take((L + 16) * 4);
   f.off = take(L * 8);
@@ -143,7 +144,8 @@ __global__ __launch_bounds__(kSmallThreads) void aircache_small_kernel(Shape sh,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = sh.L, B = sh.B, Hq = sh.Hq, Hkv = sh.Hkv, G = sh.G, Nv = sh.Nv, Nt = sh.Nt, S = sh.S;
   const int W = lo.waves, nk = (Nv + 63) / 64 * 64;
-  float *ivl = reinterpret_cast<float *>(lds + lo.ivl);  // [L][N_v]; then the kept indices
+  float *ivl = reinterpret_cast<float *>(lds + lo.ivl);  // [L][nsel][N_v]; then the kept indices
+  const int nsel = sh.nsel;
   double *st = reinterpret_cast<double *>(lds + lo.st);
   double *sk = st + (L + 16);
   int *bud = reinterpret_cast<int *>(lds + lo.bud);
@@ -234,11 +236,13 @@ __global__ __launch_bounds__(kSmallThreads) void aircache_small_kernel(Shape sh,
         small_wave_sync();
         // 2. I_v: the elite rows in order (head, then elite token); each row's
         // softmax over the visual and elite text keys, lanes over columns
-        float *iv = ivl + (size_t)l * Nv;
-        for (int c = lane; c < Nv; c += 64) iv[c] = 0.f;
+        // (one accumulator per KV head with one selection per KV head)
+        float *ivs = ivl + (size_t)l * nsel * Nv;
+        for (int c = lane; c < nsel * Nv; c += 64) ivs[c] = 0.f;
         const int ncols = Nv + ntk;
         for (int row = 0; row < Hq * ntk; ++row) {
           const int h = row / ntk, e = row - (row / ntk) * ntk, g = h / G;
+          float *iv = ivs + (size_t)(nsel > 1 ? g : 0) * Nv;
           const unsigned char *qr = qb + ((size_t)h * Nt + el[e]) * RB;
           const unsigned char *kg = kb + (size_t)g * S * RB;
           float m = -INFINITY, sum = 0.f;
@@ -255,24 +259,44 @@ __global__ __launch_bounds__(kSmallThreads) void aircache_small_kernel(Shape sh,
           for (int c = lane; c < Nv; c += 64)
             iv[c] += exp2f(Dot::run(qr, kg + (size_t)c * RB, lane) * sh.scale2 - M) * inv;
         }
-        // 3. the mean over the rows; s_t, then s_k (sample standard deviation,
-        // adjusted skewness), in double precision
+        // 3. the mean over the rows (over all query heads; per KV head too
+        // with one selection per KV head); s_t, then s_k (sample standard
+        // deviation, adjusted skewness), in double precision
         const float inv_rows = ntk > 0 ? 1.f / (float)(Hq * ntk) : 0.f;
+        const float inv_grp = ntk > 0 ? 1.f / (float)(G * ntk) : 0.f;
+        float av[kSmallMaxNv / 64];  // the lane's columns lane + 64 k
         double sum = 0.0;
-        for (int c = lane; c < Nv; c += 64) {
-          const float a = iv[c] * inv_rows;
-          iv[c] = a;
-          plan.iv[(size_t)plb * Nv + c] = a;
-          sum += (double)a;
+#pragma unroll
+        for (int k = 0; k < kSmallMaxNv / 64; ++k) {
+          const int c = lane + 64 * k;
+          av[k] = 0.f;
+          if (c < Nv) {
+            float t = 0.f;
+            for (int g = 0; g < nsel; ++g) {
+              const float ag = ivs[(size_t)g * Nv + c];
+              t += ag;
+              if (sh.per_head) {
+                ivs[(size_t)g * Nv + c] = ag * inv_grp;
+                plan.iv_head[((size_t)plb * nsel + g) * Nv + c] = ag * inv_grp;
+              }
+            }
+            const float a = t * inv_rows;
+            if (!sh.per_head) ivs[c] = a;
+            av[k] = a;
+            plan.iv[(size_t)plb * Nv + c] = a;
+            sum += (double)a;
+          }
         }
         sum = wave_sum_d(sum);
         const double mean = sum / (double)Nv;
         double m2 = 0.0, m3 = 0.0;
-        for (int c = lane; c < Nv; c += 64) {
-          const double dd = (double)iv[c] - mean;
-          m2 += dd * dd;
-          m3 += dd * dd * dd;
-        }
+#pragma unroll
+        for (int k = 0; k < kSmallMaxNv / 64; ++k)
+          if (lane + 64 * k < Nv) {
+            const double dd = (double)av[k] - mean;
+            m2 += dd * dd;
+            m3 += dd * dd * dd;
+          }
         m2 = wave_sum_d(m2);
         m3 = wave_sum_d(m3);
         if (lane == 0) {
@@ -314,9 +338,11 @@ __global__ __launch_bounds__(kSmallThreads) void aircache_small_kernel(Shape sh,
     // indices ascending (over I_v of the layer, which the keys replace).
     if (wave < W) {
       uint64_t *keys = reinterpret_cast<uint64_t *>(lds + lo.keys) + (size_t)wave * nk;
-      for (int l = wave; l < L; l += W) {
+      for (int ls = wave; ls < L * nsel; ls += W) {
+        // (layer, selection): one per layer, or one per KV head of it
+        const int l = ls / nsel, gs = ls - l * nsel;
         const int plb = l * B + b, rb = bud[l];
-        float *iv = ivl + (size_t)l * Nv;
+        float *iv = ivl + (size_t)ls * Nv;
         for (int i = lane; i < nk; i += 64)
           keys[i] = i < Nv ? ((uint64_t)__float_as_uint(iv[i]) << 16) | (uint64_t)(65535 - i) : 0ull;
         small_wave_sync();
@@ -339,7 +365,7 @@ __global__ __launch_bounds__(kSmallThreads) void aircache_small_kernel(Shape sh,
           const unsigned long long bal = __ballot(in);
           if (in) {
             const int pos = done + __popcll(bal & ((1ull << lane) - 1ull));
-            plan.kept[(size_t)plb * Nv + pos] = lane + 64 * k;
+            plan.kept[((size_t)plb * nsel + gs) * Nv + pos] = lane + 64 * k;
             kidx[pos] = lane + 64 * k;
           }
           done += __popcll(bal);
@@ -359,7 +385,7 @@ __global__ __launch_bounds__(kSmallThreads) void aircache_small_kernel(Shape sh,
       const int l = sg / (2 * Hkv), rem = sg - l * (2 * Hkv), kv = rem / Hkv, g = rem - kv * Hkv;
       const int rb = bud[l], nl = rb + Nt, np = nl * pieces;
       if (!gather || loff[l] + (int64_t)Hkv * nl * D > cap_elems) continue;
-      const int *kidx = reinterpret_cast<const int *>(ivl + (size_t)l * Nv);
+      const int *kidx = reinterpret_cast<const int *>(ivl + ((size_t)l * nsel + (nsel > 1 ? g : 0)) * Nv);
       const char *src = ptr[(1 + kv) * L + l] + b * kbytes + (size_t)g * S * RB;
       char *dst = const_cast<char *>(ptr[(3 + kv) * L + l]) + (size_t)loff[l] * ES + (size_t)g * nl * RB;
       constexpr int U = 16;

@@ -15,6 +15,8 @@ Comparison rules (per layer l and sample b):
               indices exactly; against the oracle's own I_v the sets may differ
               only in tokens within 1e-5 (relative) of the cut-off score;
   compacted   bit-exact against oracle step 6 fed the GPU's kept indices.
+With one selection per KV head, I_v^g follows the I_v rule and the kept sets
+and compacted rows the same rules per KV head.
 """
 from __future__ import annotations
 
@@ -47,21 +49,22 @@ def torch_dtype(w):
     return torch.float32 if w.dtype == wl.F32 else torch.bfloat16
 
 
-def make_aircache(w, alpha=None, ratio=None, max_elite=0, path="auto", budget_mode=0, obs_window=0):
+def make_aircache(w, alpha=None, ratio=None, max_elite=0, path="auto", budget_mode=0, obs_window=0,
+                  select="shared"):
     return AirCache(w.L, w.B, w.Hq, w.Hkv, w.D, w.Nv, w.Nt, dtype=torch_dtype(w),
                     alpha=w.alpha if alpha is None else alpha,
                     ratio=w.ratio if ratio is None else ratio, max_elite=max_elite, path=path,
-                    budget_mode=budget_mode, obs_window=obs_window)
+                    budget_mode=budget_mode, obs_window=obs_window, select=select)
 
 
 def run_gpu(inp: wl.Inputs, alpha=None, ratio=None, max_elite=0, tensors=None, compress=True, path="auto", ac=None,
-            run=False, budget_mode=0, obs_window=0):
+            run=False, budget_mode=0, obs_window=0, select="shared"):
     """Plan (and compress) on the GPU; ac: an AirCache to reuse (its workspace
     carries state from earlier calls); run: one aircache_run call instead of
     aircache_plan then aircache_compress."""
     w = inp.w
     if ac is None:
-        ac = make_aircache(w, alpha, ratio, max_elite, path, budget_mode, obs_window)
+        ac = make_aircache(w, alpha, ratio, max_elite, path, budget_mode, obs_window, select)
     q, k, v = tensors if tensors is not None else to_torch(inp)
     out = {}
     if run:
@@ -77,6 +80,8 @@ def run_gpu(inp: wl.Inputs, alpha=None, ratio=None, max_elite=0, tensors=None, c
     torch.cuda.synchronize()
     for f in ("elite_idx", "n_elite", "iv", "s_t", "s_k", "budget_x", "budget", "out_off", "kept_idx", "status"):
         out[f] = getattr(plan, f).cpu().numpy()
+    if plan.iv_head is not None:
+        out["iv_head"] = plan.iv_head.cpu().numpy()
     if compress:
         store = np.float32 if w.dtype == wl.F32 else np.uint16
         def host(t, n):
@@ -89,7 +94,7 @@ def run_gpu(inp: wl.Inputs, alpha=None, ratio=None, max_elite=0, tensors=None, c
     return out
 
 
-def reference(inp: wl.Inputs, gpu: dict, alpha=None, ratio=None, budget_mode=0, obs_window=0):
+def reference(inp: wl.Inputs, gpu: dict, alpha=None, ratio=None, budget_mode=0, obs_window=0, per_head=False):
     """Oracle values for every (l, b), conditional on the GPU's elite sets where
     they differ only in threshold-ambiguous tokens."""
     w = inp.w
@@ -98,6 +103,8 @@ def reference(inp: wl.Inputs, gpu: dict, alpha=None, ratio=None, budget_mode=0, 
     L, B = w.L, w.B
     ref = dict(iv=np.zeros((L, B, w.Nv)), s_t=np.zeros((L, B)), s_k=np.zeros((L, B)),
                elite_diff=np.zeros((L, B), bool), n_elite=np.zeros((L, B), int))
+    if per_head:
+        ref["iv_head"] = np.zeros((L, B, w.Hkv, w.Nv))
 
     def one(lb):
         l, b = lb
@@ -121,6 +128,8 @@ def reference(inp: wl.Inputs, gpu: dict, alpha=None, ratio=None, budget_mode=0, 
         ref["n_elite"][l, b] = len(el)
         iv = oracle.cross_score(w, inp.q[l], inp.k[l], b, use)
         ref["iv"][l, b] = iv
+        if per_head:
+            ref["iv_head"][l, b] = oracle.cross_score_groups(w, inp.q[l], inp.k[l], b, use)
         ref["s_t"][l, b], ref["s_k"][l, b] = oracle.layer_stats(iv)
 
     pairs = [(l, b) for l in range(L) for b in range(B)]
@@ -170,20 +179,29 @@ def compare(inp: wl.Inputs, gpu: dict, ref: dict, ratio=None, check_compacted=Tr
                 assert math.floor(hi) > math.floor(lo) and hi - lo <= 1e-3 * max(1.0, abs(xo)), (
                     f"budget ({l},{b}) {gpu['budget'][l, b]} vs {ref['budget'][l, b]} (x {xg} vs {xo})")
                 rep["budget_ambiguous"] += 1
-    # kept sets: conditional (exact) and end to end
-    for l in range(L):
-        for b in range(B):
-            kb = int(gpu["budget"][l, b])
-            kg = gpu["kept_idx"][l, b, :kb]
-            kc = oracle.topk(iv_g[l, b], kb)
-            assert np.array_equal(kg, kc), f"kept set ({l},{b}) differs from top-k of the GPU's own I_v"
-            if kb == ref["budget"][l, b] and kb > 0:
-                ko = oracle.topk(iv_r[l, b], kb)
-                if not np.array_equal(ko, kg):
-                    cut = np.sort(iv_r[l, b])[::-1][kb - 1]
-                    for j in set(ko.tolist()) ^ set(kg.tolist()):
-                        assert abs(iv_r[l, b, j] - cut) <= 1e-5 * cut, f"kept ({l},{b}) token {j} not near the cut-off"
-                    rep["kept_ambiguous"] += 1
+    # kept sets: conditional (exact) and end to end; per KV head against I_v^g
+    per_head = gpu["kept_idx"].ndim == 4
+    if per_head:
+        hg, hr = gpu["iv_head"].astype(np.float64), ref["iv_head"]
+        err = np.abs(hg - hr)
+        bad = err > 1e-3 * np.abs(hr)
+        assert not bad.any(), f"I_v per KV head mismatch at {np.argwhere(bad)[:5].tolist()}"
+        rep["iv_head_max_rel"] = float(np.max(err / np.maximum(np.abs(hr), 1e-300)))
+    sels = [(l, b, g) for l in range(L) for b in range(B) for g in range(w.Hkv if per_head else 1)]
+    for l, b, g in sels:
+        kb = int(gpu["budget"][l, b])
+        kg = gpu["kept_idx"][l, b, g, :kb] if per_head else gpu["kept_idx"][l, b, :kb]
+        own = hg[l, b, g] if per_head else iv_g[l, b]
+        rsc = hr[l, b, g] if per_head else iv_r[l, b]
+        kc = oracle.topk(own, kb)
+        assert np.array_equal(kg, kc), f"kept set ({l},{b},{g}) differs from top-k of the GPU's own scores"
+        if kb == ref["budget"][l, b] and kb > 0:
+            ko = oracle.topk(rsc, kb)
+            if not np.array_equal(ko, kg):
+                cut = np.sort(rsc)[::-1][kb - 1]
+                for j in set(ko.tolist()) ^ set(kg.tolist()):
+                    assert abs(rsc[j] - cut) <= 1e-5 * cut, f"kept ({l},{b},{g}) token {j} not near the cut-off"
+                rep["kept_ambiguous"] += 1
     # compacted cache: offsets and bytes
     if check_compacted:
         for l in range(L):
@@ -192,10 +210,12 @@ def compare(inp: wl.Inputs, gpu: dict, ref: dict, ratio=None, check_compacted=Tr
                 assert gpu["out_off"][l, b] == off
                 kb = int(gpu["budget"][l, b])
                 n = w.Hkv * (kb + w.Nt) * w.D
-                kept = gpu["kept_idx"][l, b, :kb]
                 for name, src in (("k_out", inp.k), ("v_out", inp.v)):
                     seg = gpu[name][l][off:off + n]
-                    exp = oracle.gather(w, src[l], b, kept).ravel()
+                    if per_head:
+                        exp = oracle.gather_groups(w, src[l], b, gpu["kept_idx"][l, b, :, :kb]).ravel()
+                    else:
+                        exp = oracle.gather(w, src[l], b, gpu["kept_idx"][l, b, :kb]).ravel()
                     assert np.array_equal(seg.view(np.uint8), exp.view(np.uint8)), f"{name} ({l},{b}) not bit-exact"
                 off += n
             assert gpu["out_off"][l, B] == off

@@ -22,7 +22,7 @@ def lib():
 
 def header_functions():
     text = open(os.path.join(ROOT, "include", "aircache.h")).read()
-    return sorted(set(re.findall(r"^[a-z_0-9 ]+[ *](aircache_[a-z_]+)\(", text, re.M)))
+    return sorted(set(re.findall(r"^[a-z_0-9 ]+[ *](aircache_[a-z_0-9]+)\(", text, re.M)))
 
 
 def test_exports_every_declared_function(lib):
@@ -31,24 +31,27 @@ def test_exports_every_declared_function(lib):
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.aircache_abi_version() == 1
+    assert lib.aircache_abi_version() == 2
 
 
 def test_struct_layouts():
-    # eight int32, two doubles, four int32
-    assert C.sizeof(_lib.Desc) == 8 * 4 + 2 * 8 + 4 * 4
+    # eight int32, two doubles, five int32 (padded to the doubles' alignment)
+    assert C.sizeof(_lib.Desc) == 8 * 4 + 2 * 8 + 5 * 4 + 4
     assert _lib.Desc.budget_mode.offset == 8 * 4 + 2 * 8 + 2 * 4
     assert _lib.Desc.obs_window.offset == 8 * 4 + 2 * 8 + 3 * 4
-    assert C.sizeof(_lib.PlanBuf) == 10 * 8
+    assert _lib.Desc.select_mode.offset == 8 * 4 + 2 * 8 + 4 * 4
+    assert C.sizeof(_lib.PlanBuf) == 11 * 8
+    assert _lib.PlanBuf.iv_head.offset == 10 * 8
 
 
 def desc(**kw):
     base = dict(n_layers=28, batch=1, n_q_heads=28, n_kv_heads=4, head_dim=128, n_vis=2880,
-                n_txt=128, dtype="bf16", alpha=0.9, ratio=0.1, max_elite=0, path=0, budget_mode=0, obs_window=0)
+                n_txt=128, dtype="bf16", alpha=0.9, ratio=0.1, max_elite=0, path=0, budget_mode=0, obs_window=0,
+                select=0)
     base.update(kw)
     return make_desc(*[base[k] for k in ("n_layers", "batch", "n_q_heads", "n_kv_heads", "head_dim",
                                          "n_vis", "n_txt", "dtype", "alpha", "ratio", "max_elite", "path",
-                                         "budget_mode", "obs_window")])
+                                         "budget_mode", "obs_window", "select")])
 
 
 def test_workspace_size(lib):
@@ -122,7 +125,8 @@ def test_run_launches(lib):
                                  dict(dtype="x"), dict(alpha=1.5), dict(alpha=float("nan")),
                                  dict(ratio=-0.1), dict(max_elite=129), dict(n_txt=4000), dict(path=4),
                                  dict(path=2, n_vis=4000), dict(budget_mode=5), dict(budget_mode=-1),
-                                 dict(obs_window=-1)])
+                                 dict(obs_window=-1), dict(select=2), dict(select=-1), dict(select=1, path=2),
+                                 dict(select=1, path=3)])
 def test_invalid_descriptor(lib, bad):
     if bad.get("dtype") == "x":
         d = desc()
@@ -211,3 +215,29 @@ def test_decode_workspace_and_argument_errors(lib):
     assert _lib.decode(d, fake, buf, fake, fake, fake, 16, 8, 0) == _lib.AIRCACHE_EWORKSPACE
     # a NULL layer pointer
     assert _lib.decode(d, fake[:-1] + [0], buf, fake, fake, fake, 16, 1 << 30, 0) == _lib.AIRCACHE_EINVAL
+
+
+def test_per_kv_head_selection_paths(lib):
+    """One selection per KV head runs on the tiled and small paths only."""
+    assert _lib.resolved_path(desc(select=1)) == _lib.PATH_TILED
+    assert _lib.resolved_path(desc(select=0)) == _lib.PATH_CHUNKED
+    tiny = dict(n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=64, n_vis=64, n_txt=16)
+    assert _lib.resolved_path(desc(select=1, **tiny)) == _lib.PATH_SMALL
+    assert _lib.resolved_path(desc(select=1, path=1, **tiny)) == _lib.PATH_TILED
+    # the plan call needs iv_head then
+    d = desc(select=1, **tiny)
+    ws = _lib.workspace_size(d)
+    ok = [4096, 8192]
+    assert _lib.plan(d, ok, ok, fake_buf(), 4096, ws, 0) == _lib.AIRCACHE_EINVAL
+    assert "iv_head" in lib.aircache_last_error().decode()
+
+
+def test_quantize_argument_errors(lib):
+    d = desc(n_layers=2)
+    p = [1 << 20, 2 << 20]
+    assert _lib.quantize_i8(d, _lib.PlanBuf(), p, p, p, p, 4096, 8192, 0) == _lib.AIRCACHE_EINVAL   # no plan
+    assert _lib.quantize_i8(d, fake_buf(), p, p, p, p, 0, 8192, 0) == _lib.AIRCACHE_EINVAL        # no scale
+    assert _lib.quantize_i8(d, fake_buf(), p, p, [1 << 20, 0], p, 4096, 8192, 0) == _lib.AIRCACHE_EINVAL
+    assert _lib.quantize_i8(d, fake_buf(), p, [(2 << 20) + 8, 4096], p, p, 4096, 8192, 0) == _lib.AIRCACHE_EINVAL
+    d.n_layers = 0
+    assert _lib.quantize_i8(d, fake_buf(), p, p, p, p, 4096, 8192, 0) == _lib.AIRCACHE_EINVAL
