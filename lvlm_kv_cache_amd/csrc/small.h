@@ -26,6 +26,7 @@ constexpr int kSmallWaves = kSmallThreads / 64;
 constexpr int kSmallMaxNv = 512;   // the direct rank's N_v^2 / 64 compares per lane
 constexpr int kSmallMaxZ = 8192;   // H_q * N_t logits of the elite step
 constexpr int kSmallMaxLayers = 51;
+constexpr int kSmallKeep = 4;      // logits of one I_v row kept in registers per lane (columns lane + 64 k)
 
 // Dynamic LDS (byte offsets). Region A: the sample's keys [L][H_kv][S][D] and
 // text queries [L][H_q][N_t][D] as stored, each layer's block padded to 1 KB
@@ -92,29 +93,31 @@ __device__ __forceinline__ void small_wave_sync() {
 
 // Dot product of two rows of D elements held in LDS, read in 16-byte pieces
 // starting at piece rot (mod the row's pieces): rows of one stride are then
-// read by the lanes of a wave from distinct banks.
+// read by the lanes of a wave from distinct banks. Four partial sums (one per
+// element of a piece) keep the multiply-add chains short; they are added at
+// the end as (s0 + s1) + (s2 + s3).
 template <typename Tag, int D> struct SmallDot;
 template <int D> struct SmallDot<F32Tag, D> {
   __device__ static __forceinline__ float run(const unsigned char *a, const unsigned char *b, int rot) {
     constexpr int P = D / 4;
-    float acc = 0.f;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll 8
     for (int w = 0; w < P; ++w) {
       const int i = (w + rot) & (P - 1);
       const f32x4_t x = *reinterpret_cast<const f32x4_t *>(a + 16 * i);
       const f32x4_t y = *reinterpret_cast<const f32x4_t *>(b + 16 * i);
-      acc += x[0] * y[0];
-      acc += x[1] * y[1];
-      acc += x[2] * y[2];
-      acc += x[3] * y[3];
+      s0 += x[0] * y[0];
+      s1 += x[1] * y[1];
+      s2 += x[2] * y[2];
+      s3 += x[3] * y[3];
     }
-    return acc;
+    return (s0 + s1) + (s2 + s3);
   }
 };
 template <int D> struct SmallDot<Bf16Tag, D> {
   __device__ static __forceinline__ float run(const unsigned char *a, const unsigned char *b, int rot) {
     constexpr int P = D / 8;
-    float acc = 0.f;
+    float sp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
     for (int w = 0; w < P; ++w) {
       const int i = (w + rot) & (P - 1);
@@ -122,11 +125,11 @@ template <int D> struct SmallDot<Bf16Tag, D> {
       const u32x4_t y = *reinterpret_cast<const u32x4_t *>(b + 16 * i);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc += __uint_as_float(x[e] << 16) * __uint_as_float(y[e] << 16);
-        acc += __uint_as_float(x[e] & 0xffff0000u) * __uint_as_float(y[e] & 0xffff0000u);
+        sp[e] += __uint_as_float(x[e] << 16) * __uint_as_float(y[e] << 16);
+        sp[e] += __uint_as_float(x[e] & 0xffff0000u) * __uint_as_float(y[e] & 0xffff0000u);
       }
     }
-    return acc;
+    return (sp[0] + sp[1]) + (sp[2] + sp[3]);
   }
 };
 
@@ -155,7 +158,6 @@ __global__ __launch_bounds__(kSmallThreads) void aircache_small_kernel(Shape sh,
   constexpr int pieces = RB / 16;
   if (tid == 0) flags = 0;
   for (int l = tid; l < L; l += kSmallThreads) loff[l] = 0;
-  for (int i = tid; i < 5 * L; i += kSmallThreads) ptr[i] = static_cast<const char *>(tab.p[i]);
 
   for (int b = 0; b < B; ++b) {
     // K and the text Q of every layer into LDS: whole 1 KB DMA blocks, wave w
@@ -174,6 +176,9 @@ __global__ __launch_bounds__(kSmallThreads) void aircache_small_kernel(Shape sh,
                                    : lo.qall + (size_t)l * lo.qpad + (size_t)(c - kblk) * 1024));
       }
     }
+    // the pointer tables, read while the first blocks are in flight
+    if (b == 0)
+      for (int i = tid; i < 5 * L; i += kSmallThreads) ptr[i] = static_cast<const char *>(tab.p[i]);
     wait_vmcnt<0>();
     __syncthreads();
 
@@ -245,8 +250,23 @@ __global__ __launch_bounds__(kSmallThreads) void aircache_small_kernel(Shape sh,
           float *iv = ivs + (size_t)(nsel > 1 ? g : 0) * Nv;
           const unsigned char *qr = qb + ((size_t)h * Nt + el[e]) * RB;
           const unsigned char *kg = kb + (size_t)g * S * RB;
-          float m = -INFINITY, sum = 0.f;
-          for (int c = lane; c < ncols; c += 64) {
+          // pass 1: the row's logits (the first kSmallKeep per lane kept in
+          // registers), maximum and sum
+          float tk[kSmallKeep];
+#pragma unroll
+          for (int k = 0; k < kSmallKeep; ++k) {
+            const int c = lane + 64 * k;
+            const int et = el[c - Nv > 0 ? (c - Nv < ntk ? c - Nv : ntk - 1) : 0];
+            const int key = c < Nv ? c : Nv + et;
+            tk[k] = c < ncols ? Dot::run(qr, kg + (size_t)key * RB, lane) * sh.scale2 : -INFINITY;
+          }
+          float m = -INFINITY;
+#pragma unroll
+          for (int k = 0; k < kSmallKeep; ++k) m = fmaxf(m, tk[k]);
+          float sum = 0.f;
+#pragma unroll
+          for (int k = 0; k < kSmallKeep; ++k) sum += tk[k] > -INFINITY ? exp2f(tk[k] - m) : 0.f;
+          for (int c = lane + 64 * kSmallKeep; c < ncols; c += 64) {
             const int et = el[c - Nv > 0 ? c - Nv : 0];
             const int key = c < Nv ? c : Nv + et;
             const float t = Dot::run(qr, kg + (size_t)key * RB, lane) * sh.scale2;
@@ -256,7 +276,13 @@ __global__ __launch_bounds__(kSmallThreads) void aircache_small_kernel(Shape sh,
           }
           const float M = wave_max(m);
           const float inv = 1.f / wave_sum(m > -INFINITY ? sum * exp2f(m - M) : 0.f);
-          for (int c = lane; c < Nv; c += 64)
+          // pass 2: the visual columns' weights, accumulated per wave
+#pragma unroll
+          for (int k = 0; k < kSmallKeep; ++k) {
+            const int c = lane + 64 * k;
+            if (c < Nv) iv[c] += exp2f(tk[k] - M) * inv;
+          }
+          for (int c = lane + 64 * kSmallKeep; c < Nv; c += 64)
             iv[c] += exp2f(Dot::run(qr, kg + (size_t)c * RB, lane) * sh.scale2 - M) * inv;
         }
         // 3. the mean over the rows (over all query heads; per KV head too
