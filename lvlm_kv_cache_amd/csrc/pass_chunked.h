@@ -62,6 +62,7 @@ constexpr int kPassThreads = 512;
 constexpr int kPassWaves = kPassThreads / 64;
 constexpr unsigned kSpinLimit = 1u << 20;  // polls of one wait before it gives up
 constexpr int kPassTableSlots = 256;       // layer pointers of one launch
+constexpr int kXcds = 8;                   // accelerator complex dies; workgroups are dealt to them in turn
 constexpr int kPassMaxPass = 1024;         // passes of one item at most (tag space)
 constexpr int kRingBytes = 131072;         // key tiles in LDS per workgroup
 constexpr int kKtwMax = 12;                // key tiles per wave of one chunk at most
@@ -739,11 +740,15 @@ struct PassItem {
 // text keys. Wave (head gl, sub) takes key tiles sub * ktw .. of its head's
 // chunk; they stream through its ring slots (R tiles in flight, refilled as
 // they are read), the logits stay in registers. The pass's column sums of the
-// softmax rows go to colsum (set when first, else added).
+// softmax rows go to colsum (set when first, else added). pre: the pass's
+// first ring tiles were issued by the previous pass of the item; nxt >= 0:
+// once its own tiles are read, the pass issues the first ring tiles of the
+// item's next pass (the same columns, KV heads of head group nxt), so that
+// they land while this pass waits for the other chunks' row normalisers.
 template <typename Tag, int D, int RTP>
 __device__ __forceinline__ void pass_rows(const Shape &sh, const PassWs &pw, const PassItem &it, int hg, int rg,
-                                          int pidx, bool first, unsigned char *lds, const PassLds &lo,
-                                          unsigned epoch) {
+                                          int pidx, bool first, bool pre, int nxt, unsigned char *lds,
+                                          const PassLds &lo, unsigned epoch) {
   using E = typename Tag::store_t;
   constexpr int NT = kPassThreads;
   constexpr int RTPM = pass_rtp(D, Tag::kBytes);
@@ -792,22 +797,23 @@ __device__ __forceinline__ void pass_rows(const Shape &sh, const PassWs &pw, con
   const int ncols = Nv + ntk;
   // LDS-DMA of key tile s into slot s % R: visual key col, or elite text key
   // el[col - N_v]; columns past the keys read the last visual key (masked)
-  auto issue = [&](int s) {
+  auto issue_from = [&](const E *kbase, int s) {
     const int v = col0 + s * 16;
     int row;
     if (v < Nv) row = v;
     else if (v < ncols) row = Nv + el[v - Nv];
     else row = Nv - 1;
-    const unsigned char *src = reinterpret_cast<const unsigned char *>(kb + (size_t)row * D);
+    const unsigned char *src = reinterpret_cast<const unsigned char *>(kbase + (size_t)row * D);
     unsigned char *dst = slots + (s % R) * kTile;
 #pragma unroll
     for (int j = 0; j < kDma; ++j) load_lds16(src + 16 * grp + 64 * j, dst + 1024 * j);
   };
+  auto issue = [&](int s) { issue_from(kb, s); };
   // a later pass over a chunk whose tiles all fit the ring finds them there
   const bool resident = rg > 0 && ktw <= R;
 #pragma unroll
   for (int s = 0; s < R; ++s)
-    if (s < ktw && !resident) issue(s);
+    if (s < ktw && !resident && !pre) issue(s);
 
   f32x4_t S[KM][RTP];
 #pragma unroll
@@ -840,6 +846,15 @@ __device__ __forceinline__ void pass_rows(const Shape &sh, const PassWs &pw, con
 #pragma unroll
       for (int rt = 0; rt < RTP; ++rt) S[s][rt] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
+  }
+  // the next pass's first ring tiles, once every read of this pass's tiles
+  // is done
+  if (nxt >= 0) {
+    wait_lds_reads();
+    const E *kn = static_cast<const E *>(it.k_l) + (size_t)(it.b * sh.Hkv + nxt * hgs + gl) * sh.S * D;
+#pragma unroll
+    for (int s = 0; s < R; ++s)
+      if (s < ktw) issue_from(kn, s);
   }
   // chunk-local row maxima: keys of a lane row by DPP, then the head's waves
   // in order
@@ -1588,17 +1603,17 @@ __device__ __forceinline__ void copy_rows(const char *src, char *dst, int rb, in
 
 template <typename Tag, int D>
 __device__ __forceinline__ void pass_rows_dispatch(int rtp, const Shape &sh, const PassWs &pw, const PassItem &it,
-                                                   int hg, int rg, int pidx, bool first, unsigned char *lds,
-                                                   const PassLds &lo, unsigned epoch) {
+                                                   int hg, int rg, int pidx, bool first, bool pre, int nxt,
+                                                   unsigned char *lds, const PassLds &lo, unsigned epoch) {
   constexpr int RTPM = pass_rtp(D, Tag::kBytes);
   if (RTPM >= 6 && rtp >= 6)
-    pass_rows<Tag, D, (RTPM >= 6 ? 6 : 1)>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
+    pass_rows<Tag, D, (RTPM >= 6 ? 6 : 1)>(sh, pw, it, hg, rg, pidx, first, pre, nxt, lds, lo, epoch);
   else if (RTPM >= 5 && rtp == 5)
-    pass_rows<Tag, D, (RTPM >= 5 ? 5 : 1)>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
-  else if (rtp == 4) pass_rows<Tag, D, 4>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
-  else if (rtp == 3) pass_rows<Tag, D, 3>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
-  else if (rtp == 2) pass_rows<Tag, D, 2>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
-  else pass_rows<Tag, D, 1>(sh, pw, it, hg, rg, pidx, first, lds, lo, epoch);
+    pass_rows<Tag, D, (RTPM >= 5 ? 5 : 1)>(sh, pw, it, hg, rg, pidx, first, pre, nxt, lds, lo, epoch);
+  else if (rtp == 4) pass_rows<Tag, D, 4>(sh, pw, it, hg, rg, pidx, first, pre, nxt, lds, lo, epoch);
+  else if (rtp == 3) pass_rows<Tag, D, 3>(sh, pw, it, hg, rg, pidx, first, pre, nxt, lds, lo, epoch);
+  else if (rtp == 2) pass_rows<Tag, D, 2>(sh, pw, it, hg, rg, pidx, first, pre, nxt, lds, lo, epoch);
+  else pass_rows<Tag, D, 1>(sh, pw, it, hg, rg, pidx, first, pre, nxt, lds, lo, epoch);
 }
 
 template <typename Tag, int D>
@@ -1660,8 +1675,12 @@ __global__ __launch_bounds__(kPassThreads) void aircache_pass_kernel(Shape sh, P
   const int kcap = pass_schedule<D, Tag::kBytes>(sh, pw, epoch, start, masks, preload);
   const int n_items = uniform(start[LB]);
 
-  // 3. Items i = me, me + P, ...
-  for (int i = me; i < n_items; i += P) {
+  // 3. Items i = v, v + P, ... with v this workgroup's rank counted XCD by
+  // XCD (workgroups go to the eight XCDs in turn): the chunks of one (layer,
+  // sample) are consecutive items, so they run on one XCD and read the
+  // pair's elite queries through one L2.
+  const int vme = (P % kXcds == 0) ? (me % kXcds) * (P / kXcds) + me / kXcds : me;
+  for (int i = vme; i < n_items; i += P) {
     const int tid = opaque_tid();
     PassItem it;
     it.q = pass_pair_of(start, LB, i);
@@ -1686,10 +1705,19 @@ __global__ __launch_bounds__(kPassThreads) void aircache_pass_kernel(Shape sh, P
     const int W = ip.width;
     float *colsum = reinterpret_cast<float *>(lds + lo.colsum);
     float ivacc[3] = {0.f, 0.f, 0.f};  // columns tid, tid + 512, tid + 1024
+    // a pass that streams its tiles gets its first ring tiles issued by the
+    // pass before it (a later row group of a chunk that fits the ring finds
+    // its tiles there and streams nothing)
+    constexpr int R = pass_ring(D, Tag::kBytes);
+    bool pre = false;
     for (int hg = 0; hg < pw.nhg; ++hg) {
       for (int rg = 0; rg < it.nrg; ++rg) {
         const int rtp = min(RTPM, it.rtg - rg * RTPM);
-        pass_rows_dispatch<Tag, D>(rtp, sh, pw, it, hg, rg, hg * it.nrg + rg, rg == 0, lds, lo, epoch);
+        int nxt = -1;
+        if (rg + 1 < it.nrg) nxt = it.ktw > R ? hg : -1;
+        else if (hg + 1 < pw.nhg) nxt = hg + 1;
+        pass_rows_dispatch<Tag, D>(rtp, sh, pw, it, hg, rg, hg * it.nrg + rg, rg == 0, pre, nxt, lds, lo, epoch);
+        pre = nxt >= 0;
       }
       // the head group's column sums, added over its heads in ascending order
       // (KV heads in ascending order overall)
