@@ -50,6 +50,8 @@ def parse():
                          "workloads 3-5 is a stress run with many elite text tokens, not a headline figure)")
     ap.add_argument("--max-elite", type=int, default=64)
     ap.add_argument("--path", default="auto", choices=["auto", "small", "chunked", "tiled", "rows"])
+    ap.add_argument("--select", default="shared", choices=["shared", "per_kv_head"],
+                    help="one visual-token selection per (layer, sample), the method's, or one per KV head")
     ap.add_argument("--budget-mode", default="aircache", choices=["aircache", "uniform", "strength", "skewness", "pyramid"],
                     help="layer budget rule: the method's (default) or one of its allocation ablation's variants")
     ap.add_argument("--obs-window", type=int, default=0,
@@ -58,7 +60,8 @@ def parse():
                     help="leave out the cache-warm loop (one input copy every step), so that every launch of the "
                          "run reads rotated inputs (profiles of the headline conditions)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--skip-decode", action="store_true", help="do not time decode attention over the compacted cache")
+    ap.add_argument("--skip-decode", action="store_true",
+                    help="do not time decode attention and int8 quantisation over the compacted cache")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (the reference kernel that scales "
@@ -281,7 +284,7 @@ def main():
 
     ac = AirCache(w.L, w.B, w.Hq, w.Hkv, w.D, w.Nv, w.Nt, dtype=tdtype, alpha=w.alpha, ratio=w.ratio,
                   max_elite=min(a.max_elite, w.Nt) if a.max_elite > 0 else 0, device=dev, path=a.path,
-                  budget_mode=a.budget_mode, obs_window=a.obs_window)
+                  budget_mode=a.budget_mode, obs_window=a.obs_window, select=a.select)
     plan = ac.alloc_plan()
     k_out, v_out = ac.alloc_compacted()
     stream = torch.cuda.current_stream(dev)
@@ -423,6 +426,31 @@ def main():
                "algorithmic_bytes": dec_bytes, "achieved_gbps": dec_gbps, "peak_gbps": PEAK_HBM_GBPS,
                "frac": dec_gbps / PEAK_HBM_GBPS, "dense_cache_bytes": 2.0 * w.L * w.B * w.Hkv * w.S * w.D * esz,
                "retained_row_frac": float((budget_now + w.Nt).sum()) / (w.L * w.B * (w.Nv + w.Nt))}
+    # int8 quantisation of the same compacted cache (aircache_quantize_i8);
+    # K timed calls
+    quant = None
+    if not a.skip_decode:
+        cap = k_out[0].numel()
+        kq = [torch.empty(cap, dtype=torch.int8, device=dev) for _ in range(w.L)]
+        vq = [torch.empty(cap, dtype=torch.int8, device=dev) for _ in range(w.L)]
+        ks = torch.empty(w.L, w.B, w.Hkv, dtype=torch.float32, device=dev)
+        vs = torch.empty(w.L, w.B, w.Hkv, dtype=torch.float32, device=dev)
+        bq = ac.bind_quantize(plan, k_out, v_out, kq, vq, ks, vs, stream=stream)
+        for _ in range(3):
+            bq()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(a.steps):
+            bq()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        q_us = 1e3 * e0.elapsed_time(e1) / a.steps
+        esz = 2 if w.dtype == wl.BF16 else 4
+        n_el = 2.0 * w.Hkv * w.D * float((budget_now + w.Nt).sum())  # K and V elements kept
+        q_bytes = n_el * (esz + 1)  # each element read once, its code written
+        quant = {"kernels": ["quantize_i8_kernel"], "us_per_call": q_us, "algorithmic_bytes": q_bytes,
+                 "achieved_gbps": q_bytes / (q_us * 1e-6) / 1e9, "peak_gbps": PEAK_HBM_GBPS,
+                 "frac": q_bytes / (q_us * 1e-6) / 1e9 / PEAK_HBM_GBPS}
     ceil = hbm_ceilings()
 
     tokens = w.L * w.B * w.Nv
@@ -453,7 +481,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == wl.BF16 else "f32",
         "data": "synthetic",
-        "config": dict(w.describe(), base=w.base, budget_mode=a.budget_mode, obs_window=a.obs_window, seed=seed, input_copies=ncopy, cache="hot" if a.hot else "rotated",
+        "config": dict(w.describe(), base=w.base, budget_mode=a.budget_mode, obs_window=a.obs_window, select=a.select,
+                       seed=seed, input_copies=ncopy, cache="hot" if a.hot else "rotated",
                        path=path, launches_per_step=ac.run_launches),
         "samples_per_s": w.B / (ms * 1e-3),
         "visual_tokens_per_s": w.B * w.Nv / (ms * 1e-3),  # B * N_v per step (all layers in it)
@@ -480,6 +509,7 @@ def main():
         # decode attention over the compacted cache (a consumer of the pass,
         # timed after the pass, not part of its step)
         "decode_attention": dec,
+        "quantize_i8": quant,
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, a.cpu_seconds)

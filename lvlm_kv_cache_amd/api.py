@@ -253,6 +253,12 @@ class AirCache:
                                     self._stream(stream)))
         return kq, vq, k_scale, v_scale
 
+    def bind_quantize(self, plan: PlanOutputs, k_out, v_out, kq, vq, k_scale, v_scale,
+                      stream=None) -> "BoundQuantize":
+        """A BoundQuantize running quantize_i8() on these tensors with the
+        checks and marshalling done once, here."""
+        return BoundQuantize(self, plan, k_out, v_out, kq, vq, k_scale, v_scale, stream)
+
     def bind_decode(self, q_dec, plan: PlanOutputs, k_out, v_out, o, stream=None) -> "BoundDecode":
         """A BoundDecode running decode() on these tensors with the checks and
         marshalling done once, here."""
@@ -353,6 +359,35 @@ class BoundPass:
 
     def __call__(self) -> PlanOutputs:
         return self.run()
+
+
+class BoundQuantize:
+    """AirCache.quantize_i8 over fixed tensors, validated and marshalled once
+    (as BoundPass does for the pass). The tensors must stay alive while it is
+    used."""
+
+    def __init__(self, ac: "AirCache", plan: PlanOutputs, k_out, v_out, kq, vq, k_scale, v_scale, stream=None):
+        ac.quantize_i8(plan, k_out, v_out, kq, vq, k_scale, v_scale, stream=stream)  # the checks, once
+        self.out = (kq, vq, k_scale, v_scale)
+        self._keep = (ac, plan, k_out, v_out, kq, vq, k_scale, v_scale)
+        self._lib = _lib.load()
+        self._desc = _lib.C.byref(ac.desc)
+        self._buf = plan.buf()
+        self._pbuf = _lib.C.byref(self._buf)
+        self._ko = _lib.ptr_array([t.data_ptr() for t in k_out])
+        self._vo = _lib.ptr_array([t.data_ptr() for t in v_out])
+        self._kq = _lib.ptr_array([t.data_ptr() for t in kq])
+        self._vq = _lib.ptr_array([t.data_ptr() for t in vq])
+        self._ks = _lib.C.c_void_p(k_scale.data_ptr())
+        self._vs = _lib.C.c_void_p(v_scale.data_ptr())
+        self._st = _lib.C.c_void_p(ac._stream(stream))
+
+    def __call__(self):
+        rc = self._lib.aircache_quantize_i8(self._desc, self._pbuf, self._ko, self._vo, self._kq, self._vq,
+                                            self._ks, self._vs, self._st)
+        if rc:
+            _lib.check(rc)
+        return self.out
 
 
 class BoundDecode:

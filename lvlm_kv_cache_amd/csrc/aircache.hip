@@ -1144,7 +1144,8 @@ __global__ __launch_bounds__(256) void kv_gather_kernel(Shape sh, GatherTables t
 // (layer, sample, KV head, K or V) segment of the compacted layout: the
 // segment's largest absolute value, s = max / 127, then codes
 // rint(x / s) clamped to [-127, 127], both divisions correctly rounded in
-// float32. 16 elements per thread step: one 16-byte store of codes.
+// float32. 16 elements per piece, four pieces per thread in flight, one
+// 16-byte store of codes per piece; the second read mostly hits L2.
 // ----------------------------------------------------------------------------
 struct QuantTables {
   LayerTable ko, vo;
@@ -1175,11 +1176,15 @@ template <> __device__ __forceinline__ void load16_as_f32<Bf16Tag>(const uint16_
   }
 }
 
+constexpr int kQuantThreads = 512;
+constexpr int kQuantUnroll = 4;  // 16-element pieces per thread in flight
+
 template <typename Tag>
-__global__ __launch_bounds__(256) void quantize_i8_kernel(Shape sh, QuantTables tb, PlanPtrs plan, float *k_scale,
-                                                          float *v_scale, int64_t cap_elems) {
+__global__ __launch_bounds__(kQuantThreads) void quantize_i8_kernel(Shape sh, QuantTables tb, PlanPtrs plan,
+                                                                    float *k_scale, float *v_scale, int64_t cap_elems) {
   using E = typename Tag::store_t;
-  __shared__ float wmax[4];
+  constexpr int U = kQuantUnroll;
+  __shared__ float wmax[kQuantThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kv = blockIdx.x & 1, u = blockIdx.x >> 1;
   const int g = u % sh.Hkv, lb = u / sh.Hkv, l = lb / sh.B, b = lb - (lb / sh.B) * sh.B;
@@ -1188,38 +1193,58 @@ __global__ __launch_bounds__(256) void quantize_i8_kernel(Shape sh, QuantTables 
   const int n = bud + sh.Nt;
   const int64_t seg0 = plan.out_off[(size_t)l * (sh.B + 1) + b];
   if (seg0 < 0 || seg0 + (int64_t)sh.Hkv * n * sh.D > cap_elems) return;
-  const size_t base = (size_t)seg0 + (size_t)g * n * sh.D, cnt16 = (size_t)n * sh.D / 16;
+  const size_t base = (size_t)seg0 + (size_t)g * n * sh.D;
+  const int cnt16 = n * sh.D / 16;  // at least 4 (D >= 64, n >= 1)
   const E *src = static_cast<const E *>(kv ? tb.vo.p[l] : tb.ko.p[l]) + base;
   int8_t *dst = static_cast<int8_t *>(kv ? tb.vq.p[l] : tb.kq.p[l]) + base;
+  // the largest |x|: U pieces per thread in flight, indices past the end
+  // clamped to the last piece (no branch around a load)
   float m = 0.f;
-  for (size_t p = tid; p < cnt16; p += 256) {
-    float x[16];
-    load16_as_f32<Tag>(src + 16 * p, x);
+  for (int p0 = tid; p0 < cnt16; p0 += kQuantThreads * U) {
+    float x[U][16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(x[j]));
+    for (int j = 0; j < U; ++j) {
+      const int p = p0 + j * kQuantThreads;
+      load16_as_f32<Tag>(src + 16 * (size_t)(p < cnt16 ? p : cnt16 - 1), x[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(x[j][e]));
   }
   m = wave_max(m);
   if (lane == 0) wmax[wave] = m;
   __syncthreads();
-  m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  m = wmax[0];
+  for (int w = 1; w < kQuantThreads / 64; ++w) m = fmaxf(m, wmax[w]);
   const float sc = __fdiv_rn(m, 127.0f);
   if (tid == 0) (kv ? v_scale : k_scale)[(size_t)lb * sh.Hkv + g] = sc;
-  for (size_t p = tid; p < cnt16; p += 256) {
-    float x[16];
-    load16_as_f32<Tag>(src + 16 * p, x);
-    u32x4_t out;
+  // the codes (a lane past the end writes the last piece's codes again)
+  for (int p0 = tid; p0 < cnt16; p0 += kQuantThreads * U) {
+    float x[U][16];
+    int pj[U];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      unsigned word = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float q = sc > 0.f ? rintf(__fdiv_rn(x[4 * w + j], sc)) : 0.f;
-        q = fminf(fmaxf(q, -127.f), 127.f);
-        word |= ((unsigned)(int)q & 0xffu) << (8 * j);
-      }
-      out[w] = word;
+    for (int j = 0; j < U; ++j) {
+      const int p = p0 + j * kQuantThreads;
+      pj[j] = p < cnt16 ? p : cnt16 - 1;
+      load16_as_f32<Tag>(src + 16 * (size_t)pj[j], x[j]);
     }
-    store_nt(reinterpret_cast<u32x4_t *>(dst + 16 * p), out);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      u32x4_t out;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        unsigned word = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float q = sc > 0.f ? rintf(__fdiv_rn(x[j][4 * w + e], sc)) : 0.f;
+          q = fminf(fmaxf(q, -127.f), 127.f);
+          word |= ((unsigned)(int)q & 0xffu) << (8 * e);
+        }
+        out[w] = word;
+      }
+      store_nt(reinterpret_cast<u32x4_t *>(dst + 16 * (size_t)pj[j]), out);
+    }
   }
 }
 
@@ -2196,11 +2221,11 @@ int aircache_quantize_i8(const aircache_desc *desc, const aircache_plan_buf *pla
   const int64_t cap = (int64_t)s.B * s.Hkv * s.S * s.D;
   const dim3 grid((unsigned)(2 * s.L * s.B * s.Hkv));
   if (desc->dtype == AIRCACHE_BF16)
-    hipLaunchKernelGGL(quantize_i8_kernel<Bf16Tag>, grid, dim3(256), 0, st, s, tb, plan_ptrs(plan), k_scale,
-                       v_scale, cap);
+    hipLaunchKernelGGL(quantize_i8_kernel<Bf16Tag>, grid, dim3(kQuantThreads), 0, st, s, tb, plan_ptrs(plan),
+                       k_scale, v_scale, cap);
   else
-    hipLaunchKernelGGL(quantize_i8_kernel<F32Tag>, grid, dim3(256), 0, st, s, tb, plan_ptrs(plan), k_scale,
-                       v_scale, cap);
+    hipLaunchKernelGGL(quantize_i8_kernel<F32Tag>, grid, dim3(kQuantThreads), 0, st, s, tb, plan_ptrs(plan),
+                       k_scale, v_scale, cap);
   return check_hip(hipGetLastError(), "quantize_i8_kernel launch");
 }
 

@@ -107,3 +107,25 @@ def test_quantize_i8_edge(shape, ratio):
     print(f"[f4] quantise {shape} ratio {ratio}", flush=True)
     ks, vs = _quant_case(w, 32, select="per_kv_head", zero_v_layer=0)
     assert (vs[0] == 0).all() and (ks > 0).all()
+
+
+def test_bound_quantize_matches_plain_call():
+    w = wl.custom(Nv=300, Nt=40, Hq=8, Hkv=2, D=128, dtype="bf16", L=2, B=2, ratio=0.2)
+    inp = wl.make_inputs(w, 5)
+    ac = make_aircache(w)
+    q, k, v = to_torch(inp)
+    plan = ac.alloc_plan()
+    ko, vo = ac.alloc_compacted()
+    ac.run(q, k, v, plan, ko, vo)
+    a = ac.quantize_i8(plan, ko, vo)
+    kq = [torch.full_like(t, 99) for t in a[0]]
+    vq = [torch.full_like(t, 99) for t in a[1]]
+    ks, vs = torch.full_like(a[2], -1.0), torch.full_like(a[3], -1.0)
+    bq = ac.bind_quantize(plan, ko, vo, kq, vq, ks, vs)
+    bq()
+    bq()  # twice: nothing carries over between calls
+    torch.cuda.synchronize()
+    n = plan.out_off[:, -1].cpu().tolist()
+    for l in range(w.L):
+        assert torch.equal(a[0][l][:n[l]], kq[l][:n[l]]) and torch.equal(a[1][l][:n[l]], vq[l][:n[l]])
+    assert torch.equal(a[2], ks) and torch.equal(a[3], vs)
