@@ -202,9 +202,9 @@ int64_t aircache_max_compacted_elems(const aircache_desc *desc);
 int32_t aircache_resolved_path(const aircache_desc *desc);
 
 /* Kernel launches aircache_run makes for this descriptor: 1 when the chunked
- * path compacts inside its launch, more when aircache_run falls back to
- * aircache_plan then aircache_compress; -1 for an invalid descriptor. Host
- * only; no device work. */
+ * or the small path compacts inside its launch, more when aircache_run falls
+ * back to aircache_plan then aircache_compress; -1 for an invalid descriptor.
+ * Host only; no device work. */
 int32_t aircache_run_launches(const aircache_desc *desc);
 
 /* Scores, statistics, budgets and top-k selection for all layers: the first
@@ -249,7 +249,8 @@ int aircache_compress(const aircache_desc *desc, const aircache_plan_buf *plan,
  * 5 * n_layers <= 256, one launch does both: the compaction of a (layer,
  * sample) starts as soon as its top-k is out, on workgroups that have
  * finished their scoring work, instead of in a second kernel after the last
- * top-k. Otherwise the two calls are made in order.
+ * top-k; the small path's one workgroup also compacts in its launch.
+ * Otherwise the two calls are made in order.
  *   q_txt, k, v : host arrays of n_layers device pointers (inputs, read-only)
  *   plan        : output buffers (see aircache_plan_buf), all filled
  *   k_out, v_out: compacted outputs as for aircache_compress
