@@ -244,6 +244,7 @@ __global__ __launch_bounds__(kSmallThreads) void aircache_small_kernel(Shape sh,
         // (one accumulator per KV head with one selection per KV head)
         float *ivs = ivl + (size_t)l * nsel * Nv;
         for (int c = lane; c < nsel * Nv; c += 64) ivs[c] = 0.f;
+        small_wave_sync();  // (zeroed by other lanes than those that add to them)
         const int ncols = Nv + ntk;
         for (int row = 0; row < Hq * ntk; ++row) {
           const int h = row / ntk, e = row - (row / ntk) * ntk, g = h / G;
