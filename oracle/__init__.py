@@ -64,6 +64,8 @@ def lib():
         l.orc_quantize_i8.restype = None
         l.orc_decode_attention.argtypes = [C.POINTER(Desc), P, P, C.c_int, P, P]
         l.orc_decode_attention.restype = None
+        l.orc_prefill_attention.argtypes = [C.POINTER(Desc), P, P, P, C.c_int, C.c_int, C.c_int, P]
+        l.orc_prefill_attention.restype = None
         l.orc_run.argtypes = [C.POINTER(Desc)] + [P] * 15
         l.orc_run.restype = C.c_int
         _lib = l
@@ -210,6 +212,26 @@ def decode_attention(w, k_out_l, v_out_l, out_off_l, budget_l, q_l) -> np.ndarra
         off = int(out_off_l[b])
         size = w.Hkv * n * w.D
         o[b] = decode_attention_segment(w, k_out_l[off:off + size], v_out_l[off:off + size], n, q_l[b])
+    return o
+
+
+def prefill_attention(w, q_all_l, k_l, v_l, b: int, row0: int = 0, nrows=None) -> np.ndarray:
+    """Causal prefill attention of one layer and sample: q_all_l [B][H_q][S][D]
+    (every position's query), k_l / v_l [B][H_kv][S][D]; rows row0 ..
+    row0 + nrows - 1 of every query head: o [H_q][nrows][D] (float64)."""
+    store = np.float32 if w.dtype == "f32" else np.uint16
+    S = w.Nv + w.Nt
+    if nrows is None:
+        nrows = S - row0
+    assert 0 <= row0 and row0 + nrows <= S
+    q_all_l = np.ascontiguousarray(q_all_l, dtype=store)
+    k_l = np.ascontiguousarray(k_l, dtype=store)
+    v_l = np.ascontiguousarray(v_l, dtype=store)
+    assert q_all_l.shape[-3:] == (w.Hq, S, w.D), q_all_l.shape
+    assert k_l.shape[-3:] == (w.Hkv, S, w.D) and v_l.shape == k_l.shape
+    o = np.zeros((w.Hq, nrows, w.D), np.float64)
+    lib().orc_prefill_attention(C.byref(desc_of(w)), _ptr(q_all_l), _ptr(k_l), _ptr(v_l), int(b), int(row0),
+                                int(nrows), _ptr(o))
     return o
 
 

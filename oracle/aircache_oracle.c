@@ -389,6 +389,44 @@ void orc_decode_attention(const orc_desc *w, const void *k_seg, const void *v_se
 }
 
 /*
+ * Prefill attention of one layer and sample, the attention whose keys the
+ * pass later scores: the KV-cache primer page (devpress.csdn.net), section
+ * 2.1 "到底缓存什么？", the o_t equation applied at every position t of the
+ * regrouped sequence (visual tokens first, then text), so position t attends
+ * to the keys 0..t:
+ *   o_{h,t} = softmax(q_{h,t} . K_g[0..t]^T / sqrt(D)) V_g[0..t],  g = h / (H_q / H_kv).
+ * q_all: [B][H_q][N_v + N_t][D] (every position's query); k_l, v_l:
+ * [B][H_kv][N_v + N_t][D]; rows row0 .. row0 + nrows - 1 of every query head
+ * of sample b go to o [H_q][nrows][D].
+ */
+void orc_prefill_attention(const orc_desc *w, const void *q_all, const void *k_l, const void *v_l, int b,
+                           int row0, int nrows, double *o) {
+  const int G = w->Hq / w->Hkv, D = w->D, S = w->Nv + w->Nt;
+  const double scale = sqrt((double)D);
+  double *z = (double *)malloc(sizeof(double) * (size_t)S);
+  for (int h = 0; h < w->Hq; ++h) {
+    const int g = h / G;
+    const size_t qh = ((size_t)b * w->Hq + h) * (size_t)S;
+    for (int r = 0; r < nrows; ++r) {
+      const int t = row0 + r;
+      for (int s = 0; s <= t; ++s) {
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d)
+          acc += elem(q_all, (qh + t) * D + d, w->dtype) * elem(k_l, k_index(w, b, g, s) + d, w->dtype);
+        z[s] = acc / scale;
+      }
+      softmax(z, t + 1);
+      for (int d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int s = 0; s <= t; ++s) acc += z[s] * elem(v_l, k_index(w, b, g, s) + d, w->dtype);
+        o[((size_t)h * nrows + r) * D + d] = acc;
+      }
+    }
+  }
+  free(z);
+}
+
+/*
  * The whole pass. Arrays indexed [l][b] are row-major with B columns.
  *   elite [L][B][N_t] (first n_elite valid), pbar [L][B][N_t],
  *   iv [L][B][N_v], s_t, s_k, x [L][B], budget [L][B],

@@ -638,3 +638,94 @@ def test_decode_over_the_compacted_layer_uses_offsets_and_budgets():
         for h in range(w.Hq):
             p = scipy.special.softmax(K[h // 2] @ q[b, h].astype(np.float64) / math.sqrt(w.D))
             np.testing.assert_allclose(o[b, h], p @ V[h // 2], rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------- prefill attention (f3's attention) ----
+# o_{h,t} = softmax(q_{h,t} K_g[0..t]^T / sqrt(D)) V_g[0..t] at every position t
+# of the regrouped sequence (the KV-cache primer page, section 2.1, the o_t
+# equation at each step of the prompt).
+
+def _prefill_inputs(w, rng, kscale=1.0):
+    S = w.Nv + w.Nt
+    q = rng.standard_normal((w.B, w.Hq, S, w.D)).astype(np.float32)
+    k = (rng.standard_normal((w.B, w.Hkv, S, w.D)) * kscale).astype(np.float32)
+    v = rng.standard_normal((w.B, w.Hkv, S, w.D)).astype(np.float32)
+    if w.dtype == "bf16":
+        q, k, v = wl.f32_to_bf16_bits(q), wl.f32_to_bf16_bits(k), wl.f32_to_bf16_bits(v)
+    return q, k, v
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_first_position_returns_its_value(dtype):
+    """Position 0 sees one key: its output is v_0 of its KV head, exactly."""
+    w = wl.custom(Nv=5, Nt=3, Hq=6, Hkv=2, D=16, B=2, dtype=dtype)
+    q, k, v = _prefill_inputs(w, np.random.default_rng(1))
+    for b in range(w.B):
+        o = oracle.prefill_attention(w, q[0:w.B], k, v, b, 0, 1)
+        for h in range(w.Hq):
+            assert np.array_equal(o[h, 0], _f64(w, v)[b, h // 3, 0])
+
+
+def test_prefill_equal_keys_give_the_running_mean():
+    """All keys of a head equal: uniform weights over 0..t, so o_t is the mean
+    of v_0..v_t (a causal mask that leaked later keys would fail)."""
+    w = wl.custom(Nv=6, Nt=4, Hq=4, Hkv=2, D=8)
+    q, k, v = _prefill_inputs(w, np.random.default_rng(2))
+    k[:] = k[:, :, :1]
+    o = oracle.prefill_attention(w, q, k, v, 0)
+    V = _f64(w, v)[0]
+    for h in range(w.Hq):
+        for t in range(w.Nv + w.Nt):
+            np.testing.assert_allclose(o[h, t], V[h // 2, :t + 1].mean(axis=0), rtol=0, atol=1e-12)
+
+
+def test_prefill_two_keys_closed_form():
+    """Position 1 weighs v_1 by the logistic function of (q.k_1 - q.k_0)/sqrt(D)."""
+    w = wl.custom(Nv=3, Nt=2, Hq=2, Hkv=1, D=8)
+    q, k, v = _prefill_inputs(w, np.random.default_rng(3), kscale=2.0)
+    o = oracle.prefill_attention(w, q, k, v, 0, 1, 1)
+    Q, K, V = _f64(w, q)[0], _f64(w, k)[0, 0], _f64(w, v)[0, 0]
+    for h in range(w.Hq):
+        d = (Q[h, 1] @ K[1] - Q[h, 1] @ K[0]) / math.sqrt(w.D)
+        p1 = 1.0 / (1.0 + math.exp(-d))
+        np.testing.assert_allclose(o[h, 0], (1.0 - p1) * V[0] + p1 * V[1], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("shape", [dict(Hq=1, Hkv=1), dict(Hq=6, Hkv=2), dict(Hq=4, Hkv=4, dtype="bf16")])
+def test_prefill_matches_library_softmax(seed, shape):
+    """Brute force: scipy's softmax over the masked score matrix, query head h
+    on KV head h // G, rows from a middle offset."""
+    w = wl.custom(Nv=7, Nt=5, D=16, B=2, **shape)
+    q, k, v = _prefill_inputs(w, np.random.default_rng(20 + seed), kscale=1.5)
+    b, row0 = seed % 2, 3
+    o = oracle.prefill_attention(w, q, k, v, b, row0, w.Nv + w.Nt - row0)
+    Q, K, V = _f64(w, q)[b], _f64(w, k)[b], _f64(w, v)[b]
+    G, S = w.Hq // w.Hkv, w.Nv + w.Nt
+    mask = np.tril(np.ones((S, S), bool))
+    for h in range(w.Hq):
+        z = np.where(mask, Q[h] @ K[h // G].T / math.sqrt(w.D), -np.inf)
+        ref = scipy.special.softmax(z, axis=1) @ V[h // G]
+        np.testing.assert_allclose(o[h], ref[row0:], rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_ignores_later_positions():
+    """Causality: changing keys and values after position t leaves o_t alone."""
+    w = wl.custom(Nv=6, Nt=4, Hq=2, Hkv=2, D=8)
+    q, k, v = _prefill_inputs(w, np.random.default_rng(4))
+    a = oracle.prefill_attention(w, q, k, v, 0)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, 6:] *= -3.0
+    v2[:, :, 6:] += 5.0
+    b = oracle.prefill_attention(w, q, k2, v2, 0)
+    np.testing.assert_array_equal(a[:, :6], b[:, :6])
+    assert not np.allclose(a[:, 6:], b[:, 6:])
+
+
+def test_prefill_dominant_key_selects_its_value():
+    w = wl.custom(Nv=4, Nt=4, Hq=2, Hkv=1, D=16)
+    q, k, v = _prefill_inputs(w, np.random.default_rng(5), kscale=0.01)
+    t = 6
+    k[0, 0, 2] = 40.0 * q[0, 0, t] / np.linalg.norm(q[0, 0, t])  # a key along head 0's query t
+    o = oracle.prefill_attention(w, q, k, v, 0, t, 1)
+    np.testing.assert_allclose(o[0, 0], v[0, 0, 2], atol=1e-6)
