@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-decode", action="store_true",
                     help="do not time decode attention and int8 quantisation over the compacted cache")
+    ap.add_argument("--skip-prefill", action="store_true",
+                    help="skip the prefill attention timing (aircache_prefill_layer / _attention)")
+    ap.add_argument("--prefill-reps", type=int, default=5, help="timed repetitions of each prefill variant")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (the reference kernel that scales "
@@ -238,7 +241,7 @@ def main():
     a = parse()
     if a.gpus != 1:
         print(f"bench.py measures one GPU: the pass runs on a single MI355X; --gpus {a.gpus} is not "
-              "supported (see the sharding notes in DESIGN.md)", file=sys.stderr)
+              "supported (the pass shards by sample, layer or KV head; that path is not built)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -451,6 +454,53 @@ def main():
         quant = {"kernels": ["quantize_i8_kernel"], "us_per_call": q_us, "algorithmic_bytes": q_bytes,
                  "achieved_gbps": q_bytes / (q_us * 1e-6) / 1e9, "peak_gbps": PEAK_HBM_GBPS,
                  "frac": q_bytes / (q_us * 1e-6) / 1e9 / PEAK_HBM_GBPS}
+    # Prefill attention of every layer (bfloat16 workloads): alone
+    # (aircache_prefill_attention), with the scores fused in
+    # (aircache_prefill_layer) plus the compaction, and alone followed by the
+    # separate pass (aircache_run); the first input copy, its visual queries
+    # drawn by workloads.visual_queries.
+    pf = None
+    if not a.skip_prefill and w.dtype == wl.BF16:
+        def dev_bits(arr):
+            return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+        qa = [dev_bits(wl.prefill_queries(inp, l)) for l in range(w.L)]
+        q0, k0, v0 = copies[0]
+        po = [torch.empty_like(t) for t in qa]
+        pplan = ac.alloc_plan()
+        bp_plain = ac.bind_prefill(qa, k0, v0, po, None, stream=stream)
+        bp_fused = ac.bind_prefill(qa, k0, v0, po, pplan, stream=stream)
+        bcomp = ac.bind(q0, k0, v0, pplan, k_out, v_out, stream=stream)
+        bpass = bound[0].with_status(status_words[0].data_ptr())
+
+        def timed(fn):
+            fn()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(a.prefill_reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return 1e3 * e0.elapsed_time(e1) / a.prefill_reps
+
+        us_plain = timed(bp_plain)
+        us_fused = timed(lambda: (bp_fused(), bcomp.compress()))
+        us_sep = timed(lambda: (bp_plain(), bpass.run()))
+        if int(pplan.status.item()) != 0:
+            raise RuntimeError(f"device status {int(pplan.status.item())} after the fused prefill")
+        S = w.Nv + w.Nt
+        flops = 4.0 * w.D * S * (S + 1) / 2 * w.B * w.Hq * w.L  # causal QK^T and PV, every layer
+        tf = flops / (us_plain * 1e-6) / 1e12
+        pf = {"kernels": ["prefill_kernel", "elite_select_kernel", "finalize_kernel", "topk_select_kernel",
+                          "kv_gather_kernel"],
+              "layers": w.L, "reps": a.prefill_reps,
+              "us_attention_only": us_plain,
+              "us_fused_scores_and_compaction": us_fused,
+              "us_attention_then_separate_pass": us_sep,
+              "fused_overhead_frac": us_fused / us_plain - 1.0,
+              "separate_overhead_frac": us_sep / us_plain - 1.0,
+              "attention_flops": flops, "attention_tflops": tf, "peak_tflops": PEAK_MFMA_TFLOPS["bf16"],
+              "attention_frac_of_mfma_peak": tf / PEAK_MFMA_TFLOPS["bf16"]}
+        del qa, po
     ceil = hbm_ceilings()
 
     tokens = w.L * w.B * w.Nv
@@ -510,6 +560,9 @@ def main():
         # timed after the pass, not part of its step)
         "decode_attention": dec,
         "quantize_i8": quant,
+        # prefill attention with the scores fused in, against the attention
+        # alone and the attention followed by the separate pass
+        "prefill": pf,
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, a.cpu_seconds)

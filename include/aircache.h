@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define AIRCACHE_ABI_VERSION 2
+#define AIRCACHE_ABI_VERSION 3
 #define AIRCACHE_MAX_LAYERS 128
 
 typedef enum {
@@ -329,6 +329,48 @@ size_t aircache_decode_workspace_size(const aircache_desc *desc);
 int aircache_decode(const aircache_desc *desc, const void *const *q_dec, const aircache_plan_buf *plan,
                     const void *const *k_out, const void *const *v_out, float *const *o, void *workspace,
                     size_t ws_bytes, void *stream);
+
+/* Prefill attention of one layer with the pass's scoring fused in: the
+ * attention is the KV-cache primer page's (devpress.csdn.net) section 2.1
+ * o_t equation at every position t of the regrouped sequence (visual tokens
+ * first, then text), each position attending to the keys 0..t:
+ *   o[b][h][t] = softmax(q[b][h][t] . K_g[0..t]^T / sqrt(head_dim)) V_g[0..t],
+ * g = h / (n_q_heads / n_kv_heads), float32 accumulation, the probabilities
+ * rounded to bfloat16 for the product with V, the output rounded to bfloat16.
+ * The same call writes layer `layer`'s rows of the plan as aircache_plan
+ * would (elite set, I_v, s_t, s_k; the AirCache paper-notes page, "Elite
+ * Observation Window" and the strength and skewness equations): the elite
+ * rows' logits against the visual keys are taken from the attention itself,
+ * so the visual keys are read once. The call for the last layer also computes
+ * the budgets and the top-r_hat selection of every layer ("Layer-wise KV Cache
+ * Budget Allocation"), after which the plan is complete and aircache_compress
+ * compacts the cache.
+ *   layer       : 0 .. n_layers - 1; the calls for one pass are made for the
+ *                 layers 0, 1, .., n_layers - 1 in this order on one stream
+ *                 (layer 0 opens the pass and clears plan->status)
+ *   q           : device [batch][n_q_heads][n_vis + n_txt][head_dim], every
+ *                 position's query (the text rows are the pass's q_txt)
+ *   k, v        : device [batch][n_kv_heads][n_vis + n_txt][head_dim]
+ *   o           : device [batch][n_q_heads][n_vis + n_txt][head_dim] (written;
+ *                 must not overlap q, k or v)
+ *   plan        : as for aircache_plan (every output pointer but budget_x may
+ *                 be used; iv_head with AIRCACHE_SELECT_PER_KV_HEAD)
+ *   workspace   : device scratch of ws_bytes >=
+ *                 aircache_prefill_workspace_size(desc), kept by the caller
+ *                 across the layer calls of one pass (one layer's scoring
+ *                 terms plus the pass's counters; no zeroing needed)
+ * bfloat16 only (AIRCACHE_EINVAL for float32); head_dim 64 or 128; all
+ * pointers 16-byte aligned. The descriptor's path is ignored; max_elite caps
+ * the elite rows that are scored per (layer, sample) as on the other paths
+ * (overflow is flagged in plan->status). */
+size_t aircache_prefill_workspace_size(const aircache_desc *desc);
+int aircache_prefill_layer(const aircache_desc *desc, int32_t layer, const void *q, const void *k, const void *v,
+                           void *o, const aircache_plan_buf *plan, void *workspace, size_t ws_bytes, void *stream);
+
+/* The same prefill attention of one layer without the scoring: o only, no
+ * plan and no workspace (arguments as for aircache_prefill_layer). */
+int aircache_prefill_attention(const aircache_desc *desc, const void *q, const void *k, const void *v, void *o,
+                               void *stream);
 
 /* Instrumented variants of aircache_plan / aircache_compress / aircache_run for
  * timing individual kernels. events is a host array of hipEvent_t handles created by

@@ -23,7 +23,8 @@ EXPORTS = ["aircache_abi_version", "aircache_workspace_size", "aircache_max_comp
            "aircache_resolved_path", "aircache_run_launches",
            "aircache_plan", "aircache_compress", "aircache_run", "aircache_plan_profiled",
            "aircache_compress_profiled", "aircache_run_profiled", "aircache_run_noalloc", "aircache_strerror",
-           "aircache_last_error", "aircache_decode_workspace_size", "aircache_decode", "aircache_quantize_i8"]
+           "aircache_last_error", "aircache_decode_workspace_size", "aircache_decode", "aircache_quantize_i8",
+           "aircache_prefill_workspace_size", "aircache_prefill_layer", "aircache_prefill_attention"]
 NOALLOC_SCRATCH_BYTES = 128 << 20  # AIRCACHE_NOALLOC_SCRATCH_BYTES
 PLAN_KERNELS = ["elite_select", "cross_score", "finalize", "topk_select"]
 COMPRESS_KERNELS = ["kv_gather"]
@@ -92,6 +93,13 @@ def load() -> C.CDLL:
         lib.aircache_decode.argtypes = [C.POINTER(Desc), P, C.POINTER(PlanBuf), P, P, P, P, C.c_size_t, P]
         lib.aircache_quantize_i8.restype = C.c_int
         lib.aircache_quantize_i8.argtypes = [C.POINTER(Desc), C.POINTER(PlanBuf), P, P, P, P, P, P, P]
+        lib.aircache_prefill_workspace_size.restype = C.c_size_t
+        lib.aircache_prefill_workspace_size.argtypes = [C.POINTER(Desc)]
+        lib.aircache_prefill_layer.restype = C.c_int
+        lib.aircache_prefill_layer.argtypes = [C.POINTER(Desc), C.c_int32, P, P, P, P, C.POINTER(PlanBuf), P,
+                                               C.c_size_t, P]
+        lib.aircache_prefill_attention.restype = C.c_int
+        lib.aircache_prefill_attention.argtypes = [C.POINTER(Desc), P, P, P, P, P]
         lib.aircache_strerror.restype = C.c_char_p
         lib.aircache_strerror.argtypes = [C.c_int]
         lib.aircache_last_error.restype = C.c_char_p
@@ -179,3 +187,21 @@ def quantize_i8(desc: Desc, buf: PlanBuf, ko_ptrs, vo_ptrs, kq_ptrs, vq_ptrs, k_
     ko, vo, kq, vq = [ptr_array(p) for p in (ko_ptrs, vo_ptrs, kq_ptrs, vq_ptrs)]
     return load().aircache_quantize_i8(C.byref(desc), C.byref(buf), ko, vo, kq, vq, C.c_void_p(k_scale),
                                        C.c_void_p(v_scale), C.c_void_p(stream))
+
+
+def prefill_workspace_size(desc: Desc) -> int:
+    return int(load().aircache_prefill_workspace_size(C.byref(desc)))
+
+
+def prefill_layer(desc: Desc, layer: int, q: int, k: int, v: int, o: int, buf: PlanBuf, ws_ptr: int,
+                  ws_bytes: int, stream: int) -> int:
+    """aircache_prefill_layer: one layer's prefill attention with its scores."""
+    return load().aircache_prefill_layer(C.byref(desc), int(layer), C.c_void_p(q), C.c_void_p(k), C.c_void_p(v),
+                                         C.c_void_p(o), C.byref(buf), C.c_void_p(ws_ptr), ws_bytes,
+                                         C.c_void_p(stream))
+
+
+def prefill_attention(desc: Desc, q: int, k: int, v: int, o: int, stream: int) -> int:
+    """aircache_prefill_attention: one layer's prefill attention alone."""
+    return load().aircache_prefill_attention(C.byref(desc), C.c_void_p(q), C.c_void_p(k), C.c_void_p(v),
+                                             C.c_void_p(o), C.c_void_p(stream))

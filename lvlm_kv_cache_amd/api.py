@@ -264,6 +264,54 @@ class AirCache:
         marshalling done once, here."""
         return BoundDecode(self, q_dec, plan, k_out, v_out, o, stream)
 
+    # -- prefill attention with the scores fused in (aircache_prefill_layer) --
+    def _check_prefill(self, q, k, v, o):
+        s = self.shape
+        S = s["Nv"] + s["Nt"]
+        for name, t, shp in (("q", q, (s["B"], s["Hq"], S, s["D"])), ("k", k, (s["B"], s["Hkv"], S, s["D"])),
+                             ("v", v, (s["B"], s["Hkv"], S, s["D"])), ("o", o, (s["B"], s["Hq"], S, s["D"]))):
+            if t.device != self.device or t.dtype != self.dtype or not t.is_contiguous() or tuple(t.shape) != shp:
+                raise ValueError(f"{name} must be a contiguous {self.dtype} tensor of shape {shp} on {self.device}")
+
+    @property
+    def prefill_workspace(self) -> torch.Tensor:
+        """The scoring workspace of the prefill calls (one layer's scoring
+        terms and the pass's counters), allocated on first use."""
+        if getattr(self, "_pf_ws", None) is None:
+            n = _lib.prefill_workspace_size(self.desc)
+            if n == 0:
+                _lib.check(_lib.AIRCACHE_EINVAL)
+            self._pf_ws = torch.zeros(n, dtype=torch.uint8, device=self.device)
+        return self._pf_ws
+
+    def prefill_layer(self, layer: int, q, k, v, o, plan: PlanOutputs, stream=None):
+        """Causal prefill attention of one layer (aircache_prefill_layer):
+        o = softmax(q K^T / sqrt(D), causal) V with q, o [B][H_q][N_v+N_t][D]
+        and k, v [B][H_kv][N_v+N_t][D] (bfloat16), writing that layer's elite
+        set, I_v and statistics into plan; the call for the last layer also
+        budgets and selects every layer. Call for layers 0..L-1 in order on
+        one stream, then compress()."""
+        self._check_prefill(q, k, v, o)
+        ws = self.prefill_workspace
+        _lib.check(_lib.prefill_layer(self.desc, layer, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                      plan.buf(), ws.data_ptr(), ws.numel(), self._stream(stream)))
+        return o
+
+    def prefill_attention(self, q, k, v, o=None, stream=None):
+        """The same attention of one layer without the scores
+        (aircache_prefill_attention)."""
+        o = torch.empty_like(q) if o is None else o
+        self._check_prefill(q, k, v, o)
+        _lib.check(_lib.prefill_attention(self.desc, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                          self._stream(stream)))
+        return o
+
+    def bind_prefill(self, q, k, v, o, plan: PlanOutputs | None, stream=None) -> "BoundPrefill":
+        """A BoundPrefill running every layer's prefill attention (with the
+        scores when plan is given) over these per-layer tensor lists, checked
+        and marshalled once, here."""
+        return BoundPrefill(self, q, k, v, o, plan, stream)
+
     def compress(self, plan: PlanOutputs, k, v, k_out, v_out, stream=None, events=None) -> None:
         s = self.shape
         shp = (s["B"], s["Hkv"], s["Nv"] + s["Nt"], s["D"])
@@ -423,4 +471,45 @@ class BoundDecode:
                                        self._ws_bytes, self._st)
         if rc:
             _lib.check(rc)
+        return self.out
+
+
+class BoundPrefill:
+    """The prefill calls of every layer over fixed per-layer tensors,
+    validated and marshalled once (as BoundPass does for the pass): with a
+    plan, aircache_prefill_layer for layers 0..L-1 (the plan is complete after
+    the last); without, aircache_prefill_attention per layer. The tensors must
+    stay alive while it is used."""
+
+    def __init__(self, ac: "AirCache", q, k, v, o, plan: PlanOutputs | None, stream=None):
+        L = ac.shape["L"]
+        for name, ts in (("q", q), ("k", k), ("v", v), ("o", o)):
+            if len(ts) != L:
+                raise ValueError(f"{name}: {len(ts)} layers given, {L} expected")
+        for l in range(L):
+            ac._check_prefill(q[l], k[l], v[l], o[l])
+        self.out = o
+        self._keep = (ac, q, k, v, o, plan)
+        self._lib = _lib.load()
+        self._desc = _lib.C.byref(ac.desc)
+        V = _lib.C.c_void_p
+        self._args = [(V(q[l].data_ptr()), V(k[l].data_ptr()), V(v[l].data_ptr()), V(o[l].data_ptr()))
+                      for l in range(L)]
+        self._st = V(ac._stream(stream))
+        self._score = plan is not None
+        if self._score:
+            self._buf = plan.buf()
+            self._pbuf = _lib.C.byref(self._buf)
+            ws = ac.prefill_workspace
+            self._ws, self._ws_bytes = V(ws.data_ptr()), ws.numel()
+
+    def __call__(self):
+        f = self._lib.aircache_prefill_layer if self._score else self._lib.aircache_prefill_attention
+        for l, (q, k, v, o) in enumerate(self._args):
+            if self._score:
+                rc = f(self._desc, l, q, k, v, o, self._pbuf, self._ws, self._ws_bytes, self._st)
+            else:
+                rc = f(self._desc, q, k, v, o, self._st)
+            if rc:
+                _lib.check(rc)
         return self.out

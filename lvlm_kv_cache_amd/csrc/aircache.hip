@@ -40,6 +40,9 @@ struct Shape {
   int window;       // 0: the elite window; k > 0: the last k text tokens (k <= N_t)
   int nsel;         // selections per (layer, sample): 1, or H_kv (one per KV head)
   int per_head;     // one selection per KV head (I_v^g written to plan.iv_head)
+  int lb0;          // first (layer * B + sample) of a one-layer launch (prefill), else 0
+  int nstat;        // (max, sum) pairs per row in the scoring statistics: ntiles, +1 on the prefill path
+  int qrows, qoff;  // rows per query head in the query buffers and the first text row among them
 };
 
 struct PlanPtrs {
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(256) void cross_score_kernel(Shape sh, LayerTable q
   }
 
   float *e_out = ws.e + (size_t)u * sh.Nv * sh.rcap16;
-  float2 *st_out = ws.stats + (size_t)u * sh.rcap16 * sh.ntiles;
+  float2 *st_out = ws.stats + (size_t)u * sh.rcap16 * sh.nstat;
   for (int rt = 0; rt * 16 < R; ++rt) {
     const int r = rt * 16 + n;
     Frag<Tag> qf[D / 32];
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(256) void cross_score_kernel(Shape sh, LayerTable q
     if (lane < 16) red_z[wave][lane] = zs;
     __syncthreads();
     zs = red_z[0][n] + red_z[1][n] + red_z[2][n] + red_z[3][n];
-    if (r < R && wave == 0 && grp == 0) st_out[(size_t)r * sh.ntiles + t] = make_float2(m, zs);
+    if (r < R && wave == 0 && grp == 0) st_out[(size_t)r * sh.nstat + t] = make_float2(m, zs);
     // rows R .. RP-1 of the last row tile are written as zeros, so that readers
     // can sum whole 16-row groups without masking
 #pragma unroll
@@ -364,7 +367,8 @@ __global__ __launch_bounds__(256) void finalize_kernel(Shape sh, PlanPtrs plan, 
   __shared__ int flag;
   const int tid = threadIdx.x;
   const int t = blockIdx.x % sh.ntiles;
-  const int lb = blockIdx.x / sh.ntiles, b = lb % sh.B;
+  const int lb = sh.lb0 + blockIdx.x / sh.ntiles, b = lb % sh.B;
+  const int lbw = lb - sh.lb0;  // index of (layer, sample) in the scoring workspace
   int ntk = plan.n_elite[lb];
   if (ntk > sh.cap) ntk = sh.cap;
   if (ntk < 0) ntk = 0;
@@ -374,13 +378,13 @@ __global__ __launch_bounds__(256) void finalize_kernel(Shape sh, PlanPtrs plan, 
     const int g = idx / RP, r = idx - g * RP;
     float wv = 0.f;
     if (r < R) {
-      const float2 *st = ws.stats + ((size_t)(lb * sh.Hkv + g) * sh.rcap16 + r) * sh.ntiles;
+      const float2 *st = ws.stats + ((size_t)(lbw * sh.Hkv + g) * sh.rcap16 + r) * sh.nstat;
       // online merge of the tiles' (max, sum) in ascending tile order, eight loads at a time
       float M = -INFINITY, Z = 0.f;
-      for (int t0 = 0; t0 < sh.ntiles; t0 += 8) {
+      for (int t0 = 0; t0 < sh.nstat; t0 += 8) {
         float2 v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = (t0 + j < sh.ntiles) ? st[t0 + j] : make_float2(-INFINITY, 0.f);
+        for (int j = 0; j < 8; ++j) v[j] = (t0 + j < sh.nstat) ? st[t0 + j] : make_float2(-INFINITY, 0.f);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           if (v[j].x == -INFINITY) continue;
@@ -402,7 +406,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(Shape sh, PlanPtrs plan, 
     float acc = 0.f;
     for (int g = 0; g < sh.Hkv; ++g) {
       const f32x4_t *e4 =
-          reinterpret_cast<const f32x4_t *>(ws.e + (size_t)(lb * sh.Hkv + g) * sh.Nv * sh.rcap16 + (size_t)c * RP);
+          reinterpret_cast<const f32x4_t *>(ws.e + (size_t)(lbw * sh.Hkv + g) * sh.Nv * sh.rcap16 + (size_t)c * RP);
       const f32x4_t *w4 = reinterpret_cast<const f32x4_t *>(wl + g * RP);
       float ag = 0.f;
       for (int r0 = 0; r0 < RP / 4; r0 += 4) {  // RP is a multiple of 16
@@ -763,6 +767,7 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
 #include "pass_chunked.h"
 #include "small.h"
 #include "decode.h"
+#include "prefill.h"
 
 // ----------------------------------------------------------------------------
 // Step 1: elite observation window ("Elite Observation Window", the Att and k
@@ -788,7 +793,7 @@ __global__ __launch_bounds__(kEliteThreads) void elite_select_kernel(Shape sh, L
   __shared__ float red[kEliteWaves];
   __shared__ int wtot[kEliteWaves];
   __shared__ int flag;
-  const int lb = blockIdx.x / sh.Hkv, g = blockIdx.x - lb * sh.Hkv;
+  const int lb = sh.lb0 + (int)blockIdx.x / sh.Hkv, g = (int)blockIdx.x % sh.Hkv;
   const int l = lb / sh.B, b = lb % sh.B;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, grp = lane >> 4;
@@ -829,7 +834,7 @@ __global__ __launch_bounds__(kEliteThreads) void elite_select_kernel(Shape sh, L
       const int nh = min(16, G - h0);
       const int key = kt_ * 16 + n;
       if (it < items && n < nh) {
-        const E *qrow = q + ((size_t)(b * sh.Hq + g * G + h0 + n) * Nt + (Nt - 1)) * D;
+        const E *qrow = q + ((size_t)(b * sh.Hq + g * G + h0 + n) * sh.qrows + sh.qoff + (Nt - 1)) * D;
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) qf[bi][c].load(qrow + c * 32 + grp * 8);
       } else {
@@ -883,7 +888,7 @@ __global__ __launch_bounds__(kEliteThreads) void elite_select_kernel(Shape sh, L
   }
   __syncthreads();
   // this KV head's part of pbar, heads in ascending order
-  float *part = ws.pbar_part + (size_t)blockIdx.x * Nt;
+  float *part = ws.pbar_part + (size_t)(lb * sh.Hkv + g) * Nt;
   for (int j = tid; j < Nt; j += kEliteThreads) {
     float a = 0.f;
     for (int h = 0; h < G; ++h) a += z[(size_t)h * Nt + j];
@@ -1349,6 +1354,10 @@ int make_config(const aircache_desc *d, Config *cfg) {
   s.window = d->obs_window < d->n_txt ? d->obs_window : d->n_txt;
   s.nsel = per_head ? s.Hkv : 1;
   s.per_head = per_head ? 1 : 0;
+  s.lb0 = 0;
+  s.nstat = s.ntiles;
+  s.qrows = s.Nt;
+  s.qoff = 0;
   const int esz = d->dtype == AIRCACHE_BF16 ? 2 : 4;
   (void)esz;
   cfg->elite_lds = (size_t)(s.G > 1 ? s.G : 1) * s.Nt * sizeof(float);
@@ -2013,6 +2022,133 @@ int launch_decode(const Shape &s, const DecodeTables &tb, const aircache_plan_bu
   return check_hip(hipGetLastError(), "decode_combine_kernel launch");
 }
 
+// ----------------------------------------------------------------------------
+// Prefill attention with the scores of the text rows (prefill.h). One call per
+// layer: prefill_elite_kernel (elite_select_kernel when a sample's text
+// logits do not fit one workgroup's LDS) -> prefill_kernel ->
+// prefill_finalize_kernel, and after the
+// last layer topk_select_kernel. The scoring workspace holds one layer; the
+// counters and the elite parts hold every layer (the last layer's finalize
+// computes the budgets of all layers, as on the tiled path).
+// ----------------------------------------------------------------------------
+struct PrefillCfg {
+  Config cfg;  // T = 64 (the attention's key tile), one more statistics pair per row
+  int nqt_vis, nqt_txt;
+  long long grid;
+  size_t lds;
+  int evs;           // row stride of the exponentials: N_v rounded up to the key tile
+  size_t fin_lds;    // prefill_finalize_kernel's row weights or I_v
+  bool one_wg_elite; // prefill_elite_kernel: every query head's text logits of a sample fit one LDS
+};
+
+int make_prefill_config(const aircache_desc *d, PrefillCfg *pc) {
+  if (!d) return fail(AIRCACHE_EINVAL, "desc is NULL");
+  aircache_desc dd = *d;
+  dd.path = AIRCACHE_PATH_TILED;  // the tiled path's finalize and top-k kernels
+  int rc;
+  if ((rc = make_config(&dd, &pc->cfg))) return rc;
+  if (d->dtype != AIRCACHE_BF16) return fail(AIRCACHE_EINVAL, "the prefill attention takes bfloat16 inputs");
+  Config &cfg = pc->cfg;
+  Shape &s = cfg.sh;
+  s.T = kPfKeys;
+  s.ntiles = (s.Nv + kPfKeys - 1) / kPfKeys;
+  s.nstat = s.ntiles + 1;
+  s.qrows = s.S;
+  s.qoff = s.Nv;
+  pc->nqt_vis = (s.Nv + kPfRows - 1) / kPfRows;
+  pc->nqt_txt = (s.Nt + kPfRows - 1) / kPfRows;
+  pc->grid = (long long)s.B * s.Hq * (pc->nqt_vis + pc->nqt_txt);
+  if (pc->grid > INT32_MAX) return fail(AIRCACHE_EINVAL, "prefill grid of %lld workgroups too large", pc->grid);
+  pc->lds = s.D == 128 ? (size_t)PfLayout<128>::kBytes : (size_t)PfLayout<64>::kBytes;
+  const size_t units = (size_t)s.B * s.Hkv;  // one layer
+  pc->evs = s.ntiles * kPfKeys;
+  pc->one_wg_elite = prefill_elite_lds(s.Hq, s.Nt) <= kMaxLds;
+  pc->fin_lds = (size_t)(s.rcap16 > s.Nv ? s.rcap16 : s.Nv) * sizeof(float);
+  cfg.off_e = cfg.off_stats + align_up(units * s.rcap16 * (size_t)s.nstat * sizeof(float2));
+  cfg.off_part = cfg.off_e + align_up(units * s.rcap16 * (size_t)pc->evs * sizeof(float));
+  cfg.ws_bytes = cfg.off_part + align_up(units * (size_t)s.Nv * sizeof(float));
+  return AIRCACHE_OK;
+}
+
+int check_prefill_io(const PrefillCfg &pc, const void *q, const void *k, const void *v, const void *o) {
+  if (!q || !k || !v || !o) return fail(AIRCACHE_EINVAL, "q, k, v or o is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(AIRCACHE_EINVAL, "q, k, v and o must be 16-byte aligned");
+  const Shape &s = pc.cfg.sh;
+  const size_t qb = (size_t)s.B * s.Hq * s.S * s.D * 2, kb = (size_t)s.B * s.Hkv * s.S * s.D * 2;
+  const char *oc = static_cast<const char *>(o);
+  auto overlap = [&](const void *p, size_t n) {
+    const char *c = static_cast<const char *>(p);
+    return c < oc + qb && oc < c + n;
+  };
+  if (overlap(q, qb) || overlap(k, kb) || overlap(v, kb)) return fail(AIRCACHE_EINVAL, "o overlaps q, k or v");
+  return AIRCACHE_OK;
+}
+
+template <int D>
+int launch_prefill(const PrefillCfg &pc, int layer, const void *q, const void *k, const void *v, void *o,
+                   const aircache_plan_buf *plan, void *ws_base, hipStream_t st) {
+  Config cfg = pc.cfg;
+  Shape &s = cfg.sh;
+  PrefillArgs a;
+  a.q = static_cast<const uint16_t *>(q);
+  a.k = static_cast<const uint16_t *>(k);
+  a.v = static_cast<const uint16_t *>(v);
+  a.o = static_cast<uint16_t *>(o);
+  a.nqt_vis = pc.nqt_vis;
+  a.nqt_txt = pc.nqt_txt;
+  a.layer = layer;
+  int rc;
+  if (!plan) {
+    a.score = 0;
+    a.elite = a.n_elite = nullptr;
+    a.e = nullptr;
+    a.stats = nullptr;
+    a.evs = 0;
+    if ((rc = allow_lds(prefill_kernel<D, false>, pc.lds))) return rc;
+    hipLaunchKernelGGL((prefill_kernel<D, false>), dim3((unsigned)pc.grid), dim3(kPfThreads), pc.lds, st, s, a);
+    return check_hip(hipGetLastError(), "prefill_kernel launch");
+  }
+  s.lb0 = layer * s.B;
+  const PlanPtrs pp = plan_ptrs(plan);
+  const Ws ws = ws_of(cfg, ws_base);
+  LayerTable qt, kt;
+  for (int l = 0; l < AIRCACHE_MAX_LAYERS; ++l) qt.p[l] = kt.p[l] = nullptr;
+  qt.p[layer] = q;
+  kt.p[layer] = k;
+  a.score = 1;
+  a.elite = plan->elite_idx + (size_t)s.lb0 * s.Nt;
+  a.n_elite = plan->n_elite + s.lb0;
+  a.e = ws.e;
+  a.stats = ws.stats;
+  a.evs = pc.evs;
+  if ((rc = allow_lds(prefill_kernel<D, true>, pc.lds))) return rc;
+  if ((rc = allow_lds(prefill_finalize_kernel, pc.fin_lds))) return rc;
+  if (pc.one_wg_elite) {
+    // every query head of a sample in one workgroup
+    const size_t elds = prefill_elite_lds(s.Hq, s.Nt);
+    if ((rc = allow_lds(prefill_elite_kernel<D>, elds))) return rc;
+    hipLaunchKernelGGL((prefill_elite_kernel<D>), dim3((unsigned)s.B), dim3(kPfEliteThreads), elds, st, s, a.q, a.k,
+                       pp, ws);
+    if ((rc = check_hip(hipGetLastError(), "prefill_elite_kernel launch"))) return rc;
+  } else {
+    if ((rc = allow_lds(elite_select_kernel<Bf16Tag, D>, cfg.elite_lds))) return rc;
+    hipLaunchKernelGGL((elite_select_kernel<Bf16Tag, D>), dim3((unsigned)(s.B * s.Hkv)), dim3(kEliteThreads),
+                       cfg.elite_lds, st, s, qt, kt, pp, ws);
+    if ((rc = check_hip(hipGetLastError(), "elite_select_kernel launch"))) return rc;
+  }
+  hipLaunchKernelGGL((prefill_kernel<D, true>), dim3((unsigned)pc.grid), dim3(kPfThreads), pc.lds, st, s, a);
+  if ((rc = check_hip(hipGetLastError(), "prefill_kernel launch"))) return rc;
+  hipLaunchKernelGGL(prefill_finalize_kernel, dim3((unsigned)(s.B * s.Hkv * s.ntiles)), dim3(kPfFinThreads),
+                     pc.fin_lds, st, s, pp, ws, static_cast<const float *>(ws.e), pc.evs);
+  if ((rc = check_hip(hipGetLastError(), "prefill_finalize_kernel launch"))) return rc;
+  if (layer == s.L - 1) {
+    hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)(s.L * s.B * s.nsel)), dim3(kTopkThreads), 0, st, s, pp);
+    if ((rc = check_hip(hipGetLastError(), "topk_select_kernel launch"))) return rc;
+  }
+  return AIRCACHE_OK;
+}
+
 extern "C" {
 
 int aircache_abi_version(void) { return AIRCACHE_ABI_VERSION; }
@@ -2227,6 +2363,39 @@ int aircache_quantize_i8(const aircache_desc *desc, const aircache_plan_buf *pla
     hipLaunchKernelGGL(quantize_i8_kernel<F32Tag>, grid, dim3(kQuantThreads), 0, st, s, tb, plan_ptrs(plan),
                        k_scale, v_scale, cap);
   return check_hip(hipGetLastError(), "quantize_i8_kernel launch");
+}
+
+size_t aircache_prefill_workspace_size(const aircache_desc *desc) {
+  PrefillCfg pc;
+  if (make_prefill_config(desc, &pc)) return 0;
+  return pc.cfg.ws_bytes;
+}
+
+int aircache_prefill_layer(const aircache_desc *desc, int32_t layer, const void *q, const void *k, const void *v,
+                           void *o, const aircache_plan_buf *plan, void *workspace, size_t ws_bytes, void *stream) {
+  PrefillCfg pc;
+  int rc;
+  if ((rc = make_prefill_config(desc, &pc))) return rc;
+  if (layer < 0 || layer >= pc.cfg.sh.L) return fail(AIRCACHE_EINVAL, "layer=%d outside [0, %d)", layer, pc.cfg.sh.L);
+  if ((rc = check_plan_buf(plan, false, pc.cfg))) return rc;
+  if ((rc = check_prefill_io(pc, q, k, v, o))) return rc;
+  if (!workspace || ws_bytes < pc.cfg.ws_bytes)
+    return fail(AIRCACHE_EWORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, pc.cfg.ws_bytes);
+  if (!aligned16(workspace)) return fail(AIRCACHE_EINVAL, "workspace is not 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (pc.cfg.sh.D == 128) return launch_prefill<128>(pc, layer, q, k, v, o, plan, workspace, st);
+  return launch_prefill<64>(pc, layer, q, k, v, o, plan, workspace, st);
+}
+
+int aircache_prefill_attention(const aircache_desc *desc, const void *q, const void *k, const void *v, void *o,
+                               void *stream) {
+  PrefillCfg pc;
+  int rc;
+  if ((rc = make_prefill_config(desc, &pc))) return rc;
+  if ((rc = check_prefill_io(pc, q, k, v, o))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (pc.cfg.sh.D == 128) return launch_prefill<128>(pc, 0, q, k, v, o, nullptr, nullptr, st);
+  return launch_prefill<64>(pc, 0, q, k, v, o, nullptr, nullptr, st);
 }
 
 const char *aircache_strerror(int status) {

@@ -1,0 +1,558 @@
+// Causal prefill attention of one layer, with the AirCache scores of the text
+// rows taken from the same logits; included by aircache.hip inside namespace
+// aircache.
+//
+// Attention: the KV-cache primer page (devpress.csdn.net), section 2.1
+// "到底缓存什么？", the o_t equation at every position t of the regrouped
+// sequence (visual tokens first, then text): position t attends to the keys
+// 0..t, o_t = softmax(q_t K[0..t]^T / sqrt(D)) V[0..t], query head h on KV
+// head h / G.
+//
+// Scores: the AirCache paper-notes page, "Elite Observation Window" (the
+// A_vtk and I_v equations). An elite text row j normalises its logits over
+// the N_v visual keys plus the elite text keys, with no causal mask. Its
+// logits against the visual keys are the ones the prefill computes anyway
+// (every text row sees every visual key), so a text workgroup writes, for
+// each elite row and 64-key visual tile, exp2(s - m_t) of the tile's visual
+// keys with m_t the running maximum of the attention at that tile, and after
+// the last visual tile the row's normaliser (M, Z): the visual keys' running
+// sum merged with the elite text keys' pair from a short extra product before
+// the key loop. prefill_finalize_kernel weights the exponentials by
+// exp2(m_t - M) / Z and sums the visual columns into I_v: the visual keys are
+// read once, by the attention.
+//
+// Kernel shape (gfx950): a workgroup of 4 waves takes 128 query rows of one
+// (sample, query head), 32 per wave as two 16-row MFMA blocks, and walks the
+// key tiles of 64 keys up to its last row. S^T = K Q^T by
+// v_mfma_f32_16x16x32_bf16 (keys as the A operand from an LDS tile staged by
+// LDS-DMA, the wave's queries as the B operand in registers), so the result
+// holds one query per lane column and the online softmax needs only a
+// reduction over the four 16-lane rows. The key order inside a tile is
+// permuted so that the probabilities of the lane's keys form, as they are,
+// the B operand of O^T = V^T P^T; V is transposed on its way into LDS. Two
+// buffers per operand: the next tile's loads are in flight during the
+// current tile's products.
+#pragma once
+
+constexpr int kPfThreads = 256;
+constexpr int kPfWaves = kPfThreads / 64;
+constexpr int kPfRows = 32 * kPfWaves;  // query rows per workgroup
+constexpr int kPfKeys = 64;             // keys per tile
+constexpr int kPfVtPad = 8;             // bf16 of padding per transposed V row (bank spread)
+
+template <int D> struct PfLayout {
+  static constexpr int kBlock = 16 * D * 2;                 // one 16-key block in fragment order
+  static constexpr int kKTile = 4 * kBlock;                 // a 64-key K tile
+  static constexpr int kVtRow = (kPfKeys + kPfVtPad) * 2;   // bytes of one transposed V row
+  static constexpr int kVTile = D * kVtRow;                 // the 64-key V tile, transposed
+  static constexpr int kBuf = kKTile + kVTile;
+  static constexpr int kBytes = 2 * kBuf;                   // two buffers
+};
+
+struct PrefillArgs {
+  const uint16_t *q;  // [B][Hq][S][D]
+  const uint16_t *k;  // [B][Hkv][S][D]
+  const uint16_t *v;
+  uint16_t *o;        // [B][Hq][S][D]
+  int nqt_vis, nqt_txt;  // query tiles per (sample, head) over the visual rows, the text rows
+  int score;             // write the text rows' scoring terms
+  int layer;
+  const int32_t *elite, *n_elite;  // the layer's rows of the plan
+  float *e;                        // [B][Hkv][rcap16][evs] exp2(s - m) of the elite rows (this layer)
+  float2 *stats;                   // [B][Hkv][rcap16][nstat] (m, sum) per elite row and tile
+  int evs;                         // row stride of e: N_v rounded up to the key tile
+};
+
+// Position of key row m (0..15) of block kb (0..3) inside a 64-key tile: the
+// lane of column n and row group grp then holds, in blocks 2s and 2s + 1, the
+// logits of keys 32 s + 8 grp + 0..7, which is the B-operand fragment of slice s.
+__device__ __forceinline__ int pf_key(int kb, int m) { return 32 * (kb >> 1) + 8 * (m >> 2) + 4 * (kb & 1) + (m & 3); }
+
+__device__ __forceinline__ float max_across_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// Two floats to two bf16 (round to nearest even), packed low first.
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+template <int D, bool SCORE>
+__global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, PrefillArgs a) {
+  using Lay = PfLayout<D>;
+  constexpr int NC = D / 32;  // 32-wide slices of the head dimension
+  constexpr int ND = D / 16;  // 16-row blocks of O^T
+  extern __shared__ __align__(16) unsigned char pf_lds[];
+  __shared__ int emap[kPfRows];  // elite index of each text row of the tile, or -1
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, grp = lane >> 4;
+  const int S = sh.S, Nv = sh.Nv;
+
+  // Longest workgroups first: text tiles from the last, then visual tiles.
+  const int bh = blockIdx.x % (sh.B * sh.Hq), rank = blockIdx.x / (sh.B * sh.Hq);
+  const int b = bh / sh.Hq, h = bh - b * sh.Hq, g = h / sh.G, hl = h - g * sh.G;
+  const bool text = rank < a.nqt_txt;
+  const int qt = text ? a.nqt_txt - 1 - rank : a.nqt_vis - 1 - (rank - a.nqt_txt);
+  const int row0 = text ? Nv + qt * kPfRows : qt * kPfRows;
+  const int row1 = text ? min(S, row0 + kPfRows) : min(Nv, row0 + kPfRows);
+  const int nkt = (row1 + kPfKeys - 1) / kPfKeys;
+
+  const uint16_t *qh = a.q + (size_t)(b * sh.Hq + h) * S * D;
+  const uint16_t *kh = a.k + (size_t)(b * sh.Hkv + g) * S * D;
+  const uint16_t *vh = a.v + (size_t)(b * sh.Hkv + g) * S * D;
+
+  // The wave's query fragments (rows beyond the tile are zero).
+  Frag<Bf16Tag> qf[2][NC];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = row0 + 32 * wave + 16 * qb + n;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (row < row1) qf[qb][c].load(qh + (size_t)row * D + 32 * c + 8 * grp);
+      else qf[qb][c].zero();
+    }
+  }
+
+  // Scoring set-up: the elite index of each of the tile's text rows.
+  const bool score = SCORE && text;
+  const int lbl = b;  // (layer, sample) index inside this layer's workspace
+  int ntk = 0;
+  if (score) {
+    ntk = a.n_elite[b];
+    ntk = ntk < 0 ? 0 : (ntk > sh.cap ? sh.cap : ntk);
+    for (int i = tid; i < kPfRows; i += kPfThreads) emap[i] = -1;
+    __syncthreads();
+    const int jt0 = row0 - Nv;
+    for (int e = tid; e < ntk; e += kPfThreads) {
+      const int jt = a.elite[(size_t)b * sh.Nt + e] - jt0;
+      if (jt >= 0 && jt < kPfRows) emap[jt] = e;
+    }
+    __syncthreads();
+  }
+  int erow[2] = {-1, -1};  // elite row r = hl * ntk + eidx of the lane's queries, or -1
+  if (score) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int rr = 32 * wave + 16 * qb + n;
+      const int e = (row0 + rr < row1) ? emap[rr] : -1;
+      erow[qb] = e >= 0 ? hl * ntk + e : -1;
+    }
+  }
+  float2 *st_base = a.stats + (size_t)(lbl * sh.Hkv + g) * sh.rcap16 * sh.nstat;
+  float *e_row[2];  // the lane's elite rows of the exponentials
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+    e_row[qb] = a.e + ((size_t)(lbl * sh.Hkv + g) * sh.rcap16 + (erow[qb] >= 0 ? erow[qb] : 0)) * a.evs;
+
+  // The elite text keys' (max, sum) for the elite rows: the columns the
+  // scores add to the visual keys, with no causal mask. Merged with the
+  // visual keys' running pair after the last visual tile.
+  float xm[2] = {-INFINITY, -INFINITY}, xz[2] = {0.f, 0.f};
+  if (score) {
+    float mx[2] = {-INFINITY, -INFINITY}, zx[2] = {0.f, 0.f};
+    for (int x0 = 0; x0 < ntk; x0 += 16) {
+      const int x = x0 + n;
+      Frag<Bf16Tag> kx[NC];
+      const int jt = x < ntk ? a.elite[(size_t)b * sh.Nt + x] : 0;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kx[c].load(kh + (size_t)(Nv + jt) * D + 32 * c + 8 * grp);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) mfma_slice(acc, kx[c], qf[qb][c]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (x0 + 4 * grp + i < ntk) {
+            const float v = acc[i] * sh.scale2;
+            const float mn = fmaxf(mx[qb], v);
+            zx[qb] = zx[qb] * exp2f(mx[qb] - mn) + exp2f(v - mn);
+            mx[qb] = mn;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      xm[qb] = max_across_rows(mx[qb]);
+      xz[qb] = sum_across_rows(mx[qb] > -INFINITY ? zx[qb] * exp2f(mx[qb] - xm[qb]) : 0.f);
+    }
+  }
+
+  unsigned char *buf0 = pf_lds;
+  const int kq = tid & 15, dq = tid >> 4;  // V staging: keys 4 kq .. 4 kq + 3, elements 8 dq .. 8 dq + 7
+  const bool vstage = dq < D / 8;
+
+  auto issue_k = [&](int kt, unsigned char *kbuf) {
+    const int key = min(kt * kPfKeys + pf_key(wave, n), S - 1);
+    const unsigned char *src = reinterpret_cast<const unsigned char *>(kh + (size_t)key * D) + 16 * grp;
+    unsigned char *dst = kbuf + wave * Lay::kBlock;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) load_lds16(src + 64 * j, dst + 1024 * j);
+  };
+  u32x4_t vr[4];
+  auto load_v = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = min(kt * kPfKeys + 4 * kq + i, S - 1);
+      vr[i] = vstage ? *reinterpret_cast<const u32x4_t *>(vh + (size_t)key * D + 8 * dq) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_vt = [&](unsigned char *vt) {
+    if (!vstage) return;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sh16 = 16 * (j & 1);
+      const unsigned x0 = (vr[0][j >> 1] >> sh16) & 0xffffu, x1 = (vr[1][j >> 1] >> sh16) & 0xffffu;
+      const unsigned x2 = (vr[2][j >> 1] >> sh16) & 0xffffu, x3 = (vr[3][j >> 1] >> sh16) & 0xffffu;
+      uint2 w;
+      w.x = x0 | (x1 << 16);
+      w.y = x2 | (x3 << 16);
+      *reinterpret_cast<uint2 *>(vt + (size_t)(8 * dq + j) * Lay::kVtRow + 8 * kq) = w;
+    }
+  };
+
+  f32x4_t oacc[ND][2];
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) oacc[d][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+  float zrun[2] = {0.f, 0.f};  // the scores' running sum over visual keys (same reference as lrun)
+  int qrow[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) qrow[qb] = row0 + 32 * wave + 16 * qb + n;
+
+  // prologue: tile 0 into buffer 0
+  load_v(0);
+  issue_k(0, buf0);
+  wait_vmcnt<0>();
+  store_vt(buf0 + Lay::kKTile);
+  __syncthreads();
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    unsigned char *cur = buf0 + (kt & 1) * Lay::kBuf;
+    unsigned char *nxt = buf0 + ((kt + 1) & 1) * Lay::kBuf;
+    const bool more = kt + 1 < nkt;
+    if (more) {
+      load_v(kt + 1);
+      issue_k(kt + 1, nxt);
+    }
+    const int key0 = kt * kPfKeys;
+
+    // S^T = K Q^T: four key blocks, two query blocks
+    f32x4_t s[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      s[kb][1] = s[kb][0];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        Frag<Bf16Tag> kf;
+        LdsTile<Bf16Tag>::read(kf, cur + kb * Lay::kBlock, c, lane);
+        mfma_slice(s[kb][0], kf, qf[0][c]);
+        mfma_slice(s[kb][1], kf, qf[1][c]);
+      }
+    }
+
+    // causal mask (only tiles that reach past the wave's first row), online softmax
+    const bool diag = key0 + kPfKeys - 1 > row0 + 32 * wave;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = s[kb][qb][i] * sh.scale2;
+          if (diag && key0 + pf_key(kb, 4 * grp + i) > qrow[qb]) v = -INFINITY;
+          s[kb][qb][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = max_across_rows(mx);
+      const float mnew = fmaxf(mrun[qb], mx);
+      const float alpha = exp2f(mrun[qb] - mnew);
+      mrun[qb] = mnew;
+      float ls = 0.f, zv = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = s[kb][qb][i];
+          const float p = v == -INFINITY ? 0.f : exp2f(v - mnew);
+          s[kb][qb][i] = p;
+          ls += p;
+        }
+      lrun[qb] = lrun[qb] * alpha + ls;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) oacc[d][qb] *= alpha;
+      if (score && key0 < Nv) {
+        // the tile's visual keys for the elite rows: (m, sum), and the
+        // exponentials as two runs of 8 keys per lane (keys past N_v land in
+        // the row's padding and are never read)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (key0 + pf_key(kb, 4 * grp + i) < Nv) zv += s[kb][qb][i];
+        zv = sum_across_rows(zv);
+        zrun[qb] = zrun[qb] * alpha + zv;
+        if (erow[qb] >= 0) {
+#pragma unroll
+          for (int sl = 0; sl < 2; ++sl) {
+            f32x4_t *dst = reinterpret_cast<f32x4_t *>(e_row[qb] + key0 + 32 * sl + 8 * grp);
+            dst[0] = s[2 * sl][qb];
+            dst[1] = s[2 * sl + 1][qb];
+          }
+          if (grp == 0) {
+            st_base[(size_t)erow[qb] * sh.nstat + kt] = make_float2(mnew, zv);
+            if (kt == sh.ntiles - 1) {
+              // the row's normaliser: the visual keys' running pair and the elite text keys' pair
+              const float M = fmaxf(mnew, xm[qb]);
+              const float Z = zrun[qb] * exp2f(mnew - M) + (xm[qb] > -INFINITY ? xz[qb] * exp2f(xm[qb] - M) : 0.f);
+              st_base[(size_t)erow[qb] * sh.nstat + sh.ntiles] = make_float2(M, Z);
+            }
+          }
+        }
+      }
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      Frag<Bf16Tag> pf[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        u32x4_t w;
+        w[0] = pack_bf16(s[2 * sl][qb][0], s[2 * sl][qb][1]);
+        w[1] = pack_bf16(s[2 * sl][qb][2], s[2 * sl][qb][3]);
+        w[2] = pack_bf16(s[2 * sl + 1][qb][0], s[2 * sl + 1][qb][1]);
+        w[3] = pack_bf16(s[2 * sl + 1][qb][2], s[2 * sl + 1][qb][3]);
+        pf[qb].v = __builtin_bit_cast(u16x8_t, w);
+      }
+      const unsigned char *vt = cur + Lay::kKTile + 2 * (32 * sl + 8 * grp);
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        Frag<Bf16Tag> vf;
+        vf.v = *reinterpret_cast<const u16x8_t *>(vt + (size_t)(16 * d + n) * Lay::kVtRow);
+        mfma_slice(oacc[d][0], vf, pf[0]);
+        mfma_slice(oacc[d][1], vf, pf[1]);
+      }
+    }
+
+    if (more) {
+      wait_vmcnt<NC>();  // this wave's V loads (issued before its K tile DMAs)
+      store_vt(nxt + Lay::kKTile);
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+  }
+
+  // O = O^T / l, rounded to bf16: the lane writes 4 consecutive elements of
+  // its query row per 16-row block of O^T.
+  uint16_t *oh = a.o + (size_t)(b * sh.Hq + h) * S * D;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float inv = 1.f / sum_across_rows(lrun[qb]);
+    if (qrow[qb] < row1) {
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        uint2 w;
+        w.x = pack_bf16(oacc[d][qb][0] * inv, oacc[d][qb][1] * inv);
+        w.y = pack_bf16(oacc[d][qb][2] * inv, oacc[d][qb][3] * inv);
+        *reinterpret_cast<uint2 *>(oh + (size_t)qrow[qb] * D + 16 * d + 4 * grp) = w;
+      }
+    }
+  }
+}
+
+// I_v and the statistics of one layer from the prefill's scoring terms. One
+// workgroup per (sample, KV head, 64-key column tile): the weight of each
+// elite row r of the KV head for this tile is exp2(m_t - M) / Z, with m_t the
+// reference of the tile's exponentials and (M, Z) the row's normaliser that
+// the prefill wrote after its last visual tile; 4 x 64 threads sum the rows'
+// weighted exponentials of the tile's columns into the KV head's part of I_v.
+// The last workgroup of a (layer, sample) adds the parts in ascending KV-head
+// order, divides by H_q N_tk (the I_v equation) and runs the statistics and
+// budget finisher of the other paths.
+constexpr int kPfFinThreads = 256;
+
+__global__ __launch_bounds__(kPfFinThreads) void prefill_finalize_kernel(Shape sh, PlanPtrs plan, Ws ws,
+                                                                         const float *e, int evs) {
+  extern __shared__ float wts[];  // [G N_tk] row weights; the finisher's I_v [N_v]
+  __shared__ float red[4][64];
+  __shared__ int flag;
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x % sh.ntiles;
+  const int bg = blockIdx.x / sh.ntiles;  // b * H_kv + g
+  const int g = bg % sh.Hkv, b = bg / sh.Hkv;
+  const int lb = sh.lb0 + b;
+  const int Nv = sh.Nv;
+  int ntk = plan.n_elite[lb];
+  ntk = ntk < 0 ? 0 : (ntk > sh.cap ? sh.cap : ntk);
+  const int R = sh.G * ntk;
+  for (int r = tid; r < R; r += kPfFinThreads) {
+    const float2 *st = ws.stats + ((size_t)bg * sh.rcap16 + r) * sh.nstat;
+    const float2 mz = st[sh.ntiles];  // (M, Z) of the row
+    wts[r] = exp2f(st[t].x - mz.x) / mz.y;
+  }
+  __syncthreads();
+  const int cl = tid & 63, rg = tid >> 6;
+  const int c = t * kPfKeys + cl;
+  float acc = 0.f;
+  if (c < Nv) {
+    const float *eb = e + (size_t)bg * sh.rcap16 * evs + c;
+    for (int r = rg; r < R; r += 4) acc += eb[(size_t)r * evs] * wts[r];
+  }
+  red[rg][cl] = acc;
+  __syncthreads();
+  float *part = ws.part + (size_t)b * sh.Hkv * Nv;
+  if (tid < 64 && c < Nv) {
+    const float ag = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+    store_coherent(&part[(size_t)g * Nv + c], ag);
+    if (sh.per_head) {
+      const float inv_grp = (ntk > 0) ? 1.f / (float)(sh.G * ntk) : 0.f;
+      plan.iv_head[((size_t)lb * sh.Hkv + g) * Nv + c] = ag * inv_grp;
+    }
+  }
+  wait_all_memory();
+  __syncthreads();
+  if (tid == 0) flag = (counter_add(&ws.cnt_lb[lb], 1u) == (unsigned)(sh.Hkv * sh.ntiles) - 1u);
+  __syncthreads();
+  if (!flag) return;
+
+  // last workgroup of (layer, sample): I_v = the KV heads' parts in ascending order
+  const float inv_rows = (ntk > 0) ? 1.f / (float)(sh.Hq * ntk) : 0.f;
+  float *ivc = wts;
+  const auto rp = coherent_rsrc(part, (unsigned)((size_t)sh.Hkv * Nv * sizeof(float)));
+  for (int cc = tid; cc < Nv; cc += kPfFinThreads) {
+    float a = 0.f;
+    for (int gg = 0; gg < sh.Hkv; ++gg) a += load_sc1_f(rp, (unsigned)(((size_t)gg * Nv + cc) * sizeof(float)));
+    const float v = a * inv_rows;
+    ivc[cc] = v;
+    plan.iv[(size_t)lb * Nv + cc] = v;
+  }
+  __syncthreads();
+  finish_layer_sample<kPfFinThreads>(sh, plan, ws, lb, ivc);
+}
+
+// Elite observation window of one layer for the prefill calls ("Elite
+// Observation Window", the Att and k equations): one workgroup per sample
+// computes every query head's softmax row of the last text query over the
+// N_t text keys (MFMA logits into LDS, 16 text keys by up to 16 query heads
+// of one KV head per product, as elite_select_kernel), sums the rows per KV
+// head in ascending head order and the KV heads in ascending order (the same
+// sums as elite_select_kernel, so the same sets), and keeps
+// { j : pbar_j >= alpha max pbar } (or the last window text tokens) in
+// ascending order. One workgroup holds all heads, so no election is needed.
+// It also clears the counters the layer's finalize uses.
+constexpr int kPfEliteThreads = 512;
+constexpr int kPfEliteWaves = kPfEliteThreads / 64;
+
+__host__ __device__ constexpr size_t prefill_elite_lds(int Hq, int Nt) { return (size_t)(Hq + 1) * Nt * sizeof(float); }
+
+template <int D>
+__global__ __launch_bounds__(kPfEliteThreads) void prefill_elite_kernel(Shape sh, const uint16_t *q, const uint16_t *k,
+                                                                       PlanPtrs plan, Ws ws) {
+  constexpr int NC = D / 32;
+  extern __shared__ float zl[];  // [Hq][Nt] logits, then probabilities; pbar [Nt] after them
+  __shared__ float red[kPfEliteWaves];
+  __shared__ int wtot[kPfEliteWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, grp = lane >> 4;
+  const int b = blockIdx.x, lb = sh.lb0 + b, l = lb / sh.B;
+  const int Nt = sh.Nt, G = sh.G, S = sh.S;
+  if (tid == 0) {
+    ws.cnt_lb[lb] = 0;
+    if (l == 0) ws.cnt_b[b] = 0;
+    if (lb == 0) {
+      *ws.cnt_all = 0;
+      *plan.status = 0;
+    }
+  }
+  const int nkt = (Nt + 15) >> 4, nht = (G + 15) >> 4;
+  const int items = sh.Hkv * nht * nkt;
+  for (int it = wave; it < items; it += kPfEliteWaves) {
+    const int kt = it % nkt, rest = it / nkt, ht = rest % nht, g = rest / nht;
+    const int h0 = ht * 16, nh = min(16, G - h0);
+    const int key = kt * 16 + n;
+    Frag<Bf16Tag> qf[NC], kf[NC];
+    const uint16_t *qrow = q + ((size_t)(b * sh.Hq + g * G + h0 + min(n, nh - 1)) * S + (S - 1)) * D;
+    const uint16_t *krow = k + ((size_t)(b * sh.Hkv + g) * S + sh.Nv + min(key, Nt - 1)) * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      qf[c].load(qrow + c * 32 + grp * 8);
+      kf[c].load(krow + c * 32 + grp * 8);
+    }
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c) mfma_slice(acc, kf[c], qf[c]);
+    if (n < nh) {
+      float *zr = zl + (size_t)(g * G + h0 + n) * Nt;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kk = kt * 16 + grp * 4 + i;
+        if (kk < Nt) zr[kk] = acc[i] * sh.scale2;
+      }
+    }
+  }
+  __syncthreads();
+  for (int h = wave; h < sh.Hq; h += kPfEliteWaves) {
+    float *zr = zl + (size_t)h * Nt;
+    float m = -INFINITY;
+    for (int j = lane; j < Nt; j += 64) m = fmaxf(m, zr[j]);
+    m = wave_max(m);
+    float s = 0.f;
+    for (int j = lane; j < Nt; j += 64) {
+      const float ev = exp2f(zr[j] - m);
+      zr[j] = ev;
+      s += ev;
+    }
+    s = wave_sum(s);
+    const float inv = 1.f / s;
+    for (int j = lane; j < Nt; j += 64) zr[j] *= inv;
+  }
+  __syncthreads();
+  float *pbar = zl + (size_t)sh.Hq * Nt;
+  float m = -INFINITY;
+  for (int j = tid; j < Nt; j += kPfEliteThreads) {
+    float a = 0.f;
+    for (int g = 0; g < sh.Hkv; ++g) {
+      float ag = 0.f;
+      for (int h = 0; h < G; ++h) ag += zl[(size_t)(g * G + h) * Nt + j];
+      a += ag;
+    }
+    pbar[j] = a;
+    m = fmaxf(m, a);
+  }
+  m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = red[0];
+  for (int w = 1; w < kPfEliteWaves; ++w) m = fmaxf(m, red[w]);
+  const float thr = sh.alpha * m;
+  auto keep = [&](int j) { return sh.window > 0 ? j >= Nt - sh.window : pbar[j] >= thr; };
+  const int per = (Nt + kPfEliteThreads - 1) / kPfEliteThreads;
+  const int j0 = min(Nt, tid * per), j1 = min(Nt, j0 + per);
+  int cnt = 0;
+  for (int j = j0; j < j1; ++j) cnt += keep(j) ? 1 : 0;
+  const int incl = wave_incl_scan(cnt);
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+  for (int w = 0; w < kPfEliteWaves; ++w) {
+    if (w < wave) base += wtot[w];
+    total += wtot[w];
+  }
+  int pos = base + incl - cnt;
+  int32_t *el = plan.elite + (size_t)lb * Nt;
+  for (int j = j0; j < j1; ++j)
+    if (keep(j)) el[pos++] = j;
+  if (tid == 0) plan.n_elite[lb] = total;
+}

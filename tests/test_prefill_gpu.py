@@ -1,0 +1,192 @@
+"""Prefill attention with the pass's scores fused in (aircache_prefill_layer,
+aircache_prefill_attention) against the oracle.
+
+Attention output: every compared element of o meets
+    |gpu - ref| <= 2^-9 (max_i |v_id| + |ref_d|) + 1e-5 max_i |v_id|,
+derived from the kernel's arithmetic: logits and sums in float32, the
+probabilities p_i rounded to bfloat16 (relative error <= 2^-9 each) before
+the product with V, so the numerator is off by at most 2^-9 sum_i p_i |v_id|
+<= 2^-9 max_i |v_id| of the normalised row; the output rounded to bfloat16
+(<= 2^-9 |o_d|); float32 accumulation over at most a few thousand terms
+(1e-5 of the value scale). max_i runs over the KV head's rows.
+
+Plan outputs (elite sets, I_v, statistics, budgets, kept sets) and the
+compacted cache follow the rules of tests/parity.py, against the oracle's pass
+on the same text queries (the text rows of the prefill queries).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from parity import compare, make_aircache, reference, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _host(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _o_bound(w, vh, ref):
+    """Allowed |gpu - ref| per element of ref [Hq][rows][D]: see the module
+    docstring; vh [Hkv][S][D] as float64."""
+    G = w.Hq // w.Hkv
+    vmax = np.abs(vh).max(axis=1)  # [Hkv][D]
+    vm = np.repeat(vmax, G, axis=0)[:, None, :]
+    return 2.0 ** -9 * (vm + np.abs(ref)) + 1e-5 * vm
+
+
+def _check_o(w, inp, qa, o, l, rows_by_b):
+    """o of layer l against the oracle at the given rows of every query head."""
+    worst = 0.0
+    for b, rows in rows_by_b.items():
+        vh = wl.bf16_bits_to_f32(inp.v[l][b]).astype(np.float64)
+        for r0, n in rows:
+            ref = oracle.prefill_attention(w, qa, inp.k[l], inp.v[l], b, r0, n)
+            got = wl.bf16_bits_to_f32(o[b, :, r0:r0 + n, :]).astype(np.float64)
+            bound = _o_bound(w, vh, ref)
+            err = np.abs(got - ref)
+            bad = np.argwhere(err > bound)
+            assert bad.size == 0, (f"layer {l} sample {b} rows {r0}+{n}: {len(bad)} elements off, first "
+                                   f"{tuple(bad[0])} gpu {got[tuple(bad[0])]} ref {ref[tuple(bad[0])]}")
+            worst = max(worst, float((err / bound).max()))
+    return worst
+
+
+def _run_prefill(w, inp, ac, with_plan=True):
+    """Every layer through aircache_prefill_layer (or the plain attention),
+    then aircache_compress; returns (o per layer on the host, gpu dict)."""
+    L = w.L
+    qa = [wl.prefill_queries(inp, l) for l in range(L)]
+    _, k, v = to_torch(inp)
+    q = [_dev(a) for a in qa]
+    o = [torch.empty_like(t) for t in q]
+    out = {}
+    if with_plan:
+        plan = ac.alloc_plan()
+        for l in range(L):
+            ac.prefill_layer(l, q[l], k[l], v[l], o[l], plan)
+        ko, vo = ac.alloc_compacted()
+        ac.compress(plan, k, v, ko, vo)
+        torch.cuda.synchronize()
+        for f in ("elite_idx", "n_elite", "iv", "s_t", "s_k", "budget_x", "budget", "out_off", "kept_idx",
+                  "status"):
+            out[f] = getattr(plan, f).cpu().numpy()
+        if plan.iv_head is not None:
+            out["iv_head"] = plan.iv_head.cpu().numpy()
+        out["k_out"] = [_host(ko[l][:int(out["out_off"][l, w.B])]) for l in range(L)]
+        out["v_out"] = [_host(vo[l][:int(out["out_off"][l, w.B])]) for l in range(L)]
+    else:
+        for l in range(L):
+            ac.prefill_attention(q[l], k[l], v[l], o[l])
+        torch.cuda.synchronize()
+    return qa, [_host(t) for t in o], out
+
+
+SMALL = [
+    # (name, shape): ragged key and query tiles, several text tiles, GQA groups, head_dim 64
+    ("ragged_gqa", dict(L=2, B=2, Hq=4, Hkv=2, D=128, Nv=100, Nt=40)),
+    ("two_text_tiles_g7", dict(L=2, B=1, Hq=7, Hkv=1, D=128, Nv=200, Nt=150, alpha=0.5)),
+    ("aligned_mha", dict(L=3, B=1, Hq=4, Hkv=4, D=128, Nv=128, Nt=128)),
+    ("d64", dict(L=2, B=2, Hq=8, Hkv=2, D=64, Nv=333, Nt=77)),
+    ("short_text", dict(L=2, B=1, Hq=2, Hkv=1, D=128, Nv=70, Nt=1)),
+]
+
+
+@pytest.mark.parametrize("name,shape", SMALL, ids=[n for n, _ in SMALL])
+@pytest.mark.parametrize("seed", [1, 2])
+def test_prefill_small_shapes(name, shape, seed):
+    w = wl.custom(dtype="bf16", ratio=0.3, **shape)
+    inp = wl.make_inputs(w, seed)
+    ac = make_aircache(w)
+    qa, o, gpu = _run_prefill(w, inp, ac)
+    S = w.Nv + w.Nt
+    for l in range(w.L):
+        _check_o(w, inp, qa[l], o[l], l, {b: [(0, S)] for b in range(w.B)})
+    ref = reference(inp, gpu)
+    compare(inp, gpu, ref)
+
+
+@pytest.mark.parametrize("variant", [dict(obs_window=16), dict(select="per_kv_head"), dict(budget_mode=4),
+                                     dict(max_elite=8, alpha=0.0)])
+def test_prefill_variants(variant):
+    """The window ablation, one selection per KV head, the pyramid budget and
+    an elite cap (alpha 0 makes every text token elite: the cap is exceeded
+    and flagged, as on the other paths)."""
+    w = wl.custom(L=3, B=2, Hq=6, Hkv=2, D=128, Nv=190, Nt=48, dtype="bf16", ratio=0.25)
+    inp = wl.make_inputs(w, 5)
+    alpha = variant.get("alpha")
+    ac = make_aircache(w, alpha=alpha, max_elite=variant.get("max_elite", 0),
+                       budget_mode=variant.get("budget_mode", 0), obs_window=variant.get("obs_window", 0),
+                       select=variant.get("select", "shared"))
+    qa, o, gpu = _run_prefill(w, inp, ac)
+    if "max_elite" in variant:
+        assert np.all(gpu["status"] & 1), "elite overflow not flagged"
+        return
+    assert np.all(gpu["status"] == 0)
+    ref = reference(inp, gpu, alpha=alpha, budget_mode=variant.get("budget_mode", 0),
+                    obs_window=variant.get("obs_window", 0), per_head="select" in variant)
+    compare(inp, gpu, ref)
+
+
+def test_prefill_plain_attention_matches_the_scored_call():
+    """aircache_prefill_attention writes the same o, bit for bit, as the
+    scoring call (the same attention arithmetic)."""
+    w = wl.custom(L=2, B=2, Hq=4, Hkv=2, D=128, Nv=150, Nt=60, dtype="bf16")
+    inp = wl.make_inputs(w, 3)
+    ac = make_aircache(w)
+    _, o1, _ = _run_prefill(w, inp, ac)
+    _, o2, _ = _run_prefill(w, inp, ac, with_plan=False)
+    for l in range(w.L):
+        assert np.array_equal(o1[l], o2[l])
+
+
+def test_prefill_rerun_is_bit_identical():
+    w = wl.custom(L=2, B=1, Hq=7, Hkv=1, D=128, Nv=260, Nt=90, dtype="bf16", ratio=0.2)
+    inp = wl.make_inputs(w, 4)
+    ac = make_aircache(w)
+    _, o1, g1 = _run_prefill(w, inp, ac)
+    _, o2, g2 = _run_prefill(w, inp, ac)
+    for l in range(w.L):
+        assert np.array_equal(o1[l], o2[l])
+    for f in ("iv", "s_t", "s_k", "budget", "out_off"):
+        assert np.array_equal(g1[f], g2[f]), f
+    for l in range(w.L):
+        for b in range(w.B):
+            n = int(g1["budget"][l, b])  # entries past the budget are not written
+            assert np.array_equal(g1["kept_idx"][l, b, :n], g2["kept_idx"][l, b, :n])
+    for l in range(w.L):
+        assert np.array_equal(g1["k_out"][l], g2["k_out"][l])
+
+
+def _rows_sample(w, rng):
+    """Rows of a full-size check: the first, the last visual, the first text
+    and the last position, plus a few random ones, in runs of 2."""
+    S = w.Nv + w.Nt
+    starts = {0, w.Nv - 2, w.Nv, S - 2} | set(int(x) for x in rng.integers(0, S - 2, size=4))
+    return [(s, 2) for s in sorted(starts)]
+
+
+@pytest.mark.parametrize("cid", [3, 2])
+def test_prefill_full_size(cid):
+    """Workloads 3 (gqa_tiled_image_2880) and 2 (mha7b_single_image) at full
+    size: every plan output and the compacted cache against the oracle, o on
+    sampled rows of every query head of three layers."""
+    w = wl.CONFIGS[cid]
+    inp = wl.make_inputs(w, cid)
+    ac = make_aircache(w, max_elite=64)
+    qa, o, gpu = _run_prefill(w, inp, ac)
+    assert np.all(gpu["status"] == 0)
+    rng = np.random.default_rng(cid)
+    for l in (0, w.L // 2, w.L - 1):
+        _check_o(w, inp, qa[l], o[l], l, {b: _rows_sample(w, rng) for b in range(w.B)})
+    ref = reference(inp, gpu)
+    compare(inp, gpu, ref)

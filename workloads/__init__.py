@@ -201,5 +201,24 @@ def make_inputs(w: Workload | int, seed: int, *, zero_q: bool = False) -> Inputs
     return Inputs(w=w, seed=seed, q=q, k=k, v=v, planted=planted)
 
 
+def visual_queries(w: Workload, seed: int, layer: int) -> np.ndarray:
+    """The queries of the visual positions of one layer, [B][Hq][Nv][D], for
+    the prefill attention (whose query rows are every position's): drawn like
+    the text queries (N(0, 1), times 1/sqrt(D) on the scaled base), from a
+    generator of their own keyed by (seed, layer), so that the text queries of
+    make_inputs are unchanged. Float32 or bfloat16 bits."""
+    rng = np.random.Generator(np.random.PCG64([seed, 7919, layer]))
+    x = rng.standard_normal((w.B, w.Hq, w.Nv, w.D), dtype=np.float32)
+    if w.base != "unit":
+        x *= 1.0 / math.sqrt(w.D)
+    return x if w.dtype == F32 else f32_to_bf16_bits(x)
+
+
+def prefill_queries(inp: Inputs, layer: int) -> np.ndarray:
+    """Every position's query of one layer, [B][Hq][Nv + Nt][D]: the visual
+    rows of visual_queries, then the text queries of make_inputs."""
+    return np.ascontiguousarray(np.concatenate([visual_queries(inp.w, inp.seed, layer), inp.q[layer]], axis=2))
+
+
 def parity_seeds(cid: int) -> list[int]:
     return [cid, 100 + cid, 200 + cid]
