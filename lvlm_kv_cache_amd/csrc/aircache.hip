@@ -2024,12 +2024,12 @@ int launch_decode(const Shape &s, const DecodeTables &tb, const aircache_plan_bu
 
 // ----------------------------------------------------------------------------
 // Prefill attention with the scores of the text rows (prefill.h). One call per
-// layer: prefill_elite_kernel (elite_select_kernel when a sample's text
-// logits do not fit one workgroup's LDS) -> prefill_kernel ->
-// prefill_finalize_kernel, and after the
-// last layer topk_select_kernel. The scoring workspace holds one layer; the
-// counters and the elite parts hold every layer (the last layer's finalize
-// computes the budgets of all layers, as on the tiled path).
+// layer: elite_select_kernel -> prefill_kernel, whose extra
+// workgroups finalize the previous layer (I_v, statistics); after the last
+// layer prefill_finalize_kernel for it and topk_select_kernel. The scoring
+// workspace holds two layers (by parity); the counters and the elite parts
+// hold every layer (the last layer's finalize computes the budgets of all
+// layers, as on the tiled path).
 // ----------------------------------------------------------------------------
 struct PrefillCfg {
   Config cfg;  // T = 64 (the attention's key tile), one more statistics pair per row
@@ -2038,7 +2038,7 @@ struct PrefillCfg {
   size_t lds;
   int evs;           // row stride of the exponentials: N_v rounded up to the key tile
   size_t fin_lds;    // prefill_finalize_kernel's row weights or I_v
-  bool one_wg_elite; // prefill_elite_kernel: every query head's text logits of a sample fit one LDS
+  size_t stats_slot, e_slot;  // float2 / float elements of one workspace slot
 };
 
 int make_prefill_config(const aircache_desc *d, PrefillCfg *pc) {
@@ -2062,10 +2062,16 @@ int make_prefill_config(const aircache_desc *d, PrefillCfg *pc) {
   pc->lds = s.D == 128 ? (size_t)PfLayout<128>::kBytes : (size_t)PfLayout<64>::kBytes;
   const size_t units = (size_t)s.B * s.Hkv;  // one layer
   pc->evs = s.ntiles * kPfKeys;
-  pc->one_wg_elite = prefill_elite_lds(s.Hq, s.Nt) <= kMaxLds;
   pc->fin_lds = (size_t)(s.rcap16 > s.Nv ? s.rcap16 : s.Nv) * sizeof(float);
-  cfg.off_e = cfg.off_stats + align_up(units * s.rcap16 * (size_t)s.nstat * sizeof(float2));
-  cfg.off_part = cfg.off_e + align_up(units * s.rcap16 * (size_t)pc->evs * sizeof(float));
+  if (pc->fin_lds > pc->lds)
+    return fail(AIRCACHE_EINVAL, "the prefill finalize needs %zu bytes of LDS (n_vis or the elite rows per KV head "
+                "too large; lower max_elite)", pc->fin_lds);
+  // two slots of scoring terms (layer parity): a layer's finalize runs in the
+  // next layer's launch while that layer writes the other slot
+  pc->stats_slot = units * s.rcap16 * (size_t)s.nstat;
+  pc->e_slot = units * s.rcap16 * (size_t)pc->evs;
+  cfg.off_e = cfg.off_stats + align_up(2 * pc->stats_slot * sizeof(float2));
+  cfg.off_part = cfg.off_e + align_up(2 * pc->e_slot * sizeof(float));
   cfg.ws_bytes = cfg.off_part + align_up(units * (size_t)s.Nv * sizeof(float));
   return AIRCACHE_OK;
 }
@@ -2105,6 +2111,11 @@ int launch_prefill(const PrefillCfg &pc, int layer, const void *q, const void *k
     a.e = nullptr;
     a.stats = nullptr;
     a.evs = 0;
+    a.nattn = (int)pc.grid;
+    a.fin_e = nullptr;
+    a.fin_stats = nullptr;
+    a.plan = PlanPtrs{};
+    a.ws = Ws{};
     if ((rc = allow_lds(prefill_kernel<D, false>, pc.lds))) return rc;
     hipLaunchKernelGGL((prefill_kernel<D, false>), dim3((unsigned)pc.grid), dim3(kPfThreads), pc.lds, st, s, a);
     return check_hip(hipGetLastError(), "prefill_kernel launch");
@@ -2119,30 +2130,31 @@ int launch_prefill(const PrefillCfg &pc, int layer, const void *q, const void *k
   a.score = 1;
   a.elite = plan->elite_idx + (size_t)s.lb0 * s.Nt;
   a.n_elite = plan->n_elite + s.lb0;
-  a.e = ws.e;
-  a.stats = ws.stats;
+  const int slot = layer & 1;
+  a.e = ws.e + slot * pc.e_slot;
+  a.stats = ws.stats + slot * pc.stats_slot;
   a.evs = pc.evs;
+  a.nattn = (int)pc.grid;
+  a.fin_e = ws.e + (slot ^ 1) * pc.e_slot;
+  a.fin_stats = ws.stats + (slot ^ 1) * pc.stats_slot;
+  a.plan = pp;
+  a.ws = ws;
+  const long long nfin = (long long)s.B * s.Hkv * s.ntiles;  // finalize workgroups of one layer
+  const long long grid = pc.grid + (layer > 0 ? nfin : 0);
+  if (grid > INT32_MAX) return fail(AIRCACHE_EINVAL, "prefill grid of %lld workgroups too large", grid);
   if ((rc = allow_lds(prefill_kernel<D, true>, pc.lds))) return rc;
   if ((rc = allow_lds(prefill_finalize_kernel, pc.fin_lds))) return rc;
-  if (pc.one_wg_elite) {
-    // every query head of a sample in one workgroup
-    const size_t elds = prefill_elite_lds(s.Hq, s.Nt);
-    if ((rc = allow_lds(prefill_elite_kernel<D>, elds))) return rc;
-    hipLaunchKernelGGL((prefill_elite_kernel<D>), dim3((unsigned)s.B), dim3(kPfEliteThreads), elds, st, s, a.q, a.k,
-                       pp, ws);
-    if ((rc = check_hip(hipGetLastError(), "prefill_elite_kernel launch"))) return rc;
-  } else {
-    if ((rc = allow_lds(elite_select_kernel<Bf16Tag, D>, cfg.elite_lds))) return rc;
-    hipLaunchKernelGGL((elite_select_kernel<Bf16Tag, D>), dim3((unsigned)(s.B * s.Hkv)), dim3(kEliteThreads),
-                       cfg.elite_lds, st, s, qt, kt, pp, ws);
-    if ((rc = check_hip(hipGetLastError(), "elite_select_kernel launch"))) return rc;
-  }
-  hipLaunchKernelGGL((prefill_kernel<D, true>), dim3((unsigned)pc.grid), dim3(kPfThreads), pc.lds, st, s, a);
+  if ((rc = allow_lds(elite_select_kernel<Bf16Tag, D>, cfg.elite_lds))) return rc;
+  hipLaunchKernelGGL((elite_select_kernel<Bf16Tag, D>), dim3((unsigned)(s.B * s.Hkv)), dim3(kEliteThreads),
+                     cfg.elite_lds, st, s, qt, kt, pp, ws);
+  if ((rc = check_hip(hipGetLastError(), "elite_select_kernel launch"))) return rc;
+  hipLaunchKernelGGL((prefill_kernel<D, true>), dim3((unsigned)grid), dim3(kPfThreads), pc.lds, st, s, a);
   if ((rc = check_hip(hipGetLastError(), "prefill_kernel launch"))) return rc;
-  hipLaunchKernelGGL(prefill_finalize_kernel, dim3((unsigned)(s.B * s.Hkv * s.ntiles)), dim3(kPfFinThreads),
-                     pc.fin_lds, st, s, pp, ws, static_cast<const float *>(ws.e), pc.evs);
-  if ((rc = check_hip(hipGetLastError(), "prefill_finalize_kernel launch"))) return rc;
   if (layer == s.L - 1) {
+    // the last layer's finalize, then the selection of every layer
+    hipLaunchKernelGGL(prefill_finalize_kernel, dim3((unsigned)nfin), dim3(kPfFinThreads), pc.fin_lds, st, s, pp, ws,
+                       static_cast<const float *>(a.e), static_cast<const float2 *>(a.stats), pc.evs);
+    if ((rc = check_hip(hipGetLastError(), "prefill_finalize_kernel launch"))) return rc;
     hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)(s.L * s.B * s.nsel)), dim3(kTopkThreads), 0, st, s, pp);
     if ((rc = check_hip(hipGetLastError(), "topk_select_kernel launch"))) return rc;
   }

@@ -61,6 +61,11 @@ struct PrefillArgs {
   float *e;                        // [B][Hkv][rcap16][evs] exp2(s - m) of the elite rows (this layer)
   float2 *stats;                   // [B][Hkv][rcap16][nstat] (m, sum) per elite row and tile
   int evs;                         // row stride of e: N_v rounded up to the key tile
+  int nattn;                       // attention workgroups; the blocks after them finalize the previous layer
+  const float *fin_e;              // the previous layer's scoring terms (the other workspace slot)
+  const float2 *fin_stats;
+  PlanPtrs plan;
+  Ws ws;
 };
 
 // Position of key row m (0..15) of block kb (0..3) inside a 64-key tile: the
@@ -83,6 +88,87 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+// I_v and the statistics of one layer from the prefill's scoring terms (run
+// by extra workgroups of the next layer's prefill_kernel, and for the last
+// layer by prefill_finalize_kernel). One
+// workgroup per (sample, KV head, 64-key column tile): the weight of each
+// elite row r of the KV head for this tile is exp2(m_t - M) / Z, with m_t the
+// reference of the tile's exponentials and (M, Z) the row's normaliser that
+// the prefill wrote after its last visual tile; 4 x 64 threads sum the rows'
+// weighted exponentials of the tile's columns into the KV head's part of I_v.
+// The last workgroup of a (layer, sample) adds the parts in ascending KV-head
+// order, divides by H_q N_tk (the I_v equation) and runs the statistics and
+// budget finisher of the other paths.
+constexpr int kPfFinThreads = 256;
+
+// One finalize workgroup wg (0 .. B H_kv ntiles - 1) of the layer whose first
+// (layer, sample) index is sh.lb0; wts: LDS of max(rcap16, N_v) floats.
+__device__ void prefill_finalize_wg(const Shape &sh, const PlanPtrs &plan, const Ws &ws, const float *e,
+                                    const float2 *stats, int evs, int wg, float *wts) {
+  __shared__ float red[4][64];
+  __shared__ int flag;
+  const int tid = threadIdx.x;
+  const int t = wg % sh.ntiles;
+  const int bg = wg / sh.ntiles;  // b * H_kv + g
+  const int g = bg % sh.Hkv, b = bg / sh.Hkv;
+  const int lb = sh.lb0 + b;
+  const int Nv = sh.Nv;
+  int ntk = plan.n_elite[lb];
+  ntk = ntk < 0 ? 0 : (ntk > sh.cap ? sh.cap : ntk);
+  const int R = sh.G * ntk;
+  for (int r = tid; r < R; r += kPfFinThreads) {
+    const float2 *st = stats + ((size_t)bg * sh.rcap16 + r) * sh.nstat;
+    const float2 mz = st[sh.ntiles];  // (M, Z) of the row
+    wts[r] = exp2f(st[t].x - mz.x) / mz.y;
+  }
+  __syncthreads();
+  const int cl = tid & 63, rg = tid >> 6;
+  const int c = t * kPfKeys + cl;
+  float acc = 0.f;
+  if (c < Nv) {
+    const float *eb = e + (size_t)bg * sh.rcap16 * evs + c;
+    for (int r = rg; r < R; r += 4) acc += eb[(size_t)r * evs] * wts[r];
+  }
+  red[rg][cl] = acc;
+  __syncthreads();
+  float *part = ws.part + (size_t)b * sh.Hkv * Nv;
+  if (tid < 64 && c < Nv) {
+    const float ag = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+    store_coherent(&part[(size_t)g * Nv + c], ag);
+    if (sh.per_head) {
+      const float inv_grp = (ntk > 0) ? 1.f / (float)(sh.G * ntk) : 0.f;
+      plan.iv_head[((size_t)lb * sh.Hkv + g) * Nv + c] = ag * inv_grp;
+    }
+  }
+  wait_all_memory();
+  __syncthreads();
+  if (tid == 0) flag = (counter_add(&ws.cnt_lb[lb], 1u) == (unsigned)(sh.Hkv * sh.ntiles) - 1u);
+  __syncthreads();
+  if (!flag) return;
+
+  // last workgroup of (layer, sample): I_v = the KV heads' parts in ascending order
+  const float inv_rows = (ntk > 0) ? 1.f / (float)(sh.Hq * ntk) : 0.f;
+  float *ivc = wts;
+  const auto rp = coherent_rsrc(part, (unsigned)((size_t)sh.Hkv * Nv * sizeof(float)));
+  for (int cc = tid; cc < Nv; cc += kPfFinThreads) {
+    float a = 0.f;
+    for (int gg = 0; gg < sh.Hkv; ++gg) a += load_sc1_f(rp, (unsigned)(((size_t)gg * Nv + cc) * sizeof(float)));
+    const float v = a * inv_rows;
+    ivc[cc] = v;
+    plan.iv[(size_t)lb * Nv + cc] = v;
+  }
+  __syncthreads();
+  finish_layer_sample<kPfFinThreads>(sh, plan, ws, lb, ivc);
+}
+
+// The last layer's finalize (the others run inside the next layer's prefill_kernel).
+__global__ __launch_bounds__(kPfFinThreads) void prefill_finalize_kernel(Shape sh, PlanPtrs plan, Ws ws,
+                                                                         const float *e, const float2 *stats,
+                                                                         int evs) {
+  extern __shared__ float fin_wts[];
+  prefill_finalize_wg(sh, plan, ws, e, stats, evs, blockIdx.x, fin_wts);
+}
+
 template <int D, bool SCORE>
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, PrefillArgs a) {
   using Lay = PfLayout<D>;
@@ -90,12 +176,29 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
   constexpr int ND = D / 16;  // 16-row blocks of O^T
   extern __shared__ __align__(16) unsigned char pf_lds[];
   __shared__ int emap[kPfRows];  // elite index of each text row of the tile, or -1
+  // Block order: the text tiles (the longest workgroups), then the previous
+  // layer's finalize workgroups (they run beside the text tiles), then the
+  // visual tiles from the longest.
+  const int ntxt = sh.B * sh.Hq * a.nqt_txt;
+  int blk = (int)blockIdx.x;
+  if (SCORE && blk >= ntxt) {
+    const int nfin = (int)gridDim.x - a.nattn;
+    if (blk < ntxt + nfin) {
+      // the previous layer's I_v and statistics, from the other workspace slot
+      Shape fs = sh;
+      fs.lb0 = sh.lb0 - sh.B;
+      prefill_finalize_wg(fs, a.plan, a.ws, a.fin_e, a.fin_stats, a.evs, blk - ntxt,
+                          reinterpret_cast<float *>(pf_lds));
+      return;
+    }
+    blk -= nfin;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, grp = lane >> 4;
   const int S = sh.S, Nv = sh.Nv;
 
   // Longest workgroups first: text tiles from the last, then visual tiles.
-  const int bh = blockIdx.x % (sh.B * sh.Hq), rank = blockIdx.x / (sh.B * sh.Hq);
+  const int bh = blk % (sh.B * sh.Hq), rank = blk / (sh.B * sh.Hq);
   const int b = bh / sh.Hq, h = bh - b * sh.Hq, g = h / sh.G, hl = h - g * sh.G;
   const bool text = rank < a.nqt_txt;
   const int qt = text ? a.nqt_txt - 1 - rank : a.nqt_vis - 1 - (rank - a.nqt_txt);
@@ -187,7 +290,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
 
   unsigned char *buf0 = pf_lds;
   const int kq = tid & 15, dq = tid >> 4;  // V staging: keys 4 kq .. 4 kq + 3, elements 8 dq .. 8 dq + 7
-  const bool vstage = dq < D / 8;
+  constexpr bool kAllStage = 16 * (D / 8) >= kPfThreads;  // every thread stages (head_dim 128)
+  const bool vstage = kAllStage || dq < D / 8;
 
   auto issue_k = [&](int kt, unsigned char *kbuf) {
     const int key = min(kt * kPfKeys + pf_key(wave, n), S - 1);
@@ -263,35 +367,42 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
 
     // causal mask (only tiles that reach past the wave's first row), online softmax
     const bool diag = key0 + kPfKeys - 1 > row0 + 32 * wave;
+    if (diag) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (key0 + pf_key(kb, 4 * grp + i) > qrow[qb]) s[kb][qb][i] = -INFINITY;
+    }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
+      // the scale 1/sqrt(D) (base 2) is applied after the maximum and inside
+      // the exponent; exp2 of -inf (masked keys) is 0
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = s[kb][qb][i] * sh.scale2;
-          if (diag && key0 + pf_key(kb, 4 * grp + i) > qrow[qb]) v = -INFINITY;
-          s[kb][qb][i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = max_across_rows(mx);
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
+      mx = max_across_rows(mx) * sh.scale2;
       const float mnew = fmaxf(mrun[qb], mx);
-      const float alpha = exp2f(mrun[qb] - mnew);
+      const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - mnew);
       mrun[qb] = mnew;
       float ls = 0.f, zv = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v = s[kb][qb][i];
-          const float p = v == -INFINITY ? 0.f : exp2f(v - mnew);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][i], sh.scale2, -mnew));
           s[kb][qb][i] = p;
           ls += p;
         }
       lrun[qb] = lrun[qb] * alpha + ls;
+      if (__ballot(alpha != 1.f)) {  // the maximum moved for some row of the wave
 #pragma unroll
-      for (int d = 0; d < ND; ++d) oacc[d][qb] *= alpha;
+        for (int d = 0; d < ND; ++d) oacc[d][qb] *= alpha;
+      }
       if (score && key0 < Nv) {
         // the tile's visual keys for the elite rows: (m, sum), and the
         // exponentials as two runs of 8 keys per lane (keys past N_v land in
@@ -370,189 +481,4 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
       }
     }
   }
-}
-
-// I_v and the statistics of one layer from the prefill's scoring terms. One
-// workgroup per (sample, KV head, 64-key column tile): the weight of each
-// elite row r of the KV head for this tile is exp2(m_t - M) / Z, with m_t the
-// reference of the tile's exponentials and (M, Z) the row's normaliser that
-// the prefill wrote after its last visual tile; 4 x 64 threads sum the rows'
-// weighted exponentials of the tile's columns into the KV head's part of I_v.
-// The last workgroup of a (layer, sample) adds the parts in ascending KV-head
-// order, divides by H_q N_tk (the I_v equation) and runs the statistics and
-// budget finisher of the other paths.
-constexpr int kPfFinThreads = 256;
-
-__global__ __launch_bounds__(kPfFinThreads) void prefill_finalize_kernel(Shape sh, PlanPtrs plan, Ws ws,
-                                                                         const float *e, int evs) {
-  extern __shared__ float wts[];  // [G N_tk] row weights; the finisher's I_v [N_v]
-  __shared__ float red[4][64];
-  __shared__ int flag;
-  const int tid = threadIdx.x;
-  const int t = blockIdx.x % sh.ntiles;
-  const int bg = blockIdx.x / sh.ntiles;  // b * H_kv + g
-  const int g = bg % sh.Hkv, b = bg / sh.Hkv;
-  const int lb = sh.lb0 + b;
-  const int Nv = sh.Nv;
-  int ntk = plan.n_elite[lb];
-  ntk = ntk < 0 ? 0 : (ntk > sh.cap ? sh.cap : ntk);
-  const int R = sh.G * ntk;
-  for (int r = tid; r < R; r += kPfFinThreads) {
-    const float2 *st = ws.stats + ((size_t)bg * sh.rcap16 + r) * sh.nstat;
-    const float2 mz = st[sh.ntiles];  // (M, Z) of the row
-    wts[r] = exp2f(st[t].x - mz.x) / mz.y;
-  }
-  __syncthreads();
-  const int cl = tid & 63, rg = tid >> 6;
-  const int c = t * kPfKeys + cl;
-  float acc = 0.f;
-  if (c < Nv) {
-    const float *eb = e + (size_t)bg * sh.rcap16 * evs + c;
-    for (int r = rg; r < R; r += 4) acc += eb[(size_t)r * evs] * wts[r];
-  }
-  red[rg][cl] = acc;
-  __syncthreads();
-  float *part = ws.part + (size_t)b * sh.Hkv * Nv;
-  if (tid < 64 && c < Nv) {
-    const float ag = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
-    store_coherent(&part[(size_t)g * Nv + c], ag);
-    if (sh.per_head) {
-      const float inv_grp = (ntk > 0) ? 1.f / (float)(sh.G * ntk) : 0.f;
-      plan.iv_head[((size_t)lb * sh.Hkv + g) * Nv + c] = ag * inv_grp;
-    }
-  }
-  wait_all_memory();
-  __syncthreads();
-  if (tid == 0) flag = (counter_add(&ws.cnt_lb[lb], 1u) == (unsigned)(sh.Hkv * sh.ntiles) - 1u);
-  __syncthreads();
-  if (!flag) return;
-
-  // last workgroup of (layer, sample): I_v = the KV heads' parts in ascending order
-  const float inv_rows = (ntk > 0) ? 1.f / (float)(sh.Hq * ntk) : 0.f;
-  float *ivc = wts;
-  const auto rp = coherent_rsrc(part, (unsigned)((size_t)sh.Hkv * Nv * sizeof(float)));
-  for (int cc = tid; cc < Nv; cc += kPfFinThreads) {
-    float a = 0.f;
-    for (int gg = 0; gg < sh.Hkv; ++gg) a += load_sc1_f(rp, (unsigned)(((size_t)gg * Nv + cc) * sizeof(float)));
-    const float v = a * inv_rows;
-    ivc[cc] = v;
-    plan.iv[(size_t)lb * Nv + cc] = v;
-  }
-  __syncthreads();
-  finish_layer_sample<kPfFinThreads>(sh, plan, ws, lb, ivc);
-}
-
-// Elite observation window of one layer for the prefill calls ("Elite
-// Observation Window", the Att and k equations): one workgroup per sample
-// computes every query head's softmax row of the last text query over the
-// N_t text keys (MFMA logits into LDS, 16 text keys by up to 16 query heads
-// of one KV head per product, as elite_select_kernel), sums the rows per KV
-// head in ascending head order and the KV heads in ascending order (the same
-// sums as elite_select_kernel, so the same sets), and keeps
-// { j : pbar_j >= alpha max pbar } (or the last window text tokens) in
-// ascending order. One workgroup holds all heads, so no election is needed.
-// It also clears the counters the layer's finalize uses.
-constexpr int kPfEliteThreads = 512;
-constexpr int kPfEliteWaves = kPfEliteThreads / 64;
-
-__host__ __device__ constexpr size_t prefill_elite_lds(int Hq, int Nt) { return (size_t)(Hq + 1) * Nt * sizeof(float); }
-
-template <int D>
-__global__ __launch_bounds__(kPfEliteThreads) void prefill_elite_kernel(Shape sh, const uint16_t *q, const uint16_t *k,
-                                                                       PlanPtrs plan, Ws ws) {
-  constexpr int NC = D / 32;
-  extern __shared__ float zl[];  // [Hq][Nt] logits, then probabilities; pbar [Nt] after them
-  __shared__ float red[kPfEliteWaves];
-  __shared__ int wtot[kPfEliteWaves];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, grp = lane >> 4;
-  const int b = blockIdx.x, lb = sh.lb0 + b, l = lb / sh.B;
-  const int Nt = sh.Nt, G = sh.G, S = sh.S;
-  if (tid == 0) {
-    ws.cnt_lb[lb] = 0;
-    if (l == 0) ws.cnt_b[b] = 0;
-    if (lb == 0) {
-      *ws.cnt_all = 0;
-      *plan.status = 0;
-    }
-  }
-  const int nkt = (Nt + 15) >> 4, nht = (G + 15) >> 4;
-  const int items = sh.Hkv * nht * nkt;
-  for (int it = wave; it < items; it += kPfEliteWaves) {
-    const int kt = it % nkt, rest = it / nkt, ht = rest % nht, g = rest / nht;
-    const int h0 = ht * 16, nh = min(16, G - h0);
-    const int key = kt * 16 + n;
-    Frag<Bf16Tag> qf[NC], kf[NC];
-    const uint16_t *qrow = q + ((size_t)(b * sh.Hq + g * G + h0 + min(n, nh - 1)) * S + (S - 1)) * D;
-    const uint16_t *krow = k + ((size_t)(b * sh.Hkv + g) * S + sh.Nv + min(key, Nt - 1)) * D;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      qf[c].load(qrow + c * 32 + grp * 8);
-      kf[c].load(krow + c * 32 + grp * 8);
-    }
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NC; ++c) mfma_slice(acc, kf[c], qf[c]);
-    if (n < nh) {
-      float *zr = zl + (size_t)(g * G + h0 + n) * Nt;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = kt * 16 + grp * 4 + i;
-        if (kk < Nt) zr[kk] = acc[i] * sh.scale2;
-      }
-    }
-  }
-  __syncthreads();
-  for (int h = wave; h < sh.Hq; h += kPfEliteWaves) {
-    float *zr = zl + (size_t)h * Nt;
-    float m = -INFINITY;
-    for (int j = lane; j < Nt; j += 64) m = fmaxf(m, zr[j]);
-    m = wave_max(m);
-    float s = 0.f;
-    for (int j = lane; j < Nt; j += 64) {
-      const float ev = exp2f(zr[j] - m);
-      zr[j] = ev;
-      s += ev;
-    }
-    s = wave_sum(s);
-    const float inv = 1.f / s;
-    for (int j = lane; j < Nt; j += 64) zr[j] *= inv;
-  }
-  __syncthreads();
-  float *pbar = zl + (size_t)sh.Hq * Nt;
-  float m = -INFINITY;
-  for (int j = tid; j < Nt; j += kPfEliteThreads) {
-    float a = 0.f;
-    for (int g = 0; g < sh.Hkv; ++g) {
-      float ag = 0.f;
-      for (int h = 0; h < G; ++h) ag += zl[(size_t)(g * G + h) * Nt + j];
-      a += ag;
-    }
-    pbar[j] = a;
-    m = fmaxf(m, a);
-  }
-  m = wave_max(m);
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  m = red[0];
-  for (int w = 1; w < kPfEliteWaves; ++w) m = fmaxf(m, red[w]);
-  const float thr = sh.alpha * m;
-  auto keep = [&](int j) { return sh.window > 0 ? j >= Nt - sh.window : pbar[j] >= thr; };
-  const int per = (Nt + kPfEliteThreads - 1) / kPfEliteThreads;
-  const int j0 = min(Nt, tid * per), j1 = min(Nt, j0 + per);
-  int cnt = 0;
-  for (int j = j0; j < j1; ++j) cnt += keep(j) ? 1 : 0;
-  const int incl = wave_incl_scan(cnt);
-  if (lane == 63) wtot[wave] = incl;
-  __syncthreads();
-  int base = 0, total = 0;
-  for (int w = 0; w < kPfEliteWaves; ++w) {
-    if (w < wave) base += wtot[w];
-    total += wtot[w];
-  }
-  int pos = base + incl - cnt;
-  int32_t *el = plan.elite + (size_t)lb * Nt;
-  for (int j = j0; j < j1; ++j)
-    if (keep(j)) el[pos++] = j;
-  if (tid == 0) plan.n_elite[lb] = total;
 }
