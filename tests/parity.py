@@ -220,3 +220,76 @@ def compare(inp: wl.Inputs, gpu: dict, ref: dict, ratio=None, check_compacted=Tr
                 off += n
             assert gpu["out_off"][l, B] == off
     return rep
+
+
+# ---- prefill attention with the scores fused in ------------------------------
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _host(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _o_bound(w, vh, ref):
+    """Allowed |gpu - ref| per element of the prefill attention's output ref
+    [Hq][rows][D] (vh: the KV head's values [Hkv][S][D] as float64):
+        2^-8 (max_i |v_id| + |ref_d|) + 1e-5 max_i |v_id|.
+    Logits and sums are float32; the probabilities p_i are rounded to
+    bfloat16 (8-bit significand: relative error <= 2^-8 each) before the
+    product with V, so the numerator is off by at most 2^-8 sum_i p_i |v_id|
+    <= 2^-8 max_i |v_id| of the normalised row; the output is rounded to
+    bfloat16 (<= 2^-8 |o_d|); float32 accumulation over at most a few
+    thousand terms stays within 1e-5 of the value scale."""
+    G = w.Hq // w.Hkv
+    vmax = np.abs(vh).max(axis=1)  # [Hkv][D]
+    vm = np.repeat(vmax, G, axis=0)[:, None, :]
+    return 2.0 ** -8 * (vm + np.abs(ref)) + 1e-5 * vm
+
+
+def check_prefill_o(w, inp, qa, o, l, rows_by_b):
+    """o of layer l against the oracle at the given rows of every query head."""
+    worst = 0.0
+    for b, rows in rows_by_b.items():
+        vh = wl.bf16_bits_to_f32(inp.v[l][b]).astype(np.float64)
+        for r0, n in rows:
+            ref = oracle.prefill_attention(w, qa, inp.k[l], inp.v[l], b, r0, n)
+            got = wl.bf16_bits_to_f32(o[b, :, r0:r0 + n, :]).astype(np.float64)
+            bound = _o_bound(w, vh, ref)
+            err = np.abs(got - ref)
+            bad = np.argwhere(err > bound)
+            assert bad.size == 0, (f"layer {l} sample {b} rows {r0}+{n}: {len(bad)} elements off, first "
+                                   f"{tuple(bad[0])} gpu {got[tuple(bad[0])]} ref {ref[tuple(bad[0])]}")
+            worst = max(worst, float((err / bound).max()))
+    return worst
+
+
+def run_gpu_prefill(w, inp, ac, with_plan=True):
+    """Every layer through aircache_prefill_layer (or the plain attention),
+    then aircache_compress; returns (o per layer on the host, gpu dict)."""
+    L = w.L
+    qa = [wl.prefill_queries(inp, l) for l in range(L)]
+    _, k, v = to_torch(inp)
+    q = [_dev(a) for a in qa]
+    o = [torch.empty_like(t) for t in q]
+    out = {}
+    if with_plan:
+        plan = ac.alloc_plan()
+        for l in range(L):
+            ac.prefill_layer(l, q[l], k[l], v[l], o[l], plan)
+        ko, vo = ac.alloc_compacted()
+        ac.compress(plan, k, v, ko, vo)
+        torch.cuda.synchronize()
+        for f in ("elite_idx", "n_elite", "iv", "s_t", "s_k", "budget_x", "budget", "out_off", "kept_idx",
+                  "status"):
+            out[f] = getattr(plan, f).cpu().numpy()
+        if plan.iv_head is not None:
+            out["iv_head"] = plan.iv_head.cpu().numpy()
+        out["k_out"] = [_host(ko[l][:int(out["out_off"][l, w.B])]) for l in range(L)]
+        out["v_out"] = [_host(vo[l][:int(out["out_off"][l, w.B])]) for l in range(L)]
+    else:
+        for l in range(L):
+            ac.prefill_attention(q[l], k[l], v[l], o[l])
+        torch.cuda.synchronize()
+    return qa, [_host(t) for t in o], out

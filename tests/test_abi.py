@@ -241,3 +241,34 @@ def test_quantize_argument_errors(lib):
     assert _lib.quantize_i8(d, fake_buf(), p, [(2 << 20) + 8, 4096], p, p, 4096, 8192, 0) == _lib.AIRCACHE_EINVAL
     d.n_layers = 0
     assert _lib.quantize_i8(d, fake_buf(), p, p, p, p, 4096, 8192, 0) == _lib.AIRCACHE_EINVAL
+
+
+def test_prefill_workspace_size(lib):
+    """Two slots of one layer's scoring terms plus the pass's counters: grows
+    with the elite cap, independent of the layer count beyond the counters;
+    float32 descriptors have no prefill path (size 0)."""
+    small = _lib.prefill_workspace_size(desc(max_elite=16))
+    big = _lib.prefill_workspace_size(desc(max_elite=64))
+    assert 0 < small < big
+    assert _lib.prefill_workspace_size(desc(dtype="f32")) == 0
+    d1, d28 = _lib.prefill_workspace_size(desc(n_layers=1)), _lib.prefill_workspace_size(desc(n_layers=28))
+    assert d28 - d1 < 8 << 20  # counters and elite parts only
+
+
+def test_prefill_argument_errors(lib):
+    d = desc(n_layers=2, n_vis=300, n_txt=40)
+    ws_need = _lib.prefill_workspace_size(d)
+    q = k = v = 1 << 20
+    o = 1 << 40
+    buf = fake_buf()
+    assert _lib.prefill_layer(d, 2, q, k, v, o, buf, 4096, ws_need, 0) == _lib.AIRCACHE_EINVAL      # layer range
+    assert _lib.prefill_layer(d, -1, q, k, v, o, buf, 4096, ws_need, 0) == _lib.AIRCACHE_EINVAL
+    assert _lib.prefill_layer(d, 0, q, k, v, o, buf, 4096, ws_need - 1, 0) == _lib.AIRCACHE_EWORKSPACE
+    assert _lib.prefill_layer(d, 0, q, k, v, o, _lib.PlanBuf(), 4096, ws_need, 0) == _lib.AIRCACHE_EINVAL
+    assert _lib.prefill_layer(d, 0, 0, k, v, o, buf, 4096, ws_need, 0) == _lib.AIRCACHE_EINVAL       # NULL q
+    assert _lib.prefill_layer(d, 0, q + 8, k, v, o, buf, 4096, ws_need, 0) == _lib.AIRCACHE_EINVAL   # alignment
+    assert _lib.prefill_layer(d, 0, q, k, v, q, buf, 4096, ws_need, 0) == _lib.AIRCACHE_EINVAL       # o overlaps q
+    assert _lib.prefill_attention(d, q, k, v, q + 4096, 0) == _lib.AIRCACHE_EINVAL                   # overlap
+    f = desc(n_layers=2, dtype="f32")
+    assert _lib.prefill_attention(f, q, k, v, o, 0) == _lib.AIRCACHE_EINVAL                          # bf16 only
+    assert "bfloat16" in lib.aircache_last_error().decode()
