@@ -64,7 +64,7 @@ def parse():
                     help="do not time decode attention and int8 quantisation over the compacted cache")
     ap.add_argument("--skip-prefill", action="store_true",
                     help="skip the prefill attention timing (aircache_prefill_layer / _attention)")
-    ap.add_argument("--prefill-reps", type=int, default=5, help="timed repetitions of each prefill variant")
+    ap.add_argument("--prefill-reps", type=int, default=7, help="timed calls of each prefill variant (interleaved)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (the reference kernel that scales "
@@ -472,19 +472,20 @@ def main():
         bcomp = ac.bind(q0, k0, v0, pplan, k_out, v_out, stream=stream)
         bpass = bound[0].with_status(status_words[0].data_ptr())
 
-        def timed(fn):
+        variants = [bp_plain, lambda: (bp_fused(), bcomp.compress()), lambda: (bp_plain(), bpass.run())]
+        for fn in variants:  # untimed first calls
             fn()
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(a.prefill_reps):
+        torch.cuda.synchronize()
+        # the variants interleaved, each call between its own events; medians
+        evp = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(a.prefill_reps)] for _ in variants]
+        for r in range(a.prefill_reps):
+            for vi, fn in enumerate(variants):
+                evp[vi][r][0].record(stream)
                 fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return 1e3 * e0.elapsed_time(e1) / a.prefill_reps
-
-        us_plain = timed(bp_plain)
-        us_fused = timed(lambda: (bp_fused(), bcomp.compress()))
-        us_sep = timed(lambda: (bp_plain(), bpass.run()))
+                evp[vi][r][1].record(stream)
+        torch.cuda.synchronize()
+        us_plain, us_fused, us_sep = [1e3 * float(np.median([x.elapsed_time(y) for x, y in evs])) for evs in evp]
         if int(pplan.status.item()) != 0:
             raise RuntimeError(f"device status {int(pplan.status.item())} after the fused prefill")
         S = w.Nv + w.Nt
@@ -492,7 +493,7 @@ def main():
         tf = flops / (us_plain * 1e-6) / 1e12
         pf = {"kernels": ["prefill_kernel", "elite_select_kernel", "finalize_kernel", "topk_select_kernel",
                           "kv_gather_kernel"],
-              "layers": w.L, "reps": a.prefill_reps,
+              "layers": w.L, "reps": a.prefill_reps, "statistic": "median of interleaved calls",
               "us_attention_only": us_plain,
               "us_fused_scores_and_compaction": us_fused,
               "us_attention_then_separate_pass": us_sep,
