@@ -66,6 +66,8 @@ def lib():
         l.orc_decode_attention.restype = None
         l.orc_prefill_attention.argtypes = [C.POINTER(Desc), P, P, P, C.c_int, C.c_int, C.c_int, P]
         l.orc_prefill_attention.restype = None
+        l.orc_visual_window.argtypes = [C.POINTER(Desc), P, P, C.c_int, C.c_int, P, P]
+        l.orc_visual_window.restype = None
         l.orc_run.argtypes = [C.POINTER(Desc)] + [P] * 15
         l.orc_run.restype = C.c_int
         _lib = l
@@ -213,6 +215,22 @@ def decode_attention(w, k_out_l, v_out_l, out_off_l, budget_l, q_l) -> np.ndarra
         size = w.Hkv * n * w.D
         o[b] = decode_attention_segment(w, k_out_l[off:off + size], v_out_l[off:off + size], n, q_l[b])
     return o
+
+
+def visual_window(w, q_all_l, k_l, b: int, kwin: int, groups: bool = False):
+    """I_v of the window ablation's visual window (the last kwin visual
+    tokens as the observation rows, softmax over the N_v visual keys):
+    q_all_l [B][H_q][S][D] (every position's query), k_l [B][H_kv][S][D].
+    Returns iv [N_v], or (iv, iv per KV head [H_kv][N_v]) with groups."""
+    store = np.float32 if w.dtype == "f32" else np.uint16
+    q_all_l = np.ascontiguousarray(q_all_l, dtype=store)
+    k_l = np.ascontiguousarray(k_l, dtype=store)
+    assert q_all_l.shape[-3:] == (w.Hq, w.Nv + w.Nt, w.D) and 1 <= kwin <= w.Nv
+    iv = np.zeros(w.Nv, np.float64)
+    ivg = np.zeros((w.Hkv, w.Nv), np.float64) if groups else None
+    lib().orc_visual_window(C.byref(desc_of(w)), _ptr(q_all_l), _ptr(k_l), int(b), int(kwin), _ptr(iv),
+                            _ptr(ivg) if groups else None)
+    return (iv, ivg) if groups else iv
 
 
 def prefill_attention(w, q_all_l, k_l, v_l, b: int, row0: int = 0, nrows=None) -> np.ndarray:

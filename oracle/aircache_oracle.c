@@ -39,7 +39,9 @@
  *    set from the I_v over all query heads as in the shared selection;
  *  - int8 quantisation of the kept cache: symmetric range [-127, 127], one
  *    scale per (layer, sample, KV head) for K and one for V, codes rounded
- *    half to even in float32.
+ *    half to even in float32;
+ *  - the visual observation window: the last k visual tokens as the
+ *    observation rows, each normalised over the N_v visual keys.
  */
 #include <math.h>
 #include <stdint.h>
@@ -385,6 +387,48 @@ void orc_decode_attention(const orc_desc *w, const void *k_seg, const void *v_se
       o[(size_t)h * D + d] = acc;
     }
   }
+  free(z);
+}
+
+/*
+ * The window ablation's visual window (AirCache paper-notes page, "消融实验",
+ * the window table's visual-window row, read with "Elite Observation Window"):
+ * the observation rows are the last kwin visual tokens instead of the elite
+ * text tokens. Each such row's softmax runs over the N_v visual keys (the
+ * window's own keys are among them; no causal mask, as for the elite rows),
+ * and I_v[i] is the mean over every query head and window row of the
+ * probability at visual key i. With iv_groups non-NULL, also the mean over
+ * the query heads of each KV head only ([H_kv][N_v]).
+ * q_all: [B][H_q][N_v + N_t][D] (every position's query); k_l as elsewhere.
+ */
+void orc_visual_window(const orc_desc *w, const void *q_all, const void *k_l, int b, int kwin, double *iv,
+                       double *iv_groups) {
+  const int G = w->Hq / w->Hkv, D = w->D, S = w->Nv + w->Nt;
+  double *z = (double *)malloc(sizeof(double) * (size_t)w->Nv);
+  for (int i = 0; i < w->Nv; ++i) iv[i] = 0.0;
+  if (iv_groups)
+    for (int i = 0; i < w->Hkv * w->Nv; ++i) iv_groups[i] = 0.0;
+  for (int h = 0; h < w->Hq; ++h) {
+    const int g = h / G;
+    const size_t qh = ((size_t)b * w->Hq + h) * (size_t)S;
+    for (int r = 0; r < kwin; ++r) {
+      const int jq = w->Nv - kwin + r;
+      for (int c = 0; c < w->Nv; ++c) {
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d)
+          acc += elem(q_all, (qh + jq) * D + d, w->dtype) * elem(k_l, k_index(w, b, g, c) + d, w->dtype);
+        z[c] = acc / sqrt((double)D);
+      }
+      softmax(z, w->Nv);
+      for (int c = 0; c < w->Nv; ++c) {
+        iv[c] += z[c];
+        if (iv_groups) iv_groups[(size_t)g * w->Nv + c] += z[c];
+      }
+    }
+  }
+  for (int c = 0; c < w->Nv; ++c) iv[c] /= (double)w->Hq * (double)kwin;
+  if (iv_groups)
+    for (int i = 0; i < w->Hkv * w->Nv; ++i) iv_groups[i] /= (double)G * (double)kwin;
   free(z);
 }
 

@@ -729,3 +729,67 @@ def test_prefill_dominant_key_selects_its_value():
     k[0, 0, 2] = 40.0 * q[0, 0, t] / np.linalg.norm(q[0, 0, t])  # a key along head 0's query t
     o = oracle.prefill_attention(w, q, k, v, 0, t, 1)
     np.testing.assert_allclose(o[0, 0], v[0, 0, 2], atol=1e-6)
+
+
+# ------------------------------------------- visual observation window (f1) ----
+# The window ablation's visual window: the last k visual tokens as the
+# observation rows, each normalised over the N_v visual keys.
+
+def _vw_inputs(w, seed):
+    inp = wl.make_inputs(w, seed)
+    return inp, wl.prefill_queries(inp, 0)
+
+
+def test_visual_window_rows_sum_to_one_so_strength_is_one():
+    """Every row's probabilities over the visual keys sum to 1, so I_v sums to
+    1 whatever the inputs (s_t = 1 on every layer)."""
+    w = wl.custom(Nv=40, Nt=8, Hq=6, Hkv=2, D=16, B=2)
+    inp, qa = _vw_inputs(w, 1)
+    for b in range(w.B):
+        iv = oracle.visual_window(w, qa, inp.k[0], b, 5)
+        assert abs(iv.sum() - 1.0) < 1e-12
+        s_t, _ = oracle.layer_stats(iv)
+        assert abs(s_t - 1.0) < 1e-12
+
+
+def test_visual_window_zero_queries_uniform():
+    w = wl.custom(Nv=30, Nt=4, Hq=2, Hkv=1, D=8)
+    inp, qa = _vw_inputs(w, 2)
+    qa[:] = 0
+    iv = oracle.visual_window(w, qa, inp.k[0], 0, 7)
+    np.testing.assert_allclose(iv, np.full(w.Nv, 1.0 / w.Nv), rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("shape", [dict(Hq=1, Hkv=1), dict(Hq=6, Hkv=2), dict(Hq=4, Hkv=4, dtype="bf16")])
+def test_visual_window_matches_library_softmax(seed, shape):
+    """Brute force: scipy's softmax over the visual keys for the last k visual
+    queries, query head h on KV head h // G, no mask."""
+    w = wl.custom(Nv=23, Nt=5, D=16, B=2, **shape)
+    inp, qa = _vw_inputs(w, 30 + seed)
+    b, kwin = seed % 2, 4 + seed
+    iv, ivg = oracle.visual_window(w, qa, inp.k[0], b, kwin, groups=True)
+    Q = (qa if w.dtype == "f32" else wl.bf16_bits_to_f32(qa)).astype(np.float64)[b]
+    K = inp.as_f32("k").astype(np.float64)[0, b]
+    G = w.Hq // w.Hkv
+    ref = np.zeros(w.Nv)
+    refg = np.zeros((w.Hkv, w.Nv))
+    for h in range(w.Hq):
+        P = scipy.special.softmax(Q[h, w.Nv - kwin:w.Nv] @ K[h // G, :w.Nv].T / math.sqrt(w.D), axis=1)
+        ref += P.sum(0)
+        refg[h // G] += P.sum(0)
+    np.testing.assert_allclose(iv, ref / (w.Hq * kwin), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(ivg, refg / (G * kwin), rtol=1e-12, atol=1e-15)
+
+
+def test_visual_window_ignores_text_positions():
+    """Only visual queries and visual keys enter: text rows of q, and text keys,
+    may change freely."""
+    w = wl.custom(Nv=20, Nt=6, Hq=2, Hkv=1, D=8)
+    inp, qa = _vw_inputs(w, 4)
+    a = oracle.visual_window(w, qa, inp.k[0], 0, 3)
+    qa2, k2 = qa.copy(), inp.k[0].copy()
+    qa2[:, :, w.Nv:] *= 5.0
+    k2[:, :, w.Nv:] += 1.0
+    b = oracle.visual_window(w, qa2, k2, 0, 3)
+    np.testing.assert_array_equal(a, b)
