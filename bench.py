@@ -55,7 +55,8 @@ def parse():
     ap.add_argument("--budget-mode", default="aircache", choices=["aircache", "uniform", "strength", "skewness", "pyramid"],
                     help="layer budget rule: the method's (default) or one of its allocation ablation's variants")
     ap.add_argument("--obs-window", type=int, default=0,
-                    help="0: the elite observation window (default); k > 0: the last k text tokens instead")
+                    help="0: the elite observation window (default); k > 0: the last k text tokens instead; "
+                         "-k: the last k visual tokens (the queries of every position are then drawn)")
     ap.add_argument("--skip-hot", action="store_true",
                     help="leave out the cache-warm loop (one input copy every step), so that every launch of the "
                          "run reads rotated inputs (profiles of the headline conditions)")
@@ -277,12 +278,18 @@ def main():
     # input copies, each drawn from its own seed (seed, seed + 1, ...), so
     # consecutive steps see different elite sets, budgets and schedules
     inp = wl.make_inputs(w, seed)
-    copies = [(dev_layers(inp.q), dev_layers(inp.k), dev_layers(inp.v))]
+    def queries(ci):
+        # a visual observation window reads every position's queries
+        if a.obs_window < 0:
+            return dev_layers(np.stack([wl.prefill_queries(ci, l) for l in range(w.L)]))
+        return dev_layers(ci.q)
+
+    copies = [(queries(inp), dev_layers(inp.k), dev_layers(inp.v))]
     per_copy = sum(t.numel() * t.element_size() for ts in copies[0] for t in ts)
     ncopy = 1 if a.hot else max(1, math.ceil((1 << 30) / per_copy))
     for i in range(1, ncopy):
         ci = wl.make_inputs(w, seed + i)
-        copies.append((dev_layers(ci.q), dev_layers(ci.k), dev_layers(ci.v)))
+        copies.append((queries(ci), dev_layers(ci.k), dev_layers(ci.v)))
         del ci
 
     ac = AirCache(w.L, w.B, w.Hq, w.Hkv, w.D, w.Nv, w.Nt, dtype=tdtype, alpha=w.alpha, ratio=w.ratio,
@@ -460,7 +467,7 @@ def main():
     # separate pass (aircache_run); the first input copy, its visual queries
     # drawn by workloads.visual_queries.
     pf = None
-    if not a.skip_prefill and w.dtype == wl.BF16:
+    if not a.skip_prefill and w.dtype == wl.BF16 and a.obs_window >= 0:
         def dev_bits(arr):
             return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
         qa = [dev_bits(wl.prefill_queries(inp, l)) for l in range(w.L)]

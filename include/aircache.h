@@ -103,7 +103,13 @@ typedef struct {
   int32_t budget_mode; /* layer allocation rule, AIRCACHE_BUDGET_*; 0 is the method's */
   int32_t obs_window;  /* observation window: 0 the method's elite window; k > 0 the last
                           min(k, n_txt) text tokens instead (the window ablation of the
-                          "Elite Observation Window" section: 16, 32, or all text tokens) */
+                          "Elite Observation Window" section: 16, 32, or all text tokens);
+                          -k (1 <= k <= min(n_vis, n_txt)) the last k visual tokens (the
+                          ablation's visual window): their rows normalise over the n_vis
+                          visual keys only, the query tables then hold every position's
+                          query, [batch][n_q_heads][n_vis + n_txt][head_dim] per layer, the
+                          plan's elite_idx the window's positions n_vis - k .. n_vis - 1;
+                          served by the tiled path (AUTO resolves to it) */
   int32_t select_mode; /* AIRCACHE_SELECT_*: one selection per (layer, sample), the method's
                           (0), or one per KV head (1) */
 } aircache_desc;

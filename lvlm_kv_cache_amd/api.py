@@ -84,7 +84,9 @@ class AirCache:
     allocation ablation's variants, "uniform", "strength", "skewness",
     "pyramid";
     obs_window: 0 for the elite observation window, k > 0 for the last k
-    text tokens instead (the window ablation's contiguous windows);
+    text tokens instead (the window ablation's contiguous windows), -k for
+    the last k visual tokens (its visual window; q_txt then holds every
+    position's queries, [B][H_q][N_v + N_t][D] per layer);
     select: "shared" (one selection per layer and sample, the method's) or
     "per_kv_head" (each KV head its own top-r_hat, the group-wise top-K).
     """
@@ -107,6 +109,13 @@ class AirCache:
         self.ws_bytes = ws
         # zero-filled once; the library keeps it valid from call to call
         self.workspace = torch.zeros(ws, dtype=torch.uint8, device=self.device)
+
+    @property
+    def q_rows(self) -> int:
+        """Rows per query head of the query tables: N_t (text queries), or
+        N_v + N_t (every position's) with a visual observation window."""
+        s = self.shape
+        return s["Nv"] + s["Nt"] if self.desc.obs_window < 0 else s["Nt"]
 
     @property
     def scoring_path(self) -> str:
@@ -159,7 +168,7 @@ class AirCache:
         """events: optional list of 5 torch.cuda.Event (timing=True) recorded
         around the plan's 4 kernels."""
         s = self.shape
-        self._check_layers(q_txt, (s["B"], s["Hq"], s["Nt"], s["D"]), "q_txt")
+        self._check_layers(q_txt, (s["B"], s["Hq"], self.q_rows, s["D"]), "q_txt")
         self._check_layers(k, (s["B"], s["Hkv"], s["Nv"] + s["Nt"], s["D"]), "k")
         out = out or self.alloc_plan()
         _lib.check(_lib.plan(self.desc, [t.data_ptr() for t in q_txt], [t.data_ptr() for t in k],
@@ -172,7 +181,7 @@ class AirCache:
         serves the shape); events: optional list of 2 torch.cuda.Event
         recorded around the whole pass."""
         s = self.shape
-        self._check_layers(q_txt, (s["B"], s["Hq"], s["Nt"], s["D"]), "q_txt")
+        self._check_layers(q_txt, (s["B"], s["Hq"], self.q_rows, s["D"]), "q_txt")
         shp = (s["B"], s["Hkv"], s["Nv"] + s["Nt"], s["D"])
         self._check_layers(k, shp, "k")
         self._check_layers(v, shp, "v")
@@ -336,7 +345,7 @@ class BoundPass:
 
     def __init__(self, ac: "AirCache", q_txt, k, v, plan: PlanOutputs, k_out, v_out, stream=None):
         s = ac.shape
-        ac._check_layers(q_txt, (s["B"], s["Hq"], s["Nt"], s["D"]), "q_txt")
+        ac._check_layers(q_txt, (s["B"], s["Hq"], ac.q_rows, s["D"]), "q_txt")
         shp = (s["B"], s["Hkv"], s["Nv"] + s["Nt"], s["D"])
         ac._check_layers(k, shp, "k")
         ac._check_layers(v, shp, "v")

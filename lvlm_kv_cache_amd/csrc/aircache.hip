@@ -37,7 +37,7 @@ struct Shape {
   float scale2;  // log2(e) / sqrt(D): logits are kept in the base-2 domain
   double ratio;
   int budget_mode;  // AIRCACHE_BUDGET_*
-  int window;       // 0: the elite window; k > 0: the last k text tokens (k <= N_t)
+  int window;       // 0: the elite window; k > 0: the last k text tokens (k <= N_t); -k: the last k visual tokens
   int nsel;         // selections per (layer, sample): 1, or H_kv (one per KV head)
   int per_head;     // one selection per KV head (I_v^g written to plan.iv_head)
   int lb0;          // first (layer * B + sample) of a one-layer launch (prefill), else 0
@@ -111,7 +111,9 @@ __global__ __launch_bounds__(256) void cross_score_kernel(Shape sh, LayerTable q
   const E *kb = static_cast<const E *>(kt.p[l]) + (size_t)(b * sh.Hkv + g) * sh.S * D;
   const int c0 = t * sh.T;
   const int nvis = min(sh.T, sh.Nv - c0);
-  const int nx = (t < ntk) ? (ntk - t + sh.ntiles - 1) / sh.ntiles : 0;
+  // elite text columns of this tile (none for the visual window: its rows
+  // normalise over the visual keys only)
+  const int nx = (t < ntk && sh.window >= 0) ? (ntk - t + sh.ntiles - 1) / sh.ntiles : 0;
 
   // This wave's visual key fragments stay in registers for every row tile.
   Frag<Tag> kf[KTW][D / 32];
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(256) void cross_score_kernel(Shape sh, LayerTable q
     Frag<Tag> qf[D / 32];
     if (r < R) {
       const int hl = r / ntk, e = r - hl * ntk;
-      const E *qrow = q + ((size_t)(b * sh.Hq + g * sh.G + hl) * sh.Nt + el[e]) * D;
+      const E *qrow = q + ((size_t)(b * sh.Hq + g * sh.G + hl) * sh.qrows + (sh.window < 0 ? 0 : sh.qoff) + el[e]) * D;
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) qf[c].load(qrow + c * 32 + grp * 8);
     } else {
@@ -936,6 +938,13 @@ __global__ __launch_bounds__(kEliteThreads) void elite_select_kernel(Shape sh, L
   }
   int pos = base + incl - cnt;
   int32_t *el = plan.elite + (size_t)lb * Nt;
+  if (sh.window < 0) {
+    // the visual window: its rows are the last k visual positions
+    const int kw = -sh.window;
+    for (int e = tid; e < kw; e += kEliteThreads) el[e] = sh.Nv - kw + e;
+    if (tid == 0) plan.n_elite[lb] = kw;
+    return;
+  }
   for (int j = j0; j < j1; ++j)
     if (keep(j)) el[pos++] = j;
   if (tid == 0) plan.n_elite[lb] = total;
@@ -1321,7 +1330,12 @@ int make_config(const aircache_desc *d, Config *cfg) {
     return fail(AIRCACHE_EINVAL, "path=%d unknown", d->path);
   if (d->budget_mode < AIRCACHE_BUDGET_AIRCACHE || d->budget_mode > AIRCACHE_BUDGET_PYRAMID)
     return fail(AIRCACHE_EINVAL, "budget_mode=%d unknown", d->budget_mode);
-  if (d->obs_window < 0) return fail(AIRCACHE_EINVAL, "obs_window=%d < 0", d->obs_window);
+  const bool vis_window = d->obs_window < 0;  // the last -obs_window visual tokens
+  if (vis_window && (-(long long)d->obs_window > d->n_vis || -(long long)d->obs_window > d->n_txt))
+    return fail(AIRCACHE_EINVAL, "a visual window of %lld tokens needs at most min(n_vis, n_txt) = %d",
+                -(long long)d->obs_window, d->n_vis < d->n_txt ? d->n_vis : d->n_txt);
+  if (vis_window && d->path != AIRCACHE_PATH_AUTO && d->path != AIRCACHE_PATH_TILED)
+    return fail(AIRCACHE_EINVAL, "the visual window is served by the tiled path");
   if (d->select_mode != AIRCACHE_SELECT_SHARED && d->select_mode != AIRCACHE_SELECT_PER_KV_HEAD)
     return fail(AIRCACHE_EINVAL, "select_mode=%d unknown", d->select_mode);
   const bool per_head = d->select_mode == AIRCACHE_SELECT_PER_KV_HEAD;
@@ -1337,7 +1351,7 @@ int make_config(const aircache_desc *d, Config *cfg) {
   s.Nv = d->n_vis;
   s.Nt = d->n_txt;
   s.S = s.Nv + s.Nt;
-  s.cap = d->max_elite ? d->max_elite : d->n_txt;
+  s.cap = vis_window ? -d->obs_window : (d->max_elite ? d->max_elite : d->n_txt);
   const long long rows = (long long)s.G * s.cap;
   s.rcap16 = (int)((rows + 15) / 16 * 16);
   cfg->ktw = (d->dtype == AIRCACHE_BF16) ? 4 : 2;
@@ -1351,13 +1365,15 @@ int make_config(const aircache_desc *d, Config *cfg) {
   s.scale2 = (float)(1.4426950408889634 / sqrt((double)s.D));
   s.ratio = d->ratio;
   s.budget_mode = d->budget_mode;
-  s.window = d->obs_window < d->n_txt ? d->obs_window : d->n_txt;
+  s.window = d->obs_window < d->n_txt ? d->obs_window : d->n_txt;  // negative: the visual window
   s.nsel = per_head ? s.Hkv : 1;
   s.per_head = per_head ? 1 : 0;
   s.lb0 = 0;
   s.nstat = s.ntiles;
-  s.qrows = s.Nt;
-  s.qoff = 0;
+  // the visual window reads every position's queries ([S] rows per head), the
+  // last text query among them at row N_v + N_t - 1
+  s.qrows = vis_window ? s.S : s.Nt;
+  s.qoff = vis_window ? s.Nv : 0;
   const int esz = d->dtype == AIRCACHE_BF16 ? 2 : 4;
   (void)esz;
   cfg->elite_lds = (size_t)(s.G > 1 ? s.G : 1) * s.Nt * sizeof(float);
@@ -1443,6 +1459,7 @@ int make_config(const aircache_desc *d, Config *cfg) {
                 kSmallMaxLayers);
   if (d->path != AIRCACHE_PATH_AUTO && d->path != AIRCACHE_PATH_SMALL) cfg->small = false;
   if (per_head) cfg->chunked = false, cfg->rows_kt = 0;
+  if (vis_window) cfg->chunked = false, cfg->rows_kt = 0, cfg->small = false;
   if (d->path == AIRCACHE_PATH_TILED || d->path == AIRCACHE_PATH_ROWS) cfg->chunked = false;
   if (d->path == AIRCACHE_PATH_TILED || d->path == AIRCACHE_PATH_CHUNKED) cfg->rows_kt = 0;
   if (cfg->small) cfg->chunked = false, cfg->rows_kt = 0;
@@ -2048,6 +2065,8 @@ int make_prefill_config(const aircache_desc *d, PrefillCfg *pc) {
   int rc;
   if ((rc = make_config(&dd, &pc->cfg))) return rc;
   if (d->dtype != AIRCACHE_BF16) return fail(AIRCACHE_EINVAL, "the prefill attention takes bfloat16 inputs");
+  if (d->obs_window < 0)
+    return fail(AIRCACHE_EINVAL, "the visual window is served by aircache_plan / aircache_run on every position's queries");
   Config &cfg = pc->cfg;
   Shape &s = cfg.sh;
   s.T = kPfKeys;

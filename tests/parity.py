@@ -94,9 +94,11 @@ def run_gpu(inp: wl.Inputs, alpha=None, ratio=None, max_elite=0, tensors=None, c
     return out
 
 
-def reference(inp: wl.Inputs, gpu: dict, alpha=None, ratio=None, budget_mode=0, obs_window=0, per_head=False):
+def reference(inp: wl.Inputs, gpu: dict, alpha=None, ratio=None, budget_mode=0, obs_window=0, per_head=False,
+              q_all=None):
     """Oracle values for every (l, b), conditional on the GPU's elite sets where
-    they differ only in threshold-ambiguous tokens."""
+    they differ only in threshold-ambiguous tokens. obs_window = -k: the
+    visual window over every position's queries q_all[l] [B][H_q][S][D]."""
     w = inp.w
     alpha = w.alpha if alpha is None else alpha
     ratio = w.ratio if ratio is None else ratio
@@ -109,6 +111,18 @@ def reference(inp: wl.Inputs, gpu: dict, alpha=None, ratio=None, budget_mode=0, 
     def one(lb):
         l, b = lb
         gel = gpu["elite_idx"][l, b, :gpu["n_elite"][l, b]]
+        if obs_window < 0:
+            # the visual window: its positions, and I_v over the visual keys only
+            kw = -obs_window
+            assert np.array_equal(gel, np.arange(w.Nv - kw, w.Nv)), f"(l={l}, b={b}) visual window differs"
+            ref["n_elite"][l, b] = kw
+            if per_head:
+                iv, ref["iv_head"][l, b] = oracle.visual_window(w, q_all[l], inp.k[l], b, kw, groups=True)
+            else:
+                iv = oracle.visual_window(w, q_all[l], inp.k[l], b, kw)
+            ref["iv"][l, b] = iv
+            ref["s_t"][l, b], ref["s_k"][l, b] = oracle.layer_stats(iv)
+            return
         if obs_window > 0:
             # a contiguous window: one exact answer
             el = oracle.window_select(w.Nt, obs_window)

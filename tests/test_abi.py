@@ -125,7 +125,8 @@ def test_run_launches(lib):
                                  dict(dtype="x"), dict(alpha=1.5), dict(alpha=float("nan")),
                                  dict(ratio=-0.1), dict(max_elite=129), dict(n_txt=4000), dict(path=4),
                                  dict(path=2, n_vis=4000), dict(budget_mode=5), dict(budget_mode=-1),
-                                 dict(obs_window=-1), dict(select=2), dict(select=-1), dict(select=1, path=2),
+                                 dict(obs_window=-129), dict(obs_window=-8, path=3), dict(obs_window=-8, path=4),
+                                 dict(obs_window=-8, n_vis=5), dict(select=2), dict(select=-1), dict(select=1, path=2),
                                  dict(select=1, path=3)])
 def test_invalid_descriptor(lib, bad):
     if bad.get("dtype") == "x":
@@ -272,3 +273,14 @@ def test_prefill_argument_errors(lib):
     f = desc(n_layers=2, dtype="f32")
     assert _lib.prefill_attention(f, q, k, v, o, 0) == _lib.AIRCACHE_EINVAL                          # bf16 only
     assert "bfloat16" in lib.aircache_last_error().decode()
+
+
+def test_visual_window_descriptor(lib):
+    """A visual window (obs_window = -k) resolves to the tiled path, sizes its
+    rows for the window, and is refused by the prefill entry points."""
+    d = desc(obs_window=-32)
+    assert _lib.resolved_path(d) == _lib.PATH_TILED
+    assert _lib.workspace_size(d) > 0
+    assert _lib.resolved_path(desc(obs_window=-32, path=1)) == _lib.PATH_TILED
+    assert _lib.resolved_path(desc(obs_window=-32, select=1)) == _lib.PATH_TILED
+    assert _lib.prefill_workspace_size(d) == 0
