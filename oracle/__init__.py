@@ -42,7 +42,9 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        l = C.CDLL(build())
+        # AIRCACHE_ORACLE_LIB: another build of the same source (the
+        # sanitizer build of tests/test_host_sanitizers.py)
+        l = C.CDLL(os.environ.get("AIRCACHE_ORACLE_LIB") or build())
         P = C.c_void_p
         l.orc_elite_select.argtypes = [C.POINTER(Desc), P, P, C.c_int, P, P]
         l.orc_elite_select.restype = C.c_int

@@ -15,7 +15,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(_lib.LIB_PATH):
+    # AIRCACHE_ABI_TEST_LIB: another build of the same library (the host
+    # sanitizer build of tests/test_host_sanitizers.py)
+    other = os.environ.get("AIRCACHE_ABI_TEST_LIB")
+    if other:
+        _lib.LIB_PATH = other
+    elif not os.path.exists(_lib.LIB_PATH):
         build(force=False)
     return _lib.load()
 
