@@ -59,7 +59,7 @@ struct PrefillArgs {
   int layer;
   const int32_t *elite, *n_elite;  // the layer's rows of the plan
   float *e;                        // [B][Hkv][rcap16][evs] exp2(s - m) of the elite rows (this layer)
-  float2 *stats;                   // [B][Hkv][rcap16][nstat] (m, sum) per elite row and tile
+  float2 *stats;                   // [B][Hkv][rcap16][nstat] per elite row: (m_t, 0) per visual tile, then (M, Z)
   int evs;                         // row stride of e: N_v rounded up to the key tile
   int nattn;                       // attention workgroups; the blocks after them finalize the previous layer
   const float *fin_e;              // the previous layer's scoring terms (the other workspace slot)
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) oacc[d][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
-  float zrun[2] = {0.f, 0.f};  // the scores' running sum over visual keys (same reference as lrun)
+  float zrun[2] = {0.f, 0.f};  // the lane's part of the scores' running sum over visual keys (reference as lrun)
   int qrow[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) qrow[qb] = row0 + 32 * wave + 16 * qb + n;
@@ -404,15 +404,19 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
         for (int d = 0; d < ND; ++d) oacc[d][qb] *= alpha;
       }
       if (score && key0 < Nv) {
-        // the tile's visual keys for the elite rows: (m, sum), and the
+        // the tile's visual keys for the elite rows: the reference m_t, the
         // exponentials as two runs of 8 keys per lane (keys past N_v land in
-        // the row's padding and are never read)
+        // the row's padding and are never read), and the lane's part of the
+        // running visual sum (the tile's sum ls when every key is visual)
+        if (key0 + kPfKeys > Nv) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+          for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (key0 + pf_key(kb, 4 * grp + i) < Nv) zv += s[kb][qb][i];
-        zv = sum_across_rows(zv);
+            for (int i = 0; i < 4; ++i)
+              if (key0 + pf_key(kb, 4 * grp + i) < Nv) zv += s[kb][qb][i];
+        } else {
+          zv = ls;
+        }
         zrun[qb] = zrun[qb] * alpha + zv;
         if (erow[qb] >= 0) {
 #pragma unroll
@@ -421,15 +425,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
             dst[0] = s[2 * sl][qb];
             dst[1] = s[2 * sl + 1][qb];
           }
-          if (grp == 0) {
-            st_base[(size_t)erow[qb] * sh.nstat + kt] = make_float2(mnew, zv);
-            if (kt == sh.ntiles - 1) {
-              // the row's normaliser: the visual keys' running pair and the elite text keys' pair
-              const float M = fmaxf(mnew, xm[qb]);
-              const float Z = zrun[qb] * exp2f(mnew - M) + (xm[qb] > -INFINITY ? xz[qb] * exp2f(xm[qb] - M) : 0.f);
-              st_base[(size_t)erow[qb] * sh.nstat + sh.ntiles] = make_float2(M, Z);
-            }
-          }
+          if (grp == 0) st_base[(size_t)erow[qb] * sh.nstat + kt] = make_float2(mnew, 0.f);
+        }
+        if (kt == sh.ntiles - 1) {
+          // the row's normaliser: the visual keys' running sum (the four
+          // lane rows added) and the elite text keys' pair
+          const float zvis = sum_across_rows(zrun[qb]);
+          const float M = fmaxf(mnew, xm[qb]);
+          const float Z = zvis * exp2f(mnew - M) + (xm[qb] > -INFINITY ? xz[qb] * exp2f(xm[qb] - M) : 0.f);
+          if (grp == 0 && erow[qb] >= 0) st_base[(size_t)erow[qb] * sh.nstat + sh.ntiles] = make_float2(M, Z);
         }
       }
     }
