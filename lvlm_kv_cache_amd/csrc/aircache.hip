@@ -784,7 +784,7 @@ __global__ __launch_bounds__(kRowsThreads) void cross_score_rows_kernel(Shape sh
 // The election counter resets itself: the last arriver zeroes it for the next
 // call. (The chunked path computes the elite sets inside its own launch.)
 // ----------------------------------------------------------------------------
-constexpr int kEliteThreads = 256;
+constexpr int kEliteThreads = 512;
 constexpr int kEliteWaves = kEliteThreads / 64;
 
 template <typename Tag, int D>
