@@ -68,6 +68,8 @@ def lib():
         l.orc_decode_attention.restype = None
         l.orc_prefill_attention.argtypes = [C.POINTER(Desc), P, P, P, C.c_int, C.c_int, C.c_int, P]
         l.orc_prefill_attention.restype = None
+        l.orc_decode_attention_i8.argtypes = [C.POINTER(Desc), P, P, P, P, C.c_int, P, P]
+        l.orc_decode_attention_i8.restype = None
         l.orc_visual_window.argtypes = [C.POINTER(Desc), P, P, C.c_int, C.c_int, P, P]
         l.orc_visual_window.restype = None
         l.orc_run.argtypes = [C.POINTER(Desc)] + [P] * 15
@@ -203,6 +205,23 @@ def decode_attention_segment(w, k_seg, v_seg, n: int, q) -> np.ndarray:
     assert k_seg.size == v_seg.size == w.Hkv * n * w.D and q.shape == (w.Hq, w.D)
     o = np.zeros((w.Hq, w.D), np.float64)
     lib().orc_decode_attention(C.byref(desc_of(w)), _ptr(k_seg), _ptr(v_seg), int(n), _ptr(q), _ptr(o))
+    return o
+
+
+def decode_attention_i8_segment(w, kq_seg, vq_seg, k_scale, v_scale, n: int, q) -> np.ndarray:
+    """Decode attention over one (layer, sample) segment [H_kv][n][D] of the
+    int8 cache (value = code * the KV head's scale): o [H_q][D] (float64)."""
+    store = np.float32 if w.dtype == "f32" else np.uint16
+    kq_seg = np.ascontiguousarray(kq_seg, dtype=np.int8).ravel()
+    vq_seg = np.ascontiguousarray(vq_seg, dtype=np.int8).ravel()
+    ks = np.ascontiguousarray(k_scale, dtype=np.float32).ravel()
+    vs = np.ascontiguousarray(v_scale, dtype=np.float32).ravel()
+    q = np.ascontiguousarray(q, dtype=store)
+    assert kq_seg.size == vq_seg.size == w.Hkv * n * w.D and ks.size == vs.size == w.Hkv
+    assert q.shape == (w.Hq, w.D)
+    o = np.zeros((w.Hq, w.D), np.float64)
+    lib().orc_decode_attention_i8(C.byref(desc_of(w)), _ptr(kq_seg), _ptr(vq_seg), _ptr(ks), _ptr(vs), int(n),
+                                  _ptr(q), _ptr(o))
     return o
 
 

@@ -391,6 +391,37 @@ void orc_decode_attention(const orc_desc *w, const void *k_seg, const void *v_se
 }
 
 /*
+ * Decode attention over one segment of the int8 cache: orc_decode_attention
+ * with every cached value read as code * scale (the quantisation's reading,
+ * value = code times the scale of its KV head, for K and for V), dequantised
+ * exactly in double precision. kq_seg, vq_seg: int8 [H_kv][n][D]; k_scale,
+ * v_scale: [H_kv]; q: [H_q][D] in the descriptor's dtype; o: [H_q][D].
+ */
+void orc_decode_attention_i8(const orc_desc *w, const int8_t *kq_seg, const int8_t *vq_seg, const float *k_scale,
+                             const float *v_scale, int n, const void *q, double *o) {
+  const int G = w->Hq / w->Hkv, D = w->D;
+  const double scale = sqrt((double)D);
+  double *z = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  for (int h = 0; h < w->Hq; ++h) {
+    const int g = h / G;
+    const double ks = (double)k_scale[g], vs = (double)v_scale[g];
+    for (int j = 0; j < n; ++j) {
+      double acc = 0.0;
+      for (int d = 0; d < D; ++d)
+        acc += elem(q, (size_t)h * D + d, w->dtype) * ((double)kq_seg[((size_t)g * n + j) * D + d] * ks);
+      z[j] = acc / scale;
+    }
+    softmax(z, n);
+    for (int d = 0; d < D; ++d) {
+      double acc = 0.0;
+      for (int j = 0; j < n; ++j) acc += z[j] * ((double)vq_seg[((size_t)g * n + j) * D + d] * vs);
+      o[(size_t)h * D + d] = acc;
+    }
+  }
+  free(z);
+}
+
+/*
  * The window ablation's visual window (AirCache paper-notes page, "消融实验",
  * the window table's visual-window row, read with "Elite Observation Window"):
  * the observation rows are the last kwin visual tokens instead of the elite

@@ -793,3 +793,50 @@ def test_visual_window_ignores_text_positions():
     k2[:, :, w.Nv:] += 1.0
     b = oracle.visual_window(w, qa2, k2, 0, 3)
     np.testing.assert_array_equal(a, b)
+
+
+# ----------------------------------------------- decode over the int8 cache ----
+# The decode attention with every cached value read as code * scale.
+
+def _i8seg(w, rng, n):
+    kq = rng.integers(-127, 128, size=(w.Hkv, n, w.D)).astype(np.int8)
+    vq = rng.integers(-127, 128, size=(w.Hkv, n, w.D)).astype(np.int8)
+    q = rng.standard_normal((w.Hq, w.D)).astype(np.float32)
+    if w.dtype == "bf16":
+        q = wl.f32_to_bf16_bits(q)
+    return kq, vq, q
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_i8_equals_decode_on_exactly_dequantised_values(dtype):
+    """With power-of-two scales code * scale is exact in float32, so the int8
+    decode equals the float decode of that segment (pinned above) bit for bit."""
+    w = wl.custom(Nv=8, Nt=2, Hq=6, Hkv=2, D=16, dtype=dtype)
+    rng = np.random.default_rng(40)
+    n = 9
+    kq, vq, q = _i8seg(w, rng, n)
+    ks = np.array([2.0 ** -6, 2.0 ** -8], np.float32)
+    vs = np.array([2.0 ** -5, 2.0 ** -7], np.float32)
+    o8 = oracle.decode_attention_i8_segment(w, kq, vq, ks, vs, n, q)
+    kf = (kq.astype(np.float32) * ks[:, None, None]).astype(np.float32)
+    vf = (vq.astype(np.float32) * vs[:, None, None]).astype(np.float32)
+    if dtype == "bf16":  # codes times 2^-k are exact in bfloat16 too (8-bit significand holds |code| <= 127)
+        kf, vf = wl.f32_to_bf16_bits(kf), wl.f32_to_bf16_bits(vf)
+    np.testing.assert_array_equal(o8, oracle.decode_attention_segment(w, kf, vf, n, q))
+
+
+def test_decode_i8_single_row_and_value_scale():
+    w = wl.custom(Nv=8, Nt=2, Hq=2, Hkv=1, D=8)
+    rng = np.random.default_rng(41)
+    kq, vq, q = _i8seg(w, rng, 1)
+    ks, vs = np.array([0.013], np.float32), np.array([0.021], np.float32)
+    o = oracle.decode_attention_i8_segment(w, kq, vq, ks, vs, 1, q)
+    for h in range(w.Hq):
+        np.testing.assert_array_equal(o[h], vq[0, 0].astype(np.float64) * float(vs[0]))
+    # o is linear in the V scale; zero V codes give zero
+    kq, vq, q = _i8seg(w, rng, 5)
+    a = oracle.decode_attention_i8_segment(w, kq, vq, ks, vs, 5, q)
+    b = oracle.decode_attention_i8_segment(w, kq, vq, ks, 2 * vs, 5, q)
+    np.testing.assert_allclose(b, 2 * a, rtol=1e-14, atol=0)
+    z = oracle.decode_attention_i8_segment(w, kq, np.zeros_like(vq), ks, vs, 5, q)
+    assert not z.any()
