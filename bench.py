@@ -461,6 +461,22 @@ def main():
         quant = {"kernels": ["quantize_i8_kernel"], "us_per_call": q_us, "algorithmic_bytes": q_bytes,
                  "achieved_gbps": q_bytes / (q_us * 1e-6) / 1e9, "peak_gbps": PEAK_HBM_GBPS,
                  "frac": q_bytes / (q_us * 1e-6) / 1e9 / PEAK_HBM_GBPS}
+        # decode attention over that int8 cache (aircache_decode_i8)
+        bd8 = ac.bind_decode(qd, plan, kq, vq, od, stream=stream, scales=(ks, vs))
+        for _ in range(3):
+            bd8()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(a.steps):
+            bd8()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        d8_us = 1e3 * e0.elapsed_time(e1) / a.steps
+        d8_bytes = n_el * 1 + w.L * w.B * w.Hq * w.D * (esz + 4)  # every kept code once, queries, outputs
+        dec["int8_cache"] = {"kernels": ["decode_partial_kernel (int8)", "decode_combine_kernel"],
+                             "us_per_call": d8_us, "algorithmic_bytes": d8_bytes,
+                             "achieved_gbps": d8_bytes / (d8_us * 1e-6) / 1e9,
+                             "frac": d8_bytes / (d8_us * 1e-6) / 1e9 / PEAK_HBM_GBPS}
     # Prefill attention of every layer (bfloat16 workloads): alone
     # (aircache_prefill_attention), with the scores fused in
     # (aircache_prefill_layer) plus the compaction, and alone followed by the

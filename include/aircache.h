@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define AIRCACHE_ABI_VERSION 3
+#define AIRCACHE_ABI_VERSION 4
 #define AIRCACHE_MAX_LAYERS 128
 
 typedef enum {
@@ -335,6 +335,22 @@ size_t aircache_decode_workspace_size(const aircache_desc *desc);
 int aircache_decode(const aircache_desc *desc, const void *const *q_dec, const aircache_plan_buf *plan,
                     const void *const *k_out, const void *const *v_out, float *const *o, void *workspace,
                     size_t ws_bytes, void *stream);
+
+/* Decode attention over the int8 cache that aircache_quantize_i8 wrote: the
+ * same attention as aircache_decode (the primer page's o_t equation) with
+ * every cached value read as code * scale, the scale of its (layer, sample,
+ * KV head) for K or for V. The codes' dot products with the query are formed
+ * in float32 (the codes are exact) and multiplied by the K scale; the
+ * weighted sum of V codes is multiplied by the V scale.
+ *   kq, vq      : host arrays of n_layers device pointers to the int8 codes,
+ *                 the compacted layout of aircache_quantize_i8 (read-only)
+ *   k_scale, v_scale: device float [L][B][H_kv] (read-only)
+ *   q_dec, plan, o, workspace: as for aircache_decode (the same workspace
+ *                 size, aircache_decode_workspace_size)
+ * Errors and limits as for aircache_decode; NULL scales are AIRCACHE_EINVAL. */
+int aircache_decode_i8(const aircache_desc *desc, const void *const *q_dec, const aircache_plan_buf *plan,
+                       const int8_t *const *kq, const int8_t *const *vq, const float *k_scale, const float *v_scale,
+                       float *const *o, void *workspace, size_t ws_bytes, void *stream);
 
 /* Prefill attention of one layer with the pass's scoring fused in: the
  * attention is the KV-cache primer page's (devpress.csdn.net) section 2.1

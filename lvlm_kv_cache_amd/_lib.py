@@ -24,7 +24,8 @@ EXPORTS = ["aircache_abi_version", "aircache_workspace_size", "aircache_max_comp
            "aircache_plan", "aircache_compress", "aircache_run", "aircache_plan_profiled",
            "aircache_compress_profiled", "aircache_run_profiled", "aircache_run_noalloc", "aircache_strerror",
            "aircache_last_error", "aircache_decode_workspace_size", "aircache_decode", "aircache_quantize_i8",
-           "aircache_prefill_workspace_size", "aircache_prefill_layer", "aircache_prefill_attention"]
+           "aircache_prefill_workspace_size", "aircache_prefill_layer", "aircache_prefill_attention",
+           "aircache_decode_i8"]
 NOALLOC_SCRATCH_BYTES = 128 << 20  # AIRCACHE_NOALLOC_SCRATCH_BYTES
 PLAN_KERNELS = ["elite_select", "cross_score", "finalize", "topk_select"]
 COMPRESS_KERNELS = ["kv_gather"]
@@ -91,6 +92,8 @@ def load() -> C.CDLL:
         lib.aircache_decode_workspace_size.argtypes = [C.POINTER(Desc)]
         lib.aircache_decode.restype = C.c_int
         lib.aircache_decode.argtypes = [C.POINTER(Desc), P, C.POINTER(PlanBuf), P, P, P, P, C.c_size_t, P]
+        lib.aircache_decode_i8.restype = C.c_int
+        lib.aircache_decode_i8.argtypes = [C.POINTER(Desc), P, C.POINTER(PlanBuf), P, P, P, P, P, P, C.c_size_t, P]
         lib.aircache_quantize_i8.restype = C.c_int
         lib.aircache_quantize_i8.argtypes = [C.POINTER(Desc), C.POINTER(PlanBuf), P, P, P, P, P, P, P]
         lib.aircache_prefill_workspace_size.restype = C.c_size_t
@@ -180,6 +183,14 @@ def decode(desc: Desc, q_ptrs, buf: PlanBuf, ko_ptrs, vo_ptrs, o_ptrs, ws_ptr: i
     q, ko, vo, o = [ptr_array(p) if p is not None else None for p in (q_ptrs, ko_ptrs, vo_ptrs, o_ptrs)]
     return load().aircache_decode(C.byref(desc), q, C.byref(buf), ko, vo, o, C.c_void_p(ws_ptr), ws_bytes,
                                   C.c_void_p(stream))
+
+
+def decode_i8(desc: Desc, q_ptrs, buf: PlanBuf, kq_ptrs, vq_ptrs, k_scale: int, v_scale: int, o_ptrs,
+              ws_ptr: int, ws_bytes: int, stream: int) -> int:
+    """aircache_decode_i8: decode attention over the int8 cache."""
+    q, kq, vq, o = [ptr_array(p) if p is not None else None for p in (q_ptrs, kq_ptrs, vq_ptrs, o_ptrs)]
+    return load().aircache_decode_i8(C.byref(desc), q, C.byref(buf), kq, vq, C.c_void_p(k_scale),
+                                     C.c_void_p(v_scale), o, C.c_void_p(ws_ptr), ws_bytes, C.c_void_p(stream))
 
 
 def quantize_i8(desc: Desc, buf: PlanBuf, ko_ptrs, vo_ptrs, kq_ptrs, vq_ptrs, k_scale: int, v_scale: int,

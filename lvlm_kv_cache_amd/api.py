@@ -230,6 +230,37 @@ class AirCache:
                                self._stream(stream)))
         return o
 
+    def decode_i8(self, q_dec, plan: PlanOutputs, kq, vq, k_scale, v_scale, o=None, stream=None):
+        """Decode attention over the int8 cache of quantize_i8()
+        (aircache_decode_i8): as decode(), every cached value read as code *
+        scale. kq, vq: per layer int8 tensors of at least out_off[l][B]
+        elements; k_scale, v_scale: float32 [L][B][H_kv]."""
+        s = self.shape
+        self._check_layers(q_dec, (s["B"], s["Hq"], s["D"]), "q_dec")
+        cap = _lib.max_compacted_elems(self.desc)
+        for name, ts in (("kq", kq), ("vq", vq)):
+            if len(ts) != s["L"]:
+                raise ValueError(f"{name}: {len(ts)} layers given")
+            for l, t in enumerate(ts):
+                if t.device != self.device or t.dtype != torch.int8 or not t.is_contiguous() or t.numel() < cap:
+                    raise ValueError(f"{name}[{l}] must be a contiguous int8 tensor on {self.device} "
+                                     f"with at least {cap} elements")
+        for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if t.device != self.device or t.dtype != torch.float32 or not t.is_contiguous() or \
+                    tuple(t.shape) != (s["L"], s["B"], s["Hkv"]):
+                raise ValueError(f"{name} must be a contiguous float32 [L, B, H_kv] tensor on {self.device}")
+        if o is None:
+            o = [torch.empty(s["B"], s["Hq"], s["D"], dtype=torch.float32, device=self.device)
+                 for _ in range(s["L"])]
+        need = _lib.decode_workspace_size(self.desc)
+        if getattr(self, "dec_workspace", None) is None or self.dec_workspace.numel() < need:
+            self.dec_workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+        _lib.check(_lib.decode_i8(self.desc, [t.data_ptr() for t in q_dec], plan.buf(),
+                                  [t.data_ptr() for t in kq], [t.data_ptr() for t in vq], k_scale.data_ptr(),
+                                  v_scale.data_ptr(), [t.data_ptr() for t in o], self.dec_workspace.data_ptr(),
+                                  need, self._stream(stream)))
+        return o
+
     def quantize_i8(self, plan: PlanOutputs, k_out, v_out, kq=None, vq=None, k_scale=None, v_scale=None,
                     stream=None):
         """int8 codes of the compacted cache with one float32 scale per
@@ -268,10 +299,11 @@ class AirCache:
         checks and marshalling done once, here."""
         return BoundQuantize(self, plan, k_out, v_out, kq, vq, k_scale, v_scale, stream)
 
-    def bind_decode(self, q_dec, plan: PlanOutputs, k_out, v_out, o, stream=None) -> "BoundDecode":
+    def bind_decode(self, q_dec, plan: PlanOutputs, k_out, v_out, o, stream=None, scales=None) -> "BoundDecode":
         """A BoundDecode running decode() on these tensors with the checks and
-        marshalling done once, here."""
-        return BoundDecode(self, q_dec, plan, k_out, v_out, o, stream)
+        marshalling done once, here; with scales = (k_scale, v_scale), k_out
+        and v_out are the int8 codes and it runs decode_i8()."""
+        return BoundDecode(self, q_dec, plan, k_out, v_out, o, stream, scales)
 
     # -- prefill attention with the scores fused in (aircache_prefill_layer) --
     def _check_prefill(self, q, k, v, o):
@@ -451,10 +483,16 @@ class BoundDecode:
     """AirCache.decode over fixed tensors, validated and marshalled once (as
     BoundPass does for the pass). The tensors must stay alive while it is used."""
 
-    def __init__(self, ac: "AirCache", q_dec, plan: PlanOutputs, k_out, v_out, o, stream=None):
+    def __init__(self, ac: "AirCache", q_dec, plan: PlanOutputs, k_out, v_out, o, stream=None, scales=None):
         s = ac.shape
-        ac._check_layers(q_dec, (s["B"], s["Hq"], s["D"]), "q_dec")
-        ac._check_outputs(k_out, v_out)
+        self._i8 = scales is not None
+        if self._i8:
+            ac.decode_i8(q_dec, plan, k_out, v_out, scales[0], scales[1], o=o, stream=stream)  # the checks, once
+            self._ks = _lib.C.c_void_p(scales[0].data_ptr())
+            self._vs = _lib.C.c_void_p(scales[1].data_ptr())
+        else:
+            ac._check_layers(q_dec, (s["B"], s["Hq"], s["D"]), "q_dec")
+            ac._check_outputs(k_out, v_out)
         for l, t in enumerate(o):
             if t.device != ac.device or t.dtype != torch.float32 or not t.is_contiguous() or \
                     tuple(t.shape) != (s["B"], s["Hq"], s["D"]):
@@ -462,7 +500,7 @@ class BoundDecode:
         need = _lib.decode_workspace_size(ac.desc)
         self.workspace = torch.empty(need, dtype=torch.uint8, device=ac.device)
         self.out = o
-        self._keep = (ac, q_dec, plan, k_out, v_out, o)
+        self._keep = (ac, q_dec, plan, k_out, v_out, o, scales)
         self._lib = _lib.load()
         self._desc = _lib.C.byref(ac.desc)
         self._buf = plan.buf()
@@ -476,8 +514,12 @@ class BoundDecode:
         self._st = _lib.C.c_void_p(ac._stream(stream))
 
     def __call__(self):
-        rc = self._lib.aircache_decode(self._desc, self._q, self._pbuf, self._ko, self._vo, self._o, self._ws,
-                                       self._ws_bytes, self._st)
+        if self._i8:
+            rc = self._lib.aircache_decode_i8(self._desc, self._q, self._pbuf, self._ko, self._vo, self._ks, self._vs,
+                                              self._o, self._ws, self._ws_bytes, self._st)
+        else:
+            rc = self._lib.aircache_decode(self._desc, self._q, self._pbuf, self._ko, self._vo, self._o, self._ws,
+                                           self._ws_bytes, self._st)
         if rc:
             _lib.check(rc)
         return self.out

@@ -18,6 +18,7 @@
 
 #include <mutex>
 #include <string>
+#include <type_traits>
 
 #include "aircache.h"
 #include "device_common.h"
@@ -2019,20 +2020,21 @@ size_t decode_ws_bytes(const Shape &s) {
   return align_up(units * sizeof(float2)) + align_up(units * (size_t)s.D * sizeof(float));
 }
 
-template <typename Tag, int D>
-int launch_decode(const Shape &s, const DecodeTables &tb, const aircache_plan_buf *plan, void *ws, hipStream_t st) {
+template <typename Tag, int D, bool Q8>
+int launch_decode(const Shape &s, const DecodeTables &tb, const aircache_plan_buf *plan, void *ws, hipStream_t st,
+                  DecodeScales scl) {
   const int smax = decode_splits(s.L, s.B, s.Hkv, kDecTargetCus);
   const size_t units = (size_t)s.L * s.B * s.Hq * smax;
   float2 *ml = static_cast<float2 *>(ws);
   float *acc = reinterpret_cast<float *>(static_cast<char *>(ws) + align_up(units * sizeof(float2)));
   const int64_t cap = (int64_t)s.B * s.Hkv * (int64_t)s.S * s.D;
-  const size_t lds = (size_t)decode_lds_bytes(s.G, D, Tag::kBytes);
+  const size_t lds = (size_t)decode_lds_bytes(s.G, D, Q8 ? 1 : Tag::kBytes);
   const long long grid = (long long)s.L * s.B * s.Hkv * smax;
   if (grid > INT32_MAX) return fail(AIRCACHE_EINVAL, "decode grid of %lld workgroups too large", grid);
   int rc;
-  if ((rc = allow_lds(decode_partial_kernel<Tag, D>, lds))) return rc;
-  hipLaunchKernelGGL((decode_partial_kernel<Tag, D>), dim3((unsigned)grid), dim3(kDecThreads), lds, st, s, tb,
-                     plan->budget, plan->out_off, cap, smax, ml, acc);
+  if ((rc = allow_lds(decode_partial_kernel<Tag, D, Q8>, lds))) return rc;
+  hipLaunchKernelGGL((decode_partial_kernel<Tag, D, Q8>), dim3((unsigned)grid), dim3(kDecThreads), lds, st, s, tb,
+                     plan->budget, plan->out_off, cap, smax, ml, acc, scl);
   if ((rc = check_hip(hipGetLastError(), "decode_partial_kernel launch"))) return rc;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(s.L * s.B * s.Hq)), dim3(D), 0, st, s, tb,
                      plan->budget, plan->out_off, cap, smax, ml, acc);
@@ -2178,6 +2180,47 @@ int launch_prefill(const PrefillCfg &pc, int layer, const void *q, const void *k
     if ((rc = check_hip(hipGetLastError(), "topk_select_kernel launch"))) return rc;
   }
   return AIRCACHE_OK;
+}
+
+// aircache_decode and aircache_decode_i8: kq / vq and the scales are NULL for
+// the compacted cache in the pass dtype.
+int decode_common(const aircache_desc *desc, const void *const *q_dec, const aircache_plan_buf *plan,
+                  const void *const *k_out, const void *const *v_out, const float *k_scale, const float *v_scale,
+                  float *const *o, void *workspace, size_t ws_bytes, void *stream, bool q8) {
+  Config cfg;
+  int rc;
+  if ((rc = make_config(desc, &cfg))) return rc;
+  const Shape &s = cfg.sh;
+  if (!plan || !plan->budget || !plan->out_off) return fail(AIRCACHE_EINVAL, "plan, plan->budget or plan->out_off is NULL");
+  if (!aligned16(plan->out_off)) return fail(AIRCACHE_EINVAL, "plan->out_off is not 16-byte aligned");
+  if (q8 && (!k_scale || !v_scale)) return fail(AIRCACHE_EINVAL, "k_scale or v_scale is NULL");
+  const int esize = q8 ? 1 : (desc->dtype == AIRCACHE_BF16 ? 2 : 4);
+  if ((long long)s.G * s.D / 8 > kDecThreads || decode_lds_bytes(s.G, s.D, esize) > kDecMaxLds)
+    return fail(AIRCACHE_EINVAL, "decode holds %d query heads per KV head at most for head_dim %d",
+                kDecThreads * 8 / s.D, s.D);
+  DecodeTables tb;
+  if ((rc = fill_table(q_dec, s.L, &tb.q, "q_dec"))) return rc;
+  if ((rc = fill_table(k_out, s.L, &tb.k, q8 ? "kq" : "k_out"))) return rc;
+  if ((rc = fill_table(v_out, s.L, &tb.v, q8 ? "vq" : "v_out"))) return rc;
+  LayerTable ot;
+  if ((rc = fill_table(reinterpret_cast<const void *const *>(o), s.L, &ot, "o"))) return rc;
+  for (int l = 0; l < AIRCACHE_MAX_LAYERS; ++l) tb.o.p[l] = const_cast<void *>(ot.p[l]);
+  if (!workspace || ws_bytes < decode_ws_bytes(s))
+    return fail(AIRCACHE_EWORKSPACE, "decode workspace of %zu bytes, %zu needed", ws_bytes, decode_ws_bytes(s));
+  if (!aligned16(workspace)) return fail(AIRCACHE_EINVAL, "workspace is not 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = desc->dtype == AIRCACHE_BF16;
+  const DecodeScales scl{k_scale, v_scale};
+  if (q8) {
+    if (bf && s.D == 128) return launch_decode<Bf16Tag, 128, true>(s, tb, plan, workspace, st, scl);
+    if (bf) return launch_decode<Bf16Tag, 64, true>(s, tb, plan, workspace, st, scl);
+    if (s.D == 128) return launch_decode<F32Tag, 128, true>(s, tb, plan, workspace, st, scl);
+    return launch_decode<F32Tag, 64, true>(s, tb, plan, workspace, st, scl);
+  }
+  if (bf && s.D == 128) return launch_decode<Bf16Tag, 128, false>(s, tb, plan, workspace, st, scl);
+  if (bf) return launch_decode<Bf16Tag, 64, false>(s, tb, plan, workspace, st, scl);
+  if (s.D == 128) return launch_decode<F32Tag, 128, false>(s, tb, plan, workspace, st, scl);
+  return launch_decode<F32Tag, 64, false>(s, tb, plan, workspace, st, scl);
 }
 
 extern "C" {
@@ -2337,32 +2380,15 @@ size_t aircache_decode_workspace_size(const aircache_desc *desc) {
 int aircache_decode(const aircache_desc *desc, const void *const *q_dec, const aircache_plan_buf *plan,
                     const void *const *k_out, const void *const *v_out, float *const *o, void *workspace,
                     size_t ws_bytes, void *stream) {
-  Config cfg;
-  int rc;
-  if ((rc = make_config(desc, &cfg))) return rc;
-  const Shape &s = cfg.sh;
-  if (!plan || !plan->budget || !plan->out_off) return fail(AIRCACHE_EINVAL, "plan, plan->budget or plan->out_off is NULL");
-  if (!aligned16(plan->out_off)) return fail(AIRCACHE_EINVAL, "plan->out_off is not 16-byte aligned");
-  const int esize = desc->dtype == AIRCACHE_BF16 ? 2 : 4;
-  if ((long long)s.G * s.D / 8 > kDecThreads || decode_lds_bytes(s.G, s.D, esize) > kDecMaxLds)
-    return fail(AIRCACHE_EINVAL, "decode holds %d query heads per KV head at most for head_dim %d",
-                kDecThreads * 8 / s.D, s.D);
-  DecodeTables tb;
-  if ((rc = fill_table(q_dec, s.L, &tb.q, "q_dec"))) return rc;
-  if ((rc = fill_table(k_out, s.L, &tb.k, "k_out"))) return rc;
-  if ((rc = fill_table(v_out, s.L, &tb.v, "v_out"))) return rc;
-  LayerTable ot;
-  if ((rc = fill_table(reinterpret_cast<const void *const *>(o), s.L, &ot, "o"))) return rc;
-  for (int l = 0; l < AIRCACHE_MAX_LAYERS; ++l) tb.o.p[l] = const_cast<void *>(ot.p[l]);
-  if (!workspace || ws_bytes < decode_ws_bytes(s))
-    return fail(AIRCACHE_EWORKSPACE, "decode workspace of %zu bytes, %zu needed", ws_bytes, decode_ws_bytes(s));
-  if (!aligned16(workspace)) return fail(AIRCACHE_EINVAL, "workspace is not 16-byte aligned");
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool bf = desc->dtype == AIRCACHE_BF16;
-  if (bf && s.D == 128) return launch_decode<Bf16Tag, 128>(s, tb, plan, workspace, st);
-  if (bf) return launch_decode<Bf16Tag, 64>(s, tb, plan, workspace, st);
-  if (s.D == 128) return launch_decode<F32Tag, 128>(s, tb, plan, workspace, st);
-  return launch_decode<F32Tag, 64>(s, tb, plan, workspace, st);
+  return decode_common(desc, q_dec, plan, k_out, v_out, nullptr, nullptr, o, workspace, ws_bytes, stream, false);
+}
+
+int aircache_decode_i8(const aircache_desc *desc, const void *const *q_dec, const aircache_plan_buf *plan,
+                       const int8_t *const *kq, const int8_t *const *vq, const float *k_scale, const float *v_scale,
+                       float *const *o, void *workspace, size_t ws_bytes, void *stream) {
+  return decode_common(desc, q_dec, plan, reinterpret_cast<const void *const *>(kq),
+                       reinterpret_cast<const void *const *>(vq), k_scale, v_scale, o, workspace, ws_bytes, stream,
+                       true);
 }
 
 int aircache_quantize_i8(const aircache_desc *desc, const aircache_plan_buf *plan, const void *const *k_out,

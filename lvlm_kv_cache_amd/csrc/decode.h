@@ -75,14 +75,45 @@ __host__ __device__ inline int decode_lds_bytes(int G, int D, int esize) {
   return main > red ? main : red;
 }
 
-template <typename Tag, int D>
+// Eight int8 codes (8 bytes) as an MFMA operand fragment of the query's type:
+// the integers in [-127, 127] are exact in bfloat16 and float32.
+__device__ __forceinline__ void codes_to_frag(const int8_t *p, Frag<Bf16Tag> &f) {
+  const uint2 w = *reinterpret_cast<const uint2 *>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = (int)(int8_t)(((i < 4 ? w.x : w.y) >> (8 * (i & 3))) & 0xffu);
+    f.v[i] = (uint16_t)(__float_as_uint((float)c) >> 16);  // exact: the low half is zero
+  }
+}
+__device__ __forceinline__ void codes_to_frag(const int8_t *p, Frag<F32Tag> &f) {
+  const uint2 w = *reinterpret_cast<const uint2 *>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.lo[i] = (float)(int8_t)((w.x >> (8 * i)) & 0xffu);
+    f.hi[i] = (float)(int8_t)((w.y >> (8 * i)) & 0xffu);
+  }
+}
+
+// Scales of the int8 cache (aircache_quantize_i8's): [L][B][H_kv] for K and V.
+struct DecodeScales {
+  const float *k, *v;
+};
+
+// Q8: the compacted cache is int8 codes with one scale per (layer, sample, KV
+// head) for K and for V (value = code * scale): logits are the codes' dot
+// products times the K scale, the weighted sum of V codes is times the V
+// scale, both applied once per row and per output.
+template <typename Tag, int D, bool Q8>
 __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(Shape sh, DecodeTables tb,
                                                                      const int32_t *budget, const int64_t *out_off,
                                                                      int64_t cap_elems, int S, float2 *part_ml,
-                                                                     float *part_acc) {
-  using E = typename Tag::store_t;
+                                                                     float *part_acc, DecodeScales scl) {
+  using QE = typename Tag::store_t;                      // the queries' type
+  using E = typename std::conditional<Q8, int8_t, QE>::type;  // the cache's
+  constexpr int EB = Q8 ? 1 : Tag::kBytes;
   constexpr int NT = kDecThreads;
-  constexpr int kPiece = 16 / Tag::kBytes;     // elements per 16-byte piece
+  constexpr int kPiece = 16 / EB;              // cache elements per 16-byte piece
+  constexpr int kQPiece = 16 / Tag::kBytes;    // query elements per 16-byte piece
   extern __shared__ __attribute__((aligned(16))) float dec_lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, grp = lane >> 4;
@@ -100,15 +131,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(Shape sh, D
   const int n = ok ? r + sh.Nt : 0;
   // this split's rows [lo, hi), an even share of the n rows
   const int lo = (int)((long long)n * s / S), hi = (int)((long long)n * (s + 1) / S);
-  E *qs = reinterpret_cast<E *>(dec_lds);            // [G][D] as stored (room for floats)
+  QE *qs = reinterpret_cast<QE *>(dec_lds);          // [G][D] as stored (room for floats)
   float *zp = dec_lds + G * D;                       // [G][kDecRows]
   float *run = zp + G * kDecRows;                    // [G][4]: max, sum, rescale
   E *vs = reinterpret_cast<E *>(run + G * 4);        // [kDecRows][D]
   const E *kseg = static_cast<const E *>(tb.k.p[l]) + (ok ? off + (int64_t)g * n * D : 0);
   const E *vseg = static_cast<const E *>(tb.v.p[l]) + (ok ? off + (int64_t)g * n * D : 0);
-  const E *qb = static_cast<const E *>(tb.q.p[l]) + ((size_t)b * sh.Hq + (size_t)g * G) * D;
+  const QE *qb = static_cast<const QE *>(tb.q.p[l]) + ((size_t)b * sh.Hq + (size_t)g * G) * D;
+  // the int8 cache's scales of this (layer, sample, KV head)
+  const float ksc = Q8 ? scl.k[(size_t)lb * Hkv + g] : 1.f, vsc = Q8 ? scl.v[(size_t)lb * Hkv + g] : 1.f;
   // the G query rows into LDS, as stored
-  for (int p = tid; p < G * D / kPiece; p += NT)
+  for (int p = tid; p < G * D / kQPiece; p += NT)
     reinterpret_cast<u32x4_t *>(qs)[p] = reinterpret_cast<const u32x4_t *>(qb)[p];
   for (int h = tid; h < G; h += NT) {
     run[h * 4 + 0] = -INFINITY;
@@ -142,8 +175,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(Shape sh, D
       u32x4_t vw[VP];
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) {
-        if (rv) kf[c].load(kp + c * 32);
-        else kf[c].zero();
+        if (!rv) kf[c].zero();
+        else if constexpr (Q8) codes_to_frag(kp + c * 32, kf[c]);
+        else kf[c].load(kp + c * 32);
       }
 #pragma unroll
       for (int i = 0; i < VP; ++i) vw[i] = tid + i * NT < pieces ? vp[tid + i * NT] : u32x4_t{0u, 0u, 0u, 0u};
@@ -166,7 +200,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(Shape sh, D
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rw = wave * 16 + grp * 4 + i;
-          zp[(h0 + n16) * kDecRows + rw] = rw < nr ? acc4[i] * sh.scale2 : -INFINITY;
+          zp[(h0 + n16) * kDecRows + rw] = rw < nr ? acc4[i] * (sh.scale2 * ksc) : -INFINITY;
         }
     }
     __syncthreads();
@@ -203,7 +237,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(Shape sh, D
       for (int j = opart; j < nr; j += P) {
         float vv[8];
         const E *vr = vs + j * D + 8 * oe;
-        if (Tag::kBytes == 2) {
+        if constexpr (Q8) {
+          const uint2 w = *reinterpret_cast<const uint2 *>(vr);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            vv[i] = (float)(int8_t)((w.x >> (8 * i)) & 0xffu);
+            vv[4 + i] = (float)(int8_t)((w.y >> (8 * i)) & 0xffu);
+          }
+        } else if (Tag::kBytes == 2) {
           widen(*reinterpret_cast<const u32x4_t *>(vr), vv, Tag{});
         } else {
           widen(*reinterpret_cast<const u32x4_t *>(vr), vv, Tag{});
@@ -230,7 +271,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(Shape sh, D
     const int h = i / D, d = i - h * D;
     float a = 0.f;
     for (int q = 0; q < P; ++q) a += red[((size_t)q * G + h) * D + d];
-    part_acc[(((size_t)lb * sh.Hq + (size_t)g * G + h) * S + s) * D + d] = a;
+    part_acc[(((size_t)lb * sh.Hq + (size_t)g * G + h) * S + s) * D + d] = a * vsc;
   }
 }
 

@@ -36,7 +36,7 @@ def test_exports_every_declared_function(lib):
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.aircache_abi_version() == 3
+    assert lib.aircache_abi_version() == 4
 
 
 def test_struct_layouts():

@@ -26,7 +26,10 @@ pytestmark = pytest.mark.gpu
 RTOL = 2e-4
 
 
-def _decode_case(w, seed, max_elite=0, layers=None):
+def _decode_case(w, seed, max_elite=0, layers=None, int8=False):
+    """int8: decode over the int8 cache of quantize_i8 (aircache_decode_i8),
+    against the oracle's int8 decode fed the GPU's codes and scales (the
+    quantisation itself is checked bit for bit in tests/test_f4_gpu.py)."""
     inp = wl.make_inputs(w, seed)
     ac = make_aircache(w, max_elite=max_elite)
     q, k, v = to_torch(inp)
@@ -43,7 +46,12 @@ def _decode_case(w, seed, max_elite=0, layers=None):
         qd = [torch.from_numpy(a).cuda() for a in qd32]
     print(f"[decode] {w.name} seed {seed} L={w.L} B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} Nv={w.Nv} Nt={w.Nt}",
           flush=True)
-    o = ac.decode(qd, plan, ko, vo)
+    if int8:
+        kq, vq, ks, vs = ac.quantize_i8(plan, ko, vo)
+        o = ac.decode_i8(qd, plan, kq, vq, ks, vs)
+        ks_h, vs_h = ks.cpu().numpy(), vs.cpu().numpy()
+    else:
+        o = ac.decode(qd, plan, ko, vo)
     torch.cuda.synchronize()
     assert int(plan.status.item()) == 0
     budget = plan.budget.cpu().numpy()
@@ -60,7 +68,16 @@ def _decode_case(w, seed, max_elite=0, layers=None):
 
     def check(l):
         n = int(out_off[l, w.B])
-        ref = oracle.decode_attention(w, host(ko[l], n), host(vo[l], n), out_off[l], budget[l], qd_host[l])
+        if int8:
+            kc, vc = kq[l][:n].cpu().numpy(), vq[l][:n].cpu().numpy()
+            ref = np.zeros((w.B, w.Hq, w.D))
+            for b in range(w.B):
+                rows = int(budget[l, b]) + w.Nt
+                off, size = int(out_off[l, b]), w.Hkv * rows * w.D
+                ref[b] = oracle.decode_attention_i8_segment(w, kc[off:off + size], vc[off:off + size], ks_h[l, b],
+                                                            vs_h[l, b], rows, qd_host[l][b])
+        else:
+            ref = oracle.decode_attention(w, host(ko[l], n), host(vo[l], n), out_off[l], budget[l], qd_host[l])
         got = o[l].cpu().numpy().astype(np.float64)
         scale = np.abs(ref).max(axis=-1, keepdims=True)
         err = np.abs(got - ref)
@@ -102,6 +119,18 @@ def test_decode_edge_shapes(shape, ratio):
     _decode_case(wl.custom(ratio=ratio, **shape), 4)
 
 
+@pytest.mark.parametrize("cid", [1, 3, 5])
+def test_decode_int8_workload(cid):
+    """Decode over the int8 cache, full size, every layer."""
+    _decode_case(wl.CONFIGS[cid], wl.parity_seeds(cid)[0], int8=True)
+
+
+@pytest.mark.parametrize("shape", EDGE[:4], ids=lambda s: "x".join(f"{k}{v}" for k, v in s.items()))
+@pytest.mark.parametrize("ratio", [0.0, 0.3])
+def test_decode_int8_edge_shapes(shape, ratio):
+    _decode_case(wl.custom(ratio=ratio, **shape), 5, int8=True)
+
+
 def test_decode_out_of_range_plan_gives_nan_not_a_fault():
     """A plan whose budget or offset lies outside the buffers (not one this
     library wrote) makes the kernels' own range checks give NaN rows."""
@@ -139,3 +168,13 @@ def test_bound_decode_matches_plain_call():
     torch.cuda.synchronize()
     for l in range(w.L):
         assert torch.equal(a[l], b[l])
+    # the int8 cache: the bound call equals the plain aircache_decode_i8 call
+    kq, vq, ks, vs = ac.quantize_i8(plan, ko, vo)
+    a8 = ac.decode_i8(qd, plan, kq, vq, ks, vs)
+    o8 = [torch.full((w.B, w.Hq, w.D), float("nan"), device="cuda") for _ in range(w.L)]
+    bd8 = ac.bind_decode(qd, plan, kq, vq, o8, scales=(ks, vs))
+    bd8()
+    b8 = bd8()
+    torch.cuda.synchronize()
+    for l in range(w.L):
+        assert torch.equal(a8[l], b8[l])
