@@ -2016,14 +2016,14 @@ using namespace aircache;
 // ----------------------------------------------------------------------------
 
 size_t decode_ws_bytes(const Shape &s) {
-  const size_t units = (size_t)s.L * s.B * s.Hq * decode_splits(s.L, s.B, s.Hkv, kDecTargetCus);
+  const size_t units = (size_t)s.L * s.B * s.Hq * decode_splits(s.L, s.B, s.Hkv, kDecTargetCus, s.ratio, s.Nv, s.Nt);
   return align_up(units * sizeof(float2)) + align_up(units * (size_t)s.D * sizeof(float));
 }
 
 template <typename Tag, int D, bool Q8>
 int launch_decode(const Shape &s, const DecodeTables &tb, const aircache_plan_buf *plan, void *ws, hipStream_t st,
                   DecodeScales scl) {
-  const int smax = decode_splits(s.L, s.B, s.Hkv, kDecTargetCus);
+  const int smax = decode_splits(s.L, s.B, s.Hkv, kDecTargetCus, s.ratio, s.Nv, s.Nt);
   const size_t units = (size_t)s.L * s.B * s.Hq * smax;
   float2 *ml = static_cast<float2 *>(ws);
   float *acc = reinterpret_cast<float *>(static_cast<char *>(ws) + align_up(units * sizeof(float2)));

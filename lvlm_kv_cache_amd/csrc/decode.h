@@ -48,11 +48,19 @@ struct DecodeTables {
   LayerTableOut o;
 };
 
-// Splits per (l, b, g): enough workgroups for two per CU, whatever the
-// budgets (rows split evenly, each split's rows in chunks of kDecRows).
-__host__ __device__ inline int decode_splits(int L, int B, int Hkv, int cus) {
+// Splits per (l, b, g): enough workgroups for two per CU (four when the
+// units alone outnumber the CUs: the long segments then end in a shorter
+// tail), but no more than leave half a chunk (kDecRows / 2 rows) per split at
+// the expected row count ratio * N_v + N_t (a split's fixed latency outweighs
+// a few rows, and the merge reads every split); rows are split evenly, each
+// split's rows in chunks of kDecRows. (Measured on the five workloads.)
+__host__ __device__ inline int decode_splits(int L, int B, int Hkv, int cus, double ratio, int Nv, int Nt) {
   const long long units = (long long)L * B * Hkv;
-  const long long s = (2LL * cus + units - 1) / units;
+  const long long per_cu = units >= cus ? 4 : 2;
+  long long s = (per_cu * cus + units - 1) / units;
+  const long long rows = (long long)(ratio * (double)Nv) + Nt;
+  const long long by_rows = (rows + kDecRows / 2 - 1) / (kDecRows / 2);
+  if (s > by_rows) s = by_rows;
   return (int)(s < 1 ? 1 : (s > 64 ? 64 : s));
 }
 
