@@ -2055,6 +2055,7 @@ struct PrefillCfg {
   int nqt_vis, nqt_txt;
   long long grid;
   size_t lds;
+  int nqb;           // 16-row query blocks per wave (1 or 2)
   int evs;           // row stride of the exponentials: N_v rounded up to the key tile
   size_t fin_lds;    // prefill_finalize_kernel's row weights or I_v
   size_t stats_slot, e_slot;  // float2 / float elements of one workspace slot
@@ -2076,8 +2077,17 @@ int make_prefill_config(const aircache_desc *d, PrefillCfg *pc) {
   s.nstat = s.ntiles + 1;
   s.qrows = s.S;
   s.qoff = s.Nv;
-  pc->nqt_vis = (s.Nv + kPfRows - 1) / kPfRows;
-  pc->nqt_txt = (s.Nt + kPfRows - 1) / kPfRows;
+  // 128 query rows per workgroup, or 64 when 128 would leave CUs without a
+  // workgroup (measured: 64 rows cost more per key tile than they gain in
+  // balance once every CU has one; workload 2: 735 -> 692 us, workload 3:
+  // 2654 -> 3699 us had it taken 64)
+  {
+    const long long wg128 = (long long)s.B * s.Hq * ((s.Nv + kPfRows - 1) / kPfRows + (s.Nt + kPfRows - 1) / kPfRows);
+    pc->nqb = wg128 < kTargetCus ? 1 : 2;
+  }
+  const int rw = 16 * pc->nqb * kPfWaves;
+  pc->nqt_vis = (s.Nv + rw - 1) / rw;
+  pc->nqt_txt = (s.Nt + rw - 1) / rw;
   pc->grid = (long long)s.B * s.Hq * (pc->nqt_vis + pc->nqt_txt);
   if (pc->grid > INT32_MAX) return fail(AIRCACHE_EINVAL, "prefill grid of %lld workgroups too large", pc->grid);
   pc->lds = s.D == 128 ? (size_t)PfLayout<128>::kBytes : (size_t)PfLayout<64>::kBytes;
@@ -2112,7 +2122,7 @@ int check_prefill_io(const PrefillCfg &pc, const void *q, const void *k, const v
   return AIRCACHE_OK;
 }
 
-template <int D>
+template <int D, int NQB>
 int launch_prefill(const PrefillCfg &pc, int layer, const void *q, const void *k, const void *v, void *o,
                    const aircache_plan_buf *plan, void *ws_base, hipStream_t st) {
   Config cfg = pc.cfg;
@@ -2137,8 +2147,8 @@ int launch_prefill(const PrefillCfg &pc, int layer, const void *q, const void *k
     a.fin_stats = nullptr;
     a.plan = PlanPtrs{};
     a.ws = Ws{};
-    if ((rc = allow_lds(prefill_kernel<D, false>, pc.lds))) return rc;
-    hipLaunchKernelGGL((prefill_kernel<D, false>), dim3((unsigned)pc.grid), dim3(kPfThreads), pc.lds, st, s, a);
+    if ((rc = allow_lds(prefill_kernel<D, false, NQB>, pc.lds))) return rc;
+    hipLaunchKernelGGL((prefill_kernel<D, false, NQB>), dim3((unsigned)pc.grid), dim3(kPfThreads), pc.lds, st, s, a);
     return check_hip(hipGetLastError(), "prefill_kernel launch");
   }
   s.lb0 = layer * s.B;
@@ -2163,13 +2173,13 @@ int launch_prefill(const PrefillCfg &pc, int layer, const void *q, const void *k
   const long long nfin = (long long)s.B * s.Hkv * s.ntiles;  // finalize workgroups of one layer
   const long long grid = pc.grid + (layer > 0 ? nfin : 0);
   if (grid > INT32_MAX) return fail(AIRCACHE_EINVAL, "prefill grid of %lld workgroups too large", grid);
-  if ((rc = allow_lds(prefill_kernel<D, true>, pc.lds))) return rc;
+  if ((rc = allow_lds(prefill_kernel<D, true, NQB>, pc.lds))) return rc;
   if ((rc = allow_lds(prefill_finalize_kernel, pc.fin_lds))) return rc;
   if ((rc = allow_lds(elite_select_kernel<Bf16Tag, D>, cfg.elite_lds))) return rc;
   hipLaunchKernelGGL((elite_select_kernel<Bf16Tag, D>), dim3((unsigned)(s.B * s.Hkv)), dim3(kEliteThreads),
                      cfg.elite_lds, st, s, qt, kt, pp, ws);
   if ((rc = check_hip(hipGetLastError(), "elite_select_kernel launch"))) return rc;
-  hipLaunchKernelGGL((prefill_kernel<D, true>), dim3((unsigned)grid), dim3(kPfThreads), pc.lds, st, s, a);
+  hipLaunchKernelGGL((prefill_kernel<D, true, NQB>), dim3((unsigned)grid), dim3(kPfThreads), pc.lds, st, s, a);
   if ((rc = check_hip(hipGetLastError(), "prefill_kernel launch"))) return rc;
   if (layer == s.L - 1) {
     // the last layer's finalize, then the selection of every layer
@@ -2440,8 +2450,11 @@ int aircache_prefill_layer(const aircache_desc *desc, int32_t layer, const void 
     return fail(AIRCACHE_EWORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, pc.cfg.ws_bytes);
   if (!aligned16(workspace)) return fail(AIRCACHE_EINVAL, "workspace is not 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (pc.cfg.sh.D == 128) return launch_prefill<128>(pc, layer, q, k, v, o, plan, workspace, st);
-  return launch_prefill<64>(pc, layer, q, k, v, o, plan, workspace, st);
+  if (pc.cfg.sh.D == 128)
+    return pc.nqb == 1 ? launch_prefill<128, 1>(pc, layer, q, k, v, o, plan, workspace, st)
+                       : launch_prefill<128, 2>(pc, layer, q, k, v, o, plan, workspace, st);
+  return pc.nqb == 1 ? launch_prefill<64, 1>(pc, layer, q, k, v, o, plan, workspace, st)
+                     : launch_prefill<64, 2>(pc, layer, q, k, v, o, plan, workspace, st);
 }
 
 int aircache_prefill_attention(const aircache_desc *desc, const void *q, const void *k, const void *v, void *o,
@@ -2451,8 +2464,11 @@ int aircache_prefill_attention(const aircache_desc *desc, const void *q, const v
   if ((rc = make_prefill_config(desc, &pc))) return rc;
   if ((rc = check_prefill_io(pc, q, k, v, o))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (pc.cfg.sh.D == 128) return launch_prefill<128>(pc, 0, q, k, v, o, nullptr, nullptr, st);
-  return launch_prefill<64>(pc, 0, q, k, v, o, nullptr, nullptr, st);
+  if (pc.cfg.sh.D == 128)
+    return pc.nqb == 1 ? launch_prefill<128, 1>(pc, 0, q, k, v, o, nullptr, nullptr, st)
+                       : launch_prefill<128, 2>(pc, 0, q, k, v, o, nullptr, nullptr, st);
+  return pc.nqb == 1 ? launch_prefill<64, 1>(pc, 0, q, k, v, o, nullptr, nullptr, st)
+                     : launch_prefill<64, 2>(pc, 0, q, k, v, o, nullptr, nullptr, st);
 }
 
 const char *aircache_strerror(int status) {

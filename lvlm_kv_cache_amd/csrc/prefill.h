@@ -36,7 +36,7 @@
 
 constexpr int kPfThreads = 256;
 constexpr int kPfWaves = kPfThreads / 64;
-constexpr int kPfRows = 32 * kPfWaves;  // query rows per workgroup
+constexpr int kPfRows = 32 * kPfWaves;  // query rows per workgroup at most (two 16-row blocks per wave)
 constexpr int kPfKeys = 64;             // keys per tile
 constexpr int kPfVtPad = 8;             // bf16 of padding per transposed V row (bank spread)
 
@@ -169,9 +169,11 @@ __global__ __launch_bounds__(kPfFinThreads) void prefill_finalize_kernel(Shape s
   prefill_finalize_wg(sh, plan, ws, e, stats, evs, blockIdx.x, fin_wts);
 }
 
-template <int D, bool SCORE>
+template <int D, bool SCORE, int NQB>
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, PrefillArgs a) {
   using Lay = PfLayout<D>;
+  constexpr int RPW = 16 * NQB;          // query rows per wave: NQB 16-row MFMA blocks
+  constexpr int RW = RPW * kPfWaves;     // query rows per workgroup
   constexpr int NC = D / 32;  // 32-wide slices of the head dimension
   constexpr int ND = D / 16;  // 16-row blocks of O^T
   extern __shared__ __align__(16) unsigned char pf_lds[];
@@ -202,8 +204,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
   const int b = bh / sh.Hq, h = bh - b * sh.Hq, g = h / sh.G, hl = h - g * sh.G;
   const bool text = rank < a.nqt_txt;
   const int qt = text ? a.nqt_txt - 1 - rank : a.nqt_vis - 1 - (rank - a.nqt_txt);
-  const int row0 = text ? Nv + qt * kPfRows : qt * kPfRows;
-  const int row1 = text ? min(S, row0 + kPfRows) : min(Nv, row0 + kPfRows);
+  const int row0 = text ? Nv + qt * RW : qt * RW;
+  const int row1 = text ? min(S, row0 + RW) : min(Nv, row0 + RW);
   const int nkt = (row1 + kPfKeys - 1) / kPfKeys;
 
   const uint16_t *qh = a.q + (size_t)(b * sh.Hq + h) * S * D;
@@ -211,10 +213,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
   const uint16_t *vh = a.v + (size_t)(b * sh.Hkv + g) * S * D;
 
   // The wave's query fragments (rows beyond the tile are zero).
-  Frag<Bf16Tag> qf[2][NC];
+  Frag<Bf16Tag> qf[NQB][NC];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = row0 + 32 * wave + 16 * qb + n;
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int row = row0 + RPW * wave + 16 * qb + n;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (row < row1) qf[qb][c].load(qh + (size_t)row * D + 32 * c + 8 * grp);
@@ -229,36 +231,42 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
   if (score) {
     ntk = a.n_elite[b];
     ntk = ntk < 0 ? 0 : (ntk > sh.cap ? sh.cap : ntk);
-    for (int i = tid; i < kPfRows; i += kPfThreads) emap[i] = -1;
+    for (int i = tid; i < RW; i += kPfThreads) emap[i] = -1;
     __syncthreads();
     const int jt0 = row0 - Nv;
     for (int e = tid; e < ntk; e += kPfThreads) {
       const int jt = a.elite[(size_t)b * sh.Nt + e] - jt0;
-      if (jt >= 0 && jt < kPfRows) emap[jt] = e;
+      if (jt >= 0 && jt < RW) emap[jt] = e;
     }
     __syncthreads();
   }
-  int erow[2] = {-1, -1};  // elite row r = hl * ntk + eidx of the lane's queries, or -1
+  int erow[NQB];  // elite row r = hl * ntk + eidx of the lane's queries, or -1
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) erow[qb] = -1;
   if (score) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int rr = 32 * wave + 16 * qb + n;
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int rr = RPW * wave + 16 * qb + n;
       const int e = (row0 + rr < row1) ? emap[rr] : -1;
       erow[qb] = e >= 0 ? hl * ntk + e : -1;
     }
   }
   float2 *st_base = a.stats + (size_t)(lbl * sh.Hkv + g) * sh.rcap16 * sh.nstat;
-  float *e_row[2];  // the lane's elite rows of the exponentials
+  float *e_row[NQB];  // the lane's elite rows of the exponentials
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < NQB; ++qb)
     e_row[qb] = a.e + ((size_t)(lbl * sh.Hkv + g) * sh.rcap16 + (erow[qb] >= 0 ? erow[qb] : 0)) * a.evs;
 
   // The elite text keys' (max, sum) for the elite rows: the columns the
   // scores add to the visual keys, with no causal mask. Merged with the
   // visual keys' running pair after the last visual tile.
-  float xm[2] = {-INFINITY, -INFINITY}, xz[2] = {0.f, 0.f};
+  float xm[NQB], xz[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) xm[qb] = -INFINITY, xz[qb] = 0.f;
   if (score) {
-    float mx[2] = {-INFINITY, -INFINITY}, zx[2] = {0.f, 0.f};
+    float mx[NQB], zx[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) mx[qb] = -INFINITY, zx[qb] = 0.f;
     for (int x0 = 0; x0 < ntk; x0 += 16) {
       const int x = x0 + n;
       Frag<Bf16Tag> kx[NC];
@@ -266,7 +274,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
 #pragma unroll
       for (int c = 0; c < NC; ++c) kx[c].load(kh + (size_t)(Nv + jt) * D + 32 * c + 8 * grp);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < NQB; ++qb) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NC; ++c) mfma_slice(acc, kx[c], qf[qb][c]);
@@ -282,7 +290,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
       }
     }
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
       xm[qb] = max_across_rows(mx[qb]);
       xz[qb] = sum_across_rows(mx[qb] > -INFINITY ? zx[qb] * exp2f(mx[qb] - xm[qb]) : 0.f);
     }
@@ -322,16 +330,21 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
     }
   };
 
-  f32x4_t oacc[ND][2];
+  f32x4_t oacc[ND][NQB];
 #pragma unroll
   for (int d = 0; d < ND; ++d)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) oacc[d][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
-  float zrun[2] = {0.f, 0.f};  // the lane's part of the scores' running sum over visual keys (reference as lrun)
-  int qrow[2];
+    for (int qb = 0; qb < NQB; ++qb) oacc[d][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mrun[NQB], lrun[NQB];
+  float zrun[NQB];  // the lane's part of the scores' running sum over visual keys (reference as lrun)
+  int qrow[NQB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) qrow[qb] = row0 + 32 * wave + 16 * qb + n;
+  for (int qb = 0; qb < NQB; ++qb) {
+    qrow[qb] = row0 + RPW * wave + 16 * qb + n;
+    mrun[qb] = -INFINITY;
+    lrun[qb] = 0.f;
+    zrun[qb] = 0.f;
+  }
 
   // prologue: tile 0 into buffer 0
   load_v(0);
@@ -351,25 +364,25 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
     const int key0 = kt * kPfKeys;
 
     // S^T = K Q^T: four key blocks, two query blocks
-    f32x4_t s[4][2];
+    f32x4_t s[4][NQB];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      s[kb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      s[kb][1] = s[kb][0];
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         Frag<Bf16Tag> kf;
         LdsTile<Bf16Tag>::read(kf, cur + kb * Lay::kBlock, c, lane);
-        mfma_slice(s[kb][0], kf, qf[0][c]);
-        mfma_slice(s[kb][1], kf, qf[1][c]);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) mfma_slice(s[kb][qb], kf, qf[qb][c]);
       }
     }
 
     // causal mask (only tiles that reach past the wave's first row), online softmax
-    const bool diag = key0 + kPfKeys - 1 > row0 + 32 * wave;
+    const bool diag = key0 + kPfKeys - 1 > row0 + RPW * wave;
     if (diag) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -377,7 +390,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
             if (key0 + pf_key(kb, 4 * grp + i) > qrow[qb]) s[kb][qb][i] = -INFINITY;
     }
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQB; ++qb) {
       // the scale 1/sqrt(D) (base 2) is applied after the maximum and inside
       // the exponent; exp2 of -inf (masked keys) is 0
       float mx = -INFINITY;
@@ -441,9 +454,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
     // O^T += V^T P^T
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
-      Frag<Bf16Tag> pf[2];
+      Frag<Bf16Tag> pf[NQB];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < NQB; ++qb) {
         u32x4_t w;
         w[0] = pack_bf16(s[2 * sl][qb][0], s[2 * sl][qb][1]);
         w[1] = pack_bf16(s[2 * sl][qb][2], s[2 * sl][qb][3]);
@@ -456,8 +469,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
       for (int d = 0; d < ND; ++d) {
         Frag<Bf16Tag> vf;
         vf.v = *reinterpret_cast<const u16x8_t *>(vt + (size_t)(16 * d + n) * Lay::kVtRow);
-        mfma_slice(oacc[d][0], vf, pf[0]);
-        mfma_slice(oacc[d][1], vf, pf[1]);
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) mfma_slice(oacc[d][qb], vf, pf[qb]);
       }
     }
 
@@ -473,7 +486,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
   // its query row per 16-row block of O^T.
   uint16_t *oh = a.o + (size_t)(b * sh.Hq + h) * S * D;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
     const float inv = 1.f / sum_across_rows(lrun[qb]);
     if (qrow[qb] < row1) {
 #pragma unroll

@@ -97,6 +97,24 @@ def test_prefill_rerun_is_bit_identical():
         assert np.array_equal(g1["k_out"][l], g2["k_out"][l])
 
 
+def test_prefill_large_grid_two_blocks_per_wave():
+    """A grid of at least one 128-row workgroup per CU takes 128 query rows per
+    workgroup (two 16-row blocks per wave; smaller grids, as the other small
+    cases here, take 64): o on sampled rows and every plan output against the
+    oracle."""
+    w = wl.custom(L=2, B=4, Hq=32, Hkv=8, D=128, Nv=1000, Nt=70, dtype="bf16", ratio=0.15)
+    inp = wl.make_inputs(w, 6)
+    ac = make_aircache(w)
+    qa, o, gpu = _run_prefill(w, inp, ac)
+    rng = np.random.default_rng(6)
+    for l in range(w.L):
+        _check_o(w, inp, qa[l], o[l], l, {b: _rows_sample(w, rng) for b in range(w.B)})
+    compare(inp, gpu, reference(inp, gpu))
+    _, o2, _ = _run_prefill(w, inp, ac, with_plan=False)
+    for l in range(w.L):
+        assert np.array_equal(o[l], o2[l])
+
+
 def _rows_sample(w, rng):
     """Rows of a full-size check: the first, the last visual, the first text
     and the last position, plus a few random ones, in runs of 2."""
