@@ -379,8 +379,11 @@ int aircache_decode_i8(const aircache_desc *desc, const void *const *q_dec, cons
  *                 be used; iv_head with AIRCACHE_SELECT_PER_KV_HEAD)
  *   workspace   : device scratch of ws_bytes >=
  *                 aircache_prefill_workspace_size(desc), kept by the caller
- *                 across the layer calls of one pass (one layer's scoring
- *                 terms plus the pass's counters; no zeroing needed)
+ *                 across the layer calls of one pass (two layers' scoring
+ *                 terms, sized for max_elite elite rows per (layer, sample),
+ *                 plus the pass's counters; no zeroing needed). With
+ *                 max_elite = 0 the cap is n_txt, which for long text makes
+ *                 this large (batch 8, n_txt 1024, n_vis 3072: 5.6 GB)
  * bfloat16 only (AIRCACHE_EINVAL for float32); head_dim 64 or 128; all
  * pointers 16-byte aligned. The descriptor's path is ignored; max_elite caps
  * the elite rows that are scored per (layer, sample) as on the other paths
