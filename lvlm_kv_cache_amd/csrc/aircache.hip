@@ -1132,7 +1132,7 @@ __global__ __launch_bounds__(256) void kv_gather_kernel(Shape sh, GatherTables t
   if (bud < 0 || bud > sh.Nv) return;  // not a budget written by aircache_plan
   const int nrows = bud + sh.Nt;
   const int64_t seg0 = plan.out_off[(size_t)l * (sh.B + 1) + b];
-  if (seg0 < 0 || seg0 + (int64_t)sh.Hkv * nrows * sh.D > cap_elems) return;
+  if (seg0 < 0 || seg0 > cap_elems - (int64_t)sh.Hkv * nrows * sh.D) return;  // (no wrap for stray offsets)
   const int rpc = (nrows + nch - 1) / nch;
   const int r0 = ch * rpc, r1 = min(nrows, r0 + rpc);
   const size_t src_base = (size_t)(b * sh.Hkv + g) * sh.S * RB;
@@ -1207,7 +1207,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_i8_kernel(Shape sh, Qu
   if (bud < 0 || bud > sh.Nv) return;  // not a budget written by aircache_plan
   const int n = bud + sh.Nt;
   const int64_t seg0 = plan.out_off[(size_t)l * (sh.B + 1) + b];
-  if (seg0 < 0 || seg0 + (int64_t)sh.Hkv * n * sh.D > cap_elems) return;
+  if (seg0 < 0 || seg0 > cap_elems - (int64_t)sh.Hkv * n * sh.D) return;  // (no wrap for stray offsets)
   const size_t base = (size_t)seg0 + (size_t)g * n * sh.D;
   const int cnt16 = n * sh.D / 16;  // at least 4 (D >= 64, n >= 1)
   const E *src = static_cast<const E *>(kv ? tb.vo.p[l] : tb.ko.p[l]) + base;

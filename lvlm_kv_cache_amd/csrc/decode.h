@@ -135,7 +135,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(Shape sh, D
   const int lb = l * B + b;
   const int r = budget[lb];
   const int64_t off = out_off[(size_t)l * (B + 1) + b];
-  const bool ok = r >= 0 && r <= sh.Nv && off >= 0 && off + (int64_t)Hkv * (r + sh.Nt) * D <= cap_elems;
+  // (compared as off <= cap - size: a stray offset near the top of int64 cannot wrap)
+  const bool ok = r >= 0 && r <= sh.Nv && off >= 0 && off <= cap_elems - (int64_t)Hkv * (r + sh.Nt) * D;
   const int n = ok ? r + sh.Nt : 0;
   // this split's rows [lo, hi), an even share of the n rows
   const int lo = (int)((long long)n * s / S), hi = (int)((long long)n * (s + 1) / S);
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(Shape sh, DecodeTable
   const int B = sh.B, b = lb0 % B, l = lb0 / B, lb = l * B + b;
   const int r = budget[lb];
   const int64_t off = out_off[(size_t)l * (B + 1) + b];
-  const bool ok = r >= 0 && r <= sh.Nv && off >= 0 && off + (int64_t)sh.Hkv * (r + sh.Nt) * D <= cap_elems;
+  const bool ok = r >= 0 && r <= sh.Nv && off >= 0 && off <= cap_elems - (int64_t)sh.Hkv * (r + sh.Nt) * D;
   const int ns = ok ? S : 0;
   const size_t base = ((size_t)lb * sh.Hq + h) * S;
   float M = -INFINITY;

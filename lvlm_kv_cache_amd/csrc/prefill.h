@@ -178,22 +178,18 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(Shape sh, Prefil
   constexpr int ND = D / 16;  // 16-row blocks of O^T
   extern __shared__ __align__(16) unsigned char pf_lds[];
   __shared__ int emap[kPfRows];  // elite index of each text row of the tile, or -1
-  // Block order: the text tiles (the longest workgroups), then the previous
-  // layer's finalize workgroups (they run beside the text tiles), then the
-  // visual tiles from the longest.
-  const int ntxt = sh.B * sh.Hq * a.nqt_txt;
-  int blk = (int)blockIdx.x;
-  if (SCORE && blk >= ntxt) {
-    const int nfin = (int)gridDim.x - a.nattn;
-    if (blk < ntxt + nfin) {
-      // the previous layer's I_v and statistics, from the other workspace slot
-      Shape fs = sh;
-      fs.lb0 = sh.lb0 - sh.B;
-      prefill_finalize_wg(fs, a.plan, a.ws, a.fin_e, a.fin_stats, a.evs, blk - ntxt,
-                          reinterpret_cast<float *>(pf_lds));
-      return;
-    }
-    blk -= nfin;
+  // Block order: the attention (text tiles, then visual tiles from the
+  // longest), then the previous layer's finalize workgroups, which take the
+  // slots the shortest tiles leave (measured: 4% less for the fused layer
+  // calls on workload 3 than placing them beside the text tiles).
+  const int blk = (int)blockIdx.x;
+  if (SCORE && blk >= a.nattn) {
+    // the previous layer's I_v and statistics, from the other workspace slot
+    Shape fs = sh;
+    fs.lb0 = sh.lb0 - sh.B;
+    prefill_finalize_wg(fs, a.plan, a.ws, a.fin_e, a.fin_stats, a.evs, blk - a.nattn,
+                        reinterpret_cast<float *>(pf_lds));
+    return;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, grp = lane >> 4;
