@@ -144,11 +144,18 @@ def test_decode_out_of_range_plan_gives_nan_not_a_fault():
     torch.cuda.synchronize()
     plan.budget[0, 1] = w.Nv + 5          # budget out of range
     plan.out_off[1, 0] = 1 << 40           # offset past the buffer
+    plan.out_off[1, 1] = (1 << 63) - 64    # near the top of int64: offset + size would wrap
     qd = [torch.randn(w.B, w.Hq, w.D, device="cuda").to(torch.bfloat16) for _ in range(w.L)]
     o = ac.decode(qd, plan, ko, vo)
     torch.cuda.synchronize()
-    assert torch.isnan(o[0][1]).all() and torch.isnan(o[1][0]).all()
-    assert torch.isfinite(o[0][0]).all() and torch.isfinite(o[1][1]).all()
+    assert torch.isnan(o[0][1]).all() and torch.isnan(o[1][0]).all() and torch.isnan(o[1][1]).all()
+    assert torch.isfinite(o[0][0]).all()
+    # the int8 cache, its quantisation and the compaction skip the same segments
+    kq, vq, ks, vs = ac.quantize_i8(plan, ko, vo)
+    o8 = ac.decode_i8(qd, plan, kq, vq, ks, vs)
+    ac.compress(plan, k, v, ko, vo)
+    torch.cuda.synchronize()
+    assert torch.isnan(o8[1][1]).all() and torch.isfinite(o8[0][0]).all()
 
 
 def test_bound_decode_matches_plain_call():
