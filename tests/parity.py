@@ -279,13 +279,21 @@ def check_prefill_o(w, inp, qa, o, l, rows_by_b):
     return worst
 
 
-def run_gpu_prefill(w, inp, ac, with_plan=True):
+def run_gpu_prefill(w, inp, ac, with_plan=True, keep_layers=None):
     """Every layer through aircache_prefill_layer (or the plain attention),
-    then aircache_compress; returns (o per layer on the host, gpu dict)."""
+    then aircache_compress; returns (queries per layer, o per layer on the
+    host, gpu dict). keep_layers: only those layers' queries and outputs come
+    back to the host (the others are None), for sizes whose every-position
+    queries do not fit the host comfortably."""
     L = w.L
-    qa = [wl.prefill_queries(inp, l) for l in range(L)]
+    keep = set(range(L)) if keep_layers is None else set(keep_layers)
+    qa, q = [], []
+    for l in range(L):
+        a = wl.prefill_queries(inp, l)
+        q.append(_dev(a))
+        qa.append(a if l in keep else None)
+        del a
     _, k, v = to_torch(inp)
-    q = [_dev(a) for a in qa]
     o = [torch.empty_like(t) for t in q]
     out = {}
     if with_plan:
@@ -306,4 +314,4 @@ def run_gpu_prefill(w, inp, ac, with_plan=True):
         for l in range(L):
             ac.prefill_attention(q[l], k[l], v[l], o[l])
         torch.cuda.synchronize()
-    return qa, [_host(t) for t in o], out
+    return qa, [_host(t) if l in keep else None for l, t in enumerate(o)], out

@@ -138,3 +138,21 @@ def test_prefill_full_size(cid):
         _check_o(w, inp, qa[l], o[l], l, {b: _rows_sample(w, rng) for b in range(w.B)})
     ref = reference(inp, gpu)
     compare(inp, gpu, ref)
+
+
+@pytest.mark.parametrize("cid", [4, 5])
+def test_prefill_full_size_large(cid):
+    """Workloads 4 (gqa_video_32x196) and 5 (gqa_multi_image_3x1024) at full
+    size, elite cap 64: every plan output and the compacted cache against the
+    oracle, o on sampled rows of every query head of three layers (only those
+    layers' queries and outputs are kept on the host)."""
+    w = wl.CONFIGS[cid]
+    inp = wl.make_inputs(w, cid)
+    ac = make_aircache(w, max_elite=64)
+    layers = (0, w.L // 2, w.L - 1)
+    qa, o, gpu = _run_prefill(w, inp, ac, keep_layers=layers)
+    assert np.all(gpu["status"] == 0)
+    rng = np.random.default_rng(cid)
+    for l in layers:
+        _check_o(w, inp, qa[l], o[l], l, {b: _rows_sample(w, rng) for b in (0, w.B - 1)})
+    compare(inp, gpu, reference(inp, gpu))
