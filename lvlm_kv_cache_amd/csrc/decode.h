@@ -107,12 +107,19 @@ struct DecodeScales {
   const float *k, *v;
 };
 
+// Waves per SIMD the decode kernel is compiled for: eight (64 registers, four
+// workgroups per CU) for bfloat16 queries; float32 queries need more registers
+// than that without spilling (measured on workload 5: the int8 cache 153 ->
+// 145 us, the bfloat16 cache within the run-to-run spread of a few us;
+// workloads 3 and 4 unchanged).
+template <typename Tag> constexpr int decode_waves() { return Tag::kBytes == 2 ? 8 : 1; }
+
 // Q8: the compacted cache is int8 codes with one scale per (layer, sample, KV
 // head) for K and for V (value = code * scale): logits are the codes' dot
 // products times the K scale, the weighted sum of V codes is times the V
 // scale, both applied once per row and per output.
 template <typename Tag, int D, bool Q8>
-__global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(Shape sh, DecodeTables tb,
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(decode_waves<Tag>()))) void decode_partial_kernel(Shape sh, DecodeTables tb,
                                                                      const int32_t *budget, const int64_t *out_off,
                                                                      int64_t cap_elems, int S, float2 *part_ml,
                                                                      float *part_acc, DecodeScales scl) {

@@ -97,12 +97,13 @@ def test_prefill_rerun_is_bit_identical():
         assert np.array_equal(g1["k_out"][l], g2["k_out"][l])
 
 
-def test_prefill_large_grid_two_blocks_per_wave():
+@pytest.mark.parametrize("D", [128, 64])
+def test_prefill_large_grid_two_blocks_per_wave(D):
     """A grid of at least one 128-row workgroup per CU takes 128 query rows per
     workgroup (two 16-row blocks per wave; smaller grids, as the other small
-    cases here, take 64): o on sampled rows and every plan output against the
-    oracle."""
-    w = wl.custom(L=2, B=4, Hq=32, Hkv=8, D=128, Nv=1000, Nt=70, dtype="bf16", ratio=0.15)
+    cases here, take 64), at both head dimensions: o on sampled rows and every
+    plan output against the oracle."""
+    w = wl.custom(L=2, B=4, Hq=32, Hkv=8, D=D, Nv=1000, Nt=70, dtype="bf16", ratio=0.15)
     inp = wl.make_inputs(w, 6)
     ac = make_aircache(w)
     qa, o, gpu = _run_prefill(w, inp, ac)
