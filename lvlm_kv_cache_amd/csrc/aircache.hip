@@ -2020,7 +2020,7 @@ size_t decode_ws_bytes(const Shape &s) {
   return align_up(units * sizeof(float2)) + align_up(units * (size_t)s.D * sizeof(float));
 }
 
-template <typename Tag, int D, bool Q8>
+template <typename Tag, int D, bool Q8, bool PV>
 int launch_decode(const Shape &s, const DecodeTables &tb, const aircache_plan_buf *plan, void *ws, hipStream_t st,
                   DecodeScales scl) {
   const int smax = decode_splits(s.L, s.B, s.Hkv, kDecTargetCus, s.ratio, s.Nv, s.Nt);
@@ -2028,12 +2028,12 @@ int launch_decode(const Shape &s, const DecodeTables &tb, const aircache_plan_bu
   float2 *ml = static_cast<float2 *>(ws);
   float *acc = reinterpret_cast<float *>(static_cast<char *>(ws) + align_up(units * sizeof(float2)));
   const int64_t cap = (int64_t)s.B * s.Hkv * (int64_t)s.S * s.D;
-  const size_t lds = (size_t)decode_lds_bytes(s.G, D, Q8 ? 1 : Tag::kBytes);
+  const size_t lds = PV ? (size_t)decode_pv_lds(s.G, D).total : (size_t)decode_lds_bytes(s.G, D, Q8 ? 1 : Tag::kBytes);
   const long long grid = (long long)s.L * s.B * s.Hkv * smax;
   if (grid > INT32_MAX) return fail(AIRCACHE_EINVAL, "decode grid of %lld workgroups too large", grid);
   int rc;
-  if ((rc = allow_lds(decode_partial_kernel<Tag, D, Q8>, lds))) return rc;
-  hipLaunchKernelGGL((decode_partial_kernel<Tag, D, Q8>), dim3((unsigned)grid), dim3(kDecThreads), lds, st, s, tb,
+  if ((rc = allow_lds(decode_partial_kernel<Tag, D, Q8, PV>, lds))) return rc;
+  hipLaunchKernelGGL((decode_partial_kernel<Tag, D, Q8, PV>), dim3((unsigned)grid), dim3(kDecThreads), lds, st, s, tb,
                      plan->budget, plan->out_off, cap, smax, ml, acc, scl);
   if ((rc = check_hip(hipGetLastError(), "decode_partial_kernel launch"))) return rc;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(s.L * s.B * s.Hq)), dim3(D), 0, st, s, tb,
@@ -2221,16 +2221,26 @@ int decode_common(const aircache_desc *desc, const void *const *q_dec, const air
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = desc->dtype == AIRCACHE_BF16;
   const DecodeScales scl{k_scale, v_scale};
+  // weights x V on the matrix cores for bfloat16 queries and kDecPvMinG <= G <= kDecPvMaxG
+  const bool pv = decode_pv(s.G, bf ? 2 : 4);
   if (q8) {
-    if (bf && s.D == 128) return launch_decode<Bf16Tag, 128, true>(s, tb, plan, workspace, st, scl);
-    if (bf) return launch_decode<Bf16Tag, 64, true>(s, tb, plan, workspace, st, scl);
-    if (s.D == 128) return launch_decode<F32Tag, 128, true>(s, tb, plan, workspace, st, scl);
-    return launch_decode<F32Tag, 64, true>(s, tb, plan, workspace, st, scl);
+    if (bf && s.D == 128)
+      return pv ? launch_decode<Bf16Tag, 128, true, true>(s, tb, plan, workspace, st, scl)
+                : launch_decode<Bf16Tag, 128, true, false>(s, tb, plan, workspace, st, scl);
+    if (bf)
+      return pv ? launch_decode<Bf16Tag, 64, true, true>(s, tb, plan, workspace, st, scl)
+                : launch_decode<Bf16Tag, 64, true, false>(s, tb, plan, workspace, st, scl);
+    if (s.D == 128) return launch_decode<F32Tag, 128, true, false>(s, tb, plan, workspace, st, scl);
+    return launch_decode<F32Tag, 64, true, false>(s, tb, plan, workspace, st, scl);
   }
-  if (bf && s.D == 128) return launch_decode<Bf16Tag, 128, false>(s, tb, plan, workspace, st, scl);
-  if (bf) return launch_decode<Bf16Tag, 64, false>(s, tb, plan, workspace, st, scl);
-  if (s.D == 128) return launch_decode<F32Tag, 128, false>(s, tb, plan, workspace, st, scl);
-  return launch_decode<F32Tag, 64, false>(s, tb, plan, workspace, st, scl);
+  if (bf && s.D == 128)
+    return pv ? launch_decode<Bf16Tag, 128, false, true>(s, tb, plan, workspace, st, scl)
+              : launch_decode<Bf16Tag, 128, false, false>(s, tb, plan, workspace, st, scl);
+  if (bf)
+    return pv ? launch_decode<Bf16Tag, 64, false, true>(s, tb, plan, workspace, st, scl)
+              : launch_decode<Bf16Tag, 64, false, false>(s, tb, plan, workspace, st, scl);
+  if (s.D == 128) return launch_decode<F32Tag, 128, false, false>(s, tb, plan, workspace, st, scl);
+  return launch_decode<F32Tag, 64, false, false>(s, tb, plan, workspace, st, scl);
 }
 
 extern "C" {

@@ -15,9 +15,10 @@
 // (every K and V row is read once from HBM), keeping per head a running
 // maximum, sum of exponentials and unnormalised output row (rescaled when the
 // maximum grows). decode_combine_kernel merges the splits of each (l, b, h)
-// in split order. The pass is a stream of K and V
-// rows (HBM-bound; the contraction per row is G x D multiply-adds), so the
-// arithmetic is plain fp32 on the vector units.
+// in split order. The pass is a stream of K and V rows (HBM-bound): the
+// logits are MFMA products of 16 key rows against 16 query heads, and the
+// weights x V product runs on the matrix cores for groups of 4 to 32 heads
+// (below) or in fp32 on the vector units.
 #pragma once
 
 constexpr int kDecThreads = 512;                  // 8 waves, 16 rows each
@@ -83,6 +84,49 @@ __host__ __device__ inline int decode_lds_bytes(int G, int D, int esize) {
   return main > red ? main : red;
 }
 
+// Weights x V on the matrix cores (bfloat16 queries, kDecPvMinG <= G <=
+// kDecPvMaxG): the
+// chunk's V rows go into LDS transposed (one row per output element d, the
+// chunk's rows contiguous, bfloat16; int8 codes converted exactly), so that
+// O^T = V^T P^T is a v_mfma_f32_16x16x32_bf16 product with V^T as the A
+// operand and the weights of 16 query heads as the B operand; wave w owns the
+// output elements 16 w .. 16 w + 15 of every head. A weight p in [0, 1]
+// enters as two bfloat16 terms, hi = rn(p) and lo = rn(p - hi), with
+// |p - hi - lo| <= 2^-18 p, so the products keep the float32 accuracy of the
+// vector-unit path (which float32 queries and larger groups take).
+constexpr int kDecPvMaxG = 32;
+constexpr int kDecVtStride = kDecRows * 2 + 8;  // bytes per transposed V row (8 B apart in banks, 8-byte aligned)
+constexpr int kDecZs = kDecRows + 4;            // floats per head row of the weights (bank spread of the B reads)
+
+// Dynamic LDS of the matrix-core variant (byte offsets): q of the G heads
+// [G][D] bfloat16, logits then weights [G][kDecZs] floats, per-head running
+// (max, sum, rescale) [G][4] floats, V^T [D][kDecVtStride bytes].
+struct DecPvLds {
+  int zp, run, vt, total;
+};
+__host__ __device__ inline DecPvLds decode_pv_lds(int G, int D) {
+  DecPvLds f;
+  f.zp = (G * D * 2 + 15) & ~15;
+  f.run = f.zp + ((G * kDecZs * 4 + 15) & ~15);
+  f.vt = f.run + ((G * 16 + 15) & ~15);
+  f.total = f.vt + D * kDecVtStride;
+  return f;
+}
+// (measured: G = 7, workloads 3 to 5, 17-18% less time for the bfloat16
+// cache and 10-14% for the int8 cache; G = 1, workload 2, 12% and 37% more,
+// since 15 of the 16 head columns of each product are idle)
+constexpr int kDecPvMinG = 4;
+__host__ __device__ inline bool decode_pv(int G, int qbytes) {
+  return qbytes == 2 && G >= kDecPvMinG && G <= kDecPvMaxG;
+}
+
+// Two floats to two bfloat16 (round to nearest even), packed low first.
+typedef __attribute__((ext_vector_type(2))) float dec_f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 dec_bf16x2_t;
+__device__ __forceinline__ unsigned dec_pack_bf16(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(dec_f32x2_t{a, b}, dec_bf16x2_t));
+}
+
 // Eight int8 codes (8 bytes) as an MFMA operand fragment of the query's type:
 // the integers in [-127, 127] are exact in bfloat16 and float32.
 __device__ __forceinline__ void codes_to_frag(const int8_t *p, Frag<Bf16Tag> &f) {
@@ -108,18 +152,20 @@ struct DecodeScales {
 };
 
 // Waves per SIMD the decode kernel is compiled for: eight (64 registers, four
-// workgroups per CU) for bfloat16 queries; float32 queries need more registers
-// than that without spilling (measured on workload 5: the int8 cache 153 ->
-// 145 us, the bfloat16 cache within the run-to-run spread of a few us;
-// workloads 3 and 4 unchanged).
-template <typename Tag> constexpr int decode_waves() { return Tag::kBytes == 2 ? 8 : 1; }
+// workgroups per CU) for bfloat16 queries on the vector-unit path (measured on
+// workload 5 against three workgroups per CU: the int8 cache 153 -> 145 us,
+// the bfloat16 cache within the run-to-run spread of a few us; workloads 3
+// and 4 unchanged); six (three workgroups per CU) on the matrix-core path,
+// whose V^T staging needs up to 80 registers without spilling; float32
+// queries need more registers than either.
+template <typename Tag, bool PV> constexpr int decode_waves() { return Tag::kBytes == 2 ? (PV ? 6 : 8) : 1; }
 
 // Q8: the compacted cache is int8 codes with one scale per (layer, sample, KV
 // head) for K and for V (value = code * scale): logits are the codes' dot
 // products times the K scale, the weighted sum of V codes is times the V
 // scale, both applied once per row and per output.
-template <typename Tag, int D, bool Q8>
-__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(decode_waves<Tag>()))) void decode_partial_kernel(Shape sh, DecodeTables tb,
+template <typename Tag, int D, bool Q8, bool PV>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(decode_waves<Tag, PV>()))) void decode_partial_kernel(Shape sh, DecodeTables tb,
                                                                      const int32_t *budget, const int64_t *out_off,
                                                                      int64_t cap_elems, int S, float2 *part_ml,
                                                                      float *part_acc, DecodeScales scl) {
@@ -147,10 +193,15 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(dec
   const int n = ok ? r + sh.Nt : 0;
   // this split's rows [lo, hi), an even share of the n rows
   const int lo = (int)((long long)n * s / S), hi = (int)((long long)n * (s + 1) / S);
-  QE *qs = reinterpret_cast<QE *>(dec_lds);          // [G][D] as stored (room for floats)
-  float *zp = dec_lds + G * D;                       // [G][kDecRows]
-  float *run = zp + G * kDecRows;                    // [G][4]: max, sum, rescale
-  E *vs = reinterpret_cast<E *>(run + G * 4);        // [kDecRows][D]
+  static_assert(!PV || Tag::kBytes == 2, "the matrix-core weights x V takes bfloat16 queries");
+  unsigned char *lds8 = reinterpret_cast<unsigned char *>(dec_lds);
+  const DecPvLds pl = decode_pv_lds(G, D);
+  const int zs = PV ? kDecZs : kDecRows;             // floats per head row of zp
+  QE *qs = reinterpret_cast<QE *>(dec_lds);          // [G][D] as stored (vector path: room for floats)
+  float *zp = PV ? reinterpret_cast<float *>(lds8 + pl.zp) : dec_lds + G * D;  // [G][zs]
+  float *run = PV ? reinterpret_cast<float *>(lds8 + pl.run) : zp + G * kDecRows;  // [G][4]: max, sum, rescale
+  E *vs = reinterpret_cast<E *>(run + G * 4);        // vector path: [kDecRows][D]
+  unsigned char *vt = lds8 + pl.vt;                  // matrix-core path: V^T [D][kDecVtStride bytes]
   const E *kseg = static_cast<const E *>(tb.k.p[l]) + (ok ? off + (int64_t)g * n * D : 0);
   const E *vseg = static_cast<const E *>(tb.v.p[l]) + (ok ? off + (int64_t)g * n * D : 0);
   const QE *qb = static_cast<const QE *>(tb.q.p[l]) + ((size_t)b * sh.Hq + (size_t)g * G) * D;
@@ -172,6 +223,10 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(dec
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  // matrix-core path: O^T rows 16 wave + 4 grp + i, head 16 hg + n16
+  f32x4_t oacc[kDecPvMaxG / 16];
+#pragma unroll
+  for (int hg = 0; hg < kDecPvMaxG / 16; ++hg) oacc[hg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
 
   for (int c0 = lo; c0 < hi; c0 += kDecRows) {
@@ -188,18 +243,54 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(dec
       const E *kp = kseg + (size_t)(c0 + (rv ? row : 0)) * D + grp * 8;
       const u32x4_t *vp = reinterpret_cast<const u32x4_t *>(vseg + (size_t)c0 * D);
       const int pieces = nr * D / kPiece;
-      u32x4_t vw[VP];
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) {
         if (!rv) kf[c].zero();
         else if constexpr (Q8) codes_to_frag(kp + c * 32, kf[c]);
         else kf[c].load(kp + c * 32);
       }
+      if constexpr (PV) {
+        // thread (kq, dq): rows 4 kq .. 4 kq + 3, elements 8 dq .. 8 dq + 7
+        // (rows past the chunk read its last row and go in as zeros)
+        constexpr int NDQ = D / 8;
+        using VL = typename std::conditional<Q8, uint2, u32x4_t>::type;
+        const int dq = tid % NDQ, kq = tid / NDQ;
+        const bool st = kq < kDecRows / 4;
+        VL vl[4];
 #pragma unroll
-      for (int i = 0; i < VP; ++i) vw[i] = tid + i * NT < pieces ? vp[tid + i * NT] : u32x4_t{0u, 0u, 0u, 0u};
+        for (int i = 0; i < 4; ++i) {
+          const int rr = min(4 * kq + i, nr - 1);
+          vl[i] = st ? *reinterpret_cast<const VL *>(vseg + (size_t)(c0 + rr) * D + 8 * dq) : VL{};
+        }
+        if (st) {
 #pragma unroll
-      for (int i = 0; i < VP; ++i)
-        if (tid + i * NT < pieces) reinterpret_cast<u32x4_t *>(vs)[tid + i * NT] = vw[i];
+          for (int j = 0; j < 8; ++j) {
+            unsigned x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              unsigned e;
+              if constexpr (Q8) {
+                const unsigned w = j < 4 ? vl[i].x : vl[i].y;
+                e = __float_as_uint((float)(int)(int8_t)((w >> (8 * (j & 3))) & 0xffu)) >> 16;  // exact
+              } else {
+                e = (vl[i][j >> 1] >> (16 * (j & 1))) & 0xffffu;
+              }
+              x[i] = 4 * kq + i < nr ? e : 0u;
+            }
+            uint2 wv;
+            wv.x = x[0] | (x[1] << 16);
+            wv.y = x[2] | (x[3] << 16);
+            *reinterpret_cast<uint2 *>(vt + (size_t)(8 * dq + j) * kDecVtStride + 8 * kq) = wv;
+          }
+        }
+      } else {
+        u32x4_t vw[VP];
+#pragma unroll
+        for (int i = 0; i < VP; ++i) vw[i] = tid + i * NT < pieces ? vp[tid + i * NT] : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < VP; ++i)
+          if (tid + i * NT < pieces) reinterpret_cast<u32x4_t *>(vs)[tid + i * NT] = vw[i];
+      }
     }
     // logits (log2 domain) by MFMA, 16 query heads at a time (B operand:
     // head n16): acc[i] is row 4 grp + i of the wave's 16 against head n16
@@ -216,13 +307,13 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(dec
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rw = wave * 16 + grp * 4 + i;
-          zp[(h0 + n16) * kDecRows + rw] = rw < nr ? acc4[i] * (sh.scale2 * ksc) : -INFINITY;
+          zp[(h0 + n16) * zs + rw] = rw < nr ? acc4[i] * (sh.scale2 * ksc) : -INFINITY;
         }
     }
     __syncthreads();
     // per head: the running maximum, the chunk's weights, the running sum
     for (int h = wave; h < G; h += NT / 64) {
-      float *z = zp + h * kDecRows;
+      float *z = zp + h * zs;
       float m = -INFINITY;
       for (int j = lane; j < kDecRows; j += 64) m = fmaxf(m, z[j]);
       m = wave_max(m);
@@ -243,9 +334,45 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(dec
       }
     }
     __syncthreads();
-    // accumulators rescaled to the new maximum, then weight x V over the
-    // thread's rows of the chunk (one 16-byte V read gives 8 elements)
-    if (owner) {
+    if constexpr (PV) {
+      // O^T (rescaled to the new maxima) += V^T P^T, 32 rows per product
+      if (wave < D / 16) {
+#pragma unroll
+        for (int hg = 0; hg < kDecPvMaxG / 16; ++hg) {
+          if (16 * hg < G) {
+            const int hh = min(16 * hg + n16, G - 1);
+            oacc[hg] *= run[hh * 4 + 2];
+            const float *pz = zp + hh * kDecZs;
+#pragma unroll
+            for (int ks = 0; ks < kDecRows / 32; ++ks) {
+              if (32 * ks < nr) {
+                const unsigned char *va = vt + (size_t)(16 * wave + n16) * kDecVtStride + (32 * ks + 8 * grp) * 2;
+                const uint2 a0 = *reinterpret_cast<const uint2 *>(va), a1 = *reinterpret_cast<const uint2 *>(va + 8);
+                Frag<Bf16Tag> a, bh, bl;
+                a.v = __builtin_bit_cast(u16x8_t, u32x4_t{a0.x, a0.y, a1.x, a1.y});
+                const f32x4_t p0 = *reinterpret_cast<const f32x4_t *>(pz + 32 * ks + 8 * grp);
+                const f32x4_t p1 = *reinterpret_cast<const f32x4_t *>(pz + 32 * ks + 8 * grp + 4);
+                const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+                u32x4_t wh, wl;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const unsigned h2 = dec_pack_bf16(pv[2 * i], pv[2 * i + 1]);
+                  wh[i] = h2;
+                  wl[i] = dec_pack_bf16(pv[2 * i] - __uint_as_float(h2 << 16),
+                                        pv[2 * i + 1] - __uint_as_float(h2 & 0xffff0000u));
+                }
+                bh.v = __builtin_bit_cast(u16x8_t, wh);
+                bl.v = __builtin_bit_cast(u16x8_t, wl);
+                mfma_slice(oacc[hg], a, bh);
+                mfma_slice(oacc[hg], a, bl);
+              }
+            }
+          }
+        }
+      }
+    } else if (owner) {
+      // accumulators rescaled to the new maximum, then weight x V over the
+      // thread's rows of the chunk (one 16-byte V read gives 8 elements)
       const float sc = run[oh * 4 + 2];
       const float *p = zp + oh * kDecRows;
 #pragma unroll
@@ -277,6 +404,18 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(dec
   // in part order (over q, the weights and the V rows, all read by now)
   for (int h = tid; h < G; h += NT)
     part_ml[((size_t)lb * sh.Hq + (size_t)g * G + h) * S + s] = make_float2(run[h * 4 + 0], run[h * 4 + 1]);
+  if constexpr (PV) {
+    if (wave < D / 16) {
+#pragma unroll
+      for (int hg = 0; hg < kDecPvMaxG / 16; ++hg) {
+        const int h = 16 * hg + n16;
+        if (h < G)
+          *reinterpret_cast<f32x4_t *>(part_acc + (((size_t)lb * sh.Hq + (size_t)g * G + h) * S + s) * D +
+                                       16 * wave + 4 * grp) = oacc[hg] * vsc;
+      }
+    }
+    return;
+  }
   __syncthreads();
   float *red = dec_lds;  // [P][G][D]
   if (owner)
