@@ -2020,21 +2020,34 @@ size_t decode_ws_bytes(const Shape &s) {
   return align_up(units * sizeof(float2)) + align_up(units * (size_t)s.D * sizeof(float));
 }
 
-template <typename Tag, int D, bool Q8, bool PV>
+// KIND: 0 decode_partial_kernel on the vector units, 1 the same with weights x
+// V on the matrix cores, 2 and 3 decode_wave_kernel with one or two groups of
+// 16 heads.
+template <typename Tag, int D, bool Q8, int KIND>
 int launch_decode(const Shape &s, const DecodeTables &tb, const aircache_plan_buf *plan, void *ws, hipStream_t st,
                   DecodeScales scl) {
+  constexpr bool PV = KIND == 1;
   const int smax = decode_splits(s.L, s.B, s.Hkv, kDecTargetCus, s.ratio, s.Nv, s.Nt);
   const size_t units = (size_t)s.L * s.B * s.Hq * smax;
   float2 *ml = static_cast<float2 *>(ws);
   float *acc = reinterpret_cast<float *>(static_cast<char *>(ws) + align_up(units * sizeof(float2)));
   const int64_t cap = (int64_t)s.B * s.Hkv * (int64_t)s.S * s.D;
-  const size_t lds = PV ? (size_t)decode_pv_lds(s.G, D).total : (size_t)decode_lds_bytes(s.G, D, Q8 ? 1 : Tag::kBytes);
+  const size_t lds = KIND >= 2 ? (size_t)decode_wave_lds(s.G, D)
+                    : PV ? (size_t)decode_pv_lds(s.G, D).total : (size_t)decode_lds_bytes(s.G, D, Q8 ? 1 : Tag::kBytes);
   const long long grid = (long long)s.L * s.B * s.Hkv * smax;
   if (grid > INT32_MAX) return fail(AIRCACHE_EINVAL, "decode grid of %lld workgroups too large", grid);
   int rc;
-  if ((rc = allow_lds(decode_partial_kernel<Tag, D, Q8, PV>, lds))) return rc;
-  hipLaunchKernelGGL((decode_partial_kernel<Tag, D, Q8, PV>), dim3((unsigned)grid), dim3(kDecThreads), lds, st, s, tb,
-                     plan->budget, plan->out_off, cap, smax, ml, acc, scl);
+  if constexpr (KIND >= 2) {
+    static_assert(Tag::kBytes == 2, "decode_wave_kernel takes bfloat16 queries");
+    constexpr int NHG = KIND - 1;
+    if ((rc = allow_lds(decode_wave_kernel<D, Q8, NHG>, lds))) return rc;
+    hipLaunchKernelGGL((decode_wave_kernel<D, Q8, NHG>), dim3((unsigned)grid), dim3(kDecThreads), lds, st, s, tb,
+                       plan->budget, plan->out_off, cap, smax, ml, acc, scl);
+  } else {
+    if ((rc = allow_lds(decode_partial_kernel<Tag, D, Q8, PV>, lds))) return rc;
+    hipLaunchKernelGGL((decode_partial_kernel<Tag, D, Q8, PV>), dim3((unsigned)grid), dim3(kDecThreads), lds, st, s,
+                       tb, plan->budget, plan->out_off, cap, smax, ml, acc, scl);
+  }
   if ((rc = check_hip(hipGetLastError(), "decode_partial_kernel launch"))) return rc;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(s.L * s.B * s.Hq)), dim3(D), 0, st, s, tb,
                      plan->budget, plan->out_off, cap, smax, ml, acc);
@@ -2221,26 +2234,28 @@ int decode_common(const aircache_desc *desc, const void *const *q_dec, const air
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = desc->dtype == AIRCACHE_BF16;
   const DecodeScales scl{k_scale, v_scale};
-  // weights x V on the matrix cores for bfloat16 queries and kDecPvMinG <= G <= kDecPvMaxG
-  const bool pv = decode_pv(s.G, bf ? 2 : 4);
-  if (q8) {
-    if (bf && s.D == 128)
-      return pv ? launch_decode<Bf16Tag, 128, true, true>(s, tb, plan, workspace, st, scl)
-                : launch_decode<Bf16Tag, 128, true, false>(s, tb, plan, workspace, st, scl);
-    if (bf)
-      return pv ? launch_decode<Bf16Tag, 64, true, true>(s, tb, plan, workspace, st, scl)
-                : launch_decode<Bf16Tag, 64, true, false>(s, tb, plan, workspace, st, scl);
-    if (s.D == 128) return launch_decode<F32Tag, 128, true, false>(s, tb, plan, workspace, st, scl);
-    return launch_decode<F32Tag, 64, true, false>(s, tb, plan, workspace, st, scl);
+  const int kind = decode_kind(s.G, bf ? 2 : 4, s.ratio, s.Nv, s.Nt);
+#define AIRCACHE_DECODE_KINDS(TAG, DD, Q)                                                          \
+  switch (kind) {                                                                                  \
+    case 1: return launch_decode<TAG, DD, Q, 1>(s, tb, plan, workspace, st, scl);                 \
+    case 2: return launch_decode<TAG, DD, Q, 2>(s, tb, plan, workspace, st, scl);                 \
+    case 3: return launch_decode<TAG, DD, Q, 3>(s, tb, plan, workspace, st, scl);                 \
+    default: return launch_decode<TAG, DD, Q, 0>(s, tb, plan, workspace, st, scl);                \
   }
-  if (bf && s.D == 128)
-    return pv ? launch_decode<Bf16Tag, 128, false, true>(s, tb, plan, workspace, st, scl)
-              : launch_decode<Bf16Tag, 128, false, false>(s, tb, plan, workspace, st, scl);
-  if (bf)
-    return pv ? launch_decode<Bf16Tag, 64, false, true>(s, tb, plan, workspace, st, scl)
-              : launch_decode<Bf16Tag, 64, false, false>(s, tb, plan, workspace, st, scl);
-  if (s.D == 128) return launch_decode<F32Tag, 128, false, false>(s, tb, plan, workspace, st, scl);
-  return launch_decode<F32Tag, 64, false, false>(s, tb, plan, workspace, st, scl);
+  if (bf && s.D == 128) {
+    if (q8) AIRCACHE_DECODE_KINDS(Bf16Tag, 128, true)
+    AIRCACHE_DECODE_KINDS(Bf16Tag, 128, false)
+  }
+  if (bf) {
+    if (q8) AIRCACHE_DECODE_KINDS(Bf16Tag, 64, true)
+    AIRCACHE_DECODE_KINDS(Bf16Tag, 64, false)
+  }
+#undef AIRCACHE_DECODE_KINDS
+  if (s.D == 128)
+    return q8 ? launch_decode<F32Tag, 128, true, 0>(s, tb, plan, workspace, st, scl)
+              : launch_decode<F32Tag, 128, false, 0>(s, tb, plan, workspace, st, scl);
+  return q8 ? launch_decode<F32Tag, 64, true, 0>(s, tb, plan, workspace, st, scl)
+            : launch_decode<F32Tag, 64, false, 0>(s, tb, plan, workspace, st, scl);
 }
 
 extern "C" {

@@ -10,12 +10,14 @@
 //   o[l][b][h] = softmax(q[l][b][h] . K^T / sqrt(D)) V.
 //
 // Split-row decoding: the rows of each (l, b, g) are split evenly over S
-// workgroups (S fixed by the shape, for two workgroups per CU); a workgroup
+// workgroups (S fixed by the shape, for two workgroups per CU); in
+// decode_partial_kernel a workgroup
 // takes its rows in chunks of kDecRows for all G query heads of g at once
 // (every K and V row is read once from HBM), keeping per head a running
 // maximum, sum of exponentials and unnormalised output row (rescaled when the
 // maximum grows). decode_combine_kernel merges the splits of each (l, b, h)
-// in split order. The pass is a stream of K and V rows (HBM-bound): the
+// in split order (decode_wave_kernel, below, streams a split's rows per wave
+// instead). The pass is a stream of K and V rows (HBM-bound): the
 // logits are MFMA products of 16 key rows against 16 query heads, and the
 // weights x V product runs on the matrix cores for groups of 4 to 32 heads
 // (below) or in fp32 on the vector units.
@@ -427,6 +429,229 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(dec
     float a = 0.f;
     for (int q = 0; q < P; ++q) a += red[((size_t)q * G + h) * D + d];
     part_acc[(((size_t)lb * sh.Hq + (size_t)g * G + h) * S + s) * D + d] = a * vsc;
+  }
+}
+
+// One stream of rows per wave (bfloat16 queries, kDecPvMinG <= G <= 32). The
+// split's rows go to its eight waves in 16-row slices (slice k on wave k mod
+// 8); a wave keeps, per query head of the group, its own running maximum, sum
+// and O^T, so the slices need no block barrier: per slice, the logits are
+// MFMA products of the 16 key rows (A operand) against the heads' queries (B
+// operand: head n16 of lane n16), the online softmax reduces over the lane's
+// four rows and the four 16-lane row groups, and the weights, which the
+// logits' layout already places as the B operand of a 16x16x16 product, go as
+// two bfloat16 terms (hi = rn(p), lo = rn(p - hi)) against V^T, which the wave
+// stages in its own LDS area (one 40-byte row per output element: 16 rows of
+// bfloat16 plus 8 bytes, so the operand reads of 16 lanes hit distinct banks).
+// At the end the waves' (max, sum, O^T) go through LDS and are merged in wave
+// order.
+constexpr int kDwVtStride = 40;
+
+__host__ __device__ inline int decode_wave_nhg(int G) { return G > 16 ? 2 : 1; }
+
+// The decode kernel for a shape: 0 decode_partial_kernel with weights x V on
+// the vector units, 1 the same on the matrix cores, 2 / 3 decode_wave_kernel
+// with one / two groups of 16 heads, taken when a KV head's expected rows
+// (ratio * N_v + N_t) reach kDecWaveMinRows, so that a split gives every wave
+// several slices (measured against kind 1: workload 5, 1331 rows, 142 -> 127
+// us for the bfloat16 cache and 132 -> 100 us for the int8 cache; workloads 3
+// and 4, 416 and 318 rows, 16 -> 20 us and 25 -> 33 us, as most waves there
+// get one slice or none and the merge is not repaid).
+constexpr int kDecWaveMinRows = 512;
+inline int decode_kind(int G, int qbytes, double ratio, int Nv, int Nt) {
+  if (!decode_pv(G, qbytes)) return 0;
+  const long long rows = (long long)(ratio * (double)Nv) + Nt;
+  return rows >= kDecWaveMinRows ? 1 + decode_wave_nhg(G) : 1;
+}
+__host__ __device__ inline int decode_wave_lds(int G, int D) {
+  const int nw = kDecThreads / 64, nhg = decode_wave_nhg(G);
+  const int stage = nw * D * kDwVtStride;
+  const int merge = nw * nhg * 16 * D * 4 + nw * nhg * 16 * 8;
+  return stage > merge ? stage : merge;
+}
+
+// Maximum over the four 16-lane rows (lanes n, n + 16, n + 32, n + 48).
+__device__ __forceinline__ float dec_max_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+typedef __attribute__((ext_vector_type(4))) short dec_s16x4_t;
+
+template <int D, bool Q8, int NHG>
+__global__ __launch_bounds__(kDecThreads) void decode_wave_kernel(Shape sh, DecodeTables tb, const int32_t *budget,
+                                                                  const int64_t *out_off, int64_t cap_elems, int S,
+                                                                  float2 *part_ml, float *part_acc,
+                                                                  DecodeScales scl) {
+  using E = typename std::conditional<Q8, int8_t, uint16_t>::type;
+  using VL = typename std::conditional<Q8, uint2, u32x4_t>::type;
+  constexpr int NT = kDecThreads, NW = NT / 64, NC = D / 32, ND = D / 16, NDQ = D / 8;
+  extern __shared__ __attribute__((aligned(16))) float dec_lds[];
+  unsigned char *lds8 = reinterpret_cast<unsigned char *>(dec_lds);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n16 = lane & 15, grp = lane >> 4;
+  const int G = sh.G, Hkv = sh.Hkv, B = sh.B;
+  int rest = blockIdx.x;
+  const int s = rest % S;
+  rest /= S;
+  const int g = rest % Hkv;
+  rest /= Hkv;
+  const int b = rest % B, l = rest / B;
+  const int lb = l * B + b;
+  const int r = budget[lb];
+  const int64_t off = out_off[(size_t)l * (B + 1) + b];
+  // (compared as off <= cap - size: a stray offset near the top of int64 cannot wrap)
+  const bool ok = r >= 0 && r <= sh.Nv && off >= 0 && off <= cap_elems - (int64_t)Hkv * (r + sh.Nt) * D;
+  const int n = ok ? r + sh.Nt : 0;
+  const int lo = (int)((long long)n * s / S), hi = (int)((long long)n * (s + 1) / S);
+  const E *kseg = static_cast<const E *>(tb.k.p[l]) + (ok ? off + (int64_t)g * n * D : 0);
+  const E *vseg = static_cast<const E *>(tb.v.p[l]) + (ok ? off + (int64_t)g * n * D : 0);
+  const uint16_t *qb = static_cast<const uint16_t *>(tb.q.p[l]) + ((size_t)b * sh.Hq + (size_t)g * G) * D;
+  const float ksc = Q8 ? scl.k[(size_t)lb * Hkv + g] : 1.f, vsc = Q8 ? scl.v[(size_t)lb * Hkv + g] : 1.f;
+  const float sl2 = sh.scale2 * ksc;
+
+  // the queries of heads 16 hg + n16 (clamped into the group) as B operands
+  Frag<Bf16Tag> qf[NHG][NC];
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg) {
+    const int hq = min(16 * hg + n16, G - 1);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qf[hg][c].load(qb + (size_t)hq * D + 32 * c + 8 * grp);
+  }
+  float mrun[NHG], lrun[NHG];  // head n16: running maximum (log2 domain), this lane's part of the sum
+  f32x4_t oacc[NHG][ND];       // O^T: element 16 db + 4 grp + i, head 16 hg + n16
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg) {
+    mrun[hg] = -INFINITY;
+    lrun[hg] = 0.f;
+#pragma unroll
+    for (int db = 0; db < ND; ++db) oacc[hg][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  unsigned char *vt = lds8 + wave * D * kDwVtStride;  // this wave's V^T [D][16 rows]
+  const int dq = lane % NDQ, rq = lane / NDQ;          // V staging: rows 4 rq .. 4 rq + 3, elements 8 dq .. 8 dq + 7
+  const bool st = rq < 4;
+
+  for (int r0 = lo + 16 * wave; r0 < hi; r0 += 16 * NW) {
+    const int nr = min(16, hi - r0);
+    // every load of the slice issued before the first is used (rows past the
+    // slice read its last row)
+    Frag<Bf16Tag> kf[NC];
+    {
+      const E *kp = kseg + (size_t)(r0 + min(n16, nr - 1)) * D + 8 * grp;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if constexpr (Q8) codes_to_frag(kp + 32 * c, kf[c]);
+        else kf[c].load(kp + 32 * c);
+      }
+    }
+    VL vl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = r0 + min(4 * rq + i, nr - 1);
+      vl[i] = st ? *reinterpret_cast<const VL *>(vseg + (size_t)rr * D + 8 * dq) : VL{};
+    }
+    // logits: s[hg][i] = row 4 grp + i against head 16 hg + n16
+    f32x4_t sc[NHG];
+#pragma unroll
+    for (int hg = 0; hg < NHG; ++hg) {
+      sc[hg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) mfma_slice(sc[hg], kf[c], qf[hg][c]);
+    }
+    // V^T of the slice (rows past it as zeros)
+    small_wave_sync();  // the previous slice's operand reads are done
+    if (st) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        unsigned x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          unsigned e;
+          if constexpr (Q8) {
+            const unsigned w = j < 4 ? vl[i].x : vl[i].y;
+            e = __float_as_uint((float)(int)(int8_t)((w >> (8 * (j & 3))) & 0xffu)) >> 16;  // exact
+          } else {
+            e = (vl[i][j >> 1] >> (16 * (j & 1))) & 0xffffu;
+          }
+          x[i] = 4 * rq + i < nr ? e : 0u;
+        }
+        uint2 wv;
+        wv.x = x[0] | (x[1] << 16);
+        wv.y = x[2] | (x[3] << 16);
+        *reinterpret_cast<uint2 *>(vt + (8 * dq + j) * kDwVtStride + 8 * rq) = wv;
+      }
+    }
+    small_wave_sync();
+#pragma unroll
+    for (int hg = 0; hg < NHG; ++hg) {
+      float v[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = 4 * grp + i < nr ? sc[hg][i] * sl2 : -INFINITY;
+        mx = fmaxf(mx, v[i]);
+      }
+      mx = dec_max_rows(mx);
+      const float mnew = fmaxf(mrun[hg], mx);
+      const float alpha = exp2f(mrun[hg] - mnew);  // 0 before the first slice
+      mrun[hg] = mnew;
+      float p[4], ls = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = exp2f(v[i] - mnew);
+        ls += p[i];
+      }
+      lrun[hg] = lrun[hg] * alpha + ls;
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < ND; ++db) oacc[hg][db] *= alpha;
+      }
+      const unsigned h01 = dec_pack_bf16(p[0], p[1]), h23 = dec_pack_bf16(p[2], p[3]);
+      const unsigned l01 = dec_pack_bf16(p[0] - __uint_as_float(h01 << 16), p[1] - __uint_as_float(h01 & 0xffff0000u));
+      const unsigned l23 = dec_pack_bf16(p[2] - __uint_as_float(h23 << 16), p[3] - __uint_as_float(h23 & 0xffff0000u));
+      const dec_s16x4_t bh = __builtin_bit_cast(dec_s16x4_t, uint2{h01, h23});
+      const dec_s16x4_t bl = __builtin_bit_cast(dec_s16x4_t, uint2{l01, l23});
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const uint2 a = *reinterpret_cast<const uint2 *>(vt + (16 * db + n16) * kDwVtStride + 8 * grp);
+        const dec_s16x4_t av = __builtin_bit_cast(dec_s16x4_t, a);
+        oacc[hg][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bh, oacc[hg][db], 0, 0, 0);
+        oacc[hg][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bl, oacc[hg][db], 0, 0, 0);
+      }
+    }
+  }
+
+  // the waves' (max, sum, O^T) through LDS, merged in wave order
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg) lrun[hg] = sum_across_rows(lrun[hg]);
+  __syncthreads();  // every wave's staging area is read; the LDS now holds the parts
+  float *mo = dec_lds;                                               // [NW][NHG * 16][D]
+  float2 *mm = reinterpret_cast<float2 *>(dec_lds + NW * NHG * 16 * D);  // [NW][NHG * 16]
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg) {
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+      *reinterpret_cast<f32x4_t *>(mo + ((size_t)(wave * NHG + hg) * 16 + n16) * D + 16 * db + 4 * grp) =
+          oacc[hg][db];
+    if (grp == 0) mm[(wave * NHG + hg) * 16 + n16] = make_float2(mrun[hg], lrun[hg]);
+  }
+  __syncthreads();
+  for (int t = tid; t < G * D; t += NT) {
+    const int h = t / D, d = t - (t / D) * D;
+    float M = -INFINITY;
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mm[w * NHG * 16 + h].x);
+    float a = 0.f, L = 0.f;
+    for (int w = 0; w < NW; ++w) {
+      const float2 ml = mm[w * NHG * 16 + h];
+      const float e = ml.x > -INFINITY ? exp2f(ml.x - M) : 0.f;
+      a += mo[((size_t)w * NHG * 16 + h) * D + d] * e;
+      L += ml.y * e;
+    }
+    const size_t u = ((size_t)lb * sh.Hq + (size_t)g * G + h) * S + s;
+    part_acc[u * D + d] = a * vsc;
+    if (d == 0) part_ml[u] = make_float2(M, L);
   }
 }
 
