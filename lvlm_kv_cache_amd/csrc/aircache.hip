@@ -1234,6 +1234,12 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_i8_kernel(Shape sh, Qu
   for (int w = 1; w < kQuantThreads / 64; ++w) m = fmaxf(m, wmax[w]);
   const float sc = __fdiv_rn(m, 127.0f);
   if (tid == 0) (kv ? v_scale : k_scale)[(size_t)lb * sh.Hkv + g] = sc;
+  // rint(x / sc) with x / sc correctly rounded, from t = x * (1 / sc): t is
+  // within 2 ulp of that quotient (each rounding 0.5 ulp, 1 / sc and the
+  // product), and an ulp is at most 2^-16 for |t| < 256, so when t is farther
+  // than 2^-14 from every half-integer both round to the same integer; the
+  // rest (and a non-finite t) take the exact division
+  const float rc = sc > 0.f ? __fdiv_rn(1.0f, sc) : 0.f;
   // the codes (a lane past the end writes the last piece's codes again)
   for (int p0 = tid; p0 < cnt16; p0 += kQuantThreads * U) {
     float x[U][16];
@@ -1252,7 +1258,9 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_i8_kernel(Shape sh, Qu
         unsigned word = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float q = sc > 0.f ? rintf(__fdiv_rn(x[j][4 * w + e], sc)) : 0.f;
+          const float t = x[j][4 * w + e] * rc;
+          float q = rintf(t);
+          if (!(fabsf(fabsf(t - q) - 0.5f) > 0x1p-14f)) q = sc > 0.f ? rintf(__fdiv_rn(x[j][4 * w + e], sc)) : 0.f;
           q = fminf(fmaxf(q, -127.f), 127.f);
           word |= ((unsigned)(int)q & 0xffu) << (8 * e);
         }
