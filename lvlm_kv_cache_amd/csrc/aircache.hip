@@ -1193,8 +1193,19 @@ template <> __device__ __forceinline__ void load16_as_f32<Bf16Tag>(const uint16_
 
 constexpr int kQuantThreads = 512;
 constexpr int kQuantUnroll = 4;  // 16-element pieces per thread in flight
+// bfloat16 pieces per thread kept in registers between the passes, taken when
+// a segment's expected pieces fit them and the segments fit one round of the
+// grid (the registers leave one workgroup per CU; measured: workload 3, 224
+// segments of 3328 pieces, 16.9 -> 14.1 us; workloads 4 and 5, 896 and 1792
+// segments, 3% and 8% slower with them, so they keep R = 0)
+constexpr int kQuantKeep = 16;
+inline bool quant_keep(const Shape &s) {
+  const long long pieces = ((long long)(s.ratio * (double)s.Nv) + s.Nt) * s.D / 16;
+  const long long segs = 2LL * s.L * s.B * s.Hkv;
+  return pieces <= (long long)kQuantKeep * kQuantThreads && segs <= (long long)kTargetCus;
+}
 
-template <typename Tag>
+template <typename Tag, int R>
 __global__ __launch_bounds__(kQuantThreads) void quantize_i8_kernel(Shape sh, QuantTables tb, PlanPtrs plan,
                                                                     float *k_scale, float *v_scale, int64_t cap_elems) {
   using E = typename Tag::store_t;
@@ -1212,14 +1223,47 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_i8_kernel(Shape sh, Qu
   const int cnt16 = n * sh.D / 16;  // at least 4 (D >= 64, n >= 1)
   const E *src = static_cast<const E *>(kv ? tb.vo.p[l] : tb.ko.p[l]) + base;
   int8_t *dst = static_cast<int8_t *>(kv ? tb.vq.p[l] : tb.kq.p[l]) + base;
-  // the largest |x|: U pieces per thread in flight, indices past the end
-  // clamped to the last piece (no branch around a load)
+  // Pieces [0, kept) (piece tid + j NT in slot j, R slots) stay in registers
+  // between the two passes, so only the rest of a long segment is read twice.
+  constexpr int NT = kQuantThreads;
+  static_assert(R == 0 || Tag::kBytes == 2, "pieces are kept in registers for bfloat16 only");
+  const int kept = min(cnt16, R * NT);
+  u32x4_t raw[R > 0 ? R : 1][2];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if (j * NT < kept) {  // uniform; lanes past the end reload the last kept piece
+      const u32x4_t *q = reinterpret_cast<const u32x4_t *>(src + 16 * (size_t)min(tid + j * NT, kept - 1));
+      raw[j][0] = q[0];
+      raw[j][1] = q[1];
+    }
+  }
+  auto widen_raw = [&](int j, float (&x)[16]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * h + 2 * e] = __uint_as_float(raw[j][h][e] << 16);
+        x[8 * h + 2 * e + 1] = __uint_as_float(raw[j][h][e] & 0xffff0000u);
+      }
+  };
+  // the largest |x|: the kept pieces, then the rest with U pieces per thread
+  // in flight, indices past the end clamped to the last piece (no branch
+  // around a load)
   float m = 0.f;
-  for (int p0 = tid; p0 < cnt16; p0 += kQuantThreads * U) {
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if (j * NT < kept) {
+      float x[16];
+      widen_raw(j, x);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(x[e]));
+    }
+  }
+  for (int p0 = kept + tid; p0 < cnt16; p0 += NT * U) {
     float x[U][16];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int p = p0 + j * kQuantThreads;
+      const int p = p0 + j * NT;
       load16_as_f32<Tag>(src + 16 * (size_t)(p < cnt16 ? p : cnt16 - 1), x[j]);
     }
 #pragma unroll
@@ -1240,34 +1284,45 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_i8_kernel(Shape sh, Qu
   // than 2^-14 from every half-integer both round to the same integer; the
   // rest (and a non-finite t) take the exact division
   const float rc = sc > 0.f ? __fdiv_rn(1.0f, sc) : 0.f;
-  // the codes (a lane past the end writes the last piece's codes again)
-  for (int p0 = tid; p0 < cnt16; p0 += kQuantThreads * U) {
+  // the 16 codes of piece p
+  auto emit = [&](const float (&x)[16], int p) {
+    u32x4_t out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      unsigned word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float t = x[4 * w + e] * rc;
+        float q = rintf(t);
+        if (!(fabsf(fabsf(t - q) - 0.5f) > 0x1p-14f)) q = sc > 0.f ? rintf(__fdiv_rn(x[4 * w + e], sc)) : 0.f;
+        q = fminf(fmaxf(q, -127.f), 127.f);
+        word |= ((unsigned)(int)q & 0xffu) << (8 * e);
+      }
+      out[w] = word;
+    }
+    store_nt(reinterpret_cast<u32x4_t *>(dst + 16 * (size_t)p), out);
+  };
+  // the codes: the kept pieces from registers, the rest read again (a lane
+  // past the end writes the last piece's codes again)
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if (j * NT < kept && tid + j * NT < kept) {
+      float x[16];
+      widen_raw(j, x);
+      emit(x, tid + j * NT);
+    }
+  }
+  for (int p0 = kept + tid; p0 < cnt16; p0 += NT * U) {
     float x[U][16];
     int pj[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int p = p0 + j * kQuantThreads;
+      const int p = p0 + j * NT;
       pj[j] = p < cnt16 ? p : cnt16 - 1;
       load16_as_f32<Tag>(src + 16 * (size_t)pj[j], x[j]);
     }
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      u32x4_t out;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        unsigned word = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float t = x[j][4 * w + e] * rc;
-          float q = rintf(t);
-          if (!(fabsf(fabsf(t - q) - 0.5f) > 0x1p-14f)) q = sc > 0.f ? rintf(__fdiv_rn(x[j][4 * w + e], sc)) : 0.f;
-          q = fminf(fmaxf(q, -127.f), 127.f);
-          word |= ((unsigned)(int)q & 0xffu) << (8 * e);
-        }
-        out[w] = word;
-      }
-      store_nt(reinterpret_cast<u32x4_t *>(dst + 16 * (size_t)pj[j]), out);
-    }
+    for (int j = 0; j < U; ++j) emit(x[j], pj[j]);
   }
 }
 
@@ -2456,11 +2511,14 @@ int aircache_quantize_i8(const aircache_desc *desc, const aircache_plan_buf *pla
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t cap = (int64_t)s.B * s.Hkv * s.S * s.D;
   const dim3 grid((unsigned)(2 * s.L * s.B * s.Hkv));
-  if (desc->dtype == AIRCACHE_BF16)
-    hipLaunchKernelGGL(quantize_i8_kernel<Bf16Tag>, grid, dim3(kQuantThreads), 0, st, s, tb, plan_ptrs(plan),
+  if (desc->dtype == AIRCACHE_BF16 && quant_keep(s))
+    hipLaunchKernelGGL((quantize_i8_kernel<Bf16Tag, kQuantKeep>), grid, dim3(kQuantThreads), 0, st, s, tb,
+                       plan_ptrs(plan), k_scale, v_scale, cap);
+  else if (desc->dtype == AIRCACHE_BF16)
+    hipLaunchKernelGGL((quantize_i8_kernel<Bf16Tag, 0>), grid, dim3(kQuantThreads), 0, st, s, tb, plan_ptrs(plan),
                        k_scale, v_scale, cap);
   else
-    hipLaunchKernelGGL(quantize_i8_kernel<F32Tag>, grid, dim3(kQuantThreads), 0, st, s, tb, plan_ptrs(plan),
+    hipLaunchKernelGGL((quantize_i8_kernel<F32Tag, 0>), grid, dim3(kQuantThreads), 0, st, s, tb, plan_ptrs(plan),
                        k_scale, v_scale, cap);
   return check_hip(hipGetLastError(), "quantize_i8_kernel launch");
 }
