@@ -2090,7 +2090,8 @@ template <typename Tag, int D, bool Q8, int KIND>
 int launch_decode(const Shape &s, const DecodeTables &tb, const aircache_plan_buf *plan, void *ws, hipStream_t st,
                   DecodeScales scl) {
   constexpr bool PV = KIND == 1;
-  const int smax = decode_splits(s.L, s.B, s.Hkv, kDecTargetCus, s.ratio, s.Nv, s.Nt);
+  const int smax = KIND >= 2 ? decode_wave_splits(s.L, s.B, s.Hkv, kDecTargetCus, s.ratio, s.Nv, s.Nt)
+                             : decode_splits(s.L, s.B, s.Hkv, kDecTargetCus, s.ratio, s.Nv, s.Nt);
   const size_t units = (size_t)s.L * s.B * s.Hq * smax;
   float2 *ml = static_cast<float2 *>(ws);
   float *acc = reinterpret_cast<float *>(static_cast<char *>(ws) + align_up(units * sizeof(float2)));
@@ -2297,7 +2298,7 @@ int decode_common(const aircache_desc *desc, const void *const *q_dec, const air
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = desc->dtype == AIRCACHE_BF16;
   const DecodeScales scl{k_scale, v_scale};
-  const int kind = decode_kind(s.G, bf ? 2 : 4, s.ratio, s.Nv, s.Nt);
+  const int kind = decode_kind(s.G, bf ? 2 : 4, s.ratio, s.Nv, s.Nt, s.L, s.B, s.Hkv);
 #define AIRCACHE_DECODE_KINDS(TAG, DD, Q)                                                          \
   switch (kind) {                                                                                  \
     case 1: return launch_decode<TAG, DD, Q, 1>(s, tb, plan, workspace, st, scl);                 \

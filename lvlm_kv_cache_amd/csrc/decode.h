@@ -449,19 +449,32 @@ constexpr int kDwVtStride = 40;
 
 __host__ __device__ inline int decode_wave_nhg(int G) { return G > 16 ? 2 : 1; }
 
+// Splits per (l, b, g) for decode_wave_kernel: one round of its two
+// workgroups per CU at most (never more than decode_splits, which sizes the
+// workspace).
+inline int decode_wave_splits(int L, int B, int Hkv, int cus, double ratio, int Nv, int Nt) {
+  const long long units = (long long)L * B * Hkv;
+  long long s = 2LL * cus / units;
+  const int smax = decode_splits(L, B, Hkv, cus, ratio, Nv, Nt);
+  if (s > smax) s = smax;
+  return s < 1 ? 1 : (int)s;
+}
+
 // The decode kernel for a shape: 0 decode_partial_kernel with weights x V on
 // the vector units, 1 the same on the matrix cores, 2 / 3 decode_wave_kernel
-// with one / two groups of 16 heads, taken when a KV head's expected rows
-// (ratio * N_v + N_t) reach kDecWaveMinRows, so that a split gives every wave
-// several slices (measured against kind 1: workload 5, 1331 rows, 142 -> 127
-// us for the bfloat16 cache and 132 -> 100 us for the int8 cache; workloads 3
-// and 4, 416 and 318 rows, 16 -> 20 us and 25 -> 33 us, as most waves there
-// get one slice or none and the merge is not repaid).
-constexpr int kDecWaveMinRows = 512;
-inline int decode_kind(int G, int qbytes, double ratio, int Nv, int Nt) {
+// with one / two groups of 16 heads, taken when its splits hold at least
+// kDecWaveMinRows expected rows (ratio * N_v + N_t per KV head), so that every
+// wave gets several slices. Measured against kind 1: workload 5 (1331 rows,
+// one split) 142 -> 128 us for the bfloat16 cache and 132 -> 92-96 us for the
+// int8 cache; workload 4 (318 rows, one split) 25.3 -> 23.7 us and 26.3 ->
+// 23.3 us; workload 3 (416 rows over four splits) keeps kind 1, with which it
+// took 16 us against 20 us.
+constexpr int kDecWaveMinRows = 256;
+inline int decode_kind(int G, int qbytes, double ratio, int Nv, int Nt, int L, int B, int Hkv) {
   if (!decode_pv(G, qbytes)) return 0;
   const long long rows = (long long)(ratio * (double)Nv) + Nt;
-  return rows >= kDecWaveMinRows ? 1 + decode_wave_nhg(G) : 1;
+  const int sw = decode_wave_splits(L, B, Hkv, kDecTargetCus, ratio, Nv, Nt);
+  return rows / sw >= kDecWaveMinRows ? 1 + decode_wave_nhg(G) : 1;
 }
 __host__ __device__ inline int decode_wave_lds(int G, int D) {
   const int nw = kDecThreads / 64, nhg = decode_wave_nhg(G);

@@ -110,11 +110,16 @@ EDGE = [
     dict(Nv=700, Nt=80, Hq=14, Hkv=7, D=64, dtype="bf16", L=2, B=2),
     dict(Nv=333, Nt=24, Hq=8, Hkv=2, D=64, dtype="f32", L=3, B=5),
     # the matrix-core weights x V (bfloat16, 4 <= G <= 32): head_dim 64, a
-    # second group of 16 heads only partly used; at ratio 1.0 (at least 512
-    # rows per KV head) one stream of rows per wave
+    # second group of 16 heads only partly used
     dict(Nv=500, Nt=60, Hq=16, Hkv=2, D=64, dtype="bf16", L=2, B=2),
     dict(Nv=600, Nt=30, Hq=20, Hkv=1, D=128, dtype="bf16", L=2),
     dict(Nv=520, Nt=20, Hq=24, Hkv=1, D=64, dtype="bf16", L=2),
+    # enough (layer, sample, KV head) units that at ratio 1.0 a split keeps at
+    # least 256 rows: one stream of rows per wave, head_dim 64 and 128, one
+    # and two groups of 16 heads
+    dict(Nv=500, Nt=20, Hq=32, Hkv=4, D=64, dtype="bf16", L=8, B=8),
+    dict(Nv=500, Nt=20, Hq=80, Hkv=4, D=64, dtype="bf16", L=8, B=8),
+    dict(Nv=500, Nt=20, Hq=40, Hkv=2, D=128, dtype="bf16", L=8, B=16),
     # bfloat16 with G > 32: the vector-unit weights x V
     dict(Nv=100, Nt=20, Hq=40, Hkv=1, D=64, dtype="bf16", L=2),
 ]
