@@ -2113,6 +2113,7 @@ int launch_decode(const Shape &s, const DecodeTables &tb, const aircache_plan_bu
                        tb, plan->budget, plan->out_off, cap, smax, ml, acc, scl);
   }
   if ((rc = check_hip(hipGetLastError(), "decode_partial_kernel launch"))) return rc;
+  if (KIND >= 2 && smax == 1) return AIRCACHE_OK;  // decode_wave_kernel wrote o itself
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)(s.L * s.B * s.Hq)), dim3(D), 0, st, s, tb,
                      plan->budget, plan->out_off, cap, smax, ml, acc);
   return check_hip(hipGetLastError(), "decode_combine_kernel launch");

@@ -662,6 +662,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_wave_kernel(Shape sh, Deco
       a += mo[((size_t)w * NHG * 16 + h) * D + d] * e;
       L += ml.y * e;
     }
+    if (S == 1) {
+      // one split: the output itself, as decode_combine_kernel would form it
+      // (its weight exp2(M - M) is 1; an empty segment gives 0 / 0)
+      static_cast<float *>(tb.o.p[l])[((size_t)b * sh.Hq + (size_t)g * G + h) * D + d] = (a * vsc) / L;
+      continue;
+    }
     const size_t u = ((size_t)lb * sh.Hq + (size_t)g * G + h) * S + s;
     part_acc[u * D + d] = a * vsc;
     if (d == 0) part_ml[u] = make_float2(M, L);
