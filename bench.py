@@ -432,7 +432,7 @@ def main():
         dec_bytes = (2.0 * w.Hkv * w.D * esz * float((budget_now + w.Nt).sum()) +
                      w.L * w.B * w.Hq * w.D * (esz + 4))
         dec_gbps = dec_bytes / (dec_us * 1e-6) / 1e9
-        dec = {"kernels": ["decode_partial_kernel", "decode_combine_kernel"], "us_per_call": dec_us,
+        dec = {"kernels": ["decode_partial_kernel or decode_wave_kernel", "decode_combine_kernel (none with one split)"], "us_per_call": dec_us,
                "algorithmic_bytes": dec_bytes, "achieved_gbps": dec_gbps, "peak_gbps": PEAK_HBM_GBPS,
                "frac": dec_gbps / PEAK_HBM_GBPS, "dense_cache_bytes": 2.0 * w.L * w.B * w.Hkv * w.S * w.D * esz,
                "retained_row_frac": float((budget_now + w.Nt).sum()) / (w.L * w.B * (w.Nv + w.Nt))}
@@ -473,7 +473,7 @@ def main():
         torch.cuda.synchronize()
         d8_us = 1e3 * e0.elapsed_time(e1) / a.steps
         d8_bytes = n_el * 1 + w.L * w.B * w.Hq * w.D * (esz + 4)  # every kept code once, queries, outputs
-        dec["int8_cache"] = {"kernels": ["decode_partial_kernel (int8)", "decode_combine_kernel"],
+        dec["int8_cache"] = {"kernels": ["decode_partial_kernel or decode_wave_kernel (int8)", "decode_combine_kernel (none with one split)"],
                              "us_per_call": d8_us, "algorithmic_bytes": d8_bytes,
                              "achieved_gbps": d8_bytes / (d8_us * 1e-6) / 1e9,
                              "frac": d8_bytes / (d8_us * 1e-6) / 1e9 / PEAK_HBM_GBPS}
