@@ -2299,7 +2299,7 @@ int decode_common(const aircache_desc *desc, const void *const *q_dec, const air
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = desc->dtype == AIRCACHE_BF16;
   const DecodeScales scl{k_scale, v_scale};
-  const int kind = decode_kind(s.G, bf ? 2 : 4, s.ratio, s.Nv, s.Nt, s.L, s.B, s.Hkv);
+  const int kind = decode_kind(s.G, bf ? 2 : 4, s.ratio, s.Nv, s.Nt);
 #define AIRCACHE_DECODE_KINDS(TAG, DD, Q)                                                          \
   switch (kind) {                                                                                  \
     case 1: return launch_decode<TAG, DD, Q, 1>(s, tb, plan, workspace, st, scl);                 \

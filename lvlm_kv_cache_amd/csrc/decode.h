@@ -449,12 +449,22 @@ constexpr int kDwVtStride = 40;
 
 __host__ __device__ inline int decode_wave_nhg(int G) { return G > 16 ? 2 : 1; }
 
-// Splits per (l, b, g) for decode_wave_kernel: one round of its two
-// workgroups per CU at most (never more than decode_splits, which sizes the
-// workspace).
+// decode_wave_kernel is taken when a KV head's expected rows (ratio * N_v +
+// N_t) reach kDecWaveMinRows; its splits per (l, b, g) keep at least that
+// many rows each and fill at most one round of its two workgroups per CU
+// (never more than decode_splits, which sizes the workspace). With one split
+// per unit the kernel writes the output itself. Measured against kind 1:
+// workload 3 (416 rows, one split) 16.2 -> 12.8 us for the bfloat16 cache and
+// 16.3 -> 13.7 us for the int8 cache; workload 4 (318 rows) 25.3 -> 20.6 us
+// and 26.5 -> 19.4 us; workload 5 (1331 rows) 142 -> 120 us and 132 -> 89
+// us. (With the splits of decode_partial_kernel, about 100 rows each on
+// workload 3, the per-wave kernel had been slower: 20 us.)
+constexpr int kDecWaveMinRows = 256;
 inline int decode_wave_splits(int L, int B, int Hkv, int cus, double ratio, int Nv, int Nt) {
   const long long units = (long long)L * B * Hkv;
+  const long long rows = (long long)(ratio * (double)Nv) + Nt;
   long long s = 2LL * cus / units;
+  if (s > rows / kDecWaveMinRows) s = rows / kDecWaveMinRows;
   const int smax = decode_splits(L, B, Hkv, cus, ratio, Nv, Nt);
   if (s > smax) s = smax;
   return s < 1 ? 1 : (int)s;
@@ -462,19 +472,11 @@ inline int decode_wave_splits(int L, int B, int Hkv, int cus, double ratio, int 
 
 // The decode kernel for a shape: 0 decode_partial_kernel with weights x V on
 // the vector units, 1 the same on the matrix cores, 2 / 3 decode_wave_kernel
-// with one / two groups of 16 heads, taken when its splits hold at least
-// kDecWaveMinRows expected rows (ratio * N_v + N_t per KV head), so that every
-// wave gets several slices. Measured against kind 1: workload 5 (1331 rows,
-// one split) 142 -> 128 us for the bfloat16 cache and 132 -> 92-96 us for the
-// int8 cache; workload 4 (318 rows, one split) 25.3 -> 23.7 us and 26.3 ->
-// 23.3 us; workload 3 (416 rows over four splits) keeps kind 1, with which it
-// took 16 us against 20 us.
-constexpr int kDecWaveMinRows = 256;
-inline int decode_kind(int G, int qbytes, double ratio, int Nv, int Nt, int L, int B, int Hkv) {
+// with one / two groups of 16 heads.
+inline int decode_kind(int G, int qbytes, double ratio, int Nv, int Nt) {
   if (!decode_pv(G, qbytes)) return 0;
   const long long rows = (long long)(ratio * (double)Nv) + Nt;
-  const int sw = decode_wave_splits(L, B, Hkv, kDecTargetCus, ratio, Nv, Nt);
-  return rows / sw >= kDecWaveMinRows ? 1 + decode_wave_nhg(G) : 1;
+  return rows >= kDecWaveMinRows ? 1 + decode_wave_nhg(G) : 1;
 }
 __host__ __device__ inline int decode_wave_lds(int G, int D) {
   const int nw = kDecThreads / 64, nhg = decode_wave_nhg(G);

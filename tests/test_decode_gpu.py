@@ -114,9 +114,9 @@ EDGE = [
     dict(Nv=500, Nt=60, Hq=16, Hkv=2, D=64, dtype="bf16", L=2, B=2),
     dict(Nv=600, Nt=30, Hq=20, Hkv=1, D=128, dtype="bf16", L=2),
     dict(Nv=520, Nt=20, Hq=24, Hkv=1, D=64, dtype="bf16", L=2),
-    # enough (layer, sample, KV head) units that at ratio 1.0 a split keeps at
-    # least 256 rows: one stream of rows per wave, head_dim 64 and 128, one
-    # and two groups of 16 heads
+    # enough (layer, sample, KV head) units that at ratio 1.0 the per-wave
+    # kernel takes two splits per unit (with the combine): head_dim 64 and
+    # 128, one and two groups of 16 heads
     dict(Nv=500, Nt=20, Hq=32, Hkv=4, D=64, dtype="bf16", L=8, B=8),
     dict(Nv=500, Nt=20, Hq=80, Hkv=4, D=64, dtype="bf16", L=8, B=8),
     dict(Nv=500, Nt=20, Hq=40, Hkv=2, D=128, dtype="bf16", L=8, B=16),
